@@ -1,0 +1,167 @@
+"""CPU oracle for paged sliding-window attention and the LSE merge.
+
+TEST INFRASTRUCTURE ONLY: imported by ``tests/``, by the smoke check and by the
+CPU-baseline leg of the benchmark, never by the product package.  The numerics
+live in ``oracle.c`` (plain C, IEEE double); this module only compiles it with
+gcc, marshals arrays and calls it.
+
+Parity status: every function here is pinned by the CPU tests in
+``tests/test_oracle_pins.py`` (closed forms, special cases that reduce to a
+library routine, invariants and brute force on tiny inputs).
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import subprocess
+from typing import Optional, Sequence
+
+import numpy as np
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_SRC = os.path.join(_HERE, "oracle.c")
+_LIB_PATH = os.path.join(_HERE, "liboracle.so")
+_lib = None
+
+BF16 = 0
+FP32 = 1
+
+
+def compile_source(src: str, out: str) -> str:
+    """gcc -O2 a copy of the oracle source into a shared library at ``out``."""
+    tmp = out + f".tmp{os.getpid()}"
+    subprocess.run(["gcc", "-O2", "-std=c99", "-Wall", "-Wextra", "-shared", "-fPIC",
+                    "-o", tmp, src, "-lm"], check=True)
+    os.replace(tmp, out)
+    return out
+
+
+def build(force: bool = False) -> str:
+    """Compile ``oracle.c`` into ``liboracle.so`` next to it (gcc, -O2)."""
+    stale = (not os.path.exists(_LIB_PATH)
+             or os.path.getmtime(_LIB_PATH) < os.path.getmtime(_SRC))
+    if force or stale:
+        compile_source(_SRC, _LIB_PATH)
+    return _LIB_PATH
+
+
+class OracleLib:
+    """ctypes handle on one compiled copy of ``oracle.c``."""
+
+    def __init__(self, path: str):
+        lib = ctypes.CDLL(path)
+        P = ctypes.c_void_p
+        i32, i64, f64 = ctypes.c_int32, ctypes.c_int64, ctypes.c_double
+        lib.oracle_paged_attention.restype = ctypes.c_int
+        lib.oracle_paged_attention.argtypes = [
+            i32, P, P, P, P, i32, i32, i32, i32, i32, i32, f64, i32, P, P, P, P, i64, i64, i64,
+            P, P,
+        ]
+        lib.oracle_merge_state.restype = None
+        lib.oracle_merge_state.argtypes = [i64, i32, i32, P, P, P, P, P, P]
+        self.lib = lib
+        self.path = path
+
+
+def _load():
+    global _lib
+    if _lib is None:
+        _lib = OracleLib(build())
+    return _lib
+
+
+def _ptr(a: np.ndarray):
+    return a.ctypes.data_as(ctypes.c_void_p)
+
+
+def _as_stored(t) -> tuple:
+    """(contiguous numpy array of the stored bits, dtype code)."""
+    import torch
+
+    t = t.detach().cpu().contiguous()
+    if t.dtype == torch.bfloat16:
+        return t.view(torch.int16).numpy(), BF16
+    if t.dtype == torch.float32:
+        return t.numpy(), FP32
+    raise TypeError(f"oracle: unsupported input dtype {t.dtype}")
+
+
+def _i32(t) -> np.ndarray:
+    import torch
+
+    if isinstance(t, torch.Tensor):
+        t = t.detach().cpu().numpy()
+    return np.ascontiguousarray(np.asarray(t, dtype=np.int32))
+
+
+def paged_attention(q, k_cache, v_cache, qo_indptr, kv_indptr, kv_indices, kv_last_page_len, *,
+                    num_qo_heads: int, num_kv_heads: int, head_dim: int, page_size: int,
+                    causal: bool, window_left: int, sm_scale: float,
+                    rows: Optional[Sequence[int]] = None, key_lo: int = 0,
+                    key_hi: int = np.iinfo(np.int64).max, impl: Optional[OracleLib] = None):
+    """Reference (O, LSE) in float64.
+
+    ``q``/``k_cache``/``v_cache`` are torch tensors (bf16 or fp32, any device;
+    they are copied to the host).  Returns ``o`` ``[nnz_qo, H_q, D]`` and ``lse``
+    ``[nnz_qo, H_q]``; rows not listed in ``rows`` are NaN.
+    """
+    lib = (impl or _load()).lib
+    qa, qd = _as_stored(q)
+    ka, kd = _as_stored(k_cache)
+    va, vd = _as_stored(v_cache)
+    if not (qd == kd == vd):
+        raise TypeError("oracle: q, k and v must share one stored dtype")
+    qo = _i32(qo_indptr)
+    kvp = _i32(kv_indptr)
+    kvi = _i32(kv_indices)
+    last = _i32(kv_last_page_len)
+    batch = len(kvp) - 1
+    nnz_qo = int(qo[-1])
+    o = np.full((nnz_qo, num_qo_heads, head_dim), np.nan, dtype=np.float64)
+    lse = np.full((nnz_qo, num_qo_heads), np.nan, dtype=np.float64)
+    if rows is not None:
+        rows_a = np.ascontiguousarray(np.asarray(rows, dtype=np.int64))
+        rp, nr = _ptr(rows_a), len(rows_a)
+    else:
+        rows_a, rp, nr = None, None, 0
+    rc = lib.oracle_paged_attention(
+        batch, _ptr(qo), _ptr(kvp), _ptr(kvi), _ptr(last), page_size, num_qo_heads,
+        num_kv_heads, head_dim, int(bool(causal)), window_left, float(sm_scale), qd, _ptr(qa),
+        _ptr(ka), _ptr(va), rp, nr, int(key_lo), int(key_hi), _ptr(o), _ptr(lse))
+    if rc != 0:
+        raise ValueError(f"oracle_paged_attention: malformed layout (rc={rc})")
+    return o, lse
+
+
+def case_attention(case, rows=None, window_left: Optional[int] = None, **kw):
+    """``paged_attention`` on a ``paged_kv_sliding_amd.synth.Case``."""
+    return paged_attention(
+        case.q, case.k_cache, case.v_cache, case.qo_indptr, case.kv_indptr, case.kv_indices,
+        case.kv_last_page_len, num_qo_heads=case.num_qo_heads, num_kv_heads=case.num_kv_heads,
+        head_dim=case.head_dim, page_size=case.page_size, causal=case.causal,
+        window_left=case.window_left if window_left is None else window_left,
+        sm_scale=case.sm_scale, rows=rows, **kw)
+
+
+def merge_state(v_a, s_a, v_b, s_b, impl: Optional[OracleLib] = None):
+    """Pairwise merge of two (v [N,H,D], s [N,H]) partials, float64 in and out."""
+    lib = (impl or _load()).lib
+    v_a = np.ascontiguousarray(v_a, dtype=np.float64)
+    v_b = np.ascontiguousarray(v_b, dtype=np.float64)
+    s_a = np.ascontiguousarray(s_a, dtype=np.float64)
+    s_b = np.ascontiguousarray(s_b, dtype=np.float64)
+    n, h, d = v_a.shape
+    if v_b.shape != v_a.shape or s_a.shape != (n, h) or s_b.shape != (n, h):
+        raise ValueError("merge_state: shape mismatch")
+    v = np.empty_like(v_a)
+    s = np.empty_like(s_a)
+    lib.oracle_merge_state(n, h, d, _ptr(v_a), _ptr(s_a), _ptr(v_b), _ptr(s_b), _ptr(v), _ptr(s))
+    return v, s
+
+
+def merge_many(parts, impl: Optional[OracleLib] = None):
+    """Left fold of ``merge_state`` over a list of (v, s) partials."""
+    v, s = parts[0]
+    for vb, sb in parts[1:]:
+        v, s = merge_state(v, s, vb, sb, impl=impl)
+    return v, s

@@ -1,0 +1,246 @@
+/*
+ * oracle.c -- plain CPU reference for batched attention over a paged KV cache
+ * with a sliding-window mask, plus the merge of two (output, LSE) partials.
+ *
+ * TEST INFRASTRUCTURE ONLY.  Nothing in the product library links, loads or
+ * calls this file; only the tests, the smoke check and the CPU-baseline leg
+ * of the benchmark do.  It shares no code, header or table with the HIP
+ * kernels.
+ *
+ * Every quantity is computed in IEEE double precision, straight from the
+ * definition, one (query token, query head) row at a time, with no tiling,
+ * no online rescaling and no reordering beyond what the definition states.
+ *
+ * Sources (the web pages this follows):
+ *  [PR31501]  sglang PR "[flashinfer] Pass window_left at plan time for the
+ *             SWA paged prefill wrapper", section "What".
+ *  [FIB]      sglang python/sglang/srt/layers/attention/flashinfer_backend.py,
+ *             functions named below.
+ *  [PR234]    AMD-Ecosystem/flashinfer PR "fix(rocm): correct AITER decode
+ *             backend gaps -- sliding window, CUDA graph, return_lse",
+ *             sections "Why each fix" 1 (sliding window) and 3 (return_lse).
+ */
+#include <math.h>
+#include <stdint.h>
+#include <stdlib.h>
+#include <string.h>
+
+#define ORACLE_BF16 0
+#define ORACLE_FP32 1
+
+/* Exact widening of one stored element to double.  bf16 is the upper half of
+ * an IEEE binary32, so shifting its 16 bits up gives the same value. */
+static double load_elem(const void *base, int dtype, int64_t idx)
+{
+    if (dtype == ORACLE_BF16) {
+        uint32_t u = (uint32_t)((const uint16_t *)base)[idx] << 16;
+        float f;
+        memcpy(&f, &u, sizeof f);
+        return (double)f;
+    }
+    return (double)((const float *)base)[idx];
+}
+
+/* Number of keys held by request b of a CSR page table: all pages but the
+ * last are full, the last holds kv_last_page_len[b] slots.  (The argument
+ * names are the ones [FIB] fast_prefill_plan takes: paged_kv_indptr,
+ * paged_kv_indices, paged_kv_last_page_len.) */
+static int64_t request_kv_len(const int32_t *kv_indptr, const int32_t *kv_last_page_len,
+                              int32_t page_size, int32_t b)
+{
+    int64_t npages = (int64_t)kv_indptr[b + 1] - kv_indptr[b];
+    if (npages <= 0)
+        return 0;
+    return (npages - 1) * (int64_t)page_size + kv_last_page_len[b];
+}
+
+/* Flat element offset of logical key j of request b, KV head hk, dim 0, in an
+ * NHD cache [num_pages, page_size, H_kv, D]: page id from the CSR indices,
+ * slot = j mod page_size. */
+static int64_t key_offset(const int32_t *kv_indptr, const int32_t *kv_indices,
+                          int32_t page_size, int32_t num_kv_heads, int32_t head_dim,
+                          int32_t b, int64_t j, int32_t hk)
+{
+    int64_t page = kv_indices[(int64_t)kv_indptr[b] + j / page_size];
+    int64_t slot = j % page_size;
+    return ((page * page_size + slot) * num_kv_heads + hk) * (int64_t)head_dim;
+}
+
+/* Visibility of key j to the query at absolute position p.
+ * Window ([PR234] "Why each fix" 1; [FIB] _build_swa_prefix_custom_mask):
+ * window_left = W >= 0 lets position p see keys p-W .. p, i.e. W+1 keys;
+ * W = -1 switches the window off.  Causality: keys after p are hidden.
+ * key_lo/key_hi only restrict the key range (used to split a request). */
+static int key_visible(int64_t j, int64_t p, int32_t causal, int32_t window_left,
+                       int64_t key_lo, int64_t key_hi)
+{
+    if (j < key_lo || j >= key_hi)
+        return 0;
+    if (causal && j > p)
+        return 0;
+    if (window_left >= 0 && j < p - (int64_t)window_left)
+        return 0;
+    return 1;
+}
+
+/*
+ * Attention of every query row (or of the listed rows) over its request's
+ * paged keys.
+ *
+ *  Request b holds qo_len_b = qo_indptr[b+1]-qo_indptr[b] queries and kv_len_b
+ *  keys; its queries are the last qo_len_b positions of the sequence, so query
+ *  i sits at p = (kv_len_b - qo_len_b) + i.  This is how the extend step with a
+ *  cached prefix lines up ([FIB] call_begin_forward builds qo_indptr from
+ *  seq_len - prefix_len; forward_extend writes the new keys to the cache before
+ *  the paged kernel reads them).  A decode request is qo_len_b = 1, p =
+ *  kv_len_b - 1.  A request with no keys may still carry queries (a padded
+ *  decode slot); they see nothing.
+ *
+ *  Query head h reads KV head h / (H_q / H_kv) (grouped-query heads share
+ *  contiguous groups).
+ *
+ *  s_j   = sm_scale * sum_d q[d] * k_j[d]                for visible j
+ *  m     = max_j s_j,  l = sum_j exp(s_j - m)
+ *  o     = sum_j exp(s_j - m) / l * v_j
+ *  lse   = m + ln(l)          (natural log; the log-sum-exp of the logits)
+ *  empty visible set: o = 0, lse = -inf.
+ *
+ *  Inputs are read in their stored type (ORACLE_BF16 as raw 16-bit words,
+ *  ORACLE_FP32) and widened exactly.  o is [nnz_qo, H_q, D] double, lse is
+ *  [nnz_qo, H_q] double.  rows (may be NULL) lists the global query-token
+ *  indices to compute; other rows are left untouched.
+ *
+ *  Returns 0 on success, -1 on a malformed layout, -2 when out of memory.
+ */
+int oracle_paged_attention(int32_t batch, const int32_t *qo_indptr, const int32_t *kv_indptr,
+                           const int32_t *kv_indices, const int32_t *kv_last_page_len,
+                           int32_t page_size, int32_t num_qo_heads, int32_t num_kv_heads,
+                           int32_t head_dim, int32_t causal, int32_t window_left,
+                           double sm_scale, int32_t in_dtype, const void *q,
+                           const void *k_cache, const void *v_cache, const int64_t *rows,
+                           int64_t n_rows, int64_t key_lo, int64_t key_hi, double *o,
+                           double *lse)
+{
+    if (batch < 0 || page_size <= 0 || num_kv_heads <= 0 || num_qo_heads % num_kv_heads)
+        return -1;
+    const int32_t group = num_qo_heads / num_kv_heads;
+    const int64_t nnz_qo = qo_indptr[batch];
+    const int64_t count = rows ? n_rows : nnz_qo;
+
+    int64_t max_kv = 0;
+    for (int32_t b = 0; b < batch; ++b) {
+        int64_t n = request_kv_len(kv_indptr, kv_last_page_len, page_size, b);
+        int64_t nq = (int64_t)qo_indptr[b + 1] - qo_indptr[b];
+        if (nq < 0 || (nq > n && n > 0))
+            return -1;
+        if (n > max_kv)
+            max_kv = n;
+    }
+    double *s = (double *)malloc(sizeof(double) * (size_t)(max_kv > 0 ? max_kv : 1));
+    double *acc = (double *)malloc(sizeof(double) * (size_t)head_dim);
+    if (!s || !acc) {
+        free(s);
+        free(acc);
+        return -2;
+    }
+
+    for (int64_t r = 0; r < count; ++r) {
+        const int64_t t = rows ? rows[r] : r;
+        if (t < 0 || t >= nnz_qo)
+            continue;
+        int32_t b = 0;
+        while (b + 1 < batch && qo_indptr[b + 1] <= t)
+            ++b;
+        const int64_t kv_len = request_kv_len(kv_indptr, kv_last_page_len, page_size, b);
+        const int64_t qo_len = (int64_t)qo_indptr[b + 1] - qo_indptr[b];
+        const int64_t p = (kv_len - qo_len) + (t - qo_indptr[b]);
+
+        for (int32_t h = 0; h < num_qo_heads; ++h) {
+            const int32_t hk = h / group;
+            const int64_t qoff = (t * num_qo_heads + h) * (int64_t)head_dim;
+
+            /* logits of the visible keys, and their maximum */
+            double m = -INFINITY;
+            for (int64_t j = 0; j < kv_len; ++j) {
+                if (!key_visible(j, p, causal, window_left, key_lo, key_hi))
+                    continue;
+                const int64_t koff = key_offset(kv_indptr, kv_indices, page_size, num_kv_heads,
+                                                head_dim, b, j, hk);
+                double dot = 0.0;
+                for (int32_t d = 0; d < head_dim; ++d)
+                    dot += load_elem(q, in_dtype, qoff + d) * load_elem(k_cache, in_dtype, koff + d);
+                s[j] = sm_scale * dot;
+                if (s[j] > m)
+                    m = s[j];
+            }
+
+            for (int32_t d = 0; d < head_dim; ++d)
+                acc[d] = 0.0;
+            double l = 0.0;
+            if (m != -INFINITY) {
+                for (int64_t j = 0; j < kv_len; ++j) {
+                    if (!key_visible(j, p, causal, window_left, key_lo, key_hi))
+                        continue;
+                    const double w = exp(s[j] - m);
+                    l += w;
+                    const int64_t voff = key_offset(kv_indptr, kv_indices, page_size,
+                                                    num_kv_heads, head_dim, b, j, hk);
+                    for (int32_t d = 0; d < head_dim; ++d)
+                        acc[d] += w * load_elem(v_cache, in_dtype, voff + d);
+                }
+            }
+            double *orow = o + qoff;
+            if (l > 0.0) {
+                for (int32_t d = 0; d < head_dim; ++d)
+                    orow[d] = acc[d] / l;
+                lse[t * num_qo_heads + h] = m + log(l);
+            } else {
+                for (int32_t d = 0; d < head_dim; ++d)
+                    orow[d] = 0.0;
+                lse[t * num_qo_heads + h] = -INFINITY;
+            }
+        }
+    }
+    free(s);
+    free(acc);
+    return 0;
+}
+
+/*
+ * Combine two attention partials over disjoint key sets A and B into the
+ * partial over A u B (the (v_a, s_a, v_b, s_b) -> (v, s) combine that [FIB]
+ * _safe_merge_state dispatches; the per-call LSE it consumes is what [PR234]
+ * "Why each fix" 3 asks the decode path to return).
+ *
+ *  With s_x = ln sum_{j in X} exp(logit_j) and v_x the softmax-weighted mean of
+ *  the values over X:
+ *    s = ln(exp(s_a) + exp(s_b))   evaluated as  M + ln(exp(s_a-M) + exp(s_b-M)),
+ *                                   M = max(s_a, s_b)
+ *    v = exp(s_a - s) * v_a + exp(s_b - s) * v_b
+ *  Two empty partials (s_a = s_b = -inf) give v = 0, s = -inf; one empty
+ *  partial leaves the other unchanged.
+ *
+ *  v_* are [n, H, D] and s_* are [n, H], all double.
+ */
+void oracle_merge_state(int64_t n, int32_t num_heads, int32_t head_dim, const double *v_a,
+                        const double *s_a, const double *v_b, const double *s_b, double *v_out,
+                        double *s_out)
+{
+    for (int64_t i = 0; i < n * num_heads; ++i) {
+        const double a = s_a[i], b = s_b[i];
+        const double M = a > b ? a : b;
+        const double *va = v_a + i * head_dim, *vb = v_b + i * head_dim;
+        double *vo = v_out + i * head_dim;
+        if (M == -INFINITY) {
+            for (int32_t d = 0; d < head_dim; ++d)
+                vo[d] = 0.0;
+            s_out[i] = -INFINITY;
+            continue;
+        }
+        const double s = M + log(exp(a - M) + exp(b - M));
+        const double wa = exp(a - s), wb = exp(b - s);
+        for (int32_t d = 0; d < head_dim; ++d)
+            vo[d] = wa * va[d] + wb * vb[d];
+        s_out[i] = s;
+    }
+}

@@ -1,0 +1,60 @@
+"""Planted mistakes in a copy of the oracle must each fail at least one pin.
+
+Every mutant is a one-line textual edit of ``oracle/oracle.c`` compiled into a
+temporary library; the pins of ``pins.py`` run against it on the CPU.  This
+shows the pins are strong enough to catch a dropped term, a wrong sign or
+index, or a swapped operand anywhere in the oracle.
+"""
+import os
+
+import pytest
+
+import oracle
+from pins import ALL_CHECKS
+
+SRC = os.path.join(os.path.dirname(oracle.__file__), "oracle.c")
+
+MUTANTS = {
+    "window_off_by_one": ("j < p - (int64_t)window_left", "j <= p - (int64_t)window_left"),
+    "window_zero_is_disabled": ("window_left >= 0 && j < p", "window_left > 0 && j < p"),
+    "causal_bound_loose": ("if (causal && j > p)", "if (causal && j > p + 1)"),
+    "top_left_alignment": ("const int64_t p = (kv_len - qo_len) + (t - qo_indptr[b]);",
+                           "const int64_t p = (t - qo_indptr[b]);"),
+    "gqa_modulo_map": ("const int32_t hk = h / group;", "const int32_t hk = h % num_kv_heads;"),
+    "scale_dropped": ("s[j] = sm_scale * dot;", "s[j] = dot;"),
+    "lse_base2": ("lse[t * num_qo_heads + h] = m + log(l);",
+                  "lse[t * num_qo_heads + h] = m + log2(l);"),
+    "max_not_subtracted": ("const double w = exp(s[j] - m);", "const double w = exp(s[j]);"),
+    "slot_index": ("int64_t slot = j % page_size;", "int64_t slot = (j + 1) % page_size;"),
+    "page_index": ("kv_indices[(int64_t)kv_indptr[b] + j / page_size]",
+                   "kv_indices[(int64_t)kv_indptr[b] + j / page_size / 2]"),
+    "last_page_ignored": ("return (npages - 1) * (int64_t)page_size + kv_last_page_len[b];",
+                          "return npages * (int64_t)page_size;"),
+    "values_from_keys": ("acc[d] += w * load_elem(v_cache, in_dtype, voff + d);",
+                         "acc[d] += w * load_elem(k_cache, in_dtype, voff + d);"),
+    "empty_lse_zero": ("lse[t * num_qo_heads + h] = -INFINITY;", "lse[t * num_qo_heads + h] = 0.0;"),
+    "merge_weight_sign": ("const double wa = exp(a - s), wb = exp(b - s);",
+                          "const double wa = exp(s - a), wb = exp(b - s);"),
+    "merge_shift_dropped": ("const double s = M + log(exp(a - M) + exp(b - M));",
+                            "const double s = log(exp(a - M) + exp(b - M));"),
+    "merge_empty_nonzero": ("s_out[i] = -INFINITY;", "s_out[i] = 0.0;"),
+}
+
+
+@pytest.mark.parametrize("name", sorted(MUTANTS))
+def test_pins_catch_mutant(name, tmp_path):
+    old, new = MUTANTS[name]
+    src = open(SRC).read()
+    assert src.count(old) == 1, f"mutation target not found once: {old!r}"
+    mpath = tmp_path / "oracle_mutant.c"
+    mpath.write_text(src.replace(old, new))
+    impl = oracle.OracleLib(oracle.compile_source(str(mpath), str(tmp_path / "libmut.so")))
+    failed = []
+    for check in ALL_CHECKS:
+        try:
+            check(impl)
+        except AssertionError:
+            failed.append(check.__name__)
+        except ValueError:
+            failed.append(check.__name__ + "(error)")
+    assert failed, f"no pin caught mutant {name}"
