@@ -1,0 +1,215 @@
+/*
+ * pkvs.h -- C ABI of libpkvs: batched attention over a paged KV cache with a
+ * sliding-window mask, for AMD Instinct MI355X (gfx950).
+ *
+ * Sources the operations follow (the web pages, cited by title and section):
+ *  [PR31501] sglang PR "[flashinfer] Pass window_left at plan time for the
+ *            SWA paged prefill wrapper" -- section "What": window_left must be
+ *            fixed when the work is planned, the per-element left-window mask
+ *            must always be applied (a per-tile KV-start skip alone leaks), and
+ *            the plan/run consistency check must hold.
+ *  [FIB]     sglang python/sglang/srt/layers/attention/flashinfer_backend.py --
+ *            fast_prefill_plan (plan from host-known CSR layout, no device-to-
+ *            host copy), FlashInferAttnBackend.forward_extend / forward_decode
+ *            (the run calls: sm_scale, window_left, causal, NHD paged cache,
+ *            q viewed as [tokens, heads, head_dim]), _safe_merge_state (the
+ *            (v_a, s_a, v_b, s_b) -> (v, s) combine launched over a (token,
+ *            head) grid), _full_cg_prefill_workspace_bytes (a fixed grid whose
+ *            idle blocks exit early; "increase the workspace" failure at plan),
+ *            should_use_tensor_core (grouped heads share each K/V load).
+ *  [PR234]   AMD-Ecosystem/flashinfer PR "fix(rocm): correct AITER decode
+ *            backend gaps -- sliding window, CUDA graph, return_lse" --
+ *            "Why each fix" 1 (window_left = W: the query at kv_len-1 sees W+1
+ *            keys, W = 0 is one key and never "disabled"), 2 (a launch grid
+ *            sized from per-plan batch scalars breaks replay with a larger
+ *            batch; reject at plan time), 3 (LSE is requested per run call).
+ *
+ * Conventions shared by every entry point
+ *  - Status: 0 (PKVS_OK) or a negative pkvs_status.  Nothing throws across
+ *    the ABI; pkvs_last_error() returns a thread-local detail message.
+ *  - Device pointers are HIP device memory owned by the caller.  The library
+ *    owns only the opaque pkvs_plan (and the pinned host staging buffers it
+ *    holds).  run() calls allocate nothing and are asynchronous on `stream`.
+ *  - Layouts (all row-major, contiguous):
+ *      q, o        [nnz_qo, num_qo_heads, head_dim]   (decode: nnz_qo = batch)
+ *      lse         [nnz_qo, num_qo_heads] float32, natural log of the sum of
+ *                  exp(sm_scale * q.k) over the visible keys; -inf if none
+ *      k_cache, v_cache  [num_pages, page_size, num_kv_heads, head_dim] ("NHD")
+ *      qo_indptr   [batch+1] int32, query tokens of request b are
+ *                  qo_indptr[b] .. qo_indptr[b+1]-1
+ *      kv_indptr   [batch+1] int32, in pages; kv_indices[kv_indptr[b] + i] is
+ *                  the i-th page of request b
+ *      kv_last_page_len [batch] int32 in [1, page_size] (0 for a request with
+ *                  no pages);  kv_len_b = (npages_b - 1) * page_size + last_b
+ *  - Query i of request b sits at position p = kv_len_b - qo_len_b + i (its
+ *    keys are already in the cache).  Key j is visible to it iff
+ *        j <= p (causal)  and  (window_left < 0  or  j >= p - window_left).
+ *    Query head h reads KV head h / (num_qo_heads / num_kv_heads).
+ */
+#ifndef PKVS_H
+#define PKVS_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum pkvs_status {
+    PKVS_OK = 0,
+    PKVS_ERR_INVALID_ARG = -1,   /* malformed argument or layout */
+    PKVS_ERR_UNSUPPORTED = -2,   /* head_dim / page_size / dtype / mode not built */
+    PKVS_ERR_WORKSPACE = -3,     /* a workspace is smaller than pkvs_workspace_size() */
+    PKVS_ERR_CAPACITY = -4,      /* batch / tokens / keys above the plan's capacity */
+    PKVS_ERR_PLAN_MISMATCH = -5, /* run() window_left or causal differs from the plan */
+    PKVS_ERR_HIP = -6,           /* HIP runtime or launch failure */
+    PKVS_ERR_NOT_PLANNED = -7    /* run() before a device plan was made */
+} pkvs_status;
+
+typedef enum pkvs_dtype { PKVS_BF16 = 0, PKVS_FP32 = 1 } pkvs_dtype;
+
+typedef enum pkvs_kind { PKVS_PREFILL = 0, PKVS_DECODE = 1 } pkvs_kind;
+
+/* Fixed properties of a plan.  window_left and causal are fixed here, at plan
+ * time ([PR31501] "What"); run() must pass the same values.
+ *  kind             PKVS_PREFILL or PKVS_DECODE
+ *  num_qo_heads     multiple of num_kv_heads; group = num_qo_heads/num_kv_heads
+ *                   must be a power of two <= 16 (bf16 path)
+ *  head_dim         64, 128 or 256
+ *  page_size        power of two, 1 .. 1024
+ *  dtype            q, k_cache, v_cache and o share it (PKVS_BF16 or PKVS_FP32;
+ *                   accumulation is fp32 either way)
+ *  causal           prefill: 1, or 0 only with window_left = -1; decode: ignored
+ *  window_left      -1 (no window) or W >= 0 (W+1 visible keys, [PR234] 1)
+ *  fixed_split_size decode: keys per KV chunk (a multiple of 32), or -1 to let
+ *                   the planner choose; the partial (o, lse) of the chunks of
+ *                   one request are combined by the merge of pkvs_merge_state
+ *  disable_split_kv decode: 1 = one chunk per request
+ *  batch_capacity   largest batch a plan() call may describe
+ *  qo_capacity      prefill: largest total number of query tokens
+ *  kv_capacity      largest kv_len of one request
+ * The launch grid and the workspaces are sized from these capacities and the
+ * device alone, never from one batch ([PR234] 2; [FIB]
+ * _full_cg_prefill_workspace_bytes). */
+typedef struct pkvs_desc {
+    int32_t kind;
+    int32_t num_qo_heads;
+    int32_t num_kv_heads;
+    int32_t head_dim;
+    int32_t page_size;
+    int32_t dtype;
+    int32_t causal;
+    int32_t window_left;
+    int32_t fixed_split_size;
+    int32_t disable_split_kv;
+    int32_t batch_capacity;
+    int32_t reserved;
+    int64_t qo_capacity;
+    int64_t kv_capacity;
+} pkvs_desc;
+
+/* Read-only facts about a plan (for callers, tests and profilers). */
+typedef struct pkvs_plan_info {
+    int64_t num_items;       /* work items of the last plan() */
+    int64_t num_merges;      /* (request, kv head) pairs whose chunks are merged */
+    int64_t float_ws_bytes;  /* required float workspace (fp32 partials) */
+    int64_t int_ws_bytes;    /* required int workspace (work list) */
+    int32_t grid_blocks;     /* fixed grid of the main kernel */
+    int32_t block_threads;
+    int32_t split_size;      /* decode: keys per chunk chosen by the last plan() */
+    int32_t item_words;      /* int32 words per work item */
+    int32_t query_tile;      /* prefill: query tokens per item */
+    int32_t num_cus;         /* compute units the grid was sized for */
+} pkvs_plan_info;
+
+typedef struct pkvs_plan pkvs_plan;
+
+/* Create a plan object for `desc` on the current HIP device.  Fails with
+ * INVALID_ARG / UNSUPPORTED for a descriptor outside the rules above.  Works
+ * without a GPU (then only dry plans, with null workspaces, can be made). */
+int pkvs_plan_create(pkvs_plan **out, const pkvs_desc *desc);
+
+/* Worst-case workspace sizes for the plan's capacities, in bytes.  Callers
+ * allocate device buffers at least this large (float_ws may be 0 bytes). */
+int pkvs_workspace_size(const pkvs_plan *plan, size_t *float_ws_bytes, size_t *int_ws_bytes);
+
+/* Plan a causal paged prefill (extend with cached prefix) batch.
+ * Host arrays: qo_indptr_h [batch+1], kv_indptr_h [batch+1],
+ * kv_last_page_len_h [batch] (the host-known layout of [FIB]
+ * fast_prefill_plan; no device-to-host copy happens).  Builds the work list
+ * (request, kv head, query tile, first and last key tile after the window
+ * skip) and enqueues one host-to-device copy of it into int_ws on `stream`.
+ * With int_ws == NULL the plan is built on the host only ("dry plan",
+ * inspectable with pkvs_plan_copy_items, not runnable).
+ * Errors: INVALID_ARG (qo_len_b > kv_len_b, last page length outside
+ * [1, page_size], decreasing indptr), CAPACITY, WORKSPACE, HIP. */
+int pkvs_prefill_plan(pkvs_plan *plan, const int32_t *qo_indptr_h, const int32_t *kv_indptr_h,
+                      const int32_t *kv_last_page_len_h, int32_t batch_size, void *float_ws,
+                      size_t float_ws_bytes, void *int_ws, size_t int_ws_bytes,
+                      hipStream_t stream);
+
+/* Run the planned prefill: o (and lse when non-null) for every query token.
+ * k_cache/v_cache hold num_pages pages; kv_indices_d (device, int32) holds
+ * kv_indptr_h[batch] page ids in [0, num_pages).  window_left and causal must
+ * equal the plan's (PLAN_MISMATCH otherwise, [PR31501] "What").  The exact
+ * per-element window mask is always applied. */
+int pkvs_prefill_run(const pkvs_plan *plan, const void *q, const void *k_cache,
+                     const void *v_cache, int64_t num_pages, const int32_t *kv_indices_d,
+                     void *o, float *lse, float sm_scale, int32_t window_left, int32_t causal,
+                     hipStream_t stream);
+
+/* Plan a single-token decode batch (one query per request, at kv_len-1).
+ * The window keeps the last min(kv_len, W+1) keys of each request ([FIB]
+ * FlashInferIndicesUpdaterDecode.update_sliding_window); those keys are cut
+ * into chunks of split_size keys (fixed_split_size or the planner's choice).
+ * A request with kv_len 0 yields o = 0, lse = -inf. */
+int pkvs_decode_plan(pkvs_plan *plan, const int32_t *kv_indptr_h,
+                     const int32_t *kv_last_page_len_h, int32_t batch_size, void *float_ws,
+                     size_t float_ws_bytes, void *int_ws, size_t int_ws_bytes,
+                     hipStream_t stream);
+
+/* Run the planned decode: q, o [batch, num_qo_heads, head_dim], lse
+ * [batch, num_qo_heads] (nullable).  Launches the chunk kernel and, when
+ * some request was split, the merge of its chunk partials.  window_left must
+ * equal the plan's. */
+int pkvs_decode_run(const pkvs_plan *plan, const void *q, const void *k_cache,
+                    const void *v_cache, int64_t num_pages, const int32_t *kv_indices_d,
+                    void *o, float *lse, float sm_scale, int32_t window_left,
+                    hipStream_t stream);
+
+/* Combine two attention partials over disjoint key sets ([FIB]
+ * _safe_merge_state):  s = ln(exp(s_a) + exp(s_b)),
+ * v = exp(s_a - s) * v_a + exp(s_b - s) * v_b;  s_a = s_b = -inf gives v = 0,
+ * s = -inf.  v_* [num_tokens, num_heads, head_dim] in v_dtype, s_*
+ * [num_tokens, num_heads] float32.  The grid runs over (token, head) pairs,
+ * so no head count limits the launch.  v_out/s_out may alias v_a/s_a. */
+int pkvs_merge_state(const void *v_a, const float *s_a, const void *v_b, const float *s_b,
+                     void *v_out, float *s_out, int64_t num_tokens, int32_t num_heads,
+                     int32_t head_dim, int32_t v_dtype, hipStream_t stream);
+
+/* Facts about the plan (counts refer to the last plan() call). */
+int pkvs_plan_get_info(const pkvs_plan *plan, pkvs_plan_info *info);
+
+/* Host copy of the last plan()'s work list: up to max_items items of
+ * info.item_words int32 words each into dst; *n_items receives the count. */
+int pkvs_plan_copy_items(const pkvs_plan *plan, int32_t *dst, int64_t max_items,
+                         int64_t *n_items);
+
+/* Destroy a plan (waits for its pending host-to-device copies).  NULL is a
+ * no-op. */
+void pkvs_plan_destroy(pkvs_plan *plan);
+
+/* Static description of a status code. */
+const char *pkvs_strerror(int code);
+
+/* Detail message of the last error on this thread ("" if none). */
+const char *pkvs_last_error(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* PKVS_H */

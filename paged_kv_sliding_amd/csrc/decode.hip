@@ -1,0 +1,394 @@
+// decode.hip -- single-token paged decode with grouped query heads, bf16,
+// for gfx950.
+//
+// One wavefront owns one work item: (request, kv head, chunk of keys).  The
+// G query heads that share the kv head are packed into the N dimension of
+// 16x16x32 bf16 MFMAs, so each K/V byte is fetched once and serves all G
+// heads (the reason sglang's should_use_tensor_core picks tensor cores for
+// groups of 4 or more: the head group is fused with the token dimension).
+//
+// Per 32-key block:
+//   S^T[16 keys x 16 heads] = K[16 keys x D] . Q^T[D x 16 heads]   (x2)
+//       A operand: lane (row r = lane%16, group g = lane/16) holds 8 dims of
+//       key r, read straight from the paged cache (dims 32s+8g.. at k-step s);
+//       B operand: the same dims of query head r, kept in registers.
+//   O^T[16 dims x 16 heads] += V^T[16 dims x 32 keys] . P^T[32 keys x 16 heads]
+//       B operand: the probabilities exactly where the S^T accumulator left
+//       them -- lane (head r, group g) holds keys 4g..4g+3 of both 16-key
+//       halves, and those 8 keys are its 8 k-slots;
+//       A operand: lane (r, g) loads dims 8r..8r+7 of those same 8 keys (eight
+//       16-byte row loads) and transposes the 8x8 block in registers, which
+//       gives it the A operand of 8 MFMAs at once (tile e holds dims 8r+e).
+// So the kernel needs no LDS and no barrier, reads every K/V row with whole
+// 16-byte loads, and applies the window as an exact per-key predicate.
+//
+// The window (AMD-Ecosystem/flashinfer PR 234, "Why each fix" 1): the query
+// at kv_len-1 sees keys kv_len-1-W .. kv_len-1.  The planner only cuts the key
+// range into chunks (sglang FlashInferIndicesUpdaterDecode.update_sliding_window
+// trims it to the last W+1 keys); keys before the window start or past the
+// chunk end are masked here, element by element.
+//
+// A chunk of a split request writes its fp32 partial (o normalised by its own
+// sum, lse) to a slot of the float workspace; decode_merge combines them.
+#include "device_common.h"
+#include "pkvs_internal.h"
+
+namespace pkvs {
+
+namespace {
+
+template <int D>
+struct DecodeBuf {
+    static constexpr int KS = D / 32;            // QK k-steps (32 dims each)
+    static constexpr int NV = D >= 128 ? D / 128 : 1;
+    bf16x8 k0[KS], k1[KS];                       // keys blk+r, blk+16+r
+    bf16x8 v[NV][8];                             // 8 keys x 8 dims per 128-dim chunk
+};
+
+// Page ids of a request, 64 pages at a time: lane L holds the id of page
+// base + L (cur) and of page base + 64 + L (nxt, prefetched a window ahead).
+// Windows start at a multiple of 32 keys and span 64 * page_size keys, so a
+// 32-key block never straddles two windows.  Ids are fetched from the
+// window with a cross-lane read, which keeps the dependent index loads off
+// the critical path of the K/V stream.
+struct PageWindow {
+    int base, last_pg, page_base;
+    int cur, nxt;
+};
+
+__device__ __forceinline__ int load_page_id(const DecodeArgs &a, const PageWindow &pw, int pg)
+{
+    return pg <= pw.last_pg ? a.kv_indices[pw.page_base + pg] : 0;
+}
+
+__device__ __forceinline__ void window_advance(const DecodeArgs &a, PageWindow &pw, int blk,
+                                               int lane)
+{
+    if ((blk >> a.log2_page) - pw.base >= 64) {
+        pw.base += 64;
+        pw.cur = pw.nxt;
+        pw.nxt = load_page_id(a, pw, pw.base + 64 + lane);
+    }
+}
+
+__device__ __forceinline__ int64_t window_page(const DecodeArgs &a, const PageWindow &pw, int tok)
+{
+    int64_t pg = __shfl(pw.cur, (tok >> a.log2_page) - pw.base);
+    pg = pg < 0 ? 0 : pg;
+    return pg >= a.num_pages ? a.num_pages - 1 : pg;
+}
+
+template <int D>
+__device__ __forceinline__ void decode_load(DecodeBuf<D> &buf, const DecodeArgs &a,
+                                            PageWindow &pw, int blk, int t1, int hk, int lane)
+{
+    constexpr int KS = DecodeBuf<D>::KS, NV = DecodeBuf<D>::NV;
+    const int r = lane & 15, g = lane >> 4;
+    const int P = a.page_size;
+    const uint16_t *K = static_cast<const uint16_t *>(a.k);
+    const uint16_t *V = static_cast<const uint16_t *>(a.v);
+    const int last = t1 - 1;
+    window_advance(a, pw, blk, lane);
+
+    // key rows for the A operand of S^T
+    const int tk0 = min(blk + r, last), tk1 = min(blk + 16 + r, last);
+    const int64_t rk0 =
+        nhd_offset(window_page(a, pw, tk0), tk0 & (P - 1), P, hk, a.num_kv_heads, D);
+    const int64_t rk1 =
+        nhd_offset(window_page(a, pw, tk1), tk1 & (P - 1), P, hk, a.num_kv_heads, D);
+#pragma unroll
+    for (int s = 0; s < KS; ++s) {
+        buf.k0[s] = load_bf16x8(K + rk0 + 32 * s + 8 * g);
+        buf.k1[s] = load_bf16x8(K + rk1 + 32 * s + 8 * g);
+    }
+
+    // value rows: keys blk+4g+i and blk+16+4g+i (i = 0..3), dims 8r..8r+7
+    int64_t rv[8];
+    if (P >= 4) {
+        // four consecutive keys starting at a multiple of 4 share a page
+        const int64_t pa = window_page(a, pw, min(blk + 4 * g, last));
+        const int64_t pb = window_page(a, pw, min(blk + 16 + 4 * g, last));
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const int sa = min(blk + 4 * g + i, last), sb = min(blk + 16 + 4 * g + i, last);
+            rv[i] = nhd_offset(pa, sa & (P - 1), P, hk, a.num_kv_heads, D);
+            rv[4 + i] = nhd_offset(pb, sb & (P - 1), P, hk, a.num_kv_heads, D);
+        }
+    } else {
+#pragma unroll
+        for (int j = 0; j < 8; ++j) {
+            const int t = min(blk + (j < 4 ? 4 * g + j : 16 + 4 * g + j - 4), last);
+            rv[j] = nhd_offset(window_page(a, pw, t), t & (P - 1), P, hk, a.num_kv_heads, D);
+        }
+    }
+#pragma unroll
+    for (int u = 0; u < NV; ++u)
+#pragma unroll
+        for (int j = 0; j < 8; ++j)
+            buf.v[u][j] = (8 * r + 128 * u < D) ? load_bf16x8(V + rv[j] + 128 * u + 8 * r)
+                                                : zero_bf16x8();
+}
+
+template <int D>
+struct DecodeState {
+    static constexpr int NV = DecodeBuf<D>::NV;
+    float m, l;
+    f32x4 o[NV][8];
+};
+
+template <int D>
+__device__ __forceinline__ void decode_compute(const DecodeBuf<D> &buf, DecodeState<D> &st,
+                                               const bf16x8 (&qf)[D / 32], int blk, int lo,
+                                               int t1, float scale_log2, int lane)
+{
+    constexpr int KS = DecodeBuf<D>::KS, NV = DecodeBuf<D>::NV;
+    const int g = lane >> 4;
+    f32x4 s0 = {0.f, 0.f, 0.f, 0.f}, s1 = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int s = 0; s < KS; ++s) {
+        s0 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(buf.k0[s], qf[s], s0, 0, 0, 0);
+        s1 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(buf.k1[s], qf[s], s1, 0, 0, 0);
+    }
+    // lane holds keys blk+4g+i (s0[i]) and blk+16+4g+i (s1[i]) of head lane%16
+    float x[8];
+    float mx = kNegInf;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        const int ta = blk + 4 * g + i, tb = blk + 16 + 4 * g + i;
+        x[i] = (ta >= lo && ta < t1) ? s0[i] * scale_log2 : kNegInf;
+        x[4 + i] = (tb >= lo && tb < t1) ? s1[i] * scale_log2 : kNegInf;
+        mx = fmaxf(mx, fmaxf(x[i], x[4 + i]));
+    }
+    mx = fmaxf(mx, __shfl_xor(mx, 16));
+    mx = fmaxf(mx, __shfl_xor(mx, 32));
+    const float m_new = fmaxf(st.m, mx);
+    const float m_use = m_new == kNegInf ? 0.f : m_new;
+    const float alpha = fast_exp2(st.m - m_use);
+    float p[8], rs = 0.f;
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+        p[j] = fast_exp2(x[j] - m_use);
+        rs += p[j];
+    }
+    st.l = st.l * alpha + rs;
+    st.m = m_new;
+    f32x8 pv = {p[0], p[1], p[2], p[3], p[4], p[5], p[6], p[7]};
+    const bf16x8 pb = __builtin_convertvector(pv, bf16x8);
+#pragma unroll
+    for (int u = 0; u < NV; ++u) {
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+            bf16x8 va;
+#pragma unroll
+            for (int j = 0; j < 8; ++j) va[j] = buf.v[u][j][e];
+            st.o[u][e] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(va, pb, st.o[u][e] * alpha, 0,
+                                                                 0, 0);
+        }
+    }
+}
+
+template <int D>
+__global__ __launch_bounds__(kDecodeThreads) void decode_bf16_kernel(DecodeArgs a)
+{
+    constexpr int KS = D / 32, NV = DecodeBuf<D>::NV;
+    const int lane = threadIdx.x;
+    const int r = lane & 15, g = lane >> 4;
+    const int G = 1 << a.log2_group;
+    const int n_items = a.ws[kHdrNumItems];
+    const uint16_t *Q = static_cast<const uint16_t *>(a.q);
+
+    for (int it = blockIdx.x; it < n_items; it += gridDim.x) {
+        const int32_t *w = a.ws + kHeaderWords + int64_t(it) * kDecodeItemWords;
+        const int b = w[kDiRequest], hk = w[kDiKvHead];
+        const int t0 = w[kDiTokBegin], t1 = w[kDiTokEnd], lo = w[kDiVisLo];
+        const int page_base = w[kDiPageBase], slot = w[kDiSlot];
+        (void)r;
+
+        // Q^T operand: head r of the group, dims 32s+8g..+8 (zero for padding heads)
+        bf16x8 qf[KS];
+        const int64_t qrow = (int64_t(b) * a.num_qo_heads + hk * G + r) * D;
+#pragma unroll
+        for (int s = 0; s < KS; ++s)
+            qf[s] = r < G ? load_bf16x8(Q + qrow + 32 * s + 8 * g) : zero_bf16x8();
+
+        DecodeState<D> st;
+        st.m = kNegInf;
+        st.l = 0.f;
+#pragma unroll
+        for (int u = 0; u < NV; ++u)
+#pragma unroll
+            for (int e = 0; e < 8; ++e) st.o[u][e] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+        if (t0 < t1) {
+            PageWindow pw;
+            pw.page_base = page_base;
+            pw.base = t0 >> a.log2_page;
+            pw.last_pg = (t1 - 1) >> a.log2_page;
+            pw.cur = load_page_id(a, pw, pw.base + lane);
+            pw.nxt = load_page_id(a, pw, pw.base + 64 + lane);
+            DecodeBuf<D> A, B;
+            decode_load<D>(A, a, pw, t0, t1, hk, lane);
+            int blk = t0;
+            for (;;) {
+                if (blk + kDecodeBlock < t1) {
+                    decode_load<D>(B, a, pw, blk + kDecodeBlock, t1, hk, lane);
+                    decode_compute<D>(A, st, qf, blk, lo, t1, a.scale_log2, lane);
+                } else {
+                    decode_compute<D>(A, st, qf, blk, lo, t1, a.scale_log2, lane);
+                    break;
+                }
+                blk += kDecodeBlock;
+                if (blk + kDecodeBlock < t1) {
+                    decode_load<D>(A, a, pw, blk + kDecodeBlock, t1, hk, lane);
+                    decode_compute<D>(B, st, qf, blk, lo, t1, a.scale_log2, lane);
+                } else {
+                    decode_compute<D>(B, st, qf, blk, lo, t1, a.scale_log2, lane);
+                    break;
+                }
+                blk += kDecodeBlock;
+            }
+        }
+
+        // the four lane groups hold disjoint keys of the same head: sum them
+        float l = st.l;
+        l += __shfl_xor(l, 16);
+        l += __shfl_xor(l, 32);
+        const float inv = l > 0.f ? 1.f / l : 0.f;
+        const float lse = l > 0.f ? (st.m + fast_log2(l)) * kLn2 : kNegInf;
+        if (r < G) {
+            // O^T accumulator: lane (head r, group g) holds dims 128u+32g+8i+e
+            const int h = hk * G + r;
+            if (slot < 0) {
+                uint16_t *O = static_cast<uint16_t *>(a.o);
+                const int64_t orow = (int64_t(b) * a.num_qo_heads + h) * D;
+#pragma unroll
+                for (int u = 0; u < NV; ++u)
+#pragma unroll
+                    for (int i = 0; i < 4; ++i) {
+                        const int d0 = 128 * u + 32 * g + 8 * i;
+                        if (d0 < D) {
+                            f32x8 ov;
+#pragma unroll
+                            for (int e = 0; e < 8; ++e) ov[e] = st.o[u][e][i] * inv;
+                            *reinterpret_cast<bf16x8 *>(O + orow + d0) =
+                                __builtin_convertvector(ov, bf16x8);
+                        }
+                    }
+                if (a.lse && g == 0) a.lse[int64_t(b) * a.num_qo_heads + h] = lse;
+            } else {
+                float *PO = a.part_o + (int64_t(slot) * G + r) * D;
+#pragma unroll
+                for (int u = 0; u < NV; ++u)
+#pragma unroll
+                    for (int i = 0; i < 4; ++i) {
+                        const int d0 = 128 * u + 32 * g + 8 * i;
+                        if (d0 < D) {
+                            f32x4 lo4, hi4;
+#pragma unroll
+                            for (int e = 0; e < 4; ++e) {
+                                lo4[e] = st.o[u][e][i] * inv;
+                                hi4[e] = st.o[u][e + 4][i] * inv;
+                            }
+                            *reinterpret_cast<f32x4 *>(PO + d0) = lo4;
+                            *reinterpret_cast<f32x4 *>(PO + d0 + 4) = hi4;
+                        }
+                    }
+                if (g == 0) a.part_lse[int64_t(slot) * G + r] = lse;
+            }
+        }
+    }
+}
+
+// Combine the chunk partials of every split (request, kv head): one wave per
+// (merge entry, query head of the group); the LSE-weighted sum of
+// pkvs_merge_state, folded over all chunks at once.
+template <int D>
+__global__ __launch_bounds__(kMergeThreads) void decode_merge_kernel(DecodeArgs a)
+{
+    constexpr int E = D / 64;  // elements per lane
+    const int lane = threadIdx.x;
+    const int G = 1 << a.log2_group;
+    const int n_merges = a.ws[kHdrNumMerges];
+    const int32_t *merges = a.ws + a.ws[kHdrMergeOffset];
+    const int units = n_merges << a.log2_group;
+    for (int u = blockIdx.x; u < units; u += gridDim.x) {
+        const int32_t *me = merges + (u >> a.log2_group) * kMergeWords;
+        const int h = u & (G - 1);
+        const int b = me[kMeRequest], hk = me[kMeKvHead], first = me[kMeFirstSlot],
+                  n = me[kMeNumSlots];
+        float M = kNegInf;
+        for (int k = 0; k < n; ++k) M = fmaxf(M, a.part_lse[int64_t(first + k) * G + h]);
+        float acc[E] = {};
+        float sum = 0.f;
+        if (M != kNegInf) {
+            for (int k = 0; k < n; ++k) {
+                const int64_t sl = int64_t(first + k) * G + h;
+                const float wk = fast_exp2((a.part_lse[sl] - M) * 1.44269504088896340736f);
+                sum += wk;
+                const float *po = a.part_o + sl * D;
+#pragma unroll
+                for (int e = 0; e < E; ++e) acc[e] += wk * po[lane + 64 * e];
+            }
+        }
+        const float inv = sum > 0.f ? 1.f / sum : 0.f;
+        uint16_t *O = static_cast<uint16_t *>(a.o);
+        const int64_t orow = (int64_t(b) * a.num_qo_heads + hk * G + h) * D;
+#pragma unroll
+        for (int e = 0; e < E; ++e) {
+            const __bf16 ob = __bf16(acc[e] * inv);
+            O[orow + lane + 64 * e] = __builtin_bit_cast(uint16_t, ob);
+        }
+        if (a.lse && lane == 0)
+            a.lse[int64_t(b) * a.num_qo_heads + hk * G + h] =
+                sum > 0.f ? M + fast_log2(sum) * kLn2 : kNegInf;
+    }
+}
+
+}  // namespace
+
+hipError_t launch_decode_bf16(const DecodeArgs &a, int head_dim, int grid, hipStream_t s)
+{
+    switch (head_dim) {
+    case 64: decode_bf16_kernel<64><<<grid, kDecodeThreads, 0, s>>>(a); break;
+    case 128: decode_bf16_kernel<128><<<grid, kDecodeThreads, 0, s>>>(a); break;
+    case 256: decode_bf16_kernel<256><<<grid, kDecodeThreads, 0, s>>>(a); break;
+    default: return hipErrorInvalidValue;
+    }
+    return hipGetLastError();
+}
+
+hipError_t launch_decode_merge(const DecodeArgs &a, int head_dim, int dtype, int grid,
+                               hipStream_t s)
+{
+    (void)dtype;
+    switch (head_dim) {
+    case 64: decode_merge_kernel<64><<<grid, kMergeThreads, 0, s>>>(a); break;
+    case 128: decode_merge_kernel<128><<<grid, kMergeThreads, 0, s>>>(a); break;
+    case 256: decode_merge_kernel<256><<<grid, kMergeThreads, 0, s>>>(a); break;
+    default: return hipErrorInvalidValue;
+    }
+    return hipGetLastError();
+}
+
+int decode_bf16_blocks_per_cu(int head_dim)
+{
+    int n = 0;
+    hipError_t e = hipErrorInvalidValue;
+    switch (head_dim) {
+    case 64:
+        e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, decode_bf16_kernel<64>,
+                                                         kDecodeThreads, 0);
+        break;
+    case 128:
+        e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, decode_bf16_kernel<128>,
+                                                         kDecodeThreads, 0);
+        break;
+    case 256:
+        e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, decode_bf16_kernel<256>,
+                                                         kDecodeThreads, 0);
+        break;
+    }
+    return e == hipSuccess ? n : 0;
+}
+
+}  // namespace pkvs

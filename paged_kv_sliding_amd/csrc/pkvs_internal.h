@@ -1,0 +1,103 @@
+// pkvs_internal.h -- work-list formats and tile constants shared by the
+// host planner (plan.cpp) and the gfx950 kernels (*.hip) of libpkvs.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "../../include/pkvs.h"
+
+namespace pkvs {
+
+// ---------------------------------------------------------------- work list
+// The int workspace holds a 64-byte header followed by the items, then the
+// merge entries.  Kernels read the counts from the header at run time, so the
+// launch grid never depends on one batch.
+constexpr int kHeaderWords = 16;
+enum HeaderField {
+    kHdrNumItems = 0,
+    kHdrNumMerges = 1,
+    kHdrMergeOffset = 2,  // in int32 words from the start of the workspace
+    kHdrItemWords = 3,
+};
+
+// Prefill item: one (request, kv head, query tile).
+constexpr int kPrefillItemWords = 8;
+enum PrefillItem {
+    kPiRequest = 0,
+    kPiKvHead = 1,
+    kPiQBegin = 2,   // global index of the tile's first query token
+    kPiQCount = 3,   // query tokens in the tile
+    kPiPos0 = 4,     // sequence position of the first query (prefix + offset)
+    kPiKvLen = 5,
+    kPiPageBase = 6, // kv_indptr[request]
+    kPiKvBegin = 7,  // first key processed (window start rounded down to a key tile)
+};
+
+// Decode item: one (request, kv head, key chunk).
+constexpr int kDecodeItemWords = 8;
+enum DecodeItem {
+    kDiRequest = 0,
+    kDiKvHead = 1,
+    kDiTokBegin = 2, // first key of the chunk (multiple of kDecodeBlock)
+    kDiTokEnd = 3,   // one past the last key of the chunk
+    kDiVisLo = 4,    // first visible key in the chunk (window start)
+    kDiPageBase = 5,
+    kDiSlot = 6,     // -1: write o/lse directly; else partial slot index
+    kDiKvLen = 7,
+};
+
+// Merge entry: the chunks of one (request, kv head) to combine.
+constexpr int kMergeWords = 4;
+enum MergeEntry { kMeRequest = 0, kMeKvHead = 1, kMeFirstSlot = 2, kMeNumSlots = 3 };
+
+// ---------------------------------------------------------------- tiles
+constexpr int kPrefillRows = 128;      // (query token, head) rows per workgroup
+constexpr int kPrefillThreads = 256;   // 4 waves x 32 rows
+constexpr int kPrefillKvTile = 32;     // keys per step
+constexpr int kGenericQTile = 16;      // fp32 path: query tokens per item
+constexpr int kGenericThreads = 256;
+constexpr int kDecodeBlock = 32;       // keys per decode step
+constexpr int kDecodeThreads = 64;     // one wave per workgroup
+constexpr int kMergeThreads = 64;
+
+struct PrefillArgs {
+    const void *q, *k, *v;
+    const int32_t *kv_indices;
+    void *o;
+    float *lse;
+    const int32_t *ws;  // int workspace (header + items)
+    int64_t num_pages;
+    float scale_log2;   // sm_scale * log2(e)
+    int32_t num_qo_heads, num_kv_heads, log2_group, page_size, log2_page;
+    int32_t window_left, causal;
+};
+
+struct DecodeArgs {
+    const void *q, *k, *v;
+    const int32_t *kv_indices;
+    void *o;
+    float *lse;
+    const int32_t *ws;
+    float *part_o;    // [slots, group, head_dim]
+    float *part_lse;  // [slots, group]
+    int64_t num_pages;
+    float scale_log2;
+    int32_t num_qo_heads, num_kv_heads, log2_group, page_size, log2_page;
+};
+
+// Launchers (return hipError_t of the launch).
+hipError_t launch_prefill_bf16(const PrefillArgs &a, int head_dim, int grid, hipStream_t s);
+hipError_t launch_attention_fp32(const PrefillArgs &a, int head_dim, int grid, hipStream_t s);
+hipError_t launch_decode_bf16(const DecodeArgs &a, int head_dim, int grid, hipStream_t s);
+hipError_t launch_decode_merge(const DecodeArgs &a, int head_dim, int dtype, int grid,
+                               hipStream_t s);
+hipError_t launch_merge_state(const void *va, const float *sa, const void *vb, const float *sb,
+                              void *vo, float *so, int64_t n, int32_t heads, int32_t head_dim,
+                              int32_t dtype, int grid, hipStream_t s);
+
+// Resident workgroups per CU of each kernel (occupancy query; 0 if unknown).
+int prefill_bf16_blocks_per_cu(int head_dim);
+int decode_bf16_blocks_per_cu(int head_dim);
+
+}  // namespace pkvs

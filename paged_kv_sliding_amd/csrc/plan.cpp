@@ -1,0 +1,541 @@
+// plan.cpp -- host side of libpkvs: plan objects, work-list construction,
+// workspace sizing, error reporting.
+//
+// The planner follows the statement of the problem on the pages:
+//  * window_left (and causal) are fixed at plan time, and run() must repeat
+//    them (sglang PR "Pass window_left at plan time for the SWA paged prefill
+//    wrapper", section "What");
+//  * the plan is built from host-known CSR arrays, with no device-to-host copy
+//    (sglang flashinfer_backend.py, fast_prefill_plan);
+//  * decode keeps only the last min(kv_len, W+1) keys of a request
+//    (FlashInferIndicesUpdaterDecode.update_sliding_window), and long key
+//    ranges are cut into fixed-size chunks whose partial results are merged
+//    (fixed_split_size of the deterministic-inference settings);
+//  * a prefill query tile starts reading keys at the tile that holds the
+//    window start of its first query (the per-tile KV-start skip); the exact
+//    mask is still applied per element by the kernels;
+//  * the grid and workspaces are sized from capacities and the device only,
+//    and a batch beyond the capacity is rejected, never under-launched
+//    (AMD-Ecosystem/flashinfer PR 234, "Why each fix" 2).
+#include <hip/hip_runtime.h>
+
+#include <algorithm>
+#include <cstdarg>
+#include <cstdio>
+#include <cstring>
+#include <numeric>
+#include <string>
+#include <vector>
+
+#include "pkvs_internal.h"
+#include "plan_state.h"
+
+namespace pkvs {
+
+static thread_local std::string g_last_error;
+
+int fail(int code, const char *fmt, ...)
+{
+    char buf[512];
+    va_list ap;
+    va_start(ap, fmt);
+    vsnprintf(buf, sizeof buf, fmt, ap);
+    va_end(ap);
+    g_last_error = buf;
+    return code;
+}
+
+void clear_error() { g_last_error.clear(); }
+
+static bool is_pow2(int64_t x) { return x > 0 && (x & (x - 1)) == 0; }
+
+static int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
+
+// Capacity-derived sizes; depend on the descriptor and the device only.
+static void size_plan(Plan *p)
+{
+    const pkvs_desc &d = p->desc;
+    const int64_t B = d.batch_capacity;
+    const int64_t hkv = d.num_kv_heads;
+    const int64_t group = d.num_qo_heads / d.num_kv_heads;
+    int64_t items = 0, slots = 0, merges = 0;
+    if (d.kind == PKVS_PREFILL) {
+        items = hkv * (ceil_div(d.qo_capacity, p->query_tile) + B);
+    } else {
+        // keys a request can present after the window trim, plus the
+        // alignment of the first chunk to a key block
+        int64_t nmax = d.kv_capacity;
+        if (d.window_left >= 0) nmax = std::min<int64_t>(nmax, int64_t(d.window_left) + 1);
+        nmax += kDecodeBlock - 1;
+        int64_t per_req;
+        if (d.disable_split_kv || d.dtype == PKVS_FP32) {
+            per_req = 1;
+        } else if (d.fixed_split_size > 0) {
+            per_req = std::max<int64_t>(1, ceil_div(nmax, d.fixed_split_size));
+        } else {
+            // automatic chunking never makes more than B + target/hkv chunks
+            // per head in total (see choose_split); bound per request by the
+            // smallest automatic chunk
+            per_req = std::max<int64_t>(1, ceil_div(nmax, kMinAutoSplit));
+        }
+        items = B * hkv * per_req;
+        if (d.fixed_split_size <= 0 && !d.disable_split_kv && d.dtype != PKVS_FP32)
+            items = std::min<int64_t>(items, B * hkv * 2 + int64_t(p->auto_target_items) + hkv);
+        items = std::max<int64_t>(items, B * hkv);
+        slots = (per_req > 1) ? items : 0;
+        merges = (per_req > 1) ? B * hkv : 0;
+    }
+    p->items_cap = items;
+    p->slots_cap = slots;
+    p->merges_cap = merges;
+    p->int_ws_need = sizeof(int32_t) * size_t(kHeaderWords + items * p->item_words +
+                                              merges * kMergeWords);
+    p->float_ws_need = sizeof(float) * size_t(slots * group * (d.head_dim + 1));
+}
+
+static int validate_desc(const pkvs_desc *d)
+{
+    if (!d) return fail(PKVS_ERR_INVALID_ARG, "desc is null");
+    if (d->kind != PKVS_PREFILL && d->kind != PKVS_DECODE)
+        return fail(PKVS_ERR_INVALID_ARG, "kind must be PKVS_PREFILL or PKVS_DECODE");
+    if (d->num_qo_heads <= 0 || d->num_kv_heads <= 0 || d->num_qo_heads % d->num_kv_heads)
+        return fail(PKVS_ERR_INVALID_ARG, "num_qo_heads (%d) must be a positive multiple of "
+                    "num_kv_heads (%d)", d->num_qo_heads, d->num_kv_heads);
+    const int group = d->num_qo_heads / d->num_kv_heads;
+    if (d->head_dim != 64 && d->head_dim != 128 && d->head_dim != 256)
+        return fail(PKVS_ERR_UNSUPPORTED, "head_dim %d not built (64, 128, 256)", d->head_dim);
+    if (!is_pow2(d->page_size) || d->page_size > 1024)
+        return fail(PKVS_ERR_UNSUPPORTED, "page_size %d must be a power of two <= 1024",
+                    d->page_size);
+    if (d->dtype != PKVS_BF16 && d->dtype != PKVS_FP32)
+        return fail(PKVS_ERR_UNSUPPORTED, "dtype %d not built (bf16, fp32)", d->dtype);
+    if (d->dtype == PKVS_BF16 && (!is_pow2(group) || group > 16))
+        return fail(PKVS_ERR_UNSUPPORTED, "bf16 path needs a power-of-two group <= 16, got %d",
+                    group);
+    if (d->window_left < -1)
+        return fail(PKVS_ERR_INVALID_ARG, "window_left %d: must be -1 (off) or >= 0",
+                    d->window_left);
+    if (d->kind == PKVS_PREFILL && d->causal != 1 && !(d->causal == 0 && d->window_left == -1))
+        return fail(PKVS_ERR_UNSUPPORTED, "non-causal prefill is built only without a window");
+    if (d->fixed_split_size != -1 && (d->fixed_split_size <= 0 ||
+                                      d->fixed_split_size % kDecodeBlock))
+        return fail(PKVS_ERR_INVALID_ARG, "fixed_split_size %d must be -1 or a positive "
+                    "multiple of %d", d->fixed_split_size, kDecodeBlock);
+    if (d->batch_capacity <= 0 || d->kv_capacity <= 0 ||
+        (d->kind == PKVS_PREFILL && d->qo_capacity <= 0))
+        return fail(PKVS_ERR_INVALID_ARG, "capacities must be positive");
+    if (d->kv_capacity > (int64_t(1) << 30) || d->qo_capacity > (int64_t(1) << 30))
+        return fail(PKVS_ERR_UNSUPPORTED, "capacities above 2^30 tokens are not supported");
+    return PKVS_OK;
+}
+
+// Host view of one request's layout, validated.
+struct Req {
+    int64_t qo_begin, qo_len, kv_len, page_base;
+};
+
+static int read_layout(const Plan *p, const int32_t *qo_indptr, const int32_t *kv_indptr,
+                       const int32_t *last, int32_t batch, std::vector<Req> &out)
+{
+    const pkvs_desc &d = p->desc;
+    if (batch < 0) return fail(PKVS_ERR_INVALID_ARG, "batch_size %d < 0", batch);
+    if (batch > d.batch_capacity)
+        return fail(PKVS_ERR_CAPACITY, "batch_size %d exceeds batch_capacity %d", batch,
+                    d.batch_capacity);
+    if (!kv_indptr || (batch > 0 && !last) || (d.kind == PKVS_PREFILL && !qo_indptr))
+        return fail(PKVS_ERR_INVALID_ARG, "null layout array");
+    if (kv_indptr[0] != 0 || (qo_indptr && qo_indptr[0] != 0))
+        return fail(PKVS_ERR_INVALID_ARG, "indptr arrays must start at 0");
+    out.resize(batch);
+    int64_t total_q = 0;
+    for (int32_t b = 0; b < batch; ++b) {
+        const int64_t np = int64_t(kv_indptr[b + 1]) - kv_indptr[b];
+        if (np < 0) return fail(PKVS_ERR_INVALID_ARG, "kv_indptr decreases at request %d", b);
+        int64_t kv_len = 0;
+        if (np > 0) {
+            if (last[b] < 1 || last[b] > d.page_size)
+                return fail(PKVS_ERR_INVALID_ARG, "kv_last_page_len[%d] = %d outside [1, %d]", b,
+                            last[b], d.page_size);
+            kv_len = (np - 1) * d.page_size + last[b];
+        }
+        int64_t qo_len = 1, qo_begin = b;
+        if (d.kind == PKVS_PREFILL) {
+            qo_begin = qo_indptr[b];
+            qo_len = int64_t(qo_indptr[b + 1]) - qo_indptr[b];
+            if (qo_len < 0) return fail(PKVS_ERR_INVALID_ARG, "qo_indptr decreases at %d", b);
+            if (qo_len > kv_len)
+                return fail(PKVS_ERR_INVALID_ARG, "request %d: qo_len %lld > kv_len %lld", b,
+                            (long long)qo_len, (long long)kv_len);
+        }
+        if (kv_len > d.kv_capacity)
+            return fail(PKVS_ERR_CAPACITY, "request %d: kv_len %lld exceeds kv_capacity %lld", b,
+                        (long long)kv_len, (long long)d.kv_capacity);
+        total_q += (d.kind == PKVS_PREFILL) ? qo_len : 0;
+        out[b] = Req{qo_begin, qo_len, kv_len, kv_indptr[b]};
+    }
+    if (d.kind == PKVS_PREFILL && total_q > d.qo_capacity)
+        return fail(PKVS_ERR_CAPACITY, "total query tokens %lld exceed qo_capacity %lld",
+                    (long long)total_q, (long long)d.qo_capacity);
+    return PKVS_OK;
+}
+
+// Prefill work list: (request, kv head, query tile).  The first key tile of an
+// item is the one holding the window start of its first query; the last is
+// the one holding its last query's position (causal).  Items are ordered by
+// decreasing key count so a strided persistent grid receives a balanced mix;
+// within one cost the kv head runs fastest.
+static void build_prefill(Plan *p, const std::vector<Req> &reqs)
+{
+    const pkvs_desc &d = p->desc;
+    const int tq = p->query_tile;
+    struct It { int64_t cost; int32_t w[kPrefillItemWords]; };
+    std::vector<It> items;
+    for (size_t b = 0; b < reqs.size(); ++b) {
+        const Req &r = reqs[b];
+        const int64_t prefix = r.kv_len - r.qo_len;
+        for (int64_t t0 = 0; t0 < r.qo_len; t0 += tq) {
+            const int64_t qn = std::min<int64_t>(tq, r.qo_len - t0);
+            const int64_t pos0 = prefix + t0;
+            int64_t kv_begin = 0;
+            if (d.window_left >= 0) kv_begin = std::max<int64_t>(0, pos0 - d.window_left);
+            kv_begin = kv_begin / kPrefillKvTile * kPrefillKvTile;
+            const int64_t kv_end = d.causal ? std::min<int64_t>(r.kv_len, pos0 + qn) : r.kv_len;
+            for (int32_t hk = 0; hk < d.num_kv_heads; ++hk) {
+                It it;
+                it.cost = kv_end - kv_begin;
+                it.w[kPiRequest] = int32_t(b);
+                it.w[kPiKvHead] = hk;
+                it.w[kPiQBegin] = int32_t(r.qo_begin + t0);
+                it.w[kPiQCount] = int32_t(qn);
+                it.w[kPiPos0] = int32_t(pos0);
+                it.w[kPiKvLen] = int32_t(r.kv_len);
+                it.w[kPiPageBase] = int32_t(r.page_base);
+                it.w[kPiKvBegin] = int32_t(kv_begin);
+                items.push_back(it);
+            }
+        }
+    }
+    std::stable_sort(items.begin(), items.end(),
+                     [](const It &a, const It &b) { return a.cost > b.cost; });
+    p->n_items = int64_t(items.size());
+    p->n_merges = 0;
+    p->split_size = 0;
+    p->host_ws.assign(kHeaderWords + items.size() * kPrefillItemWords, 0);
+    int32_t *w = p->host_ws.data();
+    w[kHdrNumItems] = int32_t(items.size());
+    w[kHdrNumMerges] = 0;
+    w[kHdrMergeOffset] = int32_t(p->host_ws.size());
+    w[kHdrItemWords] = kPrefillItemWords;
+    for (size_t i = 0; i < items.size(); ++i)
+        std::memcpy(w + kHeaderWords + i * kPrefillItemWords, items[i].w, sizeof items[i].w);
+}
+
+// Keys per decode chunk when the caller leaves it to the planner: aim for
+// about auto_target_items chunks over the whole batch so every wave slot of
+// the fixed grid gets work, but never cut below kMinAutoSplit keys.
+static int64_t choose_split(const Plan *p, const std::vector<Req> &reqs)
+{
+    const pkvs_desc &d = p->desc;
+    int64_t longest = kDecodeBlock, total = 0;
+    for (const Req &r : reqs) {
+        int64_t ws = d.window_left >= 0 ? std::max<int64_t>(0, r.kv_len - 1 - d.window_left) : 0;
+        int64_t n = r.kv_len - ws / kDecodeBlock * kDecodeBlock;
+        longest = std::max(longest, n);
+        total += n;
+    }
+    const int64_t no_split = ceil_div(longest, kDecodeBlock) * kDecodeBlock;
+    if (d.disable_split_kv || d.dtype == PKVS_FP32) return no_split;
+    if (d.fixed_split_size > 0) return d.fixed_split_size;
+    const int64_t units = int64_t(reqs.size()) * d.num_kv_heads;
+    const int64_t target = p->auto_target_items;
+    if (units >= target) return no_split;
+    int64_t c = ceil_div(total * d.num_kv_heads, target);
+    c = ceil_div(c, kDecodeBlock) * kDecodeBlock;
+    return std::min(no_split, std::max<int64_t>(c, kMinAutoSplit));
+}
+
+static int build_decode(Plan *p, const std::vector<Req> &reqs)
+{
+    const pkvs_desc &d = p->desc;
+    const int64_t c = choose_split(p, reqs);
+    struct It { int64_t cost; int32_t w[kDecodeItemWords]; };
+    std::vector<It> items;
+    std::vector<int32_t> merges;
+    int64_t slot = 0;
+    for (size_t b = 0; b < reqs.size(); ++b) {
+        const Req &r = reqs[b];
+        const int64_t ws =
+            d.window_left >= 0 ? std::max<int64_t>(0, r.kv_len - 1 - d.window_left) : 0;
+        const int64_t base = ws / kDecodeBlock * kDecodeBlock;
+        const int64_t nchunks = r.kv_len == 0 ? 1 : ceil_div(r.kv_len - base, c);
+        for (int32_t hk = 0; hk < d.num_kv_heads; ++hk) {
+            if (nchunks > 1) {
+                merges.insert(merges.end(), {int32_t(b), hk, int32_t(slot), int32_t(nchunks)});
+            }
+            for (int64_t k = 0; k < nchunks; ++k) {
+                It it;
+                const int64_t t0 = base + k * c;
+                const int64_t t1 = std::min<int64_t>(r.kv_len, t0 + c);
+                it.cost = t1 - t0;
+                it.w[kDiRequest] = int32_t(b);
+                it.w[kDiKvHead] = hk;
+                it.w[kDiTokBegin] = int32_t(t0);
+                it.w[kDiTokEnd] = int32_t(t1);
+                it.w[kDiVisLo] = int32_t(std::max(ws, t0));
+                it.w[kDiPageBase] = int32_t(r.page_base);
+                it.w[kDiSlot] = nchunks > 1 ? int32_t(slot++) : -1;
+                it.w[kDiKvLen] = int32_t(r.kv_len);
+                items.push_back(it);
+            }
+        }
+    }
+    if (int64_t(items.size()) > p->items_cap || slot > p->slots_cap ||
+        int64_t(merges.size() / kMergeWords) > p->merges_cap)
+        return fail(PKVS_ERR_CAPACITY, "decode work list (%zu items, %lld partial slots) "
+                    "exceeds the plan capacity (%lld items, %lld slots)", items.size(),
+                    (long long)slot, (long long)p->items_cap, (long long)p->slots_cap);
+    std::stable_sort(items.begin(), items.end(),
+                     [](const It &a, const It &b) { return a.cost > b.cost; });
+    p->n_items = int64_t(items.size());
+    p->n_merges = int64_t(merges.size() / kMergeWords);
+    p->split_size = int32_t(std::min<int64_t>(c, INT32_MAX));
+    const size_t merge_off = kHeaderWords + items.size() * kDecodeItemWords;
+    p->host_ws.assign(merge_off + merges.size(), 0);
+    int32_t *w = p->host_ws.data();
+    w[kHdrNumItems] = int32_t(items.size());
+    w[kHdrNumMerges] = int32_t(p->n_merges);
+    w[kHdrMergeOffset] = int32_t(merge_off);
+    w[kHdrItemWords] = kDecodeItemWords;
+    for (size_t i = 0; i < items.size(); ++i)
+        std::memcpy(w + kHeaderWords + i * kDecodeItemWords, items[i].w, sizeof items[i].w);
+    std::copy(merges.begin(), merges.end(), w + merge_off);
+    return PKVS_OK;
+}
+
+// Copy the host work list into the device int workspace with one async
+// host-to-device copy on `stream`, from a ring of pinned staging buffers (a
+// buffer is reused only after its previous copy has completed).
+static int upload(Plan *p, void *int_ws, hipStream_t stream)
+{
+    const size_t bytes = p->host_ws.size() * sizeof(int32_t);
+    if (!p->stage[0]) {
+        for (int i = 0; i < kStages; ++i) {
+            if (hipHostMalloc(&p->stage[i], p->int_ws_need, hipHostMallocDefault) != hipSuccess)
+                return fail(PKVS_ERR_HIP, "hipHostMalloc of %zu bytes failed", p->int_ws_need);
+            if (hipEventCreateWithFlags(&p->stage_ev[i], hipEventDisableTiming) != hipSuccess)
+                return fail(PKVS_ERR_HIP, "hipEventCreate failed");
+            p->stage_used[i] = false;
+        }
+    }
+    const int s = p->stage_next;
+    p->stage_next = (s + 1) % kStages;
+    if (p->stage_used[s] && hipEventSynchronize(p->stage_ev[s]) != hipSuccess)
+        return fail(PKVS_ERR_HIP, "waiting for a staging buffer failed");
+    std::memcpy(p->stage[s], p->host_ws.data(), bytes);
+    hipError_t e = hipMemcpyAsync(int_ws, p->stage[s], bytes, hipMemcpyHostToDevice, stream);
+    if (e != hipSuccess) return fail(PKVS_ERR_HIP, "hipMemcpyAsync: %s", hipGetErrorString(e));
+    e = hipEventRecord(p->stage_ev[s], stream);
+    if (e != hipSuccess) return fail(PKVS_ERR_HIP, "hipEventRecord: %s", hipGetErrorString(e));
+    p->stage_used[s] = true;
+    return PKVS_OK;
+}
+
+static int finish_plan(Plan *p, void *float_ws, size_t float_bytes, void *int_ws,
+                       size_t int_bytes, hipStream_t stream)
+{
+    p->planned_device = false;
+    if (!int_ws) return PKVS_OK;  // dry plan
+    if (int_bytes < p->int_ws_need)
+        return fail(PKVS_ERR_WORKSPACE, "int workspace %zu bytes < required %zu; increase the "
+                    "workspace buffer size", int_bytes, p->int_ws_need);
+    if (p->float_ws_need && (!float_ws || float_bytes < p->float_ws_need))
+        return fail(PKVS_ERR_WORKSPACE, "float workspace %zu bytes < required %zu; increase "
+                    "the workspace buffer size", float_ws ? float_bytes : 0, p->float_ws_need);
+    if (!p->have_gpu) return fail(PKVS_ERR_HIP, "no HIP device: only dry plans are possible");
+    int rc = upload(p, int_ws, stream);
+    if (rc) return rc;
+    p->int_ws = int_ws;
+    p->float_ws = float_ws;
+    p->planned_device = true;
+    return PKVS_OK;
+}
+
+}  // namespace pkvs
+
+using namespace pkvs;
+
+extern "C" {
+
+int pkvs_plan_create(pkvs_plan **out, const pkvs_desc *desc)
+{
+    clear_error();
+    if (!out) return fail(PKVS_ERR_INVALID_ARG, "out is null");
+    *out = nullptr;
+    int rc = validate_desc(desc);
+    if (rc) return rc;
+    Plan *p = new (std::nothrow) Plan();
+    if (!p) return fail(PKVS_ERR_INVALID_ARG, "out of host memory");
+    p->desc = *desc;
+    const int group = desc->num_qo_heads / desc->num_kv_heads;
+    int ndev = 0;
+    p->have_gpu = hipGetDeviceCount(&ndev) == hipSuccess && ndev > 0 &&
+                  hipGetDevice(&p->device) == hipSuccess;
+    p->num_cus = kDefaultCus;
+    if (p->have_gpu) {
+        int cus = 0;
+        if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, p->device) ==
+                hipSuccess && cus > 0)
+            p->num_cus = cus;
+    }
+    (void)hipGetLastError();
+    const bool fp32 = desc->dtype == PKVS_FP32;
+    if (desc->kind == PKVS_PREFILL) {
+        p->query_tile = fp32 ? kGenericQTile : kPrefillRows / group;
+        p->item_words = kPrefillItemWords;
+        p->block_threads = fp32 ? kGenericThreads : kPrefillThreads;
+        int per_cu = p->have_gpu && !fp32 ? prefill_bf16_blocks_per_cu(desc->head_dim) : 0;
+        p->grid_blocks = p->num_cus * std::max(per_cu, 2);
+    } else {
+        p->query_tile = 1;
+        p->item_words = fp32 ? kPrefillItemWords : kDecodeItemWords;
+        p->block_threads = fp32 ? kGenericThreads : kDecodeThreads;
+        int per_cu = p->have_gpu && !fp32 ? decode_bf16_blocks_per_cu(desc->head_dim) : 0;
+        p->grid_blocks = p->num_cus * std::max(per_cu, fp32 ? 2 : 8);
+        p->auto_target_items = 2 * p->grid_blocks;
+    }
+    (void)hipGetLastError();
+    size_plan(p);
+    if (fp32 && desc->kind == PKVS_DECODE) {
+        // the fp32 path runs decode as one-token prefill items
+        p->items_cap = int64_t(desc->batch_capacity) * desc->num_kv_heads;
+        p->slots_cap = p->merges_cap = 0;
+        p->int_ws_need = sizeof(int32_t) * size_t(kHeaderWords + p->items_cap * kPrefillItemWords);
+        p->float_ws_need = 0;
+    }
+    p->grid_blocks = int32_t(std::max<int64_t>(1, std::min<int64_t>(p->grid_blocks, p->items_cap)));
+    *out = p;
+    return PKVS_OK;
+}
+
+int pkvs_workspace_size(const pkvs_plan *p, size_t *float_ws_bytes, size_t *int_ws_bytes)
+{
+    clear_error();
+    if (!p || !float_ws_bytes || !int_ws_bytes) return fail(PKVS_ERR_INVALID_ARG, "null argument");
+    *float_ws_bytes = p->float_ws_need;
+    *int_ws_bytes = p->int_ws_need;
+    return PKVS_OK;
+}
+
+int pkvs_prefill_plan(pkvs_plan *p, const int32_t *qo_indptr_h, const int32_t *kv_indptr_h,
+                      const int32_t *kv_last_page_len_h, int32_t batch_size, void *float_ws,
+                      size_t float_ws_bytes, void *int_ws, size_t int_ws_bytes,
+                      hipStream_t stream)
+{
+    clear_error();
+    if (!p) return fail(PKVS_ERR_INVALID_ARG, "plan is null");
+    if (p->desc.kind != PKVS_PREFILL) return fail(PKVS_ERR_INVALID_ARG, "not a prefill plan");
+    p->planned_device = false;
+    std::vector<Req> reqs;
+    int rc = read_layout(p, qo_indptr_h, kv_indptr_h, kv_last_page_len_h, batch_size, reqs);
+    if (rc) return rc;
+    build_prefill(p, reqs);
+    if (p->n_items > p->items_cap)
+        return fail(PKVS_ERR_CAPACITY, "prefill work list of %lld items exceeds capacity %lld",
+                    (long long)p->n_items, (long long)p->items_cap);
+    p->batch = batch_size;
+    return finish_plan(p, float_ws, float_ws_bytes, int_ws, int_ws_bytes, stream);
+}
+
+int pkvs_decode_plan(pkvs_plan *p, const int32_t *kv_indptr_h, const int32_t *kv_last_page_len_h,
+                     int32_t batch_size, void *float_ws, size_t float_ws_bytes, void *int_ws,
+                     size_t int_ws_bytes, hipStream_t stream)
+{
+    clear_error();
+    if (!p) return fail(PKVS_ERR_INVALID_ARG, "plan is null");
+    if (p->desc.kind != PKVS_DECODE) return fail(PKVS_ERR_INVALID_ARG, "not a decode plan");
+    p->planned_device = false;
+    std::vector<Req> reqs;
+    int rc = read_layout(p, nullptr, kv_indptr_h, kv_last_page_len_h, batch_size, reqs);
+    if (rc) return rc;
+    if (p->desc.dtype == PKVS_FP32) {
+        // one-token prefill items: query b at position kv_len-1
+        std::vector<Req> as_prefill = reqs;
+        for (size_t b = 0; b < reqs.size(); ++b) {
+            as_prefill[b].qo_begin = int64_t(b);
+            as_prefill[b].qo_len = 1;
+        }
+        // a keyless request still owns its query row: it becomes an item with
+        // an empty key range, which writes o = 0 and lse = -inf
+        build_prefill(p, as_prefill);
+        p->split_size = 0;
+    } else {
+        rc = build_decode(p, reqs);
+        if (rc) return rc;
+    }
+    if (p->n_items > p->items_cap)
+        return fail(PKVS_ERR_CAPACITY, "decode work list of %lld items exceeds capacity %lld",
+                    (long long)p->n_items, (long long)p->items_cap);
+    p->batch = batch_size;
+    return finish_plan(p, float_ws, float_ws_bytes, int_ws, int_ws_bytes, stream);
+}
+
+int pkvs_plan_get_info(const pkvs_plan *p, pkvs_plan_info *info)
+{
+    clear_error();
+    if (!p || !info) return fail(PKVS_ERR_INVALID_ARG, "null argument");
+    info->num_items = p->n_items;
+    info->num_merges = p->n_merges;
+    info->float_ws_bytes = int64_t(p->float_ws_need);
+    info->int_ws_bytes = int64_t(p->int_ws_need);
+    info->grid_blocks = p->grid_blocks;
+    info->block_threads = p->block_threads;
+    info->split_size = p->split_size;
+    info->item_words = p->item_words;
+    info->query_tile = p->query_tile;
+    info->num_cus = p->num_cus;
+    return PKVS_OK;
+}
+
+int pkvs_plan_copy_items(const pkvs_plan *p, int32_t *dst, int64_t max_items, int64_t *n_items)
+{
+    clear_error();
+    if (!p || !n_items) return fail(PKVS_ERR_INVALID_ARG, "null argument");
+    *n_items = p->n_items;
+    if (!dst) return PKVS_OK;
+    const int64_t n = std::min(max_items, p->n_items);
+    if (n > 0)
+        std::memcpy(dst, p->host_ws.data() + kHeaderWords, sizeof(int32_t) * n * p->item_words);
+    return PKVS_OK;
+}
+
+void pkvs_plan_destroy(pkvs_plan *p)
+{
+    if (!p) return;
+    for (int i = 0; i < kStages; ++i) {
+        if (p->stage_ev[i]) {
+            if (p->stage_used[i]) (void)hipEventSynchronize(p->stage_ev[i]);
+            (void)hipEventDestroy(p->stage_ev[i]);
+        }
+        if (p->stage[i]) (void)hipHostFree(p->stage[i]);
+    }
+    delete p;
+}
+
+const char *pkvs_strerror(int code)
+{
+    switch (code) {
+    case PKVS_OK: return "ok";
+    case PKVS_ERR_INVALID_ARG: return "invalid argument";
+    case PKVS_ERR_UNSUPPORTED: return "unsupported configuration";
+    case PKVS_ERR_WORKSPACE: return "workspace too small";
+    case PKVS_ERR_CAPACITY: return "batch exceeds plan capacity";
+    case PKVS_ERR_PLAN_MISMATCH: return "run arguments differ from the plan";
+    case PKVS_ERR_HIP: return "HIP runtime error";
+    case PKVS_ERR_NOT_PLANNED: return "no device plan";
+    default: return "unknown status";
+    }
+}
+
+const char *pkvs_last_error(void) { return g_last_error.c_str(); }
+
+}  // extern "C"

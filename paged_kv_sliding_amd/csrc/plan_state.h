@@ -1,0 +1,51 @@
+// plan_state.h -- the opaque pkvs_plan object (host side only).
+#pragma once
+
+#include <hip/hip_runtime.h>
+
+#include <cstddef>
+#include <cstdint>
+#include <vector>
+
+#include "../../include/pkvs.h"
+
+namespace pkvs {
+
+constexpr int kStages = 4;             // pinned staging buffers for the work-list copy
+constexpr int kDefaultCus = 256;       // compute units assumed when no device is visible
+constexpr int64_t kMinAutoSplit = 256; // smallest key chunk the planner picks by itself
+
+int fail(int code, const char *fmt, ...);
+void clear_error();
+
+}  // namespace pkvs
+
+struct pkvs_plan {
+    pkvs_desc desc{};
+    int device = 0;
+    bool have_gpu = false;
+    int num_cus = 0;
+    int grid_blocks = 0, block_threads = 0, query_tile = 0, item_words = 0;
+    int64_t auto_target_items = 0;
+    int64_t items_cap = 0, slots_cap = 0, merges_cap = 0;
+    size_t int_ws_need = 0, float_ws_need = 0;
+
+    // the last plan() call
+    std::vector<int32_t> host_ws;  // header + items + merge entries
+    int64_t n_items = 0, n_merges = 0;
+    int32_t split_size = 0;
+    int32_t batch = 0;
+    bool planned_device = false;
+    void *int_ws = nullptr;
+    void *float_ws = nullptr;
+
+    // pinned staging ring for the host-to-device copy of the work list
+    void *stage[pkvs::kStages] = {};
+    hipEvent_t stage_ev[pkvs::kStages] = {};
+    bool stage_used[pkvs::kStages] = {};
+    int stage_next = 0;
+};
+
+namespace pkvs {
+using Plan = pkvs_plan;
+}

@@ -1,0 +1,171 @@
+// run.cpp -- run-side entry points of libpkvs: argument checks against the
+// plan, kernel launches, and the standalone merge_state.
+#include <hip/hip_runtime.h>
+
+#include <algorithm>
+
+#include "pkvs_internal.h"
+#include "plan_state.h"
+
+using namespace pkvs;
+
+namespace {
+
+int log2_exact(int x)
+{
+    int r = 0;
+    while ((1 << r) < x) ++r;
+    return r;
+}
+
+// run() must repeat the window and causality the plan was made for: a run-time
+// window that silently replaces the planned one is the mismatch sglang PR
+// "Pass window_left at plan time for the SWA paged prefill wrapper" fixes.
+int check_run(const pkvs_plan *p, int kind, const void *q, const void *k, const void *v,
+              int64_t num_pages, const int32_t *kv_indices, const void *o, int32_t window_left,
+              int32_t causal)
+{
+    if (!p) return fail(PKVS_ERR_INVALID_ARG, "plan is null");
+    if (p->desc.kind != kind)
+        return fail(PKVS_ERR_INVALID_ARG, kind == PKVS_PREFILL ? "not a prefill plan"
+                                                              : "not a decode plan");
+    if (window_left != p->desc.window_left)
+        return fail(PKVS_ERR_PLAN_MISMATCH, "run window_left %d differs from the planned %d",
+                    window_left, p->desc.window_left);
+    if (kind == PKVS_PREFILL && causal != p->desc.causal)
+        return fail(PKVS_ERR_PLAN_MISMATCH, "run causal %d differs from the planned %d", causal,
+                    p->desc.causal);
+    if (!p->planned_device)
+        return fail(PKVS_ERR_NOT_PLANNED, "no device plan (plan() failed, was dry, or never "
+                    "ran)");
+    if (p->n_items > 0 && (!q || !k || !v || !kv_indices || !o || num_pages <= 0))
+        return fail(PKVS_ERR_INVALID_ARG, "null tensor or num_pages <= 0");
+    return PKVS_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+int pkvs_prefill_run(const pkvs_plan *p, const void *q, const void *k_cache, const void *v_cache,
+                     int64_t num_pages, const int32_t *kv_indices_d, void *o, float *lse,
+                     float sm_scale, int32_t window_left, int32_t causal, hipStream_t stream)
+{
+    clear_error();
+    int rc = check_run(p, PKVS_PREFILL, q, k_cache, v_cache, num_pages, kv_indices_d, o,
+                       window_left, causal);
+    if (rc) return rc;
+    if (p->n_items == 0) return PKVS_OK;
+    PrefillArgs a{};
+    a.q = q;
+    a.k = k_cache;
+    a.v = v_cache;
+    a.kv_indices = kv_indices_d;
+    a.o = o;
+    a.lse = lse;
+    a.ws = static_cast<const int32_t *>(p->int_ws);
+    a.num_pages = num_pages;
+    a.scale_log2 = sm_scale * 1.44269504088896340736f;
+    a.num_qo_heads = p->desc.num_qo_heads;
+    a.num_kv_heads = p->desc.num_kv_heads;
+    a.log2_group = log2_exact(p->desc.num_qo_heads / p->desc.num_kv_heads);
+    a.page_size = p->desc.page_size;
+    a.log2_page = log2_exact(p->desc.page_size);
+    a.window_left = p->desc.window_left;
+    a.causal = p->desc.causal;
+    hipError_t e = p->desc.dtype == PKVS_BF16
+                       ? launch_prefill_bf16(a, p->desc.head_dim, p->grid_blocks, stream)
+                       : launch_attention_fp32(a, p->desc.head_dim, p->grid_blocks, stream);
+    if (e != hipSuccess) return fail(PKVS_ERR_HIP, "prefill launch: %s", hipGetErrorString(e));
+    return PKVS_OK;
+}
+
+int pkvs_decode_run(const pkvs_plan *p, const void *q, const void *k_cache, const void *v_cache,
+                    int64_t num_pages, const int32_t *kv_indices_d, void *o, float *lse,
+                    float sm_scale, int32_t window_left, hipStream_t stream)
+{
+    clear_error();
+    int rc = check_run(p, PKVS_DECODE, q, k_cache, v_cache, num_pages, kv_indices_d, o,
+                       window_left, 1);
+    if (rc) return rc;
+    if (p->n_items == 0) return PKVS_OK;
+    const int log2g = log2_exact(p->desc.num_qo_heads / p->desc.num_kv_heads);
+    const float scale_log2 = sm_scale * 1.44269504088896340736f;
+    hipError_t e;
+    if (p->desc.dtype == PKVS_FP32) {
+        PrefillArgs a{};
+        a.q = q;
+        a.k = k_cache;
+        a.v = v_cache;
+        a.kv_indices = kv_indices_d;
+        a.o = o;
+        a.lse = lse;
+        a.ws = static_cast<const int32_t *>(p->int_ws);
+        a.num_pages = num_pages;
+        a.scale_log2 = scale_log2;
+        a.num_qo_heads = p->desc.num_qo_heads;
+        a.num_kv_heads = p->desc.num_kv_heads;
+        a.log2_group = log2g;
+        a.page_size = p->desc.page_size;
+        a.log2_page = log2_exact(p->desc.page_size);
+        a.window_left = p->desc.window_left;
+        a.causal = 1;
+        e = launch_attention_fp32(a, p->desc.head_dim, p->grid_blocks, stream);
+        if (e != hipSuccess) return fail(PKVS_ERR_HIP, "decode launch: %s", hipGetErrorString(e));
+        return PKVS_OK;
+    }
+    DecodeArgs a{};
+    a.q = q;
+    a.k = k_cache;
+    a.v = v_cache;
+    a.kv_indices = kv_indices_d;
+    a.o = o;
+    a.lse = lse;
+    a.ws = static_cast<const int32_t *>(p->int_ws);
+    const int group = p->desc.num_qo_heads / p->desc.num_kv_heads;
+    a.part_o = static_cast<float *>(p->float_ws);
+    a.part_lse = a.part_o ? a.part_o + p->slots_cap * group * p->desc.head_dim : nullptr;
+    a.num_pages = num_pages;
+    a.scale_log2 = scale_log2;
+    a.num_qo_heads = p->desc.num_qo_heads;
+    a.num_kv_heads = p->desc.num_kv_heads;
+    a.log2_group = log2g;
+    a.page_size = p->desc.page_size;
+    a.log2_page = log2_exact(p->desc.page_size);
+    e = launch_decode_bf16(a, p->desc.head_dim, p->grid_blocks, stream);
+    if (e != hipSuccess) return fail(PKVS_ERR_HIP, "decode launch: %s", hipGetErrorString(e));
+    if (p->n_merges > 0) {
+        // fixed grid: sized from the capacity, never from this batch
+        const int grid = int(std::min<int64_t>(p->merges_cap * group, int64_t(p->num_cus) * 16));
+        e = launch_decode_merge(a, p->desc.head_dim, p->desc.dtype, std::max(grid, 1), stream);
+        if (e != hipSuccess)
+            return fail(PKVS_ERR_HIP, "decode merge launch: %s", hipGetErrorString(e));
+    }
+    return PKVS_OK;
+}
+
+int pkvs_merge_state(const void *v_a, const float *s_a, const void *v_b, const float *s_b,
+                     void *v_out, float *s_out, int64_t num_tokens, int32_t num_heads,
+                     int32_t head_dim, int32_t v_dtype, hipStream_t stream)
+{
+    clear_error();
+    if (num_tokens < 0 || num_heads <= 0 || head_dim <= 0)
+        return fail(PKVS_ERR_INVALID_ARG, "bad shape (%lld, %d, %d)", (long long)num_tokens,
+                    num_heads, head_dim);
+    if (v_dtype != PKVS_BF16 && v_dtype != PKVS_FP32)
+        return fail(PKVS_ERR_UNSUPPORTED, "v_dtype %d not built", v_dtype);
+    if (num_tokens == 0) return PKVS_OK;
+    if (!v_a || !s_a || !v_b || !s_b || !v_out || !s_out)
+        return fail(PKVS_ERR_INVALID_ARG, "null pointer");
+    int dev = 0, cus = 256;
+    if (hipGetDevice(&dev) == hipSuccess)
+        (void)hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev);
+    const int64_t units = num_tokens * num_heads;
+    const int grid = int(std::min<int64_t>(units, int64_t(cus) * 32));
+    hipError_t e = launch_merge_state(v_a, s_a, v_b, s_b, v_out, s_out, num_tokens, num_heads,
+                                      head_dim, v_dtype, grid, stream);
+    if (e != hipSuccess) return fail(PKVS_ERR_HIP, "merge_state launch: %s", hipGetErrorString(e));
+    return PKVS_OK;
+}
+
+}  // extern "C"

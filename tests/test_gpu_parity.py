@@ -1,0 +1,330 @@
+"""GPU parity: the HIP kernels (through the C ABI) against the CPU oracle.
+
+Tolerances: max |O - O_ref| <= 2e-2 and max |LSE - LSE_ref| <= 1e-3, compared
+in fp32; masking is checked bit-exactly (window_left = 0 returns V at the
+query's own position; one-hot values expose the attention support)."""
+import math
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from gpu_helpers import (compare, gpu_run, log, make_attention, oracle_for, sub_case)
+from paged_kv_sliding_amd import pkvs as P
+from paged_kv_sliding_amd.synth import build_case, case_from_lengths
+
+pytestmark = pytest.mark.gpu
+DEV = "cuda"
+
+
+def small(qo, kv, *, H_q=4, H_kv=1, D=128, P_=16, W=31, seed=0, dtype=torch.bfloat16,
+          decode=False, split=-1, spare=3):
+    return case_from_lengths("small", qo, kv, num_qo_heads=H_q, num_kv_heads=H_kv, head_dim=D,
+                             page_size=P_, dtype=dtype, window_left=W, seed=seed,
+                             spare_pages=spare, device=DEV, is_decode=decode,
+                             fixed_split_size=split)
+
+
+# ----------------------------------------------------------------- the five workloads
+
+
+@pytest.mark.parametrize("E", [6, 8, 12])
+def test_tiny_prefill_fp32(E):
+    case = build_case("tiny_prefill", device=DEV, extend_len=E)
+    log(f"tiny_prefill E={E} W={case.window_left}")
+    o, lse = gpu_run(case)
+    ro, rl = oracle_for(case)
+    compare(o, lse, ro, rl, tag=f"tiny E={E}")
+    # positions past the window really lose keys: LSE differs from no window
+    if E > 5:
+        _, rl_full = oracle_for(case, window_left=-1)
+        assert np.abs(rl[5:] - rl_full[5:]).max() > 1e-3
+
+
+def test_tiny_prefill_fp32_batched():
+    cases = [build_case("tiny_prefill", device="cpu", extend_len=E) for E in (6, 8, 12)]
+    qo = [c.qo_lens[0] for c in cases]
+    case = case_from_lengths("tiny3", qo, qo, num_qo_heads=2, num_kv_heads=1, head_dim=64,
+                             page_size=4, dtype=torch.float32, window_left=4, seed=7,
+                             spare_pages=6, device=DEV)
+    o, lse = gpu_run(case)
+    ro, rl = oracle_for(case)
+    compare(o, lse, ro, rl, tag="tiny batch of 3")
+
+
+def test_prefix_prefill_full():
+    case = build_case("prefix_prefill", device=DEV)
+    log(f"prefix_prefill qo={case.qo_lens} kv={case.kv_lens}")
+    o, lse = gpu_run(case)
+    ro, rl = oracle_for(case)
+    compare(o, lse, ro, rl, tag="prefix_prefill")
+
+
+@pytest.mark.parametrize("W", [-1, 0, 31, 127, 1023])
+def test_decode_sweep_full(W):
+    case = build_case("decode_sweep", device=DEV, window_left=W)
+    log(f"decode_sweep W={W}")
+    o, lse = gpu_run(case)
+    ro, rl = oracle_for(case)
+    compare(o, lse, ro, rl, tag=f"decode_sweep W={W}")
+
+
+def test_decode_sweep_saturation_equals_no_window():
+    case = build_case("decode_sweep", device=DEV, window_left=-1)
+    o1, l1 = gpu_run(case, window_left=-1)
+    o2, l2 = gpu_run(case, window_left=max(case.kv_lens) - 1)
+    assert torch.equal(o1, o2) and torch.equal(l1, l2)
+
+
+LONG_ROWS = [0, 1, 2, 7, 8, 31, 32, 33, 127, 128, 129, 4094, 4095, 4096, 4097, 4127, 4128, 8191,
+             8192, 12345, 16384, 20000, 24575, 30001, 32735, 32736, 32766, 32767]
+
+
+def test_long_prefill_sampled():
+    """The full 32k-token prefill in the benchmark's launch configuration,
+    checked on sampled query tokens (all heads)."""
+    case = build_case("long_prefill", device=DEV)
+    log("long_prefill run")
+    o, lse = gpu_run(case)
+    rng = np.random.default_rng(4)
+    rows = sorted(set(LONG_ROWS + rng.integers(0, 32768, size=20).tolist()))
+    log(f"long_prefill oracle on {len(rows)} rows")
+    ro, rl = oracle_for(case, rows=rows)
+    compare(o, lse, ro, rl, rows=rows, tag="long_prefill sampled")
+
+
+@pytest.mark.parametrize("W", [4095, -1])
+def test_split_decode_sampled(W):
+    """The full 256-request split-KV decode (2048-key chunks merged), checked
+    on sampled requests (all heads)."""
+    case = build_case("split_decode", device=DEV, window_left=W)
+    log(f"split_decode W={W} run")
+    att = make_attention(case)
+    o, lse = gpu_run(case, att=att)
+    info = att.info()
+    assert info.split_size == 2048 and info.num_merges > 0
+    rng = np.random.default_rng(5)
+    kv = np.array(case.kv_lens)
+    picks = {int(np.argmin(kv)), int(np.argmax(kv))}
+    picks |= set(rng.choice(len(kv), size=6, replace=False).tolist())
+    picks = sorted(picks)
+    sub = sub_case(case, picks)
+    log(f"split_decode oracle on requests {picks}")
+    ro, rl = oracle_for(sub)
+    compare(o[picks], lse[picks], ro, rl, tag=f"split_decode W={W}")
+
+
+# ----------------------------------------------------------------- edge cases and tails
+
+
+@pytest.mark.parametrize("P_", [1, 4, 16, 64])
+@pytest.mark.parametrize("W", [-1, 0, 1, 31, 33, 200])
+def test_prefill_small_ragged(P_, W):
+    qo = [1, 70, 0, 33, 129, 5]
+    kv = [1, 70, 9, 300, 129, 700]
+    case = small(qo, kv, H_q=8, H_kv=2, D=128, P_=P_, W=W, seed=P_ * 100 + W)
+    o, lse = gpu_run(case)
+    ro, rl = oracle_for(case)
+    compare(o, lse, ro, rl, tag=f"prefill P={P_} W={W}")
+
+
+@pytest.mark.parametrize("D,G", [(64, 1), (64, 8), (128, 2), (128, 16), (256, 4), (256, 1)])
+def test_prefill_head_shapes(D, G):
+    qo, kv = [40, 130, 3], [300, 130, 64]
+    case = small(qo, kv, H_q=2 * G, H_kv=2, D=D, P_=16, W=63, seed=D + G)
+    o, lse = gpu_run(case)
+    ro, rl = oracle_for(case)
+    compare(o, lse, ro, rl, tag=f"prefill D={D} G={G}")
+
+
+def test_prefill_fp32_ragged():
+    case = small([5, 17, 1], [40, 17, 3], H_q=4, H_kv=2, D=128, P_=4, W=6, seed=3,
+                 dtype=torch.float32)
+    o, lse = gpu_run(case)
+    ro, rl = oracle_for(case)
+    compare(o, lse, ro, rl, tag="prefill fp32")
+
+
+def test_prefill_non_causal_no_window():
+    case = small([20, 7], [50, 7], H_q=4, H_kv=1, D=128, W=-1, seed=9)
+    case.causal = False
+    o, lse = gpu_run(case)
+    ro, rl = oracle_for(case)
+    compare(o, lse, ro, rl, tag="prefill non-causal")
+
+
+@pytest.mark.parametrize("P_", [1, 4, 16])
+@pytest.mark.parametrize("W", [-1, 0, 5, 31, 32, 100])
+@pytest.mark.parametrize("split", [-1, 32, 96])
+def test_decode_small_ragged(P_, W, split):
+    kv = [1, 2, 31, 32, 33, 64, 65, 200, 1000, 0]
+    case = small([1] * len(kv), kv, H_q=32, H_kv=8, D=128, P_=P_, W=W, seed=P_ + W + split,
+                 decode=True, split=split)
+    o, lse = gpu_run(case)
+    ro, rl = oracle_for(case)
+    compare(o, lse, ro, rl, tag=f"decode P={P_} W={W} split={split}")
+    assert (o[-1] == 0).all() and torch.isneginf(lse[-1]).all()  # keyless request
+
+
+@pytest.mark.parametrize("D,G", [(64, 4), (128, 1), (128, 8), (128, 16), (256, 2)])
+def test_decode_head_shapes(D, G):
+    kv = [7, 300, 1500, 64]
+    case = small([1] * 4, kv, H_q=2 * G, H_kv=2, D=D, P_=16, W=511, seed=D * G, decode=True)
+    o, lse = gpu_run(case)
+    ro, rl = oracle_for(case)
+    compare(o, lse, ro, rl, tag=f"decode D={D} G={G}")
+
+
+def test_decode_fp32():
+    kv = [7, 300, 0, 64]
+    case = small([1] * 4, kv, H_q=8, H_kv=2, D=64, P_=4, W=20, seed=11, decode=True,
+                 dtype=torch.float32)
+    o, lse = gpu_run(case)
+    ro, rl = oracle_for(case)
+    compare(o, lse, ro, rl, tag="decode fp32")
+
+
+@pytest.mark.parametrize("split,disable", [(32, False), (64, False), (256, False), (-1, False),
+                                           (-1, True), (2048, False)])
+def test_decode_split_invariance(split, disable):
+    kv = [3000, 5000, 17, 4096, 2049]
+    case = small([1] * 5, kv, H_q=64, H_kv=8, D=128, W=-1, seed=21, decode=True)
+    o, lse = gpu_run(case, fixed_split_size=split, disable_split_kv=disable)
+    ro, rl = oracle_for(case)
+    compare(o, lse, ro, rl, tag=f"split={split} disable={disable}")
+
+
+# ----------------------------------------------------------------- exact masking
+
+
+@pytest.mark.parametrize("decode", [False, True])
+def test_window_zero_returns_own_value_bit_exact(decode):
+    if decode:
+        kv = [1, 17, 300, 4096]
+        case = small([1] * 4, kv, H_q=32, H_kv=8, D=128, W=0, seed=31, decode=True)
+    else:
+        kv = [40, 300, 77]
+        case = small([40, 100, 7], kv, H_q=8, H_kv=2, D=128, W=0, seed=32)
+    o, lse = gpu_run(case)
+    G = case.num_qo_heads // case.num_kv_heads
+    # expected: the value row of the query's own position, per KV head
+    expect = torch.empty_like(o)
+    kvp = case.kv_indptr.cpu()
+    for b in range(case.batch_size):
+        prefix = case.kv_lens[b] - case.qo_lens[b]
+        for i in range(case.qo_lens[b]):
+            p = prefix + i
+            pg = int(case.kv_indices[int(kvp[b]) + p // case.page_size])
+            vrow = case.v_cache[pg, p % case.page_size]  # [H_kv, D]
+            expect[int(case.qo_indptr[b]) + i] = vrow.repeat_interleave(G, dim=0)
+    assert torch.equal(o, expect)
+    ro, rl = oracle_for(case)
+    compare(o, lse, ro, rl, tag=f"W=0 decode={decode}")
+
+
+@pytest.mark.parametrize("decode", [False, True])
+@pytest.mark.parametrize("W", [-1, 0, 3, 40])
+def test_one_hot_values_expose_exact_support(decode, W):
+    """V_j = e_j (D >= kv_len): the output row is the attention weight vector;
+    its nonzero set must be exactly the visible keys."""
+    D = 128
+    if decode:
+        kv = [1, 50, 128, 97]
+        case = small([1] * 4, kv, H_q=8, H_kv=2, D=D, P_=4, W=W, seed=40 + W, decode=True,
+                     split=32)
+    else:
+        kv = [128, 60, 100]
+        case = small([70, 60, 1], kv, H_q=8, H_kv=2, D=D, P_=4, W=W, seed=50 + W)
+    kvp = case.kv_indptr.cpu()
+    for b in range(case.batch_size):
+        for j in range(case.kv_lens[b]):
+            pg = int(case.kv_indices[int(kvp[b]) + j // case.page_size])
+            case.v_cache[pg, j % case.page_size] = 0
+            case.v_cache[pg, j % case.page_size, :, j] = 1
+    o, lse = gpu_run(case)
+    o = o.float().cpu()
+    for b in range(case.batch_size):
+        prefix = case.kv_lens[b] - case.qo_lens[b]
+        for i in range(case.qo_lens[b]):
+            p = prefix + i
+            lo = max(0, p - W) if W >= 0 else 0
+            want = torch.zeros(D, dtype=torch.bool)
+            want[lo:p + 1] = True
+            got = o[int(case.qo_indptr[b]) + i] != 0
+            assert (got == want.unsqueeze(0)).all(), (b, i, p, lo)
+
+
+# ----------------------------------------------------------------- plan lifecycle
+
+
+def test_replan_in_place_then_capacity_error():
+    big = small([1] * 6, [500, 2000, 33, 4096, 1, 700], H_q=32, H_kv=8, D=128, W=127, seed=61,
+                decode=True)
+    att = make_attention(big, batch_capacity=6, kv_capacity=4096)
+    o, lse = gpu_run(big, att=att)
+    ro, rl = oracle_for(big)
+    compare(o, lse, ro, rl, tag="plan A")
+    smaller = small([1] * 3, [4096, 5, 900], H_q=32, H_kv=8, D=128, W=127, seed=62, decode=True)
+    o, lse = gpu_run(smaller, att=att)
+    ro, rl = oracle_for(smaller)
+    compare(o, lse, ro, rl, tag="re-plan B (smaller)")
+    larger = small([1] * 7, [10] * 7, H_q=32, H_kv=8, D=128, W=127, seed=63, decode=True)
+    with pytest.raises(P.PkvsError) as ei:
+        att.plan(kv_indptr=larger.kv_indptr.cpu(), kv_last_page_len=larger.kv_last_page_len.cpu())
+    assert ei.value.code == P.PKVS_ERR_CAPACITY
+
+
+def test_run_without_lse():
+    case = small([30], [90], H_q=4, H_kv=1, D=128, W=10, seed=71)
+    o = gpu_run(case, return_lse=False)
+    ro, _ = oracle_for(case)
+    compare(o, None, ro, None, tag="no lse")
+
+
+def test_run_rejects_mismatched_window_on_gpu():
+    case = small([30], [90], H_q=4, H_kv=1, D=128, W=10, seed=72)
+    att = make_attention(case)
+    att.plan(qo_indptr=case.qo_indptr.cpu(), kv_indptr=case.kv_indptr.cpu(),
+             kv_last_page_len=case.kv_last_page_len.cpu())
+    with pytest.raises(P.PkvsError) as ei:
+        att.run(case.q, case.k_cache, case.v_cache, case.kv_indices, sm_scale=case.sm_scale,
+                window_left=11)
+    assert ei.value.code == P.PKVS_ERR_PLAN_MISMATCH
+
+
+# ----------------------------------------------------------------- merge_state
+
+
+@pytest.mark.parametrize("dtype", [torch.bfloat16, torch.float32])
+@pytest.mark.parametrize("H,D", [(64, 128), (128, 64), (128, 256), (8, 96)])
+def test_merge_state_against_oracle(dtype, H, D):
+    g = torch.Generator(device=DEV).manual_seed(H * D)
+    n = 37
+    va = torch.randn(n, H, D, generator=g, device=DEV).to(dtype)
+    vb = torch.randn(n, H, D, generator=g, device=DEV).to(dtype)
+    sa = torch.randn(n, H, generator=g, device=DEV) * 5
+    sb = torch.randn(n, H, generator=g, device=DEV) * 5
+    sa[0, :3] = float("-inf")
+    sb[0, 1:4] = float("-inf")
+    v, s = P.pkvs_merge_state(va, sa, vb, sb)
+    torch.cuda.synchronize()
+    rv, rs = oracle.merge_state(va.double().cpu().numpy(), sa.double().cpu().numpy(),
+                                vb.double().cpu().numpy(), sb.double().cpu().numpy())
+    compare(v, s, rv, rs, tag=f"merge {dtype} H={H} D={D}")
+    assert (v[0, 1:3] == 0).all() and torch.isneginf(s[0, 1:3]).all()
+    # in place (v_out aliases v_a)
+    va2, sa2 = va.clone(), sa.clone()
+    P.pkvs_merge_state(va2, sa2, vb, sb, v_out=va2, s_out=sa2)
+    torch.cuda.synchronize()
+    assert torch.equal(va2, v) and torch.equal(sa2, s)
+
+
+def test_merge_state_of_prefill_split_equals_unsplit():
+    """Attention over keys [0, c) merged with attention over keys [c, kv_len)
+    gives the one-pass result (decode split at a chunk boundary, in the GPU)."""
+    case = small([1] * 3, [1000, 64, 3000], H_q=32, H_kv=8, D=128, W=-1, seed=81, decode=True)
+    o1, l1 = gpu_run(case, fixed_split_size=256)
+    o2, l2 = gpu_run(case, disable_split_kv=True)
+    assert (o1.float() - o2.float()).abs().max() <= 2e-2
+    assert (l1 - l2).abs().max() <= 1e-3

@@ -1,0 +1,271 @@
+"""Host-side tests of libpkvs that need no GPU: exported symbols, descriptor
+validation, and invariants of the planner's work lists (dry plans)."""
+import ctypes
+import os
+import re
+import subprocess
+
+import pytest
+import torch
+
+from paged_kv_sliding_amd import pkvs as P
+from paged_kv_sliding_amd.synth import build_case, workload_lengths
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "pkvs.h")
+
+
+def header_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(pkvs_[a-z_]+)\s*\(", text)))
+
+
+def test_header_and_binding_agree():
+    assert header_functions() == sorted(P.EXPORTED)
+
+
+def test_library_exports_every_declared_symbol():
+    out = subprocess.run(["nm", "-D", "--defined-only", P.LIB_PATH], capture_output=True,
+                         text=True, check=True).stdout
+    exported = set(re.findall(r"\bT (pkvs_\w+)", out))
+    missing = set(header_functions()) - exported
+    assert not missing, missing
+    lib = ctypes.CDLL(P.LIB_PATH)
+    for name in header_functions():
+        assert hasattr(lib, name)
+
+
+def desc(kind=P.PKVS_PREFILL, **kw):
+    base = dict(num_qo_heads=4, num_kv_heads=1, head_dim=128, page_size=16,
+                dtype=torch.bfloat16, window_left=31, causal=True, batch_capacity=16,
+                qo_capacity=8192, kv_capacity=8192)
+    base.update(kw)
+    return P.make_desc(kind, **base)
+
+
+def err_code(fn):
+    with pytest.raises(P.PkvsError) as ei:
+        fn()
+    return ei.value.code
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(window_left=-2), P.PKVS_ERR_INVALID_ARG),
+    (dict(num_qo_heads=6, num_kv_heads=4), P.PKVS_ERR_INVALID_ARG),
+    (dict(head_dim=96), P.PKVS_ERR_UNSUPPORTED),
+    (dict(page_size=12), P.PKVS_ERR_UNSUPPORTED),
+    (dict(causal=False, window_left=7), P.PKVS_ERR_UNSUPPORTED),
+    (dict(num_qo_heads=3, num_kv_heads=1), P.PKVS_ERR_UNSUPPORTED),
+    (dict(fixed_split_size=100), P.PKVS_ERR_INVALID_ARG),
+    (dict(batch_capacity=0), P.PKVS_ERR_INVALID_ARG),
+])
+def test_descriptor_rejections(kw, code):
+    assert err_code(lambda: P.pkvs_plan_create(desc(**kw))) == code
+
+
+def csr(qo_lens, kv_lens, page):
+    npages = [(n + page - 1) // page for n in kv_lens]
+    kvp = [0]
+    for n in npages:
+        kvp.append(kvp[-1] + n)
+    qop = [0]
+    for n in qo_lens:
+        qop.append(qop[-1] + n)
+    last = [0 if n == 0 else n - (m - 1) * page for n, m in zip(kv_lens, npages)]
+    return qop, kvp, last
+
+
+def visible(p, j, W, causal=True):
+    return (not causal or j <= p) and (W < 0 or j >= p - W)
+
+
+@pytest.mark.parametrize("W", [-1, 0, 4, 31, 511])
+@pytest.mark.parametrize("G", [1, 4, 8])
+def test_prefill_items_cover_every_query_once(W, G):
+    qo = [1, 0, 40, 300, 7, 129]
+    kv = [1, 5, 40, 1000, 600, 129]
+    h = P.pkvs_plan_create(desc(num_qo_heads=2 * G, num_kv_heads=2, window_left=W))
+    qop, kvp, last = csr(qo, kv, 16)
+    P.pkvs_prefill_plan(h, qop, kvp, last, len(kv), None, None)
+    info = P.pkvs_plan_get_info(h)
+    items = P.pkvs_plan_copy_items(h)
+    assert info.query_tile == 128 // G and items.shape[0] == info.num_items
+    seen = {}
+    for it in items.tolist():
+        b, hk, q0, qn, pos0, kv_len, pbase, kvb = it
+        assert 1 <= qn <= info.query_tile and kv_len == kv[b] and pbase == kvp[b]
+        prefix = kv[b] - qo[b]
+        assert pos0 == prefix + (q0 - qop[b])
+        assert kvb % 32 == 0
+        kve = min(kv_len, pos0 + qn)
+        for t in range(q0, q0 + qn):
+            seen[(b, hk, t)] = seen.get((b, hk, t), 0) + 1
+            p = prefix + (t - qop[b])
+            # every visible key of every query lies inside the item's key range
+            first_vis = max(0, p - W) if W >= 0 else 0
+            assert kvb <= first_vis and p < kve
+        # no key tile of the range is wholly invisible to the item's queries
+        for k0 in range(kvb, kve, 32):
+            assert any(visible(pos0 + i, j, W) for i in range(qn)
+                       for j in range(k0, min(k0 + 32, kve))), (it, k0)
+    expect = {(b, hk, t) for b in range(len(kv)) for hk in range(2)
+              for t in range(qop[b], qop[b + 1])}
+    assert set(seen) == expect and set(seen.values()) == {1}
+    P.pkvs_plan_destroy(h)
+
+
+def test_prefill_first_tile_matches_paged_trim():
+    """The key range of a request's first query tile starts at the tile holding
+    kv_start = seq - min(seq, W + seq - prefix) (sglang update_sliding_window,
+    paged branch)."""
+    W = 100
+    qo, kv = [50, 10, 300], [1000, 10, 400]
+    h = P.pkvs_plan_create(desc(window_left=W))
+    qop, kvp, last = csr(qo, kv, 16)
+    P.pkvs_prefill_plan(h, qop, kvp, last, 3, None, None)
+    for it in P.pkvs_plan_copy_items(h).tolist():
+        b, _, q0, _, _, _, _, kvb = it
+        if q0 == qop[b]:
+            seq, prefix = kv[b], kv[b] - qo[b]
+            kv_start = seq - min(seq, W + seq - prefix)
+            assert kvb == kv_start // 32 * 32
+
+
+@pytest.mark.parametrize("W,split", [(-1, -1), (-1, 2048), (0, -1), (31, 64), (1023, 256),
+                                     (4095, 2048), (-1, 32)])
+def test_decode_chunks_partition_the_window(W, split):
+    kv = [0, 1, 2, 31, 32, 33, 500, 4096, 5000, 17]
+    h = P.pkvs_plan_create(desc(P.PKVS_DECODE, num_qo_heads=32, num_kv_heads=8, window_left=W,
+                                fixed_split_size=split, batch_capacity=len(kv)))
+    _, kvp, last = csr([1] * len(kv), kv, 16)
+    P.pkvs_decode_plan(h, kvp, last, len(kv), None, None)
+    info = P.pkvs_plan_get_info(h)
+    items = P.pkvs_plan_copy_items(h).tolist()
+    if split > 0:
+        assert info.split_size == split
+    by = {}
+    for b_, hk, t0, t1, lo, pbase, slot, kv_len in items:
+        assert kv_len == kv[b_] and pbase == kvp[b_]
+        by.setdefault((b_, hk), []).append((t0, t1, lo, slot))
+    slots = []
+    for b, n in enumerate(kv):
+        ws = max(0, n - 1 - W) if W >= 0 else 0
+        # the window of a decode query: the last min(kv_len, W+1) keys
+        assert n - ws == (min(n, W + 1) if W >= 0 else n)
+        for hk in range(8):
+            ch = sorted(by[(b, hk)])
+            if n == 0:
+                assert ch == [(0, 0, 0, -1)]
+                continue
+            assert ch[0][0] == ws // 32 * 32 and ch[-1][1] == n
+            for (a0, a1, alo, _), (b0, _, _, _) in zip(ch, ch[1:]):
+                assert a1 == b0  # contiguous, disjoint
+            for t0, t1, lo, slot in ch:
+                assert t0 % 32 == 0 and t0 < t1 and lo == max(ws, t0) and lo < t1
+                if split > 0:
+                    assert t1 - t0 <= split
+            if len(ch) == 1:
+                assert ch[0][3] == -1
+            else:
+                slots.append(sorted(c[3] for c in ch))
+    for s in slots:
+        assert s == list(range(s[0], s[0] + len(s)))
+    assert info.num_merges == len(slots)
+
+
+def test_grid_does_not_depend_on_the_batch():
+    h = P.pkvs_plan_create(desc(P.PKVS_DECODE, num_qo_heads=32, num_kv_heads=8, window_left=-1,
+                                batch_capacity=64, kv_capacity=4096))
+    grids = []
+    for kv in ([5], [4096] * 64, [1, 2, 3]):
+        _, kvp, last = csr([1] * len(kv), kv, 16)
+        P.pkvs_decode_plan(h, kvp, last, len(kv), None, None)
+        grids.append(P.pkvs_plan_get_info(h).grid_blocks)
+    assert len(set(grids)) == 1
+
+
+def test_capacity_is_enforced_not_underlaunched():
+    """A larger batch than the plan was made for is rejected at plan time
+    (AMD-Ecosystem/flashinfer PR 234, "Why each fix" 2)."""
+    h = P.pkvs_plan_create(desc(P.PKVS_DECODE, num_qo_heads=32, num_kv_heads=8,
+                                batch_capacity=4, kv_capacity=1024))
+    _, kvp, last = csr([1] * 4, [10, 20, 30, 1024], 16)
+    P.pkvs_decode_plan(h, kvp, last, 4, None, None)
+    _, kvp, last = csr([1] * 5, [10] * 5, 16)
+    assert err_code(lambda: P.pkvs_decode_plan(h, kvp, last, 5, None, None)) == P.PKVS_ERR_CAPACITY
+    _, kvp, last = csr([1], [1025], 16)
+    assert err_code(lambda: P.pkvs_decode_plan(h, kvp, last, 1, None, None)) == P.PKVS_ERR_CAPACITY
+    hp = P.pkvs_plan_create(desc(qo_capacity=100))
+    qop, kvp, last = csr([60, 50], [60, 50], 16)
+    assert err_code(lambda: P.pkvs_prefill_plan(hp, qop, kvp, last, 2, None, None)) == \
+        P.PKVS_ERR_CAPACITY
+
+
+def test_layout_rejections():
+    h = P.pkvs_plan_create(desc())
+    qop, kvp, last = csr([10], [5], 16)
+    assert err_code(lambda: P.pkvs_prefill_plan(h, qop, kvp, last, 1, None, None)) == \
+        P.PKVS_ERR_INVALID_ARG
+    qop, kvp, last = csr([5], [5], 16)
+    last[0] = 17
+    assert err_code(lambda: P.pkvs_prefill_plan(h, qop, kvp, last, 1, None, None)) == \
+        P.PKVS_ERR_INVALID_ARG
+    assert err_code(lambda: P.pkvs_prefill_plan(h, [0, 5], [0, 2, 1], [5, 5], 2, None, None)) == \
+        P.PKVS_ERR_INVALID_ARG
+
+
+def test_workspace_too_small_is_reported():
+    h = P.pkvs_plan_create(desc())
+    _, ib = P.pkvs_workspace_size(h)
+    qop, kvp, last = csr([5], [5], 16)
+    small = torch.empty(ib // 2, dtype=torch.uint8)
+    # the size check happens before any device copy
+    (qp, qt), (kp, kt), (lp, lt) = P._host_i32(qop), P._host_i32(kvp), P._host_i32(last)
+    rc = P._lib.pkvs_prefill_plan(h, qp, kp, lp, 1, None, 0, ctypes.c_void_p(small.data_ptr()),
+                                  small.numel(), None)
+    assert rc == P.PKVS_ERR_WORKSPACE, P.last_error()
+
+
+def test_run_rejects_a_window_other_than_the_planned_one():
+    """run(window_left != plan) fails before touching any data (sglang PR
+    'Pass window_left at plan time...', section What)."""
+    h = P.pkvs_plan_create(desc(window_left=31))
+    qop, kvp, last = csr([5], [5], 16)
+    P.pkvs_prefill_plan(h, qop, kvp, last, 1, None, None)
+    lib = P._lib
+    rc = lib.pkvs_prefill_run(h, None, None, None, 1, None, None, None, 1.0, 30, 1, None)
+    assert rc == P.PKVS_ERR_PLAN_MISMATCH
+    rc = lib.pkvs_prefill_run(h, None, None, None, 1, None, None, None, 1.0, 31, 0, None)
+    assert rc == P.PKVS_ERR_PLAN_MISMATCH
+    rc = lib.pkvs_prefill_run(h, None, None, None, 1, None, None, None, 1.0, 31, 1, None)
+    assert rc == P.PKVS_ERR_NOT_PLANNED  # a dry plan cannot run
+    hd = P.pkvs_plan_create(desc(P.PKVS_DECODE, num_qo_heads=4, window_left=0))
+    rc = lib.pkvs_decode_run(hd, None, None, None, 1, None, None, None, 1.0, -1, None)
+    assert rc == P.PKVS_ERR_PLAN_MISMATCH
+
+
+def test_workload_plans_fit_their_capacities():
+    """The five workloads plan within the workspaces their capacities give."""
+    for name in ("tiny_prefill", "prefix_prefill", "decode_sweep", "long_prefill",
+                 "split_decode"):
+        qo, kv = workload_lengths(name, torch.Generator().manual_seed(1), 12)
+        decode = name.endswith("decode") or name == "decode_sweep"
+        kind = P.PKVS_DECODE if decode else P.PKVS_PREFILL
+        dims = dict(tiny_prefill=(2, 1, 64, 4, torch.float32),
+                    prefix_prefill=(4, 1, 256, 16, torch.bfloat16),
+                    decode_sweep=(32, 8, 128, 16, torch.bfloat16),
+                    long_prefill=(32, 8, 128, 16, torch.bfloat16),
+                    split_decode=(64, 8, 128, 16, torch.bfloat16))[name]
+        h = P.pkvs_plan_create(desc(kind, num_qo_heads=dims[0], num_kv_heads=dims[1],
+                                    head_dim=dims[2], page_size=dims[3], dtype=dims[4],
+                                    window_left=4095, batch_capacity=len(kv),
+                                    qo_capacity=sum(qo), kv_capacity=max(kv),
+                                    fixed_split_size=2048 if name == "split_decode" else -1))
+        qop, kvp, last = csr(qo, kv, dims[3])
+        if decode:
+            P.pkvs_decode_plan(h, kvp, last, len(kv), None, None)
+        else:
+            P.pkvs_prefill_plan(h, qop, kvp, last, len(kv), None, None)
+        assert P.pkvs_plan_get_info(h).num_items > 0
+        P.pkvs_plan_destroy(h)
