@@ -103,7 +103,8 @@ def paged_attention(q, k_cache, v_cache, qo_indptr, kv_indptr, kv_indices, kv_la
 
     ``q``/``k_cache``/``v_cache`` are torch tensors (bf16 or fp32, any device;
     they are copied to the host).  Returns ``o`` ``[nnz_qo, H_q, D]`` and ``lse``
-    ``[nnz_qo, H_q]``; rows not listed in ``rows`` are NaN.
+    ``[nnz_qo, H_q]``; with ``rows`` (global query-token indices) the outputs
+    are compact: ``[len(rows), H_q, D]`` and ``[len(rows), H_q]``.
     """
     lib = (impl or _load()).lib
     qa, qd = _as_stored(q)
@@ -117,8 +118,9 @@ def paged_attention(q, k_cache, v_cache, qo_indptr, kv_indptr, kv_indices, kv_la
     last = _i32(kv_last_page_len)
     batch = len(kvp) - 1
     nnz_qo = int(qo[-1])
-    o = np.full((nnz_qo, num_qo_heads, head_dim), np.nan, dtype=np.float64)
-    lse = np.full((nnz_qo, num_qo_heads), np.nan, dtype=np.float64)
+    n_out = nnz_qo if rows is None else len(rows)
+    o = np.full((n_out, num_qo_heads, head_dim), np.nan, dtype=np.float64)
+    lse = np.full((n_out, num_qo_heads), np.nan, dtype=np.float64)
     if rows is not None:
         rows_a = np.ascontiguousarray(np.asarray(rows, dtype=np.int64))
         rp, nr = _ptr(rows_a), len(rows_a)

@@ -108,7 +108,8 @@ static int key_visible(int64_t j, int64_t p, int32_t causal, int32_t window_left
  *  Inputs are read in their stored type (ORACLE_BF16 as raw 16-bit words,
  *  ORACLE_FP32) and widened exactly.  o is [nnz_qo, H_q, D] double, lse is
  *  [nnz_qo, H_q] double.  rows (may be NULL) lists the global query-token
- *  indices to compute; other rows are left untouched.
+ *  indices to compute; then o and lse are compact, [n_rows, H_q, D] and
+ *  [n_rows, H_q], row r holding query token rows[r].
  *
  *  Returns 0 on success, -1 on a malformed layout, -2 when out of memory.
  */
@@ -155,9 +156,11 @@ int oracle_paged_attention(int32_t batch, const int32_t *qo_indptr, const int32_
         const int64_t qo_len = (int64_t)qo_indptr[b + 1] - qo_indptr[b];
         const int64_t p = (kv_len - qo_len) + (t - qo_indptr[b]);
 
+        const int64_t out_row = rows ? r : t;
         for (int32_t h = 0; h < num_qo_heads; ++h) {
             const int32_t hk = h / group;
             const int64_t qoff = (t * num_qo_heads + h) * (int64_t)head_dim;
+            const int64_t ooff = (out_row * num_qo_heads + h) * (int64_t)head_dim;
 
             /* logits of the visible keys, and their maximum */
             double m = -INFINITY;
@@ -189,15 +192,15 @@ int oracle_paged_attention(int32_t batch, const int32_t *qo_indptr, const int32_
                         acc[d] += w * load_elem(v_cache, in_dtype, voff + d);
                 }
             }
-            double *orow = o + qoff;
+            double *orow = o + ooff;
             if (l > 0.0) {
                 for (int32_t d = 0; d < head_dim; ++d)
                     orow[d] = acc[d] / l;
-                lse[t * num_qo_heads + h] = m + log(l);
+                lse[out_row * num_qo_heads + h] = m + log(l);
             } else {
                 for (int32_t d = 0; d < head_dim; ++d)
                     orow[d] = 0.0;
-                lse[t * num_qo_heads + h] = -INFINITY;
+                lse[out_row * num_qo_heads + h] = -INFINITY;
             }
         }
     }

@@ -22,8 +22,8 @@ MUTANTS = {
                            "const int64_t p = (t - qo_indptr[b]);"),
     "gqa_modulo_map": ("const int32_t hk = h / group;", "const int32_t hk = h % num_kv_heads;"),
     "scale_dropped": ("s[j] = sm_scale * dot;", "s[j] = dot;"),
-    "lse_base2": ("lse[t * num_qo_heads + h] = m + log(l);",
-                  "lse[t * num_qo_heads + h] = m + log2(l);"),
+    "lse_base2": ("lse[out_row * num_qo_heads + h] = m + log(l);",
+                  "lse[out_row * num_qo_heads + h] = m + log2(l);"),
     "max_not_subtracted": ("const double w = exp(s[j] - m);", "const double w = exp(s[j]);"),
     "slot_index": ("int64_t slot = j % page_size;", "int64_t slot = (j + 1) % page_size;"),
     "page_index": ("kv_indices[(int64_t)kv_indptr[b] + j / page_size]",
@@ -32,7 +32,8 @@ MUTANTS = {
                           "return npages * (int64_t)page_size;"),
     "values_from_keys": ("acc[d] += w * load_elem(v_cache, in_dtype, voff + d);",
                          "acc[d] += w * load_elem(k_cache, in_dtype, voff + d);"),
-    "empty_lse_zero": ("lse[t * num_qo_heads + h] = -INFINITY;", "lse[t * num_qo_heads + h] = 0.0;"),
+    "empty_lse_zero": ("lse[out_row * num_qo_heads + h] = -INFINITY;",
+                       "lse[out_row * num_qo_heads + h] = 0.0;"),
     "merge_weight_sign": ("const double wa = exp(a - s), wb = exp(b - s);",
                           "const double wa = exp(s - a), wb = exp(b - s);"),
     "merge_shift_dropped": ("const double s = M + log(exp(a - M) + exp(b - M));",
