@@ -52,8 +52,7 @@ constexpr int kMergeWords = 4;
 enum MergeEntry { kMeRequest = 0, kMeKvHead = 1, kMeFirstSlot = 2, kMeNumSlots = 3 };
 
 // ---------------------------------------------------------------- tiles
-constexpr int kPrefillRows = 128;      // (query token, head) rows per workgroup
-constexpr int kPrefillThreads = 256;   // 4 waves x 32 rows
+constexpr int kPrefillRowsPerWave = 32; // (query token, head) rows per wave
 constexpr int kPrefillKvTile = 32;     // keys per step
 constexpr int kGenericQTile = 16;      // fp32 path: query tokens per item
 constexpr int kGenericThreads = 256;
@@ -87,7 +86,8 @@ struct DecodeArgs {
 };
 
 // Launchers (return hipError_t of the launch).
-hipError_t launch_prefill_bf16(const PrefillArgs &a, int head_dim, int grid, hipStream_t s);
+hipError_t launch_prefill_bf16(const PrefillArgs &a, int head_dim, int waves, int grid,
+                               hipStream_t s);
 hipError_t launch_attention_fp32(const PrefillArgs &a, int head_dim, int grid, hipStream_t s);
 hipError_t launch_decode_bf16(const DecodeArgs &a, int head_dim, int grid, hipStream_t s);
 hipError_t launch_decode_merge(const DecodeArgs &a, int head_dim, int dtype, int grid,
@@ -97,7 +97,7 @@ hipError_t launch_merge_state(const void *va, const float *sa, const void *vb, c
                               int32_t dtype, int grid, hipStream_t s);
 
 // Resident workgroups per CU of each kernel (occupancy query; 0 if unknown).
-int prefill_bf16_blocks_per_cu(int head_dim);
+int prefill_bf16_blocks_per_cu(int head_dim, int waves);
 int decode_bf16_blocks_per_cu(int head_dim);
 
 }  // namespace pkvs

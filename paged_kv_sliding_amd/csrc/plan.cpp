@@ -390,11 +390,20 @@ int pkvs_plan_create(pkvs_plan **out, const pkvs_desc *desc)
     (void)hipGetLastError();
     const bool fp32 = desc->dtype == PKVS_FP32;
     if (desc->kind == PKVS_PREFILL) {
-        p->query_tile = fp32 ? kGenericQTile : kPrefillRows / group;
+        // 8-wave workgroups (256 rows) share each staged key tile between twice
+        // the rows and keep two waves per SIMD; 4-wave groups (128 rows) serve
+        // head_dim 256 and batches too small to fill the device with 256-row
+        // tiles.
+        const int64_t big_tiles =
+            ceil_div(desc->qo_capacity, 8 * kPrefillRowsPerWave / group) * desc->num_kv_heads;
+        p->prefill_waves = (!fp32 && desc->head_dim <= 128 && big_tiles >= 2 * p->num_cus) ? 8 : 4;
+        p->query_tile = fp32 ? kGenericQTile : p->prefill_waves * kPrefillRowsPerWave / group;
         p->item_words = kPrefillItemWords;
-        p->block_threads = fp32 ? kGenericThreads : kPrefillThreads;
-        int per_cu = p->have_gpu && !fp32 ? prefill_bf16_blocks_per_cu(desc->head_dim) : 0;
-        p->grid_blocks = p->num_cus * std::max(per_cu, 2);
+        p->block_threads = fp32 ? kGenericThreads : 64 * p->prefill_waves;
+        int per_cu = p->have_gpu && !fp32
+                         ? prefill_bf16_blocks_per_cu(desc->head_dim, p->prefill_waves)
+                         : 0;
+        p->grid_blocks = p->num_cus * std::max(per_cu, fp32 ? 2 : 1);
     } else {
         p->query_tile = 1;
         p->item_words = fp32 ? kPrefillItemWords : kDecodeItemWords;

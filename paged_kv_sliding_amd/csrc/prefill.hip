@@ -1,10 +1,11 @@
 // prefill.hip -- causal paged prefill (extend with a cached prefix) with the
 // exact sliding-window mask, for gfx950.
 //
-// bf16 path: one workgroup (4 waves) owns one work item = (request, kv head,
-// tile of 128/G query tokens).  The G query heads of the kv head are packed
-// with the tokens into 128 rows (row = token * G + head), so a K/V tile staged
-// in LDS serves all of them.  Each wave owns 32 rows and runs
+// bf16 path: one workgroup of NW = 4 or 8 waves owns one work item =
+// (request, kv head, tile of 32*NW/G query tokens).  The G query heads of the
+// kv head are packed with the tokens into 32*NW rows (row = token * G + head),
+// so a K/V tile staged in LDS serves all of them.  Each wave owns 32 rows and
+// runs
 //     S^T[32 keys x 32 rows] = K[32 keys x D] . Q^T[D x 32 rows]
 //     O^T[32 dims x 32 rows] += V^T[32 dims x 32 keys] . P^T[32 keys x 32 rows]
 // on v_mfma_f32_32x32x16_bf16.  With S^T (keys in M) every lane holds 16 keys
@@ -13,6 +14,11 @@
 // operand of the PV product.  K sits in LDS row-major (A operand reads 16
 // bytes of one key), V is transposed while it is staged (A operand reads
 // 8 bytes = 4 keys of one dim).
+//
+// Key tiles are double-buffered in LDS (one barrier per tile); the tile after
+// next is read from HBM into registers while the current one is multiplied.
+// The running row maximum is only moved (and O rescaled) when it grows by more
+// than 2^8, which most tiles never do.
 //
 // The key loop starts at the tile holding the window start of the item's
 // first query (the per-tile KV-start skip of the planner) and stops at the
@@ -34,133 +40,143 @@ namespace pkvs {
 namespace {
 
 constexpr int KT = kPrefillKvTile;
-constexpr int KPAD = 8;  // bf16 of padding per K row in LDS
-constexpr int VPAD = 4;  // bf16 of padding per V^T row in LDS (rows of 36 = 18 dwords)
+constexpr int KPAD = 8;                // bf16 of padding per K row in LDS
+constexpr int VPAD = 4;                // bf16 of padding per V^T row (rows of 36 = 18 dwords)
+constexpr float kRescaleLog2 = 8.0f;   // rescale O only when a row max grows by > 2^8
 
 template <int D>
-struct PrefillLds {
+struct PrefillBuf {
     uint16_t k[KT][D + KPAD];
     uint16_t vt[D][KT + VPAD];
 };
 
-template <int D>
-struct TileRegs {
-    static constexpr int KCH = KT * D / 8 / kPrefillThreads;   // 16-byte K chunks per thread
-    static constexpr int VBLK = (D + kPrefillThreads - 1) / kPrefillThreads;  // 4x8 V blocks
-    u32x4 k[KCH > 0 ? KCH : 1];
-    u32x4 v[VBLK][4];
+// Per-thread staging of one key tile: NW waves stage 32 keys of K (16-byte
+// chunks, row-major) and of V (blocks of 4 keys x 8 dims, transposed on the
+// way into LDS).  Row offsets are computed one tile before the loads that
+// use them, so the page-table read is off the critical path.
+template <int D, int NW>
+struct Stage {
+    static constexpr int T = NW * 64;
+    static constexpr int NCH = KT * D / 8;          // K chunks per tile
+    static constexpr int KCH = (NCH + T - 1) / T;   // per thread
+    static constexpr int VB = (D + T - 1) / T;      // V blocks per thread (D blocks per tile)
+    u32x4 k[KCH];
+    u32x4 v[VB][4];
+    int64_t koff[KCH];
+    int64_t voff[VB][4];
 };
 
-// Page ids of the keys this thread stages for one tile (K chunks and one V
-// block), fetched a tile ahead of the K/V loads that use them so the
-// dependent index load never sits on the critical path.
-template <int D>
-struct TilePages {
-    int64_t k[TileRegs<D>::KCH > 0 ? TileRegs<D>::KCH : 1];
-    int64_t v[4];
+struct RowAddr {
+    const int32_t *kv_indices;
+    int64_t num_pages, page_stride, slot_stride, head_off;
+    int page_base, log2_page, page_mask, kv_len;
+
+    // element offset of key `key` (clamped into the request) of this kv head
+    __device__ __forceinline__ int64_t operator()(int key) const
+    {
+        key = min(key, kv_len - 1);
+        int64_t pg = kv_indices[page_base + (key >> log2_page)];
+        pg = pg < 0 ? 0 : (pg >= num_pages ? num_pages - 1 : pg);
+        return pg * page_stride + int64_t(key & page_mask) * slot_stride + head_off;
+    }
 };
 
-template <int D>
-__device__ __forceinline__ void pages_load(TilePages<D> &pg, const PrefillArgs &a, int k0,
-                                           int kv_len, int page_base, int tid)
+template <int D, int NW>
+__device__ __forceinline__ void stage_offsets(Stage<D, NW> &st, const RowAddr &ra, int k0,
+                                              int tid)
 {
-    constexpr int KCH = TileRegs<D>::KCH;
+    using S = Stage<D, NW>;
     constexpr int CPR = D / 8;
 #pragma unroll
-    for (int i = 0; i < KCH; ++i) {
-        const int key = min(k0 + (tid + i * kPrefillThreads) / CPR, kv_len - 1);
-        pg.k[i] = page_of(a.kv_indices, page_base, max(key, 0), a.log2_page, a.num_pages);
+    for (int i = 0; i < S::KCH; ++i) {
+        const int c = tid + i * S::T;
+        st.koff[i] = ra(k0 + c / CPR) + (c % CPR) * 8;
     }
-    const int kq = tid & 7;
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-        const int key = min(k0 + 4 * kq + i, kv_len - 1);
-        pg.v[i] = (a.page_size >= 4 && i > 0)
-                      ? pg.v[0]
-                      : page_of(a.kv_indices, page_base, max(key, 0), a.log2_page, a.num_pages);
+    for (int bi = 0; bi < S::VB; ++bi) {
+        const int c = tid + bi * S::T;
+        const int kq = c & 7, ch = c >> 3;
+        if (ra.page_mask >= 3) {
+            // four keys from a multiple of 4 share a page
+            const int64_t base = ra(k0 + 4 * kq) + ch * 8;
+#pragma unroll
+            for (int i = 0; i < 4; ++i) st.voff[bi][i] = base + int64_t(i) * ra.slot_stride;
+        } else {
+#pragma unroll
+            for (int i = 0; i < 4; ++i) st.voff[bi][i] = ra(k0 + 4 * kq + i) + ch * 8;
+        }
     }
 }
 
-// Global -> registers for the key tile starting at k0, at the pages in pg.
-// Keys outside [0, kv_len) are zero-filled so that no unwritten slot (which
-// may hold any bits, even NaN) ever reaches the MFMA.
-template <int D>
-__device__ __forceinline__ void tile_load(TileRegs<D> &t, const TilePages<D> &pg,
-                                          const PrefillArgs &a, int k0, int kv_len, int hk,
-                                          int tid)
+// Global -> registers.  Keys at or past kv_len are zero-filled: no unwritten
+// slot (whatever its bits, even NaN) ever reaches an MFMA.
+template <int D, int NW>
+__device__ __forceinline__ void stage_load(Stage<D, NW> &st, const PrefillArgs &a, int k0,
+                                           int kv_len, int tid)
 {
-    constexpr int KCH = TileRegs<D>::KCH, VBLK = TileRegs<D>::VBLK;
-    constexpr int CPR = D / 8;  // 16-byte chunks per key row
+    using S = Stage<D, NW>;
+    constexpr int CPR = D / 8;
     const uint16_t *K = static_cast<const uint16_t *>(a.k);
     const uint16_t *V = static_cast<const uint16_t *>(a.v);
-    const int P = a.page_size;
 #pragma unroll
-    for (int i = 0; i < KCH; ++i) {
-        const int c = tid + i * kPrefillThreads;
-        const int key = k0 + c / CPR, ch = c % CPR;
-        t.k[i] = key < kv_len
-                     ? *reinterpret_cast<const u32x4 *>(
-                           K + nhd_offset(pg.k[i], key & (P - 1), P, hk, a.num_kv_heads, D) +
-                           ch * 8)
-                     : u32x4{0u, 0u, 0u, 0u};
+    for (int i = 0; i < S::KCH; ++i) {
+        const int c = tid + i * S::T;
+        const bool ok = (S::NCH % S::T == 0 || c < S::NCH) && k0 + c / CPR < kv_len;
+        st.k[i] = ok ? *reinterpret_cast<const u32x4 *>(K + st.koff[i]) : u32x4{0u, 0u, 0u, 0u};
     }
 #pragma unroll
-    for (int bi = 0; bi < VBLK; ++bi) {
-        const int c = tid + bi * kPrefillThreads;  // block: 4 keys x 8 dims
+    for (int bi = 0; bi < S::VB; ++bi) {
+        const int c = tid + bi * S::T;
         if (c < D) {
-            const int kq = c & 7, ch = c >> 3;
+            const int kq = c & 7;
 #pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                const int key = k0 + 4 * kq + i;
-                t.v[bi][i] = key < kv_len
-                                 ? *reinterpret_cast<const u32x4 *>(
-                                       V + nhd_offset(pg.v[i], key & (P - 1), P, hk,
-                                                      a.num_kv_heads, D) +
-                                       ch * 8)
-                                 : u32x4{0u, 0u, 0u, 0u};
-            }
+            for (int i = 0; i < 4; ++i)
+                st.v[bi][i] = k0 + 4 * kq + i < kv_len
+                                  ? *reinterpret_cast<const u32x4 *>(V + st.voff[bi][i])
+                                  : u32x4{0u, 0u, 0u, 0u};
         }
     }
 }
 
 // Registers -> LDS; V is transposed on the way (4 keys x 8 dims -> 8 rows of
 // 4 keys).
-template <int D>
-__device__ __forceinline__ void tile_store(const TileRegs<D> &t, PrefillLds<D> &s, int tid)
+template <int D, int NW>
+__device__ __forceinline__ void stage_store(const Stage<D, NW> &st, PrefillBuf<D> &b, int tid)
 {
-    constexpr int KCH = TileRegs<D>::KCH, VBLK = TileRegs<D>::VBLK;
+    using S = Stage<D, NW>;
     constexpr int CPR = D / 8;
 #pragma unroll
-    for (int i = 0; i < KCH; ++i) {
-        const int c = tid + i * kPrefillThreads;
-        *reinterpret_cast<u32x4 *>(&s.k[c / CPR][(c % CPR) * 8]) = t.k[i];
+    for (int i = 0; i < S::KCH; ++i) {
+        const int c = tid + i * S::T;
+        if (S::NCH % S::T == 0 || c < S::NCH)
+            *reinterpret_cast<u32x4 *>(&b.k[c / CPR][(c % CPR) * 8]) = st.k[i];
     }
 #pragma unroll
-    for (int bi = 0; bi < VBLK; ++bi) {
-        const int c = tid + bi * kPrefillThreads;
+    for (int bi = 0; bi < S::VB; ++bi) {
+        const int c = tid + bi * S::T;
         if (c < D) {
             const int kq = c & 7, ch = c >> 3;
 #pragma unroll
             for (int e = 0; e < 8; ++e) {
                 // dim ch*8+e of keys 4kq..4kq+3: 16-bit halves of the rows' dword e/2
                 const int sh = (e & 1) * 16;
-                const uint32_t x0 = (t.v[bi][0][e >> 1] >> sh) & 0xffffu;
-                const uint32_t x1 = (t.v[bi][1][e >> 1] >> sh) & 0xffffu;
-                const uint32_t x2 = (t.v[bi][2][e >> 1] >> sh) & 0xffffu;
-                const uint32_t x3 = (t.v[bi][3][e >> 1] >> sh) & 0xffffu;
-                *reinterpret_cast<u32x2 *>(&s.vt[ch * 8 + e][4 * kq]) =
+                const uint32_t x0 = (st.v[bi][0][e >> 1] >> sh) & 0xffffu;
+                const uint32_t x1 = (st.v[bi][1][e >> 1] >> sh) & 0xffffu;
+                const uint32_t x2 = (st.v[bi][2][e >> 1] >> sh) & 0xffffu;
+                const uint32_t x3 = (st.v[bi][3][e >> 1] >> sh) & 0xffffu;
+                *reinterpret_cast<u32x2 *>(&b.vt[ch * 8 + e][4 * kq]) =
                     u32x2{x0 | (x1 << 16), x2 | (x3 << 16)};
             }
         }
     }
 }
 
-template <int D>
-__global__ __launch_bounds__(kPrefillThreads) void prefill_bf16_kernel(PrefillArgs a)
+template <int D, int NW>
+__global__ __launch_bounds__(NW * 64) void prefill_bf16_kernel(PrefillArgs a)
 {
     constexpr int KSTEPS = D / 16;  // QK k-steps
     constexpr int DT = D / 32;      // O^T dim tiles
-    __shared__ __attribute__((aligned(16))) PrefillLds<D> lds;
+    __shared__ __attribute__((aligned(16))) PrefillBuf<D> lds[2];
 
     const int tid = threadIdx.x;
     const int wave = tid >> 6, lane = tid & 63, l32 = lane & 31, hw = lane >> 5;
@@ -168,16 +184,28 @@ __global__ __launch_bounds__(kPrefillThreads) void prefill_bf16_kernel(PrefillAr
     const int n_items = a.ws[kHdrNumItems];
     const uint16_t *Q = static_cast<const uint16_t *>(a.q);
     const int W = a.window_left;
+    const float c = a.scale_log2;
+
+    RowAddr ra;
+    ra.kv_indices = a.kv_indices;
+    ra.num_pages = a.num_pages;
+    ra.slot_stride = int64_t(a.num_kv_heads) * D;
+    ra.page_stride = ra.slot_stride * a.page_size;
+    ra.log2_page = a.log2_page;
+    ra.page_mask = a.page_size - 1;
 
     for (int it = blockIdx.x; it < n_items; it += gridDim.x) {
         const int32_t *w = a.ws + kHeaderWords + int64_t(it) * kPrefillItemWords;
         const int hk = w[kPiKvHead], q_begin = w[kPiQBegin], q_count = w[kPiQCount];
-        const int pos0 = w[kPiPos0], kv_len = w[kPiKvLen], page_base = w[kPiPageBase];
+        const int pos0 = w[kPiPos0], kv_len = w[kPiKvLen];
         const int kv_begin = w[kPiKvBegin];
         const int kv_end = a.causal ? min(kv_len, pos0 + q_count) : kv_len;
         const int pos_last = pos0 + q_count - 1;
+        ra.page_base = w[kPiPageBase];
+        ra.kv_len = kv_len;
+        ra.head_off = int64_t(hk) * D;
 
-        // this lane's row (both S^T and O^T keep one row per lane: column l32)
+        // this lane's row (S^T and O^T keep one row per lane: column l32)
         const int row = wave * 32 + l32;
         const int row_tok = row >> a.log2_group, row_head = row & (G - 1);
         const bool row_valid = row_tok < q_count;
@@ -197,95 +225,106 @@ __global__ __launch_bounds__(kPrefillThreads) void prefill_bf16_kernel(PrefillAr
 #pragma unroll
             for (int i = 0; i < 16; ++i) o[dt][i] = 0.f;
 
-        TileRegs<D> regs;
-        TilePages<D> pages;
+        Stage<D, NW> st;
         if (kv_begin < kv_end) {
-            pages_load<D>(pages, a, kv_begin, kv_len, page_base, tid);
-            tile_load<D>(regs, pages, a, kv_begin, kv_len, hk, tid);
-            pages_load<D>(pages, a, kv_begin + KT, kv_len, page_base, tid);
-        }
-
-        for (int k0 = kv_begin; k0 < kv_end; k0 += KT) {
-            __syncthreads();  // every wave is done reading the previous tile
-            tile_store<D>(regs, lds, tid);
-            __syncthreads();
-            if (k0 + KT < kv_end) {
-                tile_load<D>(regs, pages, a, k0 + KT, kv_len, hk, tid);
-                pages_load<D>(pages, a, k0 + 2 * KT, kv_len, page_base, tid);
+            // prologue: tile 0 into LDS buffer 0, tile 1 in flight, tile 2's rows known
+            stage_offsets(st, ra, kv_begin, tid);
+            stage_load(st, a, kv_begin, kv_len, tid);
+            stage_offsets(st, ra, kv_begin + KT, tid);
+            stage_store(st, lds[0], tid);
+            if (kv_begin + KT < kv_end) {
+                stage_load(st, a, kv_begin + KT, kv_len, tid);
+                stage_offsets(st, ra, kv_begin + 2 * KT, tid);
             }
+        }
+        __syncthreads();
+
+        int j = 0;
+        for (int k0 = kv_begin; k0 < kv_end; k0 += KT, ++j) {
+            const PrefillBuf<D> &cur = lds[j & 1];
 
             // S^T = K . Q^T
-            f32x16 sacc;
+            f32x16 s;
 #pragma unroll
-            for (int i = 0; i < 16; ++i) sacc[i] = 0.f;
+            for (int i = 0; i < 16; ++i) s[i] = 0.f;
 #pragma unroll
             for (int ks = 0; ks < KSTEPS; ++ks) {
-                const bf16x8 kf = *reinterpret_cast<const bf16x8 *>(&lds.k[l32][ks * 16 + hw * 8]);
-                sacc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf, qf[ks], sacc, 0, 0, 0);
+                const bf16x8 kf = *reinterpret_cast<const bf16x8 *>(&cur.k[l32][ks * 16 + hw * 8]);
+                s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf, qf[ks], s, 0, 0, 0);
             }
 
-            // key of accumulator entry i = 4*m0 + m1: k0 + 8*m0 + 4*hw + m1
+            // accumulator entry i holds key k0 + 8*(i/4) + 4*hw + i%4 of this row
             const bool interior = k0 + KT <= kv_len && (!a.causal || k0 + KT - 1 <= pos0) &&
                                   (W < 0 || k0 >= pos_last - W);
-            float x[16];
-            float mx = kNegInf;
-            if (interior) {
-#pragma unroll
-                for (int i = 0; i < 16; ++i) {
-                    x[i] = sacc[i] * a.scale_log2;
-                    mx = fmaxf(mx, x[i]);
-                }
-            } else {
+            if (!interior) {
 #pragma unroll
                 for (int i = 0; i < 16; ++i) {
                     const int key = k0 + 8 * (i >> 2) + 4 * hw + (i & 3);
                     const bool vis = key < kv_len && (!a.causal || key <= p_row) &&
                                      (W < 0 || key >= p_row - W);
-                    x[i] = vis ? sacc[i] * a.scale_log2 : kNegInf;
-                    mx = fmaxf(mx, x[i]);
+                    s[i] = vis ? s[i] : kNegInf;
                 }
             }
-            mx = fmaxf(mx, __shfl_xor(mx, 32));
-            const float m_new = fmaxf(m, mx);
-            const float m_use = m_new == kNegInf ? 0.f : m_new;
-            const float alpha = fast_exp2(m - m_use);
-            float rs = 0.f;
+            float mx = s[0];
+#pragma unroll
+            for (int i = 1; i < 16; ++i) mx = fmaxf(mx, s[i]);
+            mx = fmaxf(mx, __shfl_xor(mx, 32)) * c;
+
+            // lazy rescale: keep the running maximum unless some row's grows by
+            // more than 2^8 (probabilities then stay below 2^8, exact in fp32
+            // and bf16 range), so most tiles skip the O rescale
+            if (__any(mx > m + kRescaleLog2)) {
+                const float m_new = fmaxf(m, mx);
+                const float alpha = m_new == kNegInf ? 1.f : fast_exp2(m - m_new);
+                l *= alpha;
+#pragma unroll
+                for (int dt = 0; dt < DT; ++dt) o[dt] *= alpha;
+                m = m_new;
+            }
+            const float mu = m == kNegInf ? 0.f : m;
             f32x16 pr;
+            float rs = 0.f;
 #pragma unroll
             for (int i = 0; i < 16; ++i) {
-                pr[i] = fast_exp2(x[i] - m_use);
+                pr[i] = fast_exp2(__builtin_fmaf(s[i], c, -mu));
                 rs += pr[i];
             }
-            l = l * alpha + rs;
-            m = m_new;
+            l += rs;
 
             // O^T += V^T . P^T, two k-steps of 16 keys
 #pragma unroll
             for (int kk = 0; kk < 2; ++kk) {
                 f32x8 p8;
 #pragma unroll
-                for (int j = 0; j < 8; ++j) p8[j] = pr[8 * kk + j];
+                for (int jj = 0; jj < 8; ++jj) p8[jj] = pr[8 * kk + jj];
                 const bf16x8 pb = __builtin_convertvector(p8, bf16x8);
 #pragma unroll
                 for (int dt = 0; dt < DT; ++dt) {
                     const int d = dt * 32 + l32;
-                    const u32x2 lo = *reinterpret_cast<const u32x2 *>(&lds.vt[d][16 * kk + 4 * hw]);
+                    const u32x2 lo = *reinterpret_cast<const u32x2 *>(&cur.vt[d][16 * kk + 4 * hw]);
                     const u32x2 hi =
-                        *reinterpret_cast<const u32x2 *>(&lds.vt[d][16 * kk + 8 + 4 * hw]);
+                        *reinterpret_cast<const u32x2 *>(&cur.vt[d][16 * kk + 8 + 4 * hw]);
                     const bf16x8 va = __builtin_bit_cast(bf16x8, u32x4{lo[0], lo[1], hi[0], hi[1]});
-                    f32x16 c = o[dt];
-                    if (kk == 0) c *= alpha;
-                    o[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(va, pb, c, 0, 0, 0);
+                    o[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(va, pb, o[dt], 0, 0, 0);
                 }
             }
+
+            // stage tile j+1 into the other buffer, start loading tile j+2
+            if (k0 + KT < kv_end) {
+                stage_store(st, lds[(j + 1) & 1], tid);
+                if (k0 + 2 * KT < kv_end) {
+                    stage_load(st, a, k0 + 2 * KT, kv_len, tid);
+                    stage_offsets(st, ra, k0 + 3 * KT, tid);
+                }
+            }
+            __syncthreads();
         }
 
-        // epilogue: rows are split over the two half-waves' key sets
+        // epilogue: the two half-waves hold disjoint keys of each row
         l += __shfl_xor(l, 32);
         const float inv = l > 0.f ? 1.f / l : 0.f;
         if (row_valid) {
             uint16_t *O = static_cast<uint16_t *>(a.o);
-            const int64_t orow = qrow;
 #pragma unroll
             for (int dt = 0; dt < DT; ++dt)
 #pragma unroll
@@ -293,7 +332,7 @@ __global__ __launch_bounds__(kPrefillThreads) void prefill_bf16_kernel(PrefillAr
                     f32x4 v4;
 #pragma unroll
                     for (int m1 = 0; m1 < 4; ++m1) v4[m1] = o[dt][4 * m0 + m1] * inv;
-                    *reinterpret_cast<bf16x4 *>(O + orow + dt * 32 + 8 * m0 + 4 * hw) =
+                    *reinterpret_cast<bf16x4 *>(O + qrow + dt * 32 + 8 * m0 + 4 * hw) =
                         __builtin_convertvector(v4, bf16x4);
                 }
             if (a.lse && hw == 0)
@@ -358,13 +397,22 @@ __global__ __launch_bounds__(kGenericThreads) void attention_fp32_kernel(Prefill
 
 }  // namespace
 
-hipError_t launch_prefill_bf16(const PrefillArgs &a, int head_dim, int grid, hipStream_t s)
+hipError_t launch_prefill_bf16(const PrefillArgs &a, int head_dim, int waves, int grid,
+                               hipStream_t s)
 {
-    switch (head_dim) {
-    case 64: prefill_bf16_kernel<64><<<grid, kPrefillThreads, 0, s>>>(a); break;
-    case 128: prefill_bf16_kernel<128><<<grid, kPrefillThreads, 0, s>>>(a); break;
-    case 256: prefill_bf16_kernel<256><<<grid, kPrefillThreads, 0, s>>>(a); break;
-    default: return hipErrorInvalidValue;
+    if (waves == 8) {
+        switch (head_dim) {
+        case 64: prefill_bf16_kernel<64, 8><<<grid, 512, 0, s>>>(a); break;
+        case 128: prefill_bf16_kernel<128, 8><<<grid, 512, 0, s>>>(a); break;
+        default: return hipErrorInvalidValue;
+        }
+    } else {
+        switch (head_dim) {
+        case 64: prefill_bf16_kernel<64, 4><<<grid, 256, 0, s>>>(a); break;
+        case 128: prefill_bf16_kernel<128, 4><<<grid, 256, 0, s>>>(a); break;
+        case 256: prefill_bf16_kernel<256, 4><<<grid, 256, 0, s>>>(a); break;
+        default: return hipErrorInvalidValue;
+        }
     }
     return hipGetLastError();
 }
@@ -375,23 +423,22 @@ hipError_t launch_attention_fp32(const PrefillArgs &a, int head_dim, int grid, h
     return hipGetLastError();
 }
 
-int prefill_bf16_blocks_per_cu(int head_dim)
+int prefill_bf16_blocks_per_cu(int head_dim, int waves)
 {
     int n = 0;
     hipError_t e = hipErrorInvalidValue;
-    switch (head_dim) {
-    case 64:
-        e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, prefill_bf16_kernel<64>,
-                                                         kPrefillThreads, 0);
-        break;
-    case 128:
-        e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, prefill_bf16_kernel<128>,
-                                                         kPrefillThreads, 0);
-        break;
-    case 256:
-        e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, prefill_bf16_kernel<256>,
-                                                         kPrefillThreads, 0);
-        break;
+    if (waves == 8) {
+        if (head_dim == 64)
+            e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, prefill_bf16_kernel<64, 8>, 512, 0);
+        else if (head_dim == 128)
+            e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, prefill_bf16_kernel<128, 8>, 512, 0);
+    } else {
+        if (head_dim == 64)
+            e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, prefill_bf16_kernel<64, 4>, 256, 0);
+        else if (head_dim == 128)
+            e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, prefill_bf16_kernel<128, 4>, 256, 0);
+        else if (head_dim == 256)
+            e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, prefill_bf16_kernel<256, 4>, 256, 0);
     }
     return e == hipSuccess ? n : 0;
 }
