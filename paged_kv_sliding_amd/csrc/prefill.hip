@@ -11,12 +11,12 @@
 // on v_mfma_f32_32x32x16_bf16.  With S^T (keys in M) every lane holds 16 keys
 // of one row, so the row maximum and sum are lane-local plus one exchange
 // with the lane 32 away, and the probabilities are already laid out as the B
-// operand of the PV product.  K sits in LDS row-major (A operand reads 16
-// bytes of one key), V is transposed while it is staged (A operand reads
-// 8 bytes = 4 keys of one dim).
+// operand of the PV product.  K and V sit in LDS row-major; the V^T operand
+// comes from gfx950's transposing LDS read.
 //
-// Key tiles are double-buffered in LDS (one barrier per tile); the tile after
-// next is read from HBM into registers while the current one is multiplied.
+// Three key tiles are in flight in LDS (one barrier per tile): while tile j's
+// softmax runs, the MFMAs of tile j+1's S^T are already issued, tile j+2 is
+// being written to LDS and tile j+3 read from HBM into registers.
 // The running row maximum is only moved (and O rescaled) when it grows by more
 // than 2^8, which most tiles never do.
 //
@@ -40,30 +40,34 @@ namespace pkvs {
 namespace {
 
 constexpr int KT = kPrefillKvTile;
-constexpr int KPAD = 8;                // bf16 of padding per K row in LDS
-constexpr int VPAD = 4;                // bf16 of padding per V^T row (rows of 36 = 18 dwords)
+constexpr int KPAD = 8;                // K rows: D+8 bf16, a stride of 4 dwords mod 64 banks
+constexpr int VPAD = 32;               // V rows: D+32 bf16, a stride of 16 dwords mod 64 banks
+constexpr int NBUF = 3;                // LDS tile sets in flight
 constexpr float kRescaleLog2 = 8.0f;   // rescale O only when a row max grows by > 2^8
 
+typedef short i16x4 __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) i16x4 lds_i16x4;
+
+// One key tile in LDS, K and V both row-major.  The A operand of S^T = K.Q^T
+// is a plain 16-byte read of a key row.  The A operand of O^T = V^T.P^T needs
+// 8 keys of one dim per lane; gfx950's transposing LDS read provides it: in
+// each 16-lane group, the lane 4e+q that points at V[k0+e][d0+4q] makes lane
+// i receive V[k0..k0+3][d0 + i mod 16].
 template <int D>
 struct PrefillBuf {
     uint16_t k[KT][D + KPAD];
-    uint16_t vt[D][KT + VPAD];
+    uint16_t v[KT][D + VPAD];
 };
 
-// Per-thread staging of one key tile: NW waves stage 32 keys of K (16-byte
-// chunks, row-major) and of V (blocks of 4 keys x 8 dims, transposed on the
-// way into LDS).  Row offsets are computed one tile before the loads that
-// use them, so the page-table read is off the critical path.
+// Per-thread staging of one key tile: the NW*64 threads copy the tile's K and
+// V rows in 16-byte chunks (chunk c: key c / (D/8), dims 8*(c % (D/8))).
 template <int D, int NW>
 struct Stage {
     static constexpr int T = NW * 64;
-    static constexpr int NCH = KT * D / 8;          // K chunks per tile
+    static constexpr int NCH = KT * D / 8;          // chunks per tile and tensor
     static constexpr int KCH = (NCH + T - 1) / T;   // per thread
-    static constexpr int VB = (D + T - 1) / T;      // V blocks per thread (D blocks per tile)
-    u32x4 k[KCH];
-    u32x4 v[VB][4];
-    int64_t koff[KCH];
-    int64_t voff[VB][4];
+    u32x4 k[KCH], v[KCH];
+    int64_t off[KCH];  // element offset of the chunk in the cache (same for K and V)
 };
 
 struct RowAddr {
@@ -82,6 +86,13 @@ struct RowAddr {
 };
 
 template <int D, int NW>
+__device__ __forceinline__ bool chunk_exists(int c)
+{
+    using S = Stage<D, NW>;
+    return S::NCH % S::T == 0 || c < S::NCH;
+}
+
+template <int D, int NW>
 __device__ __forceinline__ void stage_offsets(Stage<D, NW> &st, const RowAddr &ra, int k0,
                                               int tid)
 {
@@ -90,21 +101,7 @@ __device__ __forceinline__ void stage_offsets(Stage<D, NW> &st, const RowAddr &r
 #pragma unroll
     for (int i = 0; i < S::KCH; ++i) {
         const int c = tid + i * S::T;
-        st.koff[i] = ra(k0 + c / CPR) + (c % CPR) * 8;
-    }
-#pragma unroll
-    for (int bi = 0; bi < S::VB; ++bi) {
-        const int c = tid + bi * S::T;
-        const int kq = c & 7, ch = c >> 3;
-        if (ra.page_mask >= 3) {
-            // four keys from a multiple of 4 share a page
-            const int64_t base = ra(k0 + 4 * kq) + ch * 8;
-#pragma unroll
-            for (int i = 0; i < 4; ++i) st.voff[bi][i] = base + int64_t(i) * ra.slot_stride;
-        } else {
-#pragma unroll
-            for (int i = 0; i < 4; ++i) st.voff[bi][i] = ra(k0 + 4 * kq + i) + ch * 8;
-        }
+        st.off[i] = ra(k0 + c / CPR) + (c % CPR) * 8;
     }
 }
 
@@ -121,25 +118,13 @@ __device__ __forceinline__ void stage_load(Stage<D, NW> &st, const PrefillArgs &
 #pragma unroll
     for (int i = 0; i < S::KCH; ++i) {
         const int c = tid + i * S::T;
-        const bool ok = (S::NCH % S::T == 0 || c < S::NCH) && k0 + c / CPR < kv_len;
-        st.k[i] = ok ? *reinterpret_cast<const u32x4 *>(K + st.koff[i]) : u32x4{0u, 0u, 0u, 0u};
-    }
-#pragma unroll
-    for (int bi = 0; bi < S::VB; ++bi) {
-        const int c = tid + bi * S::T;
-        if (c < D) {
-            const int kq = c & 7;
-#pragma unroll
-            for (int i = 0; i < 4; ++i)
-                st.v[bi][i] = k0 + 4 * kq + i < kv_len
-                                  ? *reinterpret_cast<const u32x4 *>(V + st.voff[bi][i])
-                                  : u32x4{0u, 0u, 0u, 0u};
-        }
+        const bool ok = chunk_exists<D, NW>(c) && k0 + c / CPR < kv_len;
+        const u32x4 z = {0u, 0u, 0u, 0u};
+        st.k[i] = ok ? *reinterpret_cast<const u32x4 *>(K + st.off[i]) : z;
+        st.v[i] = ok ? *reinterpret_cast<const u32x4 *>(V + st.off[i]) : z;
     }
 }
 
-// Registers -> LDS; V is transposed on the way (4 keys x 8 dims -> 8 rows of
-// 4 keys).
 template <int D, int NW>
 __device__ __forceinline__ void stage_store(const Stage<D, NW> &st, PrefillBuf<D> &b, int tid)
 {
@@ -148,27 +133,27 @@ __device__ __forceinline__ void stage_store(const Stage<D, NW> &st, PrefillBuf<D
 #pragma unroll
     for (int i = 0; i < S::KCH; ++i) {
         const int c = tid + i * S::T;
-        if (S::NCH % S::T == 0 || c < S::NCH)
+        if (chunk_exists<D, NW>(c)) {
             *reinterpret_cast<u32x4 *>(&b.k[c / CPR][(c % CPR) * 8]) = st.k[i];
-    }
-#pragma unroll
-    for (int bi = 0; bi < S::VB; ++bi) {
-        const int c = tid + bi * S::T;
-        if (c < D) {
-            const int kq = c & 7, ch = c >> 3;
-#pragma unroll
-            for (int e = 0; e < 8; ++e) {
-                // dim ch*8+e of keys 4kq..4kq+3: 16-bit halves of the rows' dword e/2
-                const int sh = (e & 1) * 16;
-                const uint32_t x0 = (st.v[bi][0][e >> 1] >> sh) & 0xffffu;
-                const uint32_t x1 = (st.v[bi][1][e >> 1] >> sh) & 0xffffu;
-                const uint32_t x2 = (st.v[bi][2][e >> 1] >> sh) & 0xffffu;
-                const uint32_t x3 = (st.v[bi][3][e >> 1] >> sh) & 0xffffu;
-                *reinterpret_cast<u32x2 *>(&b.vt[ch * 8 + e][4 * kq]) =
-                    u32x2{x0 | (x1 << 16), x2 | (x3 << 16)};
-            }
+            *reinterpret_cast<u32x4 *>(&b.v[c / CPR][(c % CPR) * 8]) = st.v[i];
         }
     }
+}
+
+// S^T[32 keys x 32 rows] = K . Q^T for the tile in b.
+template <int D>
+__device__ __forceinline__ f32x16 qk_tile(const PrefillBuf<D> &b, const bf16x8 (&qf)[D / 16],
+                                          int l32, int hw)
+{
+    f32x16 s;
+#pragma unroll
+    for (int i = 0; i < 16; ++i) s[i] = 0.f;
+#pragma unroll
+    for (int ks = 0; ks < D / 16; ++ks) {
+        const bf16x8 kf = *reinterpret_cast<const bf16x8 *>(&b.k[l32][ks * 16 + hw * 8]);
+        s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf, qf[ks], s, 0, 0, 0);
+    }
+    return s;
 }
 
 template <int D, int NW>
@@ -176,7 +161,7 @@ __global__ __launch_bounds__(NW * 64) void prefill_bf16_kernel(PrefillArgs a)
 {
     constexpr int KSTEPS = D / 16;  // QK k-steps
     constexpr int DT = D / 32;      // O^T dim tiles
-    __shared__ __attribute__((aligned(16))) PrefillBuf<D> lds[2];
+    __shared__ __attribute__((aligned(16))) PrefillBuf<D> lds[NBUF];
 
     const int tid = threadIdx.x;
     const int wave = tid >> 6, lane = tid & 63, l32 = lane & 31, hw = lane >> 5;
@@ -185,6 +170,10 @@ __global__ __launch_bounds__(NW * 64) void prefill_bf16_kernel(PrefillArgs a)
     const uint16_t *Q = static_cast<const uint16_t *>(a.q);
     const int W = a.window_left;
     const float c = a.scale_log2;
+
+    // transposing-read coordinates of this lane (see PrefillBuf)
+    const int tr_key = 4 * hw + ((lane & 15) >> 2);             // + 16*kk (+8)
+    const int tr_dim = 16 * ((lane >> 4) & 1) + 4 * (lane & 3);  // + 32*dt
 
     RowAddr ra;
     ra.kv_indices = a.kv_indices;
@@ -201,6 +190,7 @@ __global__ __launch_bounds__(NW * 64) void prefill_bf16_kernel(PrefillArgs a)
         const int kv_begin = w[kPiKvBegin];
         const int kv_end = a.causal ? min(kv_len, pos0 + q_count) : kv_len;
         const int pos_last = pos0 + q_count - 1;
+        const int ntiles = kv_end > kv_begin ? (kv_end - kv_begin + KT - 1) / KT : 0;
         ra.page_base = w[kPiPageBase];
         ra.kv_len = kv_len;
         ra.head_off = int64_t(hk) * D;
@@ -225,35 +215,41 @@ __global__ __launch_bounds__(NW * 64) void prefill_bf16_kernel(PrefillArgs a)
 #pragma unroll
             for (int i = 0; i < 16; ++i) o[dt][i] = 0.f;
 
+        // prologue: tiles 0 and 1 in LDS sets 0 and 1, tile 2 in registers,
+        // tile 3's rows known
         Stage<D, NW> st;
-        if (kv_begin < kv_end) {
-            // prologue: tile 0 into LDS buffer 0, tile 1 in flight, tile 2's rows known
+        if (ntiles > 0) {
             stage_offsets(st, ra, kv_begin, tid);
             stage_load(st, a, kv_begin, kv_len, tid);
-            stage_offsets(st, ra, kv_begin + KT, tid);
             stage_store(st, lds[0], tid);
-            if (kv_begin + KT < kv_end) {
+            if (ntiles > 1) {
+                stage_offsets(st, ra, kv_begin + KT, tid);
                 stage_load(st, a, kv_begin + KT, kv_len, tid);
                 stage_offsets(st, ra, kv_begin + 2 * KT, tid);
+                stage_store(st, lds[1], tid);
+                if (ntiles > 2) {
+                    stage_load(st, a, kv_begin + 2 * KT, kv_len, tid);
+                    stage_offsets(st, ra, kv_begin + 3 * KT, tid);
+                }
             }
         }
         __syncthreads();
+        f32x16 s_cur;
+        if (ntiles > 0) s_cur = qk_tile<D>(lds[0], qf, l32, hw);
 
-        int j = 0;
-        for (int k0 = kv_begin; k0 < kv_end; k0 += KT, ++j) {
-            const PrefillBuf<D> &cur = lds[j & 1];
+        int cur = 0;  // LDS set of tile j
+        for (int j = 0; j < ntiles; ++j) {
+            const int k0 = kv_begin + j * KT;
+            const int nxt = cur == NBUF - 1 ? 0 : cur + 1;
+            const int nn = nxt == NBUF - 1 ? 0 : nxt + 1;
 
-            // S^T = K . Q^T
-            f32x16 s;
-#pragma unroll
-            for (int i = 0; i < 16; ++i) s[i] = 0.f;
-#pragma unroll
-            for (int ks = 0; ks < KSTEPS; ++ks) {
-                const bf16x8 kf = *reinterpret_cast<const bf16x8 *>(&cur.k[l32][ks * 16 + hw * 8]);
-                s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf, qf[ks], s, 0, 0, 0);
-            }
+            // S^T of tile j+1 goes to the matrix cores while this tile's softmax
+            // runs on the vector ALUs
+            f32x16 s_nxt;
+            if (j + 1 < ntiles) s_nxt = qk_tile<D>(lds[nxt], qf, l32, hw);
 
             // accumulator entry i holds key k0 + 8*(i/4) + 4*hw + i%4 of this row
+            f32x16 s = s_cur;
             const bool interior = k0 + KT <= kv_len && (!a.causal || k0 + KT - 1 <= pos0) &&
                                   (W < 0 || k0 >= pos_last - W);
             if (!interior) {
@@ -265,14 +261,14 @@ __global__ __launch_bounds__(NW * 64) void prefill_bf16_kernel(PrefillArgs a)
                     s[i] = vis ? s[i] : kNegInf;
                 }
             }
-            float mx = s[0];
+            float mx = fmaxf(s[0], s[1]);
 #pragma unroll
-            for (int i = 1; i < 16; ++i) mx = fmaxf(mx, s[i]);
+            for (int i = 2; i < 16; i += 2) mx = fmaxf(mx, fmaxf(s[i], s[i + 1]));
             mx = fmaxf(mx, __shfl_xor(mx, 32)) * c;
 
             // lazy rescale: keep the running maximum unless some row's grows by
             // more than 2^8 (probabilities then stay below 2^8, exact in fp32
-            // and bf16 range), so most tiles skip the O rescale
+            // and in bf16 range), so most tiles skip the O rescale
             if (__any(mx > m + kRescaleLog2)) {
                 const float m_new = fmaxf(m, mx);
                 const float alpha = m_new == kNegInf ? 1.f : fast_exp2(m - m_new);
@@ -292,6 +288,7 @@ __global__ __launch_bounds__(NW * 64) void prefill_bf16_kernel(PrefillArgs a)
             l += rs;
 
             // O^T += V^T . P^T, two k-steps of 16 keys
+            const PrefillBuf<D> &bj = lds[cur];
 #pragma unroll
             for (int kk = 0; kk < 2; ++kk) {
                 f32x8 p8;
@@ -300,24 +297,27 @@ __global__ __launch_bounds__(NW * 64) void prefill_bf16_kernel(PrefillArgs a)
                 const bf16x8 pb = __builtin_convertvector(p8, bf16x8);
 #pragma unroll
                 for (int dt = 0; dt < DT; ++dt) {
-                    const int d = dt * 32 + l32;
-                    const u32x2 lo = *reinterpret_cast<const u32x2 *>(&cur.vt[d][16 * kk + 4 * hw]);
-                    const u32x2 hi =
-                        *reinterpret_cast<const u32x2 *>(&cur.vt[d][16 * kk + 8 + 4 * hw]);
-                    const bf16x8 va = __builtin_bit_cast(bf16x8, u32x4{lo[0], lo[1], hi[0], hi[1]});
+                    const uint16_t *v0 = &bj.v[16 * kk + tr_key][32 * dt + tr_dim];
+                    const i16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4 *)v0);
+                    const i16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+                        (lds_i16x4 *)(v0 + 8 * (D + VPAD)));
+                    const bf16x8 va = __builtin_bit_cast(
+                        bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
                     o[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(va, pb, o[dt], 0, 0, 0);
                 }
             }
 
-            // stage tile j+1 into the other buffer, start loading tile j+2
-            if (k0 + KT < kv_end) {
-                stage_store(st, lds[(j + 1) & 1], tid);
-                if (k0 + 2 * KT < kv_end) {
-                    stage_load(st, a, k0 + 2 * KT, kv_len, tid);
-                    stage_offsets(st, ra, k0 + 3 * KT, tid);
+            // stage tile j+2 into the free LDS set, start loading tile j+3
+            if (j + 2 < ntiles) {
+                stage_store(st, lds[nn], tid);
+                if (j + 3 < ntiles) {
+                    stage_load(st, a, k0 + 3 * KT, kv_len, tid);
+                    stage_offsets(st, ra, k0 + 4 * KT, tid);
                 }
             }
             __syncthreads();
+            s_cur = s_nxt;
+            cur = nxt;
         }
 
         // epilogue: the two half-waves hold disjoint keys of each row
@@ -339,6 +339,7 @@ __global__ __launch_bounds__(NW * 64) void prefill_bf16_kernel(PrefillArgs a)
                 a.lse[int64_t(q_begin + row_tok) * a.num_qo_heads + hk * G + row_head] =
                     l > 0.f ? (m + fast_log2(l)) * kLn2 : kNegInf;
         }
+        __syncthreads();  // the next item's prologue overwrites LDS set 0
     }
 }
 
