@@ -88,6 +88,10 @@ typedef enum pkvs_kind { PKVS_PREFILL = 0, PKVS_DECODE = 1 } pkvs_kind;
  *                   the planner choose; the partial (o, lse) of the chunks of
  *                   one request are combined by the merge of pkvs_merge_state
  *  disable_split_kv decode: 1 = one chunk per request
+ *  prefill_variant  prefill kernel shape: 0 = planner's choice (from head_dim and
+ *                   qo_capacity), 1 = 4 waves x 32 rows, 2 = 8 waves x 32 rows,
+ *                   3 = 4 waves x 64 rows, software-pipelined (2 and 3: head_dim
+ *                   <= 128); rows are (query token, head) pairs
  *  batch_capacity   largest batch a plan() call may describe
  *  qo_capacity      prefill: largest total number of query tokens
  *  kv_capacity      largest kv_len of one request
@@ -106,7 +110,7 @@ typedef struct pkvs_desc {
     int32_t fixed_split_size;
     int32_t disable_split_kv;
     int32_t batch_capacity;
-    int32_t reserved;
+    int32_t prefill_variant;
     int64_t qo_capacity;
     int64_t kv_capacity;
 } pkvs_desc;

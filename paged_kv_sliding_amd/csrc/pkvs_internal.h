@@ -52,7 +52,13 @@ constexpr int kMergeWords = 4;
 enum MergeEntry { kMeRequest = 0, kMeKvHead = 1, kMeFirstSlot = 2, kMeNumSlots = 3 };
 
 // ---------------------------------------------------------------- tiles
-constexpr int kPrefillRowsPerWave = 32; // (query token, head) rows per wave
+// bf16 prefill kernel variants (rows = (query token, head) pairs per workgroup)
+enum PrefillVariant {
+    kPrefillAuto = 0,
+    kPrefillRows128 = 1,  // 4 waves x 32 rows
+    kPrefillRows256 = 2,  // 8 waves x 32 rows
+    kPrefillWide = 3,     // 4 waves x 64 rows, software-pipelined (head_dim <= 128)
+};
 constexpr int kPrefillKvTile = 32;     // keys per step
 constexpr int kGenericQTile = 16;      // fp32 path: query tokens per item
 constexpr int kGenericThreads = 256;
@@ -86,7 +92,7 @@ struct DecodeArgs {
 };
 
 // Launchers (return hipError_t of the launch).
-hipError_t launch_prefill_bf16(const PrefillArgs &a, int head_dim, int waves, int grid,
+hipError_t launch_prefill_bf16(const PrefillArgs &a, int head_dim, int variant, int grid,
                                hipStream_t s);
 hipError_t launch_attention_fp32(const PrefillArgs &a, int head_dim, int grid, hipStream_t s);
 hipError_t launch_decode_bf16(const DecodeArgs &a, int head_dim, int grid, hipStream_t s);
@@ -97,7 +103,7 @@ hipError_t launch_merge_state(const void *va, const float *sa, const void *vb, c
                               int32_t dtype, int grid, hipStream_t s);
 
 // Resident workgroups per CU of each kernel (occupancy query; 0 if unknown).
-int prefill_bf16_blocks_per_cu(int head_dim, int waves);
+int prefill_bf16_blocks_per_cu(int head_dim, int variant);
 int decode_bf16_blocks_per_cu(int head_dim);
 
 }  // namespace pkvs

@@ -121,6 +121,10 @@ static int validate_desc(const pkvs_desc *d)
                                       d->fixed_split_size % kDecodeBlock))
         return fail(PKVS_ERR_INVALID_ARG, "fixed_split_size %d must be -1 or a positive "
                     "multiple of %d", d->fixed_split_size, kDecodeBlock);
+    if (d->prefill_variant < 0 || d->prefill_variant > 3)
+        return fail(PKVS_ERR_INVALID_ARG, "prefill_variant %d must be 0..3", d->prefill_variant);
+    if (d->prefill_variant > 1 && d->head_dim > 128)
+        return fail(PKVS_ERR_UNSUPPORTED, "256-row prefill variants are built for head_dim <= 128");
     if (d->batch_capacity <= 0 || d->kv_capacity <= 0 ||
         (d->kind == PKVS_PREFILL && d->qo_capacity <= 0))
         return fail(PKVS_ERR_INVALID_ARG, "capacities must be positive");
@@ -390,19 +394,21 @@ int pkvs_plan_create(pkvs_plan **out, const pkvs_desc *desc)
     (void)hipGetLastError();
     const bool fp32 = desc->dtype == PKVS_FP32;
     if (desc->kind == PKVS_PREFILL) {
-        // 8-wave workgroups (256 rows) share each staged key tile between twice
-        // the rows and keep two waves per SIMD; 4-wave groups (128 rows) serve
-        // head_dim 256 and batches too small to fill the device with 256-row
-        // tiles.
-        const int64_t big_tiles =
-            ceil_div(desc->qo_capacity, 8 * kPrefillRowsPerWave / group) * desc->num_kv_heads;
-        p->prefill_waves = (!fp32 && desc->head_dim <= 128 && big_tiles >= 2 * p->num_cus) ? 8 : 4;
-        p->query_tile = fp32 ? kGenericQTile : p->prefill_waves * kPrefillRowsPerWave / group;
+        // Kernel variant: 256-row workgroups (8 waves x 32 rows) share each
+        // staged key tile between more rows and keep two waves per SIMD; they
+        // are the fastest measured for head_dim <= 128.  128-row workgroups
+        // serve head_dim 256 and batches too small to fill the device with
+        // 256-row tiles.  The wide variant is available on request.
+        const int64_t big_tiles = ceil_div(desc->qo_capacity, 256 / group) * desc->num_kv_heads;
+        int v = kPrefillRows128;
+        if (desc->head_dim <= 128 && big_tiles >= 2 * p->num_cus) v = kPrefillRows256;
+        if (desc->prefill_variant) v = desc->prefill_variant;
+        p->prefill_variant = v;
+        const int rows = v == kPrefillRows128 ? 128 : 256;
+        p->query_tile = fp32 ? kGenericQTile : rows / group;
         p->item_words = kPrefillItemWords;
-        p->block_threads = fp32 ? kGenericThreads : 64 * p->prefill_waves;
-        int per_cu = p->have_gpu && !fp32
-                         ? prefill_bf16_blocks_per_cu(desc->head_dim, p->prefill_waves)
-                         : 0;
+        p->block_threads = fp32 ? kGenericThreads : (v == kPrefillRows256 ? 512 : 256);
+        int per_cu = p->have_gpu && !fp32 ? prefill_bf16_blocks_per_cu(desc->head_dim, v) : 0;
         p->grid_blocks = p->num_cus * std::max(per_cu, fp32 ? 2 : 1);
     } else {
         p->query_tile = 1;

@@ -26,7 +26,7 @@ struct pkvs_plan {
     bool have_gpu = false;
     int num_cus = 0;
     int grid_blocks = 0, block_threads = 0, query_tile = 0, item_words = 0;
-    int prefill_waves = 4;  // waves per prefill workgroup (4 or 8)
+    int prefill_variant = 1;  // bf16 prefill kernel variant (PrefillVariant)
     int64_t auto_target_items = 0;
     int64_t items_cap = 0, slots_cap = 0, merges_cap = 0;
     size_t int_ws_need = 0, float_ws_need = 0;

@@ -60,14 +60,17 @@ struct PrefillBuf {
 };
 
 // Per-thread staging of one key tile: the NW*64 threads copy the tile's K and
-// V rows in 16-byte chunks (chunk c: key c / (D/8), dims 8*(c % (D/8))).
+// V rows in 16-byte chunks (chunk c: key c / (D/8), dims 8*(c % (D/8))).  The
+// page ids of a tile are read one tile before its K/V loads and kept raw: the
+// address arithmetic that needs them runs only when the loads are issued, so
+// no wait on the page-table read sits behind freshly issued K/V loads.
 template <int D, int NW>
 struct Stage {
     static constexpr int T = NW * 64;
     static constexpr int NCH = KT * D / 8;          // chunks per tile and tensor
     static constexpr int KCH = (NCH + T - 1) / T;   // per thread
     u32x4 k[KCH], v[KCH];
-    int64_t off[KCH];  // element offset of the chunk in the cache (same for K and V)
+    int32_t page[KCH];  // page id of the chunk's key (next tile to load)
 };
 
 struct RowAddr {
@@ -75,13 +78,17 @@ struct RowAddr {
     int64_t num_pages, page_stride, slot_stride, head_off;
     int page_base, log2_page, page_mask, kv_len;
 
-    // element offset of key `key` (clamped into the request) of this kv head
-    __device__ __forceinline__ int64_t operator()(int key) const
+    __device__ __forceinline__ int clamp_key(int key) const { return min(key, kv_len - 1); }
+    __device__ __forceinline__ int32_t page_id(int key) const
     {
-        key = min(key, kv_len - 1);
-        int64_t pg = kv_indices[page_base + (key >> log2_page)];
-        pg = pg < 0 ? 0 : (pg >= num_pages ? num_pages - 1 : pg);
-        return pg * page_stride + int64_t(key & page_mask) * slot_stride + head_off;
+        return kv_indices[page_base + (clamp_key(key) >> log2_page)];
+    }
+    // element offset of `key` (clamped into the request) on page `pg`
+    __device__ __forceinline__ int64_t offset(int32_t pg, int key) const
+    {
+        const int32_t p = min(max(pg, 0), int32_t(num_pages - 1));
+        return int64_t(p) * page_stride +
+               int32_t((clamp_key(key) & page_mask) * int32_t(slot_stride) + int32_t(head_off));
     }
 };
 
@@ -93,36 +100,70 @@ __device__ __forceinline__ bool chunk_exists(int c)
 }
 
 template <int D, int NW>
-__device__ __forceinline__ void stage_offsets(Stage<D, NW> &st, const RowAddr &ra, int k0,
-                                              int tid)
+__device__ __forceinline__ void stage_pages(Stage<D, NW> &st, const RowAddr &ra, int k0, int tid)
 {
     using S = Stage<D, NW>;
     constexpr int CPR = D / 8;
 #pragma unroll
-    for (int i = 0; i < S::KCH; ++i) {
-        const int c = tid + i * S::T;
-        st.off[i] = ra(k0 + c / CPR) + (c % CPR) * 8;
-    }
+    for (int i = 0; i < S::KCH; ++i) st.page[i] = ra.page_id(k0 + (tid + i * S::T) / CPR);
 }
 
 // Global -> registers.  Keys at or past kv_len are zero-filled: no unwritten
 // slot (whatever its bits, even NaN) ever reaches an MFMA.
 template <int D, int NW>
-__device__ __forceinline__ void stage_load(Stage<D, NW> &st, const PrefillArgs &a, int k0,
-                                           int kv_len, int tid)
+__device__ __forceinline__ void stage_load(Stage<D, NW> &st, const PrefillArgs &a,
+                                           const RowAddr &ra, int k0, int tid)
 {
     using S = Stage<D, NW>;
     constexpr int CPR = D / 8;
     const uint16_t *K = static_cast<const uint16_t *>(a.k);
     const uint16_t *V = static_cast<const uint16_t *>(a.v);
+    if (k0 + KT <= ra.kv_len) {
+        // the whole tile is inside the request (the common case)
+#pragma unroll
+        for (int i = 0; i < S::KCH; ++i) {
+            const int c = tid + i * S::T;
+            if (chunk_exists<D, NW>(c)) {
+                const int64_t off = ra.offset(st.page[i], k0 + c / CPR) + (c % CPR) * 8;
+                st.k[i] = *reinterpret_cast<const u32x4 *>(K + off);
+                st.v[i] = *reinterpret_cast<const u32x4 *>(V + off);
+            }
+        }
+        return;
+    }
 #pragma unroll
     for (int i = 0; i < S::KCH; ++i) {
         const int c = tid + i * S::T;
-        const bool ok = chunk_exists<D, NW>(c) && k0 + c / CPR < kv_len;
+        const int key = k0 + c / CPR;
+        const bool ok = chunk_exists<D, NW>(c) && key < ra.kv_len;
+        const int64_t off = ra.offset(st.page[i], key) + (c % CPR) * 8;
         const u32x4 z = {0u, 0u, 0u, 0u};
-        st.k[i] = ok ? *reinterpret_cast<const u32x4 *>(K + st.off[i]) : z;
-        st.v[i] = ok ? *reinterpret_cast<const u32x4 *>(V + st.off[i]) : z;
+        st.k[i] = ok ? *reinterpret_cast<const u32x4 *>(K + off) : z;
+        st.v[i] = ok ? *reinterpret_cast<const u32x4 *>(V + off) : z;
     }
+}
+
+// Per-element window/causal/length mask of one 32-key tile for a lane's row
+// (entry i: key k0 + 8*(i/4) + 4*hw + i%4).  Branch-free on purpose.
+__device__ __forceinline__ void mask_tile(f32x16 &s, int k0, int hw, int p, int kv_len,
+                                          int causal, int W)
+{
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+        const int key = k0 + 8 * (i >> 2) + 4 * hw + (i & 3);
+        const bool vis = (key < kv_len) & ((causal == 0) | (key <= p)) & ((W < 0) | (key >= p - W));
+        s[i] = vis ? s[i] : kNegInf;
+    }
+}
+
+__device__ __forceinline__ float max16(const f32x16 &s)
+{
+    float a = fmaxf(s[0], fmaxf(s[1], s[2]));
+    float b = fmaxf(s[3], fmaxf(s[4], s[5]));
+    float c = fmaxf(s[6], fmaxf(s[7], s[8]));
+    float d = fmaxf(s[9], fmaxf(s[10], s[11]));
+    float e = fmaxf(s[12], fmaxf(s[13], s[14]));
+    return fmaxf(fmaxf(a, fmaxf(b, c)), fmaxf(fmaxf(d, e), s[15]));
 }
 
 template <int D, int NW>
@@ -216,24 +257,28 @@ __global__ __launch_bounds__(NW * 64) void prefill_bf16_kernel(PrefillArgs a)
             for (int i = 0; i < 16; ++i) o[dt][i] = 0.f;
 
         // prologue: tiles 0 and 1 in LDS sets 0 and 1, tile 2 in registers,
-        // tile 3's rows known
+        // tile 3's page ids read
         Stage<D, NW> st;
         if (ntiles > 0) {
-            stage_offsets(st, ra, kv_begin, tid);
-            stage_load(st, a, kv_begin, kv_len, tid);
+            stage_pages(st, ra, kv_begin, tid);
+            stage_load(st, a, ra, kv_begin, tid);
+            stage_pages(st, ra, kv_begin + KT, tid);
             stage_store(st, lds[0], tid);
             if (ntiles > 1) {
-                stage_offsets(st, ra, kv_begin + KT, tid);
-                stage_load(st, a, kv_begin + KT, kv_len, tid);
-                stage_offsets(st, ra, kv_begin + 2 * KT, tid);
+                stage_load(st, a, ra, kv_begin + KT, tid);
+                stage_pages(st, ra, kv_begin + 2 * KT, tid);
                 stage_store(st, lds[1], tid);
                 if (ntiles > 2) {
-                    stage_load(st, a, kv_begin + 2 * KT, kv_len, tid);
-                    stage_offsets(st, ra, kv_begin + 3 * KT, tid);
+                    stage_load(st, a, ra, kv_begin + 2 * KT, tid);
+                    stage_pages(st, ra, kv_begin + 3 * KT, tid);
                 }
             }
         }
         __syncthreads();
+        // Everything issued so far (the Q operand included) has landed: say so
+        // once here, so the loop's first MFMA does not wait for the in-flight
+        // K/V loads of later tiles.
+        __builtin_amdgcn_s_waitcnt(0);
         f32x16 s_cur;
         if (ntiles > 0) s_cur = qk_tile<D>(lds[0], qf, l32, hw);
 
@@ -243,27 +288,12 @@ __global__ __launch_bounds__(NW * 64) void prefill_bf16_kernel(PrefillArgs a)
             const int nxt = cur == NBUF - 1 ? 0 : cur + 1;
             const int nn = nxt == NBUF - 1 ? 0 : nxt + 1;
 
-            // S^T of tile j+1 goes to the matrix cores while this tile's softmax
-            // runs on the vector ALUs
-            f32x16 s_nxt;
-            if (j + 1 < ntiles) s_nxt = qk_tile<D>(lds[nxt], qf, l32, hw);
-
             // accumulator entry i holds key k0 + 8*(i/4) + 4*hw + i%4 of this row
             f32x16 s = s_cur;
             const bool interior = k0 + KT <= kv_len && (!a.causal || k0 + KT - 1 <= pos0) &&
                                   (W < 0 || k0 >= pos_last - W);
-            if (!interior) {
-#pragma unroll
-                for (int i = 0; i < 16; ++i) {
-                    const int key = k0 + 8 * (i >> 2) + 4 * hw + (i & 3);
-                    const bool vis = key < kv_len && (!a.causal || key <= p_row) &&
-                                     (W < 0 || key >= p_row - W);
-                    s[i] = vis ? s[i] : kNegInf;
-                }
-            }
-            float mx = fmaxf(s[0], s[1]);
-#pragma unroll
-            for (int i = 2; i < 16; i += 2) mx = fmaxf(mx, fmaxf(s[i], s[i + 1]));
+            if (!interior) mask_tile(s, k0, hw, p_row, kv_len, a.causal, W);
+            float mx = max16(s);
             mx = fmaxf(mx, __shfl_xor(mx, 32)) * c;
 
             // lazy rescale: keep the running maximum unless some row's grows by
@@ -278,15 +308,35 @@ __global__ __launch_bounds__(NW * 64) void prefill_bf16_kernel(PrefillArgs a)
                 m = m_new;
             }
             const float mu = m == kNegInf ? 0.f : m;
+
+            // S^T of tile j+1 (its LDS set is ready; after the last tile the
+            // result is simply unused) is interleaved by hand with this tile's
+            // exponentials: each dependent QK MFMA is followed by the FMA+exp of
+            // 16/KSTEPS scores, which the vector ALU runs while the matrix core
+            // works.  The fences keep the compiler from regrouping them.
+            constexpr int EPS = 16 / KSTEPS;  // scores per QK step (D=128: 2)
+            const PrefillBuf<D> &bn = lds[nxt];
+            f32x16 s_nxt;
+#pragma unroll
+            for (int i = 0; i < 16; ++i) s_nxt[i] = 0.f;
             f32x16 pr;
             float rs = 0.f;
+            bf16x8 kf = *reinterpret_cast<const bf16x8 *>(&bn.k[l32][hw * 8]);
 #pragma unroll
-            for (int i = 0; i < 16; ++i) {
-                pr[i] = fast_exp2(__builtin_fmaf(s[i], c, -mu));
-                rs += pr[i];
+            for (int ks = 0; ks < KSTEPS; ++ks) {
+                const bf16x8 kc = kf;
+                if (ks + 1 < KSTEPS)
+                    kf = *reinterpret_cast<const bf16x8 *>(&bn.k[l32][(ks + 1) * 16 + hw * 8]);
+                s_nxt = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kc, qf[ks], s_nxt, 0, 0, 0);
+#pragma unroll
+                for (int e = 0; e < EPS; ++e) {
+                    const int i = ks * EPS + e;
+                    pr[i] = fast_exp2(__builtin_fmaf(s[i], c, -mu));
+                    rs += pr[i];
+                }
+                __builtin_amdgcn_sched_barrier(0);
             }
             l += rs;
-
             // O^T += V^T . P^T, two k-steps of 16 keys
             const PrefillBuf<D> &bj = lds[cur];
 #pragma unroll
@@ -311,8 +361,8 @@ __global__ __launch_bounds__(NW * 64) void prefill_bf16_kernel(PrefillArgs a)
             if (j + 2 < ntiles) {
                 stage_store(st, lds[nn], tid);
                 if (j + 3 < ntiles) {
-                    stage_load(st, a, k0 + 3 * KT, kv_len, tid);
-                    stage_offsets(st, ra, k0 + 4 * KT, tid);
+                    stage_load(st, a, ra, k0 + 3 * KT, tid);
+                    stage_pages(st, ra, k0 + 4 * KT, tid);
                 }
             }
             __syncthreads();
@@ -340,6 +390,308 @@ __global__ __launch_bounds__(NW * 64) void prefill_bf16_kernel(PrefillArgs a)
                     l > 0.f ? (m + fast_log2(l)) * kLn2 : kNegInf;
         }
         __syncthreads();  // the next item's prologue overwrites LDS set 0
+    }
+}
+
+// Wide variant for head_dim <= 128: 4 waves x 64 rows (two 32-row N tiles per
+// wave, 256 rows per workgroup), one wave per SIMD.  Every K / V^T operand
+// read from LDS feeds two MFMAs (half the LDS traffic of the 32-row waves),
+// and the wave pipelines its own work: iteration j issues the PV MFMAs of
+// tile j-1 and the QK MFMAs of tile j+1 -- neither depends on tile j's
+// softmax -- interleaved instruction by instruction with tile j's max and
+// exponentials, so the matrix cores and the vector ALUs run together.  Four
+// LDS tile sets are live: V of j-1, V of j, K and V of j+1, and j+2 being
+// written.  A rescale of O (rare, see kRescaleLog2) is applied after PV of
+// tile j-1 has landed, before PV of tile j.
+constexpr int WIDE_SETS = 4;
+
+template <int D>
+struct WideOps {
+    static constexpr int KS = D / 16;  // QK k-steps
+    static constexpr int DT = D / 32;  // O^T dim tiles
+    static constexpr int NQ = 2 * DT;  // V^T operands per tile (dim tile x 16-key step)
+};
+
+template <int D>
+__device__ __forceinline__ bf16x8 wide_vop(const PrefillBuf<D> &b, int q, int tr_key, int tr_dim)
+{
+    const int dt = q >> 1, kk = q & 1;
+    const uint16_t *v0 = &b.v[16 * kk + tr_key][32 * dt + tr_dim];
+    const i16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4 *)v0);
+    const i16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4 *)(v0 + 8 * (D + VPAD)));
+    return __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
+}
+
+template <int D>
+__device__ __forceinline__ bf16x8 wide_kop(const PrefillBuf<D> &b, int ks, int l32, int hw)
+{
+    return *reinterpret_cast<const bf16x8 *>(&b.k[l32][ks * 16 + hw * 8]);
+}
+
+template <int D>
+__global__ __launch_bounds__(256) void prefill_wide_kernel(PrefillArgs a)
+{
+    constexpr int KS = WideOps<D>::KS, DT = WideOps<D>::DT, NQ = WideOps<D>::NQ;
+    constexpr int NW = 4;
+    __shared__ __attribute__((aligned(16))) PrefillBuf<D> lds[WIDE_SETS];
+
+    const int tid = threadIdx.x;
+    const int wave = tid >> 6, lane = tid & 63, l32 = lane & 31, hw = lane >> 5;
+    const int G = 1 << a.log2_group;
+    const int n_items = a.ws[kHdrNumItems];
+    const uint16_t *Q = static_cast<const uint16_t *>(a.q);
+    const int W = a.window_left;
+    const float c = a.scale_log2;
+    const int tr_key = 4 * hw + ((lane & 15) >> 2);
+    const int tr_dim = 16 * ((lane >> 4) & 1) + 4 * (lane & 3);
+
+    RowAddr ra;
+    ra.kv_indices = a.kv_indices;
+    ra.num_pages = a.num_pages;
+    ra.slot_stride = int64_t(a.num_kv_heads) * D;
+    ra.page_stride = ra.slot_stride * a.page_size;
+    ra.log2_page = a.log2_page;
+    ra.page_mask = a.page_size - 1;
+
+    for (int it = blockIdx.x; it < n_items; it += gridDim.x) {
+        const int32_t *w = a.ws + kHeaderWords + int64_t(it) * kPrefillItemWords;
+        const int hk = w[kPiKvHead], q_begin = w[kPiQBegin], q_count = w[kPiQCount];
+        const int pos0 = w[kPiPos0], kv_len = w[kPiKvLen];
+        const int kv_begin = w[kPiKvBegin];
+        const int kv_end = a.causal ? min(kv_len, pos0 + q_count) : kv_len;
+        const int pos_last = pos0 + q_count - 1;
+        const int ntiles = kv_end > kv_begin ? (kv_end - kv_begin + KT - 1) / KT : 0;
+        ra.page_base = w[kPiPageBase];
+        ra.kv_len = kv_len;
+        ra.head_off = int64_t(hk) * D;
+
+        // the lane's two rows: N tile n holds row wave*64 + 32n + l32
+        int row_tok[2], row_head[2], p_row[2];
+        bool row_valid[2];
+        int64_t qrow[2];
+        bf16x8 qf[2][KS];
+#pragma unroll
+        for (int n = 0; n < 2; ++n) {
+            const int row = wave * 64 + 32 * n + l32;
+            row_tok[n] = row >> a.log2_group;
+            row_head[n] = row & (G - 1);
+            row_valid[n] = row_tok[n] < q_count;
+            p_row[n] = pos0 + row_tok[n];
+            qrow[n] = (int64_t(q_begin + row_tok[n]) * a.num_qo_heads + hk * G + row_head[n]) * D;
+#pragma unroll
+            for (int ks = 0; ks < KS; ++ks)
+                qf[n][ks] = row_valid[n] ? load_bf16x8(Q + qrow[n] + ks * 16 + hw * 8)
+                                         : zero_bf16x8();
+        }
+
+        float m[2] = {kNegInf, kNegInf}, l[2] = {0.f, 0.f};
+        f32x16 o[2][DT];
+#pragma unroll
+        for (int n = 0; n < 2; ++n)
+#pragma unroll
+            for (int dt = 0; dt < DT; ++dt)
+#pragma unroll
+                for (int i = 0; i < 16; ++i) o[n][dt][i] = 0.f;
+
+        // prologue: tiles 0 and 1 in sets 0 and 1, tile 2 in registers, tile 3's
+        // page ids read; the V rows of set 3 (read as "tile -1") are zeroed
+        Stage<D, NW> st;
+        for (int e = tid; e < KT * (D + VPAD) / 8; e += NW * 64)
+            reinterpret_cast<u32x4 *>(&lds[WIDE_SETS - 1].v[0][0])[e] = u32x4{0u, 0u, 0u, 0u};
+        if (ntiles > 0) {
+            stage_pages(st, ra, kv_begin, tid);
+            stage_load(st, a, ra, kv_begin, tid);
+            stage_pages(st, ra, kv_begin + KT, tid);
+            stage_store(st, lds[0], tid);
+            if (ntiles > 1) {
+                stage_load(st, a, ra, kv_begin + KT, tid);
+                stage_pages(st, ra, kv_begin + 2 * KT, tid);
+                stage_store(st, lds[1], tid);
+                if (ntiles > 2) {
+                    stage_load(st, a, ra, kv_begin + 2 * KT, tid);
+                    stage_pages(st, ra, kv_begin + 3 * KT, tid);
+                }
+            }
+        }
+        __syncthreads();
+        __builtin_amdgcn_s_waitcnt(0);
+
+        f32x16 s_cur[2];
+#pragma unroll
+        for (int n = 0; n < 2; ++n)
+#pragma unroll
+            for (int i = 0; i < 16; ++i) s_cur[n][i] = 0.f;
+        if (ntiles > 0) {
+#pragma unroll
+            for (int ks = 0; ks < KS; ++ks) {
+                const bf16x8 kf = wide_kop<D>(lds[0], ks, l32, hw);
+#pragma unroll
+                for (int n = 0; n < 2; ++n)
+                    s_cur[n] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf, qf[n][ks], s_cur[n],
+                                                                       0, 0, 0);
+            }
+        }
+        bf16x8 p_prev[2][2];
+#pragma unroll
+        for (int n = 0; n < 2; ++n) p_prev[n][0] = p_prev[n][1] = zero_bf16x8();
+
+        for (int j = 0; j < ntiles; ++j) {
+            const int k0 = kv_begin + j * KT;
+            const int cur = j & 3, nxt = (j + 1) & 3, nn = (j + 2) & 3, prv = (j + 3) & 3;
+
+            // exact mask on tiles that straddle the window edge, the diagonal or
+            // the end of the keys (entry i: key k0 + 8*(i/4) + 4*hw + i%4)
+            const bool interior = k0 + KT <= kv_len && (!a.causal || k0 + KT - 1 <= pos0) &&
+                                  (W < 0 || k0 >= pos_last - W);
+            if (!interior) {
+#pragma unroll
+                for (int n = 0; n < 2; ++n)
+#pragma unroll
+                    for (int i = 0; i < 16; ++i) {
+                        const int key = k0 + 8 * (i >> 2) + 4 * hw + (i & 3);
+                        const bool vis = key < kv_len && (!a.causal || key <= p_row[n]) &&
+                                         (W < 0 || key >= p_row[n] - W);
+                        s_cur[n][i] = vis ? s_cur[n][i] : kNegInf;
+                    }
+            }
+
+            // region 1: PV of tile j-1 on the matrix cores, row maxima on the VALU
+            float mx[2] = {kNegInf, kNegInf};
+            {
+                const PrefillBuf<D> &bp = lds[prv];
+                bf16x8 va = wide_vop<D>(bp, 0, tr_key, tr_dim);
+#pragma unroll
+                for (int q = 0; q < NQ; ++q) {
+                    const bf16x8 vc = va;
+                    if (q + 1 < NQ) va = wide_vop<D>(bp, q + 1, tr_key, tr_dim);
+                    const int dt = q >> 1, kk = q & 1;
+#pragma unroll
+                    for (int n = 0; n < 2; ++n)
+                        o[n][dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vc, p_prev[n][kk],
+                                                                           o[n][dt], 0, 0, 0);
+                    // 32 scores over NQ steps
+#pragma unroll
+                    for (int e = 0; e < 32 / NQ; e += 2) {
+                        const int f = q * (32 / NQ) + e, n = f >> 4, i = f & 15;
+                        mx[n] = fmaxf(mx[n], fmaxf(s_cur[n][i], s_cur[n][i + 1]));
+                    }
+                    __builtin_amdgcn_sched_barrier(0);
+                }
+            }
+            float m_new[2], alpha[2], mu[2];
+#pragma unroll
+            for (int n = 0; n < 2; ++n) mx[n] = fmaxf(mx[n], __shfl_xor(mx[n], 32)) * c;
+            const bool need = __any(mx[0] > m[0] + kRescaleLog2 || mx[1] > m[1] + kRescaleLog2);
+#pragma unroll
+            for (int n = 0; n < 2; ++n) {
+                m_new[n] = need ? fmaxf(m[n], mx[n]) : m[n];
+                alpha[n] = m_new[n] == kNegInf ? 1.f : fast_exp2(m[n] - m_new[n]);
+                mu[n] = m_new[n] == kNegInf ? 0.f : m_new[n];
+            }
+
+            // region 2: QK of tile j+1 (after the last tile the result is unused)
+            // on the matrix cores, exponentials of tile j on the VALU, packed to
+            // bf16 pairs as they are made
+            f32x16 s_nxt[2];
+            bf16x8 p_cur[2][2];
+            float rs[2] = {0.f, 0.f};
+            {
+                const PrefillBuf<D> &bn = lds[nxt];
+                bf16x8 kf = wide_kop<D>(bn, 0, l32, hw);
+#pragma unroll
+                for (int ks = 0; ks < KS; ++ks) {
+                    const bf16x8 kc = kf;
+                    if (ks + 1 < KS) kf = wide_kop<D>(bn, ks + 1, l32, hw);
+#pragma unroll
+                    for (int n = 0; n < 2; ++n) {
+                        if (ks == 0) {
+                            const f32x16 z = {};
+                            s_nxt[n] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kc, qf[n][0], z,
+                                                                               0, 0, 0);
+                        } else {
+                            s_nxt[n] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kc, qf[n][ks],
+                                                                               s_nxt[n], 0, 0, 0);
+                        }
+                    }
+#pragma unroll
+                    for (int e = 0; e < 32 / KS; e += 2) {
+                        const int f = ks * (32 / KS) + e, n = f >> 4, i = f & 15;
+                        const float e0 = fast_exp2(__builtin_fmaf(s_cur[n][i], c, -mu[n]));
+                        const float e1 = fast_exp2(__builtin_fmaf(s_cur[n][i + 1], c, -mu[n]));
+                        rs[n] += e0 + e1;
+                        typedef float f32x2 __attribute__((ext_vector_type(2)));
+                        typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+                        const bf16x2 pk = __builtin_convertvector(f32x2{e0, e1}, bf16x2);
+                        p_cur[n][i >> 3][i & 7] = pk[0];
+                        p_cur[n][i >> 3][(i & 7) + 1] = pk[1];
+                        // keep this step's VALU work here, between its MFMAs
+                        asm volatile("" ::"v"(rs[n]));
+                    }
+                    __builtin_amdgcn_sched_barrier(0);
+                }
+            }
+#pragma unroll
+            for (int n = 0; n < 2; ++n) l[n] = l[n] * alpha[n] + rs[n];
+            if (need) {
+                // O holds PV up to tile j-1 at the old maximum
+#pragma unroll
+                for (int n = 0; n < 2; ++n)
+#pragma unroll
+                    for (int dt = 0; dt < DT; ++dt) o[n][dt] *= alpha[n];
+            }
+
+            // stage tile j+2 into its LDS set, start loading tile j+3
+            if (j + 2 < ntiles) {
+                stage_store(st, lds[nn], tid);
+                if (j + 3 < ntiles) {
+                    stage_load(st, a, ra, k0 + 3 * KT, tid);
+                    stage_pages(st, ra, k0 + 4 * KT, tid);
+                }
+            }
+            __syncthreads();
+#pragma unroll
+            for (int n = 0; n < 2; ++n) {
+                s_cur[n] = s_nxt[n];
+                p_prev[n][0] = p_cur[n][0];
+                p_prev[n][1] = p_cur[n][1];
+                m[n] = m_new[n];
+            }
+        }
+
+        // epilogue: PV of the last tile, then normalise
+        if (ntiles > 0) {
+            const PrefillBuf<D> &bl = lds[(ntiles - 1) & 3];
+#pragma unroll
+            for (int q = 0; q < NQ; ++q) {
+                const bf16x8 vc = wide_vop<D>(bl, q, tr_key, tr_dim);
+#pragma unroll
+                for (int n = 0; n < 2; ++n)
+                    o[n][q >> 1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vc, p_prev[n][q & 1],
+                                                                           o[n][q >> 1], 0, 0, 0);
+            }
+        }
+#pragma unroll
+        for (int n = 0; n < 2; ++n) {
+            float ln = l[n] + __shfl_xor(l[n], 32);
+            const float inv = ln > 0.f ? 1.f / ln : 0.f;
+            if (row_valid[n]) {
+                uint16_t *O = static_cast<uint16_t *>(a.o);
+#pragma unroll
+                for (int dt = 0; dt < DT; ++dt)
+#pragma unroll
+                    for (int m0 = 0; m0 < 4; ++m0) {
+                        f32x4 v4;
+#pragma unroll
+                        for (int m1 = 0; m1 < 4; ++m1) v4[m1] = o[n][dt][4 * m0 + m1] * inv;
+                        *reinterpret_cast<bf16x4 *>(O + qrow[n] + dt * 32 + 8 * m0 + 4 * hw) =
+                            __builtin_convertvector(v4, bf16x4);
+                    }
+                if (a.lse && hw == 0)
+                    a.lse[int64_t(q_begin + row_tok[n]) * a.num_qo_heads + hk * G + row_head[n]] =
+                        ln > 0.f ? (m[n] + fast_log2(ln)) * kLn2 : kNegInf;
+            }
+        }
+        __syncthreads();  // the next item's prologue overwrites the LDS sets
     }
 }
 
@@ -398,10 +750,16 @@ __global__ __launch_bounds__(kGenericThreads) void attention_fp32_kernel(Prefill
 
 }  // namespace
 
-hipError_t launch_prefill_bf16(const PrefillArgs &a, int head_dim, int waves, int grid,
+hipError_t launch_prefill_bf16(const PrefillArgs &a, int head_dim, int variant, int grid,
                                hipStream_t s)
 {
-    if (waves == 8) {
+    if (variant == kPrefillWide) {
+        switch (head_dim) {
+        case 64: prefill_wide_kernel<64><<<grid, 256, 0, s>>>(a); break;
+        case 128: prefill_wide_kernel<128><<<grid, 256, 0, s>>>(a); break;
+        default: return hipErrorInvalidValue;
+        }
+    } else if (variant == kPrefillRows256) {
         switch (head_dim) {
         case 64: prefill_bf16_kernel<64, 8><<<grid, 512, 0, s>>>(a); break;
         case 128: prefill_bf16_kernel<128, 8><<<grid, 512, 0, s>>>(a); break;
@@ -424,11 +782,16 @@ hipError_t launch_attention_fp32(const PrefillArgs &a, int head_dim, int grid, h
     return hipGetLastError();
 }
 
-int prefill_bf16_blocks_per_cu(int head_dim, int waves)
+int prefill_bf16_blocks_per_cu(int head_dim, int variant)
 {
     int n = 0;
     hipError_t e = hipErrorInvalidValue;
-    if (waves == 8) {
+    if (variant == kPrefillWide) {
+        if (head_dim == 64)
+            e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, prefill_wide_kernel<64>, 256, 0);
+        else if (head_dim == 128)
+            e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, prefill_wide_kernel<128>, 256, 0);
+    } else if (variant == kPrefillRows256) {
         if (head_dim == 64)
             e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, prefill_bf16_kernel<64, 8>, 512, 0);
         else if (head_dim == 128)

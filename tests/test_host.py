@@ -59,6 +59,9 @@ def err_code(fn):
     (dict(num_qo_heads=3, num_kv_heads=1), P.PKVS_ERR_UNSUPPORTED),
     (dict(fixed_split_size=100), P.PKVS_ERR_INVALID_ARG),
     (dict(batch_capacity=0), P.PKVS_ERR_INVALID_ARG),
+    (dict(prefill_variant=6), P.PKVS_ERR_INVALID_ARG),
+    (dict(prefill_variant=2, head_dim=256), P.PKVS_ERR_UNSUPPORTED),
+    (dict(prefill_variant=3, head_dim=256), P.PKVS_ERR_UNSUPPORTED),
 ])
 def test_descriptor_rejections(kw, code):
     assert err_code(lambda: P.pkvs_plan_create(desc(**kw))) == code
@@ -90,7 +93,8 @@ def test_prefill_items_cover_every_query_once(W, G):
     P.pkvs_prefill_plan(h, qop, kvp, last, len(kv), None, None)
     info = P.pkvs_plan_get_info(h)
     items = P.pkvs_plan_copy_items(h)
-    assert info.query_tile == 128 // G and items.shape[0] == info.num_items
+    assert info.query_tile in (128 // G, 256 // G)
+    assert items.shape[0] == info.num_items
     seen = {}
     for it in items.tolist():
         b, hk, q0, qn, pos0, kv_len, pbase, kvb = it
