@@ -14,9 +14,11 @@
 // operand of the PV product.  K and V sit in LDS row-major; the V^T operand
 // comes from gfx950's transposing LDS read.
 //
-// Three key tiles are in flight in LDS (one barrier per tile): while tile j's
+// Four LDS tile sets are in flight (one barrier per tile): while tile j's
 // softmax runs, the MFMAs of tile j+1's S^T are already issued, tile j+2 is
-// being written to LDS and tile j+3 read from HBM into registers.
+// being written to LDS and tile j+3 read from HBM into registers; with 8 waves
+// the second half of the waves multiplies P.V one tile late (ping-pong), which
+// keeps V of tile j-1 live in the fourth set.
 // The running row maximum is only moved (and O rescaled) when it grows by more
 // than 2^8, which most tiles never do.
 //
@@ -42,7 +44,7 @@ namespace {
 constexpr int KT = kPrefillKvTile;
 constexpr int KPAD = 8;                // K rows: D+8 bf16, a stride of 4 dwords mod 64 banks
 constexpr int VPAD = 32;               // V rows: D+32 bf16, a stride of 16 dwords mod 64 banks
-constexpr int NBUF = 3;                // LDS tile sets in flight
+constexpr int NBUF = 4;                // LDS tile sets in flight
 constexpr float kRescaleLog2 = 8.0f;   // rescale O only when a row max grows by > 2^8
 
 typedef short i16x4 __attribute__((ext_vector_type(4)));
@@ -108,8 +110,9 @@ __device__ __forceinline__ void stage_pages(Stage<D, NW> &st, const RowAddr &ra,
     for (int i = 0; i < S::KCH; ++i) st.page[i] = ra.page_id(k0 + (tid + i * S::T) / CPR);
 }
 
-// Global -> registers.  Keys at or past kv_len are zero-filled: no unwritten
-// slot (whatever its bits, even NaN) ever reaches an MFMA.
+// Global -> registers.  Keys past the request are clamped to its last key
+// (a valid row); stage_store zeroes them, so no unwritten slot (whatever its
+// bits, even NaN) ever reaches an MFMA.
 template <int D, int NW>
 __device__ __forceinline__ void stage_load(Stage<D, NW> &st, const PrefillArgs &a,
                                            const RowAddr &ra, int k0, int tid)
@@ -118,28 +121,14 @@ __device__ __forceinline__ void stage_load(Stage<D, NW> &st, const PrefillArgs &
     constexpr int CPR = D / 8;
     const uint16_t *K = static_cast<const uint16_t *>(a.k);
     const uint16_t *V = static_cast<const uint16_t *>(a.v);
-    if (k0 + KT <= ra.kv_len) {
-        // the whole tile is inside the request (the common case)
-#pragma unroll
-        for (int i = 0; i < S::KCH; ++i) {
-            const int c = tid + i * S::T;
-            if (chunk_exists<D, NW>(c)) {
-                const int64_t off = ra.offset(st.page[i], k0 + c / CPR) + (c % CPR) * 8;
-                st.k[i] = *reinterpret_cast<const u32x4 *>(K + off);
-                st.v[i] = *reinterpret_cast<const u32x4 *>(V + off);
-            }
-        }
-        return;
-    }
 #pragma unroll
     for (int i = 0; i < S::KCH; ++i) {
         const int c = tid + i * S::T;
-        const int key = k0 + c / CPR;
-        const bool ok = chunk_exists<D, NW>(c) && key < ra.kv_len;
-        const int64_t off = ra.offset(st.page[i], key) + (c % CPR) * 8;
-        const u32x4 z = {0u, 0u, 0u, 0u};
-        st.k[i] = ok ? *reinterpret_cast<const u32x4 *>(K + off) : z;
-        st.v[i] = ok ? *reinterpret_cast<const u32x4 *>(V + off) : z;
+        if (chunk_exists<D, NW>(c)) {
+            const int64_t off = ra.offset(st.page[i], k0 + c / CPR) + (c % CPR) * 8;
+            st.k[i] = *reinterpret_cast<const u32x4 *>(K + off);
+            st.v[i] = *reinterpret_cast<const u32x4 *>(V + off);
+        }
     }
 }
 
@@ -167,10 +156,21 @@ __device__ __forceinline__ float max16(const f32x16 &s)
 }
 
 template <int D, int NW>
-__device__ __forceinline__ void stage_store(const Stage<D, NW> &st, PrefillBuf<D> &b, int tid)
+__device__ __forceinline__ void stage_store(Stage<D, NW> &st, PrefillBuf<D> &b, int k0,
+                                            int kv_len, int tid)
 {
     using S = Stage<D, NW>;
     constexpr int CPR = D / 8;
+    if (k0 + KT > kv_len) {
+        // the request's last tile: keys past its end become zeros
+#pragma unroll
+        for (int i = 0; i < S::KCH; ++i) {
+            const bool past = k0 + (tid + i * S::T) / CPR >= kv_len;
+            const u32x4 z = {0u, 0u, 0u, 0u};
+            st.k[i] = past ? z : st.k[i];
+            st.v[i] = past ? z : st.v[i];
+        }
+    }
 #pragma unroll
     for (int i = 0; i < S::KCH; ++i) {
         const int c = tid + i * S::T;
@@ -195,6 +195,25 @@ __device__ __forceinline__ f32x16 qk_tile(const PrefillBuf<D> &b, const bf16x8 (
         s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf, qf[ks], s, 0, 0, 0);
     }
     return s;
+}
+
+// O^T += V^T . P^T for one 32-key tile (two k-steps of 16 keys).
+template <int D>
+__device__ __forceinline__ void pv_tile(const PrefillBuf<D> &b, const bf16x8 (&pb)[2],
+                                        f32x16 (&o)[D / 32], int tr_key, int tr_dim)
+{
+#pragma unroll
+    for (int kk = 0; kk < 2; ++kk)
+#pragma unroll
+        for (int dt = 0; dt < D / 32; ++dt) {
+            const uint16_t *v0 = &b.v[16 * kk + tr_key][32 * dt + tr_dim];
+            const i16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4 *)v0);
+            const i16x4 hi =
+                __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4 *)(v0 + 8 * (D + VPAD)));
+            const bf16x8 va =
+                __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
+            o[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(va, pb[kk], o[dt], 0, 0, 0);
+        }
 }
 
 template <int D, int NW>
@@ -263,11 +282,11 @@ __global__ __launch_bounds__(NW * 64) void prefill_bf16_kernel(PrefillArgs a)
             stage_pages(st, ra, kv_begin, tid);
             stage_load(st, a, ra, kv_begin, tid);
             stage_pages(st, ra, kv_begin + KT, tid);
-            stage_store(st, lds[0], tid);
+            stage_store(st, lds[0], kv_begin, kv_len, tid);
             if (ntiles > 1) {
                 stage_load(st, a, ra, kv_begin + KT, tid);
                 stage_pages(st, ra, kv_begin + 2 * KT, tid);
-                stage_store(st, lds[1], tid);
+                stage_store(st, lds[1], kv_begin + KT, kv_len, tid);
                 if (ntiles > 2) {
                     stage_load(st, a, ra, kv_begin + 2 * KT, tid);
                     stage_pages(st, ra, kv_begin + 3 * KT, tid);
@@ -282,11 +301,15 @@ __global__ __launch_bounds__(NW * 64) void prefill_bf16_kernel(PrefillArgs a)
         f32x16 s_cur;
         if (ntiles > 0) s_cur = qk_tile<D>(lds[0], qf, l32, hw);
 
-        int cur = 0;  // LDS set of tile j
+        // Ping-pong: with 8 waves, waves w and w+4 share a SIMD.  Waves 4..7
+        // issue the PV product of a tile one iteration late, so in every
+        // iteration one wave of each SIMD starts with its exponentials
+        // (vector ALU) while the other starts with PV (matrix core).
+        const bool lag = NW == 8 && wave >= 4;
+        bf16x8 pb_prev[2] = {zero_bf16x8(), zero_bf16x8()};
         for (int j = 0; j < ntiles; ++j) {
             const int k0 = kv_begin + j * KT;
-            const int nxt = cur == NBUF - 1 ? 0 : cur + 1;
-            const int nn = nxt == NBUF - 1 ? 0 : nxt + 1;
+            if (lag && j > 0) pv_tile<D>(lds[(j - 1) & 3], pb_prev, o, tr_key, tr_dim);
 
             // accumulator entry i holds key k0 + 8*(i/4) + 4*hw + i%4 of this row
             f32x16 s = s_cur;
@@ -298,7 +321,8 @@ __global__ __launch_bounds__(NW * 64) void prefill_bf16_kernel(PrefillArgs a)
 
             // lazy rescale: keep the running maximum unless some row's grows by
             // more than 2^8 (probabilities then stay below 2^8, exact in fp32
-            // and in bf16 range), so most tiles skip the O rescale
+            // and in bf16 range), so most tiles skip the O rescale.  O holds PV
+            // up to tile j-1 here, for both wave groups.
             if (__any(mx > m + kRescaleLog2)) {
                 const float m_new = fmaxf(m, mx);
                 const float alpha = m_new == kNegInf ? 1.f : fast_exp2(m - m_new);
@@ -315,51 +339,50 @@ __global__ __launch_bounds__(NW * 64) void prefill_bf16_kernel(PrefillArgs a)
             // 16/KSTEPS scores, which the vector ALU runs while the matrix core
             // works.  The fences keep the compiler from regrouping them.
             constexpr int EPS = 16 / KSTEPS;  // scores per QK step (D=128: 2)
-            const PrefillBuf<D> &bn = lds[nxt];
+            const PrefillBuf<D> &bn = lds[(j + 1) & 3];
             f32x16 s_nxt;
 #pragma unroll
             for (int i = 0; i < 16; ++i) s_nxt[i] = 0.f;
             f32x16 pr;
-            float rs = 0.f;
-            bf16x8 kf = *reinterpret_cast<const bf16x8 *>(&bn.k[l32][hw * 8]);
+            // all K operands of the next tile are requested up front so their
+            // LDS latency hides behind the first steps
+            bf16x8 kf[KSTEPS];
+#pragma unroll
+            for (int ks = 0; ks < KSTEPS; ++ks)
+                kf[ks] = *reinterpret_cast<const bf16x8 *>(&bn.k[l32][ks * 16 + hw * 8]);
 #pragma unroll
             for (int ks = 0; ks < KSTEPS; ++ks) {
-                const bf16x8 kc = kf;
-                if (ks + 1 < KSTEPS)
-                    kf = *reinterpret_cast<const bf16x8 *>(&bn.k[l32][(ks + 1) * 16 + hw * 8]);
-                s_nxt = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kc, qf[ks], s_nxt, 0, 0, 0);
+                s_nxt = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf[ks], qf[ks], s_nxt, 0, 0, 0);
 #pragma unroll
                 for (int e = 0; e < EPS; ++e) {
                     const int i = ks * EPS + e;
                     pr[i] = fast_exp2(__builtin_fmaf(s[i], c, -mu));
-                    rs += pr[i];
                 }
                 __builtin_amdgcn_sched_barrier(0);
             }
-            l += rs;
-            // O^T += V^T . P^T, two k-steps of 16 keys
-            const PrefillBuf<D> &bj = lds[cur];
+            // row sum as a tree (short dependency chains)
+            float t8[8];
+#pragma unroll
+            for (int i = 0; i < 8; ++i) t8[i] = pr[2 * i] + pr[2 * i + 1];
+            l += ((t8[0] + t8[1]) + (t8[2] + t8[3])) + ((t8[4] + t8[5]) + (t8[6] + t8[7]));
+            bf16x8 pb[2];
 #pragma unroll
             for (int kk = 0; kk < 2; ++kk) {
                 f32x8 p8;
 #pragma unroll
                 for (int jj = 0; jj < 8; ++jj) p8[jj] = pr[8 * kk + jj];
-                const bf16x8 pb = __builtin_convertvector(p8, bf16x8);
-#pragma unroll
-                for (int dt = 0; dt < DT; ++dt) {
-                    const uint16_t *v0 = &bj.v[16 * kk + tr_key][32 * dt + tr_dim];
-                    const i16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4 *)v0);
-                    const i16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-                        (lds_i16x4 *)(v0 + 8 * (D + VPAD)));
-                    const bf16x8 va = __builtin_bit_cast(
-                        bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
-                    o[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(va, pb, o[dt], 0, 0, 0);
-                }
+                pb[kk] = __builtin_convertvector(p8, bf16x8);
+            }
+            if (!lag) {
+                pv_tile<D>(lds[j & 3], pb, o, tr_key, tr_dim);
+            } else {
+                pb_prev[0] = pb[0];
+                pb_prev[1] = pb[1];
             }
 
             // stage tile j+2 into the free LDS set, start loading tile j+3
             if (j + 2 < ntiles) {
-                stage_store(st, lds[nn], tid);
+                stage_store(st, lds[(j + 2) & 3], k0 + 2 * KT, kv_len, tid);
                 if (j + 3 < ntiles) {
                     stage_load(st, a, ra, k0 + 3 * KT, tid);
                     stage_pages(st, ra, k0 + 4 * KT, tid);
@@ -367,8 +390,8 @@ __global__ __launch_bounds__(NW * 64) void prefill_bf16_kernel(PrefillArgs a)
             }
             __syncthreads();
             s_cur = s_nxt;
-            cur = nxt;
         }
+        if (lag && ntiles > 0) pv_tile<D>(lds[(ntiles - 1) & 3], pb_prev, o, tr_key, tr_dim);
 
         // epilogue: the two half-waves hold disjoint keys of each row
         l += __shfl_xor(l, 32);
@@ -502,11 +525,11 @@ __global__ __launch_bounds__(256) void prefill_wide_kernel(PrefillArgs a)
             stage_pages(st, ra, kv_begin, tid);
             stage_load(st, a, ra, kv_begin, tid);
             stage_pages(st, ra, kv_begin + KT, tid);
-            stage_store(st, lds[0], tid);
+            stage_store(st, lds[0], kv_begin, kv_len, tid);
             if (ntiles > 1) {
                 stage_load(st, a, ra, kv_begin + KT, tid);
                 stage_pages(st, ra, kv_begin + 2 * KT, tid);
-                stage_store(st, lds[1], tid);
+                stage_store(st, lds[1], kv_begin + KT, kv_len, tid);
                 if (ntiles > 2) {
                     stage_load(st, a, ra, kv_begin + 2 * KT, tid);
                     stage_pages(st, ra, kv_begin + 3 * KT, tid);
@@ -545,14 +568,7 @@ __global__ __launch_bounds__(256) void prefill_wide_kernel(PrefillArgs a)
                                   (W < 0 || k0 >= pos_last - W);
             if (!interior) {
 #pragma unroll
-                for (int n = 0; n < 2; ++n)
-#pragma unroll
-                    for (int i = 0; i < 16; ++i) {
-                        const int key = k0 + 8 * (i >> 2) + 4 * hw + (i & 3);
-                        const bool vis = key < kv_len && (!a.causal || key <= p_row[n]) &&
-                                         (W < 0 || key >= p_row[n] - W);
-                        s_cur[n][i] = vis ? s_cur[n][i] : kNegInf;
-                    }
+                for (int n = 0; n < 2; ++n) mask_tile(s_cur[n], k0, hw, p_row[n], kv_len, a.causal, W);
             }
 
             // region 1: PV of tile j-1 on the matrix cores, row maxima on the VALU
@@ -642,7 +658,7 @@ __global__ __launch_bounds__(256) void prefill_wide_kernel(PrefillArgs a)
 
             // stage tile j+2 into its LDS set, start loading tile j+3
             if (j + 2 < ntiles) {
-                stage_store(st, lds[nn], tid);
+                stage_store(st, lds[nn], k0 + 2 * KT, kv_len, tid);
                 if (j + 3 < ntiles) {
                     stage_load(st, a, ra, k0 + 3 * KT, tid);
                     stage_pages(st, ra, k0 + 4 * KT, tid);
