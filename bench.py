@@ -78,6 +78,128 @@ def load_traffic(kernel: str):
     return ent.get("hbm_bytes_per_launch")
 
 
+def prefill_algorithmic_bytes(case) -> int:
+    """Compulsory HBM bytes of one prefill launch: Q read once, the K and V rows
+    the queries can see read once, O written once (same dtype), LSE in fp32."""
+    W = case.window_left
+    esz = case.q.element_size()
+    kv_rows = 0
+    for qo, kv in zip(case.qo_lens, case.kv_lens):
+        first = max(0, kv - qo - W) if W >= 0 else 0
+        kv_rows += kv - first
+    tokens = sum(case.qo_lens)
+    return (2 * tokens * case.num_qo_heads * case.head_dim * esz
+            + 2 * kv_rows * case.num_kv_heads * case.head_dim * esz
+            + tokens * case.num_qo_heads * 4)
+
+
+COPY_BYTES = 1 << 30        # calibration copy: 1 GiB read + 1 GiB written
+
+
+def profile_kernel(which: str, reps: int) -> None:
+    """Launch one kernel `reps` times and nothing else timed, for rocprofv3
+    counter passes; prints the source digest the counters belong to."""
+    import torch
+
+    from paged_kv_sliding_amd import pkvs as P
+    from paged_kv_sliding_amd.synth import build_case
+
+    torch.cuda.set_device(0)
+    print(f"source_digest={source_digest()}", flush=True)
+    if which == "copy":
+        src = torch.empty(COPY_BYTES, dtype=torch.uint8, device="cuda").fill_(7)
+        dst = torch.empty_like(src)
+        for _ in range(reps):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        print(f"copy bytes={COPY_BYTES} reps={reps}", flush=True)
+        return
+    name = "long_prefill" if which == "prefill" else "split_decode"
+    c = build_case(name, device="cuda")
+    att = P.BatchAttention(P.PKVS_PREFILL if which == "prefill" else P.PKVS_DECODE,
+                           num_qo_heads=c.num_qo_heads, num_kv_heads=c.num_kv_heads,
+                           head_dim=c.head_dim, page_size=c.page_size, dtype=c.dtype,
+                           window_left=c.window_left, fixed_split_size=c.fixed_split_size,
+                           batch_capacity=c.batch_size, qo_capacity=sum(c.qo_lens),
+                           kv_capacity=max(c.kv_lens))
+    if which == "prefill":
+        att.plan(qo_indptr=c.qo_indptr.cpu(), kv_indptr=c.kv_indptr.cpu(),
+                 kv_last_page_len=c.kv_last_page_len.cpu())
+    else:
+        att.plan(kv_indptr=c.kv_indptr.cpu(), kv_last_page_len=c.kv_last_page_len.cpu())
+    o = torch.empty_like(c.q)
+    lse = torch.empty(c.q.shape[:2], dtype=torch.float32, device="cuda")
+    for _ in range(reps):
+        att.run(c.q, c.k_cache, c.v_cache, c.kv_indices, sm_scale=c.sm_scale,
+                window_left=c.window_left, out=o, lse=lse)
+    torch.cuda.synchronize()
+    alg = prefill_algorithmic_bytes(c) if which == "prefill" else decode_bytes(c, c.window_left)
+    print(f"{which} workload={name} reps={reps} algorithmic_bytes={alg}", flush=True)
+
+
+def _counter_means(csv_path: str, counter: str) -> dict:
+    """Mean per-dispatch value of `counter` for each kernel in a rocprofv3
+    counter_collection.csv."""
+    import csv
+
+    acc = {}
+    with open(csv_path, newline="") as f:
+        for row in csv.DictReader(f):
+            if row["Counter_Name"] != counter:
+                continue
+            name = row["Kernel_Name"]
+            acc.setdefault(name, []).append(float(row["Counter_Value"]))
+    return {k: sum(v) / len(v) for k, v in acc.items()}, {k: len(v) for k, v in acc.items()}
+
+
+def ingest_counters(d: str) -> None:
+    """Turn the FETCH_SIZE / WRITE_SIZE passes under `d` into HBM bytes per
+    launch, calibrated by the plain 1 GiB copy, and write profiles/traffic.json."""
+    import glob
+
+    digest = source_digest()
+    for out in glob.glob(os.path.join(d, "*.out")):
+        for ln in open(out):
+            if ln.startswith("source_digest=") and ln.strip().split("=")[1] != digest:
+                sys.exit(f"ingest: {out} was taken on other kernel sources; run the passes again")
+
+    def pass_means(kind, ctr):
+        path = os.path.join(d, f"{ctr.lower()}_{kind}", "p_counter_collection.csv")
+        return _counter_means(path, ctr)
+
+    def pick(means, key):
+        names = [n for n in means[0] if key in n]
+        if len(names) != 1:
+            sys.exit(f"ingest: expected one kernel matching {key!r}, found {names}")
+        return names[0]
+
+    # calibration: KiB the counters report for a copy of COPY_BYTES in and out
+    cal = {}
+    for ctr in ("FETCH_SIZE", "WRITE_SIZE"):
+        m = pass_means("copy", ctr)
+        n = pick(m, "copyBuffer")
+        cal[ctr] = COPY_BYTES / (m[0][n] * 1024.0)
+    res = {"calibration": {"copy_bytes": COPY_BYTES,
+                           "fetch_factor": round(cal["FETCH_SIZE"], 4),
+                           "write_factor": round(cal["WRITE_SIZE"], 4)}}
+    for kind, kernels in (("prefill", ["prefill_bf16_kernel<128"]),
+                          ("decode", ["decode_bf16_kernel<128", "decode_merge_kernel<128"])):
+        fm, wm = pass_means(kind, "FETCH_SIZE"), pass_means(kind, "WRITE_SIZE")
+        for key in kernels:
+            nf, nw = pick(fm, key), pick(wm, key)
+            fetch = fm[0][nf] * 1024.0 * cal["FETCH_SIZE"]
+            write = wm[0][nw] * 1024.0 * cal["WRITE_SIZE"]
+            res[key + ">"] = {"source_digest": digest, "dispatches": fm[1][nf],
+                              "fetch_bytes_per_launch": int(fetch),
+                              "write_bytes_per_launch": int(write),
+                              "hbm_bytes_per_launch": int(fetch + write)}
+    path = os.path.join(ROOT, "profiles", "traffic.json")
+    with open(path, "w") as f:
+        json.dump(res, f, indent=1)
+        f.write("\n")
+    print(json.dumps(res, indent=1))
+
+
 def cpu_baseline(case, budget_s: float = 15.0):
     """Time the CPU oracle on a bounded sample of the prefill workload."""
     import numpy as np
@@ -121,11 +243,23 @@ def main():
     ap.add_argument("--cpu-budget", type=float, default=15.0)
     ap.add_argument("--only", choices=["prefill", "decode", "all"], default="all",
                     help="restrict the timed step (for profiling runs)")
+    ap.add_argument("--profile-kernel", choices=["prefill", "decode", "copy"],
+                    help="launch only this kernel --reps times (rocprofv3 counter passes)")
+    ap.add_argument("--reps", type=int, default=5)
+    ap.add_argument("--ingest-counters", metavar="DIR",
+                    help="write profiles/traffic.json from FETCH_SIZE/WRITE_SIZE passes in DIR")
     args = ap.parse_args()
+    if args.ingest_counters:
+        ingest_counters(args.ingest_counters)
+        return
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py: this build measures one GPU only; multi-GPU sharding is a design "
               "note, not a code path (run with --gpus 1)", file=sys.stderr)
         sys.exit(2)
+
+    if args.profile_kernel:
+        profile_kernel(args.profile_kernel, args.reps)
+        return
 
     import torch
 
@@ -265,6 +399,7 @@ def main():
                             "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
                             "frac": round(tflops / PEAK_BF16_TFLOPS, 4),
                             "traffic": load_traffic("prefill_bf16_kernel<128>"),
+                            "algorithmic_bytes": prefill_algorithmic_bytes(pre),
                             "kernel": "prefill_bf16_kernel<128>",
                             "work_per_launch": flops}
     if "dec" in res:
