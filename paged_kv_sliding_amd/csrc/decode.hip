@@ -37,6 +37,13 @@ namespace pkvs {
 
 namespace {
 
+// K and V rows are streamed once per work item and never re-read by it:
+// non-temporal loads keep them from displacing other lines in the caches.
+__device__ __forceinline__ bf16x8 load_stream(const void *p)
+{
+    return __builtin_bit_cast(bf16x8, __builtin_nontemporal_load(reinterpret_cast<const u32x4 *>(p)));
+}
+
 template <int D>
 struct DecodeBuf {
     static constexpr int KS = D / 32;            // QK k-steps (32 dims each)
@@ -98,8 +105,8 @@ __device__ __forceinline__ void decode_load(DecodeBuf<D> &buf, const DecodeArgs 
         nhd_offset(window_page(a, pw, tk1), tk1 & (P - 1), P, hk, a.num_kv_heads, D);
 #pragma unroll
     for (int s = 0; s < KS; ++s) {
-        buf.k0[s] = load_bf16x8(K + rk0 + 32 * s + 8 * g);
-        buf.k1[s] = load_bf16x8(K + rk1 + 32 * s + 8 * g);
+        buf.k0[s] = load_stream(K + rk0 + 32 * s + 8 * g);
+        buf.k1[s] = load_stream(K + rk1 + 32 * s + 8 * g);
     }
 
     // value rows: keys blk+4g+i and blk+16+4g+i (i = 0..3), dims 8r..8r+7
@@ -125,7 +132,7 @@ __device__ __forceinline__ void decode_load(DecodeBuf<D> &buf, const DecodeArgs 
     for (int u = 0; u < NV; ++u)
 #pragma unroll
         for (int j = 0; j < 8; ++j)
-            buf.v[u][j] = (8 * r + 128 * u < D) ? load_bf16x8(V + rv[j] + 128 * u + 8 * r)
+            buf.v[u][j] = (8 * r + 128 * u < D) ? load_stream(V + rv[j] + 128 * u + 8 * r)
                                                 : zero_bf16x8();
 }
 
@@ -187,7 +194,15 @@ __device__ __forceinline__ void decode_compute(const DecodeBuf<D> &buf, DecodeSt
     }
 }
 
+// Register buffers in the pipeline: for D <= 128 one wave holds three 32-key
+// buffers (two in flight while the third is consumed) and still fits in one
+// wave's 512 registers; D = 256 keeps two.
 template <int D>
+constexpr int decode_stages() { return D >= 256 ? 2 : 3; }
+
+// NS register buffers of 32 keys each: NS-1 blocks are in flight while one is
+// being computed.
+template <int D, int NS>
 __global__ __launch_bounds__(kDecodeThreads) void decode_bf16_kernel(DecodeArgs a)
 {
     constexpr int KS = D / 32, NV = DecodeBuf<D>::NV;
@@ -226,26 +241,26 @@ __global__ __launch_bounds__(kDecodeThreads) void decode_bf16_kernel(DecodeArgs 
             pw.last_pg = (t1 - 1) >> a.log2_page;
             pw.cur = load_page_id(a, pw, pw.base + lane);
             pw.nxt = load_page_id(a, pw, pw.base + 64 + lane);
-            DecodeBuf<D> A, B;
-            decode_load<D>(A, a, pw, t0, t1, hk, lane);
+            DecodeBuf<D> buf[NS];
+#pragma unroll
+            for (int s = 0; s + 1 < NS; ++s)
+                if (t0 + kDecodeBlock * s < t1)
+                    decode_load<D>(buf[s], a, pw, t0 + kDecodeBlock * s, t1, hk, lane);
             int blk = t0;
-            for (;;) {
-                if (blk + kDecodeBlock < t1) {
-                    decode_load<D>(B, a, pw, blk + kDecodeBlock, t1, hk, lane);
-                    decode_compute<D>(A, st, qf, blk, lo, t1, a.scale_log2, lane);
-                } else {
-                    decode_compute<D>(A, st, qf, blk, lo, t1, a.scale_log2, lane);
-                    break;
+            bool done = false;
+            while (!done) {
+#pragma unroll
+                for (int s = 0; s < NS; ++s) {
+                    const int ahead = blk + kDecodeBlock * (NS - 1);
+                    if (ahead < t1)
+                        decode_load<D>(buf[(s + NS - 1) % NS], a, pw, ahead, t1, hk, lane);
+                    decode_compute<D>(buf[s], st, qf, blk, lo, t1, a.scale_log2, lane);
+                    blk += kDecodeBlock;
+                    if (blk >= t1) {
+                        done = true;
+                        break;
+                    }
                 }
-                blk += kDecodeBlock;
-                if (blk + kDecodeBlock < t1) {
-                    decode_load<D>(A, a, pw, blk + kDecodeBlock, t1, hk, lane);
-                    decode_compute<D>(B, st, qf, blk, lo, t1, a.scale_log2, lane);
-                } else {
-                    decode_compute<D>(B, st, qf, blk, lo, t1, a.scale_log2, lane);
-                    break;
-                }
-                blk += kDecodeBlock;
             }
         }
 
@@ -349,9 +364,9 @@ __global__ __launch_bounds__(kMergeThreads) void decode_merge_kernel(DecodeArgs 
 hipError_t launch_decode_bf16(const DecodeArgs &a, int head_dim, int grid, hipStream_t s)
 {
     switch (head_dim) {
-    case 64: decode_bf16_kernel<64><<<grid, kDecodeThreads, 0, s>>>(a); break;
-    case 128: decode_bf16_kernel<128><<<grid, kDecodeThreads, 0, s>>>(a); break;
-    case 256: decode_bf16_kernel<256><<<grid, kDecodeThreads, 0, s>>>(a); break;
+    case 64: decode_bf16_kernel<64, decode_stages<64>()><<<grid, kDecodeThreads, 0, s>>>(a); break;
+    case 128: decode_bf16_kernel<128, decode_stages<128>()><<<grid, kDecodeThreads, 0, s>>>(a); break;
+    case 256: decode_bf16_kernel<256, decode_stages<256>()><<<grid, kDecodeThreads, 0, s>>>(a); break;
     default: return hipErrorInvalidValue;
     }
     return hipGetLastError();
@@ -376,15 +391,15 @@ int decode_bf16_blocks_per_cu(int head_dim)
     hipError_t e = hipErrorInvalidValue;
     switch (head_dim) {
     case 64:
-        e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, decode_bf16_kernel<64>,
+        e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, decode_bf16_kernel<64, decode_stages<64>()>,
                                                          kDecodeThreads, 0);
         break;
     case 128:
-        e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, decode_bf16_kernel<128>,
+        e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, decode_bf16_kernel<128, decode_stages<128>()>,
                                                          kDecodeThreads, 0);
         break;
     case 256:
-        e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, decode_bf16_kernel<256>,
+        e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, decode_bf16_kernel<256, decode_stages<256>()>,
                                                          kDecodeThreads, 0);
         break;
     }

@@ -107,6 +107,9 @@ static int validate_desc(const pkvs_desc *d)
     if (!is_pow2(d->page_size) || d->page_size > 1024)
         return fail(PKVS_ERR_UNSUPPORTED, "page_size %d must be a power of two <= 1024",
                     d->page_size);
+    if (int64_t(d->page_size) * d->num_kv_heads * d->head_dim >= (int64_t(1) << 31))
+        return fail(PKVS_ERR_UNSUPPORTED, "one page (page_size x num_kv_heads x head_dim "
+                    "elements) must stay below 2^31 elements");
     if (d->dtype != PKVS_BF16 && d->dtype != PKVS_FP32)
         return fail(PKVS_ERR_UNSUPPORTED, "dtype %d not built (bf16, fp32)", d->dtype);
     if (d->dtype == PKVS_BF16 && (!is_pow2(group) || group > 16))
@@ -271,7 +274,10 @@ static int build_decode(Plan *p, const std::vector<Req> &reqs)
         const int64_t ws =
             d.window_left >= 0 ? std::max<int64_t>(0, r.kv_len - 1 - d.window_left) : 0;
         const int64_t base = ws / kDecodeBlock * kDecodeBlock;
-        const int64_t nchunks = r.kv_len == 0 ? 1 : ceil_div(r.kv_len - base, c);
+        int64_t nchunks = r.kv_len == 0 ? 1 : ceil_div(r.kv_len - base, c);
+        // a trailing piece shorter than one key block joins the chunk before it
+        // rather than becoming a work item and a partial of its own
+        if (nchunks > 1 && r.kv_len - base - (nchunks - 1) * c < kDecodeBlock) --nchunks;
         for (int32_t hk = 0; hk < d.num_kv_heads; ++hk) {
             if (nchunks > 1) {
                 merges.insert(merges.end(), {int32_t(b), hk, int32_t(slot), int32_t(nchunks)});
@@ -279,7 +285,7 @@ static int build_decode(Plan *p, const std::vector<Req> &reqs)
             for (int64_t k = 0; k < nchunks; ++k) {
                 It it;
                 const int64_t t0 = base + k * c;
-                const int64_t t1 = std::min<int64_t>(r.kv_len, t0 + c);
+                const int64_t t1 = k + 1 == nchunks ? r.kv_len : t0 + c;
                 it.cost = t1 - t0;
                 it.w[kDiRequest] = int32_t(b);
                 it.w[kDiKvHead] = hk;

@@ -85,11 +85,12 @@ struct RowAddr {
     {
         return kv_indices[page_base + (clamp_key(key) >> log2_page)];
     }
-    // element offset of `key` (clamped into the request) on page `pg`
+    // element offset of `key` (clamped into the request) on page `pg`; the
+    // planner keeps page_stride below 2^31, so one 32x32->64 multiply does
     __device__ __forceinline__ int64_t offset(int32_t pg, int key) const
     {
-        const int32_t p = min(max(pg, 0), int32_t(num_pages - 1));
-        return int64_t(p) * page_stride +
+        const uint32_t p = uint32_t(min(max(pg, 0), int32_t(num_pages - 1)));
+        return int64_t(uint64_t(p) * uint32_t(page_stride)) +
                int32_t((clamp_key(key) & page_mask) * int32_t(slot_stride) + int32_t(head_off));
     }
 };
@@ -298,26 +299,45 @@ __global__ __launch_bounds__(NW * 64) void prefill_bf16_kernel(PrefillArgs a)
         // once here, so the loop's first MFMA does not wait for the in-flight
         // K/V loads of later tiles.
         __builtin_amdgcn_s_waitcnt(0);
-        f32x16 s_cur;
-        if (ntiles > 0) s_cur = qk_tile<D>(lds[0], qf, l32, hw);
+        // S^T of tile 0 (s_a); each step leaves the next tile's in s_b
+        f32x16 s_a, s_b;
+        if (ntiles > 0) s_a = qk_tile<D>(lds[0], qf, l32, hw);
 
         // Ping-pong: with 8 waves, waves w and w+4 share a SIMD.  Waves 4..7
         // issue the PV product of a tile one iteration late, so in every
         // iteration one wave of each SIMD starts with its exponentials
         // (vector ALU) while the other starts with PV (matrix core).
-        const bool lag = NW == 8 && wave >= 4;
-        bf16x8 pb_prev[2] = {zero_bf16x8(), zero_bf16x8()};
-        for (int j = 0; j < ntiles; ++j) {
+        const bool lag = NW == 8 && __builtin_amdgcn_readfirstlane(wave) >= 4;
+        bf16x8 pb_a[2] = {zero_bf16x8(), zero_bf16x8()};
+        bf16x8 pb_b[2] = {zero_bf16x8(), zero_bf16x8()};
+
+        // one key tile: s_in = S^T of tile j in, s_out = S^T of tile j+1 out;
+        // pb_out = P^T of tile j, pb_in = P^T of tile j-1 (lagging waves)
+        auto step = [&](int j, const f32x16 &s_in, f32x16 &s_out, bf16x8 (&pb_out)[2],
+                        const bf16x8 (&pb_in)[2]) __attribute__((always_inline)) {
             const int k0 = kv_begin + j * KT;
-            if (lag && j > 0) pv_tile<D>(lds[(j - 1) & 3], pb_prev, o, tr_key, tr_dim);
+            if (lag && j > 0) pv_tile<D>(lds[(j - 1) & (NBUF - 1)], pb_in, o, tr_key, tr_dim);
+            // K operands of tile j+1 (its LDS set is ready; after the last tile
+            // they are read but unused), requested before the row maximum
+            const PrefillBuf<D> &bn = lds[(j + 1) & (NBUF - 1)];
+            bf16x8 kf[KSTEPS];
+#pragma unroll
+            for (int ks = 0; ks < KSTEPS; ++ks)
+                kf[ks] = *reinterpret_cast<const bf16x8 *>(&bn.k[l32][ks * 16 + hw * 8]);
 
             // accumulator entry i holds key k0 + 8*(i/4) + 4*hw + i%4 of this row
-            f32x16 s = s_cur;
+            f32x16 s = s_in;
             const bool interior = k0 + KT <= kv_len && (!a.causal || k0 + KT - 1 <= pos0) &&
                                   (W < 0 || k0 >= pos_last - W);
             if (!interior) mask_tile(s, k0, hw, p_row, kv_len, a.causal, W);
+            // row maximum: lane-local over 16 keys, then across the two halves
+            // of the wave with a lane swap (a VALU op, no LDS round trip)
             float mx = max16(s);
-            mx = fmaxf(mx, __shfl_xor(mx, 32)) * c;
+            {
+                const auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(mx),
+                                                                 __float_as_uint(mx), false, false);
+                mx = fmaxf(__uint_as_float(sw[0]), __uint_as_float(sw[1])) * c;
+            }
 
             // lazy rescale: keep the running maximum unless some row's grows by
             // more than 2^8 (probabilities then stay below 2^8, exact in fp32
@@ -333,26 +353,17 @@ __global__ __launch_bounds__(NW * 64) void prefill_bf16_kernel(PrefillArgs a)
             }
             const float mu = m == kNegInf ? 0.f : m;
 
-            // S^T of tile j+1 (its LDS set is ready; after the last tile the
-            // result is simply unused) is interleaved by hand with this tile's
-            // exponentials: each dependent QK MFMA is followed by the FMA+exp of
-            // 16/KSTEPS scores, which the vector ALU runs while the matrix core
-            // works.  The fences keep the compiler from regrouping them.
+            // S^T of tile j+1 interleaved by hand with this tile's exponentials:
+            // each dependent QK MFMA is followed by the FMA+exp of 16/KSTEPS
+            // scores, which the vector ALU runs while the matrix core works.
+            // The fences keep the compiler from regrouping them.
             constexpr int EPS = 16 / KSTEPS;  // scores per QK step (D=128: 2)
-            const PrefillBuf<D> &bn = lds[(j + 1) & 3];
-            f32x16 s_nxt;
 #pragma unroll
-            for (int i = 0; i < 16; ++i) s_nxt[i] = 0.f;
+            for (int i = 0; i < 16; ++i) s_out[i] = 0.f;
             f32x16 pr;
-            // all K operands of the next tile are requested up front so their
-            // LDS latency hides behind the first steps
-            bf16x8 kf[KSTEPS];
-#pragma unroll
-            for (int ks = 0; ks < KSTEPS; ++ks)
-                kf[ks] = *reinterpret_cast<const bf16x8 *>(&bn.k[l32][ks * 16 + hw * 8]);
 #pragma unroll
             for (int ks = 0; ks < KSTEPS; ++ks) {
-                s_nxt = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf[ks], qf[ks], s_nxt, 0, 0, 0);
+                s_out = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf[ks], qf[ks], s_out, 0, 0, 0);
 #pragma unroll
                 for (int e = 0; e < EPS; ++e) {
                     const int i = ks * EPS + e;
@@ -365,33 +376,33 @@ __global__ __launch_bounds__(NW * 64) void prefill_bf16_kernel(PrefillArgs a)
 #pragma unroll
             for (int i = 0; i < 8; ++i) t8[i] = pr[2 * i] + pr[2 * i + 1];
             l += ((t8[0] + t8[1]) + (t8[2] + t8[3])) + ((t8[4] + t8[5]) + (t8[6] + t8[7]));
-            bf16x8 pb[2];
 #pragma unroll
             for (int kk = 0; kk < 2; ++kk) {
                 f32x8 p8;
 #pragma unroll
                 for (int jj = 0; jj < 8; ++jj) p8[jj] = pr[8 * kk + jj];
-                pb[kk] = __builtin_convertvector(p8, bf16x8);
+                pb_out[kk] = __builtin_convertvector(p8, bf16x8);
             }
-            if (!lag) {
-                pv_tile<D>(lds[j & 3], pb, o, tr_key, tr_dim);
-            } else {
-                pb_prev[0] = pb[0];
-                pb_prev[1] = pb[1];
-            }
+            if (!lag) pv_tile<D>(lds[j & (NBUF - 1)], pb_out, o, tr_key, tr_dim);
 
             // stage tile j+2 into the free LDS set, start loading tile j+3
             if (j + 2 < ntiles) {
-                stage_store(st, lds[(j + 2) & 3], k0 + 2 * KT, kv_len, tid);
+                stage_store(st, lds[(j + 2) & (NBUF - 1)], k0 + 2 * KT, kv_len, tid);
                 if (j + 3 < ntiles) {
                     stage_load(st, a, ra, k0 + 3 * KT, tid);
                     stage_pages(st, ra, k0 + 4 * KT, tid);
                 }
             }
             __syncthreads();
-            s_cur = s_nxt;
+        };
+
+        for (int j = 0; j < ntiles; ++j) {
+            step(j, s_a, s_b, pb_a, pb_b);
+            s_a = s_b;
+            pb_b[0] = pb_a[0];
+            pb_b[1] = pb_a[1];
         }
-        if (lag && ntiles > 0) pv_tile<D>(lds[(ntiles - 1) & 3], pb_prev, o, tr_key, tr_dim);
+        if (lag && ntiles > 0) pv_tile<D>(lds[(ntiles - 1) & (NBUF - 1)], pb_b, o, tr_key, tr_dim);
 
         // epilogue: the two half-waves hold disjoint keys of each row
         l += __shfl_xor(l, 32);

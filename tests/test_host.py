@@ -62,6 +62,9 @@ def err_code(fn):
     (dict(prefill_variant=6), P.PKVS_ERR_INVALID_ARG),
     (dict(prefill_variant=2, head_dim=256), P.PKVS_ERR_UNSUPPORTED),
     (dict(prefill_variant=3, head_dim=256), P.PKVS_ERR_UNSUPPORTED),
+    # one page of 1024 slots x 8192 kv heads x 256 dims is 2^31 elements
+    (dict(num_qo_heads=8192, num_kv_heads=8192, head_dim=256, page_size=1024),
+     P.PKVS_ERR_UNSUPPORTED),
 ])
 def test_descriptor_rejections(kw, code):
     assert err_code(lambda: P.pkvs_plan_create(desc(**kw))) == code
@@ -137,7 +140,7 @@ def test_prefill_first_tile_matches_paged_trim():
 
 
 @pytest.mark.parametrize("W,split", [(-1, -1), (-1, 2048), (0, -1), (31, 64), (1023, 256),
-                                     (4095, 2048), (-1, 32)])
+                                     (4095, 2048), (-1, 32), (4095, 1024), (100, 64)])
 def test_decode_chunks_partition_the_window(W, split):
     kv = [0, 1, 2, 31, 32, 33, 500, 4096, 5000, 17]
     h = P.pkvs_plan_create(desc(P.PKVS_DECODE, num_qo_heads=32, num_kv_heads=8, window_left=W,
@@ -168,7 +171,10 @@ def test_decode_chunks_partition_the_window(W, split):
             for t0, t1, lo, slot in ch:
                 assert t0 % 32 == 0 and t0 < t1 and lo == max(ws, t0) and lo < t1
                 if split > 0:
-                    assert t1 - t0 <= split
+                    # only a last chunk grows, by a piece shorter than one 32-key block
+                    assert t1 - t0 <= split or (t1 == n and t1 - t0 < split + 32)
+            if split > 0 and len(ch) > 1:
+                assert ch[-1][1] - ch[-1][0] >= 32
             if len(ch) == 1:
                 assert ch[0][3] == -1
             else:
