@@ -91,7 +91,10 @@ typedef enum pkvs_kind { PKVS_PREFILL = 0, PKVS_DECODE = 1 } pkvs_kind;
  *  prefill_variant  prefill kernel shape: 0 = planner's choice (from head_dim and
  *                   qo_capacity), 1 = 4 waves x 32 rows, 2 = 8 waves x 32 rows,
  *                   3 = 4 waves x 64 rows, software-pipelined (2 and 3: head_dim
- *                   <= 128); rows are (query token, head) pairs
+ *                   <= 128), 4 = 8 waves x 32 rows with K/V rows loaded straight
+ *                   into LDS (head_dim 128; a plan() whose items span more than
+ *                   2048 pages of keys runs variant 2 instead); rows are (query
+ *                   token, head) pairs
  *  batch_capacity   largest batch a plan() call may describe
  *  qo_capacity      prefill: largest total number of query tokens
  *  kv_capacity      largest kv_len of one request
@@ -127,6 +130,7 @@ typedef struct pkvs_plan_info {
     int32_t item_words;      /* int32 words per work item */
     int32_t query_tile;      /* prefill: query tokens per item */
     int32_t num_cus;         /* compute units the grid was sized for */
+    int32_t prefill_variant; /* prefill: kernel variant the last plan() runs */
 } pkvs_plan_info;
 
 typedef struct pkvs_plan pkvs_plan;

@@ -58,7 +58,11 @@ enum PrefillVariant {
     kPrefillRows128 = 1,  // 4 waves x 32 rows
     kPrefillRows256 = 2,  // 8 waves x 32 rows
     kPrefillWide = 3,     // 4 waves x 64 rows, software-pipelined (head_dim <= 128)
+    kPrefillDma = 4,      // 8 waves x 32 rows, K/V rows loaded straight into LDS
+                          // (head_dim 128; an item's key range spans at most
+                          // kPrefillDmaPages pages)
 };
+constexpr int kPrefillDmaPages = 2048;
 constexpr int kPrefillKvTile = 32;     // keys per step
 constexpr int kGenericQTile = 16;      // fp32 path: query tokens per item
 constexpr int kGenericThreads = 256;

@@ -124,10 +124,13 @@ static int validate_desc(const pkvs_desc *d)
                                       d->fixed_split_size % kDecodeBlock))
         return fail(PKVS_ERR_INVALID_ARG, "fixed_split_size %d must be -1 or a positive "
                     "multiple of %d", d->fixed_split_size, kDecodeBlock);
-    if (d->prefill_variant < 0 || d->prefill_variant > 3)
-        return fail(PKVS_ERR_INVALID_ARG, "prefill_variant %d must be 0..3", d->prefill_variant);
+    if (d->prefill_variant < 0 || d->prefill_variant > 4)
+        return fail(PKVS_ERR_INVALID_ARG, "prefill_variant %d must be 0..4", d->prefill_variant);
     if (d->prefill_variant > 1 && d->head_dim > 128)
         return fail(PKVS_ERR_UNSUPPORTED, "256-row prefill variants are built for head_dim <= 128");
+    if (d->prefill_variant == kPrefillDma && d->head_dim != 128)
+        return fail(PKVS_ERR_UNSUPPORTED, "the direct-to-LDS prefill variant is built for "
+                    "head_dim 128");
     if (d->batch_capacity <= 0 || d->kv_capacity <= 0 ||
         (d->kind == PKVS_PREFILL && d->qo_capacity <= 0))
         return fail(PKVS_ERR_INVALID_ARG, "capacities must be positive");
@@ -224,6 +227,25 @@ static void build_prefill(Plan *p, const std::vector<Req> &reqs)
     }
     std::stable_sort(items.begin(), items.end(),
                      [](const It &a, const It &b) { return a.cost > b.cost; });
+    // the direct-to-LDS variant keeps an item's page ids in LDS: the key range
+    // it loads (whole tiles, cut at the request's end) must fit the table
+    p->run_variant = p->prefill_variant;
+    if (p->prefill_variant == kPrefillDma) {
+        for (const It &it : items) {
+            const int64_t kb = it.w[kPiKvBegin];
+            const int64_t kv_len = it.w[kPiKvLen];
+            const int64_t kv_end =
+                d.causal ? std::min<int64_t>(kv_len, int64_t(it.w[kPiPos0]) + it.w[kPiQCount])
+                         : kv_len;
+            if (kv_end <= kb) continue;
+            const int64_t last = std::min(kb + ceil_div(kv_end - kb, kPrefillKvTile) *
+                                                   kPrefillKvTile, kv_len) - 1;
+            if (last / d.page_size - kb / d.page_size + 1 > kPrefillDmaPages) {
+                p->run_variant = kPrefillRows256;
+                break;
+            }
+        }
+    }
     p->n_items = int64_t(items.size());
     p->n_merges = 0;
     p->split_size = 0;
@@ -407,13 +429,19 @@ int pkvs_plan_create(pkvs_plan **out, const pkvs_desc *desc)
         // 256-row tiles.  The wide variant is available on request.
         const int64_t big_tiles = ceil_div(desc->qo_capacity, 256 / group) * desc->num_kv_heads;
         int v = kPrefillRows128;
-        if (desc->head_dim <= 128 && big_tiles >= 2 * p->num_cus) v = kPrefillRows256;
+        if (desc->head_dim <= 128 && big_tiles >= 2 * p->num_cus)
+            v = desc->head_dim == 128 ? kPrefillDma : kPrefillRows256;
         if (desc->prefill_variant) v = desc->prefill_variant;
-        p->prefill_variant = v;
+        // the direct-to-LDS variant needs ~156 KiB of LDS per workgroup
+        if (v == kPrefillDma && p->have_gpu && !fp32 &&
+            prefill_bf16_blocks_per_cu(desc->head_dim, v) < 1)
+            v = kPrefillRows256;
+        p->prefill_variant = p->run_variant = v;
         const int rows = v == kPrefillRows128 ? 128 : 256;
         p->query_tile = fp32 ? kGenericQTile : rows / group;
         p->item_words = kPrefillItemWords;
-        p->block_threads = fp32 ? kGenericThreads : (v == kPrefillRows256 ? 512 : 256);
+        p->block_threads =
+            fp32 ? kGenericThreads : (v == kPrefillRows256 || v == kPrefillDma ? 512 : 256);
         int per_cu = p->have_gpu && !fp32 ? prefill_bf16_blocks_per_cu(desc->head_dim, v) : 0;
         p->grid_blocks = p->num_cus * std::max(per_cu, fp32 ? 2 : 1);
     } else {
@@ -513,6 +541,7 @@ int pkvs_plan_get_info(const pkvs_plan *p, pkvs_plan_info *info)
     info->split_size = p->split_size;
     info->item_words = p->item_words;
     info->query_tile = p->query_tile;
+    info->prefill_variant = p->desc.kind == PKVS_PREFILL ? p->run_variant : 0;
     info->num_cus = p->num_cus;
     return PKVS_OK;
 }

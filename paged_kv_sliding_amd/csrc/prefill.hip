@@ -217,12 +217,82 @@ __device__ __forceinline__ void pv_tile(const PrefillBuf<D> &b, const bf16x8 (&p
         }
 }
 
-template <int D, int NW>
+// Direct-to-LDS staging (DMA = true, head_dim 128, 8 waves).  Each K/V row of
+// a tile is fetched with one global_load_lds_dword: the 64 lanes move the
+// row's 256 bytes straight into its padded LDS row, with no registers, no
+// address arithmetic per lane (a scalar base per row plus the lane's fixed
+// 4-byte offset) and no LDS store instruction.  The loads are tracked only
+// by the vector memory counter, so the tile sets are waited for by hand: six
+// tiles are in flight ahead of the one being computed, in eight LDS sets.
+// The page ids of the item's key range sit in an LDS table filled by the
+// item's prologue, so finding a row's page is an LDS read.
+constexpr int DMA_SETS = 8;
+constexpr int DMA_AHEAD = DMA_SETS - 2;  // sets j-1 (lagging PV) .. j+AHEAD
+constexpr int DMA_ROWS = KT / 8;         // rows of K (and of V) per wave per tile
+constexpr int DMA_PER_TILE = 2 * DMA_ROWS;  // loads per wave per tile
+
+// s_waitcnt vmcnt(N), the other counters left alone (gfx9 encoding)
+template <int N>
+__device__ __forceinline__ void wait_vmcnt()
+{
+    static_assert(N >= 0 && N < 64, "vmcnt is six bits");
+    __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4) | (15 << 8));
+}
+
+// Row loads global -> LDS (global_load_lds_dword): the 64 lanes move one
+// 256-byte row, lane i's bytes 4i..4i+3 to LDS byte address M0 + 4i.  M0 is
+// a register the compiler reserves, so each statement restores it.
+//
+// One K row and the V row at the same offset:
+__device__ __forceinline__ void dma_row_kv(uint32_t mk, uint32_t mv, uint32_t lane_off,
+                                           const void *ksrc, const void *vsrc)
+{
+    uint32_t saved;
+    asm volatile("s_mov_b32 %0, m0\n\t"
+                 "s_mov_b32 m0, %1\n\tglobal_load_lds_dword %3, %4\n\t"
+                 "s_mov_b32 m0, %2\n\tglobal_load_lds_dword %3, %5\n\t"
+                 "s_mov_b32 m0, %0"
+                 : "=&s"(saved)
+                 : "s"(mk), "s"(mv), "v"(lane_off), "s"(ksrc), "s"(vsrc)
+                 : "memory");
+}
+
+// Four K rows and four V rows at the lane offsets off[0..3] from one base each:
+__device__ __forceinline__ void dma_rows4_kv(const uint32_t (&mk)[4], const uint32_t (&mv)[4],
+                                             const uint32_t (&off)[4], const void *kb,
+                                             const void *vb)
+{
+    uint32_t saved;
+    asm volatile("s_mov_b32 %0, m0\n\t"
+                 "s_mov_b32 m0, %1\n\tglobal_load_lds_dword %9, %13\n\t"
+                 "s_mov_b32 m0, %2\n\tglobal_load_lds_dword %10, %13\n\t"
+                 "s_mov_b32 m0, %3\n\tglobal_load_lds_dword %11, %13\n\t"
+                 "s_mov_b32 m0, %4\n\tglobal_load_lds_dword %12, %13\n\t"
+                 "s_mov_b32 m0, %5\n\tglobal_load_lds_dword %9, %14\n\t"
+                 "s_mov_b32 m0, %6\n\tglobal_load_lds_dword %10, %14\n\t"
+                 "s_mov_b32 m0, %7\n\tglobal_load_lds_dword %11, %14\n\t"
+                 "s_mov_b32 m0, %8\n\tglobal_load_lds_dword %12, %14\n\t"
+                 "s_mov_b32 m0, %0"
+                 : "=&s"(saved)
+                 : "s"(mk[0]), "s"(mk[1]), "s"(mk[2]), "s"(mk[3]), "s"(mv[0]), "s"(mv[1]),
+                   "s"(mv[2]), "s"(mv[3]), "v"(off[0]), "v"(off[1]), "v"(off[2]), "v"(off[3]),
+                   "s"(kb), "s"(vb)
+                 : "memory");
+}
+
+template <int D, int NW, bool DMA>
 __global__ __launch_bounds__(NW * 64) void prefill_bf16_kernel(PrefillArgs a)
 {
+    static_assert(!DMA || (D == 128 && NW == 8), "direct-to-LDS staging: D = 128, 8 waves");
     constexpr int KSTEPS = D / 16;  // QK k-steps
     constexpr int DT = D / 32;      // O^T dim tiles
-    __shared__ __attribute__((aligned(16))) PrefillBuf<D> lds[NBUF];
+    constexpr int NS = DMA ? DMA_SETS : NBUF;  // LDS tile sets (a power of two)
+    struct Lds {
+        PrefillBuf<D> set[NS];
+        int32_t pages[DMA ? kPrefillDmaPages : 1];
+    };
+    __shared__ __attribute__((aligned(16))) Lds sh;
+    PrefillBuf<D> *const lds = sh.set;
 
     const int tid = threadIdx.x;
     const int wave = tid >> 6, lane = tid & 63, l32 = lane & 31, hw = lane >> 5;
@@ -244,6 +314,19 @@ __global__ __launch_bounds__(NW * 64) void prefill_bf16_kernel(PrefillArgs a)
     ra.log2_page = a.log2_page;
     ra.page_mask = a.page_size - 1;
 
+    // direct-to-LDS staging: LDS byte address of set 0, the wave's rows
+    const uint32_t lds0 =
+        uint32_t(reinterpret_cast<uintptr_t>((__attribute__((address_space(3))) void *)lds));
+    const int uwave = __builtin_amdgcn_readfirstlane(wave);
+    const uint32_t lane_off = 4u * uint32_t(lane);
+    const uint32_t page_bytes = uint32_t(ra.page_stride * 2);
+    const int32_t slot_bytes = int32_t(ra.slot_stride * 2);
+    uint32_t row_off[DMA_ROWS];  // lane offset of row i of a same-page run
+#pragma unroll
+    for (int i = 0; i < DMA_ROWS; ++i) row_off[i] = lane_off + uint32_t(i * slot_bytes);
+    const char *const Kb = static_cast<const char *>(a.k);
+    const char *const Vb = static_cast<const char *>(a.v);
+
     for (int it = blockIdx.x; it < n_items; it += gridDim.x) {
         const int32_t *w = a.ws + kHeaderWords + int64_t(it) * kPrefillItemWords;
         const int hk = w[kPiKvHead], q_begin = w[kPiQBegin], q_count = w[kPiQCount];
@@ -255,6 +338,8 @@ __global__ __launch_bounds__(NW * 64) void prefill_bf16_kernel(PrefillArgs a)
         ra.page_base = w[kPiPageBase];
         ra.kv_len = kv_len;
         ra.head_off = int64_t(hk) * D;
+        const int pt_lo = kv_begin >> a.log2_page;
+        const int32_t head_bytes = int32_t(ra.head_off * 2);
 
         // this lane's row (S^T and O^T keep one row per lane: column l32)
         const int row = wave * 32 + l32;
@@ -276,29 +361,103 @@ __global__ __launch_bounds__(NW * 64) void prefill_bf16_kernel(PrefillArgs a)
 #pragma unroll
             for (int i = 0; i < 16; ++i) o[dt][i] = 0.f;
 
-        // prologue: tiles 0 and 1 in LDS sets 0 and 1, tile 2 in registers,
-        // tile 3's page ids read
-        Stage<D, NW> st;
-        if (ntiles > 0) {
-            stage_pages(st, ra, kv_begin, tid);
-            stage_load(st, a, ra, kv_begin, tid);
-            stage_pages(st, ra, kv_begin + KT, tid);
-            stage_store(st, lds[0], kv_begin, kv_len, tid);
-            if (ntiles > 1) {
-                stage_load(st, a, ra, kv_begin + KT, tid);
-                stage_pages(st, ra, kv_begin + 2 * KT, tid);
-                stage_store(st, lds[1], kv_begin + KT, kv_len, tid);
-                if (ntiles > 2) {
-                    stage_load(st, a, ra, kv_begin + 2 * KT, tid);
-                    stage_pages(st, ra, kv_begin + 3 * KT, tid);
+        // Issue the row loads of tile t (direct-to-LDS staging): the wave's
+        // DMA_ROWS consecutive rows of K and of V.  Keys past the item's last
+        // tile or past the request read its last loaded key (finite data,
+        // masked out), so tiles past the end can be issued as well and every
+        // wave always has the same number of loads in flight.  Page ids come
+        // from the LDS table; `pg0` is the id of the page of the first row.
+        const int kv_last = min(kv_begin + ntiles * KT, kv_len) - 1;
+        // page id of `key` from the LDS table; the planner keeps every index
+        // inside the entries the prologue wrote, the clamps only keep a
+        // corrupt work list from reading past the table or the cache
+        auto page_entry = [&](int key) __attribute__((always_inline)) {
+            const int e = min(max((key >> a.log2_page) - pt_lo, 0), kPrefillDmaPages - 1);
+            return min(max(sh.pages[e], 0), int32_t(a.num_pages - 1));
+        };
+        auto dma_tile = [&](int t, int32_t pg0) __attribute__((always_inline)) {
+            const int k0 = kv_begin + t * KT;
+            const int r0 = DMA_ROWS * uwave;
+            const uint32_t set_b = lds0 + uint32_t((t & (NS - 1)) * sizeof(PrefillBuf<D>));
+            const uint32_t mk = set_b + uint32_t(offsetof(PrefillBuf<D>, k) + r0 * (D + KPAD) * 2);
+            const uint32_t mv = set_b + uint32_t(offsetof(PrefillBuf<D>, v) + r0 * (D + VPAD) * 2);
+            const int key0 = min(k0 + r0, kv_last);
+            static_assert(DMA_ROWS == 4, "dma_rows4_kv moves four rows");
+            if (k0 + r0 + DMA_ROWS - 1 <= kv_last &&
+                (key0 & ra.page_mask) + DMA_ROWS <= a.page_size) {
+                // the rows are consecutive slots of one page: one scalar base,
+                // the row step sits in the lane offsets
+                const int64_t off = int64_t(uint64_t(uint32_t(pg0)) * page_bytes) +
+                                    int32_t((key0 & ra.page_mask) * slot_bytes + head_bytes);
+                uint32_t m0k[DMA_ROWS], m0v[DMA_ROWS];
+#pragma unroll
+                for (int i = 0; i < DMA_ROWS; ++i) {
+                    m0k[i] = mk + uint32_t(i * (D + KPAD) * 2);
+                    m0v[i] = mv + uint32_t(i * (D + VPAD) * 2);
+                }
+                dma_rows4_kv(m0k, m0v, row_off, Kb + off, Vb + off);
+            } else {
+#pragma unroll
+                for (int i = 0; i < DMA_ROWS; ++i) {
+                    const int key = min(k0 + r0 + i, kv_last);
+                    const int32_t pg = __builtin_amdgcn_readfirstlane(page_entry(key));
+                    const int64_t off = int64_t(uint64_t(uint32_t(pg)) * page_bytes) +
+                                        int32_t((key & ra.page_mask) * slot_bytes + head_bytes);
+                    dma_row_kv(mk + uint32_t(i * (D + KPAD) * 2), mv + uint32_t(i * (D + VPAD) * 2),
+                               lane_off, Kb + off, Vb + off);
                 }
             }
+        };
+        // LDS read of the page id of the wave's first row of tile t
+        auto dma_page = [&](int t) __attribute__((always_inline)) {
+            return page_entry(min(kv_begin + t * KT + DMA_ROWS * uwave, kv_last));
+        };
+
+        Stage<D, NW> st;
+        if constexpr (DMA) {
+            // prologue: page table of the item (ids clamped into the cache),
+            // then tiles 0 .. AHEAD-1 in flight; wait for tiles 0 and 1
+            const int pt_n =
+                ntiles > 0 ? min((kv_last >> a.log2_page) - pt_lo + 1, kPrefillDmaPages) : 0;
+            for (int e = tid; e < pt_n; e += NW * 64) {
+                const int32_t pg = a.kv_indices[ra.page_base + pt_lo + e];
+                sh.pages[e] = min(max(pg, 0), int32_t(a.num_pages - 1));
+            }
+            // the Q operand and the page ids have landed (and nothing else is
+            // in flight): later waits count only row loads
+            __builtin_amdgcn_s_waitcnt(0);
+            __syncthreads();
+            if (ntiles > 0) {
+#pragma unroll 1
+                for (int t = 0; t < DMA_AHEAD; ++t)
+                    dma_tile(t, __builtin_amdgcn_readfirstlane(dma_page(t)));
+                wait_vmcnt<(DMA_AHEAD - 2) * DMA_PER_TILE>();  // tiles 0 and 1 landed
+            }
+            __syncthreads();
+        } else {
+            // prologue: tiles 0 and 1 in LDS sets 0 and 1, tile 2 in registers,
+            // tile 3's page ids read
+            if (ntiles > 0) {
+                stage_pages(st, ra, kv_begin, tid);
+                stage_load(st, a, ra, kv_begin, tid);
+                stage_pages(st, ra, kv_begin + KT, tid);
+                stage_store(st, lds[0], kv_begin, kv_len, tid);
+                if (ntiles > 1) {
+                    stage_load(st, a, ra, kv_begin + KT, tid);
+                    stage_pages(st, ra, kv_begin + 2 * KT, tid);
+                    stage_store(st, lds[1], kv_begin + KT, kv_len, tid);
+                    if (ntiles > 2) {
+                        stage_load(st, a, ra, kv_begin + 2 * KT, tid);
+                        stage_pages(st, ra, kv_begin + 3 * KT, tid);
+                    }
+                }
+            }
+            __syncthreads();
+            // Everything issued so far (the Q operand included) has landed: say
+            // so once here, so the loop's first MFMA does not wait for the
+            // in-flight K/V loads of later tiles.
+            __builtin_amdgcn_s_waitcnt(0);
         }
-        __syncthreads();
-        // Everything issued so far (the Q operand included) has landed: say so
-        // once here, so the loop's first MFMA does not wait for the in-flight
-        // K/V loads of later tiles.
-        __builtin_amdgcn_s_waitcnt(0);
         // S^T of tile 0 (s_a); each step leaves the next tile's in s_b
         f32x16 s_a, s_b;
         if (ntiles > 0) s_a = qk_tile<D>(lds[0], qf, l32, hw);
@@ -307,7 +466,7 @@ __global__ __launch_bounds__(NW * 64) void prefill_bf16_kernel(PrefillArgs a)
         // issue the PV product of a tile one iteration late, so in every
         // iteration one wave of each SIMD starts with its exponentials
         // (vector ALU) while the other starts with PV (matrix core).
-        const bool lag = NW == 8 && __builtin_amdgcn_readfirstlane(wave) >= 4;
+        const bool lag = NW == 8 && uwave >= 4;
         bf16x8 pb_a[2] = {zero_bf16x8(), zero_bf16x8()};
         bf16x8 pb_b[2] = {zero_bf16x8(), zero_bf16x8()};
 
@@ -316,10 +475,13 @@ __global__ __launch_bounds__(NW * 64) void prefill_bf16_kernel(PrefillArgs a)
         auto step = [&](int j, const f32x16 &s_in, f32x16 &s_out, bf16x8 (&pb_out)[2],
                         const bf16x8 (&pb_in)[2]) __attribute__((always_inline)) {
             const int k0 = kv_begin + j * KT;
-            if (lag && j > 0) pv_tile<D>(lds[(j - 1) & (NBUF - 1)], pb_in, o, tr_key, tr_dim);
+            // page of tile j+AHEAD, requested early (used at the end of the step)
+            int32_t pg_next = 0;
+            if constexpr (DMA) pg_next = dma_page(j + DMA_AHEAD);
+            if (lag && j > 0) pv_tile<D>(lds[(j - 1) & (NS - 1)], pb_in, o, tr_key, tr_dim);
             // K operands of tile j+1 (its LDS set is ready; after the last tile
             // they are read but unused), requested before the row maximum
-            const PrefillBuf<D> &bn = lds[(j + 1) & (NBUF - 1)];
+            const PrefillBuf<D> &bn = lds[(j + 1) & (NS - 1)];
             bf16x8 kf[KSTEPS];
 #pragma unroll
             for (int ks = 0; ks < KSTEPS; ++ks)
@@ -383,14 +545,21 @@ __global__ __launch_bounds__(NW * 64) void prefill_bf16_kernel(PrefillArgs a)
                 for (int jj = 0; jj < 8; ++jj) p8[jj] = pr[8 * kk + jj];
                 pb_out[kk] = __builtin_convertvector(p8, bf16x8);
             }
-            if (!lag) pv_tile<D>(lds[j & (NBUF - 1)], pb_out, o, tr_key, tr_dim);
+            if (!lag) pv_tile<D>(lds[j & (NS - 1)], pb_out, o, tr_key, tr_dim);
 
-            // stage tile j+2 into the free LDS set, start loading tile j+3
-            if (j + 2 < ntiles) {
-                stage_store(st, lds[(j + 2) & (NBUF - 1)], k0 + 2 * KT, kv_len, tid);
-                if (j + 3 < ntiles) {
-                    stage_load(st, a, ra, k0 + 3 * KT, tid);
-                    stage_pages(st, ra, k0 + 4 * KT, tid);
+            if constexpr (DMA) {
+                // tile j+AHEAD into the set tile j-2 used; then tile j+2 must
+                // have landed (in every wave) before the barrier
+                dma_tile(j + DMA_AHEAD, __builtin_amdgcn_readfirstlane(pg_next));
+                wait_vmcnt<(DMA_AHEAD - 2) * DMA_PER_TILE>();
+            } else {
+                // stage tile j+2 into the free LDS set, start loading tile j+3
+                if (j + 2 < ntiles) {
+                    stage_store(st, lds[(j + 2) & (NS - 1)], k0 + 2 * KT, kv_len, tid);
+                    if (j + 3 < ntiles) {
+                        stage_load(st, a, ra, k0 + 3 * KT, tid);
+                        stage_pages(st, ra, k0 + 4 * KT, tid);
+                    }
                 }
             }
             __syncthreads();
@@ -402,7 +571,7 @@ __global__ __launch_bounds__(NW * 64) void prefill_bf16_kernel(PrefillArgs a)
             pb_b[0] = pb_a[0];
             pb_b[1] = pb_a[1];
         }
-        if (lag && ntiles > 0) pv_tile<D>(lds[(ntiles - 1) & (NBUF - 1)], pb_b, o, tr_key, tr_dim);
+        if (lag && ntiles > 0) pv_tile<D>(lds[(ntiles - 1) & (NS - 1)], pb_b, o, tr_key, tr_dim);
 
         // epilogue: the two half-waves hold disjoint keys of each row
         l += __shfl_xor(l, 32);
@@ -423,7 +592,7 @@ __global__ __launch_bounds__(NW * 64) void prefill_bf16_kernel(PrefillArgs a)
                 a.lse[int64_t(q_begin + row_tok) * a.num_qo_heads + hk * G + row_head] =
                     l > 0.f ? (m + fast_log2(l)) * kLn2 : kNegInf;
         }
-        __syncthreads();  // the next item's prologue overwrites LDS set 0
+        __syncthreads();  // the next item's prologue overwrites the LDS sets
     }
 }
 
@@ -780,7 +949,10 @@ __global__ __launch_bounds__(kGenericThreads) void attention_fp32_kernel(Prefill
 hipError_t launch_prefill_bf16(const PrefillArgs &a, int head_dim, int variant, int grid,
                                hipStream_t s)
 {
-    if (variant == kPrefillWide) {
+    if (variant == kPrefillDma) {
+        if (head_dim != 128) return hipErrorInvalidValue;
+        prefill_bf16_kernel<128, 8, true><<<grid, 512, 0, s>>>(a);
+    } else if (variant == kPrefillWide) {
         switch (head_dim) {
         case 64: prefill_wide_kernel<64><<<grid, 256, 0, s>>>(a); break;
         case 128: prefill_wide_kernel<128><<<grid, 256, 0, s>>>(a); break;
@@ -788,15 +960,15 @@ hipError_t launch_prefill_bf16(const PrefillArgs &a, int head_dim, int variant, 
         }
     } else if (variant == kPrefillRows256) {
         switch (head_dim) {
-        case 64: prefill_bf16_kernel<64, 8><<<grid, 512, 0, s>>>(a); break;
-        case 128: prefill_bf16_kernel<128, 8><<<grid, 512, 0, s>>>(a); break;
+        case 64: prefill_bf16_kernel<64, 8, false><<<grid, 512, 0, s>>>(a); break;
+        case 128: prefill_bf16_kernel<128, 8, false><<<grid, 512, 0, s>>>(a); break;
         default: return hipErrorInvalidValue;
         }
     } else {
         switch (head_dim) {
-        case 64: prefill_bf16_kernel<64, 4><<<grid, 256, 0, s>>>(a); break;
-        case 128: prefill_bf16_kernel<128, 4><<<grid, 256, 0, s>>>(a); break;
-        case 256: prefill_bf16_kernel<256, 4><<<grid, 256, 0, s>>>(a); break;
+        case 64: prefill_bf16_kernel<64, 4, false><<<grid, 256, 0, s>>>(a); break;
+        case 128: prefill_bf16_kernel<128, 4, false><<<grid, 256, 0, s>>>(a); break;
+        case 256: prefill_bf16_kernel<256, 4, false><<<grid, 256, 0, s>>>(a); break;
         default: return hipErrorInvalidValue;
         }
     }
@@ -809,29 +981,32 @@ hipError_t launch_attention_fp32(const PrefillArgs &a, int head_dim, int grid, h
     return hipGetLastError();
 }
 
-int prefill_bf16_blocks_per_cu(int head_dim, int variant)
+template <typename K>
+static int blocks_per_cu(K kernel, int threads)
 {
     int n = 0;
-    hipError_t e = hipErrorInvalidValue;
+    return hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, kernel, threads, 0) == hipSuccess ? n
+                                                                                             : 0;
+}
+
+int prefill_bf16_blocks_per_cu(int head_dim, int variant)
+{
+    if (variant == kPrefillDma)
+        return head_dim == 128 ? blocks_per_cu(prefill_bf16_kernel<128, 8, true>, 512) : 0;
     if (variant == kPrefillWide) {
-        if (head_dim == 64)
-            e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, prefill_wide_kernel<64>, 256, 0);
-        else if (head_dim == 128)
-            e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, prefill_wide_kernel<128>, 256, 0);
-    } else if (variant == kPrefillRows256) {
-        if (head_dim == 64)
-            e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, prefill_bf16_kernel<64, 8>, 512, 0);
-        else if (head_dim == 128)
-            e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, prefill_bf16_kernel<128, 8>, 512, 0);
-    } else {
-        if (head_dim == 64)
-            e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, prefill_bf16_kernel<64, 4>, 256, 0);
-        else if (head_dim == 128)
-            e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, prefill_bf16_kernel<128, 4>, 256, 0);
-        else if (head_dim == 256)
-            e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, prefill_bf16_kernel<256, 4>, 256, 0);
+        if (head_dim == 64) return blocks_per_cu(prefill_wide_kernel<64>, 256);
+        if (head_dim == 128) return blocks_per_cu(prefill_wide_kernel<128>, 256);
+        return 0;
     }
-    return e == hipSuccess ? n : 0;
+    if (variant == kPrefillRows256) {
+        if (head_dim == 64) return blocks_per_cu(prefill_bf16_kernel<64, 8, false>, 512);
+        if (head_dim == 128) return blocks_per_cu(prefill_bf16_kernel<128, 8, false>, 512);
+        return 0;
+    }
+    if (head_dim == 64) return blocks_per_cu(prefill_bf16_kernel<64, 4, false>, 256);
+    if (head_dim == 128) return blocks_per_cu(prefill_bf16_kernel<128, 4, false>, 256);
+    if (head_dim == 256) return blocks_per_cu(prefill_bf16_kernel<256, 4, false>, 256);
+    return 0;
 }
 
 }  // namespace pkvs

@@ -74,7 +74,7 @@ int pkvs_prefill_run(const pkvs_plan *p, const void *q, const void *k_cache, con
     a.window_left = p->desc.window_left;
     a.causal = p->desc.causal;
     hipError_t e = p->desc.dtype == PKVS_BF16
-                       ? launch_prefill_bf16(a, p->desc.head_dim, p->prefill_variant,
+                       ? launch_prefill_bf16(a, p->desc.head_dim, p->run_variant,
                                              p->grid_blocks, stream)
                        : launch_attention_fp32(a, p->desc.head_dim, p->grid_blocks, stream);
     if (e != hipSuccess) return fail(PKVS_ERR_HIP, "prefill launch: %s", hipGetErrorString(e));

@@ -64,6 +64,7 @@ class pkvs_plan_info(ctypes.Structure):
         ("grid_blocks", ctypes.c_int32), ("block_threads", ctypes.c_int32),
         ("split_size", ctypes.c_int32), ("item_words", ctypes.c_int32),
         ("query_tile", ctypes.c_int32), ("num_cus", ctypes.c_int32),
+        ("prefill_variant", ctypes.c_int32),
     ]
 
 

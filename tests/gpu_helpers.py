@@ -19,7 +19,7 @@ def log(msg: str) -> None:
 
 
 def make_attention(case: Case, window_left=None, fixed_split_size=None, disable_split_kv=False,
-                   batch_capacity=None, kv_capacity=None, qo_capacity=None):
+                   batch_capacity=None, kv_capacity=None, qo_capacity=None, prefill_variant=0):
     W = case.window_left if window_left is None else window_left
     kind = P.PKVS_DECODE if case.is_decode else P.PKVS_PREFILL
     split = case.fixed_split_size if fixed_split_size is None else fixed_split_size
@@ -29,7 +29,8 @@ def make_attention(case: Case, window_left=None, fixed_split_size=None, disable_
         causal=case.causal, fixed_split_size=split, disable_split_kv=disable_split_kv,
         batch_capacity=batch_capacity or max(case.batch_size, 1),
         qo_capacity=qo_capacity or max(int(case.qo_indptr[-1]), 1),
-        kv_capacity=kv_capacity or max(max(case.kv_lens, default=1), 1))
+        kv_capacity=kv_capacity or max(max(case.kv_lens, default=1), 1),
+        prefill_variant=prefill_variant)
 
 
 def gpu_run(case: Case, window_left=None, att=None, return_lse=True, **kw):

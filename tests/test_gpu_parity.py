@@ -86,7 +86,9 @@ def test_long_prefill_sampled():
     checked on sampled query tokens (all heads)."""
     case = build_case("long_prefill", device=DEV)
     log("long_prefill run")
-    o, lse = gpu_run(case)
+    att = make_attention(case)
+    o, lse = gpu_run(case, att=att)
+    assert att.info().prefill_variant == 4  # the direct-to-LDS kernel the bench times
     rng = np.random.default_rng(4)
     rows = sorted(set(LONG_ROWS + rng.integers(0, 32768, size=20).tolist()))
     log(f"long_prefill oracle on {len(rows)} rows")
@@ -127,6 +129,43 @@ def test_prefill_small_ragged(P_, W):
     o, lse = gpu_run(case)
     ro, rl = oracle_for(case)
     compare(o, lse, ro, rl, tag=f"prefill P={P_} W={W}")
+
+
+# every bf16 prefill kernel variant on the ragged batch: 1 = 4x32 rows, 2 = 8x32
+# rows (register staging), 3 = 4x64 rows, 4 = 8x32 rows with direct-to-LDS
+# row loads (page sizes 1 and 2 take its per-row page path, the others its
+# same-page path; the last tile of each item its clamped-row path)
+@pytest.mark.parametrize("variant", [1, 2, 3, 4])
+@pytest.mark.parametrize("P_", [1, 2, 4, 16])
+@pytest.mark.parametrize("W", [-1, 0, 33, 200])
+def test_prefill_variants_ragged(variant, P_, W):
+    qo = [1, 70, 0, 33, 129, 5, 300]
+    kv = [1, 70, 9, 300, 129, 700, 301]
+    case = small(qo, kv, H_q=8, H_kv=2, D=128, P_=P_, W=W, seed=variant * 1000 + P_ * 10 + W)
+    att = make_attention(case, prefill_variant=variant)
+    o, lse = gpu_run(case, att=att)
+    assert att.info().prefill_variant == variant
+    ro, rl = oracle_for(case)
+    compare(o, lse, ro, rl, tag=f"prefill variant={variant} P={P_} W={W}")
+
+
+def test_prefill_dma_variant_prefix_non_causal_and_fallback():
+    # non-causal, no window: every item loads all keys of its request
+    case = small([20, 7, 64], [50, 7, 400], H_q=8, H_kv=2, D=128, W=-1, seed=21)
+    case.causal = False
+    att = make_attention(case, prefill_variant=4)
+    o, lse = gpu_run(case, att=att)
+    assert att.info().prefill_variant == 4
+    ro, rl = oracle_for(case)
+    compare(o, lse, ro, rl, tag="dma non-causal")
+    # page size 1 and 2100 keys: an item spans more pages than the LDS page
+    # table holds, so the plan runs the register-staged 256-row kernel
+    case = small([40], [2100], H_q=8, H_kv=2, D=128, P_=1, W=-1, seed=22)
+    att = make_attention(case, prefill_variant=4)
+    o, lse = gpu_run(case, att=att)
+    assert att.info().prefill_variant == 2
+    ro, rl = oracle_for(case)
+    compare(o, lse, ro, rl, tag="dma fallback")
 
 
 @pytest.mark.parametrize("D,G", [(64, 1), (64, 8), (128, 2), (128, 16), (256, 4), (256, 1)])

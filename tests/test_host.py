@@ -184,6 +184,32 @@ def test_decode_chunks_partition_the_window(W, split):
     assert info.num_merges == len(slots)
 
 
+def test_prefill_variant_choice_and_page_table_fallback():
+    """Large head_dim-128 prefill plans pick the direct-to-LDS kernel (variant
+    4); a plan() whose items span more pages than its LDS page table (2048)
+    runs the register-staged 256-row kernel (variant 2) instead."""
+    big = dict(num_qo_heads=32, num_kv_heads=8, window_left=-1, qo_capacity=32768,
+               kv_capacity=65536, batch_capacity=4)
+    h = P.pkvs_plan_create(desc(page_size=16, **big))
+    qop, kvp, last = csr([4096], [4096], 16)
+    P.pkvs_prefill_plan(h, qop, kvp, last, 1, None, None)
+    assert P.pkvs_plan_get_info(h).prefill_variant == 4
+    qop, kvp, last = csr([64], [32768], 16)   # 2048 pages of 16 keys: fits
+    P.pkvs_prefill_plan(h, qop, kvp, last, 1, None, None)
+    assert P.pkvs_plan_get_info(h).prefill_variant == 4
+    qop, kvp, last = csr([64], [32769], 16)   # 2049 pages
+    P.pkvs_prefill_plan(h, qop, kvp, last, 1, None, None)
+    assert P.pkvs_plan_get_info(h).prefill_variant == 2
+    h1 = P.pkvs_plan_create(desc(page_size=1, **dict(big, window_left=1023)))
+    qop, kvp, last = csr([8192], [8192], 1)   # windowed items span ~1100 pages
+    P.pkvs_prefill_plan(h1, qop, kvp, last, 1, None, None)
+    assert P.pkvs_plan_get_info(h1).prefill_variant == 4
+    # head_dim 64 keeps the register-staged kernel; asking for 4 is refused
+    assert P.pkvs_plan_get_info(P.pkvs_plan_create(desc(head_dim=64, **big))).prefill_variant == 2
+    assert err_code(lambda: P.pkvs_plan_create(desc(head_dim=64, prefill_variant=4))) == \
+        P.PKVS_ERR_UNSUPPORTED
+
+
 def test_grid_does_not_depend_on_the_batch():
     h = P.pkvs_plan_create(desc(P.PKVS_DECODE, num_qo_heads=32, num_kv_heads=8, window_left=-1,
                                 batch_capacity=64, kv_capacity=4096))
