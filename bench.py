@@ -64,18 +64,21 @@ def source_digest() -> str:
     return h.hexdigest()[:16]
 
 
-def load_traffic(kernel: str):
-    """HBM bytes per launch from committed rocprofv3 counter runs, if they were
-    taken on the current kernel sources (else None)."""
+def load_traffic(*kernels: str):
+    """HBM bytes per launch (summed over `kernels`) from committed rocprofv3
+    counter runs, if they were taken on the current kernel sources (else None)."""
     path = os.path.join(ROOT, "profiles", "traffic.json")
     try:
         data = json.load(open(path))
     except (OSError, ValueError):
         return None
-    ent = data.get(kernel)
-    if not ent or ent.get("source_digest") != source_digest():
-        return None
-    return ent.get("hbm_bytes_per_launch")
+    total, digest = 0, source_digest()
+    for kernel in kernels:
+        ent = data.get(kernel)
+        if not ent or ent.get("source_digest") != digest:
+            return None
+        total += ent["hbm_bytes_per_launch"]
+    return total
 
 
 def prefill_algorithmic_bytes(case) -> int:
@@ -238,7 +241,7 @@ def main():
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawTextHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
-    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-budget", type=float, default=15.0)
     ap.add_argument("--only", choices=["prefill", "decode", "all"], default="all",
@@ -409,7 +412,8 @@ def main():
         line["roofline_decode"] = {"bound": "hbm", "achieved": round(gbps, 1),
                                    "peak": PEAK_HBM_GBPS, "unit": "GB/s",
                                    "frac": round(gbps / PEAK_HBM_GBPS, 4),
-                                   "traffic": load_traffic("decode_bf16_kernel<128>"),
+                                   "traffic": load_traffic("decode_bf16_kernel<128>",
+                                                           "decode_merge_kernel<128>"),
                                    "kernel": "decode_bf16_kernel<128> + decode_merge_kernel<128>",
                                    "work_per_launch": nbytes}
     if full is not None:
