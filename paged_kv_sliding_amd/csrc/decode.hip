@@ -63,26 +63,48 @@ struct PageWindow {
     int cur, nxt;
 };
 
+// Every load of the block loop is issued unconditionally (indexes clamped),
+// so each block issues the same number of vector memory instructions and the
+// compiler can wait for a block's own loads only, with the blocks behind it
+// still in flight.
 __device__ __forceinline__ int load_page_id(const DecodeArgs &a, const PageWindow &pw, int pg)
 {
-    return pg <= pw.last_pg ? a.kv_indices[pw.page_base + pg] : 0;
+    return a.kv_indices[pw.page_base + min(pg, pw.last_pg)];
 }
 
-__device__ __forceinline__ void window_advance(const DecodeArgs &a, PageWindow &pw, int blk,
+// The window moves (a wave-uniform decision) when a block's first key leaves
+// it; the ids of the window after the current one are re-read on every block
+// (the same ids until it moves).  The empty asm keeps the move a branch: as a
+// select it would wait for the latest id load on every block.
+__device__ __forceinline__ void window_advance(const DecodeArgs &a, PageWindow &pw, int key,
                                                int lane)
 {
-    if ((blk >> a.log2_page) - pw.base >= 64) {
+    if ((key >> a.log2_page) - pw.base >= 64) {
         pw.base += 64;
         pw.cur = pw.nxt;
-        pw.nxt = load_page_id(a, pw, pw.base + 64 + lane);
+        asm volatile("" : "+v"(pw.cur));
     }
+    pw.nxt = load_page_id(a, pw, pw.base + 64 + lane);
 }
 
-__device__ __forceinline__ int64_t window_page(const DecodeArgs &a, const PageWindow &pw, int tok)
+__device__ __forceinline__ int64_t clamp_page(const DecodeArgs &a, int64_t pg)
 {
-    int64_t pg = __shfl(pw.cur, (tok >> a.log2_page) - pw.base);
     pg = pg < 0 ? 0 : pg;
     return pg >= a.num_pages ? a.num_pages - 1 : pg;
+}
+
+// page of key `tok` (any lane's own key): a cross-lane read of the window
+__device__ __forceinline__ int64_t window_page(const DecodeArgs &a, const PageWindow &pw, int tok)
+{
+    return clamp_page(a, __shfl(pw.cur, (tok >> a.log2_page) - pw.base));
+}
+
+// page of key `tok`, the same for every lane: a scalar read of the window
+__device__ __forceinline__ int64_t window_page_uniform(const DecodeArgs &a, const PageWindow &pw,
+                                                       int tok)
+{
+    const int idx = __builtin_amdgcn_readfirstlane((tok >> a.log2_page) - pw.base);
+    return clamp_page(a, __builtin_amdgcn_readlane(pw.cur, idx & 63));
 }
 
 template <int D>
@@ -95,33 +117,33 @@ __device__ __forceinline__ void decode_load(DecodeBuf<D> &buf, const DecodeArgs 
     const uint16_t *K = static_cast<const uint16_t *>(a.k);
     const uint16_t *V = static_cast<const uint16_t *>(a.v);
     const int last = t1 - 1;
-    window_advance(a, pw, blk, lane);
+    // blocks past the end read the request's last key; the window never moves
+    // past its page
+    window_advance(a, pw, min(blk, last), lane);
 
-    // key rows for the A operand of S^T
-    const int tk0 = min(blk + r, last), tk1 = min(blk + 16 + r, last);
-    const int64_t rk0 =
-        nhd_offset(window_page(a, pw, tk0), tk0 & (P - 1), P, hk, a.num_kv_heads, D);
-    const int64_t rk1 =
-        nhd_offset(window_page(a, pw, tk1), tk1 & (P - 1), P, hk, a.num_kv_heads, D);
-#pragma unroll
-    for (int s = 0; s < KS; ++s) {
-        buf.k0[s] = load_stream(K + rk0 + 32 * s + 8 * g);
-        buf.k1[s] = load_stream(K + rk1 + 32 * s + 8 * g);
-    }
-
+    // key rows of the A operand of S^T: keys blk+r and blk+16+r;
     // value rows: keys blk+4g+i and blk+16+4g+i (i = 0..3), dims 8r..8r+7
-    int64_t rv[8];
-    if (P >= 4) {
-        // four consecutive keys starting at a multiple of 4 share a page
-        const int64_t pa = window_page(a, pw, min(blk + 4 * g, last));
-        const int64_t pb = window_page(a, pw, min(blk + 16 + 4 * g, last));
+    const int tk0 = min(blk + r, last), tk1 = min(blk + 16 + r, last);
+    const int64_t head = int64_t(hk) * D;
+    const int64_t slot_stride = int64_t(a.num_kv_heads) * D;
+    int64_t rk0, rk1, rv[8];
+    if (P >= 16) {
+        // a block starts at a multiple of 32 keys, so each 16-key half lies in
+        // one page: two wave-uniform page ids per block, scalar address bases
+        const int64_t page_stride = slot_stride * P;
+        const int64_t ba = window_page_uniform(a, pw, min(blk, last)) * page_stride + head;
+        const int64_t bb = window_page_uniform(a, pw, min(blk + 16, last)) * page_stride + head;
+        rk0 = ba + (tk0 & (P - 1)) * slot_stride;
+        rk1 = bb + (tk1 & (P - 1)) * slot_stride;
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
             const int sa = min(blk + 4 * g + i, last), sb = min(blk + 16 + 4 * g + i, last);
-            rv[i] = nhd_offset(pa, sa & (P - 1), P, hk, a.num_kv_heads, D);
-            rv[4 + i] = nhd_offset(pb, sb & (P - 1), P, hk, a.num_kv_heads, D);
+            rv[i] = ba + (sa & (P - 1)) * slot_stride;
+            rv[4 + i] = bb + (sb & (P - 1)) * slot_stride;
         }
     } else {
+        rk0 = nhd_offset(window_page(a, pw, tk0), tk0 & (P - 1), P, hk, a.num_kv_heads, D);
+        rk1 = nhd_offset(window_page(a, pw, tk1), tk1 & (P - 1), P, hk, a.num_kv_heads, D);
 #pragma unroll
         for (int j = 0; j < 8; ++j) {
             const int t = min(blk + (j < 4 ? 4 * g + j : 16 + 4 * g + j - 4), last);
@@ -129,11 +151,19 @@ __device__ __forceinline__ void decode_load(DecodeBuf<D> &buf, const DecodeArgs 
         }
     }
 #pragma unroll
+    for (int s = 0; s < KS; ++s) {
+        buf.k0[s] = load_stream(K + rk0 + 32 * s + 8 * g);
+        buf.k1[s] = load_stream(K + rk1 + 32 * s + 8 * g);
+    }
+    // (D = 64: lanes r >= 8 read a valid slice of the row and drop it)
+    const int dv = min(8 * r, D - 8);
+#pragma unroll
     for (int u = 0; u < NV; ++u)
 #pragma unroll
-        for (int j = 0; j < 8; ++j)
-            buf.v[u][j] = (8 * r + 128 * u < D) ? load_stream(V + rv[j] + 128 * u + 8 * r)
-                                                : zero_bf16x8();
+        for (int j = 0; j < 8; ++j) {
+            const bf16x8 x = load_stream(V + rv[j] + 128 * u + dv);
+            buf.v[u][j] = (8 * r + 128 * u < D) ? x : zero_bf16x8();
+        }
 }
 
 template <int D>
@@ -166,8 +196,17 @@ __device__ __forceinline__ void decode_compute(const DecodeBuf<D> &buf, DecodeSt
         x[4 + i] = (tb >= lo && tb < t1) ? s1[i] * scale_log2 : kNegInf;
         mx = fmaxf(mx, fmaxf(x[i], x[4 + i]));
     }
-    mx = fmaxf(mx, __shfl_xor(mx, 16));
-    mx = fmaxf(mx, __shfl_xor(mx, 32));
+    // across the four lane groups: row swaps (VALU), no LDS round trip
+    {
+        const auto sw = __builtin_amdgcn_permlane16_swap(__float_as_uint(mx), __float_as_uint(mx),
+                                                         false, false);
+        mx = fmaxf(__uint_as_float(sw[0]), __uint_as_float(sw[1]));
+    }
+    {
+        const auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(mx), __float_as_uint(mx),
+                                                         false, false);
+        mx = fmaxf(__uint_as_float(sw[0]), __uint_as_float(sw[1]));
+    }
     const float m_new = fmaxf(st.m, mx);
     const float m_use = m_new == kNegInf ? 0.f : m_new;
     const float alpha = fast_exp2(st.m - m_use);
@@ -237,23 +276,23 @@ __global__ __launch_bounds__(kDecodeThreads) void decode_bf16_kernel(DecodeArgs 
         if (t0 < t1) {
             PageWindow pw;
             pw.page_base = page_base;
-            pw.base = t0 >> a.log2_page;
+            pw.base = __builtin_amdgcn_readfirstlane(t0 >> a.log2_page);
             pw.last_pg = (t1 - 1) >> a.log2_page;
             pw.cur = load_page_id(a, pw, pw.base + lane);
             pw.nxt = load_page_id(a, pw, pw.base + 64 + lane);
             DecodeBuf<D> buf[NS];
+            // blocks past the end load the request's last key (clamped) and
+            // are never computed
 #pragma unroll
             for (int s = 0; s + 1 < NS; ++s)
-                if (t0 + kDecodeBlock * s < t1)
-                    decode_load<D>(buf[s], a, pw, t0 + kDecodeBlock * s, t1, hk, lane);
+                decode_load<D>(buf[s], a, pw, t0 + kDecodeBlock * s, t1, hk, lane);
             int blk = t0;
             bool done = false;
             while (!done) {
 #pragma unroll
                 for (int s = 0; s < NS; ++s) {
-                    const int ahead = blk + kDecodeBlock * (NS - 1);
-                    if (ahead < t1)
-                        decode_load<D>(buf[(s + NS - 1) % NS], a, pw, ahead, t1, hk, lane);
+                    decode_load<D>(buf[(s + NS - 1) % NS], a, pw, blk + kDecodeBlock * (NS - 1),
+                                   t1, hk, lane);
                     decode_compute<D>(buf[s], st, qf, blk, lo, t1, a.scale_log2, lane);
                     blk += kDecodeBlock;
                     if (blk >= t1) {
