@@ -55,7 +55,9 @@ int pkvs_prefill_run(const pkvs_plan *p, const void *q, const void *k_cache, con
     int rc = check_run(p, PKVS_PREFILL, q, k_cache, v_cache, num_pages, kv_indices_d, o,
                        window_left, causal);
     if (rc) return rc;
-    if (p->n_items == 0) return PKVS_OK;
+    // (an empty work list still launches: the kernels read the item count
+    // from the workspace, so a captured graph replays correctly after any
+    // later plan of the same capacities)
     PrefillArgs a{};
     a.q = q;
     a.k = k_cache;
@@ -89,7 +91,9 @@ int pkvs_decode_run(const pkvs_plan *p, const void *q, const void *k_cache, cons
     int rc = check_run(p, PKVS_DECODE, q, k_cache, v_cache, num_pages, kv_indices_d, o,
                        window_left, 1);
     if (rc) return rc;
-    if (p->n_items == 0) return PKVS_OK;
+    // (an empty work list still launches: the kernels read the item count
+    // from the workspace, so a captured graph replays correctly after any
+    // later plan of the same capacities)
     const int log2g = log2_exact(p->desc.num_qo_heads / p->desc.num_kv_heads);
     const float scale_log2 = sm_scale * 1.44269504088896340736f;
     hipError_t e;
@@ -135,8 +139,10 @@ int pkvs_decode_run(const pkvs_plan *p, const void *q, const void *k_cache, cons
     a.log2_page = log2_exact(p->desc.page_size);
     e = launch_decode_bf16(a, p->desc.head_dim, p->grid_blocks, stream);
     if (e != hipSuccess) return fail(PKVS_ERR_HIP, "decode launch: %s", hipGetErrorString(e));
-    if (p->n_merges > 0) {
-        // fixed grid: sized from the capacity, never from this batch
+    if (p->merges_cap > 0) {
+        // launched whenever the plan can have merges (the kernel reads their
+        // count), with a fixed grid sized from the capacity, never from this
+        // batch: a captured graph stays valid for every later plan
         const int grid = int(std::min<int64_t>(p->merges_cap * group, int64_t(p->num_cus) * 16));
         e = launch_decode_merge(a, p->desc.head_dim, p->desc.dtype, std::max(grid, 1), stream);
         if (e != hipSuccess)

@@ -272,9 +272,12 @@ class BatchAttention:
     def _check_shapes(self, q, k_cache, v_cache, kv_indices, out, lse):
         d = self.desc
         dt = {PKVS_BF16: torch.bfloat16, PKVS_FP32: torch.float32}[d.dtype]
-        exp_q = (self._nnz_qo, d.num_qo_heads, d.head_dim)
+        # rows past the planned batch (capacity-sized buffers, e.g. under a
+        # captured graph) are neither read nor written
+        exp_q = (max(self._nnz_qo, q.shape[0] if q.dim() == 3 else 0), d.num_qo_heads, d.head_dim)
         if tuple(q.shape) != exp_q or q.dtype != dt:
-            raise ValueError(f"q must be {dt} {exp_q}, got {q.dtype} {tuple(q.shape)}")
+            raise ValueError(f"q must be {dt} [>= {self._nnz_qo}, {d.num_qo_heads}, "
+                             f"{d.head_dim}], got {q.dtype} {tuple(q.shape)}")
         if out.shape != q.shape or out.dtype != dt:
             raise ValueError("out must match q")
         kv_shape = (d.page_size, d.num_kv_heads, d.head_dim)

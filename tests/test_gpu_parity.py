@@ -297,6 +297,96 @@ def test_one_hot_values_expose_exact_support(decode, W):
 # ----------------------------------------------------------------- plan lifecycle
 
 
+def _sub_layout(case, picks):
+    """Layout of the requests `picks` of `case`, over the same cache pages:
+    (q rows, kv_indices, qo_indptr, kv_indptr, kv_last_page_len)."""
+    qop, kvp = case.qo_indptr.cpu(), case.kv_indptr.cpu()
+    idx = case.kv_indices.cpu()
+    rows, pages, qo_ind, kv_ind, last = [], [], [0], [0], []
+    for b in picks:
+        rows += list(range(int(qop[b]), int(qop[b + 1])))
+        pages.append(idx[int(kvp[b]):int(kvp[b + 1])])
+        qo_ind.append(qo_ind[-1] + int(qop[b + 1] - qop[b]))
+        kv_ind.append(kv_ind[-1] + int(kvp[b + 1] - kvp[b]))
+        last.append(int(case.kv_last_page_len[b]))
+    i32 = dict(dtype=torch.int32)
+    return (rows, torch.cat(pages).to(**i32), torch.tensor(qo_ind, **i32),
+            torch.tensor(kv_ind, **i32), torch.tensor(last, **i32))
+
+
+@pytest.mark.parametrize("decode", [False, True])
+def test_graph_replay_follows_replans(decode):
+    """run() captured once in a HIP graph stays valid for every later plan() of
+    the same capacities (AMD-Ecosystem/flashinfer PR 234, "Why each fix" 2: the
+    grid and the launch set come from the capacities, the work from the
+    workspace).  Each replay, with eager work and synchronisations between
+    replays, must equal an eager run() of the batch planned last, bit for bit."""
+    if decode:
+        qo, kv = [1] * 6, [300, 1, 77, 2000, 64, 900]
+        case = small(qo, kv, H_q=16, H_kv=2, D=128, P_=16, W=255, seed=61, decode=True, split=64)
+    else:
+        qo, kv = [40, 1, 130, 7, 64], [300, 1, 130, 500, 64]
+        case = small(qo, kv, H_q=8, H_kv=2, D=128, P_=16, W=100, seed=62)
+    att = make_attention(case)
+    B, n_q = case.batch_size, case.q.shape[0]
+    q_buf = case.q.clone()
+    idx_buf = case.kv_indices.clone()
+    o_buf = torch.zeros_like(case.q)
+    l_buf = torch.zeros(n_q, case.num_qo_heads, dtype=torch.float32, device=DEV)
+
+    def plan(layout):
+        _, _, qo_ind, kv_ind, last = layout
+        if decode:
+            att.plan(kv_indptr=kv_ind, kv_last_page_len=last)
+        else:
+            att.plan(qo_indptr=qo_ind, kv_indptr=kv_ind, kv_last_page_len=last)
+
+    def load(layout):
+        rows, pages, *_ = layout
+        q_buf.zero_()
+        q_buf[:len(rows)] = case.q[torch.tensor(rows, device=DEV)]
+        idx_buf.zero_()
+        idx_buf[:len(pages)] = pages.to(DEV)
+
+    def run():
+        att.run(q_buf, case.k_cache, case.v_cache, idx_buf, sm_scale=case.sm_scale,
+                window_left=case.window_left, out=o_buf, lse=l_buf)
+
+    layouts = [_sub_layout(case, list(range(B))), _sub_layout(case, [2]),
+               _sub_layout(case, [0, 3, 4]), _sub_layout(case, list(range(B)))]
+    load(layouts[0])
+    plan(layouts[0])
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        run()  # warm-up outside the capture
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        run()
+    for k, layout in enumerate(layouts):
+        load(layout)
+        plan(layout)
+        n = len(layout[0])
+        o_buf.fill_(7.0)
+        run()
+        torch.cuda.synchronize()
+        want_o, want_l = o_buf[:n].clone(), l_buf[:n].clone()
+        for rep in range(3):
+            o_buf.fill_(-3.0)
+            l_buf.fill_(-3.0)
+            junk = torch.randn(256, 256, device=DEV) @ torch.randn(256, 256, device=DEV)
+            g.replay()
+            torch.cuda.synchronize()
+            assert torch.isfinite(junk).all()
+            assert torch.equal(o_buf[:n], want_o), (k, rep)
+            assert torch.equal(l_buf[:n], want_l), (k, rep)
+        if k == 0:
+            ro, rl = oracle_for(case)
+            compare(want_o, want_l, ro, rl, tag=f"graph decode={decode}")
+
+
 def test_replan_in_place_then_capacity_error():
     big = small([1] * 6, [500, 2000, 33, 4096, 1, 700], H_q=32, H_kv=8, D=128, W=127, seed=61,
                 decode=True)
