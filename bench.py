@@ -20,6 +20,9 @@ Reported (one JSON line):
   cpu_baseline   the CPU oracle (single thread, fp64) on a bounded sample of
                  the prefill workload, in the same unit
   decode_no_window  the same decode batch with window_left -1, timed apart
+  cascade        the cascade prefill (new tokens' K/V contiguous, cached prefix
+                 paged, merged), timed apart on two batches with cached
+                 prefixes, beside the one paged prefill of the same batch
 
     python bench.py [--steps K] [--warmup W] [--gpus 1] [--no-cpu-baseline]
 """
@@ -97,6 +100,80 @@ def prefill_algorithmic_bytes(case) -> int:
 
 
 COPY_BYTES = 1 << 30        # calibration copy: 1 GiB read + 1 GiB written
+
+
+CASCADE_WORKLOADS = {
+    # 8 requests, prefix U[0,1024], U[1,512] new tokens, W 511, head_dim 256
+    "prefix_prefill": None,
+    # the last 8192 tokens of a 32768-token prompt over its cached 24576
+    "chunk_8192_after_24576": dict(qo=[8192], kv=[32768], H_q=32, H_kv=8, D=128, P=16,
+                                   W=4095, seed=6),
+}
+
+
+def bench_cascade(reps: int) -> dict:
+    """Cascade prefill beside the one paged prefill of the same batch, both
+    timed with HIP events around run() on the launch stream."""
+    import torch
+
+    from paged_kv_sliding_amd import pkvs as P
+    from paged_kv_sliding_amd.synth import build_case, cascade_inputs, case_from_lengths
+
+    out = {}
+    for name, w in CASCADE_WORKLOADS.items():
+        if w is None:
+            c = build_case(name, device="cuda")
+        else:
+            c = case_from_lengths(name, w["qo"], w["kv"], num_qo_heads=w["H_q"],
+                                  num_kv_heads=w["H_kv"], head_dim=w["D"], page_size=w["P"],
+                                  dtype=torch.bfloat16, window_left=w["W"], seed=w["seed"],
+                                  device="cuda")
+        W = c.window_left
+        ci = cascade_inputs(c, trim_to=W)
+        kw = dict(num_qo_heads=c.num_qo_heads, num_kv_heads=c.num_kv_heads,
+                  head_dim=c.head_dim, page_size=c.page_size, dtype=c.dtype, window_left=W,
+                  batch_capacity=c.batch_size, qo_capacity=sum(c.qo_lens))
+        cas = P.CascadeAttention(kv_capacity=max(max(ci.table_lens), 1), **kw)
+        cas.plan(qo_indptr=c.qo_indptr.cpu(), kv_indptr=ci.kv_indptr,
+                 kv_last_page_len=ci.kv_last_page_len)
+        one = P.BatchAttention(P.PKVS_PREFILL, kv_capacity=max(c.kv_lens), **kw)
+        one.plan(qo_indptr=c.qo_indptr.cpu(), kv_indptr=c.kv_indptr.cpu(),
+                 kv_last_page_len=c.kv_last_page_len.cpu())
+        o = torch.empty_like(c.q)
+        lse = torch.empty(c.q.shape[:2], dtype=torch.float32, device="cuda")
+
+        def run_cascade():
+            cas.run(c.q, ci.k_extend, ci.v_extend, ci.k_cache, ci.v_cache, ci.kv_indices,
+                    sm_scale=c.sm_scale, window_left=W, out=o, lse=lse)
+
+        def run_one():
+            one.run(c.q, c.k_cache, c.v_cache, c.kv_indices, sm_scale=c.sm_scale,
+                    window_left=W, out=o, lse=lse)
+
+        res = {}
+        for tag, fn in (("cascade", run_cascade), ("paged", run_one)):
+            for _ in range(3):
+                fn()
+            ts = []
+            for _ in range(reps):
+                a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+                a.record()
+                fn()
+                b.record()
+                torch.cuda.synchronize()
+                ts.append(a.elapsed_time(b))
+            res[tag] = sum(ts) / len(ts)
+        flops = prefill_flops(c)
+        out[name] = {"ms": round(res["cascade"], 4),
+                     "tflops": round(flops / (res["cascade"] * 1e-3) / 1e12, 2),
+                     "paged_prefill_ms": round(res["paged"], 4),
+                     "window_effective_flops": flops,
+                     "prefill_variant": cas.info().prefill_variant,
+                     "batch": c.batch_size, "new_tokens": sum(c.qo_lens),
+                     "cached_keys_in_tables": sum(ci.table_lens)}
+        del ci, c
+        torch.cuda.empty_cache()
+    return out
 
 
 def profile_kernel(which: str, reps: int) -> None:
@@ -244,7 +321,7 @@ def main():
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-budget", type=float, default=15.0)
-    ap.add_argument("--only", choices=["prefill", "decode", "all"], default="all",
+    ap.add_argument("--only", choices=["prefill", "decode", "cascade", "all"], default="all",
                     help="restrict the timed step (for profiling runs)")
     ap.add_argument("--profile-kernel", choices=["prefill", "decode", "copy"],
                     help="launch only this kernel --reps times (rocprofv3 counter passes)")
@@ -262,6 +339,10 @@ def main():
 
     if args.profile_kernel:
         profile_kernel(args.profile_kernel, args.reps)
+        return
+
+    if args.only == "cascade":
+        print(json.dumps({"cascade": bench_cascade(args.steps)}), flush=True)
         return
 
     import torch
@@ -418,6 +499,9 @@ def main():
                                    "work_per_launch": nbytes}
     if full is not None:
         line["decode_no_window"] = full
+    if args.only == "all":
+        print("bench: cascade prefill", file=sys.stderr, flush=True)
+        line["cascade"] = bench_cascade(max(5, args.steps // 2))
     if not args.no_cpu_baseline and args.only == "all":
         print("bench: cpu baseline (oracle)", file=sys.stderr, flush=True)
         line["cpu_baseline"] = cpu_baseline(pre, args.cpu_budget)

@@ -16,7 +16,10 @@
  *            (v_a, s_a, v_b, s_b) -> (v, s) combine launched over a (token,
  *            head) grid), _full_cg_prefill_workspace_bytes (a fixed grid whose
  *            idle blocks exit early; "increase the workspace" failure at plan),
- *            should_use_tensor_core (grouped heads share each K/V load).
+ *            should_use_tensor_core (grouped heads share each K/V load),
+ *            FlashInferIndicesUpdaterPrefill.update_sliding_window and
+ *            _build_swa_prefix_custom_mask (the cascade's trimmed prefix
+ *            table and its left-window mask).
  *  [PR234]   AMD-Ecosystem/flashinfer PR "fix(rocm): correct AITER decode
  *            backend gaps -- sliding window, CUDA graph, return_lse" --
  *            "Why each fix" 1 (window_left = W: the query at kv_len-1 sees W+1
@@ -71,18 +74,21 @@ typedef enum pkvs_status {
 
 typedef enum pkvs_dtype { PKVS_BF16 = 0, PKVS_FP32 = 1 } pkvs_dtype;
 
-typedef enum pkvs_kind { PKVS_PREFILL = 0, PKVS_DECODE = 1 } pkvs_kind;
+typedef enum pkvs_kind { PKVS_PREFILL = 0, PKVS_DECODE = 1, PKVS_CASCADE = 2 } pkvs_kind;
 
 /* Fixed properties of a plan.  window_left and causal are fixed here, at plan
  * time ([PR31501] "What"); run() must pass the same values.
- *  kind             PKVS_PREFILL or PKVS_DECODE
+ *  kind             PKVS_PREFILL, PKVS_DECODE or PKVS_CASCADE (a prefill whose
+ *                   new tokens' keys come in a contiguous array and whose cached
+ *                   prefix sits in the paged cache; see pkvs_cascade_plan)
  *  num_qo_heads     multiple of num_kv_heads; group = num_qo_heads/num_kv_heads
  *                   must be a power of two <= 16 (bf16 path)
  *  head_dim         64, 128 or 256
  *  page_size        power of two, 1 .. 1024
  *  dtype            q, k_cache, v_cache and o share it (PKVS_BF16 or PKVS_FP32;
  *                   accumulation is fp32 either way)
- *  causal           prefill: 1, or 0 only with window_left = -1; decode: ignored
+ *  causal           prefill, cascade: 1, or 0 only with window_left = -1;
+ *                   decode: ignored
  *  window_left      -1 (no window) or W >= 0 (W+1 visible keys, [PR234] 1)
  *  fixed_split_size decode: keys per KV chunk (a multiple of 32), or -1 to let
  *                   the planner choose; the partial (o, lse) of the chunks of
@@ -96,8 +102,9 @@ typedef enum pkvs_kind { PKVS_PREFILL = 0, PKVS_DECODE = 1 } pkvs_kind;
  *                   2048 pages of keys runs variant 2 instead); rows are (query
  *                   token, head) pairs
  *  batch_capacity   largest batch a plan() call may describe
- *  qo_capacity      prefill: largest total number of query tokens
- *  kv_capacity      largest kv_len of one request
+ *  qo_capacity      prefill, cascade: largest total number of query tokens
+ *  kv_capacity      largest kv_len of one request (cascade: the most cached
+ *                   keys one request's page table may hold)
  * The launch grid and the workspaces are sized from these capacities and the
  * device alone, never from one batch ([PR234] 2; [FIB]
  * _full_cg_prefill_workspace_bytes). */
@@ -188,6 +195,47 @@ int pkvs_decode_run(const pkvs_plan *plan, const void *q, const void *k_cache,
                     void *o, float *lse, float sm_scale, int32_t window_left,
                     hipStream_t stream);
 
+/* Plan a cascade prefill ([FIB] FlashInferAttnBackend.forward_extend, the
+ * branch for a batch with cached prefixes: a ragged pass over the new tokens'
+ * own keys, a paged pass over the cached prefix, and _safe_merge_state of the
+ * two (o, lse) pairs).  The plan must have kind PKVS_CASCADE.
+ *  qo_indptr_h [batch+1]   new (query) tokens of request b; their keys and
+ *                          values are the same rows of k_extend / v_extend
+ *  kv_indptr_h, kv_last_page_len_h   the page table of the cached keys that
+ *                          precede the new tokens: request b's table holds
+ *                          kv_len_b keys, the last kv_len_b before its first
+ *                          new token.  It may start anywhere at or before the
+ *                          window's reach -- the whole prefix, or only its
+ *                          last min(prefix, window_left) keys ([FIB]
+ *                          FlashInferIndicesUpdaterPrefill.update_sliding_window
+ *                          trims it so); keys beyond the window are skipped.
+ * New token i of request b (position kv_len_b + i relative to the table's
+ * first key) sees cached key j iff window_left < 0 or j >= kv_len_b + i -
+ * window_left ([FIB] _build_swa_prefix_custom_mask), and new key i' iff
+ * i' <= i (causal) and (window_left < 0 or i' >= i - window_left).  The
+ * result equals pkvs_prefill_run over one page table holding the table's keys
+ * followed by the new keys.  Zero new tokens or zero cached keys are legal.
+ * Builds both passes' work lists and enqueues two host-to-device copies into
+ * int_ws on `stream` (int_ws == NULL: dry plan).  float_ws holds the paged
+ * pass's o and both passes' lse.  Errors as pkvs_prefill_plan (a request may
+ * have more new tokens than cached keys). */
+int pkvs_cascade_plan(pkvs_plan *plan, const int32_t *qo_indptr_h, const int32_t *kv_indptr_h,
+                      const int32_t *kv_last_page_len_h, int32_t batch_size, void *float_ws,
+                      size_t float_ws_bytes, void *int_ws, size_t int_ws_bytes,
+                      hipStream_t stream);
+
+/* Run the planned cascade: q, o [nnz_qo, num_qo_heads, head_dim]; k_extend,
+ * v_extend [nnz_qo, num_kv_heads, head_dim] (row r is the key / value of query
+ * token r); k_cache, v_cache, num_pages and kv_indices_d as pkvs_prefill_run
+ * (they may be NULL / 0 when the planned batch has no cached keys); lse
+ * nullable.  Three launches on `stream`: the ragged pass writes o and an lse
+ * into float_ws, the paged pass its (o, lse) into float_ws, and the merge
+ * combines them into o and lse in place.  window_left must equal the plan's. */
+int pkvs_cascade_run(const pkvs_plan *plan, const void *q, const void *k_extend,
+                     const void *v_extend, const void *k_cache, const void *v_cache,
+                     int64_t num_pages, const int32_t *kv_indices_d, void *o, float *lse,
+                     float sm_scale, int32_t window_left, hipStream_t stream);
+
 /* Combine two attention partials over disjoint key sets ([FIB]
  * _safe_merge_state):  s = ln(exp(s_a) + exp(s_b)),
  * v = exp(s_a - s) * v_a + exp(s_b - s) * v_b;  s_a = s_b = -inf gives v = 0,
@@ -202,7 +250,8 @@ int pkvs_merge_state(const void *v_a, const float *s_a, const void *v_b, const f
 int pkvs_plan_get_info(const pkvs_plan *plan, pkvs_plan_info *info);
 
 /* Host copy of the last plan()'s work list: up to max_items items of
- * info.item_words int32 words each into dst; *n_items receives the count. */
+ * info.item_words int32 words each into dst; *n_items receives the count.  A
+ * cascade lists its ragged pass's items, then its paged pass's. */
 int pkvs_plan_copy_items(const pkvs_plan *plan, int32_t *dst, int64_t max_items,
                          int64_t *n_items);
 

@@ -19,6 +19,7 @@ enum HeaderField {
     kHdrNumMerges = 1,
     kHdrMergeOffset = 2,  // in int32 words from the start of the workspace
     kHdrItemWords = 3,
+    kHdrNumTokens = 4,    // query tokens of the planned batch (the cascade merge reads it)
 };
 
 // Prefill item: one (request, kv head, query tile).
@@ -63,6 +64,11 @@ enum PrefillVariant {
                           // kPrefillDmaPages pages)
 };
 constexpr int kPrefillDmaPages = 2048;
+// A contiguous ("ragged") K/V of [tokens, kv heads, head_dim] is addressed like
+// a paged cache whose page-table entries are row indices: entry t of a request
+// starting at row r0 is r0 + t * kRaggedPage, and key j sits on row
+// entry(j / kRaggedPage) + j % kRaggedPage.
+constexpr int kRaggedPage = 256;
 constexpr int kPrefillKvTile = 32;     // keys per step
 constexpr int kGenericQTile = 16;      // fp32 path: query tokens per item
 constexpr int kGenericThreads = 256;
@@ -79,6 +85,7 @@ struct PrefillArgs {
     int64_t num_pages;
     float scale_log2;   // sm_scale * log2(e)
     int32_t num_qo_heads, num_kv_heads, log2_group, page_size, log2_page;
+    int32_t page_rows;  // cache rows one page-table step spans: page_size, or 1 (ragged)
     int32_t window_left, causal;
 };
 
@@ -102,9 +109,12 @@ hipError_t launch_attention_fp32(const PrefillArgs &a, int head_dim, int grid, h
 hipError_t launch_decode_bf16(const DecodeArgs &a, int head_dim, int grid, hipStream_t s);
 hipError_t launch_decode_merge(const DecodeArgs &a, int head_dim, int dtype, int grid,
                                hipStream_t s);
+// n tokens, or (count != null) the token count the kernel reads from
+// count[0] at run time, at most n
 hipError_t launch_merge_state(const void *va, const float *sa, const void *vb, const float *sb,
-                              void *vo, float *so, int64_t n, int32_t heads, int32_t head_dim,
-                              int32_t dtype, int grid, hipStream_t s);
+                              void *vo, float *so, int64_t n, const int32_t *count,
+                              int32_t heads, int32_t head_dim, int32_t dtype, int grid,
+                              hipStream_t s);
 
 // Resident workgroups per CU of each kernel (occupancy query; 0 if unknown).
 int prefill_bf16_blocks_per_cu(int head_dim, int variant);

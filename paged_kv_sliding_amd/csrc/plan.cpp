@@ -61,6 +61,9 @@ static void size_plan(Plan *p)
     int64_t items = 0, slots = 0, merges = 0;
     if (d.kind == PKVS_PREFILL) {
         items = hkv * (ceil_div(d.qo_capacity, p->query_tile) + B);
+        // a ragged pass's row-index table: at most one entry per kRaggedPage
+        // tokens of each request, rounded up per request
+        if (p->ragged) p->lead_words = (ceil_div(d.qo_capacity, kRaggedPage) + B + 15) / 16 * 16;
     } else {
         // keys a request can present after the window trim, plus the
         // alignment of the first chunk to a key block
@@ -88,16 +91,18 @@ static void size_plan(Plan *p)
     p->items_cap = items;
     p->slots_cap = slots;
     p->merges_cap = merges;
-    p->int_ws_need = sizeof(int32_t) * size_t(kHeaderWords + items * p->item_words +
-                                              merges * kMergeWords);
+    p->int_ws_need = sizeof(int32_t) * size_t(p->lead_words + kHeaderWords +
+                                              items * p->item_words + merges * kMergeWords);
     p->float_ws_need = sizeof(float) * size_t(slots * group * (d.head_dim + 1));
 }
 
 static int validate_desc(const pkvs_desc *d)
 {
     if (!d) return fail(PKVS_ERR_INVALID_ARG, "desc is null");
-    if (d->kind != PKVS_PREFILL && d->kind != PKVS_DECODE)
-        return fail(PKVS_ERR_INVALID_ARG, "kind must be PKVS_PREFILL or PKVS_DECODE");
+    if (d->kind != PKVS_PREFILL && d->kind != PKVS_DECODE && d->kind != PKVS_CASCADE)
+        return fail(PKVS_ERR_INVALID_ARG, "kind must be PKVS_PREFILL, PKVS_DECODE or "
+                    "PKVS_CASCADE");
+    const bool prefill_like = d->kind != PKVS_DECODE;
     if (d->num_qo_heads <= 0 || d->num_kv_heads <= 0 || d->num_qo_heads % d->num_kv_heads)
         return fail(PKVS_ERR_INVALID_ARG, "num_qo_heads (%d) must be a positive multiple of "
                     "num_kv_heads (%d)", d->num_qo_heads, d->num_kv_heads);
@@ -107,9 +112,12 @@ static int validate_desc(const pkvs_desc *d)
     if (!is_pow2(d->page_size) || d->page_size > 1024)
         return fail(PKVS_ERR_UNSUPPORTED, "page_size %d must be a power of two <= 1024",
                     d->page_size);
-    if (int64_t(d->page_size) * d->num_kv_heads * d->head_dim >= (int64_t(1) << 31))
+    const int64_t page_rows = d->kind == PKVS_CASCADE ? std::max(d->page_size, kRaggedPage)
+                                                      : d->page_size;
+    if (page_rows * d->num_kv_heads * d->head_dim >= (int64_t(1) << 31))
         return fail(PKVS_ERR_UNSUPPORTED, "one page (page_size x num_kv_heads x head_dim "
-                    "elements) must stay below 2^31 elements");
+                    "elements, %d rows for a cascade's extend keys) must stay below 2^31 "
+                    "elements", kRaggedPage);
     if (d->dtype != PKVS_BF16 && d->dtype != PKVS_FP32)
         return fail(PKVS_ERR_UNSUPPORTED, "dtype %d not built (bf16, fp32)", d->dtype);
     if (d->dtype == PKVS_BF16 && (!is_pow2(group) || group > 16))
@@ -118,7 +126,7 @@ static int validate_desc(const pkvs_desc *d)
     if (d->window_left < -1)
         return fail(PKVS_ERR_INVALID_ARG, "window_left %d: must be -1 (off) or >= 0",
                     d->window_left);
-    if (d->kind == PKVS_PREFILL && d->causal != 1 && !(d->causal == 0 && d->window_left == -1))
+    if (prefill_like && d->causal != 1 && !(d->causal == 0 && d->window_left == -1))
         return fail(PKVS_ERR_UNSUPPORTED, "non-causal prefill is built only without a window");
     if (d->fixed_split_size != -1 && (d->fixed_split_size <= 0 ||
                                       d->fixed_split_size % kDecodeBlock))
@@ -132,7 +140,7 @@ static int validate_desc(const pkvs_desc *d)
         return fail(PKVS_ERR_UNSUPPORTED, "the direct-to-LDS prefill variant is built for "
                     "head_dim 128");
     if (d->batch_capacity <= 0 || d->kv_capacity <= 0 ||
-        (d->kind == PKVS_PREFILL && d->qo_capacity <= 0))
+        (prefill_like && d->qo_capacity <= 0))
         return fail(PKVS_ERR_INVALID_ARG, "capacities must be positive");
     if (d->kv_capacity > (int64_t(1) << 30) || d->qo_capacity > (int64_t(1) << 30))
         return fail(PKVS_ERR_UNSUPPORTED, "capacities above 2^30 tokens are not supported");
@@ -173,7 +181,7 @@ static int read_layout(const Plan *p, const int32_t *qo_indptr, const int32_t *k
             qo_begin = qo_indptr[b];
             qo_len = int64_t(qo_indptr[b + 1]) - qo_indptr[b];
             if (qo_len < 0) return fail(PKVS_ERR_INVALID_ARG, "qo_indptr decreases at %d", b);
-            if (qo_len > kv_len)
+            if (qo_len > kv_len && !p->queries_after_kv)
                 return fail(PKVS_ERR_INVALID_ARG, "request %d: qo_len %lld > kv_len %lld", b,
                             (long long)qo_len, (long long)kv_len);
         }
@@ -202,7 +210,9 @@ static void build_prefill(Plan *p, const std::vector<Req> &reqs)
     std::vector<It> items;
     for (size_t b = 0; b < reqs.size(); ++b) {
         const Req &r = reqs[b];
-        const int64_t prefix = r.kv_len - r.qo_len;
+        // first query position: after the request's cached prefix, or (a
+        // cascade's prefix pass) after every key of its table
+        const int64_t prefix = p->queries_after_kv ? r.kv_len : r.kv_len - r.qo_len;
         for (int64_t t0 = 0; t0 < r.qo_len; t0 += tq) {
             const int64_t qn = std::min<int64_t>(tq, r.qo_len - t0);
             const int64_t pos0 = prefix + t0;
@@ -249,12 +259,26 @@ static void build_prefill(Plan *p, const std::vector<Req> &reqs)
     p->n_items = int64_t(items.size());
     p->n_merges = 0;
     p->split_size = 0;
-    p->host_ws.assign(kHeaderWords + items.size() * kPrefillItemWords, 0);
-    int32_t *w = p->host_ws.data();
+    p->host_ws.assign(p->lead_words + kHeaderWords + items.size() * kPrefillItemWords, 0);
+    int64_t tokens = 0, keys = 0;
+    for (const Req &r : reqs) {
+        tokens += r.qo_len;
+        keys += r.kv_len;
+    }
+    p->planned_keys = keys;
+    if (p->ragged) {
+        // row-index table: entry t of request b is the row of its key
+        // t * kRaggedPage in the contiguous K/V (rows follow the queries)
+        for (const Req &r : reqs)
+            for (int64_t t = 0; t * kRaggedPage < r.kv_len; ++t)
+                p->host_ws[r.page_base + t] = int32_t(r.qo_begin + t * kRaggedPage);
+    }
+    int32_t *w = p->host_ws.data() + p->lead_words;
     w[kHdrNumItems] = int32_t(items.size());
     w[kHdrNumMerges] = 0;
-    w[kHdrMergeOffset] = int32_t(p->host_ws.size());
+    w[kHdrMergeOffset] = int32_t(p->host_ws.size() - p->lead_words);
     w[kHdrItemWords] = kPrefillItemWords;
+    w[kHdrNumTokens] = int32_t(tokens);
     for (size_t i = 0; i < items.size(); ++i)
         std::memcpy(w + kHeaderWords + i * kPrefillItemWords, items[i].w, sizeof items[i].w);
 }
@@ -392,22 +416,14 @@ static int finish_plan(Plan *p, void *float_ws, size_t float_bytes, void *int_ws
     return PKVS_OK;
 }
 
-}  // namespace pkvs
-
-using namespace pkvs;
-
-extern "C" {
-
-int pkvs_plan_create(pkvs_plan **out, const pkvs_desc *desc)
+// A validated prefill or decode descriptor -> plan object (ragged: a
+// cascade's extend pass, see plan_state.h).
+static int create_plan(const pkvs_desc *desc, bool ragged, Plan **out)
 {
-    clear_error();
-    if (!out) return fail(PKVS_ERR_INVALID_ARG, "out is null");
-    *out = nullptr;
-    int rc = validate_desc(desc);
-    if (rc) return rc;
     Plan *p = new (std::nothrow) Plan();
     if (!p) return fail(PKVS_ERR_INVALID_ARG, "out of host memory");
     p->desc = *desc;
+    p->ragged = ragged;
     const int group = desc->num_qo_heads / desc->num_kv_heads;
     int ndev = 0;
     p->have_gpu = hipGetDeviceCount(&ndev) == hipSuccess && ndev > 0 &&
@@ -464,6 +480,87 @@ int pkvs_plan_create(pkvs_plan **out, const pkvs_desc *desc)
     p->grid_blocks = int32_t(std::max<int64_t>(1, std::min<int64_t>(p->grid_blocks, p->items_cap)));
     *out = p;
     return PKVS_OK;
+}
+
+static void destroy_plan(Plan *p)
+{
+    if (!p) return;
+    destroy_plan(p->ext);
+    destroy_plan(p->pre);
+    for (int i = 0; i < kStages; ++i) {
+        if (p->stage_ev[i]) {
+            if (p->stage_used[i]) (void)hipEventSynchronize(p->stage_ev[i]);
+            (void)hipEventDestroy(p->stage_ev[i]);
+        }
+        if (p->stage[i]) (void)hipHostFree(p->stage[i]);
+    }
+    delete p;
+}
+
+static size_t align256(size_t x) { return (x + 255) / 256 * 256; }
+
+// A cascade prefill is two prefill passes and one merge ([FIB]
+// FlashInferAttnBackend.forward_extend, the branch for requests with a cached
+// prefix).  The extend pass attends each request's new tokens to their own
+// keys, read from a contiguous K/V (causal, with the window); the prefix pass
+// attends them to the cached keys of the page table.  Every cached key comes
+// before every new token, so there only the window's left edge hides keys
+// ([FIB] FlashInferIndicesUpdaterPrefill._build_swa_prefix_custom_mask:
+// visible iff k_abs >= q_abs - window).  merge_state combines the two (o, lse)
+// pairs.  The float workspace holds the prefix pass's o and both passes' lse.
+static int create_cascade(const pkvs_desc *desc, Plan **out)
+{
+    pkvs_desc e = *desc, r = *desc;
+    e.kind = r.kind = PKVS_PREFILL;
+    e.page_size = kRaggedPage;          // row-index table entries
+    e.kv_capacity = desc->qo_capacity;  // a request's extend keys are its queries
+    r.causal = 1;                       // the causal bound never hides a cached key
+    Plan *p = new (std::nothrow) Plan();
+    if (!p) return fail(PKVS_ERR_INVALID_ARG, "out of host memory");
+    p->desc = *desc;
+    int rc = create_plan(&e, true, &p->ext);
+    if (!rc) rc = create_plan(&r, false, &p->pre);
+    if (rc) {
+        destroy_plan(p);
+        return rc;
+    }
+    const Plan *q = p->pre;
+    p->pre->queries_after_kv = true;
+    p->device = q->device;
+    p->have_gpu = q->have_gpu;
+    p->num_cus = q->num_cus;
+    p->grid_blocks = q->grid_blocks;
+    p->block_threads = q->block_threads;
+    p->query_tile = q->query_tile;
+    p->item_words = q->item_words;
+    p->prefill_variant = p->run_variant = q->prefill_variant;
+    p->items_cap = p->ext->items_cap + q->items_cap;
+    p->pre_int_off = align256(p->ext->int_ws_need);
+    p->int_ws_need = p->pre_int_off + q->int_ws_need;
+    const size_t esz = desc->dtype == PKVS_BF16 ? 2 : 4;
+    const size_t rows = size_t(desc->qo_capacity) * size_t(desc->num_qo_heads);
+    p->o2_off = 0;
+    p->lse1_off = align256(rows * size_t(desc->head_dim) * esz);
+    p->lse2_off = p->lse1_off + align256(rows * sizeof(float));
+    p->float_ws_need = p->lse2_off + rows * sizeof(float);
+    *out = p;
+    return PKVS_OK;
+}
+
+}  // namespace pkvs
+
+using namespace pkvs;
+
+extern "C" {
+
+int pkvs_plan_create(pkvs_plan **out, const pkvs_desc *desc)
+{
+    clear_error();
+    if (!out) return fail(PKVS_ERR_INVALID_ARG, "out is null");
+    *out = nullptr;
+    int rc = validate_desc(desc);
+    if (rc) return rc;
+    return desc->kind == PKVS_CASCADE ? create_cascade(desc, out) : create_plan(desc, false, out);
 }
 
 int pkvs_workspace_size(const pkvs_plan *p, size_t *float_ws_bytes, size_t *int_ws_bytes)
@@ -528,6 +625,57 @@ int pkvs_decode_plan(pkvs_plan *p, const int32_t *kv_indptr_h, const int32_t *kv
     return finish_plan(p, float_ws, float_ws_bytes, int_ws, int_ws_bytes, stream);
 }
 
+int pkvs_cascade_plan(pkvs_plan *p, const int32_t *qo_indptr_h, const int32_t *kv_indptr_h,
+                      const int32_t *kv_last_page_len_h, int32_t batch_size, void *float_ws,
+                      size_t float_ws_bytes, void *int_ws, size_t int_ws_bytes,
+                      hipStream_t stream)
+{
+    clear_error();
+    if (!p) return fail(PKVS_ERR_INVALID_ARG, "plan is null");
+    if (p->desc.kind != PKVS_CASCADE) return fail(PKVS_ERR_INVALID_ARG, "not a cascade plan");
+    p->planned_device = false;
+    Plan *e = p->ext, *r = p->pre;
+    e->planned_device = r->planned_device = false;
+    std::vector<Req> pre_reqs;
+    int rc = read_layout(r, qo_indptr_h, kv_indptr_h, kv_last_page_len_h, batch_size, pre_reqs);
+    if (rc) return rc;
+    // extend keys of request b: rows qo_begin .. qo_begin + qo_len - 1 of the
+    // contiguous K/V, reached through table entries page_base ..
+    std::vector<Req> ext_reqs(pre_reqs.size());
+    int64_t entries = 0;
+    for (size_t b = 0; b < pre_reqs.size(); ++b) {
+        const Req &q = pre_reqs[b];
+        ext_reqs[b] = Req{q.qo_begin, q.qo_len, q.qo_len, entries};
+        entries += ceil_div(q.qo_len, kRaggedPage);
+    }
+    build_prefill(e, ext_reqs);
+    build_prefill(r, pre_reqs);
+    if (e->n_items > e->items_cap || r->n_items > r->items_cap)
+        return fail(PKVS_ERR_CAPACITY, "cascade work lists (%lld, %lld items) exceed capacity "
+                    "(%lld, %lld)", (long long)e->n_items, (long long)r->n_items,
+                    (long long)e->items_cap, (long long)r->items_cap);
+    p->n_items = e->n_items + r->n_items;
+    p->run_variant = r->run_variant;
+    p->planned_keys = r->planned_keys;
+    p->batch = e->batch = r->batch = batch_size;
+    if (!int_ws) return PKVS_OK;  // dry plan
+    if (int_ws_bytes < p->int_ws_need)
+        return fail(PKVS_ERR_WORKSPACE, "int workspace %zu bytes < required %zu; increase the "
+                    "workspace buffer size", int_ws_bytes, p->int_ws_need);
+    if (!float_ws || float_ws_bytes < p->float_ws_need)
+        return fail(PKVS_ERR_WORKSPACE, "float workspace %zu bytes < required %zu; increase "
+                    "the workspace buffer size", float_ws ? float_ws_bytes : 0, p->float_ws_need);
+    rc = finish_plan(e, nullptr, 0, int_ws, p->pre_int_off, stream);
+    if (!rc)
+        rc = finish_plan(r, nullptr, 0, static_cast<char *>(int_ws) + p->pre_int_off,
+                         int_ws_bytes - p->pre_int_off, stream);
+    if (rc) return rc;
+    p->int_ws = int_ws;
+    p->float_ws = float_ws;
+    p->planned_device = true;
+    return PKVS_OK;
+}
+
 int pkvs_plan_get_info(const pkvs_plan *p, pkvs_plan_info *info)
 {
     clear_error();
@@ -541,7 +689,7 @@ int pkvs_plan_get_info(const pkvs_plan *p, pkvs_plan_info *info)
     info->split_size = p->split_size;
     info->item_words = p->item_words;
     info->query_tile = p->query_tile;
-    info->prefill_variant = p->desc.kind == PKVS_PREFILL ? p->run_variant : 0;
+    info->prefill_variant = p->desc.kind != PKVS_DECODE ? p->run_variant : 0;
     info->num_cus = p->num_cus;
     return PKVS_OK;
 }
@@ -552,24 +700,25 @@ int pkvs_plan_copy_items(const pkvs_plan *p, int32_t *dst, int64_t max_items, in
     if (!p || !n_items) return fail(PKVS_ERR_INVALID_ARG, "null argument");
     *n_items = p->n_items;
     if (!dst) return PKVS_OK;
-    const int64_t n = std::min(max_items, p->n_items);
-    if (n > 0)
-        std::memcpy(dst, p->host_ws.data() + kHeaderWords, sizeof(int32_t) * n * p->item_words);
+    // a cascade lists its extend pass's items, then its prefix pass's
+    const Plan *parts[2] = {p, nullptr};
+    if (p->desc.kind == PKVS_CASCADE) {
+        parts[0] = p->ext;
+        parts[1] = p->pre;
+    }
+    int64_t done = 0;
+    for (const Plan *s : parts) {
+        if (!s) continue;
+        const int64_t n = std::min(max_items - done, s->n_items);
+        if (n <= 0) break;
+        std::memcpy(dst + done * s->item_words, s->host_ws.data() + s->lead_words + kHeaderWords,
+                    sizeof(int32_t) * n * s->item_words);
+        done += n;
+    }
     return PKVS_OK;
 }
 
-void pkvs_plan_destroy(pkvs_plan *p)
-{
-    if (!p) return;
-    for (int i = 0; i < kStages; ++i) {
-        if (p->stage_ev[i]) {
-            if (p->stage_used[i]) (void)hipEventSynchronize(p->stage_ev[i]);
-            (void)hipEventDestroy(p->stage_ev[i]);
-        }
-        if (p->stage[i]) (void)hipHostFree(p->stage[i]);
-    }
-    delete p;
-}
+void pkvs_plan_destroy(pkvs_plan *p) { destroy_plan(p); }
 
 const char *pkvs_strerror(int code)
 {

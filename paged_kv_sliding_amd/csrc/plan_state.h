@@ -32,6 +32,22 @@ struct pkvs_plan {
     int64_t items_cap = 0, slots_cap = 0, merges_cap = 0;
     size_t int_ws_need = 0, float_ws_need = 0;
 
+    // Passes of a cascade prefill (internal prefill plans).  A ragged pass
+    // reads keys from a contiguous [tokens, kv heads, head_dim] array indexed
+    // like the queries; its page table of row indices sits in the lead_words
+    // in front of the work-list header.  A queries_after_kv pass places every
+    // query after the last key of its request's table (the cached prefix).
+    bool ragged = false;
+    bool queries_after_kv = false;
+    int64_t lead_words = 0;
+    int64_t planned_keys = 0;  // keys of all requests in the last plan()
+
+    // A cascade plan (kind PKVS_CASCADE) owns its two passes and splits the
+    // caller's workspaces between them.
+    pkvs_plan *ext = nullptr, *pre = nullptr;
+    size_t pre_int_off = 0;                         // bytes into int_ws
+    size_t o2_off = 0, lse1_off = 0, lse2_off = 0;  // bytes into float_ws
+
     // the last plan() call
     std::vector<int32_t> host_ws;  // header + items + merge entries
     int64_t n_items = 0, n_merges = 0;

@@ -310,7 +310,7 @@ __global__ __launch_bounds__(NW * 64) void prefill_bf16_kernel(PrefillArgs a)
     ra.kv_indices = a.kv_indices;
     ra.num_pages = a.num_pages;
     ra.slot_stride = int64_t(a.num_kv_heads) * D;
-    ra.page_stride = ra.slot_stride * a.page_size;
+    ra.page_stride = ra.slot_stride * a.page_rows;
     ra.log2_page = a.log2_page;
     ra.page_mask = a.page_size - 1;
 
@@ -652,7 +652,7 @@ __global__ __launch_bounds__(256) void prefill_wide_kernel(PrefillArgs a)
     ra.kv_indices = a.kv_indices;
     ra.num_pages = a.num_pages;
     ra.slot_stride = int64_t(a.num_kv_heads) * D;
-    ra.page_stride = ra.slot_stride * a.page_size;
+    ra.page_stride = ra.slot_stride * a.page_rows;
     ra.log2_page = a.log2_page;
     ra.page_mask = a.page_size - 1;
 
@@ -923,7 +923,7 @@ __global__ __launch_bounds__(kGenericThreads) void attention_fp32_kernel(Prefill
             float m = kNegInf, l = 0.f;
             for (int j = lo; j <= hi; ++j) {
                 const int64_t pg = page_of(a.kv_indices, page_base, j, a.log2_page, a.num_pages);
-                const int64_t off = nhd_offset(pg, j & (P - 1), P, hk, a.num_kv_heads, D);
+                const int64_t off = nhd_offset(pg, j & (P - 1), a.page_rows, hk, a.num_kv_heads, D);
                 float dot = 0.f;
                 for (int e = 0; e < E; ++e) dot += q[e] * K[off + lane + 64 * e];
                 for (int s = 32; s >= 1; s >>= 1) dot += __shfl_xor(dot, s);

@@ -43,6 +43,39 @@ int check_run(const pkvs_plan *p, int kind, const void *q, const void *k, const 
     return PKVS_OK;
 }
 
+// Launch the kernel of a planned prefill pass.  An empty work list still
+// launches: the kernels read the item count from the workspace, so a captured
+// graph replays correctly after any later plan of the same capacities.  A
+// ragged pass reads its keys through the row-index table in front of its
+// work list.
+hipError_t launch_prefill_pass(const pkvs_plan *p, const void *q, const void *k, const void *v,
+                               int64_t num_pages, const int32_t *kv_indices, void *o, float *lse,
+                               float sm_scale, hipStream_t stream)
+{
+    const int32_t *ws = static_cast<const int32_t *>(p->int_ws);
+    PrefillArgs a{};
+    a.q = q;
+    a.k = k;
+    a.v = v;
+    a.kv_indices = p->ragged ? ws : kv_indices;
+    a.o = o;
+    a.lse = lse;
+    a.ws = ws + p->lead_words;
+    a.num_pages = p->ragged ? p->desc.qo_capacity : num_pages;
+    a.scale_log2 = sm_scale * 1.44269504088896340736f;
+    a.num_qo_heads = p->desc.num_qo_heads;
+    a.num_kv_heads = p->desc.num_kv_heads;
+    a.log2_group = log2_exact(p->desc.num_qo_heads / p->desc.num_kv_heads);
+    a.page_size = p->desc.page_size;
+    a.log2_page = log2_exact(p->desc.page_size);
+    a.page_rows = p->ragged ? 1 : p->desc.page_size;
+    a.window_left = p->desc.window_left;
+    a.causal = p->desc.causal;
+    return p->desc.dtype == PKVS_BF16
+               ? launch_prefill_bf16(a, p->desc.head_dim, p->run_variant, p->grid_blocks, stream)
+               : launch_attention_fp32(a, p->desc.head_dim, p->grid_blocks, stream);
+}
+
 }  // namespace
 
 extern "C" {
@@ -55,31 +88,52 @@ int pkvs_prefill_run(const pkvs_plan *p, const void *q, const void *k_cache, con
     int rc = check_run(p, PKVS_PREFILL, q, k_cache, v_cache, num_pages, kv_indices_d, o,
                        window_left, causal);
     if (rc) return rc;
-    // (an empty work list still launches: the kernels read the item count
-    // from the workspace, so a captured graph replays correctly after any
-    // later plan of the same capacities)
-    PrefillArgs a{};
-    a.q = q;
-    a.k = k_cache;
-    a.v = v_cache;
-    a.kv_indices = kv_indices_d;
-    a.o = o;
-    a.lse = lse;
-    a.ws = static_cast<const int32_t *>(p->int_ws);
-    a.num_pages = num_pages;
-    a.scale_log2 = sm_scale * 1.44269504088896340736f;
-    a.num_qo_heads = p->desc.num_qo_heads;
-    a.num_kv_heads = p->desc.num_kv_heads;
-    a.log2_group = log2_exact(p->desc.num_qo_heads / p->desc.num_kv_heads);
-    a.page_size = p->desc.page_size;
-    a.log2_page = log2_exact(p->desc.page_size);
-    a.window_left = p->desc.window_left;
-    a.causal = p->desc.causal;
-    hipError_t e = p->desc.dtype == PKVS_BF16
-                       ? launch_prefill_bf16(a, p->desc.head_dim, p->run_variant,
-                                             p->grid_blocks, stream)
-                       : launch_attention_fp32(a, p->desc.head_dim, p->grid_blocks, stream);
+    hipError_t e = launch_prefill_pass(p, q, k_cache, v_cache, num_pages, kv_indices_d, o, lse,
+                                       sm_scale, stream);
     if (e != hipSuccess) return fail(PKVS_ERR_HIP, "prefill launch: %s", hipGetErrorString(e));
+    return PKVS_OK;
+}
+
+int pkvs_cascade_run(const pkvs_plan *p, const void *q, const void *k_extend,
+                     const void *v_extend, const void *k_cache, const void *v_cache,
+                     int64_t num_pages, const int32_t *kv_indices_d, void *o, float *lse,
+                     float sm_scale, int32_t window_left, hipStream_t stream)
+{
+    clear_error();
+    if (!p) return fail(PKVS_ERR_INVALID_ARG, "plan is null");
+    if (p->desc.kind != PKVS_CASCADE) return fail(PKVS_ERR_INVALID_ARG, "not a cascade plan");
+    if (window_left != p->desc.window_left)
+        return fail(PKVS_ERR_PLAN_MISMATCH, "run window_left %d differs from the planned %d",
+                    window_left, p->desc.window_left);
+    if (!p->planned_device)
+        return fail(PKVS_ERR_NOT_PLANNED, "no device plan (plan() failed, was dry, or never "
+                    "ran)");
+    if (p->n_items > 0 && (!q || !k_extend || !v_extend || !o))
+        return fail(PKVS_ERR_INVALID_ARG, "null q, extend K/V or o");
+    if (p->planned_keys > 0 && (!k_cache || !v_cache || !kv_indices_d || num_pages <= 0))
+        return fail(PKVS_ERR_INVALID_ARG, "the planned batch has cached keys: null cache, page "
+                    "table or num_pages <= 0");
+    char *fws = static_cast<char *>(p->float_ws);
+    void *o2 = fws + p->o2_off;
+    float *lse1 = reinterpret_cast<float *>(fws + p->lse1_off);
+    float *lse2 = reinterpret_cast<float *>(fws + p->lse2_off);
+    // extend pass -> (o, lse1); prefix pass -> (o2, lse2); o, lse = merge
+    hipError_t e = launch_prefill_pass(p->ext, q, k_extend, v_extend, 0, nullptr, o, lse1,
+                                       sm_scale, stream);
+    if (e != hipSuccess) return fail(PKVS_ERR_HIP, "extend pass launch: %s", hipGetErrorString(e));
+    e = launch_prefill_pass(p->pre, q, k_cache, v_cache, std::max<int64_t>(num_pages, 1),
+                            kv_indices_d, o2, lse2, sm_scale, stream);
+    if (e != hipSuccess) return fail(PKVS_ERR_HIP, "prefix pass launch: %s", hipGetErrorString(e));
+    // the merge reads the planned token count from the extend pass's work
+    // list header, over a grid fixed by the capacity
+    const int heads = p->desc.num_qo_heads;
+    const int64_t units = p->desc.qo_capacity * heads;
+    const int grid = int(std::max<int64_t>(1, std::min<int64_t>(units, int64_t(p->num_cus) * 32)));
+    const int32_t *hdr = static_cast<const int32_t *>(p->ext->int_ws) + p->ext->lead_words;
+    e = launch_merge_state(o, lse1, o2, lse2, o, lse ? lse : lse1, p->desc.qo_capacity,
+                           hdr + kHdrNumTokens, heads, p->desc.head_dim, p->desc.dtype, grid,
+                           stream);
+    if (e != hipSuccess) return fail(PKVS_ERR_HIP, "merge launch: %s", hipGetErrorString(e));
     return PKVS_OK;
 }
 
@@ -113,6 +167,7 @@ int pkvs_decode_run(const pkvs_plan *p, const void *q, const void *k_cache, cons
         a.log2_group = log2g;
         a.page_size = p->desc.page_size;
         a.log2_page = log2_exact(p->desc.page_size);
+        a.page_rows = p->desc.page_size;
         a.window_left = p->desc.window_left;
         a.causal = 1;
         e = launch_attention_fp32(a, p->desc.head_dim, p->grid_blocks, stream);
@@ -169,8 +224,8 @@ int pkvs_merge_state(const void *v_a, const float *s_a, const void *v_b, const f
         (void)hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev);
     const int64_t units = num_tokens * num_heads;
     const int grid = int(std::min<int64_t>(units, int64_t(cus) * 32));
-    hipError_t e = launch_merge_state(v_a, s_a, v_b, s_b, v_out, s_out, num_tokens, num_heads,
-                                      head_dim, v_dtype, grid, stream);
+    hipError_t e = launch_merge_state(v_a, s_a, v_b, s_b, v_out, s_out, num_tokens, nullptr,
+                                      num_heads, head_dim, v_dtype, grid, stream);
     if (e != hipSuccess) return fail(PKVS_ERR_HIP, "merge_state launch: %s", hipGetErrorString(e));
     return PKVS_OK;
 }

@@ -34,13 +34,15 @@ PKVS_BF16 = 0
 PKVS_FP32 = 1
 PKVS_PREFILL = 0
 PKVS_DECODE = 1
+PKVS_CASCADE = 2
 
 _DTYPES = {torch.bfloat16: PKVS_BF16, torch.float32: PKVS_FP32}
 
 # Every symbol include/pkvs.h declares.
 EXPORTED = [
     "pkvs_plan_create", "pkvs_workspace_size", "pkvs_prefill_plan", "pkvs_prefill_run",
-    "pkvs_decode_plan", "pkvs_decode_run", "pkvs_merge_state", "pkvs_plan_get_info",
+    "pkvs_decode_plan", "pkvs_decode_run", "pkvs_cascade_plan", "pkvs_cascade_run",
+    "pkvs_merge_state", "pkvs_plan_get_info",
     "pkvs_plan_copy_items", "pkvs_plan_destroy", "pkvs_strerror", "pkvs_last_error",
 ]
 
@@ -88,6 +90,8 @@ def _load() -> ctypes.CDLL:
         "pkvs_prefill_run": (ctypes.c_int, [P, P, P, P, i64, P, P, P, f32, i32, i32, P]),
         "pkvs_decode_plan": (ctypes.c_int, [P, P, P, i32, P, sz, P, sz, P]),
         "pkvs_decode_run": (ctypes.c_int, [P, P, P, P, i64, P, P, P, f32, i32, P]),
+        "pkvs_cascade_plan": (ctypes.c_int, [P, P, P, P, i32, P, sz, P, sz, P]),
+        "pkvs_cascade_run": (ctypes.c_int, [P, P, P, P, P, P, i64, P, P, P, f32, i32, P]),
         "pkvs_merge_state": (ctypes.c_int, [P, P, P, P, P, P, i64, i32, i32, i32, P]),
         "pkvs_plan_get_info": (ctypes.c_int, [P, ctypes.POINTER(pkvs_plan_info)]),
         "pkvs_plan_copy_items": (ctypes.c_int, [P, P, i64, ctypes.POINTER(i64)]),
@@ -189,6 +193,28 @@ def pkvs_decode_plan(plan, kv_indptr_h, kv_last_page_len_h, batch_size: int,
     st = _stream(stream) if int_ws is not None else None
     _check(_lib.pkvs_decode_plan(plan, kp, lp, batch_size, _ptr(float_ws), fb, _ptr(int_ws), ib,
                                  st), "pkvs_decode_plan")
+
+
+def pkvs_cascade_plan(plan, qo_indptr_h, kv_indptr_h, kv_last_page_len_h, batch_size: int,
+                      float_ws: Optional[torch.Tensor], int_ws: Optional[torch.Tensor],
+                      stream=None) -> None:
+    qp, _q = _host_i32(qo_indptr_h)
+    kp, _k = _host_i32(kv_indptr_h)
+    lp, _l = _host_i32(kv_last_page_len_h)
+    fb = float_ws.numel() * float_ws.element_size() if float_ws is not None else 0
+    ib = int_ws.numel() * int_ws.element_size() if int_ws is not None else 0
+    st = _stream(stream) if int_ws is not None else None
+    _check(_lib.pkvs_cascade_plan(plan, qp, kp, lp, batch_size, _ptr(float_ws), fb, _ptr(int_ws),
+                                  ib, st), "pkvs_cascade_plan")
+
+
+def pkvs_cascade_run(plan, q, k_extend, v_extend, k_cache, v_cache, kv_indices, o, lse,
+                     sm_scale: float, window_left: int, stream=None) -> None:
+    _need_device(q, k_extend, v_extend, k_cache, v_cache, kv_indices, o, lse)
+    _check(_lib.pkvs_cascade_run(plan, _ptr(q), _ptr(k_extend), _ptr(v_extend), _ptr(k_cache),
+                                 _ptr(v_cache), k_cache.shape[0], _ptr(kv_indices), _ptr(o),
+                                 _ptr(lse), float(sm_scale), window_left, _stream(stream)),
+           "pkvs_cascade_run")
 
 
 def pkvs_prefill_run(plan, q, k_cache, v_cache, kv_indices, o, lse, sm_scale: float,
@@ -304,6 +330,80 @@ class BatchAttention:
         else:
             pkvs_decode_run(self.handle, q, k_cache, v_cache, kv_indices, out, lse, sm_scale,
                             window_left, stream)
+        return (out, lse) if return_lse else out
+
+    def info(self) -> pkvs_plan_info:
+        return pkvs_plan_get_info(self.handle)
+
+    def close(self):
+        if self.handle is not None:
+            pkvs_plan_destroy(self.handle)
+            self.handle = None
+
+    def __del__(self):
+        try:
+            self.close()
+        except Exception:
+            pass
+
+
+class CascadeAttention:
+    """Cascade prefill holder: new tokens' K/V in a contiguous array, cached
+    prefix in the paged cache (``pkvs_cascade_plan`` / ``pkvs_cascade_run``).
+
+    Keywords are the fields of ``pkvs_desc`` (kind is PKVS_CASCADE);
+    ``kv_capacity`` bounds the cached keys of one request's page table.
+    """
+
+    def __init__(self, device="cuda", **desc_kw):
+        self.desc = make_desc(PKVS_CASCADE, **desc_kw)
+        self.handle = pkvs_plan_create(self.desc)
+        fb, ib = pkvs_workspace_size(self.handle)
+        self.float_ws = torch.empty(max(fb, 4), dtype=torch.uint8, device=device)
+        self.int_ws = torch.empty(ib, dtype=torch.uint8, device=device)
+
+    def plan(self, *, qo_indptr, kv_indptr, kv_last_page_len, stream=None):
+        batch = len(kv_last_page_len)
+        self._nnz_pages = int(torch.as_tensor(kv_indptr)[-1])
+        self._nnz_qo = int(torch.as_tensor(qo_indptr)[-1])
+        pkvs_cascade_plan(self.handle, qo_indptr, kv_indptr, kv_last_page_len, batch,
+                          self.float_ws, self.int_ws, stream)
+
+    def _check_shapes(self, q, k_extend, v_extend, k_cache, v_cache, kv_indices, out, lse):
+        d = self.desc
+        dt = {PKVS_BF16: torch.bfloat16, PKVS_FP32: torch.float32}[d.dtype]
+        rows = max(self._nnz_qo, q.shape[0] if q.dim() == 3 else 0)
+        if tuple(q.shape) != (rows, d.num_qo_heads, d.head_dim) or q.dtype != dt:
+            raise ValueError(f"q must be {dt} [>= {self._nnz_qo}, {d.num_qo_heads}, "
+                             f"{d.head_dim}], got {q.dtype} {tuple(q.shape)}")
+        if out.shape != q.shape or out.dtype != dt:
+            raise ValueError("out must match q")
+        for t in (k_extend, v_extend):
+            if (t.dim() != 3 or t.shape[0] < self._nnz_qo
+                    or tuple(t.shape[1:]) != (d.num_kv_heads, d.head_dim) or t.dtype != dt):
+                raise ValueError(f"k_extend / v_extend must be {dt} [>= {self._nnz_qo}, "
+                                 f"{d.num_kv_heads}, {d.head_dim}]")
+        kv_shape = (d.page_size, d.num_kv_heads, d.head_dim)
+        for c in (k_cache, v_cache):
+            if c.dim() != 4 or tuple(c.shape[1:]) != kv_shape or c.dtype != dt:
+                raise ValueError(f"caches must be {dt} [num_pages, {kv_shape}]")
+        if k_cache.shape[0] != v_cache.shape[0]:
+            raise ValueError("k_cache and v_cache page counts differ")
+        if kv_indices.dtype != torch.int32 or kv_indices.numel() < self._nnz_pages:
+            raise ValueError(f"kv_indices must be int32 with >= {self._nnz_pages} entries")
+        if lse is not None and (tuple(lse.shape) != (rows, d.num_qo_heads)
+                                or lse.dtype != torch.float32):
+            raise ValueError(f"lse must be float32 {(rows, d.num_qo_heads)}")
+
+    def run(self, q, k_extend, v_extend, k_cache, v_cache, kv_indices, *, sm_scale: float,
+            window_left: int, return_lse: bool = True, out=None, lse=None, stream=None):
+        if out is None:
+            out = torch.empty_like(q)
+        if return_lse and lse is None:
+            lse = torch.empty(q.shape[0], q.shape[1], dtype=torch.float32, device=q.device)
+        self._check_shapes(q, k_extend, v_extend, k_cache, v_cache, kv_indices, out, lse)
+        pkvs_cascade_run(self.handle, q, k_extend, v_extend, k_cache, v_cache, kv_indices, out,
+                         lse, sm_scale, window_left, stream)
         return (out, lse) if return_lse else out
 
     def info(self) -> pkvs_plan_info:

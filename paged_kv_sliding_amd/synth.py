@@ -33,9 +33,11 @@ from typing import List, Optional, Sequence
 import torch
 
 __all__ = [
+    "CascadeInputs",
     "Case",
     "WORKLOADS",
     "build_case",
+    "cascade_inputs",
     "case_from_lengths",
     "workload_lengths",
 ]
@@ -249,3 +251,73 @@ def build_case(name: str, *, device: str = "cpu", window_left: Optional[int] = N
         fixed_split_size=w.get("split", -1),
         perm_gen=gen,
     )
+
+
+@dataclasses.dataclass
+class CascadeInputs:
+    """A paged batch rearranged the way a cascade prefill receives it: the
+    keys / values of each request's query tokens in contiguous arrays, and a
+    page table over the cached keys before them."""
+
+    k_extend: torch.Tensor        # [nnz_qo, H_kv, D], row r = key of query token r
+    v_extend: torch.Tensor
+    k_cache: torch.Tensor         # copy of the pool, NaN outside the prefix tables
+    v_cache: torch.Tensor
+    kv_indptr: torch.Tensor       # [B+1] int32 (host)
+    kv_indices: torch.Tensor      # int32, on the case's device
+    kv_last_page_len: torch.Tensor  # [B] int32 (host)
+    table_lens: List[int]         # cached keys each request's table holds
+
+
+def cascade_inputs(case: Case, trim_to: Optional[int] = None) -> CascadeInputs:
+    """Rearrange a paged prefill case (whose query tokens' keys already sit in
+    the cache, after each request's prefix) into cascade inputs.
+
+    The last ``qo_len`` keys of each request are gathered into ``k_extend`` /
+    ``v_extend``.  The page table keeps the request's pages up to its prefix
+    end; with ``trim_to`` = n >= 0 it starts at the page holding key
+    ``max(0, prefix - n)`` (the pages before it are dropped, the way a
+    sliding-window pool trims a prefix to the window).  Every slot of the pool
+    that no table covers is NaN in the returned caches, so a read of it shows.
+    """
+    P = case.page_size
+    B = len(case.kv_lens)
+    kvp = case.kv_indptr.cpu().tolist()
+    idx = case.kv_indices.cpu()
+    dev = case.k_cache.device
+    rows_pg, rows_slot = [], []
+    new_kvp, new_idx, last, tlen = [0], [], [], []
+    keep = torch.zeros(case.k_cache.shape[0], P, dtype=torch.bool)
+    for b in range(B):
+        pages = idx[kvp[b]:kvp[b + 1]]
+        prefix = case.kv_lens[b] - case.qo_lens[b]
+        for pos in range(prefix, case.kv_lens[b]):
+            rows_pg.append(int(pages[pos // P]))
+            rows_slot.append(pos % P)
+        start = 0
+        if trim_to is not None and trim_to >= 0:
+            start = max(0, prefix - trim_to) // P * P
+        n = prefix - start
+        np_ = (n + P - 1) // P
+        tab = pages[start // P:start // P + np_]
+        new_idx.append(tab)
+        new_kvp.append(new_kvp[-1] + np_)
+        last.append(0 if n == 0 else n - (np_ - 1) * P)
+        tlen.append(n)
+        for i, pg in enumerate(tab.tolist()):
+            keep[pg, : (P if i + 1 < np_ else last[-1])] = True
+    pg_t = torch.tensor(rows_pg, dtype=torch.long, device=dev)
+    sl_t = torch.tensor(rows_slot, dtype=torch.long, device=dev)
+    k_ext = case.k_cache[pg_t, sl_t].contiguous()
+    v_ext = case.v_cache[pg_t, sl_t].contiguous()
+    drop = (~keep).to(dev)
+    k_cache = case.k_cache.clone()
+    v_cache = case.v_cache.clone()
+    k_cache[drop] = float("nan")
+    v_cache[drop] = float("nan")
+    kv_indices = torch.cat(new_idx).to(torch.int32) if new_idx else torch.zeros(0, dtype=torch.int32)
+    return CascadeInputs(
+        k_extend=k_ext, v_extend=v_ext, k_cache=k_cache, v_cache=v_cache,
+        kv_indptr=torch.tensor(new_kvp, dtype=torch.int32), kv_indices=kv_indices.to(dev),
+        kv_last_page_len=torch.tensor(last, dtype=torch.int32), table_lens=tlen)
+

@@ -12,7 +12,7 @@ import torch
 import oracle
 from gpu_helpers import (compare, gpu_run, log, make_attention, oracle_for, sub_case)
 from paged_kv_sliding_amd import pkvs as P
-from paged_kv_sliding_amd.synth import build_case, case_from_lengths
+from paged_kv_sliding_amd.synth import build_case, cascade_inputs, case_from_lengths
 
 pytestmark = pytest.mark.gpu
 DEV = "cuda"
@@ -457,3 +457,175 @@ def test_merge_state_of_prefill_split_equals_unsplit():
     o2, l2 = gpu_run(case, disable_split_kv=True)
     assert (o1.float() - o2.float()).abs().max() <= 2e-2
     assert (l1 - l2).abs().max() <= 1e-3
+
+
+# ----------------------------------------------------------------- cascade prefill
+# sglang flashinfer_backend.py, FlashInferAttnBackend.forward_extend (the
+# branch with cached prefixes): a ragged pass over the new tokens' own keys, a
+# paged pass over the cached prefix, merged.  The result must equal the one
+# paged prefill over prefix + new keys (the oracle on the combined layout).
+
+
+def make_cascade(case, window_left=None, prefill_variant=0, qo_capacity=None,
+                 kv_capacity=None, batch_capacity=None):
+    W = case.window_left if window_left is None else window_left
+    prefix = [k - q for q, k in zip(case.qo_lens, case.kv_lens)]
+    return P.CascadeAttention(
+        num_qo_heads=case.num_qo_heads, num_kv_heads=case.num_kv_heads, head_dim=case.head_dim,
+        page_size=case.page_size, dtype=case.dtype, window_left=W, causal=case.causal,
+        batch_capacity=batch_capacity or max(case.batch_size, 1),
+        qo_capacity=qo_capacity or max(int(case.qo_indptr[-1]), 1),
+        kv_capacity=kv_capacity or max(max(prefix, default=1), 1),
+        prefill_variant=prefill_variant)
+
+
+def cascade_run(case, trim=False, att=None, return_lse=True, **kw):
+    W = case.window_left
+    cin = cascade_inputs(case, trim_to=W if trim else None)
+    if att is None:
+        att = make_cascade(case, **kw)
+    att.plan(qo_indptr=case.qo_indptr.cpu(), kv_indptr=cin.kv_indptr,
+             kv_last_page_len=cin.kv_last_page_len)
+    res = att.run(case.q, cin.k_extend, cin.v_extend, cin.k_cache, cin.v_cache, cin.kv_indices,
+                  sm_scale=case.sm_scale, window_left=W, return_lse=return_lse)
+    torch.cuda.synchronize()
+    return res, att
+
+
+@pytest.mark.parametrize("P_", [1, 16])
+@pytest.mark.parametrize("W", [-1, 0, 5, 100, 511])
+@pytest.mark.parametrize("trim", [False, True])
+def test_cascade_equals_one_paged_prefill(P_, W, trim):
+    qo = [1, 70, 0, 33, 129, 5, 300, 40]
+    kv = [1, 90, 9, 300, 129, 700, 301, 1000]
+    case = small(qo, kv, H_q=8, H_kv=2, D=128, P_=P_, W=W, seed=P_ * 31 + W + 7 * trim)
+    (o, lse), att = cascade_run(case, trim=trim)
+    ro, rl = oracle_for(case)
+    compare(o, lse, ro, rl, tag=f"cascade P={P_} W={W} trim={trim} "
+                                f"variant={att.info().prefill_variant}")
+
+
+@pytest.mark.parametrize("variant", [1, 2, 3, 4])
+def test_cascade_prefill_variants(variant):
+    qo = [64, 1, 257, 33, 600]
+    kv = [64, 800, 300, 1000, 700]
+    case = small(qo, kv, H_q=8, H_kv=2, D=128, P_=16, W=200, seed=900 + variant)
+    (o, lse), att = cascade_run(case, prefill_variant=variant)
+    assert att.info().prefill_variant == variant
+    ro, rl = oracle_for(case)
+    compare(o, lse, ro, rl, tag=f"cascade variant={variant}")
+
+
+@pytest.mark.parametrize("D,G", [(64, 8), (128, 1), (256, 4)])
+def test_cascade_head_shapes(D, G):
+    case = small([40, 130, 7], [90, 130, 500], H_q=2 * G, H_kv=2, D=D, P_=16, W=63,
+                 seed=D + G)
+    (o, lse), _ = cascade_run(case, trim=True)
+    ro, rl = oracle_for(case)
+    compare(o, lse, ro, rl, tag=f"cascade D={D} G={G}")
+
+
+def test_cascade_fp32_and_no_window_non_causal():
+    case = small([6, 8, 12], [10, 8, 20], H_q=2, H_kv=1, D=64, P_=4, W=4, seed=5,
+                 dtype=torch.float32)
+    (o, lse), _ = cascade_run(case)
+    ro, rl = oracle_for(case)
+    compare(o, lse, ro, rl, tag="cascade fp32")
+    case = small([20, 7, 64], [50, 7, 400], H_q=8, H_kv=2, D=128, W=-1, seed=23)
+    case.causal = False
+    (o, lse), _ = cascade_run(case)
+    ro, rl = oracle_for(case)
+    compare(o, lse, ro, rl, tag="cascade non-causal")
+
+
+def test_cascade_prefix_prefill_workload():
+    """The batched prefill with cached prefixes (8 requests, prefix up to 1024,
+    up to 512 new tokens, window 511, head_dim 256) run as a cascade with the
+    prefix table trimmed to the window."""
+    case = build_case("prefix_prefill", device=DEV)
+    (o, lse), _ = cascade_run(case, trim=True)
+    ro, rl = oracle_for(case)
+    compare(o, lse, ro, rl, tag="cascade prefix_prefill")
+
+
+def test_cascade_without_lse_and_without_cached_keys():
+    case = small([30, 9], [90, 40], H_q=4, H_kv=1, D=128, W=10, seed=73)
+    (o), _ = cascade_run(case, return_lse=False)
+    ro, _ = oracle_for(case)
+    compare(o, None, ro, None, tag="cascade no lse")
+    # no request has cached keys: the paged pass sees empty tables
+    case = small([30, 9], [30, 9], H_q=4, H_kv=1, D=128, W=10, seed=74)
+    (o, lse), _ = cascade_run(case)
+    ro, rl = oracle_for(case)
+    compare(o, lse, ro, rl, tag="cascade without cached keys")
+
+
+def test_cascade_graph_replay_follows_replans():
+    """The cascade's three launches captured once replay correctly after
+    re-plans of the same capacities (the merge reads the token count from the
+    workspace), bit for bit against eager runs."""
+    qo, kv = [40, 1, 130, 7, 64], [300, 1, 200, 500, 64]
+    case = small(qo, kv, H_q=8, H_kv=2, D=128, P_=16, W=100, seed=64)
+    cin = cascade_inputs(case)
+    att = make_cascade(case)
+    qop = case.qo_indptr.cpu().tolist()
+    q_buf = case.q.clone()
+    ke_buf, ve_buf = cin.k_extend.clone(), cin.v_extend.clone()
+    idx_buf = cin.kv_indices.clone()
+    o_buf = torch.zeros_like(case.q)
+    l_buf = torch.zeros(case.q.shape[0], case.num_qo_heads, dtype=torch.float32, device=DEV)
+    kvp = cin.kv_indptr.tolist()
+
+    def plan_and_load(picks):
+        rows, pages, qo_ind, kv_ind, last = [], [], [0], [0], []
+        for b in picks:
+            rows += list(range(qop[b], qop[b + 1]))
+            pages.append(cin.kv_indices[kvp[b]:kvp[b + 1]])
+            qo_ind.append(qo_ind[-1] + qop[b + 1] - qop[b])
+            kv_ind.append(kv_ind[-1] + kvp[b + 1] - kvp[b])
+            last.append(int(cin.kv_last_page_len[b]))
+        r = torch.tensor(rows, device=DEV)
+        for buf, src in ((q_buf, case.q), (ke_buf, cin.k_extend), (ve_buf, cin.v_extend)):
+            buf.zero_()
+            buf[:len(rows)] = src[r]
+        idx_buf.zero_()
+        pg = torch.cat(pages)
+        idx_buf[:len(pg)] = pg
+        att.plan(qo_indptr=qo_ind, kv_indptr=kv_ind, kv_last_page_len=last)
+        return len(rows)
+
+    def run():
+        att.run(q_buf, ke_buf, ve_buf, cin.k_cache, cin.v_cache, idx_buf,
+                sm_scale=case.sm_scale, window_left=case.window_left, out=o_buf, lse=l_buf)
+
+    B = case.batch_size
+    picks = [list(range(B)), [2], [0, 3, 4], list(range(B))]
+    plan_and_load(picks[0])
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        run()
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        run()
+    for k, pk in enumerate(picks):
+        n = plan_and_load(pk)
+        o_buf.fill_(7.0)
+        run()
+        torch.cuda.synchronize()
+        want_o, want_l = o_buf[:n].clone(), l_buf[:n].clone()
+        for rep in range(3):
+            o_buf.fill_(-3.0)
+            l_buf.fill_(-3.0)
+            junk = torch.randn(256, 256, device=DEV) @ torch.randn(256, 256, device=DEV)
+            g.replay()
+            torch.cuda.synchronize()
+            assert torch.isfinite(junk).all()
+            assert torch.equal(o_buf[:n], want_o), (k, rep)
+            assert torch.equal(l_buf[:n], want_l), (k, rep)
+        if k == 0:
+            ro, rl = oracle_for(case)
+            compare(want_o, want_l, ro, rl, tag="cascade graph")
+

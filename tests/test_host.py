@@ -305,3 +305,96 @@ def test_workload_plans_fit_their_capacities():
             P.pkvs_prefill_plan(h, qop, kvp, last, len(kv), None, None)
         assert P.pkvs_plan_get_info(h).num_items > 0
         P.pkvs_plan_destroy(h)
+
+
+# ----------------------------------------------------------------- cascade prefill
+
+
+def test_cascade_passes_cover_every_query_once():
+    """A cascade plan lists its extend pass (keys = the request's own query
+    tokens, read through a row-index table) and then its prefix pass (queries
+    placed after every cached key of the table), each covering every query
+    once.  A request may have more new tokens than cached keys."""
+    W = 40
+    qo = [1, 70, 0, 33, 129, 300]
+    tab = [0, 20, 9, 267, 2, 100]  # cached keys in each request's table
+    h = P.pkvs_plan_create(desc(P.PKVS_CASCADE, num_qo_heads=8, num_kv_heads=2, window_left=W))
+    qop, kvp, last = csr(qo, tab, 16)
+    P.pkvs_cascade_plan(h, qop, kvp, last, len(qo), None, None)
+    info = P.pkvs_plan_get_info(h)
+    items = P.pkvs_plan_copy_items(h).tolist()
+    assert len(items) == info.num_items
+    n_ext = sum(1 for it in items if it[6] >= 0 and it[5] == qo[it[0]] and it[4] < qo[it[0]])
+    ext, pre = items[:n_ext], items[n_ext:]
+    for part, name in ((ext, "extend"), (pre, "prefix")):
+        seen = {}
+        for b, hk, q0, qn, pos0, kv_len, pbase, kvb in part:
+            i0 = q0 - qop[b]
+            if name == "extend":
+                assert kv_len == qo[b] and pos0 == i0
+            else:
+                assert kv_len == tab[b] and pbase == kvp[b] and pos0 == tab[b] + i0
+            assert kvb % 32 == 0 and kvb <= max(0, pos0 - W)
+            for t in range(q0, q0 + qn):
+                seen[(b, hk, t)] = seen.get((b, hk, t), 0) + 1
+        expect = {(b, hk, t) for b in range(len(qo)) for hk in range(2)
+                  for t in range(qop[b], qop[b + 1])}
+        assert set(seen) == expect and set(seen.values()) == {1}, name
+    # extend tables of consecutive requests do not overlap
+    bases = sorted({(it[0], it[6]) for it in ext})
+    for (b0, p0), (b1, p1) in zip(bases, bases[1:]):
+        assert p1 - p0 >= (qo[b0] + 255) // 256
+    P.pkvs_plan_destroy(h)
+
+
+def test_cascade_workspace_and_errors():
+    kw = dict(num_qo_heads=8, num_kv_heads=2, window_left=31, qo_capacity=1000,
+              kv_capacity=500, batch_capacity=4)
+    h = P.pkvs_plan_create(desc(P.PKVS_CASCADE, **kw))
+    fb, ib = P.pkvs_workspace_size(h)
+    rows = 1000 * 8
+    assert fb >= rows * 128 * 2 + 2 * rows * 4
+    hp = P.pkvs_plan_create(desc(P.PKVS_PREFILL, **kw))
+    assert ib > P.pkvs_workspace_size(hp)[1]
+    qop, kvp, last = csr([10, 600], [0, 5], 16)
+    # the wrong entry point for each kind
+    assert err_code(lambda: P.pkvs_prefill_plan(h, qop, kvp, last, 2, None, None)) == \
+        P.PKVS_ERR_INVALID_ARG
+    assert err_code(lambda: P.pkvs_cascade_plan(hp, qop, kvp, last, 2, None, None)) == \
+        P.PKVS_ERR_INVALID_ARG
+    P.pkvs_cascade_plan(h, qop, kvp, last, 2, None, None)  # 600 new tokens over 5 cached keys
+    # capacities: total new tokens, cached keys per request, batch
+    qop2, kvp2, last2 = csr([600, 401], [1, 1], 16)
+    assert err_code(lambda: P.pkvs_cascade_plan(h, qop2, kvp2, last2, 2, None, None)) == \
+        P.PKVS_ERR_CAPACITY
+    qop2, kvp2, last2 = csr([1], [501], 16)
+    assert err_code(lambda: P.pkvs_cascade_plan(h, qop2, kvp2, last2, 1, None, None)) == \
+        P.PKVS_ERR_CAPACITY
+    qop2, kvp2, last2 = csr([1] * 5, [1] * 5, 16)
+    assert err_code(lambda: P.pkvs_cascade_plan(h, qop2, kvp2, last2, 5, None, None)) == \
+        P.PKVS_ERR_CAPACITY
+    # workspaces too small are reported before any device copy
+    (qp, _a), (kp, _b), (lp, _c) = P._host_i32(qop), P._host_i32(kvp), P._host_i32(last)
+    small = torch.empty(ib // 2, dtype=torch.uint8)
+    rc = P._lib.pkvs_cascade_plan(h, qp, kp, lp, 2, None, 0, ctypes.c_void_p(small.data_ptr()),
+                                  small.numel(), None)
+    assert rc == P.PKVS_ERR_WORKSPACE, P.last_error()
+    big = torch.empty(ib, dtype=torch.uint8)
+    fsmall = torch.empty(fb // 2, dtype=torch.uint8)
+    rc = P._lib.pkvs_cascade_plan(h, qp, kp, lp, 2, ctypes.c_void_p(fsmall.data_ptr()),
+                                  fsmall.numel(), ctypes.c_void_p(big.data_ptr()), big.numel(),
+                                  None)
+    assert rc == P.PKVS_ERR_WORKSPACE, P.last_error()
+    # run: window other than the planned one, a dry plan, the wrong kind
+    lib = P._lib
+    rc = lib.pkvs_cascade_run(h, None, None, None, None, None, 1, None, None, None, 1.0, 30, None)
+    assert rc == P.PKVS_ERR_PLAN_MISMATCH
+    rc = lib.pkvs_cascade_run(h, None, None, None, None, None, 1, None, None, None, 1.0, 31, None)
+    assert rc == P.PKVS_ERR_NOT_PLANNED
+    rc = lib.pkvs_cascade_run(hp, None, None, None, None, None, 1, None, None, None, 1.0, 31, None)
+    assert rc == P.PKVS_ERR_INVALID_ARG
+    # a window needs causal attention, as for prefill
+    assert err_code(lambda: P.pkvs_plan_create(desc(P.PKVS_CASCADE, causal=False))) == \
+        P.PKVS_ERR_UNSUPPORTED
+    P.pkvs_plan_destroy(h)
+    P.pkvs_plan_destroy(hp)
