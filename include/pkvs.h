@@ -217,8 +217,8 @@ int pkvs_decode_run(const pkvs_plan *plan, const void *q, const void *k_cache,
  * followed by the new keys.  Zero new tokens or zero cached keys are legal.
  * Builds both passes' work lists and enqueues two host-to-device copies into
  * int_ws on `stream` (int_ws == NULL: dry plan).  float_ws holds the paged
- * pass's o and both passes' lse.  Errors as pkvs_prefill_plan (a request may
- * have more new tokens than cached keys). */
+ * pass's (o, lse).  Errors as pkvs_prefill_plan (a request may have more new
+ * tokens than cached keys). */
 int pkvs_cascade_plan(pkvs_plan *plan, const int32_t *qo_indptr_h, const int32_t *kv_indptr_h,
                       const int32_t *kv_last_page_len_h, int32_t batch_size, void *float_ws,
                       size_t float_ws_bytes, void *int_ws, size_t int_ws_bytes,
@@ -228,9 +228,10 @@ int pkvs_cascade_plan(pkvs_plan *plan, const int32_t *qo_indptr_h, const int32_t
  * v_extend [nnz_qo, num_kv_heads, head_dim] (row r is the key / value of query
  * token r); k_cache, v_cache, num_pages and kv_indices_d as pkvs_prefill_run
  * (they may be NULL / 0 when the planned batch has no cached keys); lse
- * nullable.  Three launches on `stream`: the ragged pass writes o and an lse
- * into float_ws, the paged pass its (o, lse) into float_ws, and the merge
- * combines them into o and lse in place.  window_left must equal the plan's. */
+ * nullable.  Two launches on `stream`: the paged pass writes its (o, lse) into
+ * float_ws, then the ragged pass stores the merge_state combine of its own
+ * (o, lse) with them into o and lse (the merge runs in its epilogue).
+ * window_left must equal the plan's. */
 int pkvs_cascade_run(const pkvs_plan *plan, const void *q, const void *k_extend,
                      const void *v_extend, const void *k_cache, const void *v_cache,
                      int64_t num_pages, const int32_t *kv_indices_d, void *o, float *lse,

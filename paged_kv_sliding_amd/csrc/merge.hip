@@ -37,10 +37,9 @@ __device__ __forceinline__ void st<uint16_t>(uint16_t *p, int64_t i, float x)
 template <typename T>
 __global__ __launch_bounds__(kMergeThreads) void merge_state_kernel(
     const T *va, const float *sa, const T *vb, const float *sb, T *vo, float *so, int64_t units,
-    const int32_t *count, int heads, int head_dim)
+    int head_dim)
 {
     const int lane = threadIdx.x;
-    if (count) units = min(units, int64_t(count[0]) * heads);
     for (int64_t u = blockIdx.x; u < units; u += gridDim.x) {
         const float a = sa[u], b = sb[u];
         const float M = fmaxf(a, b);
@@ -66,20 +65,19 @@ __global__ __launch_bounds__(kMergeThreads) void merge_state_kernel(
 }  // namespace
 
 hipError_t launch_merge_state(const void *va, const float *sa, const void *vb, const float *sb,
-                              void *vo, float *so, int64_t n, const int32_t *count,
-                              int32_t heads, int32_t head_dim, int32_t dtype, int grid,
-                              hipStream_t s)
+                              void *vo, float *so, int64_t n, int32_t heads, int32_t head_dim,
+                              int32_t dtype, int grid, hipStream_t s)
 {
     const int64_t units = n * heads;
     if (units == 0) return hipSuccess;
     if (dtype == PKVS_BF16)
         merge_state_kernel<uint16_t><<<grid, kMergeThreads, 0, s>>>(
             static_cast<const uint16_t *>(va), sa, static_cast<const uint16_t *>(vb), sb,
-            static_cast<uint16_t *>(vo), so, units, count, heads, head_dim);
+            static_cast<uint16_t *>(vo), so, units, head_dim);
     else
         merge_state_kernel<float><<<grid, kMergeThreads, 0, s>>>(
             static_cast<const float *>(va), sa, static_cast<const float *>(vb), sb,
-            static_cast<float *>(vo), so, units, count, heads, head_dim);
+            static_cast<float *>(vo), so, units, head_dim);
     return hipGetLastError();
 }
 

@@ -19,7 +19,6 @@ enum HeaderField {
     kHdrNumMerges = 1,
     kHdrMergeOffset = 2,  // in int32 words from the start of the workspace
     kHdrItemWords = 3,
-    kHdrNumTokens = 4,    // query tokens of the planned batch (the cascade merge reads it)
 };
 
 // Prefill item: one (request, kv head, query tile).
@@ -87,6 +86,11 @@ struct PrefillArgs {
     int32_t num_qo_heads, num_kv_heads, log2_group, page_size, log2_page;
     int32_t page_rows;  // cache rows one page-table step spans: page_size, or 1 (ragged)
     int32_t window_left, causal;
+    // optional partial (o, lse) over other keys of the same queries, laid out
+    // like o / lse: when set, the kernel stores the merge of its own result
+    // with it (merge_state folded into the epilogue)
+    const void *fold_o;
+    const float *fold_lse;
 };
 
 struct DecodeArgs {
@@ -109,12 +113,9 @@ hipError_t launch_attention_fp32(const PrefillArgs &a, int head_dim, int grid, h
 hipError_t launch_decode_bf16(const DecodeArgs &a, int head_dim, int grid, hipStream_t s);
 hipError_t launch_decode_merge(const DecodeArgs &a, int head_dim, int dtype, int grid,
                                hipStream_t s);
-// n tokens, or (count != null) the token count the kernel reads from
-// count[0] at run time, at most n
 hipError_t launch_merge_state(const void *va, const float *sa, const void *vb, const float *sb,
-                              void *vo, float *so, int64_t n, const int32_t *count,
-                              int32_t heads, int32_t head_dim, int32_t dtype, int grid,
-                              hipStream_t s);
+                              void *vo, float *so, int64_t n, int32_t heads, int32_t head_dim,
+                              int32_t dtype, int grid, hipStream_t s);
 
 // Resident workgroups per CU of each kernel (occupancy query; 0 if unknown).
 int prefill_bf16_blocks_per_cu(int head_dim, int variant);

@@ -260,11 +260,8 @@ static void build_prefill(Plan *p, const std::vector<Req> &reqs)
     p->n_merges = 0;
     p->split_size = 0;
     p->host_ws.assign(p->lead_words + kHeaderWords + items.size() * kPrefillItemWords, 0);
-    int64_t tokens = 0, keys = 0;
-    for (const Req &r : reqs) {
-        tokens += r.qo_len;
-        keys += r.kv_len;
-    }
+    int64_t keys = 0;
+    for (const Req &r : reqs) keys += r.kv_len;
     p->planned_keys = keys;
     if (p->ragged) {
         // row-index table: entry t of request b is the row of its key
@@ -278,7 +275,6 @@ static void build_prefill(Plan *p, const std::vector<Req> &reqs)
     w[kHdrNumMerges] = 0;
     w[kHdrMergeOffset] = int32_t(p->host_ws.size() - p->lead_words);
     w[kHdrItemWords] = kPrefillItemWords;
-    w[kHdrNumTokens] = int32_t(tokens);
     for (size_t i = 0; i < items.size(); ++i)
         std::memcpy(w + kHeaderWords + i * kPrefillItemWords, items[i].w, sizeof items[i].w);
 }
@@ -507,7 +503,8 @@ static size_t align256(size_t x) { return (x + 255) / 256 * 256; }
 // before every new token, so there only the window's left edge hides keys
 // ([FIB] FlashInferIndicesUpdaterPrefill._build_swa_prefix_custom_mask:
 // visible iff k_abs >= q_abs - window).  merge_state combines the two (o, lse)
-// pairs.  The float workspace holds the prefix pass's o and both passes' lse.
+// pairs: the prefix pass runs first and leaves its (o, lse) in the float
+// workspace, and the extend pass folds them into its own in its epilogue.
 static int create_cascade(const pkvs_desc *desc, Plan **out)
 {
     pkvs_desc e = *desc, r = *desc;
@@ -540,8 +537,7 @@ static int create_cascade(const pkvs_desc *desc, Plan **out)
     const size_t esz = desc->dtype == PKVS_BF16 ? 2 : 4;
     const size_t rows = size_t(desc->qo_capacity) * size_t(desc->num_qo_heads);
     p->o2_off = 0;
-    p->lse1_off = align256(rows * size_t(desc->head_dim) * esz);
-    p->lse2_off = p->lse1_off + align256(rows * sizeof(float));
+    p->lse2_off = align256(rows * size_t(desc->head_dim) * esz);
     p->float_ws_need = p->lse2_off + rows * sizeof(float);
     *out = p;
     return PKVS_OK;

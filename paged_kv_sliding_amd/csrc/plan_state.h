@@ -46,7 +46,7 @@ struct pkvs_plan {
     // caller's workspaces between them.
     pkvs_plan *ext = nullptr, *pre = nullptr;
     size_t pre_int_off = 0;                         // bytes into int_ws
-    size_t o2_off = 0, lse1_off = 0, lse2_off = 0;  // bytes into float_ws
+    size_t o2_off = 0, lse2_off = 0;                // bytes into float_ws
 
     // the last plan() call
     std::vector<int32_t> host_ws;  // header + items + merge entries

@@ -47,6 +47,24 @@ constexpr int VPAD = 32;               // V rows: D+32 bf16, a stride of 16 dwor
 constexpr int NBUF = 4;                // LDS tile sets in flight
 constexpr float kRescaleLog2 = 8.0f;   // rescale O only when a row max grows by > 2^8
 
+// Folding this pass's (o, lse) of a row into a second partial over other keys
+// of the same query (sglang flashinfer_backend.py, _safe_merge_state):
+// s = ln(e^s_self + e^s_other), o = e^(s_self - s) o_self + e^(s_other - s) o_other;
+// two empty partials stay empty (o = 0, s = -inf).
+struct Fold {
+    float self, other, lse;
+};
+
+__device__ __forceinline__ Fold fold_weights(float s_self, float s_other)
+{
+    constexpr float kLog2e = 1.44269504088896340736f;
+    const float M = fmaxf(s_self, s_other);
+    if (M == kNegInf) return Fold{0.f, 0.f, kNegInf};
+    const float ea = fast_exp2((s_self - M) * kLog2e), eb = fast_exp2((s_other - M) * kLog2e);
+    const float sum = ea + eb;
+    return Fold{ea / sum, eb / sum, M + fast_log2(sum) * kLn2};
+}
+
 typedef short i16x4 __attribute__((ext_vector_type(4)));
 typedef __attribute__((address_space(3))) i16x4 lds_i16x4;
 
@@ -575,22 +593,35 @@ __global__ __launch_bounds__(NW * 64) void prefill_bf16_kernel(PrefillArgs a)
 
         // epilogue: the two half-waves hold disjoint keys of each row
         l += __shfl_xor(l, 32);
-        const float inv = l > 0.f ? 1.f / l : 0.f;
         if (row_valid) {
+            const int64_t lrow = int64_t(q_begin + row_tok) * a.num_qo_heads + hk * G + row_head;
+            float w_self = l > 0.f ? 1.f / l : 0.f, w_other = 0.f;
+            float lse_row = l > 0.f ? (m + fast_log2(l)) * kLn2 : kNegInf;
+            if (a.fold_lse) {
+                const Fold f = fold_weights(lse_row, a.fold_lse[lrow]);
+                w_self *= f.self;
+                w_other = f.other;
+                lse_row = f.lse;
+            }
             uint16_t *O = static_cast<uint16_t *>(a.o);
+            const uint16_t *FO = static_cast<const uint16_t *>(a.fold_o);
 #pragma unroll
             for (int dt = 0; dt < DT; ++dt)
 #pragma unroll
                 for (int m0 = 0; m0 < 4; ++m0) {
+                    const int64_t at = qrow + dt * 32 + 8 * m0 + 4 * hw;
                     f32x4 v4;
 #pragma unroll
-                    for (int m1 = 0; m1 < 4; ++m1) v4[m1] = o[dt][4 * m0 + m1] * inv;
-                    *reinterpret_cast<bf16x4 *>(O + qrow + dt * 32 + 8 * m0 + 4 * hw) =
-                        __builtin_convertvector(v4, bf16x4);
+                    for (int m1 = 0; m1 < 4; ++m1) v4[m1] = o[dt][4 * m0 + m1] * w_self;
+                    if (FO) {
+                        const f32x4 f4 = __builtin_convertvector(
+                            *reinterpret_cast<const bf16x4 *>(FO + at), f32x4);
+#pragma unroll
+                        for (int m1 = 0; m1 < 4; ++m1) v4[m1] += f4[m1] * w_other;
+                    }
+                    *reinterpret_cast<bf16x4 *>(O + at) = __builtin_convertvector(v4, bf16x4);
                 }
-            if (a.lse && hw == 0)
-                a.lse[int64_t(q_begin + row_tok) * a.num_qo_heads + hk * G + row_head] =
-                    l > 0.f ? (m + fast_log2(l)) * kLn2 : kNegInf;
+            if (a.lse && hw == 0) a.lse[lrow] = lse_row;
         }
         __syncthreads();  // the next item's prologue overwrites the LDS sets
     }
@@ -869,22 +900,36 @@ __global__ __launch_bounds__(256) void prefill_wide_kernel(PrefillArgs a)
 #pragma unroll
         for (int n = 0; n < 2; ++n) {
             float ln = l[n] + __shfl_xor(l[n], 32);
-            const float inv = ln > 0.f ? 1.f / ln : 0.f;
             if (row_valid[n]) {
+                const int64_t lrow =
+                    int64_t(q_begin + row_tok[n]) * a.num_qo_heads + hk * G + row_head[n];
+                float w_self = ln > 0.f ? 1.f / ln : 0.f, w_other = 0.f;
+                float lse_row = ln > 0.f ? (m[n] + fast_log2(ln)) * kLn2 : kNegInf;
+                if (a.fold_lse) {
+                    const Fold f = fold_weights(lse_row, a.fold_lse[lrow]);
+                    w_self *= f.self;
+                    w_other = f.other;
+                    lse_row = f.lse;
+                }
                 uint16_t *O = static_cast<uint16_t *>(a.o);
+                const uint16_t *FO = static_cast<const uint16_t *>(a.fold_o);
 #pragma unroll
                 for (int dt = 0; dt < DT; ++dt)
 #pragma unroll
                     for (int m0 = 0; m0 < 4; ++m0) {
+                        const int64_t at = qrow[n] + dt * 32 + 8 * m0 + 4 * hw;
                         f32x4 v4;
 #pragma unroll
-                        for (int m1 = 0; m1 < 4; ++m1) v4[m1] = o[n][dt][4 * m0 + m1] * inv;
-                        *reinterpret_cast<bf16x4 *>(O + qrow[n] + dt * 32 + 8 * m0 + 4 * hw) =
-                            __builtin_convertvector(v4, bf16x4);
+                        for (int m1 = 0; m1 < 4; ++m1) v4[m1] = o[n][dt][4 * m0 + m1] * w_self;
+                        if (FO) {
+                            const f32x4 f4 = __builtin_convertvector(
+                                *reinterpret_cast<const bf16x4 *>(FO + at), f32x4);
+#pragma unroll
+                            for (int m1 = 0; m1 < 4; ++m1) v4[m1] += f4[m1] * w_other;
+                        }
+                        *reinterpret_cast<bf16x4 *>(O + at) = __builtin_convertvector(v4, bf16x4);
                     }
-                if (a.lse && hw == 0)
-                    a.lse[int64_t(q_begin + row_tok[n]) * a.num_qo_heads + hk * G + row_head[n]] =
-                        ln > 0.f ? (m[n] + fast_log2(ln)) * kLn2 : kNegInf;
+                if (a.lse && hw == 0) a.lse[lrow] = lse_row;
             }
         }
         __syncthreads();  // the next item's prologue overwrites the LDS sets
@@ -935,11 +980,21 @@ __global__ __launch_bounds__(kGenericThreads) void attention_fp32_kernel(Prefill
                 for (int e = 0; e < E; ++e) acc[e] = acc[e] * alpha + pj * V[off + lane + 64 * e];
                 m = m_new;
             }
-            const float inv = l > 0.f ? 1.f / l : 0.f;
-            for (int e = 0; e < E; ++e) O[qrow + lane + 64 * e] = acc[e] * inv;
-            if (a.lse && lane == 0)
-                a.lse[int64_t(q_begin + tok) * a.num_qo_heads + h] =
-                    l > 0.f ? (m + fast_log2(l)) * kLn2 : kNegInf;
+            const int64_t lrow = int64_t(q_begin + tok) * a.num_qo_heads + h;
+            float w_self = l > 0.f ? 1.f / l : 0.f, w_other = 0.f;
+            float lse_row = l > 0.f ? (m + fast_log2(l)) * kLn2 : kNegInf;
+            if (a.fold_lse) {
+                const Fold f = fold_weights(lse_row, a.fold_lse[lrow]);
+                w_self *= f.self;
+                w_other = f.other;
+                lse_row = f.lse;
+            }
+            const float *FO = static_cast<const float *>(a.fold_o);
+            for (int e = 0; e < E; ++e) {
+                const int64_t at = qrow + lane + 64 * e;
+                O[at] = acc[e] * w_self + (FO ? FO[at] * w_other : 0.f);
+            }
+            if (a.lse && lane == 0) a.lse[lrow] = lse_row;
         }
     }
 }

@@ -47,10 +47,12 @@ int check_run(const pkvs_plan *p, int kind, const void *q, const void *k, const 
 // launches: the kernels read the item count from the workspace, so a captured
 // graph replays correctly after any later plan of the same capacities.  A
 // ragged pass reads its keys through the row-index table in front of its
-// work list.
+// work list.  With fold_lse set the pass stores the merge of its result with
+// the partial (fold_o, fold_lse) of the same queries.
 hipError_t launch_prefill_pass(const pkvs_plan *p, const void *q, const void *k, const void *v,
                                int64_t num_pages, const int32_t *kv_indices, void *o, float *lse,
-                               float sm_scale, hipStream_t stream)
+                               float sm_scale, hipStream_t stream, const void *fold_o = nullptr,
+                               const float *fold_lse = nullptr)
 {
     const int32_t *ws = static_cast<const int32_t *>(p->int_ws);
     PrefillArgs a{};
@@ -71,6 +73,8 @@ hipError_t launch_prefill_pass(const pkvs_plan *p, const void *q, const void *k,
     a.page_rows = p->ragged ? 1 : p->desc.page_size;
     a.window_left = p->desc.window_left;
     a.causal = p->desc.causal;
+    a.fold_o = fold_o;
+    a.fold_lse = fold_lse;
     return p->desc.dtype == PKVS_BF16
                ? launch_prefill_bf16(a, p->desc.head_dim, p->run_variant, p->grid_blocks, stream)
                : launch_attention_fp32(a, p->desc.head_dim, p->grid_blocks, stream);
@@ -115,25 +119,15 @@ int pkvs_cascade_run(const pkvs_plan *p, const void *q, const void *k_extend,
                     "table or num_pages <= 0");
     char *fws = static_cast<char *>(p->float_ws);
     void *o2 = fws + p->o2_off;
-    float *lse1 = reinterpret_cast<float *>(fws + p->lse1_off);
     float *lse2 = reinterpret_cast<float *>(fws + p->lse2_off);
-    // extend pass -> (o, lse1); prefix pass -> (o2, lse2); o, lse = merge
-    hipError_t e = launch_prefill_pass(p->ext, q, k_extend, v_extend, 0, nullptr, o, lse1,
-                                       sm_scale, stream);
-    if (e != hipSuccess) return fail(PKVS_ERR_HIP, "extend pass launch: %s", hipGetErrorString(e));
-    e = launch_prefill_pass(p->pre, q, k_cache, v_cache, std::max<int64_t>(num_pages, 1),
-                            kv_indices_d, o2, lse2, sm_scale, stream);
+    // prefix pass -> (o2, lse2); the extend pass stores the merge of its own
+    // (o, lse) with them
+    hipError_t e = launch_prefill_pass(p->pre, q, k_cache, v_cache, std::max<int64_t>(num_pages, 1),
+                                       kv_indices_d, o2, lse2, sm_scale, stream);
     if (e != hipSuccess) return fail(PKVS_ERR_HIP, "prefix pass launch: %s", hipGetErrorString(e));
-    // the merge reads the planned token count from the extend pass's work
-    // list header, over a grid fixed by the capacity
-    const int heads = p->desc.num_qo_heads;
-    const int64_t units = p->desc.qo_capacity * heads;
-    const int grid = int(std::max<int64_t>(1, std::min<int64_t>(units, int64_t(p->num_cus) * 32)));
-    const int32_t *hdr = static_cast<const int32_t *>(p->ext->int_ws) + p->ext->lead_words;
-    e = launch_merge_state(o, lse1, o2, lse2, o, lse ? lse : lse1, p->desc.qo_capacity,
-                           hdr + kHdrNumTokens, heads, p->desc.head_dim, p->desc.dtype, grid,
-                           stream);
-    if (e != hipSuccess) return fail(PKVS_ERR_HIP, "merge launch: %s", hipGetErrorString(e));
+    e = launch_prefill_pass(p->ext, q, k_extend, v_extend, 0, nullptr, o, lse, sm_scale, stream,
+                            o2, lse2);
+    if (e != hipSuccess) return fail(PKVS_ERR_HIP, "extend pass launch: %s", hipGetErrorString(e));
     return PKVS_OK;
 }
 
@@ -224,8 +218,8 @@ int pkvs_merge_state(const void *v_a, const float *s_a, const void *v_b, const f
         (void)hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev);
     const int64_t units = num_tokens * num_heads;
     const int grid = int(std::min<int64_t>(units, int64_t(cus) * 32));
-    hipError_t e = launch_merge_state(v_a, s_a, v_b, s_b, v_out, s_out, num_tokens, nullptr,
-                                      num_heads, head_dim, v_dtype, grid, stream);
+    hipError_t e = launch_merge_state(v_a, s_a, v_b, s_b, v_out, s_out, num_tokens, num_heads,
+                                      head_dim, v_dtype, grid, stream);
     if (e != hipSuccess) return fail(PKVS_ERR_HIP, "merge_state launch: %s", hipGetErrorString(e));
     return PKVS_OK;
 }
