@@ -59,6 +59,10 @@ class OracleLib:
         ]
         lib.oracle_merge_state.restype = None
         lib.oracle_merge_state.argtypes = [i64, i32, i32, P, P, P, P, P, P]
+        lib.oracle_append_kv.restype = i64
+        lib.oracle_append_kv.argtypes = [i64, P, i64, P, P, i64, P, P]
+        lib.oracle_build_kv_indices.restype = i64
+        lib.oracle_build_kv_indices.argtypes = [i32, P, i64, i64, P, P, P, P, P, i64]
         self.lib = lib
         self.path = path
 
@@ -167,3 +171,49 @@ def merge_many(parts, impl: Optional[OracleLib] = None):
     for vb, sb in parts[1:]:
         v, s = merge_state(v, s, vb, sb, impl=impl)
     return v, s
+
+
+def append_kv(k_new, v_new, loc, k_cache, v_cache, impl: Optional[OracleLib] = None):
+    """Host copies of the caches after writing row i of k_new / v_new to slot
+    loc[i] (slot = page * page_size + position in the page); returns
+    (k_cache, v_cache, skipped rows).  Inputs are torch tensors of one dtype."""
+    import torch
+
+    lib = (impl or _load()).lib
+    kc = k_cache.detach().cpu().contiguous().clone()
+    vc = v_cache.detach().cpu().contiguous().clone()
+    kn = k_new.detach().cpu().contiguous()
+    vn = v_new.detach().cpu().contiguous()
+    if not (kc.dtype == vc.dtype == kn.dtype == vn.dtype):
+        raise TypeError("append_kv: one dtype for caches and new rows")
+    row = kn[0].numel() * kn.element_size() if kn.shape[0] else 0
+    num_slots = kc.numel() * kc.element_size() // row if row else 0
+    lo = np.ascontiguousarray(torch.as_tensor(loc).cpu().numpy().astype(np.int64))
+    u8 = lambda t: t.view(torch.uint8).numpy()
+    kb, vb = u8(kc.view(-1)), u8(vc.view(-1))
+    skipped = lib.oracle_append_kv(kn.shape[0], _ptr(lo), row, _ptr(u8(kn.view(-1))),
+                                   _ptr(u8(vn.view(-1))), num_slots, _ptr(kb), _ptr(vb))
+    return kc, vc, int(skipped)
+
+
+def build_kv_indices(page_map, slot, length, start=None, capacity=None,
+                     impl: Optional[OracleLib] = None):
+    """(kv_indptr [B+1], kv_indices [capacity], errors) gathered from the
+    request-to-page map ``page_map`` [rows, cols] int32.  Unwritten entries of
+    kv_indices hold the sentinel 0x7fffffff."""
+    lib = (impl or _load()).lib
+    m = _i32(page_map)
+    if m.ndim != 2:
+        raise ValueError("build_kv_indices: the map is 2-D")
+    sl, ln = _i32(slot), _i32(length)
+    st = _i32(start) if start is not None else None
+    B = len(sl)
+    if capacity is None:
+        capacity = int(np.maximum(ln, 0).sum())
+    indptr = np.zeros(B + 1, dtype=np.int32)
+    idx = np.full(max(capacity, 1), 0x7FFFFFFF, dtype=np.int32)
+    err = lib.oracle_build_kv_indices(B, _ptr(m), m.shape[0], m.shape[1], _ptr(sl),
+                                      _ptr(st) if st is not None else None, _ptr(ln),
+                                      _ptr(indptr), _ptr(idx), capacity)
+    return indptr, idx[:capacity], int(err)
+

@@ -1,6 +1,8 @@
 /*
  * oracle.c -- plain CPU reference for batched attention over a paged KV cache
- * with a sliding-window mask, plus the merge of two (output, LSE) partials.
+ * with a sliding-window mask, the merge of two (output, LSE) partials, and the
+ * two steps on either side of it: writing new key/value rows into the cache
+ * and building the page table from a request-to-page map.
  *
  * TEST INFRASTRUCTURE ONLY.  Nothing in the product library links, loads or
  * calls this file; only the tests, the smoke check and the CPU-baseline leg
@@ -246,4 +248,79 @@ void oracle_merge_state(int64_t n, int32_t num_heads, int32_t head_dim, const do
             vo[d] = wa * va[d] + wb * vb[d];
         s_out[i] = s;
     }
+}
+
+/*
+ * Writing new keys and values into the cache ([FIB] forward_extend and
+ * forward_decode call token_to_kv_pool.set_kv_buffer with the batch's cache
+ * locations before the paged attention reads them).
+ *
+ * The cache is viewed as num_slots rows of row_bytes bytes (slot = page *
+ * page_size + position in the page).  Row i of k_new / v_new goes to slot
+ * loc[i]; a loc outside [0, num_slots) writes nothing and is counted.
+ * Returns the number of such skipped rows.
+ */
+int64_t oracle_append_kv(int64_t n, const int64_t *loc, int64_t row_bytes, const uint8_t *k_new,
+                         const uint8_t *v_new, int64_t num_slots, uint8_t *k_cache,
+                         uint8_t *v_cache)
+{
+    int64_t skipped = 0;
+    for (int64_t i = 0; i < n; ++i) {
+        const int64_t s = loc[i];
+        if (s < 0 || s >= num_slots) {
+            ++skipped;
+            continue;
+        }
+        memcpy(k_cache + s * row_bytes, k_new + i * row_bytes, (size_t)row_bytes);
+        memcpy(v_cache + s * row_bytes, v_new + i * row_bytes, (size_t)row_bytes);
+    }
+    return skipped;
+}
+
+/*
+ * Building the page table on the device ([FIB] call_begin_forward: kv_indptr
+ * is the running sum of the per-request lengths, and the gather
+ * create_flashinfer_kv_indices_triton copies, for request b, entries
+ * start[b] .. start[b] + len[b] - 1 of row slot[b] of the request-to-page map
+ * into kv_indices from kv_indptr[b] on).
+ *
+ *  map      [map_rows, map_cols] int32     start  [batch] or NULL (all 0)
+ *  slot     [batch] rows of the map        len    [batch] entries per request
+ *  kv_indptr [batch + 1] (out)             kv_indices [capacity] (out)
+ *
+ * A negative len counts as 0; an entry whose source lies outside the map is
+ * written as -1; an entry past `capacity` is not written.  Each of these is
+ * counted in the return value.
+ */
+int64_t oracle_build_kv_indices(int32_t batch, const int32_t *map, int64_t map_rows,
+                                int64_t map_cols, const int32_t *slot, const int32_t *start,
+                                const int32_t *len, int32_t *kv_indptr, int32_t *kv_indices,
+                                int64_t capacity)
+{
+    int64_t errors = 0;
+    kv_indptr[0] = 0;
+    for (int32_t b = 0; b < batch; ++b) {
+        int64_t n = len[b];
+        if (n < 0) {
+            ++errors;
+            n = 0;
+        }
+        kv_indptr[b + 1] = (int32_t)(kv_indptr[b] + n);
+        const int64_t s0 = start ? start[b] : 0;
+        for (int64_t j = 0; j < n; ++j) {
+            const int64_t dst = (int64_t)kv_indptr[b] + j;
+            if (dst >= capacity) {
+                ++errors;
+                continue;
+            }
+            const int64_t col = s0 + j;
+            if (slot[b] < 0 || slot[b] >= map_rows || col < 0 || col >= map_cols) {
+                ++errors;
+                kv_indices[dst] = -1;
+            } else {
+                kv_indices[dst] = map[(int64_t)slot[b] * map_cols + col];
+            }
+        }
+    }
+    return errors;
 }

@@ -19,6 +19,7 @@ of the oracle (see ``test_oracle_mutants.py``).
 """
 from __future__ import annotations
 
+import dataclasses
 import math
 import os
 
@@ -376,6 +377,115 @@ def check_merge_algebra(impl=None):
     assert close(v, (va + vb) / 2) and close(s, sa + math.log(2.0))
 
 
+# --------------------------------------------------------------------------- cache writes, page tables
+
+
+def check_append_round_trip(impl=None):
+    """Writing every key / value of a paged batch into an empty pool at slot
+    page * P + (position mod P) rebuilds the cache at those slots, and the
+    attention over the rebuilt pool equals the attention over the original."""
+    for P in (1, 4):
+        case = small_case([3, 5, 1], [7, 5, 13], P=P, H_q=4, H_kv=2, D=8, seed=20 + P)
+        kvp = case.kv_indptr.tolist()
+        loc, ks, vs = [], [], []
+        for b in range(case.batch_size):
+            K, V = dense_kv(case, b)
+            pages = case.kv_indices[kvp[b]:kvp[b + 1]].tolist()
+            for j in range(case.kv_lens[b]):
+                loc.append(pages[j // P] * P + j % P)
+            ks.append(torch.from_numpy(K).float())
+            vs.append(torch.from_numpy(V).float())
+        order = np.random.default_rng(P).permutation(len(loc))  # any write order
+        k_new = torch.cat(ks)[order]
+        v_new = torch.cat(vs)[order]
+        loc = torch.tensor(loc)[order]
+        empty_k = torch.full_like(case.k_cache, float("nan"))
+        empty_v = torch.full_like(case.v_cache, float("nan"))
+        kc, vc, skipped = oracle.append_kv(k_new, v_new, loc, empty_k, empty_v, impl=impl)
+        assert skipped == 0
+        flat = lambda t: t.reshape(-1, case.num_kv_heads, case.head_dim)
+        assert torch.equal(flat(kc)[loc], flat(case.k_cache)[loc])
+        assert torch.equal(flat(vc)[loc], flat(case.v_cache)[loc])
+        rebuilt = dataclasses.replace(case, k_cache=kc, v_cache=vc)
+        o1, l1 = run(case, impl)
+        o2, l2 = run(rebuilt, impl)
+        assert np.array_equal(o1, o2) and np.array_equal(l1, l2), P
+
+
+def check_append_matches_scatter(impl=None):
+    """Row i lands in slot loc[i] (numpy indexed assignment); rows whose slot
+    lies outside the pool are skipped and counted; other slots keep their
+    bytes (bf16 rows, compared bit for bit)."""
+    rng = np.random.default_rng(5)
+    cache_k = torch.from_numpy(rng.standard_normal((6, 4, 2, 8))).to(torch.bfloat16)
+    cache_v = torch.from_numpy(rng.standard_normal((6, 4, 2, 8))).to(torch.bfloat16)
+    k_new = torch.from_numpy(rng.standard_normal((7, 2, 8))).to(torch.bfloat16)
+    v_new = torch.from_numpy(rng.standard_normal((7, 2, 8))).to(torch.bfloat16)
+    loc = np.array([23, 0, -1, 5, 24, 17, 9])
+    kc, vc, skipped = oracle.append_kv(k_new, v_new, torch.from_numpy(loc), cache_k, cache_v,
+                                       impl=impl)
+    assert skipped == 2
+    for got, cache, new in ((kc, cache_k, k_new), (vc, cache_v, v_new)):
+        want = cache.view(torch.int16).numpy().reshape(24, 2, 8).copy()
+        ok = (loc >= 0) & (loc < 24)
+        want[loc[ok]] = new.view(torch.int16).numpy()[ok]
+        assert np.array_equal(got.view(torch.int16).numpy().reshape(24, 2, 8), want)
+
+
+def check_build_indices_golden(impl=None):
+    """The hand-derived example of tests/golden/kv_indices_build.txt."""
+    rows = {}
+    with open(os.path.join(GOLDEN, "kv_indices_build.txt")) as f:
+        for line in f:
+            if line.strip() and not line.startswith("#"):
+                key, *vals = line.split()
+                rows.setdefault(key, []).append([int(v) for v in vals])
+    m = np.array([[100 * r + c for c in range(6)] for r in range(4)], dtype=np.int32)
+    spec = np.array(rows["map"])
+    indptr, idx, err = oracle.build_kv_indices(m, spec[:, 0], spec[:, 2], start=spec[:, 1],
+                                               impl=impl)
+    assert err == 0
+    assert indptr.tolist() == rows["indptr"][0]
+    assert idx.tolist() == rows["indices"][0]
+
+
+def check_build_indices_reproduce_page_tables(impl=None):
+    """A map whose rows hold each request's pages (rows in shuffled order, junk
+    after the last page) gives back the batch's CSR page table; with a start it
+    gives the slice from that page on (numpy slicing)."""
+    case = small_case([1, 1, 1, 1], [9, 1, 30, 17], P=4, seed=31, spare=5)
+    kvp = case.kv_indptr.tolist()
+    pages = [case.kv_indices[kvp[b]:kvp[b + 1]].tolist() for b in range(4)]
+    cols = max(len(p) for p in pages) + 3
+    row_of = [2, 0, 3, 1]
+    m = np.full((4, cols), 999, dtype=np.int32)
+    for b, p in enumerate(pages):
+        m[row_of[b], :len(p)] = p
+    lens = [len(p) for p in pages]
+    indptr, idx, err = oracle.build_kv_indices(m, row_of, lens, impl=impl)
+    assert err == 0 and indptr.tolist() == kvp
+    assert idx.tolist() == case.kv_indices.tolist()
+    start = [1, 0, 5, 2]
+    lens2 = [lens[b] - start[b] for b in range(4)]
+    indptr, idx, err = oracle.build_kv_indices(m, row_of, lens2, start=start, impl=impl)
+    want = np.concatenate([m[row_of[b], start[b]:start[b] + lens2[b]] for b in range(4)])
+    assert err == 0 and np.array_equal(idx, want)
+    assert np.array_equal(np.diff(indptr), lens2)
+
+
+def check_build_indices_errors(impl=None):
+    """Entries outside the map come out as -1, a negative length counts as 0,
+    entries past the capacity are not written; each is counted."""
+    m = np.arange(12, dtype=np.int32).reshape(3, 4)
+    indptr, idx, err = oracle.build_kv_indices(m, [0, 5, 2, 1], [2, 1, -3, 3],
+                                               start=[3, 0, 0, -1], capacity=5, impl=impl)
+    assert indptr.tolist() == [0, 2, 3, 3, 6]
+    # request 0: col 3 ok, col 4 outside; request 1: row 5 outside;
+    # request 2: negative length; request 3: col -1 outside, col 0 ok, dst 5 past capacity
+    assert idx.tolist() == [3, -1, -1, -1, 4]
+    assert err == 1 + 1 + 1 + 1 + 1
+
+
 ALL_CHECKS = [
     check_zero_query_closed_form,
     check_golden_decode_counts,
@@ -389,6 +499,11 @@ ALL_CHECKS = [
     check_paging_invariance,
     check_empty_sets,
     check_decode_trim,
+    check_append_round_trip,
+    check_append_matches_scatter,
+    check_build_indices_golden,
+    check_build_indices_reproduce_page_tables,
+    check_build_indices_errors,
     check_prefill_trim,
     check_merge_split_equals_unsplit,
     check_merge_algebra,

@@ -39,6 +39,15 @@ MUTANTS = {
     "merge_shift_dropped": ("const double s = M + log(exp(a - M) + exp(b - M));",
                             "const double s = log(exp(a - M) + exp(b - M));"),
     "merge_empty_nonzero": ("s_out[i] = -INFINITY;", "s_out[i] = 0.0;"),
+    "append_values_from_keys": ("memcpy(v_cache + s * row_bytes, v_new + i * row_bytes",
+                                "memcpy(v_cache + s * row_bytes, k_new + i * row_bytes"),
+    "append_ignores_loc": ("const int64_t s = loc[i];", "const int64_t s = i;"),
+    "indices_start_ignored": ("const int64_t s0 = start ? start[b] : 0;", "const int64_t s0 = 0;"),
+    "indptr_not_cumulative": ("kv_indptr[b + 1] = (int32_t)(kv_indptr[b] + n);",
+                              "kv_indptr[b + 1] = (int32_t)n;"),
+    "indices_map_transposed": ("kv_indices[dst] = map[(int64_t)slot[b] * map_cols + col];",
+                               "kv_indices[dst] = map[col * map_rows + slot[b]];"),
+    "indices_bad_source_kept": ("kv_indices[dst] = -1;", "kv_indices[dst] = 0;"),
 }
 
 
