@@ -23,6 +23,8 @@ Reported (one JSON line):
   cascade        the cascade prefill (new tokens' K/V contiguous, cached prefix
                  paged, merged), timed apart on two batches with cached
                  prefixes, beside the one paged prefill of the same batch
+  pool           cache writes of a 32768-token prompt's K/V and the split
+                 decode's page-table build, timed apart
 
     python bench.py [--steps K] [--warmup W] [--gpus 1] [--no-cpu-baseline]
 """
@@ -176,6 +178,61 @@ def bench_cascade(reps: int) -> dict:
     return out
 
 
+def bench_pool(reps: int) -> dict:
+    """The steps on either side of the attention: writing a 32768-token
+    prompt's keys and values into its pages (slot = page * 16 + position, the
+    long prefill's own page table) and building the split decode's page table
+    (256 requests, up to 2048 pages each) from a request-to-page map.  HIP
+    events around each call on the launch stream."""
+    import torch
+
+    from paged_kv_sliding_amd import pkvs as P
+
+    def timed(fn):
+        for _ in range(3):
+            fn()
+        ts = []
+        for _ in range(reps):
+            a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            a.record()
+            fn()
+            b.record()
+            torch.cuda.synchronize()
+            ts.append(a.elapsed_time(b))
+        return sum(ts) / len(ts)
+
+    out = {}
+    g = torch.Generator(device="cuda").manual_seed(41)
+    n, H, D, Psz = 32768, 8, 128, 16
+    pages = torch.randperm(n // Psz, device="cuda")
+    pos = torch.arange(n, device="cuda")
+    loc = (pages[pos // Psz] * Psz + pos % Psz).to(torch.int64)
+    k_new = torch.randn(n, H, D, generator=g, device="cuda").to(torch.bfloat16)
+    v_new = torch.randn(n, H, D, generator=g, device="cuda").to(torch.bfloat16)
+    kc = torch.empty(n // Psz, Psz, H, D, dtype=torch.bfloat16, device="cuda")
+    vc = torch.empty_like(kc)
+    ms = timed(lambda: P.pkvs_append_kv(k_new, v_new, loc, kc, vc))
+    nbytes = 2 * 2 * n * H * D * 2  # K and V rows, read once and written once
+    out["kv_append"] = {"rows": n, "row_bytes": H * D * 2, "ms": round(ms, 4),
+                        "bytes": nbytes, "GB/s": round(nbytes / (ms * 1e-3) / 1e9, 1),
+                        "frac_of_hbm_peak": round(nbytes / (ms * 1e-3) / 1e9 / PEAK_HBM_GBPS, 4)}
+    del k_new, v_new, kc, vc
+    gen = torch.Generator().manual_seed(5)
+    kv = torch.randint(1024, 32769, (256,), generator=gen)
+    npg = ((kv + 15) // 16).to(torch.int32)
+    page_map = torch.randint(0, 1 << 20, (256, 2048), dtype=torch.int32, device="cuda")
+    slot = torch.randperm(256, device="cuda").to(torch.int32)
+    length = npg.to("cuda")
+    cap = int(npg.sum())
+    kp = torch.empty(257, dtype=torch.int32, device="cuda")
+    ki = torch.empty(cap, dtype=torch.int32, device="cuda")
+    ms = timed(lambda: P.pkvs_build_kv_indices(page_map, slot, length, kv_indptr=kp,
+                                               kv_indices=ki, capacity=cap))
+    out["page_table_build"] = {"requests": 256, "entries": cap, "ms": round(ms, 4),
+                               "bytes": cap * 8 + 256 * 12}
+    return out
+
+
 def profile_kernel(which: str, reps: int) -> None:
     """Launch one kernel `reps` times and nothing else timed, for rocprofv3
     counter passes; prints the source digest the counters belong to."""
@@ -321,7 +378,8 @@ def main():
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-budget", type=float, default=15.0)
-    ap.add_argument("--only", choices=["prefill", "decode", "cascade", "all"], default="all",
+    ap.add_argument("--only", choices=["prefill", "decode", "cascade", "pool", "all"],
+                    default="all",
                     help="restrict the timed step (for profiling runs)")
     ap.add_argument("--profile-kernel", choices=["prefill", "decode", "copy"],
                     help="launch only this kernel --reps times (rocprofv3 counter passes)")
@@ -343,6 +401,9 @@ def main():
 
     if args.only == "cascade":
         print(json.dumps({"cascade": bench_cascade(args.steps)}), flush=True)
+        return
+    if args.only == "pool":
+        print(json.dumps({"pool": bench_pool(args.steps)}), flush=True)
         return
 
     import torch
@@ -502,6 +563,8 @@ def main():
     if args.only == "all":
         print("bench: cascade prefill", file=sys.stderr, flush=True)
         line["cascade"] = bench_cascade(max(5, args.steps // 2))
+        print("bench: cache writes and page-table build", file=sys.stderr, flush=True)
+        line["pool"] = bench_pool(max(5, args.steps // 2))
     if not args.no_cpu_baseline and args.only == "all":
         print("bench: cpu baseline (oracle)", file=sys.stderr, flush=True)
         line["cpu_baseline"] = cpu_baseline(pre, args.cpu_budget)

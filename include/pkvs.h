@@ -247,6 +247,43 @@ int pkvs_merge_state(const void *v_a, const float *s_a, const void *v_b, const f
                      void *v_out, float *s_out, int64_t num_tokens, int32_t num_heads,
                      int32_t head_dim, int32_t v_dtype, hipStream_t stream);
 
+/* Write the batch's new key/value rows into the paged cache ([FIB]
+ * forward_extend / forward_decode: token_to_kv_pool.set_kv_buffer with the
+ * batch's cache locations, before the paged attention reads them).
+ *  k_new, v_new  [num_tokens, num_kv_heads, head_dim] in dtype, 16-byte aligned
+ *  loc_d         [num_tokens] int64 (device): the cache slot of each row,
+ *                slot = page * page_size + position in the page
+ *  k_cache, v_cache  the cache viewed as [num_slots, num_kv_heads, head_dim]
+ *                (num_slots = num_pages * page_size), 16-byte aligned
+ *  status_d      nullable device int32: the kernel adds the number of rows
+ *                whose slot lies outside [0, num_slots) (they are not written)
+ * Slots must be distinct (two rows to one slot leave either).  One launch on
+ * `stream`, no allocation.  Errors: INVALID_ARG (shape, null or misaligned
+ * pointer), UNSUPPORTED (dtype, a row not a multiple of 16 bytes), HIP. */
+int pkvs_append_kv(const void *k_new, const void *v_new, const int64_t *loc_d,
+                   int64_t num_tokens, void *k_cache, void *v_cache, int64_t num_slots,
+                   int32_t num_kv_heads, int32_t head_dim, int32_t dtype, int32_t *status_d,
+                   hipStream_t stream);
+
+/* Build the page table on the device ([FIB] call_begin_forward: kv_indptr is
+ * the running sum of the per-request lengths; create_flashinfer_kv_indices_triton
+ * gathers, for request b, entries start[b] .. start[b] + len[b] - 1 of row
+ * slot[b] of the request-to-token map into kv_indices from kv_indptr[b] on; a
+ * sliding-window wrapper passes start = the first key of the window).  With
+ * page_size 1 the map holds token slots, as on the pages; with larger pages
+ * it holds page ids and start / len count pages.  All arrays are device int32:
+ *  page_map_d   [map_rows, map_cols]        slot_d, len_d  [batch_size]
+ *  start_d      [batch_size] or NULL (0)    kv_indptr_d    [batch_size + 1] (out)
+ *  kv_indices_d [capacity] (out)
+ * A negative length counts as 0; an entry whose source lies outside the map
+ * is written as -1; entries at or past `capacity` are not written; each adds 1
+ * to *status_d when it is given.  Two launches on `stream` (the running sum,
+ * then the gather), no allocation.  Errors: INVALID_ARG, HIP. */
+int pkvs_build_kv_indices(const int32_t *page_map_d, int64_t map_rows, int64_t map_cols,
+                          const int32_t *slot_d, const int32_t *start_d, const int32_t *len_d,
+                          int32_t batch_size, int32_t *kv_indptr_d, int32_t *kv_indices_d,
+                          int64_t capacity, int32_t *status_d, hipStream_t stream);
+
 /* Facts about the plan (counts refer to the last plan() call). */
 int pkvs_plan_get_info(const pkvs_plan *plan, pkvs_plan_info *info);
 

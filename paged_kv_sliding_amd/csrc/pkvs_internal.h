@@ -74,6 +74,9 @@ constexpr int kGenericThreads = 256;
 constexpr int kDecodeBlock = 32;       // keys per decode step
 constexpr int kDecodeThreads = 64;     // one wave per workgroup
 constexpr int kMergeThreads = 64;
+constexpr int kAppendThreads = 256;    // cache writes: threads per workgroup (max)
+constexpr int kIndptrThreads = 1024;   // page-table build: the running-sum workgroup
+constexpr int kGatherThreads = 256;    // page-table build: threads per request
 
 struct PrefillArgs {
     const void *q, *k, *v;
@@ -116,6 +119,15 @@ hipError_t launch_decode_merge(const DecodeArgs &a, int head_dim, int dtype, int
 hipError_t launch_merge_state(const void *va, const float *sa, const void *vb, const float *sb,
                               void *vo, float *so, int64_t n, int32_t heads, int32_t head_dim,
                               int32_t dtype, int grid, hipStream_t s);
+
+// Cache writes and page-table build (pool.hip).
+hipError_t launch_append_kv(const void *k_new, const void *v_new, const int64_t *loc, int64_t n,
+                            int64_t row_bytes, void *k_cache, void *v_cache, int64_t num_slots,
+                            int32_t *status, int grid, hipStream_t s);
+hipError_t launch_build_kv_indices(const int32_t *map, int64_t map_rows, int64_t map_cols,
+                                   const int32_t *slot, const int32_t *start, const int32_t *len,
+                                   int32_t batch, int32_t *kv_indptr, int32_t *kv_indices,
+                                   int64_t capacity, int32_t *status, int grid, hipStream_t s);
 
 // Resident workgroups per CU of each kernel (occupancy query; 0 if unknown).
 int prefill_bf16_blocks_per_cu(int head_dim, int variant);

@@ -3,6 +3,7 @@
 #include <hip/hip_runtime.h>
 
 #include <algorithm>
+#include <cstdint>
 
 #include "pkvs_internal.h"
 #include "plan_state.h"
@@ -10,6 +11,16 @@
 using namespace pkvs;
 
 namespace {
+
+// compute units of the current device (256 when it cannot be queried)
+int device_cus()
+{
+    int dev = 0, cus = 256;
+    if (hipGetDevice(&dev) == hipSuccess)
+        (void)hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev);
+    (void)hipGetLastError();
+    return cus > 0 ? cus : 256;
+}
 
 int log2_exact(int x)
 {
@@ -213,14 +224,62 @@ int pkvs_merge_state(const void *v_a, const float *s_a, const void *v_b, const f
     if (num_tokens == 0) return PKVS_OK;
     if (!v_a || !s_a || !v_b || !s_b || !v_out || !s_out)
         return fail(PKVS_ERR_INVALID_ARG, "null pointer");
-    int dev = 0, cus = 256;
-    if (hipGetDevice(&dev) == hipSuccess)
-        (void)hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev);
     const int64_t units = num_tokens * num_heads;
-    const int grid = int(std::min<int64_t>(units, int64_t(cus) * 32));
+    const int grid = int(std::min<int64_t>(units, int64_t(device_cus()) * 32));
     hipError_t e = launch_merge_state(v_a, s_a, v_b, s_b, v_out, s_out, num_tokens, num_heads,
                                       head_dim, v_dtype, grid, stream);
     if (e != hipSuccess) return fail(PKVS_ERR_HIP, "merge_state launch: %s", hipGetErrorString(e));
+    return PKVS_OK;
+}
+
+int pkvs_append_kv(const void *k_new, const void *v_new, const int64_t *loc_d,
+                   int64_t num_tokens, void *k_cache, void *v_cache, int64_t num_slots,
+                   int32_t num_kv_heads, int32_t head_dim, int32_t dtype, int32_t *status_d,
+                   hipStream_t stream)
+{
+    clear_error();
+    if (num_tokens < 0 || num_slots < 0 || num_kv_heads <= 0 || head_dim <= 0)
+        return fail(PKVS_ERR_INVALID_ARG, "bad shape (%lld tokens, %lld slots, %d heads, %d "
+                    "dims)", (long long)num_tokens, (long long)num_slots, num_kv_heads,
+                    head_dim);
+    if (dtype != PKVS_BF16 && dtype != PKVS_FP32)
+        return fail(PKVS_ERR_UNSUPPORTED, "dtype %d not built (bf16, fp32)", dtype);
+    const int64_t row_bytes = int64_t(num_kv_heads) * head_dim * (dtype == PKVS_BF16 ? 2 : 4);
+    if (row_bytes % 16)
+        return fail(PKVS_ERR_UNSUPPORTED, "a cache row (num_kv_heads x head_dim elements) "
+                    "must be a multiple of 16 bytes, got %lld", (long long)row_bytes);
+    if (num_tokens == 0) return PKVS_OK;
+    if (!k_new || !v_new || !loc_d || !k_cache || !v_cache)
+        return fail(PKVS_ERR_INVALID_ARG, "null pointer");
+    for (const void *ptr : {k_new, v_new, static_cast<const void *>(k_cache),
+                            static_cast<const void *>(v_cache)})
+        if (reinterpret_cast<uintptr_t>(ptr) % 16)
+            return fail(PKVS_ERR_INVALID_ARG, "k/v rows and caches must be 16-byte aligned");
+    const int grid = int(std::min<int64_t>(num_tokens, int64_t(device_cus()) * 16));
+    hipError_t e = launch_append_kv(k_new, v_new, loc_d, num_tokens, row_bytes, k_cache, v_cache,
+                                    num_slots, status_d, grid, stream);
+    if (e != hipSuccess) return fail(PKVS_ERR_HIP, "append launch: %s", hipGetErrorString(e));
+    return PKVS_OK;
+}
+
+int pkvs_build_kv_indices(const int32_t *page_map_d, int64_t map_rows, int64_t map_cols,
+                          const int32_t *slot_d, const int32_t *start_d, const int32_t *len_d,
+                          int32_t batch_size, int32_t *kv_indptr_d, int32_t *kv_indices_d,
+                          int64_t capacity, int32_t *status_d, hipStream_t stream)
+{
+    clear_error();
+    if (batch_size < 0 || map_rows < 0 || map_cols < 0 || capacity < 0)
+        return fail(PKVS_ERR_INVALID_ARG, "negative batch, map shape or capacity");
+    if (!kv_indptr_d) return fail(PKVS_ERR_INVALID_ARG, "kv_indptr is null");
+    if (batch_size > 0 && (!page_map_d || !slot_d || !len_d || (capacity > 0 && !kv_indices_d)))
+        return fail(PKVS_ERR_INVALID_ARG, "null map, slot, length or kv_indices array");
+    const int grid = int(std::max<int64_t>(1, std::min<int64_t>(batch_size,
+                                                                int64_t(device_cus()) * 8)));
+    hipError_t e = launch_build_kv_indices(page_map_d, map_rows, map_cols, slot_d, start_d, len_d,
+                                           batch_size, kv_indptr_d, kv_indices_d, capacity,
+                                           status_d, grid, stream);
+    if (e != hipSuccess)
+        return fail(PKVS_ERR_HIP, "page-table build launch: %s", hipGetErrorString(e));
     return PKVS_OK;
 }
 

@@ -42,7 +42,7 @@ _DTYPES = {torch.bfloat16: PKVS_BF16, torch.float32: PKVS_FP32}
 EXPORTED = [
     "pkvs_plan_create", "pkvs_workspace_size", "pkvs_prefill_plan", "pkvs_prefill_run",
     "pkvs_decode_plan", "pkvs_decode_run", "pkvs_cascade_plan", "pkvs_cascade_run",
-    "pkvs_merge_state", "pkvs_plan_get_info",
+    "pkvs_merge_state", "pkvs_append_kv", "pkvs_build_kv_indices", "pkvs_plan_get_info",
     "pkvs_plan_copy_items", "pkvs_plan_destroy", "pkvs_strerror", "pkvs_last_error",
 ]
 
@@ -93,6 +93,8 @@ def _load() -> ctypes.CDLL:
         "pkvs_cascade_plan": (ctypes.c_int, [P, P, P, P, i32, P, sz, P, sz, P]),
         "pkvs_cascade_run": (ctypes.c_int, [P, P, P, P, P, P, i64, P, P, P, f32, i32, P]),
         "pkvs_merge_state": (ctypes.c_int, [P, P, P, P, P, P, i64, i32, i32, i32, P]),
+        "pkvs_append_kv": (ctypes.c_int, [P, P, P, i64, P, P, i64, i32, i32, i32, P, P]),
+        "pkvs_build_kv_indices": (ctypes.c_int, [P, i64, i64, P, P, P, i32, P, P, i64, P, P]),
         "pkvs_plan_get_info": (ctypes.c_int, [P, ctypes.POINTER(pkvs_plan_info)]),
         "pkvs_plan_copy_items": (ctypes.c_int, [P, P, i64, ctypes.POINTER(i64)]),
         "pkvs_plan_destroy": (None, [P]),
@@ -246,6 +248,51 @@ def pkvs_merge_state(v_a, s_a, v_b, s_b, v_out=None, s_out=None, stream=None):
                                  _ptr(s_out), n, h, d, _DTYPES[v_a.dtype], _stream(stream)),
            "pkvs_merge_state")
     return v_out, s_out
+
+
+def pkvs_append_kv(k_new, v_new, loc, k_cache, v_cache, status=None, stream=None) -> None:
+    """k_cache.view(-1, H_kv, D)[loc[i]] = k_new[i] (same for v) on the GPU;
+    ``loc`` int64 device slots; ``status`` optional int32 device counter."""
+    _need_device(k_new, v_new, loc, k_cache, v_cache, status)
+    n, h, d = k_new.shape
+    if v_new.shape != k_new.shape or k_cache.shape != v_cache.shape:
+        raise ValueError("pkvs_append_kv: k/v shapes differ")
+    if k_cache.dtype != k_new.dtype or v_cache.dtype != k_new.dtype or v_new.dtype != k_new.dtype:
+        raise ValueError("pkvs_append_kv: one dtype for new rows and caches")
+    if tuple(k_cache.shape[-2:]) != (h, d):
+        raise ValueError("pkvs_append_kv: cache rows must be [.., num_kv_heads, head_dim]")
+    if loc.dtype != torch.int64 or loc.numel() < n:
+        raise ValueError("pkvs_append_kv: loc must be int64 with one slot per row")
+    num_slots = k_cache.numel() // (h * d)
+    _check(_lib.pkvs_append_kv(_ptr(k_new), _ptr(v_new), _ptr(loc), n, _ptr(k_cache),
+                               _ptr(v_cache), num_slots, h, d, _DTYPES[k_new.dtype], _ptr(status),
+                               _stream(stream)), "pkvs_append_kv")
+
+
+def pkvs_build_kv_indices(page_map, slot, length, start=None, kv_indptr=None, kv_indices=None,
+                          capacity: Optional[int] = None, status=None, stream=None):
+    """Device page table from a request-to-page map (all int32 device
+    tensors); allocates kv_indptr / kv_indices when not given."""
+    _need_device(page_map, slot, length, start, kv_indptr, kv_indices, status)
+    for t in (page_map, slot, length, start):
+        if t is not None and t.dtype != torch.int32:
+            raise ValueError("pkvs_build_kv_indices: int32 arrays")
+    if page_map.dim() != 2:
+        raise ValueError("pkvs_build_kv_indices: the map is [rows, cols]")
+    B = slot.numel()
+    if kv_indptr is None:
+        kv_indptr = torch.empty(B + 1, dtype=torch.int32, device=slot.device)
+    if kv_indices is None:
+        kv_indices = torch.empty(max(capacity or 0, 1), dtype=torch.int32, device=slot.device)
+    if capacity is None:
+        capacity = kv_indices.numel()
+    if capacity > kv_indices.numel() or kv_indptr.numel() < B + 1:
+        raise ValueError("pkvs_build_kv_indices: output arrays too small")
+    _check(_lib.pkvs_build_kv_indices(_ptr(page_map), page_map.shape[0], page_map.shape[1],
+                                      _ptr(slot), _ptr(start), _ptr(length), B, _ptr(kv_indptr),
+                                      _ptr(kv_indices), capacity, _ptr(status), _stream(stream)),
+           "pkvs_build_kv_indices")
+    return kv_indptr, kv_indices
 
 
 def pkvs_plan_get_info(plan) -> pkvs_plan_info:

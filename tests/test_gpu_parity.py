@@ -629,3 +629,116 @@ def test_cascade_graph_replay_follows_replans():
             ro, rl = oracle_for(case)
             compare(want_o, want_l, ro, rl, tag="cascade graph")
 
+
+
+# ----------------------------------------------------------------- cache writes, page-table build
+# sglang flashinfer_backend.py: set_kv_buffer before the paged attention reads
+# the new keys; call_begin_forward builds kv_indptr / kv_indices on the device.
+# Integer and byte work: bit-exact against the oracle.
+
+
+@pytest.mark.parametrize("dtype,H,D", [(torch.bfloat16, 8, 128), (torch.bfloat16, 1, 256),
+                                       (torch.float32, 2, 64), (torch.bfloat16, 3, 64)])
+def test_append_kv_bit_exact(dtype, H, D):
+    g = torch.Generator().manual_seed(H * D)
+    pages, Psz = 40, 16
+    slots = pages * Psz
+    k_cache = torch.randn(pages, Psz, H, D, generator=g).to(dtype)
+    v_cache = torch.randn(pages, Psz, H, D, generator=g).to(dtype)
+    n = 300
+    loc = torch.randperm(slots, generator=g)[:n].to(torch.int64)
+    loc[7], loc[100], loc[299] = -1, slots, -5  # outside the pool: skipped and counted
+    k_new = torch.randn(n, H, D, generator=g).to(dtype)
+    v_new = torch.randn(n, H, D, generator=g).to(dtype)
+    rk, rv, skipped = oracle.append_kv(k_new, v_new, loc, k_cache, v_cache)
+    kc, vc = k_cache.to(DEV), v_cache.to(DEV)
+    status = torch.zeros(1, dtype=torch.int32, device=DEV)
+    log(f"append dtype={dtype} H={H} D={D} n={n}")
+    P.pkvs_append_kv(k_new.to(DEV), v_new.to(DEV), loc.to(DEV), kc, vc, status=status)
+    torch.cuda.synchronize()
+    assert torch.equal(kc.cpu().view(torch.uint8), rk.view(torch.uint8))
+    assert torch.equal(vc.cpu().view(torch.uint8), rv.view(torch.uint8))
+    assert int(status) == skipped == 3
+
+
+@pytest.mark.parametrize("batch", [0, 1, 37, 3000])
+@pytest.mark.parametrize("with_start", [False, True])
+def test_build_kv_indices_bit_exact(batch, with_start):
+    g = torch.Generator().manual_seed(batch + 7 * with_start)
+    rows, cols = 64, 300
+    page_map = torch.randint(0, 1 << 20, (rows, cols), generator=g, dtype=torch.int32)
+    slot = torch.randint(0, rows, (batch,), generator=g, dtype=torch.int32)
+    length = torch.randint(0, 40 if batch < 1000 else 6, (batch,), generator=g,
+                           dtype=torch.int32)
+    start = torch.randint(0, cols - 40, (batch,), generator=g, dtype=torch.int32)
+    if batch >= 37:
+        length[3] = -2          # negative: counts as 0
+        slot[5] = rows          # row outside the map: -1 entries
+        start[9] = cols - 2     # runs off the row end: -1 past it
+    if not with_start:
+        start = None
+    total = int(length.clamp(min=0).sum())
+    capacity = max(total - 3, 0) if batch >= 37 else total  # the last entries do not fit
+    indptr, idx, err = oracle.build_kv_indices(page_map, slot, length, start=start,
+                                               capacity=capacity)
+    out_idx = torch.full((max(capacity, 1),), 0x7FFFFFFF, dtype=torch.int32, device=DEV)
+    status = torch.zeros(1, dtype=torch.int32, device=DEV)
+    log(f"build batch={batch} start={with_start} capacity={capacity}")
+    kp, ki = P.pkvs_build_kv_indices(page_map.to(DEV), slot.to(DEV), length.to(DEV),
+                                     start=None if start is None else start.to(DEV),
+                                     kv_indices=out_idx, capacity=capacity, status=status)
+    torch.cuda.synchronize()
+    assert kp.cpu().tolist() == indptr.tolist()
+    assert ki.cpu()[:capacity].tolist() == idx.tolist()
+    assert int(status) == err
+
+
+@pytest.mark.parametrize("W", [-1, 127])
+def test_decode_step_appends_and_builds_its_page_table(W):
+    """One decode step the way a serving loop runs it: write each request's new
+    key/value into its slot, build the page table on the device from the
+    request-to-page map (from the first page of the window when W >= 0), plan
+    with the host lengths, decode; equal to the oracle on the full batch."""
+    kv = [1, 300, 77, 2000, 16, 129]
+    case = small([1] * len(kv), kv, H_q=16, H_kv=2, D=128, P_=16, W=W, seed=91,
+                 decode=True)
+    Psz, B = case.page_size, case.batch_size
+    kvp = case.kv_indptr.cpu().tolist()
+    pages = [case.kv_indices.cpu()[kvp[b]:kvp[b + 1]] for b in range(B)]
+    # the new tokens' rows, taken out of the cache and poisoned there
+    loc, k_new, v_new = [], [], []
+    flat_k = case.k_cache.view(-1, case.num_kv_heads, case.head_dim)
+    flat_v = case.v_cache.view(-1, case.num_kv_heads, case.head_dim)
+    for b in range(B):
+        j = kv[b] - 1
+        s = int(pages[b][j // Psz]) * Psz + j % Psz
+        loc.append(s)
+        k_new.append(flat_k[s].clone())
+        v_new.append(flat_v[s].clone())
+    kc, vc = case.k_cache.clone(), case.v_cache.clone()
+    kc.view(-1, case.num_kv_heads, case.head_dim)[torch.tensor(loc, device=DEV)] = float("nan")
+    vc.view(-1, case.num_kv_heads, case.head_dim)[torch.tensor(loc, device=DEV)] = float("nan")
+    P.pkvs_append_kv(torch.stack(k_new), torch.stack(v_new), torch.tensor(loc, device=DEV), kc, vc)
+    # request b's pages live in map row (b * 5) % 8, the window trims whole pages
+    rows = [(b * 5) % 8 for b in range(B)]
+    page_map = torch.full((8, 200), -7, dtype=torch.int32)
+    for b in range(B):
+        page_map[rows[b], :len(pages[b])] = pages[b]
+    first = [0 if W < 0 else max(0, kv[b] - 1 - W) // Psz for b in range(B)]
+    npg = [len(pages[b]) - first[b] for b in range(B)]
+    kp, ki = P.pkvs_build_kv_indices(
+        page_map.to(DEV), torch.tensor(rows, dtype=torch.int32, device=DEV),
+        torch.tensor(npg, dtype=torch.int32, device=DEV),
+        start=torch.tensor(first, dtype=torch.int32, device=DEV), capacity=sum(npg))
+    table_len = [kv[b] - first[b] * Psz for b in range(B)]
+    last = [t - (n - 1) * Psz for t, n in zip(table_len, npg)]
+    att = make_attention(case)
+    host_indptr = [0]
+    for n in npg:
+        host_indptr.append(host_indptr[-1] + n)
+    att.plan(kv_indptr=host_indptr, kv_last_page_len=last)
+    o, lse = att.run(case.q, kc, vc, ki, sm_scale=case.sm_scale, window_left=W)
+    torch.cuda.synchronize()
+    assert kp.cpu().tolist() == host_indptr
+    ro, rl = oracle_for(case)
+    compare(o, lse, ro, rl, tag=f"decode step with append + device page table W={W}")

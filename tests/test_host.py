@@ -398,3 +398,35 @@ def test_cascade_workspace_and_errors():
         P.PKVS_ERR_UNSUPPORTED
     P.pkvs_plan_destroy(h)
     P.pkvs_plan_destroy(hp)
+
+
+# ----------------------------------------------------------------- cache writes, page-table build
+
+
+def test_append_and_build_reject_bad_arguments():
+    """Argument checks run before any launch (so they hold without a GPU)."""
+    lib = P._lib
+    buf = torch.empty(64, dtype=torch.uint8)
+    p = ctypes.c_void_p(buf.data_ptr())
+    odd = ctypes.c_void_p(buf.data_ptr() + 2)
+    # append: negative count, unsupported dtype, a row that is not 16 bytes, nulls, misalignment
+    assert lib.pkvs_append_kv(p, p, p, -1, p, p, 4, 1, 64, P.PKVS_BF16, None, None) == \
+        P.PKVS_ERR_INVALID_ARG
+    assert lib.pkvs_append_kv(p, p, p, 1, p, p, 4, 1, 64, 7, None, None) == P.PKVS_ERR_UNSUPPORTED
+    assert lib.pkvs_append_kv(p, p, p, 1, p, p, 4, 1, 4, P.PKVS_BF16, None, None) == \
+        P.PKVS_ERR_UNSUPPORTED
+    assert lib.pkvs_append_kv(None, p, p, 1, p, p, 4, 1, 64, P.PKVS_BF16, None, None) == \
+        P.PKVS_ERR_INVALID_ARG
+    assert lib.pkvs_append_kv(odd, p, p, 1, p, p, 4, 1, 64, P.PKVS_BF16, None, None) == \
+        P.PKVS_ERR_INVALID_ARG
+    assert lib.pkvs_append_kv(None, None, None, 0, None, None, 0, 1, 64, P.PKVS_BF16, None,
+                              None) == P.PKVS_OK  # nothing to write
+    # build: negative sizes, missing outputs or inputs
+    assert lib.pkvs_build_kv_indices(p, 2, 2, p, None, p, -1, p, p, 4, None, None) == \
+        P.PKVS_ERR_INVALID_ARG
+    assert lib.pkvs_build_kv_indices(p, 2, 2, p, None, p, 1, None, p, 4, None, None) == \
+        P.PKVS_ERR_INVALID_ARG
+    assert lib.pkvs_build_kv_indices(None, 2, 2, p, None, p, 1, p, p, 4, None, None) == \
+        P.PKVS_ERR_INVALID_ARG
+    assert lib.pkvs_build_kv_indices(p, 2, 2, p, None, p, 1, p, None, 4, None, None) == \
+        P.PKVS_ERR_INVALID_ARG
