@@ -54,8 +54,8 @@ class OracleLib:
         i32, i64, f64 = ctypes.c_int32, ctypes.c_int64, ctypes.c_double
         lib.oracle_paged_attention.restype = ctypes.c_int
         lib.oracle_paged_attention.argtypes = [
-            i32, P, P, P, P, i32, i32, i32, i32, i32, i32, f64, i32, P, P, P, P, i64, i64, i64,
-            P, P,
+            i32, P, P, P, P, i32, i32, i32, i32, i32, i32, f64, f64, i32, P, P, P, P, i64, i64,
+            i64, P, P,
         ]
         lib.oracle_merge_state.restype = None
         lib.oracle_merge_state.argtypes = [i64, i32, i32, P, P, P, P, P, P]
@@ -100,7 +100,7 @@ def _i32(t) -> np.ndarray:
 
 def paged_attention(q, k_cache, v_cache, qo_indptr, kv_indptr, kv_indices, kv_last_page_len, *,
                     num_qo_heads: int, num_kv_heads: int, head_dim: int, page_size: int,
-                    causal: bool, window_left: int, sm_scale: float,
+                    causal: bool, window_left: int, sm_scale: float, soft_cap: float = 0.0,
                     rows: Optional[Sequence[int]] = None, key_lo: int = 0,
                     key_hi: int = np.iinfo(np.int64).max, impl: Optional[OracleLib] = None):
     """Reference (O, LSE) in float64.
@@ -132,7 +132,8 @@ def paged_attention(q, k_cache, v_cache, qo_indptr, kv_indptr, kv_indices, kv_la
         rows_a, rp, nr = None, None, 0
     rc = lib.oracle_paged_attention(
         batch, _ptr(qo), _ptr(kvp), _ptr(kvi), _ptr(last), page_size, num_qo_heads,
-        num_kv_heads, head_dim, int(bool(causal)), window_left, float(sm_scale), qd, _ptr(qa),
+        num_kv_heads, head_dim, int(bool(causal)), window_left, float(sm_scale),
+        float(soft_cap), qd, _ptr(qa),
         _ptr(ka), _ptr(va), rp, nr, int(key_lo), int(key_hi), _ptr(o), _ptr(lse))
     if rc != 0:
         raise ValueError(f"oracle_paged_attention: malformed layout (rc={rc})")
@@ -146,7 +147,7 @@ def case_attention(case, rows=None, window_left: Optional[int] = None, **kw):
         case.kv_last_page_len, num_qo_heads=case.num_qo_heads, num_kv_heads=case.num_kv_heads,
         head_dim=case.head_dim, page_size=case.page_size, causal=case.causal,
         window_left=case.window_left if window_left is None else window_left,
-        sm_scale=case.sm_scale, rows=rows, **kw)
+        sm_scale=case.sm_scale, soft_cap=case.logits_soft_cap, rows=rows, **kw)
 
 
 def merge_state(v_a, s_a, v_b, s_b, impl: Optional[OracleLib] = None):

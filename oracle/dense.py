@@ -43,8 +43,11 @@ def visibility(qo_len: int, kv_len: int, causal: bool, window_left: int) -> np.n
 
 
 def attention(case, window_left=None):
-    """(O [nnz_qo,H_q,D], LSE [nnz_qo,H_q]) for a ``synth.Case``, float64."""
+    """(O [nnz_qo,H_q,D], LSE [nnz_qo,H_q]) for a ``synth.Case``, float64.
+    A positive ``case.logits_soft_cap`` c replaces each scaled logit x by
+    c * tanh(x / c) (numpy's tanh)."""
     W = case.window_left if window_left is None else window_left
+    cap = case.logits_soft_cap
     q = _to_f64(case.q)
     kc = _to_f64(case.k_cache)
     vc = _to_f64(case.v_cache)
@@ -62,6 +65,8 @@ def attention(case, window_left=None):
         vis = visibility(len(qb), len(K), case.causal, W)
         for h in range(case.num_qo_heads):
             logits = case.sm_scale * (qb[:, h, :] @ K[:, h // G, :].T)  # [qo, kv]
+            if cap > 0:
+                logits = cap * np.tanh(logits / cap)
             for i in range(len(qb)):
                 if not vis[i].any():
                     continue

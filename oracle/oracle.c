@@ -102,6 +102,10 @@ static int key_visible(int64_t j, int64_t p, int32_t causal, int32_t window_left
  *  contiguous groups).
  *
  *  s_j   = sm_scale * sum_d q[d] * k_j[d]                for visible j
+ *  s_j  <- soft_cap * tanh(s_j / soft_cap)   when soft_cap > 0 (the logits
+ *          soft cap [FIB] forward_extend / forward_decode pass to the
+ *          wrappers as logits_soft_cap; the pages do not print its formula,
+ *          this is the tanh cap of the scaled logits)
  *  m     = max_j s_j,  l = sum_j exp(s_j - m)
  *  o     = sum_j exp(s_j - m) / l * v_j
  *  lse   = m + ln(l)          (natural log; the log-sum-exp of the logits)
@@ -119,7 +123,7 @@ int oracle_paged_attention(int32_t batch, const int32_t *qo_indptr, const int32_
                            const int32_t *kv_indices, const int32_t *kv_last_page_len,
                            int32_t page_size, int32_t num_qo_heads, int32_t num_kv_heads,
                            int32_t head_dim, int32_t causal, int32_t window_left,
-                           double sm_scale, int32_t in_dtype, const void *q,
+                           double sm_scale, double soft_cap, int32_t in_dtype, const void *q,
                            const void *k_cache, const void *v_cache, const int64_t *rows,
                            int64_t n_rows, int64_t key_lo, int64_t key_hi, double *o,
                            double *lse)
@@ -175,6 +179,8 @@ int oracle_paged_attention(int32_t batch, const int32_t *qo_indptr, const int32_
                 for (int32_t d = 0; d < head_dim; ++d)
                     dot += load_elem(q, in_dtype, qoff + d) * load_elem(k_cache, in_dtype, koff + d);
                 s[j] = sm_scale * dot;
+                if (soft_cap > 0.0)
+                    s[j] = soft_cap * tanh(s[j] / soft_cap);
                 if (s[j] > m)
                     m = s[j];
             }

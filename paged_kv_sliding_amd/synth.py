@@ -67,6 +67,7 @@ class Case:
     kv_last_page_len: torch.Tensor
     fixed_split_size: int = -1
     is_decode: bool = False
+    logits_soft_cap: float = 0.0  # 0: no cap
 
     @property
     def batch_size(self) -> int:
@@ -146,6 +147,7 @@ def case_from_lengths(
     fixed_split_size: int = -1,
     value_gen: Optional[torch.Generator] = None,
     perm_gen: Optional[torch.Generator] = None,
+    logits_soft_cap: float = 0.0,
 ) -> Case:
     """Build a paged batch for explicit lengths.
 
@@ -219,6 +221,7 @@ def case_from_lengths(
         kv_last_page_len=last.to(device),
         fixed_split_size=fixed_split_size,
         is_decode=is_decode,
+        logits_soft_cap=float(logits_soft_cap),
     )
 
 

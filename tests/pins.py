@@ -34,10 +34,11 @@ GOLDEN = os.path.join(os.path.dirname(os.path.abspath(__file__)), "golden")
 
 
 def small_case(qo_lens, kv_lens, *, H_q=2, H_kv=1, D=16, P=4, W=4, seed=0,
-               dtype=torch.float32, spare=2, causal=True, sm_scale=None):
+               dtype=torch.float32, spare=2, causal=True, sm_scale=None, soft_cap=0.0):
     return case_from_lengths("pin", qo_lens, kv_lens, num_qo_heads=H_q, num_kv_heads=H_kv,
                              head_dim=D, page_size=P, dtype=dtype, window_left=W, seed=seed,
-                             causal=causal, spare_pages=spare, sm_scale=sm_scale)
+                             causal=causal, spare_pages=spare, sm_scale=sm_scale,
+                             logits_soft_cap=soft_cap)
 
 
 def run(case, impl, **kw):
@@ -377,6 +378,49 @@ def check_merge_algebra(impl=None):
     assert close(v, (va + vb) / 2) and close(s, sa + math.log(2.0))
 
 
+# --------------------------------------------------------------------------- logits soft cap
+
+
+def check_soft_cap_brute_force(impl=None):
+    """With a cap c each scaled logit x becomes c * tanh(x / c): the oracle
+    equals the dense NumPy version (numpy's tanh) on tiny inputs."""
+    for cap in (0.7, 3.0, 30.0):
+        for W in (-1, 0, 3):
+            case = small_case([3, 6], [8, 6], W=W, P=2, H_q=4, H_kv=2, seed=int(cap * 10) + W,
+                              sm_scale=0.9, soft_cap=cap)
+            o, lse = run(case, impl)
+            ro, rl = dense.attention(case)
+            assert close(o, ro) and close(lse, rl), (cap, W)
+
+
+def check_soft_cap_saturation(impl=None):
+    """Keys all equal to u and queries = 1000 u: every logit is huge, the cap
+    saturates at c, so LSE = c + ln n and O is the plain mean of the visible
+    values."""
+    cap = 5.0
+    case = small_case([4], [9], W=3, P=4, H_q=1, H_kv=1, D=8, seed=3, soft_cap=cap)
+    u = torch.linspace(0.5, 1.5, 8)
+    case.k_cache[:] = u
+    case.q[:] = 1000.0 * u
+    o, lse = run(case, impl)
+    _, V = dense_kv(case, 0)
+    for i in range(4):
+        lo, hi = visible_range(5 + i, 3)
+        assert close(lse[i, 0], cap + math.log(hi - lo + 1)), (i, lse[i, 0])
+        assert close(o[i, 0], V[lo:hi + 1, 0].mean(axis=0)), i
+
+
+def check_soft_cap_large_is_no_cap(impl=None):
+    """c * tanh(x / c) -> x as c grows: a cap of 1e6 changes nothing beyond
+    1e-9."""
+    case = small_case([5], [12], W=6, P=4, H_q=2, H_kv=1, seed=9, soft_cap=1e6)
+    o, lse = run(case, impl)
+    case.logits_soft_cap = 0.0
+    o0, l0 = run(case, impl)
+    assert close(o, o0, tol=1e-9) and close(lse, l0, tol=1e-9)
+    assert not np.array_equal(lse, l0)  # the cap is applied at all
+
+
 # --------------------------------------------------------------------------- cache writes, page tables
 
 
@@ -499,6 +543,9 @@ ALL_CHECKS = [
     check_paging_invariance,
     check_empty_sets,
     check_decode_trim,
+    check_soft_cap_brute_force,
+    check_soft_cap_saturation,
+    check_soft_cap_large_is_no_cap,
     check_append_round_trip,
     check_append_matches_scatter,
     check_build_indices_golden,

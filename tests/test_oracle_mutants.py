@@ -39,6 +39,10 @@ MUTANTS = {
     "merge_shift_dropped": ("const double s = M + log(exp(a - M) + exp(b - M));",
                             "const double s = log(exp(a - M) + exp(b - M));"),
     "merge_empty_nonzero": ("s_out[i] = -INFINITY;", "s_out[i] = 0.0;"),
+    "cap_of_unscaled_logit": ("s[j] = soft_cap * tanh(s[j] / soft_cap);",
+                              "s[j] = soft_cap * tanh(dot / soft_cap);"),
+    "cap_factor_dropped": ("s[j] = soft_cap * tanh(s[j] / soft_cap);",
+                           "s[j] = tanh(s[j] / soft_cap);"),
     "append_values_from_keys": ("memcpy(v_cache + s * row_bytes, v_new + i * row_bytes",
                                 "memcpy(v_cache + s * row_bytes, k_new + i * row_bytes"),
     "append_ignores_loc": ("const int64_t s = loc[i];", "const int64_t s = i;"),
