@@ -105,6 +105,11 @@ typedef enum pkvs_kind { PKVS_PREFILL = 0, PKVS_DECODE = 1, PKVS_CASCADE = 2 } p
  *  qo_capacity      prefill, cascade: largest total number of query tokens
  *  kv_capacity      largest kv_len of one request (cascade: the most cached
  *                   keys one request's page table may hold)
+ *  logits_soft_cap  0 (off) or c > 0: every logit x = sm_scale * q.k becomes
+ *                   c * tanh(x / c) before the softmax and the LSE ([FIB]
+ *                   forward_extend / forward_decode pass logits_soft_cap to
+ *                   the wrappers; the tanh cap of the scaled logit is the
+ *                   reading taken)
  * The launch grid and the workspaces are sized from these capacities and the
  * device alone, never from one batch ([PR234] 2; [FIB]
  * _full_cg_prefill_workspace_bytes). */
@@ -123,6 +128,7 @@ typedef struct pkvs_desc {
     int32_t prefill_variant;
     int64_t qo_capacity;
     int64_t kv_capacity;
+    float logits_soft_cap;
 } pkvs_desc;
 
 /* Read-only facts about a plan (for callers, tests and profilers). */

@@ -176,7 +176,7 @@ struct DecodeState {
 template <int D>
 __device__ __forceinline__ void decode_compute(const DecodeBuf<D> &buf, DecodeState<D> &st,
                                                const bf16x8 (&qf)[D / 32], int blk, int lo,
-                                               int t1, float scale_log2, int lane)
+                                               int t1, float scale_log2, float cap_a, int lane)
 {
     constexpr int KS = DecodeBuf<D>::KS, NV = DecodeBuf<D>::NV;
     const int g = lane >> 4;
@@ -192,8 +192,13 @@ __device__ __forceinline__ void decode_compute(const DecodeBuf<D> &buf, DecodeSt
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
         const int ta = blk + 4 * g + i, tb = blk + 16 + 4 * g + i;
-        x[i] = (ta >= lo && ta < t1) ? s0[i] * scale_log2 : kNegInf;
-        x[4 + i] = (tb >= lo && tb < t1) ? s1[i] * scale_log2 : kNegInf;
+        float ra = s0[i], rb = s1[i];
+        if (cap_a != 0.f) {
+            ra = soft_cap_unit(ra, cap_a);
+            rb = soft_cap_unit(rb, cap_a);
+        }
+        x[i] = (ta >= lo && ta < t1) ? ra * scale_log2 : kNegInf;
+        x[4 + i] = (tb >= lo && tb < t1) ? rb * scale_log2 : kNegInf;
         mx = fmaxf(mx, fmaxf(x[i], x[4 + i]));
     }
     // across the four lane groups: row swaps (VALU), no LDS round trip
@@ -293,7 +298,7 @@ __global__ __launch_bounds__(kDecodeThreads) void decode_bf16_kernel(DecodeArgs 
                 for (int s = 0; s < NS; ++s) {
                     decode_load<D>(buf[(s + NS - 1) % NS], a, pw, blk + kDecodeBlock * (NS - 1),
                                    t1, hk, lane);
-                    decode_compute<D>(buf[s], st, qf, blk, lo, t1, a.scale_log2, lane);
+                    decode_compute<D>(buf[s], st, qf, blk, lo, t1, a.scale_log2, a.cap_a, lane);
                     blk += kDecodeBlock;
                     if (blk >= t1) {
                         done = true;

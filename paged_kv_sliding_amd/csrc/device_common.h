@@ -20,6 +20,15 @@ constexpr float kLn2 = 0.69314718055994530942f;
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 __device__ __forceinline__ float fast_log2(float x) { return __builtin_amdgcn_logf(x); }
 
+// Logits soft cap: with a = 2 log2(e) * sm_scale / cap, the capped logit
+// cap * tanh(sm_scale * s / cap) is cap * soft_cap_unit(s, a), from
+// tanh(y) = 1 - 2 / (e^(2y) + 1) (limits exactly -1 and +1 for large |y|).
+__device__ __forceinline__ float soft_cap_unit(float s, float a)
+{
+    const float e = fast_exp2(s * a);
+    return 1.f - 2.f * __builtin_amdgcn_rcpf(e + 1.f);
+}
+
 __device__ __forceinline__ float bf16_bits_to_float(uint16_t b)
 {
     return __uint_as_float(uint32_t(b) << 16);

@@ -85,7 +85,8 @@ struct PrefillArgs {
     float *lse;
     const int32_t *ws;  // int workspace (header + items)
     int64_t num_pages;
-    float scale_log2;   // sm_scale * log2(e)
+    float scale_log2;   // sm_scale * log2(e), or cap * log2(e) with a soft cap
+    float cap_a;        // soft cap: 2 log2(e) sm_scale / cap (soft_cap_unit), 0 = none
     int32_t num_qo_heads, num_kv_heads, log2_group, page_size, log2_page;
     int32_t page_rows;  // cache rows one page-table step spans: page_size, or 1 (ragged)
     int32_t window_left, causal;
@@ -105,7 +106,8 @@ struct DecodeArgs {
     float *part_o;    // [slots, group, head_dim]
     float *part_lse;  // [slots, group]
     int64_t num_pages;
-    float scale_log2;
+    float scale_log2;   // as PrefillArgs
+    float cap_a;
     int32_t num_qo_heads, num_kv_heads, log2_group, page_size, log2_page;
 };
 

@@ -123,6 +123,13 @@ static int validate_desc(const pkvs_desc *d)
     if (d->dtype == PKVS_BF16 && (!is_pow2(group) || group > 16))
         return fail(PKVS_ERR_UNSUPPORTED, "bf16 path needs a power-of-two group <= 16, got %d",
                     group);
+    // (bit test: this file is built with -fno-honor-nans, which folds NaN
+    // comparisons away)
+    uint32_t cap_bits;
+    std::memcpy(&cap_bits, &d->logits_soft_cap, sizeof cap_bits);
+    if ((cap_bits & 0x7f800000u) == 0x7f800000u || ((cap_bits >> 31) && (cap_bits << 1)))
+        return fail(PKVS_ERR_INVALID_ARG, "logits_soft_cap %g: must be 0 (off) or a positive "
+                    "finite cap", double(d->logits_soft_cap));
     if (d->window_left < -1)
         return fail(PKVS_ERR_INVALID_ARG, "window_left %d: must be -1 (off) or >= 0",
                     d->window_left);

@@ -319,6 +319,7 @@ __global__ __launch_bounds__(NW * 64) void prefill_bf16_kernel(PrefillArgs a)
     const uint16_t *Q = static_cast<const uint16_t *>(a.q);
     const int W = a.window_left;
     const float c = a.scale_log2;
+    const float cap_a = a.cap_a;
 
     // transposing-read coordinates of this lane (see PrefillBuf)
     const int tr_key = 4 * hw + ((lane & 15) >> 2);             // + 16*kk (+8)
@@ -507,6 +508,10 @@ __global__ __launch_bounds__(NW * 64) void prefill_bf16_kernel(PrefillArgs a)
 
             // accumulator entry i holds key k0 + 8*(i/4) + 4*hw + i%4 of this row
             f32x16 s = s_in;
+            if (cap_a != 0.f) {
+#pragma unroll
+                for (int i = 0; i < 16; ++i) s[i] = soft_cap_unit(s[i], cap_a);
+            }
             const bool interior = k0 + KT <= kv_len && (!a.causal || k0 + KT - 1 <= pos0) &&
                                   (W < 0 || k0 >= pos_last - W);
             if (!interior) mask_tile(s, k0, hw, p_row, kv_len, a.causal, W);
@@ -777,6 +782,12 @@ __global__ __launch_bounds__(256) void prefill_wide_kernel(PrefillArgs a)
             // the end of the keys (entry i: key k0 + 8*(i/4) + 4*hw + i%4)
             const bool interior = k0 + KT <= kv_len && (!a.causal || k0 + KT - 1 <= pos0) &&
                                   (W < 0 || k0 >= pos_last - W);
+            if (a.cap_a != 0.f) {
+#pragma unroll
+                for (int n = 0; n < 2; ++n)
+#pragma unroll
+                    for (int i = 0; i < 16; ++i) s_cur[n][i] = soft_cap_unit(s_cur[n][i], a.cap_a);
+            }
             if (!interior) {
 #pragma unroll
                 for (int n = 0; n < 2; ++n) mask_tile(s_cur[n], k0, hw, p_row[n], kv_len, a.causal, W);
@@ -972,7 +983,7 @@ __global__ __launch_bounds__(kGenericThreads) void attention_fp32_kernel(Prefill
                 float dot = 0.f;
                 for (int e = 0; e < E; ++e) dot += q[e] * K[off + lane + 64 * e];
                 for (int s = 32; s >= 1; s >>= 1) dot += __shfl_xor(dot, s);
-                const float x = dot * a.scale_log2;
+                const float x = (a.cap_a != 0.f ? soft_cap_unit(dot, a.cap_a) : dot) * a.scale_log2;
                 const float m_new = fmaxf(m, x);
                 const float alpha = fast_exp2(m - m_new);
                 const float pj = fast_exp2(x - m_new);

@@ -22,6 +22,21 @@ int device_cus()
     return cus > 0 ? cus : 256;
 }
 
+// Base-2 logit scale and soft-cap factor (see soft_cap_unit): without a cap
+// the kernels take exp2(s * sm_scale * log2 e); with a cap c they take
+// exp2(c * log2 e * tanh(sm_scale * s / c)).
+void logit_scales(const pkvs_desc &d, float sm_scale, float *scale_log2, float *cap_a)
+{
+    constexpr float kLog2e = 1.44269504088896340736f;
+    if (d.logits_soft_cap > 0.f) {
+        *scale_log2 = d.logits_soft_cap * kLog2e;
+        *cap_a = 2.f * kLog2e * sm_scale / d.logits_soft_cap;
+    } else {
+        *scale_log2 = sm_scale * kLog2e;
+        *cap_a = 0.f;
+    }
+}
+
 int log2_exact(int x)
 {
     int r = 0;
@@ -75,7 +90,7 @@ hipError_t launch_prefill_pass(const pkvs_plan *p, const void *q, const void *k,
     a.lse = lse;
     a.ws = ws + p->lead_words;
     a.num_pages = p->ragged ? p->desc.qo_capacity : num_pages;
-    a.scale_log2 = sm_scale * 1.44269504088896340736f;
+    logit_scales(p->desc, sm_scale, &a.scale_log2, &a.cap_a);
     a.num_qo_heads = p->desc.num_qo_heads;
     a.num_kv_heads = p->desc.num_kv_heads;
     a.log2_group = log2_exact(p->desc.num_qo_heads / p->desc.num_kv_heads);
@@ -154,7 +169,8 @@ int pkvs_decode_run(const pkvs_plan *p, const void *q, const void *k_cache, cons
     // from the workspace, so a captured graph replays correctly after any
     // later plan of the same capacities)
     const int log2g = log2_exact(p->desc.num_qo_heads / p->desc.num_kv_heads);
-    const float scale_log2 = sm_scale * 1.44269504088896340736f;
+    float scale_log2, cap_a;
+    logit_scales(p->desc, sm_scale, &scale_log2, &cap_a);
     hipError_t e;
     if (p->desc.dtype == PKVS_FP32) {
         PrefillArgs a{};
@@ -167,6 +183,7 @@ int pkvs_decode_run(const pkvs_plan *p, const void *q, const void *k_cache, cons
         a.ws = static_cast<const int32_t *>(p->int_ws);
         a.num_pages = num_pages;
         a.scale_log2 = scale_log2;
+        a.cap_a = cap_a;
         a.num_qo_heads = p->desc.num_qo_heads;
         a.num_kv_heads = p->desc.num_kv_heads;
         a.log2_group = log2g;
@@ -192,6 +209,7 @@ int pkvs_decode_run(const pkvs_plan *p, const void *q, const void *k_cache, cons
     a.part_lse = a.part_o ? a.part_o + p->slots_cap * group * p->desc.head_dim : nullptr;
     a.num_pages = num_pages;
     a.scale_log2 = scale_log2;
+    a.cap_a = cap_a;
     a.num_qo_heads = p->desc.num_qo_heads;
     a.num_kv_heads = p->desc.num_kv_heads;
     a.log2_group = log2g;

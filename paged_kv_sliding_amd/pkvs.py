@@ -55,7 +55,7 @@ class pkvs_desc(ctypes.Structure):
         ("window_left", ctypes.c_int32), ("fixed_split_size", ctypes.c_int32),
         ("disable_split_kv", ctypes.c_int32), ("batch_capacity", ctypes.c_int32),
         ("prefill_variant", ctypes.c_int32), ("qo_capacity", ctypes.c_int64),
-        ("kv_capacity", ctypes.c_int64),
+        ("kv_capacity", ctypes.c_int64), ("logits_soft_cap", ctypes.c_float),
     ]
 
 
@@ -153,10 +153,11 @@ def make_desc(kind: int, *, num_qo_heads: int, num_kv_heads: int, head_dim: int,
               dtype: torch.dtype, window_left: int, causal: bool = True,
               fixed_split_size: int = -1, disable_split_kv: bool = False,
               batch_capacity: int, qo_capacity: int = 0, kv_capacity: int,
-              prefill_variant: int = 0) -> pkvs_desc:
+              prefill_variant: int = 0, logits_soft_cap: float = 0.0) -> pkvs_desc:
     return pkvs_desc(kind, num_qo_heads, num_kv_heads, head_dim, page_size, _DTYPES[dtype],
                      int(bool(causal)), window_left, fixed_split_size, int(bool(disable_split_kv)),
-                     batch_capacity, prefill_variant, qo_capacity, kv_capacity)
+                     batch_capacity, prefill_variant, qo_capacity, kv_capacity,
+                     float(logits_soft_cap))
 
 
 def pkvs_plan_create(desc: pkvs_desc) -> ctypes.c_void_p:

@@ -30,7 +30,7 @@ def make_attention(case: Case, window_left=None, fixed_split_size=None, disable_
         batch_capacity=batch_capacity or max(case.batch_size, 1),
         qo_capacity=qo_capacity or max(int(case.qo_indptr[-1]), 1),
         kv_capacity=kv_capacity or max(max(case.kv_lens, default=1), 1),
-        prefill_variant=prefill_variant)
+        prefill_variant=prefill_variant, logits_soft_cap=case.logits_soft_cap)
 
 
 def gpu_run(case: Case, window_left=None, att=None, return_lse=True, **kw):

@@ -19,11 +19,11 @@ DEV = "cuda"
 
 
 def small(qo, kv, *, H_q=4, H_kv=1, D=128, P_=16, W=31, seed=0, dtype=torch.bfloat16,
-          decode=False, split=-1, spare=3):
+          decode=False, split=-1, spare=3, cap=0.0):
     return case_from_lengths("small", qo, kv, num_qo_heads=H_q, num_kv_heads=H_kv, head_dim=D,
                              page_size=P_, dtype=dtype, window_left=W, seed=seed,
                              spare_pages=spare, device=DEV, is_decode=decode,
-                             fixed_split_size=split)
+                             fixed_split_size=split, logits_soft_cap=cap)
 
 
 # ----------------------------------------------------------------- the five workloads
@@ -476,7 +476,7 @@ def make_cascade(case, window_left=None, prefill_variant=0, qo_capacity=None,
         batch_capacity=batch_capacity or max(case.batch_size, 1),
         qo_capacity=qo_capacity or max(int(case.qo_indptr[-1]), 1),
         kv_capacity=kv_capacity or max(max(prefix, default=1), 1),
-        prefill_variant=prefill_variant)
+        prefill_variant=prefill_variant, logits_soft_cap=case.logits_soft_cap)
 
 
 def cascade_run(case, trim=False, att=None, return_lse=True, **kw):
@@ -742,3 +742,61 @@ def test_decode_step_appends_and_builds_its_page_table(W):
     assert kp.cpu().tolist() == host_indptr
     ro, rl = oracle_for(case)
     compare(o, lse, ro, rl, tag=f"decode step with append + device page table W={W}")
+
+
+# ----------------------------------------------------------------- logits soft cap
+# sglang flashinfer_backend.py forward_extend / forward_decode pass
+# logits_soft_cap to the wrappers; every logit x becomes c * tanh(x / c).
+# sm_scale 0.3 on N(0,1) data puts many logits near and past the cap.
+
+
+@pytest.mark.parametrize("variant", [1, 2, 3, 4])
+@pytest.mark.parametrize("cap", [2.0, 30.0])
+@pytest.mark.parametrize("W", [-1, 33])
+def test_soft_cap_prefill_variants(variant, cap, W):
+    qo = [1, 70, 33, 129, 300]
+    kv = [1, 70, 300, 129, 301]
+    case = small(qo, kv, H_q=8, H_kv=2, D=128, P_=16, W=W, seed=int(cap) * 10 + variant, cap=cap)
+    case.sm_scale = 0.3
+    att = make_attention(case, prefill_variant=variant)
+    o, lse = gpu_run(case, att=att)
+    ro, rl = oracle_for(case)
+    compare(o, lse, ro, rl, tag=f"soft cap {cap} variant={variant} W={W}")
+    if cap == 2.0:  # the cap matters: without it the LSE differs
+        _, rl0 = oracle.paged_attention(
+            case.q, case.k_cache, case.v_cache, case.qo_indptr, case.kv_indptr, case.kv_indices,
+            case.kv_last_page_len, num_qo_heads=8, num_kv_heads=2, head_dim=128, page_size=16,
+            causal=True, window_left=W, sm_scale=0.3)
+        assert np.abs(rl0 - rl).max() > 0.1
+
+
+@pytest.mark.parametrize("D,G", [(64, 4), (128, 8), (256, 2)])
+@pytest.mark.parametrize("split", [-1, 64])
+def test_soft_cap_decode(D, G, split):
+    kv = [1, 300, 77, 2000, 64, 900]
+    case = small([1] * len(kv), kv, H_q=2 * G, H_kv=2, D=D, P_=16, W=127, seed=D + G + split,
+                 decode=True, split=split, cap=5.0)
+    case.sm_scale = 0.3
+    o, lse = gpu_run(case)
+    ro, rl = oracle_for(case)
+    compare(o, lse, ro, rl, tag=f"soft cap decode D={D} G={G} split={split}")
+
+
+def test_soft_cap_fp32_and_cascade():
+    case = small([6, 8, 12], [6, 10, 12], H_q=2, H_kv=1, D=64, P_=4, W=4, seed=3,
+                 dtype=torch.float32, cap=1.5)
+    case.sm_scale = 0.3
+    o, lse = gpu_run(case)
+    ro, rl = oracle_for(case)
+    compare(o, lse, ro, rl, tag="soft cap fp32 prefill")
+    dec = small([1] * 3, [9, 40, 100], H_q=2, H_kv=1, D=64, P_=4, W=20, seed=4,
+                dtype=torch.float32, decode=True, cap=1.5)
+    dec.sm_scale = 0.3
+    o, lse = gpu_run(dec)
+    ro, rl = oracle_for(dec)
+    compare(o, lse, ro, rl, tag="soft cap fp32 decode")
+    cas = small([40, 130, 7], [90, 130, 500], H_q=8, H_kv=2, D=128, P_=16, W=63, seed=5, cap=4.0)
+    cas.sm_scale = 0.3
+    (o, lse), _ = cascade_run(cas, trim=True)
+    ro, rl = oracle_for(cas)
+    compare(o, lse, ro, rl, tag="soft cap cascade")

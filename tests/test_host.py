@@ -430,3 +430,9 @@ def test_append_and_build_reject_bad_arguments():
         P.PKVS_ERR_INVALID_ARG
     assert lib.pkvs_build_kv_indices(p, 2, 2, p, None, p, 1, p, None, 4, None, None) == \
         P.PKVS_ERR_INVALID_ARG
+
+
+@pytest.mark.parametrize("cap", [-1.0, float("nan"), float("inf")])
+def test_soft_cap_must_be_zero_or_positive_finite(cap):
+    assert err_code(lambda: P.pkvs_plan_create(desc(logits_soft_cap=cap))) == \
+        P.PKVS_ERR_INVALID_ARG
