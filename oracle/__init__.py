@@ -25,6 +25,7 @@ _lib = None
 
 BF16 = 0
 FP32 = 1
+FP16 = 2
 
 
 def compile_source(src: str, out: str) -> str:
@@ -59,6 +60,8 @@ class OracleLib:
         ]
         lib.oracle_merge_state.restype = None
         lib.oracle_merge_state.argtypes = [i64, i32, i32, P, P, P, P, P, P]
+        lib.oracle_widen.restype = None
+        lib.oracle_widen.argtypes = [i32, P, i64, P]
         lib.oracle_append_kv.restype = i64
         lib.oracle_append_kv.argtypes = [i64, P, i64, P, P, i64, P, P]
         lib.oracle_build_kv_indices.restype = i64
@@ -85,6 +88,8 @@ def _as_stored(t) -> tuple:
     t = t.detach().cpu().contiguous()
     if t.dtype == torch.bfloat16:
         return t.view(torch.int16).numpy(), BF16
+    if t.dtype == torch.float16:
+        return t.view(torch.int16).numpy(), FP16
     if t.dtype == torch.float32:
         return t.numpy(), FP32
     raise TypeError(f"oracle: unsupported input dtype {t.dtype}")
@@ -217,4 +222,14 @@ def build_kv_indices(page_map, slot, length, start=None, capacity=None,
                                       _ptr(st) if st is not None else None, _ptr(ln),
                                       _ptr(indptr), _ptr(idx), capacity)
     return indptr, idx[:capacity], int(err)
+
+
+def widen(t, impl: Optional[OracleLib] = None) -> np.ndarray:
+    """The oracle's exact float64 reading of a tensor's stored elements."""
+    lib = (impl or _load()).lib
+    a, code = _as_stored(t)
+    a = np.ascontiguousarray(a).reshape(-1)
+    out = np.empty(a.size, dtype=np.float64)
+    lib.oracle_widen(code, _ptr(a), a.size, _ptr(out))
+    return out
 

@@ -29,9 +29,12 @@
 
 #define ORACLE_BF16 0
 #define ORACLE_FP32 1
+#define ORACLE_FP16 2
 
 /* Exact widening of one stored element to double.  bf16 is the upper half of
- * an IEEE binary32, so shifting its 16 bits up gives the same value. */
+ * an IEEE binary32, so shifting its 16 bits up gives the same value.  An IEEE
+ * binary16 with exponent field e and fraction f is (1 + f/1024) * 2^(e-15)
+ * for 0 < e < 31, f * 2^-24 for e = 0 (subnormal), +-inf or NaN for e = 31. */
 static double load_elem(const void *base, int dtype, int64_t idx)
 {
     if (dtype == ORACLE_BF16) {
@@ -40,7 +43,27 @@ static double load_elem(const void *base, int dtype, int64_t idx)
         memcpy(&f, &u, sizeof f);
         return (double)f;
     }
+    if (dtype == ORACLE_FP16) {
+        const uint16_t h = ((const uint16_t *)base)[idx];
+        const int e = (h >> 10) & 31, f = h & 1023;
+        double v;
+        if (e == 0)
+            v = ldexp((double)f, -24);
+        else if (e == 31)
+            v = f ? NAN : INFINITY;
+        else
+            v = ldexp((double)(1024 + f), e - 25);
+        return (h >> 15) ? -v : v;
+    }
     return (double)((const float *)base)[idx];
+}
+
+/* The stored elements src[0 .. n-1] widened to double (the reading every
+ * input of the oracle goes through). */
+void oracle_widen(int32_t dtype, const void *src, int64_t n, double *dst)
+{
+    for (int64_t i = 0; i < n; ++i)
+        dst[i] = load_elem(src, dtype, i);
 }
 
 /* Number of keys held by request b of a CSR page table: all pages but the

@@ -378,6 +378,25 @@ def check_merge_algebra(impl=None):
     assert close(v, (va + vb) / 2) and close(s, sa + math.log(2.0))
 
 
+# --------------------------------------------------------------------------- input widening
+
+
+def check_widening_every_16_bit_pattern(impl=None):
+    """Every bf16 and every IEEE half bit pattern widens to the float64 that
+    torch's / numpy's own conversions give (NaN patterns to NaN); fp32 values
+    pass through unchanged."""
+    bits = torch.arange(-32768, 32768, dtype=torch.int32).to(torch.int16)
+    for dt in (torch.bfloat16, torch.float16):
+        got = oracle.widen(bits.view(dt), impl=impl)
+        want = bits.view(dt).to(torch.float64).numpy()
+        if dt == torch.float16:
+            want_np = bits.numpy().view(np.float16).astype(np.float64)
+            assert np.array_equal(want, want_np, equal_nan=True)
+        assert np.array_equal(got, want, equal_nan=True), dt
+    x = torch.randn(1000, dtype=torch.float32) * 1e3
+    assert np.array_equal(oracle.widen(x, impl=impl), x.double().numpy())
+
+
 # --------------------------------------------------------------------------- logits soft cap
 
 
@@ -543,6 +562,7 @@ ALL_CHECKS = [
     check_paging_invariance,
     check_empty_sets,
     check_decode_trim,
+    check_widening_every_16_bit_pattern,
     check_soft_cap_brute_force,
     check_soft_cap_saturation,
     check_soft_cap_large_is_no_cap,

@@ -39,6 +39,9 @@ MUTANTS = {
     "merge_shift_dropped": ("const double s = M + log(exp(a - M) + exp(b - M));",
                             "const double s = log(exp(a - M) + exp(b - M));"),
     "merge_empty_nonzero": ("s_out[i] = -INFINITY;", "s_out[i] = 0.0;"),
+    "half_exponent_bias": ("v = ldexp((double)(1024 + f), e - 25);",
+                           "v = ldexp((double)(1024 + f), e - 24);"),
+    "half_subnormal_scale": ("v = ldexp((double)f, -24);", "v = ldexp((double)f, -25);"),
     "cap_of_unscaled_logit": ("s[j] = soft_cap * tanh(s[j] / soft_cap);",
                               "s[j] = soft_cap * tanh(dot / soft_cap);"),
     "cap_factor_dropped": ("s[j] = soft_cap * tanh(s[j] / soft_cap);",
