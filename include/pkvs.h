@@ -72,7 +72,7 @@ typedef enum pkvs_status {
     PKVS_ERR_NOT_PLANNED = -7    /* run() before a device plan was made */
 } pkvs_status;
 
-typedef enum pkvs_dtype { PKVS_BF16 = 0, PKVS_FP32 = 1 } pkvs_dtype;
+typedef enum pkvs_dtype { PKVS_BF16 = 0, PKVS_FP32 = 1, PKVS_FP16 = 2 } pkvs_dtype;
 
 typedef enum pkvs_kind { PKVS_PREFILL = 0, PKVS_DECODE = 1, PKVS_CASCADE = 2 } pkvs_kind;
 
@@ -82,11 +82,12 @@ typedef enum pkvs_kind { PKVS_PREFILL = 0, PKVS_DECODE = 1, PKVS_CASCADE = 2 } p
  *                   new tokens' keys come in a contiguous array and whose cached
  *                   prefix sits in the paged cache; see pkvs_cascade_plan)
  *  num_qo_heads     multiple of num_kv_heads; group = num_qo_heads/num_kv_heads
- *                   must be a power of two <= 16 (bf16 path)
+ *                   must be a power of two <= 16 (bf16 and fp16 paths)
  *  head_dim         64, 128 or 256
  *  page_size        power of two, 1 .. 1024
- *  dtype            q, k_cache, v_cache and o share it (PKVS_BF16 or PKVS_FP32;
- *                   accumulation is fp32 either way)
+ *  dtype            q, k_cache, v_cache and o share it: PKVS_BF16, PKVS_FP16
+ *                   (IEEE half; the dtype sweep of [PR234] "Tests added") or
+ *                   PKVS_FP32; accumulation is fp32 in every case
  *  causal           prefill, cascade: 1, or 0 only with window_left = -1;
  *                   decode: ignored
  *  window_left      -1 (no window) or W >= 0 (W+1 visible keys, [PR234] 1)

@@ -173,7 +173,7 @@ struct DecodeState {
     f32x4 o[NV][8];
 };
 
-template <int D>
+template <int D, bool F16>
 __device__ __forceinline__ void decode_compute(const DecodeBuf<D> &buf, DecodeState<D> &st,
                                                const bf16x8 (&qf)[D / 32], int blk, int lo,
                                                int t1, float scale_log2, float cap_a, int lane)
@@ -183,8 +183,8 @@ __device__ __forceinline__ void decode_compute(const DecodeBuf<D> &buf, DecodeSt
     f32x4 s0 = {0.f, 0.f, 0.f, 0.f}, s1 = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
     for (int s = 0; s < KS; ++s) {
-        s0 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(buf.k0[s], qf[s], s0, 0, 0, 0);
-        s1 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(buf.k1[s], qf[s], s1, 0, 0, 0);
+        s0 = mfma16x16x32<F16>(buf.k0[s], qf[s], s0);
+        s1 = mfma16x16x32<F16>(buf.k1[s], qf[s], s1);
     }
     // lane holds keys blk+4g+i (s0[i]) and blk+16+4g+i (s1[i]) of head lane%16
     float x[8];
@@ -224,7 +224,7 @@ __device__ __forceinline__ void decode_compute(const DecodeBuf<D> &buf, DecodeSt
     st.l = st.l * alpha + rs;
     st.m = m_new;
     f32x8 pv = {p[0], p[1], p[2], p[3], p[4], p[5], p[6], p[7]};
-    const bf16x8 pb = __builtin_convertvector(pv, bf16x8);
+    const bf16x8 pb = to16x8<F16>(pv);
 #pragma unroll
     for (int u = 0; u < NV; ++u) {
 #pragma unroll
@@ -232,8 +232,7 @@ __device__ __forceinline__ void decode_compute(const DecodeBuf<D> &buf, DecodeSt
             bf16x8 va;
 #pragma unroll
             for (int j = 0; j < 8; ++j) va[j] = buf.v[u][j][e];
-            st.o[u][e] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(va, pb, st.o[u][e] * alpha, 0,
-                                                                 0, 0);
+            st.o[u][e] = mfma16x16x32<F16>(va, pb, st.o[u][e] * alpha);
         }
     }
 }
@@ -246,8 +245,8 @@ constexpr int decode_stages() { return D >= 256 ? 2 : 3; }
 
 // NS register buffers of 32 keys each: NS-1 blocks are in flight while one is
 // being computed.
-template <int D, int NS>
-__global__ __launch_bounds__(kDecodeThreads) void decode_bf16_kernel(DecodeArgs a)
+template <int D, int NS, bool F16>
+__global__ __launch_bounds__(kDecodeThreads) void decode_kernel(DecodeArgs a)
 {
     constexpr int KS = D / 32, NV = DecodeBuf<D>::NV;
     const int lane = threadIdx.x;
@@ -298,7 +297,7 @@ __global__ __launch_bounds__(kDecodeThreads) void decode_bf16_kernel(DecodeArgs 
                 for (int s = 0; s < NS; ++s) {
                     decode_load<D>(buf[(s + NS - 1) % NS], a, pw, blk + kDecodeBlock * (NS - 1),
                                    t1, hk, lane);
-                    decode_compute<D>(buf[s], st, qf, blk, lo, t1, a.scale_log2, a.cap_a, lane);
+                    decode_compute<D, F16>(buf[s], st, qf, blk, lo, t1, a.scale_log2, a.cap_a, lane);
                     blk += kDecodeBlock;
                     if (blk >= t1) {
                         done = true;
@@ -329,8 +328,7 @@ __global__ __launch_bounds__(kDecodeThreads) void decode_bf16_kernel(DecodeArgs 
                             f32x8 ov;
 #pragma unroll
                             for (int e = 0; e < 8; ++e) ov[e] = st.o[u][e][i] * inv;
-                            *reinterpret_cast<bf16x8 *>(O + orow + d0) =
-                                __builtin_convertvector(ov, bf16x8);
+                            *reinterpret_cast<bf16x8 *>(O + orow + d0) = to16x8<F16>(ov);
                         }
                     }
                 if (a.lse && g == 0) a.lse[int64_t(b) * a.num_qo_heads + h] = lse;
@@ -361,7 +359,7 @@ __global__ __launch_bounds__(kDecodeThreads) void decode_bf16_kernel(DecodeArgs 
 // Combine the chunk partials of every split (request, kv head): one wave per
 // (merge entry, query head of the group); the LSE-weighted sum of
 // pkvs_merge_state, folded over all chunks at once.
-template <int D>
+template <int D, bool F16>
 __global__ __launch_bounds__(kMergeThreads) void decode_merge_kernel(DecodeArgs a)
 {
     constexpr int E = D / 64;  // elements per lane
@@ -393,10 +391,7 @@ __global__ __launch_bounds__(kMergeThreads) void decode_merge_kernel(DecodeArgs 
         uint16_t *O = static_cast<uint16_t *>(a.o);
         const int64_t orow = (int64_t(b) * a.num_qo_heads + hk * G + h) * D;
 #pragma unroll
-        for (int e = 0; e < E; ++e) {
-            const __bf16 ob = __bf16(acc[e] * inv);
-            O[orow + lane + 64 * e] = __builtin_bit_cast(uint16_t, ob);
-        }
+        for (int e = 0; e < E; ++e) O[orow + lane + 64 * e] = to16<F16>(acc[e] * inv);
         if (a.lse && lane == 0)
             a.lse[int64_t(b) * a.num_qo_heads + hk * G + h] =
                 sum > 0.f ? M + fast_log2(sum) * kLn2 : kNegInf;
@@ -405,49 +400,69 @@ __global__ __launch_bounds__(kMergeThreads) void decode_merge_kernel(DecodeArgs 
 
 }  // namespace
 
-hipError_t launch_decode_bf16(const DecodeArgs &a, int head_dim, int grid, hipStream_t s)
+template <bool F16>
+static hipError_t launch_decode_t(const DecodeArgs &a, int head_dim, int grid, hipStream_t s)
 {
     switch (head_dim) {
-    case 64: decode_bf16_kernel<64, decode_stages<64>()><<<grid, kDecodeThreads, 0, s>>>(a); break;
-    case 128: decode_bf16_kernel<128, decode_stages<128>()><<<grid, kDecodeThreads, 0, s>>>(a); break;
-    case 256: decode_bf16_kernel<256, decode_stages<256>()><<<grid, kDecodeThreads, 0, s>>>(a); break;
+    case 64: decode_kernel<64, decode_stages<64>(), F16><<<grid, kDecodeThreads, 0, s>>>(a); break;
+    case 128: decode_kernel<128, decode_stages<128>(), F16><<<grid, kDecodeThreads, 0, s>>>(a); break;
+    case 256: decode_kernel<256, decode_stages<256>(), F16><<<grid, kDecodeThreads, 0, s>>>(a); break;
     default: return hipErrorInvalidValue;
     }
     return hipGetLastError();
 }
 
-hipError_t launch_decode_merge(const DecodeArgs &a, int head_dim, int dtype, int grid,
+hipError_t launch_decode_16bit(const DecodeArgs &a, int head_dim, bool f16, int grid,
                                hipStream_t s)
 {
-    (void)dtype;
+    return f16 ? launch_decode_t<true>(a, head_dim, grid, s)
+               : launch_decode_t<false>(a, head_dim, grid, s);
+}
+
+template <bool F16>
+static hipError_t launch_merge_t(const DecodeArgs &a, int head_dim, int grid, hipStream_t s)
+{
     switch (head_dim) {
-    case 64: decode_merge_kernel<64><<<grid, kMergeThreads, 0, s>>>(a); break;
-    case 128: decode_merge_kernel<128><<<grid, kMergeThreads, 0, s>>>(a); break;
-    case 256: decode_merge_kernel<256><<<grid, kMergeThreads, 0, s>>>(a); break;
+    case 64: decode_merge_kernel<64, F16><<<grid, kMergeThreads, 0, s>>>(a); break;
+    case 128: decode_merge_kernel<128, F16><<<grid, kMergeThreads, 0, s>>>(a); break;
+    case 256: decode_merge_kernel<256, F16><<<grid, kMergeThreads, 0, s>>>(a); break;
     default: return hipErrorInvalidValue;
     }
     return hipGetLastError();
 }
 
-int decode_bf16_blocks_per_cu(int head_dim)
+hipError_t launch_decode_merge(const DecodeArgs &a, int head_dim, bool f16, int grid,
+                               hipStream_t s)
+{
+    return f16 ? launch_merge_t<true>(a, head_dim, grid, s)
+               : launch_merge_t<false>(a, head_dim, grid, s);
+}
+
+template <bool F16>
+static int decode_blocks_per_cu_t(int head_dim)
 {
     int n = 0;
     hipError_t e = hipErrorInvalidValue;
     switch (head_dim) {
     case 64:
-        e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, decode_bf16_kernel<64, decode_stages<64>()>,
-                                                         kDecodeThreads, 0);
+        e = hipOccupancyMaxActiveBlocksPerMultiprocessor(
+            &n, decode_kernel<64, decode_stages<64>(), F16>, kDecodeThreads, 0);
         break;
     case 128:
-        e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, decode_bf16_kernel<128, decode_stages<128>()>,
-                                                         kDecodeThreads, 0);
+        e = hipOccupancyMaxActiveBlocksPerMultiprocessor(
+            &n, decode_kernel<128, decode_stages<128>(), F16>, kDecodeThreads, 0);
         break;
     case 256:
-        e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, decode_bf16_kernel<256, decode_stages<256>()>,
-                                                         kDecodeThreads, 0);
+        e = hipOccupancyMaxActiveBlocksPerMultiprocessor(
+            &n, decode_kernel<256, decode_stages<256>(), F16>, kDecodeThreads, 0);
         break;
     }
     return e == hipSuccess ? n : 0;
+}
+
+int decode_blocks_per_cu(int head_dim, bool f16)
+{
+    return f16 ? decode_blocks_per_cu_t<true>(head_dim) : decode_blocks_per_cu_t<false>(head_dim);
 }
 
 }  // namespace pkvs

@@ -13,6 +13,11 @@ typedef float f32x8 __attribute__((ext_vector_type(8)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+typedef float f32x2 __attribute__((ext_vector_type(2)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
+typedef _Float16 f16x4 __attribute__((ext_vector_type(4)));
+typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
 
 constexpr float kNegInf = -__builtin_inff();
 constexpr float kLn2 = 0.69314718055994530942f;
@@ -50,6 +55,66 @@ __device__ __forceinline__ int64_t nhd_offset(int64_t page, int slot, int page_s
                                               int num_kv_heads, int head_dim)
 {
     return ((page * page_size + slot) * num_kv_heads + hk) * int64_t(head_dim);
+}
+
+// 16-bit inputs -- bfloat16, or IEEE half when F16 -- travel through
+// registers and LDS as raw 16-bit patterns held in bf16 vectors; only the
+// matrix instructions and the conversions from and to fp32 read them as
+// numbers.
+template <bool F16>
+__device__ __forceinline__ f32x16 mfma32x32x16(bf16x8 a, bf16x8 b, f32x16 c)
+{
+    if constexpr (F16)
+        return __builtin_amdgcn_mfma_f32_32x32x16_f16(__builtin_bit_cast(f16x8, a),
+                                                      __builtin_bit_cast(f16x8, b), c, 0, 0, 0);
+    else
+        return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
+}
+
+template <bool F16>
+__device__ __forceinline__ f32x4 mfma16x16x32(bf16x8 a, bf16x8 b, f32x4 c)
+{
+    if constexpr (F16)
+        return __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(f16x8, a),
+                                                      __builtin_bit_cast(f16x8, b), c, 0, 0, 0);
+    else
+        return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
+}
+
+// fp32 -> 16-bit, round to nearest even
+template <bool F16>
+__device__ __forceinline__ bf16x8 to16x8(f32x8 v)
+{
+    if constexpr (F16) return __builtin_bit_cast(bf16x8, __builtin_convertvector(v, f16x8));
+    else return __builtin_convertvector(v, bf16x8);
+}
+
+template <bool F16>
+__device__ __forceinline__ bf16x4 to16x4(f32x4 v)
+{
+    if constexpr (F16) return __builtin_bit_cast(bf16x4, __builtin_convertvector(v, f16x4));
+    else return __builtin_convertvector(v, bf16x4);
+}
+
+template <bool F16>
+__device__ __forceinline__ bf16x2 to16x2(f32x2 v)
+{
+    if constexpr (F16) return __builtin_bit_cast(bf16x2, __builtin_convertvector(v, f16x2));
+    else return __builtin_convertvector(v, bf16x2);
+}
+
+template <bool F16>
+__device__ __forceinline__ uint16_t to16(float x)
+{
+    if constexpr (F16) return __builtin_bit_cast(uint16_t, _Float16(x));
+    else return __builtin_bit_cast(uint16_t, __bf16(x));
+}
+
+template <bool F16>
+__device__ __forceinline__ f32x4 from16x4(bf16x4 v)
+{
+    if constexpr (F16) return __builtin_convertvector(__builtin_bit_cast(f16x4, v), f32x4);
+    else return __builtin_convertvector(v, f32x4);
 }
 
 __device__ __forceinline__ bf16x8 load_bf16x8(const void *p)

@@ -24,6 +24,12 @@ __device__ __forceinline__ float ld<uint16_t>(const uint16_t *p, int64_t i)
     return bf16_bits_to_float(p[i]);
 }
 
+template <>
+__device__ __forceinline__ float ld<_Float16>(const _Float16 *p, int64_t i)
+{
+    return float(p[i]);
+}
+
 template <typename T>
 __device__ __forceinline__ void st(T *p, int64_t i, float x);
 template <>
@@ -32,6 +38,12 @@ template <>
 __device__ __forceinline__ void st<uint16_t>(uint16_t *p, int64_t i, float x)
 {
     p[i] = __builtin_bit_cast(uint16_t, __bf16(x));
+}
+
+template <>
+__device__ __forceinline__ void st<_Float16>(_Float16 *p, int64_t i, float x)
+{
+    p[i] = _Float16(x);
 }
 
 template <typename T>
@@ -70,7 +82,11 @@ hipError_t launch_merge_state(const void *va, const float *sa, const void *vb, c
 {
     const int64_t units = n * heads;
     if (units == 0) return hipSuccess;
-    if (dtype == PKVS_BF16)
+    if (dtype == PKVS_FP16)
+        merge_state_kernel<_Float16><<<grid, kMergeThreads, 0, s>>>(
+            static_cast<const _Float16 *>(va), sa, static_cast<const _Float16 *>(vb), sb,
+            static_cast<_Float16 *>(vo), so, units, head_dim);
+    else if (dtype == PKVS_BF16)
         merge_state_kernel<uint16_t><<<grid, kMergeThreads, 0, s>>>(
             static_cast<const uint16_t *>(va), sa, static_cast<const uint16_t *>(vb), sb,
             static_cast<uint16_t *>(vo), so, units, head_dim);

@@ -112,11 +112,13 @@ struct DecodeArgs {
 };
 
 // Launchers (return hipError_t of the launch).
-hipError_t launch_prefill_bf16(const PrefillArgs &a, int head_dim, int variant, int grid,
-                               hipStream_t s);
+// 16-bit paths: bf16, or IEEE half when f16
+hipError_t launch_prefill_16bit(const PrefillArgs &a, int head_dim, int variant, bool f16,
+                                int grid, hipStream_t s);
 hipError_t launch_attention_fp32(const PrefillArgs &a, int head_dim, int grid, hipStream_t s);
-hipError_t launch_decode_bf16(const DecodeArgs &a, int head_dim, int grid, hipStream_t s);
-hipError_t launch_decode_merge(const DecodeArgs &a, int head_dim, int dtype, int grid,
+hipError_t launch_decode_16bit(const DecodeArgs &a, int head_dim, bool f16, int grid,
+                               hipStream_t s);
+hipError_t launch_decode_merge(const DecodeArgs &a, int head_dim, bool f16, int grid,
                                hipStream_t s);
 hipError_t launch_merge_state(const void *va, const float *sa, const void *vb, const float *sb,
                               void *vo, float *so, int64_t n, int32_t heads, int32_t head_dim,
@@ -132,7 +134,7 @@ hipError_t launch_build_kv_indices(const int32_t *map, int64_t map_rows, int64_t
                                    int64_t capacity, int32_t *status, int grid, hipStream_t s);
 
 // Resident workgroups per CU of each kernel (occupancy query; 0 if unknown).
-int prefill_bf16_blocks_per_cu(int head_dim, int variant);
-int decode_bf16_blocks_per_cu(int head_dim);
+int prefill_blocks_per_cu(int head_dim, int variant, bool f16);
+int decode_blocks_per_cu(int head_dim, bool f16);
 
 }  // namespace pkvs

@@ -118,11 +118,11 @@ static int validate_desc(const pkvs_desc *d)
         return fail(PKVS_ERR_UNSUPPORTED, "one page (page_size x num_kv_heads x head_dim "
                     "elements, %d rows for a cascade's extend keys) must stay below 2^31 "
                     "elements", kRaggedPage);
-    if (d->dtype != PKVS_BF16 && d->dtype != PKVS_FP32)
-        return fail(PKVS_ERR_UNSUPPORTED, "dtype %d not built (bf16, fp32)", d->dtype);
-    if (d->dtype == PKVS_BF16 && (!is_pow2(group) || group > 16))
-        return fail(PKVS_ERR_UNSUPPORTED, "bf16 path needs a power-of-two group <= 16, got %d",
-                    group);
+    if (d->dtype != PKVS_BF16 && d->dtype != PKVS_FP32 && d->dtype != PKVS_FP16)
+        return fail(PKVS_ERR_UNSUPPORTED, "dtype %d not built (bf16, fp16, fp32)", d->dtype);
+    if (d->dtype != PKVS_FP32 && (!is_pow2(group) || group > 16))
+        return fail(PKVS_ERR_UNSUPPORTED, "the 16-bit paths need a power-of-two group <= 16, "
+                    "got %d", group);
     // (bit test: this file is built with -fno-honor-nans, which folds NaN
     // comparisons away)
     uint32_t cap_bits;
@@ -439,7 +439,7 @@ static int create_plan(const pkvs_desc *desc, bool ragged, Plan **out)
             p->num_cus = cus;
     }
     (void)hipGetLastError();
-    const bool fp32 = desc->dtype == PKVS_FP32;
+    const bool fp32 = desc->dtype == PKVS_FP32, f16 = desc->dtype == PKVS_FP16;
     if (desc->kind == PKVS_PREFILL) {
         // Kernel variant: 256-row workgroups (8 waves x 32 rows) share each
         // staged key tile between more rows and keep two waves per SIMD; they
@@ -453,7 +453,7 @@ static int create_plan(const pkvs_desc *desc, bool ragged, Plan **out)
         if (desc->prefill_variant) v = desc->prefill_variant;
         // the direct-to-LDS variant needs ~156 KiB of LDS per workgroup
         if (v == kPrefillDma && p->have_gpu && !fp32 &&
-            prefill_bf16_blocks_per_cu(desc->head_dim, v) < 1)
+            prefill_blocks_per_cu(desc->head_dim, v, f16) < 1)
             v = kPrefillRows256;
         p->prefill_variant = p->run_variant = v;
         const int rows = v == kPrefillRows128 ? 128 : 256;
@@ -461,13 +461,13 @@ static int create_plan(const pkvs_desc *desc, bool ragged, Plan **out)
         p->item_words = kPrefillItemWords;
         p->block_threads =
             fp32 ? kGenericThreads : (v == kPrefillRows256 || v == kPrefillDma ? 512 : 256);
-        int per_cu = p->have_gpu && !fp32 ? prefill_bf16_blocks_per_cu(desc->head_dim, v) : 0;
+        int per_cu = p->have_gpu && !fp32 ? prefill_blocks_per_cu(desc->head_dim, v, f16) : 0;
         p->grid_blocks = p->num_cus * std::max(per_cu, fp32 ? 2 : 1);
     } else {
         p->query_tile = 1;
         p->item_words = fp32 ? kPrefillItemWords : kDecodeItemWords;
         p->block_threads = fp32 ? kGenericThreads : kDecodeThreads;
-        int per_cu = p->have_gpu && !fp32 ? decode_bf16_blocks_per_cu(desc->head_dim) : 0;
+        int per_cu = p->have_gpu && !fp32 ? decode_blocks_per_cu(desc->head_dim, f16) : 0;
         p->grid_blocks = p->num_cus * std::max(per_cu, fp32 ? 2 : 8);
         p->auto_target_items = 2 * p->grid_blocks;
     }
@@ -541,7 +541,7 @@ static int create_cascade(const pkvs_desc *desc, Plan **out)
     p->items_cap = p->ext->items_cap + q->items_cap;
     p->pre_int_off = align256(p->ext->int_ws_need);
     p->int_ws_need = p->pre_int_off + q->int_ws_need;
-    const size_t esz = desc->dtype == PKVS_BF16 ? 2 : 4;
+    const size_t esz = desc->dtype == PKVS_FP32 ? 4 : 2;
     const size_t rows = size_t(desc->qo_capacity) * size_t(desc->num_qo_heads);
     p->o2_off = 0;
     p->lse2_off = align256(rows * size_t(desc->head_dim) * esz);

@@ -201,7 +201,7 @@ __device__ __forceinline__ void stage_store(Stage<D, NW> &st, PrefillBuf<D> &b, 
 }
 
 // S^T[32 keys x 32 rows] = K . Q^T for the tile in b.
-template <int D>
+template <int D, bool F16>
 __device__ __forceinline__ f32x16 qk_tile(const PrefillBuf<D> &b, const bf16x8 (&qf)[D / 16],
                                           int l32, int hw)
 {
@@ -211,13 +211,13 @@ __device__ __forceinline__ f32x16 qk_tile(const PrefillBuf<D> &b, const bf16x8 (
 #pragma unroll
     for (int ks = 0; ks < D / 16; ++ks) {
         const bf16x8 kf = *reinterpret_cast<const bf16x8 *>(&b.k[l32][ks * 16 + hw * 8]);
-        s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf, qf[ks], s, 0, 0, 0);
+        s = mfma32x32x16<F16>(kf, qf[ks], s);
     }
     return s;
 }
 
 // O^T += V^T . P^T for one 32-key tile (two k-steps of 16 keys).
-template <int D>
+template <int D, bool F16>
 __device__ __forceinline__ void pv_tile(const PrefillBuf<D> &b, const bf16x8 (&pb)[2],
                                         f32x16 (&o)[D / 32], int tr_key, int tr_dim)
 {
@@ -231,7 +231,7 @@ __device__ __forceinline__ void pv_tile(const PrefillBuf<D> &b, const bf16x8 (&p
                 __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4 *)(v0 + 8 * (D + VPAD)));
             const bf16x8 va =
                 __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
-            o[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(va, pb[kk], o[dt], 0, 0, 0);
+            o[dt] = mfma32x32x16<F16>(va, pb[kk], o[dt]);
         }
 }
 
@@ -298,8 +298,8 @@ __device__ __forceinline__ void dma_rows4_kv(const uint32_t (&mk)[4], const uint
                  : "memory");
 }
 
-template <int D, int NW, bool DMA>
-__global__ __launch_bounds__(NW * 64) void prefill_bf16_kernel(PrefillArgs a)
+template <int D, int NW, bool DMA, bool F16>
+__global__ __launch_bounds__(NW * 64) void prefill_kernel(PrefillArgs a)
 {
     static_assert(!DMA || (D == 128 && NW == 8), "direct-to-LDS staging: D = 128, 8 waves");
     constexpr int KSTEPS = D / 16;  // QK k-steps
@@ -479,7 +479,7 @@ __global__ __launch_bounds__(NW * 64) void prefill_bf16_kernel(PrefillArgs a)
         }
         // S^T of tile 0 (s_a); each step leaves the next tile's in s_b
         f32x16 s_a, s_b;
-        if (ntiles > 0) s_a = qk_tile<D>(lds[0], qf, l32, hw);
+        if (ntiles > 0) s_a = qk_tile<D, F16>(lds[0], qf, l32, hw);
 
         // Ping-pong: with 8 waves, waves w and w+4 share a SIMD.  Waves 4..7
         // issue the PV product of a tile one iteration late, so in every
@@ -497,7 +497,7 @@ __global__ __launch_bounds__(NW * 64) void prefill_bf16_kernel(PrefillArgs a)
             // page of tile j+AHEAD, requested early (used at the end of the step)
             int32_t pg_next = 0;
             if constexpr (DMA) pg_next = dma_page(j + DMA_AHEAD);
-            if (lag && j > 0) pv_tile<D>(lds[(j - 1) & (NS - 1)], pb_in, o, tr_key, tr_dim);
+            if (lag && j > 0) pv_tile<D, F16>(lds[(j - 1) & (NS - 1)], pb_in, o, tr_key, tr_dim);
             // K operands of tile j+1 (its LDS set is ready; after the last tile
             // they are read but unused), requested before the row maximum
             const PrefillBuf<D> &bn = lds[(j + 1) & (NS - 1)];
@@ -548,7 +548,7 @@ __global__ __launch_bounds__(NW * 64) void prefill_bf16_kernel(PrefillArgs a)
             f32x16 pr;
 #pragma unroll
             for (int ks = 0; ks < KSTEPS; ++ks) {
-                s_out = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf[ks], qf[ks], s_out, 0, 0, 0);
+                s_out = mfma32x32x16<F16>(kf[ks], qf[ks], s_out);
 #pragma unroll
                 for (int e = 0; e < EPS; ++e) {
                     const int i = ks * EPS + e;
@@ -566,9 +566,9 @@ __global__ __launch_bounds__(NW * 64) void prefill_bf16_kernel(PrefillArgs a)
                 f32x8 p8;
 #pragma unroll
                 for (int jj = 0; jj < 8; ++jj) p8[jj] = pr[8 * kk + jj];
-                pb_out[kk] = __builtin_convertvector(p8, bf16x8);
+                pb_out[kk] = to16x8<F16>(p8);
             }
-            if (!lag) pv_tile<D>(lds[j & (NS - 1)], pb_out, o, tr_key, tr_dim);
+            if (!lag) pv_tile<D, F16>(lds[j & (NS - 1)], pb_out, o, tr_key, tr_dim);
 
             if constexpr (DMA) {
                 // tile j+AHEAD into the set tile j-2 used; then tile j+2 must
@@ -594,7 +594,7 @@ __global__ __launch_bounds__(NW * 64) void prefill_bf16_kernel(PrefillArgs a)
             pb_b[0] = pb_a[0];
             pb_b[1] = pb_a[1];
         }
-        if (lag && ntiles > 0) pv_tile<D>(lds[(ntiles - 1) & (NS - 1)], pb_b, o, tr_key, tr_dim);
+        if (lag && ntiles > 0) pv_tile<D, F16>(lds[(ntiles - 1) & (NS - 1)], pb_b, o, tr_key, tr_dim);
 
         // epilogue: the two half-waves hold disjoint keys of each row
         l += __shfl_xor(l, 32);
@@ -619,12 +619,11 @@ __global__ __launch_bounds__(NW * 64) void prefill_bf16_kernel(PrefillArgs a)
 #pragma unroll
                     for (int m1 = 0; m1 < 4; ++m1) v4[m1] = o[dt][4 * m0 + m1] * w_self;
                     if (FO) {
-                        const f32x4 f4 = __builtin_convertvector(
-                            *reinterpret_cast<const bf16x4 *>(FO + at), f32x4);
+                        const f32x4 f4 = from16x4<F16>(*reinterpret_cast<const bf16x4 *>(FO + at));
 #pragma unroll
                         for (int m1 = 0; m1 < 4; ++m1) v4[m1] += f4[m1] * w_other;
                     }
-                    *reinterpret_cast<bf16x4 *>(O + at) = __builtin_convertvector(v4, bf16x4);
+                    *reinterpret_cast<bf16x4 *>(O + at) = to16x4<F16>(v4);
                 }
             if (a.lse && hw == 0) a.lse[lrow] = lse_row;
         }
@@ -667,7 +666,7 @@ __device__ __forceinline__ bf16x8 wide_kop(const PrefillBuf<D> &b, int ks, int l
     return *reinterpret_cast<const bf16x8 *>(&b.k[l32][ks * 16 + hw * 8]);
 }
 
-template <int D>
+template <int D, bool F16>
 __global__ __launch_bounds__(256) void prefill_wide_kernel(PrefillArgs a)
 {
     constexpr int KS = WideOps<D>::KS, DT = WideOps<D>::DT, NQ = WideOps<D>::NQ;
@@ -766,8 +765,7 @@ __global__ __launch_bounds__(256) void prefill_wide_kernel(PrefillArgs a)
                 const bf16x8 kf = wide_kop<D>(lds[0], ks, l32, hw);
 #pragma unroll
                 for (int n = 0; n < 2; ++n)
-                    s_cur[n] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf, qf[n][ks], s_cur[n],
-                                                                       0, 0, 0);
+                    s_cur[n] = mfma32x32x16<F16>(kf, qf[n][ks], s_cur[n]);
             }
         }
         bf16x8 p_prev[2][2];
@@ -805,8 +803,7 @@ __global__ __launch_bounds__(256) void prefill_wide_kernel(PrefillArgs a)
                     const int dt = q >> 1, kk = q & 1;
 #pragma unroll
                     for (int n = 0; n < 2; ++n)
-                        o[n][dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vc, p_prev[n][kk],
-                                                                           o[n][dt], 0, 0, 0);
+                        o[n][dt] = mfma32x32x16<F16>(vc, p_prev[n][kk], o[n][dt]);
                     // 32 scores over NQ steps
 #pragma unroll
                     for (int e = 0; e < 32 / NQ; e += 2) {
@@ -844,11 +841,9 @@ __global__ __launch_bounds__(256) void prefill_wide_kernel(PrefillArgs a)
                     for (int n = 0; n < 2; ++n) {
                         if (ks == 0) {
                             const f32x16 z = {};
-                            s_nxt[n] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kc, qf[n][0], z,
-                                                                               0, 0, 0);
+                            s_nxt[n] = mfma32x32x16<F16>(kc, qf[n][0], z);
                         } else {
-                            s_nxt[n] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kc, qf[n][ks],
-                                                                               s_nxt[n], 0, 0, 0);
+                            s_nxt[n] = mfma32x32x16<F16>(kc, qf[n][ks], s_nxt[n]);
                         }
                     }
 #pragma unroll
@@ -857,9 +852,7 @@ __global__ __launch_bounds__(256) void prefill_wide_kernel(PrefillArgs a)
                         const float e0 = fast_exp2(__builtin_fmaf(s_cur[n][i], c, -mu[n]));
                         const float e1 = fast_exp2(__builtin_fmaf(s_cur[n][i + 1], c, -mu[n]));
                         rs[n] += e0 + e1;
-                        typedef float f32x2 __attribute__((ext_vector_type(2)));
-                        typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
-                        const bf16x2 pk = __builtin_convertvector(f32x2{e0, e1}, bf16x2);
+                        const bf16x2 pk = to16x2<F16>(f32x2{e0, e1});
                         p_cur[n][i >> 3][i & 7] = pk[0];
                         p_cur[n][i >> 3][(i & 7) + 1] = pk[1];
                         // keep this step's VALU work here, between its MFMAs
@@ -904,8 +897,7 @@ __global__ __launch_bounds__(256) void prefill_wide_kernel(PrefillArgs a)
                 const bf16x8 vc = wide_vop<D>(bl, q, tr_key, tr_dim);
 #pragma unroll
                 for (int n = 0; n < 2; ++n)
-                    o[n][q >> 1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vc, p_prev[n][q & 1],
-                                                                           o[n][q >> 1], 0, 0, 0);
+                    o[n][q >> 1] = mfma32x32x16<F16>(vc, p_prev[n][q & 1], o[n][q >> 1]);
             }
         }
 #pragma unroll
@@ -933,12 +925,11 @@ __global__ __launch_bounds__(256) void prefill_wide_kernel(PrefillArgs a)
 #pragma unroll
                         for (int m1 = 0; m1 < 4; ++m1) v4[m1] = o[n][dt][4 * m0 + m1] * w_self;
                         if (FO) {
-                            const f32x4 f4 = __builtin_convertvector(
-                                *reinterpret_cast<const bf16x4 *>(FO + at), f32x4);
+                            const f32x4 f4 = from16x4<F16>(*reinterpret_cast<const bf16x4 *>(FO + at));
 #pragma unroll
                             for (int m1 = 0; m1 < 4; ++m1) v4[m1] += f4[m1] * w_other;
                         }
-                        *reinterpret_cast<bf16x4 *>(O + at) = __builtin_convertvector(v4, bf16x4);
+                        *reinterpret_cast<bf16x4 *>(O + at) = to16x4<F16>(v4);
                     }
                 if (a.lse && hw == 0) a.lse[lrow] = lse_row;
             }
@@ -1012,33 +1003,41 @@ __global__ __launch_bounds__(kGenericThreads) void attention_fp32_kernel(Prefill
 
 }  // namespace
 
-hipError_t launch_prefill_bf16(const PrefillArgs &a, int head_dim, int variant, int grid,
-                               hipStream_t s)
+template <bool F16>
+static hipError_t launch_prefill_t(const PrefillArgs &a, int head_dim, int variant, int grid,
+                                   hipStream_t s)
 {
     if (variant == kPrefillDma) {
         if (head_dim != 128) return hipErrorInvalidValue;
-        prefill_bf16_kernel<128, 8, true><<<grid, 512, 0, s>>>(a);
+        prefill_kernel<128, 8, true, F16><<<grid, 512, 0, s>>>(a);
     } else if (variant == kPrefillWide) {
         switch (head_dim) {
-        case 64: prefill_wide_kernel<64><<<grid, 256, 0, s>>>(a); break;
-        case 128: prefill_wide_kernel<128><<<grid, 256, 0, s>>>(a); break;
+        case 64: prefill_wide_kernel<64, F16><<<grid, 256, 0, s>>>(a); break;
+        case 128: prefill_wide_kernel<128, F16><<<grid, 256, 0, s>>>(a); break;
         default: return hipErrorInvalidValue;
         }
     } else if (variant == kPrefillRows256) {
         switch (head_dim) {
-        case 64: prefill_bf16_kernel<64, 8, false><<<grid, 512, 0, s>>>(a); break;
-        case 128: prefill_bf16_kernel<128, 8, false><<<grid, 512, 0, s>>>(a); break;
+        case 64: prefill_kernel<64, 8, false, F16><<<grid, 512, 0, s>>>(a); break;
+        case 128: prefill_kernel<128, 8, false, F16><<<grid, 512, 0, s>>>(a); break;
         default: return hipErrorInvalidValue;
         }
     } else {
         switch (head_dim) {
-        case 64: prefill_bf16_kernel<64, 4, false><<<grid, 256, 0, s>>>(a); break;
-        case 128: prefill_bf16_kernel<128, 4, false><<<grid, 256, 0, s>>>(a); break;
-        case 256: prefill_bf16_kernel<256, 4, false><<<grid, 256, 0, s>>>(a); break;
+        case 64: prefill_kernel<64, 4, false, F16><<<grid, 256, 0, s>>>(a); break;
+        case 128: prefill_kernel<128, 4, false, F16><<<grid, 256, 0, s>>>(a); break;
+        case 256: prefill_kernel<256, 4, false, F16><<<grid, 256, 0, s>>>(a); break;
         default: return hipErrorInvalidValue;
         }
     }
     return hipGetLastError();
+}
+
+hipError_t launch_prefill_16bit(const PrefillArgs &a, int head_dim, int variant, bool f16,
+                                int grid, hipStream_t s)
+{
+    return f16 ? launch_prefill_t<true>(a, head_dim, variant, grid, s)
+               : launch_prefill_t<false>(a, head_dim, variant, grid, s);
 }
 
 hipError_t launch_attention_fp32(const PrefillArgs &a, int head_dim, int grid, hipStream_t s)
@@ -1055,24 +1054,31 @@ static int blocks_per_cu(K kernel, int threads)
                                                                                              : 0;
 }
 
-int prefill_bf16_blocks_per_cu(int head_dim, int variant)
+template <bool F16>
+static int prefill_blocks_per_cu_t(int head_dim, int variant)
 {
     if (variant == kPrefillDma)
-        return head_dim == 128 ? blocks_per_cu(prefill_bf16_kernel<128, 8, true>, 512) : 0;
+        return head_dim == 128 ? blocks_per_cu(prefill_kernel<128, 8, true, F16>, 512) : 0;
     if (variant == kPrefillWide) {
-        if (head_dim == 64) return blocks_per_cu(prefill_wide_kernel<64>, 256);
-        if (head_dim == 128) return blocks_per_cu(prefill_wide_kernel<128>, 256);
+        if (head_dim == 64) return blocks_per_cu(prefill_wide_kernel<64, F16>, 256);
+        if (head_dim == 128) return blocks_per_cu(prefill_wide_kernel<128, F16>, 256);
         return 0;
     }
     if (variant == kPrefillRows256) {
-        if (head_dim == 64) return blocks_per_cu(prefill_bf16_kernel<64, 8, false>, 512);
-        if (head_dim == 128) return blocks_per_cu(prefill_bf16_kernel<128, 8, false>, 512);
+        if (head_dim == 64) return blocks_per_cu(prefill_kernel<64, 8, false, F16>, 512);
+        if (head_dim == 128) return blocks_per_cu(prefill_kernel<128, 8, false, F16>, 512);
         return 0;
     }
-    if (head_dim == 64) return blocks_per_cu(prefill_bf16_kernel<64, 4, false>, 256);
-    if (head_dim == 128) return blocks_per_cu(prefill_bf16_kernel<128, 4, false>, 256);
-    if (head_dim == 256) return blocks_per_cu(prefill_bf16_kernel<256, 4, false>, 256);
+    if (head_dim == 64) return blocks_per_cu(prefill_kernel<64, 4, false, F16>, 256);
+    if (head_dim == 128) return blocks_per_cu(prefill_kernel<128, 4, false, F16>, 256);
+    if (head_dim == 256) return blocks_per_cu(prefill_kernel<256, 4, false, F16>, 256);
     return 0;
+}
+
+int prefill_blocks_per_cu(int head_dim, int variant, bool f16)
+{
+    return f16 ? prefill_blocks_per_cu_t<true>(head_dim, variant)
+               : prefill_blocks_per_cu_t<false>(head_dim, variant);
 }
 
 }  // namespace pkvs

@@ -101,9 +101,10 @@ hipError_t launch_prefill_pass(const pkvs_plan *p, const void *q, const void *k,
     a.causal = p->desc.causal;
     a.fold_o = fold_o;
     a.fold_lse = fold_lse;
-    return p->desc.dtype == PKVS_BF16
-               ? launch_prefill_bf16(a, p->desc.head_dim, p->run_variant, p->grid_blocks, stream)
-               : launch_attention_fp32(a, p->desc.head_dim, p->grid_blocks, stream);
+    return p->desc.dtype == PKVS_FP32
+               ? launch_attention_fp32(a, p->desc.head_dim, p->grid_blocks, stream)
+               : launch_prefill_16bit(a, p->desc.head_dim, p->run_variant,
+                                      p->desc.dtype == PKVS_FP16, p->grid_blocks, stream);
 }
 
 }  // namespace
@@ -215,14 +216,15 @@ int pkvs_decode_run(const pkvs_plan *p, const void *q, const void *k_cache, cons
     a.log2_group = log2g;
     a.page_size = p->desc.page_size;
     a.log2_page = log2_exact(p->desc.page_size);
-    e = launch_decode_bf16(a, p->desc.head_dim, p->grid_blocks, stream);
+    const bool f16 = p->desc.dtype == PKVS_FP16;
+    e = launch_decode_16bit(a, p->desc.head_dim, f16, p->grid_blocks, stream);
     if (e != hipSuccess) return fail(PKVS_ERR_HIP, "decode launch: %s", hipGetErrorString(e));
     if (p->merges_cap > 0) {
         // launched whenever the plan can have merges (the kernel reads their
         // count), with a fixed grid sized from the capacity, never from this
         // batch: a captured graph stays valid for every later plan
         const int grid = int(std::min<int64_t>(p->merges_cap * group, int64_t(p->num_cus) * 16));
-        e = launch_decode_merge(a, p->desc.head_dim, p->desc.dtype, std::max(grid, 1), stream);
+        e = launch_decode_merge(a, p->desc.head_dim, f16, std::max(grid, 1), stream);
         if (e != hipSuccess)
             return fail(PKVS_ERR_HIP, "decode merge launch: %s", hipGetErrorString(e));
     }
@@ -237,7 +239,7 @@ int pkvs_merge_state(const void *v_a, const float *s_a, const void *v_b, const f
     if (num_tokens < 0 || num_heads <= 0 || head_dim <= 0)
         return fail(PKVS_ERR_INVALID_ARG, "bad shape (%lld, %d, %d)", (long long)num_tokens,
                     num_heads, head_dim);
-    if (v_dtype != PKVS_BF16 && v_dtype != PKVS_FP32)
+    if (v_dtype != PKVS_BF16 && v_dtype != PKVS_FP32 && v_dtype != PKVS_FP16)
         return fail(PKVS_ERR_UNSUPPORTED, "v_dtype %d not built", v_dtype);
     if (num_tokens == 0) return PKVS_OK;
     if (!v_a || !s_a || !v_b || !s_b || !v_out || !s_out)
@@ -260,9 +262,9 @@ int pkvs_append_kv(const void *k_new, const void *v_new, const int64_t *loc_d,
         return fail(PKVS_ERR_INVALID_ARG, "bad shape (%lld tokens, %lld slots, %d heads, %d "
                     "dims)", (long long)num_tokens, (long long)num_slots, num_kv_heads,
                     head_dim);
-    if (dtype != PKVS_BF16 && dtype != PKVS_FP32)
-        return fail(PKVS_ERR_UNSUPPORTED, "dtype %d not built (bf16, fp32)", dtype);
-    const int64_t row_bytes = int64_t(num_kv_heads) * head_dim * (dtype == PKVS_BF16 ? 2 : 4);
+    if (dtype != PKVS_BF16 && dtype != PKVS_FP32 && dtype != PKVS_FP16)
+        return fail(PKVS_ERR_UNSUPPORTED, "dtype %d not built (bf16, fp16, fp32)", dtype);
+    const int64_t row_bytes = int64_t(num_kv_heads) * head_dim * (dtype == PKVS_FP32 ? 4 : 2);
     if (row_bytes % 16)
         return fail(PKVS_ERR_UNSUPPORTED, "a cache row (num_kv_heads x head_dim elements) "
                     "must be a multiple of 16 bytes, got %lld", (long long)row_bytes);

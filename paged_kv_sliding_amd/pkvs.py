@@ -32,11 +32,13 @@ PKVS_ERR_NOT_PLANNED = -7
 
 PKVS_BF16 = 0
 PKVS_FP32 = 1
+PKVS_FP16 = 2
 PKVS_PREFILL = 0
 PKVS_DECODE = 1
 PKVS_CASCADE = 2
 
-_DTYPES = {torch.bfloat16: PKVS_BF16, torch.float32: PKVS_FP32}
+_DTYPES = {torch.bfloat16: PKVS_BF16, torch.float32: PKVS_FP32, torch.float16: PKVS_FP16}
+_TORCH_DTYPES = {v: k for k, v in _DTYPES.items()}
 
 # Every symbol include/pkvs.h declares.
 EXPORTED = [
@@ -345,7 +347,7 @@ class BatchAttention:
 
     def _check_shapes(self, q, k_cache, v_cache, kv_indices, out, lse):
         d = self.desc
-        dt = {PKVS_BF16: torch.bfloat16, PKVS_FP32: torch.float32}[d.dtype]
+        dt = _TORCH_DTYPES[d.dtype]
         # rows past the planned batch (capacity-sized buffers, e.g. under a
         # captured graph) are neither read nor written
         exp_q = (max(self._nnz_qo, q.shape[0] if q.dim() == 3 else 0), d.num_qo_heads, d.head_dim)
@@ -419,7 +421,7 @@ class CascadeAttention:
 
     def _check_shapes(self, q, k_extend, v_extend, k_cache, v_cache, kv_indices, out, lse):
         d = self.desc
-        dt = {PKVS_BF16: torch.bfloat16, PKVS_FP32: torch.float32}[d.dtype]
+        dt = _TORCH_DTYPES[d.dtype]
         rows = max(self._nnz_qo, q.shape[0] if q.dim() == 3 else 0)
         if tuple(q.shape) != (rows, d.num_qo_heads, d.head_dim) or q.dtype != dt:
             raise ValueError(f"q must be {dt} [>= {self._nnz_qo}, {d.num_qo_heads}, "

@@ -425,7 +425,7 @@ def test_run_rejects_mismatched_window_on_gpu():
 # ----------------------------------------------------------------- merge_state
 
 
-@pytest.mark.parametrize("dtype", [torch.bfloat16, torch.float32])
+@pytest.mark.parametrize("dtype", [torch.bfloat16, torch.float32, torch.float16])
 @pytest.mark.parametrize("H,D", [(64, 128), (128, 64), (128, 256), (8, 96)])
 def test_merge_state_against_oracle(dtype, H, D):
     g = torch.Generator(device=DEV).manual_seed(H * D)
@@ -638,7 +638,8 @@ def test_cascade_graph_replay_follows_replans():
 
 
 @pytest.mark.parametrize("dtype,H,D", [(torch.bfloat16, 8, 128), (torch.bfloat16, 1, 256),
-                                       (torch.float32, 2, 64), (torch.bfloat16, 3, 64)])
+                                       (torch.float32, 2, 64), (torch.bfloat16, 3, 64),
+                                       (torch.float16, 8, 128)])
 def test_append_kv_bit_exact(dtype, H, D):
     g = torch.Generator().manual_seed(H * D)
     pages, Psz = 40, 16
@@ -800,3 +801,57 @@ def test_soft_cap_fp32_and_cascade():
     (o, lse), _ = cascade_run(cas, trim=True)
     ro, rl = oracle_for(cas)
     compare(o, lse, ro, rl, tag="soft cap cascade")
+
+
+# ----------------------------------------------------------------- fp16 inputs
+# The dtype sweep of AMD-Ecosystem/flashinfer PR 234 ("Tests added") runs fp16
+# and bf16; the 16-bit kernels read IEEE half on the fp16 matrix instructions.
+
+
+@pytest.mark.parametrize("variant", [1, 2, 3, 4])
+@pytest.mark.parametrize("W", [-1, 0, 33])
+def test_fp16_prefill_variants(variant, W):
+    qo = [1, 70, 0, 33, 129, 5, 300]
+    kv = [1, 70, 9, 300, 129, 700, 301]
+    case = small(qo, kv, H_q=8, H_kv=2, D=128, P_=4, W=W, seed=700 + variant * 10 + W,
+                 dtype=torch.float16)
+    att = make_attention(case, prefill_variant=variant)
+    o, lse = gpu_run(case, att=att)
+    assert o.dtype == torch.float16 and att.info().prefill_variant == variant
+    ro, rl = oracle_for(case)
+    compare(o, lse, ro, rl, tag=f"fp16 prefill variant={variant} W={W}")
+
+
+@pytest.mark.parametrize("D,G", [(64, 8), (128, 4), (256, 1)])
+def test_fp16_prefill_head_shapes(D, G):
+    case = small([40, 130, 7], [90, 130, 500], H_q=2 * G, H_kv=2, D=D, P_=16, W=63,
+                 seed=D * G, dtype=torch.float16)
+    o, lse = gpu_run(case)
+    ro, rl = oracle_for(case)
+    compare(o, lse, ro, rl, tag=f"fp16 prefill D={D} G={G}")
+
+
+@pytest.mark.parametrize("D,G", [(64, 4), (128, 8), (256, 2)])
+@pytest.mark.parametrize("W,split", [(-1, 64), (127, -1), (0, -1)])
+def test_fp16_decode(D, G, W, split):
+    kv = [1, 300, 77, 2000, 64, 900]
+    case = small([1] * len(kv), kv, H_q=2 * G, H_kv=2, D=D, P_=16, W=W, seed=D + G + W,
+                 decode=True, split=split, dtype=torch.float16)
+    o, lse = gpu_run(case)
+    assert o.dtype == torch.float16
+    ro, rl = oracle_for(case)
+    compare(o, lse, ro, rl, tag=f"fp16 decode D={D} G={G} W={W} split={split}")
+
+
+def test_fp16_cascade_and_soft_cap():
+    case = small([40, 130, 7], [90, 130, 500], H_q=8, H_kv=2, D=128, P_=16, W=63, seed=77,
+                 dtype=torch.float16)
+    (o, lse), _ = cascade_run(case, trim=True)
+    ro, rl = oracle_for(case)
+    compare(o, lse, ro, rl, tag="fp16 cascade")
+    capped = small([70, 33], [70, 300], H_q=8, H_kv=2, D=128, P_=16, W=-1, seed=78,
+                   dtype=torch.float16, cap=3.0)
+    capped.sm_scale = 0.3
+    o, lse = gpu_run(capped)
+    ro, rl = oracle_for(capped)
+    compare(o, lse, ro, rl, tag="fp16 soft cap")

@@ -57,6 +57,7 @@ def err_code(fn):
     (dict(page_size=12), P.PKVS_ERR_UNSUPPORTED),
     (dict(causal=False, window_left=7), P.PKVS_ERR_UNSUPPORTED),
     (dict(num_qo_heads=3, num_kv_heads=1), P.PKVS_ERR_UNSUPPORTED),
+    (dict(num_qo_heads=3, num_kv_heads=1, dtype=torch.float16), P.PKVS_ERR_UNSUPPORTED),
     (dict(fixed_split_size=100), P.PKVS_ERR_INVALID_ARG),
     (dict(batch_capacity=0), P.PKVS_ERR_INVALID_ARG),
     (dict(prefill_variant=6), P.PKVS_ERR_INVALID_ARG),
