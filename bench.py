@@ -319,8 +319,8 @@ def ingest_counters(d: str) -> None:
     res = {"calibration": {"copy_bytes": COPY_BYTES,
                            "fetch_factor": round(cal["FETCH_SIZE"], 4),
                            "write_factor": round(cal["WRITE_SIZE"], 4)}}
-    for kind, kernels in (("prefill", ["prefill_bf16_kernel<128"]),
-                          ("decode", ["decode_bf16_kernel<128", "decode_merge_kernel<128"])):
+    for kind, kernels in (("prefill", ["prefill_kernel<128"]),
+                          ("decode", ["decode_kernel<128", "decode_merge_kernel<128"])):
         fm, wm = pass_means(kind, "FETCH_SIZE"), pass_means(kind, "WRITE_SIZE")
         for key in kernels:
             nf, nw = pick(fm, key), pick(wm, key)
@@ -543,9 +543,9 @@ def main():
         line["roofline"] = {"bound": "mfma", "achieved": round(tflops, 2),
                             "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
                             "frac": round(tflops / PEAK_BF16_TFLOPS, 4),
-                            "traffic": load_traffic("prefill_bf16_kernel<128>"),
+                            "traffic": load_traffic("prefill_kernel<128>"),
                             "algorithmic_bytes": prefill_algorithmic_bytes(pre),
-                            "kernel": "prefill_bf16_kernel<128>",
+                            "kernel": "prefill_kernel<128>",
                             "work_per_launch": flops}
     if "dec" in res:
         dec_ms, gbps, nbytes = res["dec"]
@@ -554,9 +554,9 @@ def main():
         line["roofline_decode"] = {"bound": "hbm", "achieved": round(gbps, 1),
                                    "peak": PEAK_HBM_GBPS, "unit": "GB/s",
                                    "frac": round(gbps / PEAK_HBM_GBPS, 4),
-                                   "traffic": load_traffic("decode_bf16_kernel<128>",
+                                   "traffic": load_traffic("decode_kernel<128>",
                                                            "decode_merge_kernel<128>"),
-                                   "kernel": "decode_bf16_kernel<128> + decode_merge_kernel<128>",
+                                   "kernel": "decode_kernel<128> + decode_merge_kernel<128>",
                                    "work_per_launch": nbytes}
     if full is not None:
         line["decode_no_window"] = full
