@@ -26,6 +26,8 @@ _lib = None
 BF16 = 0
 FP32 = 1
 FP16 = 2
+FP8_E4M3 = 3
+FP8_E5M2 = 4
 
 
 def compile_source(src: str, out: str) -> str:
@@ -55,8 +57,8 @@ class OracleLib:
         i32, i64, f64 = ctypes.c_int32, ctypes.c_int64, ctypes.c_double
         lib.oracle_paged_attention.restype = ctypes.c_int
         lib.oracle_paged_attention.argtypes = [
-            i32, P, P, P, P, i32, i32, i32, i32, i32, i32, f64, f64, i32, P, P, P, P, i64, i64,
-            i64, P, P,
+            i32, P, P, P, P, i32, i32, i32, i32, i32, i32, f64, f64, i32, P, i32, f64, f64, P, P,
+            P, i64, i64, i64, P, P,
         ]
         lib.oracle_merge_state.restype = None
         lib.oracle_merge_state.argtypes = [i64, i32, i32, P, P, P, P, P, P]
@@ -90,6 +92,10 @@ def _as_stored(t) -> tuple:
         return t.view(torch.int16).numpy(), BF16
     if t.dtype == torch.float16:
         return t.view(torch.int16).numpy(), FP16
+    if t.dtype == torch.float8_e4m3fn:
+        return t.view(torch.uint8).numpy(), FP8_E4M3
+    if t.dtype == torch.float8_e5m2:
+        return t.view(torch.uint8).numpy(), FP8_E5M2
     if t.dtype == torch.float32:
         return t.numpy(), FP32
     raise TypeError(f"oracle: unsupported input dtype {t.dtype}")
@@ -106,6 +112,7 @@ def _i32(t) -> np.ndarray:
 def paged_attention(q, k_cache, v_cache, qo_indptr, kv_indptr, kv_indices, kv_last_page_len, *,
                     num_qo_heads: int, num_kv_heads: int, head_dim: int, page_size: int,
                     causal: bool, window_left: int, sm_scale: float, soft_cap: float = 0.0,
+                    k_scale: float = 1.0, v_scale: float = 1.0,
                     rows: Optional[Sequence[int]] = None, key_lo: int = 0,
                     key_hi: int = np.iinfo(np.int64).max, impl: Optional[OracleLib] = None):
     """Reference (O, LSE) in float64.
@@ -119,8 +126,8 @@ def paged_attention(q, k_cache, v_cache, qo_indptr, kv_indptr, kv_indices, kv_la
     qa, qd = _as_stored(q)
     ka, kd = _as_stored(k_cache)
     va, vd = _as_stored(v_cache)
-    if not (qd == kd == vd):
-        raise TypeError("oracle: q, k and v must share one stored dtype")
+    if kd != vd:
+        raise TypeError("oracle: k and v caches must share one stored dtype")
     qo = _i32(qo_indptr)
     kvp = _i32(kv_indptr)
     kvi = _i32(kv_indices)
@@ -138,7 +145,7 @@ def paged_attention(q, k_cache, v_cache, qo_indptr, kv_indptr, kv_indices, kv_la
     rc = lib.oracle_paged_attention(
         batch, _ptr(qo), _ptr(kvp), _ptr(kvi), _ptr(last), page_size, num_qo_heads,
         num_kv_heads, head_dim, int(bool(causal)), window_left, float(sm_scale),
-        float(soft_cap), qd, _ptr(qa),
+        float(soft_cap), qd, _ptr(qa), kd, float(k_scale), float(v_scale),
         _ptr(ka), _ptr(va), rp, nr, int(key_lo), int(key_hi), _ptr(o), _ptr(lse))
     if rc != 0:
         raise ValueError(f"oracle_paged_attention: malformed layout (rc={rc})")
@@ -152,7 +159,8 @@ def case_attention(case, rows=None, window_left: Optional[int] = None, **kw):
         case.kv_last_page_len, num_qo_heads=case.num_qo_heads, num_kv_heads=case.num_kv_heads,
         head_dim=case.head_dim, page_size=case.page_size, causal=case.causal,
         window_left=case.window_left if window_left is None else window_left,
-        sm_scale=case.sm_scale, soft_cap=case.logits_soft_cap, rows=rows, **kw)
+        sm_scale=case.sm_scale, soft_cap=case.logits_soft_cap, k_scale=case.k_scale,
+        v_scale=case.v_scale, rows=rows, **kw)
 
 
 def merge_state(v_a, s_a, v_b, s_b, impl: Optional[OracleLib] = None):

@@ -30,6 +30,8 @@
 #define ORACLE_BF16 0
 #define ORACLE_FP32 1
 #define ORACLE_FP16 2
+#define ORACLE_FP8_E4M3 3
+#define ORACLE_FP8_E5M2 4
 
 /* Exact widening of one stored element to double.  bf16 is the upper half of
  * an IEEE binary32, so shifting its 16 bits up gives the same value.  An IEEE
@@ -54,6 +56,26 @@ static double load_elem(const void *base, int dtype, int64_t idx)
         else
             v = ldexp((double)(1024 + f), e - 25);
         return (h >> 15) ? -v : v;
+    }
+    if (dtype == ORACLE_FP8_E4M3 || dtype == ORACLE_FP8_E5M2) {
+        /* OCP 8-bit floats.  E4M3 ("fn"): exponent bias 7, subnormals
+         * f/8 * 2^-6, no infinities, S.1111.111 is NaN.  E5M2: the upper byte
+         * of an IEEE binary16 (bias 15, subnormals f/4 * 2^-14, inf/NaN at
+         * exponent 31). */
+        const uint8_t x = ((const uint8_t *)base)[idx];
+        const int e4 = dtype == ORACLE_FP8_E4M3;
+        const int mbits = e4 ? 3 : 2, bias = e4 ? 7 : 15;
+        const int e = (x & 0x7f) >> mbits, f = x & ((1 << mbits) - 1);
+        double v;
+        if (e4 && e == 15 && f == 7)
+            v = NAN;
+        else if (!e4 && e == 31)
+            v = f ? NAN : INFINITY;
+        else if (e == 0)
+            v = ldexp((double)f, 1 - bias - mbits);
+        else
+            v = ldexp((double)((1 << mbits) + f), e - bias - mbits);
+        return (x & 0x80) ? -v : v;
     }
     return (double)((const float *)base)[idx];
 }
@@ -124,6 +146,10 @@ static int key_visible(int64_t j, int64_t p, int32_t causal, int32_t window_left
  *  Query head h reads KV head h / (H_q / H_kv) (grouped-query heads share
  *  contiguous groups).
  *
+ *  Keys and values are read as k_scale * k and v_scale * v from a cache of
+ *  type kv_dtype ([FIB] forward_extend / forward_decode pass k_scale and
+ *  v_scale with the cache; an 8-bit cache holds K / k_scale and V / v_scale).
+ *
  *  s_j   = sm_scale * sum_d q[d] * k_j[d]                for visible j
  *  s_j  <- soft_cap * tanh(s_j / soft_cap)   when soft_cap > 0 (the logits
  *          soft cap [FIB] forward_extend / forward_decode pass to the
@@ -147,6 +173,7 @@ int oracle_paged_attention(int32_t batch, const int32_t *qo_indptr, const int32_
                            int32_t page_size, int32_t num_qo_heads, int32_t num_kv_heads,
                            int32_t head_dim, int32_t causal, int32_t window_left,
                            double sm_scale, double soft_cap, int32_t in_dtype, const void *q,
+                           int32_t kv_dtype, double k_scale, double v_scale,
                            const void *k_cache, const void *v_cache, const int64_t *rows,
                            int64_t n_rows, int64_t key_lo, int64_t key_hi, double *o,
                            double *lse)
@@ -200,7 +227,8 @@ int oracle_paged_attention(int32_t batch, const int32_t *qo_indptr, const int32_
                                                 head_dim, b, j, hk);
                 double dot = 0.0;
                 for (int32_t d = 0; d < head_dim; ++d)
-                    dot += load_elem(q, in_dtype, qoff + d) * load_elem(k_cache, in_dtype, koff + d);
+                    dot += load_elem(q, in_dtype, qoff + d) *
+                           (k_scale * load_elem(k_cache, kv_dtype, koff + d));
                 s[j] = sm_scale * dot;
                 if (soft_cap > 0.0)
                     s[j] = soft_cap * tanh(s[j] / soft_cap);
@@ -220,7 +248,7 @@ int oracle_paged_attention(int32_t batch, const int32_t *qo_indptr, const int32_
                     const int64_t voff = key_offset(kv_indptr, kv_indices, page_size,
                                                     num_kv_heads, head_dim, b, j, hk);
                     for (int32_t d = 0; d < head_dim; ++d)
-                        acc[d] += w * load_elem(v_cache, in_dtype, voff + d);
+                        acc[d] += w * (v_scale * load_elem(v_cache, kv_dtype, voff + d));
                 }
             }
             double *orow = o + ooff;

@@ -68,6 +68,8 @@ class Case:
     fixed_split_size: int = -1
     is_decode: bool = False
     logits_soft_cap: float = 0.0  # 0: no cap
+    k_scale: float = 1.0          # the cache holds K / k_scale and V / v_scale
+    v_scale: float = 1.0
 
     @property
     def batch_size(self) -> int:
@@ -148,12 +150,17 @@ def case_from_lengths(
     value_gen: Optional[torch.Generator] = None,
     perm_gen: Optional[torch.Generator] = None,
     logits_soft_cap: float = 0.0,
+    kv_dtype: Optional[torch.dtype] = None,
+    k_scale: float = 1.0,
+    v_scale: float = 1.0,
 ) -> Case:
     """Build a paged batch for explicit lengths.
 
     Page placement and values are drawn from generators seeded with ``seed``
     (page permutation on the CPU, values on ``device``).  ``spare_pages``
-    extra pool pages are allocated and left unused (NaN-poisoned).
+    extra pool pages are allocated and left unused (NaN-poisoned).  With an
+    8-bit ``kv_dtype`` the caches hold the N(0,1) keys and values divided by
+    ``k_scale`` / ``v_scale``, rounded to that type (torch's conversion).
     """
     B = len(kv_lens)
     assert len(qo_lens) == B
@@ -176,7 +183,9 @@ def case_from_lengths(
     if value_gen is None:
         value_gen = torch.Generator(device=device).manual_seed(seed + 1_000_003)
     q = torch.empty(nnz_qo, num_qo_heads, head_dim, dtype=dtype, device=device)
-    k_cache = torch.empty(max(pool, 1), P, num_kv_heads, head_dim, dtype=dtype, device=device)
+    cache_dtype = dtype if kv_dtype is None else torch.float32
+    k_cache = torch.empty(max(pool, 1), P, num_kv_heads, head_dim, dtype=cache_dtype,
+                          device=device)
     v_cache = torch.empty_like(k_cache)
     _fill_normal(q, value_gen)
     _fill_normal(k_cache, value_gen)
@@ -198,6 +207,9 @@ def case_from_lengths(
                 k_cache[pg, int(last[b]):].fill_(float("nan"))
                 v_cache[pg, int(last[b]):].fill_(float("nan"))
 
+    if kv_dtype is not None:
+        k_cache = (k_cache / k_scale).to(kv_dtype)
+        v_cache = (v_cache / v_scale).to(kv_dtype)
     if sm_scale is None:
         sm_scale = 1.0 / math.sqrt(head_dim)
     return Case(
@@ -222,6 +234,8 @@ def case_from_lengths(
         fixed_split_size=fixed_split_size,
         is_decode=is_decode,
         logits_soft_cap=float(logits_soft_cap),
+        k_scale=float(k_scale),
+        v_scale=float(v_scale),
     )
 
 

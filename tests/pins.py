@@ -28,7 +28,7 @@ import torch
 
 import oracle
 from oracle import dense
-from paged_kv_sliding_amd.synth import case_from_lengths
+from paged_kv_sliding_amd.synth import case_from_lengths  # noqa: F401 (also used directly)
 
 GOLDEN = os.path.join(os.path.dirname(os.path.abspath(__file__)), "golden")
 
@@ -381,6 +381,38 @@ def check_merge_algebra(impl=None):
 # --------------------------------------------------------------------------- input widening
 
 
+def check_widening_every_8_bit_pattern(impl=None):
+    """Every OCP e4m3 ("fn") and e5m2 byte widens to the float64 torch's
+    float8 types give (NaN to NaN, e5m2 infinities to infinities)."""
+    bits = torch.arange(256, dtype=torch.int32).to(torch.uint8)
+    for dt in (torch.float8_e4m3fn, torch.float8_e5m2):
+        got = oracle.widen(bits.view(dt), impl=impl)
+        want = bits.view(dt).to(torch.float64).numpy()
+        assert np.array_equal(got, want, equal_nan=True), dt
+
+
+def check_kv_scales(impl=None):
+    """An 8-bit cache with scales reads as k_scale * k, v_scale * v: with
+    power-of-two scales the oracle equals the oracle on an fp32 cache holding
+    those products (exact), and for any scale k_scale moves into sm_scale
+    and v_scale multiplies the output."""
+    for dt in (torch.float8_e4m3fn, torch.float8_e5m2):
+        case = case_from_lengths("pin8", [3, 5], [9, 5], num_qo_heads=4, num_kv_heads=2,
+                                 head_dim=16, page_size=4, dtype=torch.float32, window_left=4,
+                                 seed=12, spare_pages=2, kv_dtype=dt, k_scale=0.125,
+                                 v_scale=4.0)
+        o, lse = run(case, impl)
+        wide = dataclasses.replace(case, k_cache=case.k_cache.float() * 0.125,
+                                   v_cache=case.v_cache.float() * 4.0, k_scale=1.0, v_scale=1.0)
+        o2, l2 = run(wide, impl)
+        assert np.array_equal(o, o2, equal_nan=True) and np.array_equal(lse, l2), dt
+        odd = dataclasses.replace(case, k_scale=0.37, v_scale=1.9)
+        o3, l3 = run(odd, impl)
+        ref = dataclasses.replace(case, k_scale=1.0, v_scale=1.0, sm_scale=case.sm_scale * 0.37)
+        o4, l4 = run(ref, impl)
+        assert close(l3, l4) and close(o3, 1.9 * o4), dt
+
+
 def check_widening_every_16_bit_pattern(impl=None):
     """Every bf16 and every IEEE half bit pattern widens to the float64 that
     torch's / numpy's own conversions give (NaN patterns to NaN); fp32 values
@@ -563,6 +595,8 @@ ALL_CHECKS = [
     check_empty_sets,
     check_decode_trim,
     check_widening_every_16_bit_pattern,
+    check_widening_every_8_bit_pattern,
+    check_kv_scales,
     check_soft_cap_brute_force,
     check_soft_cap_saturation,
     check_soft_cap_large_is_no_cap,

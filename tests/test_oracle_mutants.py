@@ -30,8 +30,8 @@ MUTANTS = {
                    "kv_indices[(int64_t)kv_indptr[b] + j / page_size / 2]"),
     "last_page_ignored": ("return (npages - 1) * (int64_t)page_size + kv_last_page_len[b];",
                           "return npages * (int64_t)page_size;"),
-    "values_from_keys": ("acc[d] += w * load_elem(v_cache, in_dtype, voff + d);",
-                         "acc[d] += w * load_elem(k_cache, in_dtype, voff + d);"),
+    "values_from_keys": ("acc[d] += w * (v_scale * load_elem(v_cache, kv_dtype, voff + d));",
+                         "acc[d] += w * (v_scale * load_elem(k_cache, kv_dtype, voff + d));"),
     "empty_lse_zero": ("lse[out_row * num_qo_heads + h] = -INFINITY;",
                        "lse[out_row * num_qo_heads + h] = 0.0;"),
     "merge_weight_sign": ("const double wa = exp(a - s), wb = exp(b - s);",
@@ -42,6 +42,14 @@ MUTANTS = {
     "half_exponent_bias": ("v = ldexp((double)(1024 + f), e - 25);",
                            "v = ldexp((double)(1024 + f), e - 24);"),
     "half_subnormal_scale": ("v = ldexp((double)f, -24);", "v = ldexp((double)f, -25);"),
+    "k_scale_dropped": ("(k_scale * load_elem(k_cache, kv_dtype, koff + d))",
+                        "(load_elem(k_cache, kv_dtype, koff + d))"),
+    "v_scale_on_keys": ("(k_scale * load_elem(k_cache, kv_dtype, koff + d))",
+                        "(v_scale * load_elem(k_cache, kv_dtype, koff + d))"),
+    "fp8_bias": ("const int mbits = e4 ? 3 : 2, bias = e4 ? 7 : 15;",
+                 "const int mbits = e4 ? 3 : 2, bias = e4 ? 8 : 15;"),
+    "fp8_subnormal_scale": ("v = ldexp((double)f, 1 - bias - mbits);",
+                            "v = ldexp((double)f, -bias - mbits);"),
     "cap_of_unscaled_logit": ("s[j] = soft_cap * tanh(s[j] / soft_cap);",
                               "s[j] = soft_cap * tanh(dot / soft_cap);"),
     "cap_factor_dropped": ("s[j] = soft_cap * tanh(s[j] / soft_cap);",
