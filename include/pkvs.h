@@ -74,6 +74,16 @@ typedef enum pkvs_status {
 
 typedef enum pkvs_dtype { PKVS_BF16 = 0, PKVS_FP32 = 1, PKVS_FP16 = 2 } pkvs_dtype;
 
+/* Storage of the K/V cache: the plan's dtype, or OCP 8-bit floats (e4m3,
+ * "float8_e4m3fn"; e5m2) holding K / k_scale and V / v_scale ([FIB]
+ * forward_extend / forward_decode pass k_scale and v_scale with the cache;
+ * should_use_tensor_core names both 8-bit cache types). */
+typedef enum pkvs_kv_format {
+    PKVS_KV_SAME = 0,
+    PKVS_KV_FP8_E4M3 = 1,
+    PKVS_KV_FP8_E5M2 = 2
+} pkvs_kv_format;
+
 typedef enum pkvs_kind { PKVS_PREFILL = 0, PKVS_DECODE = 1, PKVS_CASCADE = 2 } pkvs_kind;
 
 /* Fixed properties of a plan.  window_left and causal are fixed here, at plan
@@ -106,6 +116,11 @@ typedef enum pkvs_kind { PKVS_PREFILL = 0, PKVS_DECODE = 1, PKVS_CASCADE = 2 } p
  *  qo_capacity      prefill, cascade: largest total number of query tokens
  *  kv_capacity      largest kv_len of one request (cascade: the most cached
  *                   keys one request's page table may hold)
+ *  kv_format        PKVS_KV_SAME (k_cache / v_cache in dtype) or an 8-bit
+ *                   format (dtype bf16 or fp16 only; widened exactly to dtype
+ *                   on the way to the matrix cores; prefill variants 1 and 2,
+ *                   the planner picks one).  A cascade's new-token K/V stay in
+ *                   dtype; only its cache is 8-bit.
  *  logits_soft_cap  0 (off) or c > 0: every logit x = sm_scale * q.k becomes
  *                   c * tanh(x / c) before the softmax and the LSE ([FIB]
  *                   forward_extend / forward_decode pass logits_soft_cap to
@@ -130,6 +145,7 @@ typedef struct pkvs_desc {
     int64_t qo_capacity;
     int64_t kv_capacity;
     float logits_soft_cap;
+    int32_t kv_format;
 } pkvs_desc;
 
 /* Read-only facts about a plan (for callers, tests and profilers). */
@@ -177,11 +193,14 @@ int pkvs_prefill_plan(pkvs_plan *plan, const int32_t *qo_indptr_h, const int32_t
  * k_cache/v_cache hold num_pages pages; kv_indices_d (device, int32) holds
  * kv_indptr_h[batch] page ids in [0, num_pages).  window_left and causal must
  * equal the plan's (PLAN_MISMATCH otherwise, [PR31501] "What").  The exact
- * per-element window mask is always applied. */
+ * per-element window mask is always applied.  Keys and values are read as
+ * k_scale * k and v_scale * v (positive finite; 1 for an unscaled cache;
+ * INVALID_ARG otherwise), k_scale folded into the logit scale and v_scale
+ * into the output normalisation, for every cache type. */
 int pkvs_prefill_run(const pkvs_plan *plan, const void *q, const void *k_cache,
                      const void *v_cache, int64_t num_pages, const int32_t *kv_indices_d,
                      void *o, float *lse, float sm_scale, int32_t window_left, int32_t causal,
-                     hipStream_t stream);
+                     float k_scale, float v_scale, hipStream_t stream);
 
 /* Plan a single-token decode batch (one query per request, at kv_len-1).
  * The window keeps the last min(kv_len, W+1) keys of each request ([FIB]
@@ -196,11 +215,11 @@ int pkvs_decode_plan(pkvs_plan *plan, const int32_t *kv_indptr_h,
 /* Run the planned decode: q, o [batch, num_qo_heads, head_dim], lse
  * [batch, num_qo_heads] (nullable).  Launches the chunk kernel and, when
  * some request was split, the merge of its chunk partials.  window_left must
- * equal the plan's. */
+ * equal the plan's; k_scale / v_scale as pkvs_prefill_run. */
 int pkvs_decode_run(const pkvs_plan *plan, const void *q, const void *k_cache,
                     const void *v_cache, int64_t num_pages, const int32_t *kv_indices_d,
-                    void *o, float *lse, float sm_scale, int32_t window_left,
-                    hipStream_t stream);
+                    void *o, float *lse, float sm_scale, int32_t window_left, float k_scale,
+                    float v_scale, hipStream_t stream);
 
 /* Plan a cascade prefill ([FIB] FlashInferAttnBackend.forward_extend, the
  * branch for a batch with cached prefixes: a ragged pass over the new tokens'
@@ -238,11 +257,13 @@ int pkvs_cascade_plan(pkvs_plan *plan, const int32_t *qo_indptr_h, const int32_t
  * nullable.  Two launches on `stream`: the paged pass writes its (o, lse) into
  * float_ws, then the ragged pass stores the merge_state combine of its own
  * (o, lse) with them into o and lse (the merge runs in its epilogue).
- * window_left must equal the plan's. */
+ * window_left must equal the plan's.  k_scale / v_scale apply to the cache
+ * (as pkvs_prefill_run); the new tokens' K/V are read unscaled. */
 int pkvs_cascade_run(const pkvs_plan *plan, const void *q, const void *k_extend,
                      const void *v_extend, const void *k_cache, const void *v_cache,
                      int64_t num_pages, const int32_t *kv_indices_d, void *o, float *lse,
-                     float sm_scale, int32_t window_left, hipStream_t stream);
+                     float sm_scale, int32_t window_left, float k_scale, float v_scale,
+                     hipStream_t stream);
 
 /* Combine two attention partials over disjoint key sets ([FIB]
  * _safe_merge_state):  s = ln(exp(s_a) + exp(s_b)),

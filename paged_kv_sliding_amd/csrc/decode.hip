@@ -30,6 +30,8 @@
 //
 // A chunk of a split request writes its fp32 partial (o normalised by its own
 // sum, lse) to a slot of the float workspace; decode_merge combines them.
+#include <type_traits>
+
 #include "device_common.h"
 #include "pkvs_internal.h"
 
@@ -44,13 +46,28 @@ __device__ __forceinline__ bf16x8 load_stream(const void *p)
     return __builtin_bit_cast(bf16x8, __builtin_nontemporal_load(reinterpret_cast<const u32x4 *>(p)));
 }
 
-template <int D>
+__device__ __forceinline__ u32x2 load_stream8(const void *p)
+{
+    return __builtin_nontemporal_load(reinterpret_cast<const u32x2 *>(p));
+}
+
+// Loaded K/V of one 32-key block, as stored: 8 elements per slot (16 bytes of
+// a 16-bit cache, 8 bytes of an 8-bit one, widened where they are used).
+template <int D, int KVF>
 struct DecodeBuf {
     static constexpr int KS = D / 32;            // QK k-steps (32 dims each)
     static constexpr int NV = D >= 128 ? D / 128 : 1;
-    bf16x8 k0[KS], k1[KS];                       // keys blk+r, blk+16+r
-    bf16x8 v[NV][8];                             // 8 keys x 8 dims per 128-dim chunk
+    using Raw = typename std::conditional<KVF == 0, bf16x8, u32x2>::type;
+    Raw k0[KS], k1[KS];                          // keys blk+r, blk+16+r
+    Raw v[NV][8];                                // 8 keys x 8 dims per 128-dim chunk
 };
+
+template <bool F16, int KVF>
+__device__ __forceinline__ bf16x8 widen_slot(const typename DecodeBuf<64, KVF>::Raw &x)
+{
+    if constexpr (KVF == 0) return x;
+    else return widen_fp8<KVF, F16>(x);
+}
 
 // Page ids of a request, 64 pages at a time: lane L holds the id of page
 // base + L (cur) and of page base + 64 + L (nxt, prefetched a window ahead).
@@ -107,15 +124,17 @@ __device__ __forceinline__ int64_t window_page_uniform(const DecodeArgs &a, cons
     return clamp_page(a, __builtin_amdgcn_readlane(pw.cur, idx & 63));
 }
 
-template <int D>
-__device__ __forceinline__ void decode_load(DecodeBuf<D> &buf, const DecodeArgs &a,
+template <int D, int KVF>
+__device__ __forceinline__ void decode_load(DecodeBuf<D, KVF> &buf, const DecodeArgs &a,
                                             PageWindow &pw, int blk, int t1, int hk, int lane)
 {
-    constexpr int KS = DecodeBuf<D>::KS, NV = DecodeBuf<D>::NV;
+    using Buf = DecodeBuf<D, KVF>;
+    constexpr int KS = Buf::KS, NV = Buf::NV;
+    using Elem = typename std::conditional<KVF == 0, uint16_t, uint8_t>::type;
     const int r = lane & 15, g = lane >> 4;
     const int P = a.page_size;
-    const uint16_t *K = static_cast<const uint16_t *>(a.k);
-    const uint16_t *V = static_cast<const uint16_t *>(a.v);
+    const Elem *K = static_cast<const Elem *>(a.k);
+    const Elem *V = static_cast<const Elem *>(a.v);
     const int last = t1 - 1;
     // blocks past the end read the request's last key; the window never moves
     // past its page
@@ -150,10 +169,14 @@ __device__ __forceinline__ void decode_load(DecodeBuf<D> &buf, const DecodeArgs 
             rv[j] = nhd_offset(window_page(a, pw, t), t & (P - 1), P, hk, a.num_kv_heads, D);
         }
     }
+    auto load = [](const Elem *p) __attribute__((always_inline)) {
+        if constexpr (KVF == 0) return load_stream(p);
+        else return load_stream8(p);
+    };
 #pragma unroll
     for (int s = 0; s < KS; ++s) {
-        buf.k0[s] = load_stream(K + rk0 + 32 * s + 8 * g);
-        buf.k1[s] = load_stream(K + rk1 + 32 * s + 8 * g);
+        buf.k0[s] = load(K + rk0 + 32 * s + 8 * g);
+        buf.k1[s] = load(K + rk1 + 32 * s + 8 * g);
     }
     // (D = 64: lanes r >= 8 read a valid slice of the row and drop it)
     const int dv = min(8 * r, D - 8);
@@ -161,30 +184,31 @@ __device__ __forceinline__ void decode_load(DecodeBuf<D> &buf, const DecodeArgs 
     for (int u = 0; u < NV; ++u)
 #pragma unroll
         for (int j = 0; j < 8; ++j) {
-            const bf16x8 x = load_stream(V + rv[j] + 128 * u + dv);
-            buf.v[u][j] = (8 * r + 128 * u < D) ? x : zero_bf16x8();
+            const typename Buf::Raw x = load(V + rv[j] + 128 * u + dv);
+            const typename Buf::Raw z = {};
+            buf.v[u][j] = (8 * r + 128 * u < D) ? x : z;
         }
 }
 
 template <int D>
 struct DecodeState {
-    static constexpr int NV = DecodeBuf<D>::NV;
+    static constexpr int NV = DecodeBuf<D, 0>::NV;
     float m, l;
     f32x4 o[NV][8];
 };
 
-template <int D, bool F16>
-__device__ __forceinline__ void decode_compute(const DecodeBuf<D> &buf, DecodeState<D> &st,
+template <int D, bool F16, int KVF>
+__device__ __forceinline__ void decode_compute(const DecodeBuf<D, KVF> &buf, DecodeState<D> &st,
                                                const bf16x8 (&qf)[D / 32], int blk, int lo,
                                                int t1, float scale_log2, float cap_a, int lane)
 {
-    constexpr int KS = DecodeBuf<D>::KS, NV = DecodeBuf<D>::NV;
+    constexpr int KS = DecodeBuf<D, KVF>::KS, NV = DecodeBuf<D, KVF>::NV;
     const int g = lane >> 4;
     f32x4 s0 = {0.f, 0.f, 0.f, 0.f}, s1 = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
     for (int s = 0; s < KS; ++s) {
-        s0 = mfma16x16x32<F16>(buf.k0[s], qf[s], s0);
-        s1 = mfma16x16x32<F16>(buf.k1[s], qf[s], s1);
+        s0 = mfma16x16x32<F16>(widen_slot<F16, KVF>(buf.k0[s]), qf[s], s0);
+        s1 = mfma16x16x32<F16>(widen_slot<F16, KVF>(buf.k1[s]), qf[s], s1);
     }
     // lane holds keys blk+4g+i (s0[i]) and blk+16+4g+i (s1[i]) of head lane%16
     float x[8];
@@ -227,11 +251,14 @@ __device__ __forceinline__ void decode_compute(const DecodeBuf<D> &buf, DecodeSt
     const bf16x8 pb = to16x8<F16>(pv);
 #pragma unroll
     for (int u = 0; u < NV; ++u) {
+        bf16x8 vrow[8];
+#pragma unroll
+        for (int j = 0; j < 8; ++j) vrow[j] = widen_slot<F16, KVF>(buf.v[u][j]);
 #pragma unroll
         for (int e = 0; e < 8; ++e) {
             bf16x8 va;
 #pragma unroll
-            for (int j = 0; j < 8; ++j) va[j] = buf.v[u][j][e];
+            for (int j = 0; j < 8; ++j) va[j] = vrow[j][e];
             st.o[u][e] = mfma16x16x32<F16>(va, pb, st.o[u][e] * alpha);
         }
     }
@@ -245,10 +272,10 @@ constexpr int decode_stages() { return D >= 256 ? 2 : 3; }
 
 // NS register buffers of 32 keys each: NS-1 blocks are in flight while one is
 // being computed.
-template <int D, int NS, bool F16>
+template <int D, int NS, bool F16, int KVF>
 __global__ __launch_bounds__(kDecodeThreads) void decode_kernel(DecodeArgs a)
 {
-    constexpr int KS = D / 32, NV = DecodeBuf<D>::NV;
+    constexpr int KS = D / 32, NV = DecodeBuf<D, KVF>::NV;
     const int lane = threadIdx.x;
     const int r = lane & 15, g = lane >> 4;
     const int G = 1 << a.log2_group;
@@ -284,20 +311,20 @@ __global__ __launch_bounds__(kDecodeThreads) void decode_kernel(DecodeArgs a)
             pw.last_pg = (t1 - 1) >> a.log2_page;
             pw.cur = load_page_id(a, pw, pw.base + lane);
             pw.nxt = load_page_id(a, pw, pw.base + 64 + lane);
-            DecodeBuf<D> buf[NS];
+            DecodeBuf<D, KVF> buf[NS];
             // blocks past the end load the request's last key (clamped) and
             // are never computed
 #pragma unroll
             for (int s = 0; s + 1 < NS; ++s)
-                decode_load<D>(buf[s], a, pw, t0 + kDecodeBlock * s, t1, hk, lane);
+                decode_load<D, KVF>(buf[s], a, pw, t0 + kDecodeBlock * s, t1, hk, lane);
             int blk = t0;
             bool done = false;
             while (!done) {
 #pragma unroll
                 for (int s = 0; s < NS; ++s) {
-                    decode_load<D>(buf[(s + NS - 1) % NS], a, pw, blk + kDecodeBlock * (NS - 1),
+                    decode_load<D, KVF>(buf[(s + NS - 1) % NS], a, pw, blk + kDecodeBlock * (NS - 1),
                                    t1, hk, lane);
-                    decode_compute<D, F16>(buf[s], st, qf, blk, lo, t1, a.scale_log2, a.cap_a, lane);
+                    decode_compute<D, F16, KVF>(buf[s], st, qf, blk, lo, t1, a.scale_log2, a.cap_a, lane);
                     blk += kDecodeBlock;
                     if (blk >= t1) {
                         done = true;
@@ -311,7 +338,7 @@ __global__ __launch_bounds__(kDecodeThreads) void decode_kernel(DecodeArgs a)
         float l = st.l;
         l += __shfl_xor(l, 16);
         l += __shfl_xor(l, 32);
-        const float inv = l > 0.f ? 1.f / l : 0.f;
+        const float inv = l > 0.f ? a.v_scale / l : 0.f;
         const float lse = l > 0.f ? (st.m + fast_log2(l)) * kLn2 : kNegInf;
         if (r < G) {
             // O^T accumulator: lane (head r, group g) holds dims 128u+32g+8i+e
@@ -400,23 +427,41 @@ __global__ __launch_bounds__(kMergeThreads) void decode_merge_kernel(DecodeArgs 
 
 }  // namespace
 
-template <bool F16>
+template <bool F16, int KVF>
 static hipError_t launch_decode_t(const DecodeArgs &a, int head_dim, int grid, hipStream_t s)
 {
     switch (head_dim) {
-    case 64: decode_kernel<64, decode_stages<64>(), F16><<<grid, kDecodeThreads, 0, s>>>(a); break;
-    case 128: decode_kernel<128, decode_stages<128>(), F16><<<grid, kDecodeThreads, 0, s>>>(a); break;
-    case 256: decode_kernel<256, decode_stages<256>(), F16><<<grid, kDecodeThreads, 0, s>>>(a); break;
+    case 64:
+        decode_kernel<64, decode_stages<64>(), F16, KVF><<<grid, kDecodeThreads, 0, s>>>(a);
+        break;
+    case 128:
+        decode_kernel<128, decode_stages<128>(), F16, KVF><<<grid, kDecodeThreads, 0, s>>>(a);
+        break;
+    case 256:
+        decode_kernel<256, decode_stages<256>(), F16, KVF><<<grid, kDecodeThreads, 0, s>>>(a);
+        break;
     default: return hipErrorInvalidValue;
     }
     return hipGetLastError();
 }
 
-hipError_t launch_decode_16bit(const DecodeArgs &a, int head_dim, bool f16, int grid,
-                               hipStream_t s)
+template <bool F16>
+static hipError_t launch_decode_f(const DecodeArgs &a, int head_dim, int kv_format, int grid,
+                                  hipStream_t s)
 {
-    return f16 ? launch_decode_t<true>(a, head_dim, grid, s)
-               : launch_decode_t<false>(a, head_dim, grid, s);
+    switch (kv_format) {
+    case 0: return launch_decode_t<F16, 0>(a, head_dim, grid, s);
+    case PKVS_KV_FP8_E4M3: return launch_decode_t<F16, 1>(a, head_dim, grid, s);
+    case PKVS_KV_FP8_E5M2: return launch_decode_t<F16, 2>(a, head_dim, grid, s);
+    default: return hipErrorInvalidValue;
+    }
+}
+
+hipError_t launch_decode_16bit(const DecodeArgs &a, int head_dim, bool f16, int kv_format,
+                               int grid, hipStream_t s)
+{
+    return f16 ? launch_decode_f<true>(a, head_dim, kv_format, grid, s)
+               : launch_decode_f<false>(a, head_dim, kv_format, grid, s);
 }
 
 template <bool F16>
@@ -438,7 +483,7 @@ hipError_t launch_decode_merge(const DecodeArgs &a, int head_dim, bool f16, int 
                : launch_merge_t<false>(a, head_dim, grid, s);
 }
 
-template <bool F16>
+template <bool F16, int KVF>
 static int decode_blocks_per_cu_t(int head_dim)
 {
     int n = 0;
@@ -446,23 +491,35 @@ static int decode_blocks_per_cu_t(int head_dim)
     switch (head_dim) {
     case 64:
         e = hipOccupancyMaxActiveBlocksPerMultiprocessor(
-            &n, decode_kernel<64, decode_stages<64>(), F16>, kDecodeThreads, 0);
+            &n, decode_kernel<64, decode_stages<64>(), F16, KVF>, kDecodeThreads, 0);
         break;
     case 128:
         e = hipOccupancyMaxActiveBlocksPerMultiprocessor(
-            &n, decode_kernel<128, decode_stages<128>(), F16>, kDecodeThreads, 0);
+            &n, decode_kernel<128, decode_stages<128>(), F16, KVF>, kDecodeThreads, 0);
         break;
     case 256:
         e = hipOccupancyMaxActiveBlocksPerMultiprocessor(
-            &n, decode_kernel<256, decode_stages<256>(), F16>, kDecodeThreads, 0);
+            &n, decode_kernel<256, decode_stages<256>(), F16, KVF>, kDecodeThreads, 0);
         break;
     }
     return e == hipSuccess ? n : 0;
 }
 
-int decode_blocks_per_cu(int head_dim, bool f16)
+template <bool F16>
+static int decode_blocks_per_cu_f(int head_dim, int kv_format)
 {
-    return f16 ? decode_blocks_per_cu_t<true>(head_dim) : decode_blocks_per_cu_t<false>(head_dim);
+    switch (kv_format) {
+    case 0: return decode_blocks_per_cu_t<F16, 0>(head_dim);
+    case PKVS_KV_FP8_E4M3: return decode_blocks_per_cu_t<F16, 1>(head_dim);
+    case PKVS_KV_FP8_E5M2: return decode_blocks_per_cu_t<F16, 2>(head_dim);
+    default: return 0;
+    }
+}
+
+int decode_blocks_per_cu(int head_dim, bool f16, int kv_format)
+{
+    return f16 ? decode_blocks_per_cu_f<true>(head_dim, kv_format)
+               : decode_blocks_per_cu_f<false>(head_dim, kv_format);
 }
 
 }  // namespace pkvs

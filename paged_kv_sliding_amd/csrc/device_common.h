@@ -117,6 +117,31 @@ __device__ __forceinline__ f32x4 from16x4(bf16x4 v)
     else return __builtin_convertvector(v, f32x4);
 }
 
+// Eight OCP 8-bit floats (KVF 1: e4m3, 2: e5m2) packed in two dwords, byte j
+// = element j, widened exactly to fp32 and then to the 16-bit type (also
+// exact: every e4m3 and e5m2 value is a bf16 and a half).
+template <int KVF, bool F16>
+__device__ __forceinline__ bf16x8 widen_fp8(u32x2 raw)
+{
+    f32x8 f;
+#pragma unroll
+    for (int w = 0; w < 2; ++w) {
+        f32x2 lo, hi;
+        if constexpr (KVF == 1) {
+            lo = __builtin_amdgcn_cvt_pk_f32_fp8(int(raw[w]), false);
+            hi = __builtin_amdgcn_cvt_pk_f32_fp8(int(raw[w]), true);
+        } else {
+            lo = __builtin_amdgcn_cvt_pk_f32_bf8(int(raw[w]), false);
+            hi = __builtin_amdgcn_cvt_pk_f32_bf8(int(raw[w]), true);
+        }
+        f[4 * w] = lo[0];
+        f[4 * w + 1] = lo[1];
+        f[4 * w + 2] = hi[0];
+        f[4 * w + 3] = hi[1];
+    }
+    return to16x8<F16>(f);
+}
+
 __device__ __forceinline__ bf16x8 load_bf16x8(const void *p)
 {
     return *reinterpret_cast<const bf16x8 *>(p);

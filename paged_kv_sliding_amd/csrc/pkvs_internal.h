@@ -87,6 +87,7 @@ struct PrefillArgs {
     int64_t num_pages;
     float scale_log2;   // sm_scale * log2(e), or cap * log2(e) with a soft cap
     float cap_a;        // soft cap: 2 log2(e) sm_scale / cap (soft_cap_unit), 0 = none
+    float v_scale;      // values are read as v_scale * v (k_scale is in scale_log2 / cap_a)
     int32_t num_qo_heads, num_kv_heads, log2_group, page_size, log2_page;
     int32_t page_rows;  // cache rows one page-table step spans: page_size, or 1 (ragged)
     int32_t window_left, causal;
@@ -108,16 +109,18 @@ struct DecodeArgs {
     int64_t num_pages;
     float scale_log2;   // as PrefillArgs
     float cap_a;
+    float v_scale;
     int32_t num_qo_heads, num_kv_heads, log2_group, page_size, log2_page;
 };
 
 // Launchers (return hipError_t of the launch).
-// 16-bit paths: bf16, or IEEE half when f16
+// 16-bit paths: bf16, or IEEE half when f16; K/V in the same type (kv_format
+// 0) or 8-bit (PKVS_KV_FP8_E4M3 / _E5M2: register-staged prefill variants only)
 hipError_t launch_prefill_16bit(const PrefillArgs &a, int head_dim, int variant, bool f16,
-                                int grid, hipStream_t s);
+                                int kv_format, int grid, hipStream_t s);
 hipError_t launch_attention_fp32(const PrefillArgs &a, int head_dim, int grid, hipStream_t s);
-hipError_t launch_decode_16bit(const DecodeArgs &a, int head_dim, bool f16, int grid,
-                               hipStream_t s);
+hipError_t launch_decode_16bit(const DecodeArgs &a, int head_dim, bool f16, int kv_format,
+                               int grid, hipStream_t s);
 hipError_t launch_decode_merge(const DecodeArgs &a, int head_dim, bool f16, int grid,
                                hipStream_t s);
 hipError_t launch_merge_state(const void *va, const float *sa, const void *vb, const float *sb,
@@ -134,7 +137,7 @@ hipError_t launch_build_kv_indices(const int32_t *map, int64_t map_rows, int64_t
                                    int64_t capacity, int32_t *status, int grid, hipStream_t s);
 
 // Resident workgroups per CU of each kernel (occupancy query; 0 if unknown).
-int prefill_blocks_per_cu(int head_dim, int variant, bool f16);
-int decode_blocks_per_cu(int head_dim, bool f16);
+int prefill_blocks_per_cu(int head_dim, int variant, bool f16, int kv_format);
+int decode_blocks_per_cu(int head_dim, bool f16, int kv_format);
 
 }  // namespace pkvs

@@ -130,6 +130,15 @@ static int validate_desc(const pkvs_desc *d)
     if ((cap_bits & 0x7f800000u) == 0x7f800000u || ((cap_bits >> 31) && (cap_bits << 1)))
         return fail(PKVS_ERR_INVALID_ARG, "logits_soft_cap %g: must be 0 (off) or a positive "
                     "finite cap", double(d->logits_soft_cap));
+    if (d->kv_format < PKVS_KV_SAME || d->kv_format > PKVS_KV_FP8_E5M2)
+        return fail(PKVS_ERR_INVALID_ARG, "kv_format %d: must be 0 (same as dtype), 1 (e4m3) or "
+                    "2 (e5m2)", d->kv_format);
+    if (d->kv_format != PKVS_KV_SAME && d->dtype == PKVS_FP32)
+        return fail(PKVS_ERR_UNSUPPORTED, "8-bit K/V are built for bf16 and fp16 queries");
+    if (d->kv_format != PKVS_KV_SAME &&
+        (d->prefill_variant == kPrefillWide || d->prefill_variant == kPrefillDma))
+        return fail(PKVS_ERR_UNSUPPORTED, "8-bit K/V are widened on the register-staged prefill "
+                    "variants (1, 2)");
     if (d->window_left < -1)
         return fail(PKVS_ERR_INVALID_ARG, "window_left %d: must be -1 (off) or >= 0",
                     d->window_left);
@@ -440,6 +449,7 @@ static int create_plan(const pkvs_desc *desc, bool ragged, Plan **out)
     }
     (void)hipGetLastError();
     const bool fp32 = desc->dtype == PKVS_FP32, f16 = desc->dtype == PKVS_FP16;
+    const int kvf = desc->kv_format;
     if (desc->kind == PKVS_PREFILL) {
         // Kernel variant: 256-row workgroups (8 waves x 32 rows) share each
         // staged key tile between more rows and keep two waves per SIMD; they
@@ -449,11 +459,11 @@ static int create_plan(const pkvs_desc *desc, bool ragged, Plan **out)
         const int64_t big_tiles = ceil_div(desc->qo_capacity, 256 / group) * desc->num_kv_heads;
         int v = kPrefillRows128;
         if (desc->head_dim <= 128 && big_tiles >= 2 * p->num_cus)
-            v = desc->head_dim == 128 ? kPrefillDma : kPrefillRows256;
+            v = desc->head_dim == 128 && kvf == PKVS_KV_SAME ? kPrefillDma : kPrefillRows256;
         if (desc->prefill_variant) v = desc->prefill_variant;
         // the direct-to-LDS variant needs ~156 KiB of LDS per workgroup
         if (v == kPrefillDma && p->have_gpu && !fp32 &&
-            prefill_blocks_per_cu(desc->head_dim, v, f16) < 1)
+            prefill_blocks_per_cu(desc->head_dim, v, f16, kvf) < 1)
             v = kPrefillRows256;
         p->prefill_variant = p->run_variant = v;
         const int rows = v == kPrefillRows128 ? 128 : 256;
@@ -461,13 +471,14 @@ static int create_plan(const pkvs_desc *desc, bool ragged, Plan **out)
         p->item_words = kPrefillItemWords;
         p->block_threads =
             fp32 ? kGenericThreads : (v == kPrefillRows256 || v == kPrefillDma ? 512 : 256);
-        int per_cu = p->have_gpu && !fp32 ? prefill_blocks_per_cu(desc->head_dim, v, f16) : 0;
+        int per_cu =
+            p->have_gpu && !fp32 ? prefill_blocks_per_cu(desc->head_dim, v, f16, kvf) : 0;
         p->grid_blocks = p->num_cus * std::max(per_cu, fp32 ? 2 : 1);
     } else {
         p->query_tile = 1;
         p->item_words = fp32 ? kPrefillItemWords : kDecodeItemWords;
         p->block_threads = fp32 ? kGenericThreads : kDecodeThreads;
-        int per_cu = p->have_gpu && !fp32 ? decode_blocks_per_cu(desc->head_dim, f16) : 0;
+        int per_cu = p->have_gpu && !fp32 ? decode_blocks_per_cu(desc->head_dim, f16, kvf) : 0;
         p->grid_blocks = p->num_cus * std::max(per_cu, fp32 ? 2 : 8);
         p->auto_target_items = 2 * p->grid_blocks;
     }
@@ -518,6 +529,7 @@ static int create_cascade(const pkvs_desc *desc, Plan **out)
     e.kind = r.kind = PKVS_PREFILL;
     e.page_size = kRaggedPage;          // row-index table entries
     e.kv_capacity = desc->qo_capacity;  // a request's extend keys are its queries
+    e.kv_format = PKVS_KV_SAME;         // the new tokens' K/V come in the query dtype
     r.causal = 1;                       // the causal bound never hides a cached key
     Plan *p = new (std::nothrow) Plan();
     if (!p) return fail(PKVS_ERR_INVALID_ARG, "out of host memory");

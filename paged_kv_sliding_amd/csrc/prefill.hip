@@ -34,6 +34,8 @@
 // fp32 path (attention_fp32_kernel): a plain wave-per-row loop in fp32 for
 // fp32 inputs, used for small correctness-critical problems; it serves both
 // prefill items and decode (as one-query items).
+#include <type_traits>
+
 #include "device_common.h"
 #include "pkvs_internal.h"
 
@@ -80,16 +82,19 @@ struct PrefillBuf {
 };
 
 // Per-thread staging of one key tile: the NW*64 threads copy the tile's K and
-// V rows in 16-byte chunks (chunk c: key c / (D/8), dims 8*(c % (D/8))).  The
-// page ids of a tile are read one tile before its K/V loads and kept raw: the
-// address arithmetic that needs them runs only when the loads are issued, so
-// no wait on the page-table read sits behind freshly issued K/V loads.
-template <int D, int NW>
+// V rows in chunks of 8 elements (chunk c: key c / (D/8), dims 8*(c % (D/8)));
+// 16 bytes from a 16-bit cache, 8 bytes from an 8-bit one (KVF != 0), widened
+// to 16 bits on the way into LDS.  The page ids of a tile are read one tile
+// before its K/V loads and kept raw: the address arithmetic that needs them
+// runs only when the loads are issued, so no wait on the page-table read sits
+// behind freshly issued K/V loads.
+template <int D, int NW, int KVF>
 struct Stage {
     static constexpr int T = NW * 64;
     static constexpr int NCH = KT * D / 8;          // chunks per tile and tensor
     static constexpr int KCH = (NCH + T - 1) / T;   // per thread
-    u32x4 k[KCH], v[KCH];
+    using Raw = typename std::conditional<KVF == 0, u32x4, u32x2>::type;
+    Raw k[KCH], v[KCH];
     int32_t page[KCH];  // page id of the chunk's key (next tile to load)
 };
 
@@ -116,14 +121,15 @@ struct RowAddr {
 template <int D, int NW>
 __device__ __forceinline__ bool chunk_exists(int c)
 {
-    using S = Stage<D, NW>;
+    using S = Stage<D, NW, 0>;
     return S::NCH % S::T == 0 || c < S::NCH;
 }
 
-template <int D, int NW>
-__device__ __forceinline__ void stage_pages(Stage<D, NW> &st, const RowAddr &ra, int k0, int tid)
+template <int D, int NW, int KVF>
+__device__ __forceinline__ void stage_pages(Stage<D, NW, KVF> &st, const RowAddr &ra, int k0,
+                                            int tid)
 {
-    using S = Stage<D, NW>;
+    using S = Stage<D, NW, KVF>;
     constexpr int CPR = D / 8;
 #pragma unroll
     for (int i = 0; i < S::KCH; ++i) st.page[i] = ra.page_id(k0 + (tid + i * S::T) / CPR);
@@ -132,23 +138,34 @@ __device__ __forceinline__ void stage_pages(Stage<D, NW> &st, const RowAddr &ra,
 // Global -> registers.  Keys past the request are clamped to its last key
 // (a valid row); stage_store zeroes them, so no unwritten slot (whatever its
 // bits, even NaN) ever reaches an MFMA.
-template <int D, int NW>
-__device__ __forceinline__ void stage_load(Stage<D, NW> &st, const PrefillArgs &a,
+template <int D, int NW, int KVF>
+__device__ __forceinline__ void stage_load(Stage<D, NW, KVF> &st, const PrefillArgs &a,
                                            const RowAddr &ra, int k0, int tid)
 {
-    using S = Stage<D, NW>;
+    using S = Stage<D, NW, KVF>;
+    using Raw = typename S::Raw;
+    using Elem = typename std::conditional<KVF == 0, uint16_t, uint8_t>::type;
     constexpr int CPR = D / 8;
-    const uint16_t *K = static_cast<const uint16_t *>(a.k);
-    const uint16_t *V = static_cast<const uint16_t *>(a.v);
+    const Elem *K = static_cast<const Elem *>(a.k);
+    const Elem *V = static_cast<const Elem *>(a.v);
 #pragma unroll
     for (int i = 0; i < S::KCH; ++i) {
         const int c = tid + i * S::T;
         if (chunk_exists<D, NW>(c)) {
             const int64_t off = ra.offset(st.page[i], k0 + c / CPR) + (c % CPR) * 8;
-            st.k[i] = *reinterpret_cast<const u32x4 *>(K + off);
-            st.v[i] = *reinterpret_cast<const u32x4 *>(V + off);
+            st.k[i] = *reinterpret_cast<const Raw *>(K + off);
+            st.v[i] = *reinterpret_cast<const Raw *>(V + off);
         }
     }
+}
+
+// 16-bit bits of a staged chunk (8-bit caches: widened exactly, OCP e4m3 or
+// e5m2 -> fp32 -> bf16 / half)
+template <bool F16, int KVF>
+__device__ __forceinline__ u32x4 chunk_bits(const typename Stage<64, 4, KVF>::Raw &raw)
+{
+    if constexpr (KVF == 0) return raw;
+    else return __builtin_bit_cast(u32x4, widen_fp8<KVF, F16>(raw));
 }
 
 // Per-element window/causal/length mask of one 32-key tile for a lane's row
@@ -174,18 +191,18 @@ __device__ __forceinline__ float max16(const f32x16 &s)
     return fmaxf(fmaxf(a, fmaxf(b, c)), fmaxf(fmaxf(d, e), s[15]));
 }
 
-template <int D, int NW>
-__device__ __forceinline__ void stage_store(Stage<D, NW> &st, PrefillBuf<D> &b, int k0,
+template <bool F16, int D, int NW, int KVF>
+__device__ __forceinline__ void stage_store(Stage<D, NW, KVF> &st, PrefillBuf<D> &b, int k0,
                                             int kv_len, int tid)
 {
-    using S = Stage<D, NW>;
+    using S = Stage<D, NW, KVF>;
     constexpr int CPR = D / 8;
     if (k0 + KT > kv_len) {
         // the request's last tile: keys past its end become zeros
 #pragma unroll
         for (int i = 0; i < S::KCH; ++i) {
             const bool past = k0 + (tid + i * S::T) / CPR >= kv_len;
-            const u32x4 z = {0u, 0u, 0u, 0u};
+            const typename S::Raw z = {};
             st.k[i] = past ? z : st.k[i];
             st.v[i] = past ? z : st.v[i];
         }
@@ -194,8 +211,8 @@ __device__ __forceinline__ void stage_store(Stage<D, NW> &st, PrefillBuf<D> &b, 
     for (int i = 0; i < S::KCH; ++i) {
         const int c = tid + i * S::T;
         if (chunk_exists<D, NW>(c)) {
-            *reinterpret_cast<u32x4 *>(&b.k[c / CPR][(c % CPR) * 8]) = st.k[i];
-            *reinterpret_cast<u32x4 *>(&b.v[c / CPR][(c % CPR) * 8]) = st.v[i];
+            *reinterpret_cast<u32x4 *>(&b.k[c / CPR][(c % CPR) * 8]) = chunk_bits<F16, KVF>(st.k[i]);
+            *reinterpret_cast<u32x4 *>(&b.v[c / CPR][(c % CPR) * 8]) = chunk_bits<F16, KVF>(st.v[i]);
         }
     }
 }
@@ -298,10 +315,11 @@ __device__ __forceinline__ void dma_rows4_kv(const uint32_t (&mk)[4], const uint
                  : "memory");
 }
 
-template <int D, int NW, bool DMA, bool F16>
+template <int D, int NW, bool DMA, bool F16, int KVF>
 __global__ __launch_bounds__(NW * 64) void prefill_kernel(PrefillArgs a)
 {
-    static_assert(!DMA || (D == 128 && NW == 8), "direct-to-LDS staging: D = 128, 8 waves");
+    static_assert(!DMA || (D == 128 && NW == 8 && KVF == 0),
+                  "direct-to-LDS staging: D = 128, 8 waves, 16-bit K/V");
     constexpr int KSTEPS = D / 16;  // QK k-steps
     constexpr int DT = D / 32;      // O^T dim tiles
     constexpr int NS = DMA ? DMA_SETS : NBUF;  // LDS tile sets (a power of two)
@@ -432,7 +450,7 @@ __global__ __launch_bounds__(NW * 64) void prefill_kernel(PrefillArgs a)
             return page_entry(min(kv_begin + t * KT + DMA_ROWS * uwave, kv_last));
         };
 
-        Stage<D, NW> st;
+        Stage<D, NW, KVF> st;
         if constexpr (DMA) {
             // prologue: page table of the item (ids clamped into the cache),
             // then tiles 0 .. AHEAD-1 in flight; wait for tiles 0 and 1
@@ -460,11 +478,11 @@ __global__ __launch_bounds__(NW * 64) void prefill_kernel(PrefillArgs a)
                 stage_pages(st, ra, kv_begin, tid);
                 stage_load(st, a, ra, kv_begin, tid);
                 stage_pages(st, ra, kv_begin + KT, tid);
-                stage_store(st, lds[0], kv_begin, kv_len, tid);
+                stage_store<F16>(st, lds[0], kv_begin, kv_len, tid);
                 if (ntiles > 1) {
                     stage_load(st, a, ra, kv_begin + KT, tid);
                     stage_pages(st, ra, kv_begin + 2 * KT, tid);
-                    stage_store(st, lds[1], kv_begin + KT, kv_len, tid);
+                    stage_store<F16>(st, lds[1], kv_begin + KT, kv_len, tid);
                     if (ntiles > 2) {
                         stage_load(st, a, ra, kv_begin + 2 * KT, tid);
                         stage_pages(st, ra, kv_begin + 3 * KT, tid);
@@ -578,7 +596,7 @@ __global__ __launch_bounds__(NW * 64) void prefill_kernel(PrefillArgs a)
             } else {
                 // stage tile j+2 into the free LDS set, start loading tile j+3
                 if (j + 2 < ntiles) {
-                    stage_store(st, lds[(j + 2) & (NS - 1)], k0 + 2 * KT, kv_len, tid);
+                    stage_store<F16>(st, lds[(j + 2) & (NS - 1)], k0 + 2 * KT, kv_len, tid);
                     if (j + 3 < ntiles) {
                         stage_load(st, a, ra, k0 + 3 * KT, tid);
                         stage_pages(st, ra, k0 + 4 * KT, tid);
@@ -600,7 +618,7 @@ __global__ __launch_bounds__(NW * 64) void prefill_kernel(PrefillArgs a)
         l += __shfl_xor(l, 32);
         if (row_valid) {
             const int64_t lrow = int64_t(q_begin + row_tok) * a.num_qo_heads + hk * G + row_head;
-            float w_self = l > 0.f ? 1.f / l : 0.f, w_other = 0.f;
+            float w_self = l > 0.f ? a.v_scale / l : 0.f, w_other = 0.f;
             float lse_row = l > 0.f ? (m + fast_log2(l)) * kLn2 : kNegInf;
             if (a.fold_lse) {
                 const Fold f = fold_weights(lse_row, a.fold_lse[lrow]);
@@ -733,18 +751,18 @@ __global__ __launch_bounds__(256) void prefill_wide_kernel(PrefillArgs a)
 
         // prologue: tiles 0 and 1 in sets 0 and 1, tile 2 in registers, tile 3's
         // page ids read; the V rows of set 3 (read as "tile -1") are zeroed
-        Stage<D, NW> st;
+        Stage<D, NW, 0> st;
         for (int e = tid; e < KT * (D + VPAD) / 8; e += NW * 64)
             reinterpret_cast<u32x4 *>(&lds[WIDE_SETS - 1].v[0][0])[e] = u32x4{0u, 0u, 0u, 0u};
         if (ntiles > 0) {
             stage_pages(st, ra, kv_begin, tid);
             stage_load(st, a, ra, kv_begin, tid);
             stage_pages(st, ra, kv_begin + KT, tid);
-            stage_store(st, lds[0], kv_begin, kv_len, tid);
+            stage_store<F16>(st, lds[0], kv_begin, kv_len, tid);
             if (ntiles > 1) {
                 stage_load(st, a, ra, kv_begin + KT, tid);
                 stage_pages(st, ra, kv_begin + 2 * KT, tid);
-                stage_store(st, lds[1], kv_begin + KT, kv_len, tid);
+                stage_store<F16>(st, lds[1], kv_begin + KT, kv_len, tid);
                 if (ntiles > 2) {
                     stage_load(st, a, ra, kv_begin + 2 * KT, tid);
                     stage_pages(st, ra, kv_begin + 3 * KT, tid);
@@ -873,7 +891,7 @@ __global__ __launch_bounds__(256) void prefill_wide_kernel(PrefillArgs a)
 
             // stage tile j+2 into its LDS set, start loading tile j+3
             if (j + 2 < ntiles) {
-                stage_store(st, lds[nn], k0 + 2 * KT, kv_len, tid);
+                stage_store<F16>(st, lds[nn], k0 + 2 * KT, kv_len, tid);
                 if (j + 3 < ntiles) {
                     stage_load(st, a, ra, k0 + 3 * KT, tid);
                     stage_pages(st, ra, k0 + 4 * KT, tid);
@@ -906,7 +924,7 @@ __global__ __launch_bounds__(256) void prefill_wide_kernel(PrefillArgs a)
             if (row_valid[n]) {
                 const int64_t lrow =
                     int64_t(q_begin + row_tok[n]) * a.num_qo_heads + hk * G + row_head[n];
-                float w_self = ln > 0.f ? 1.f / ln : 0.f, w_other = 0.f;
+                float w_self = ln > 0.f ? a.v_scale / ln : 0.f, w_other = 0.f;
                 float lse_row = ln > 0.f ? (m[n] + fast_log2(ln)) * kLn2 : kNegInf;
                 if (a.fold_lse) {
                     const Fold f = fold_weights(lse_row, a.fold_lse[lrow]);
@@ -983,7 +1001,7 @@ __global__ __launch_bounds__(kGenericThreads) void attention_fp32_kernel(Prefill
                 m = m_new;
             }
             const int64_t lrow = int64_t(q_begin + tok) * a.num_qo_heads + h;
-            float w_self = l > 0.f ? 1.f / l : 0.f, w_other = 0.f;
+            float w_self = l > 0.f ? a.v_scale / l : 0.f, w_other = 0.f;
             float lse_row = l > 0.f ? (m + fast_log2(l)) * kLn2 : kNegInf;
             if (a.fold_lse) {
                 const Fold f = fold_weights(lse_row, a.fold_lse[lrow]);
@@ -1003,41 +1021,61 @@ __global__ __launch_bounds__(kGenericThreads) void attention_fp32_kernel(Prefill
 
 }  // namespace
 
-template <bool F16>
+template <bool F16, int KVF>
 static hipError_t launch_prefill_t(const PrefillArgs &a, int head_dim, int variant, int grid,
                                    hipStream_t s)
 {
-    if (variant == kPrefillDma) {
-        if (head_dim != 128) return hipErrorInvalidValue;
-        prefill_kernel<128, 8, true, F16><<<grid, 512, 0, s>>>(a);
-    } else if (variant == kPrefillWide) {
-        switch (head_dim) {
-        case 64: prefill_wide_kernel<64, F16><<<grid, 256, 0, s>>>(a); break;
-        case 128: prefill_wide_kernel<128, F16><<<grid, 256, 0, s>>>(a); break;
-        default: return hipErrorInvalidValue;
+    if constexpr (KVF == 0) {
+        if (variant == kPrefillDma) {
+            if (head_dim != 128) return hipErrorInvalidValue;
+            prefill_kernel<128, 8, true, F16, 0><<<grid, 512, 0, s>>>(a);
+            return hipGetLastError();
         }
-    } else if (variant == kPrefillRows256) {
+        if (variant == kPrefillWide) {
+            switch (head_dim) {
+            case 64: prefill_wide_kernel<64, F16><<<grid, 256, 0, s>>>(a); break;
+            case 128: prefill_wide_kernel<128, F16><<<grid, 256, 0, s>>>(a); break;
+            default: return hipErrorInvalidValue;
+            }
+            return hipGetLastError();
+        }
+    } else if (variant == kPrefillDma || variant == kPrefillWide) {
+        return hipErrorInvalidValue;  // 8-bit K/V are widened on the register-staged path
+    }
+    if (variant == kPrefillRows256) {
         switch (head_dim) {
-        case 64: prefill_kernel<64, 8, false, F16><<<grid, 512, 0, s>>>(a); break;
-        case 128: prefill_kernel<128, 8, false, F16><<<grid, 512, 0, s>>>(a); break;
+        case 64: prefill_kernel<64, 8, false, F16, KVF><<<grid, 512, 0, s>>>(a); break;
+        case 128: prefill_kernel<128, 8, false, F16, KVF><<<grid, 512, 0, s>>>(a); break;
         default: return hipErrorInvalidValue;
         }
     } else {
         switch (head_dim) {
-        case 64: prefill_kernel<64, 4, false, F16><<<grid, 256, 0, s>>>(a); break;
-        case 128: prefill_kernel<128, 4, false, F16><<<grid, 256, 0, s>>>(a); break;
-        case 256: prefill_kernel<256, 4, false, F16><<<grid, 256, 0, s>>>(a); break;
+        case 64: prefill_kernel<64, 4, false, F16, KVF><<<grid, 256, 0, s>>>(a); break;
+        case 128: prefill_kernel<128, 4, false, F16, KVF><<<grid, 256, 0, s>>>(a); break;
+        case 256: prefill_kernel<256, 4, false, F16, KVF><<<grid, 256, 0, s>>>(a); break;
         default: return hipErrorInvalidValue;
         }
     }
     return hipGetLastError();
 }
 
-hipError_t launch_prefill_16bit(const PrefillArgs &a, int head_dim, int variant, bool f16,
-                                int grid, hipStream_t s)
+template <bool F16>
+static hipError_t launch_prefill_f(const PrefillArgs &a, int head_dim, int variant, int kv_format,
+                                   int grid, hipStream_t s)
 {
-    return f16 ? launch_prefill_t<true>(a, head_dim, variant, grid, s)
-               : launch_prefill_t<false>(a, head_dim, variant, grid, s);
+    switch (kv_format) {
+    case 0: return launch_prefill_t<F16, 0>(a, head_dim, variant, grid, s);
+    case PKVS_KV_FP8_E4M3: return launch_prefill_t<F16, 1>(a, head_dim, variant, grid, s);
+    case PKVS_KV_FP8_E5M2: return launch_prefill_t<F16, 2>(a, head_dim, variant, grid, s);
+    default: return hipErrorInvalidValue;
+    }
+}
+
+hipError_t launch_prefill_16bit(const PrefillArgs &a, int head_dim, int variant, bool f16,
+                                int kv_format, int grid, hipStream_t s)
+{
+    return f16 ? launch_prefill_f<true>(a, head_dim, variant, kv_format, grid, s)
+               : launch_prefill_f<false>(a, head_dim, variant, kv_format, grid, s);
 }
 
 hipError_t launch_attention_fp32(const PrefillArgs &a, int head_dim, int grid, hipStream_t s)
@@ -1054,31 +1092,46 @@ static int blocks_per_cu(K kernel, int threads)
                                                                                              : 0;
 }
 
-template <bool F16>
+template <bool F16, int KVF>
 static int prefill_blocks_per_cu_t(int head_dim, int variant)
 {
-    if (variant == kPrefillDma)
-        return head_dim == 128 ? blocks_per_cu(prefill_kernel<128, 8, true, F16>, 512) : 0;
-    if (variant == kPrefillWide) {
-        if (head_dim == 64) return blocks_per_cu(prefill_wide_kernel<64, F16>, 256);
-        if (head_dim == 128) return blocks_per_cu(prefill_wide_kernel<128, F16>, 256);
+    if constexpr (KVF == 0) {
+        if (variant == kPrefillDma)
+            return head_dim == 128 ? blocks_per_cu(prefill_kernel<128, 8, true, F16, 0>, 512) : 0;
+        if (variant == kPrefillWide) {
+            if (head_dim == 64) return blocks_per_cu(prefill_wide_kernel<64, F16>, 256);
+            if (head_dim == 128) return blocks_per_cu(prefill_wide_kernel<128, F16>, 256);
+            return 0;
+        }
+    } else if (variant == kPrefillDma || variant == kPrefillWide) {
         return 0;
     }
     if (variant == kPrefillRows256) {
-        if (head_dim == 64) return blocks_per_cu(prefill_kernel<64, 8, false, F16>, 512);
-        if (head_dim == 128) return blocks_per_cu(prefill_kernel<128, 8, false, F16>, 512);
+        if (head_dim == 64) return blocks_per_cu(prefill_kernel<64, 8, false, F16, KVF>, 512);
+        if (head_dim == 128) return blocks_per_cu(prefill_kernel<128, 8, false, F16, KVF>, 512);
         return 0;
     }
-    if (head_dim == 64) return blocks_per_cu(prefill_kernel<64, 4, false, F16>, 256);
-    if (head_dim == 128) return blocks_per_cu(prefill_kernel<128, 4, false, F16>, 256);
-    if (head_dim == 256) return blocks_per_cu(prefill_kernel<256, 4, false, F16>, 256);
+    if (head_dim == 64) return blocks_per_cu(prefill_kernel<64, 4, false, F16, KVF>, 256);
+    if (head_dim == 128) return blocks_per_cu(prefill_kernel<128, 4, false, F16, KVF>, 256);
+    if (head_dim == 256) return blocks_per_cu(prefill_kernel<256, 4, false, F16, KVF>, 256);
     return 0;
 }
 
-int prefill_blocks_per_cu(int head_dim, int variant, bool f16)
+template <bool F16>
+static int prefill_blocks_per_cu_f(int head_dim, int variant, int kv_format)
 {
-    return f16 ? prefill_blocks_per_cu_t<true>(head_dim, variant)
-               : prefill_blocks_per_cu_t<false>(head_dim, variant);
+    switch (kv_format) {
+    case 0: return prefill_blocks_per_cu_t<F16, 0>(head_dim, variant);
+    case PKVS_KV_FP8_E4M3: return prefill_blocks_per_cu_t<F16, 1>(head_dim, variant);
+    case PKVS_KV_FP8_E5M2: return prefill_blocks_per_cu_t<F16, 2>(head_dim, variant);
+    default: return 0;
+    }
+}
+
+int prefill_blocks_per_cu(int head_dim, int variant, bool f16, int kv_format)
+{
+    return f16 ? prefill_blocks_per_cu_f<true>(head_dim, variant, kv_format)
+               : prefill_blocks_per_cu_f<false>(head_dim, variant, kv_format);
 }
 
 }  // namespace pkvs

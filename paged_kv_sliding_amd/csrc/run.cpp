@@ -4,6 +4,7 @@
 
 #include <algorithm>
 #include <cstdint>
+#include <cstring>
 
 #include "pkvs_internal.h"
 #include "plan_state.h"
@@ -35,6 +36,15 @@ void logit_scales(const pkvs_desc &d, float sm_scale, float *scale_log2, float *
         *scale_log2 = sm_scale * kLog2e;
         *cap_a = 0.f;
     }
+}
+
+// A k_scale / v_scale must be positive and finite (bit test: the library is
+// built with -fno-honor-nans).
+bool bad_scale(float x)
+{
+    uint32_t b;
+    std::memcpy(&b, &x, sizeof b);
+    return (b >> 31) || (b & 0x7f800000u) == 0x7f800000u || (b & 0x7fffffffu) == 0;
 }
 
 int log2_exact(int x)
@@ -77,8 +87,8 @@ int check_run(const pkvs_plan *p, int kind, const void *q, const void *k, const 
 // the partial (fold_o, fold_lse) of the same queries.
 hipError_t launch_prefill_pass(const pkvs_plan *p, const void *q, const void *k, const void *v,
                                int64_t num_pages, const int32_t *kv_indices, void *o, float *lse,
-                               float sm_scale, hipStream_t stream, const void *fold_o = nullptr,
-                               const float *fold_lse = nullptr)
+                               float sm_scale, float k_scale, float v_scale, hipStream_t stream,
+                               const void *fold_o = nullptr, const float *fold_lse = nullptr)
 {
     const int32_t *ws = static_cast<const int32_t *>(p->int_ws);
     PrefillArgs a{};
@@ -90,7 +100,8 @@ hipError_t launch_prefill_pass(const pkvs_plan *p, const void *q, const void *k,
     a.lse = lse;
     a.ws = ws + p->lead_words;
     a.num_pages = p->ragged ? p->desc.qo_capacity : num_pages;
-    logit_scales(p->desc, sm_scale, &a.scale_log2, &a.cap_a);
+    logit_scales(p->desc, sm_scale * k_scale, &a.scale_log2, &a.cap_a);
+    a.v_scale = v_scale;
     a.num_qo_heads = p->desc.num_qo_heads;
     a.num_kv_heads = p->desc.num_kv_heads;
     a.log2_group = log2_exact(p->desc.num_qo_heads / p->desc.num_kv_heads);
@@ -104,7 +115,8 @@ hipError_t launch_prefill_pass(const pkvs_plan *p, const void *q, const void *k,
     return p->desc.dtype == PKVS_FP32
                ? launch_attention_fp32(a, p->desc.head_dim, p->grid_blocks, stream)
                : launch_prefill_16bit(a, p->desc.head_dim, p->run_variant,
-                                      p->desc.dtype == PKVS_FP16, p->grid_blocks, stream);
+                                      p->desc.dtype == PKVS_FP16, p->desc.kv_format,
+                                      p->grid_blocks, stream);
 }
 
 }  // namespace
@@ -113,14 +125,18 @@ extern "C" {
 
 int pkvs_prefill_run(const pkvs_plan *p, const void *q, const void *k_cache, const void *v_cache,
                      int64_t num_pages, const int32_t *kv_indices_d, void *o, float *lse,
-                     float sm_scale, int32_t window_left, int32_t causal, hipStream_t stream)
+                     float sm_scale, int32_t window_left, int32_t causal, float k_scale,
+                     float v_scale, hipStream_t stream)
 {
     clear_error();
+    if (bad_scale(k_scale) || bad_scale(v_scale))
+        return fail(PKVS_ERR_INVALID_ARG, "k_scale %g / v_scale %g must be positive and finite",
+                    double(k_scale), double(v_scale));
     int rc = check_run(p, PKVS_PREFILL, q, k_cache, v_cache, num_pages, kv_indices_d, o,
                        window_left, causal);
     if (rc) return rc;
     hipError_t e = launch_prefill_pass(p, q, k_cache, v_cache, num_pages, kv_indices_d, o, lse,
-                                       sm_scale, stream);
+                                       sm_scale, k_scale, v_scale, stream);
     if (e != hipSuccess) return fail(PKVS_ERR_HIP, "prefill launch: %s", hipGetErrorString(e));
     return PKVS_OK;
 }
@@ -128,11 +144,15 @@ int pkvs_prefill_run(const pkvs_plan *p, const void *q, const void *k_cache, con
 int pkvs_cascade_run(const pkvs_plan *p, const void *q, const void *k_extend,
                      const void *v_extend, const void *k_cache, const void *v_cache,
                      int64_t num_pages, const int32_t *kv_indices_d, void *o, float *lse,
-                     float sm_scale, int32_t window_left, hipStream_t stream)
+                     float sm_scale, int32_t window_left, float k_scale, float v_scale,
+                     hipStream_t stream)
 {
     clear_error();
     if (!p) return fail(PKVS_ERR_INVALID_ARG, "plan is null");
     if (p->desc.kind != PKVS_CASCADE) return fail(PKVS_ERR_INVALID_ARG, "not a cascade plan");
+    if (bad_scale(k_scale) || bad_scale(v_scale))
+        return fail(PKVS_ERR_INVALID_ARG, "k_scale %g / v_scale %g must be positive and finite",
+                    double(k_scale), double(v_scale));
     if (window_left != p->desc.window_left)
         return fail(PKVS_ERR_PLAN_MISMATCH, "run window_left %d differs from the planned %d",
                     window_left, p->desc.window_left);
@@ -150,19 +170,23 @@ int pkvs_cascade_run(const pkvs_plan *p, const void *q, const void *k_extend,
     // prefix pass -> (o2, lse2); the extend pass stores the merge of its own
     // (o, lse) with them
     hipError_t e = launch_prefill_pass(p->pre, q, k_cache, v_cache, std::max<int64_t>(num_pages, 1),
-                                       kv_indices_d, o2, lse2, sm_scale, stream);
+                                       kv_indices_d, o2, lse2, sm_scale, k_scale, v_scale, stream);
     if (e != hipSuccess) return fail(PKVS_ERR_HIP, "prefix pass launch: %s", hipGetErrorString(e));
-    e = launch_prefill_pass(p->ext, q, k_extend, v_extend, 0, nullptr, o, lse, sm_scale, stream,
-                            o2, lse2);
+    e = launch_prefill_pass(p->ext, q, k_extend, v_extend, 0, nullptr, o, lse, sm_scale, 1.f, 1.f,
+                            stream, o2, lse2);
     if (e != hipSuccess) return fail(PKVS_ERR_HIP, "extend pass launch: %s", hipGetErrorString(e));
     return PKVS_OK;
 }
 
 int pkvs_decode_run(const pkvs_plan *p, const void *q, const void *k_cache, const void *v_cache,
                     int64_t num_pages, const int32_t *kv_indices_d, void *o, float *lse,
-                    float sm_scale, int32_t window_left, hipStream_t stream)
+                    float sm_scale, int32_t window_left, float k_scale, float v_scale,
+                    hipStream_t stream)
 {
     clear_error();
+    if (bad_scale(k_scale) || bad_scale(v_scale))
+        return fail(PKVS_ERR_INVALID_ARG, "k_scale %g / v_scale %g must be positive and finite",
+                    double(k_scale), double(v_scale));
     int rc = check_run(p, PKVS_DECODE, q, k_cache, v_cache, num_pages, kv_indices_d, o,
                        window_left, 1);
     if (rc) return rc;
@@ -171,7 +195,7 @@ int pkvs_decode_run(const pkvs_plan *p, const void *q, const void *k_cache, cons
     // later plan of the same capacities)
     const int log2g = log2_exact(p->desc.num_qo_heads / p->desc.num_kv_heads);
     float scale_log2, cap_a;
-    logit_scales(p->desc, sm_scale, &scale_log2, &cap_a);
+    logit_scales(p->desc, sm_scale * k_scale, &scale_log2, &cap_a);
     hipError_t e;
     if (p->desc.dtype == PKVS_FP32) {
         PrefillArgs a{};
@@ -185,6 +209,7 @@ int pkvs_decode_run(const pkvs_plan *p, const void *q, const void *k_cache, cons
         a.num_pages = num_pages;
         a.scale_log2 = scale_log2;
         a.cap_a = cap_a;
+        a.v_scale = v_scale;
         a.num_qo_heads = p->desc.num_qo_heads;
         a.num_kv_heads = p->desc.num_kv_heads;
         a.log2_group = log2g;
@@ -211,13 +236,14 @@ int pkvs_decode_run(const pkvs_plan *p, const void *q, const void *k_cache, cons
     a.num_pages = num_pages;
     a.scale_log2 = scale_log2;
     a.cap_a = cap_a;
+    a.v_scale = v_scale;
     a.num_qo_heads = p->desc.num_qo_heads;
     a.num_kv_heads = p->desc.num_kv_heads;
     a.log2_group = log2g;
     a.page_size = p->desc.page_size;
     a.log2_page = log2_exact(p->desc.page_size);
     const bool f16 = p->desc.dtype == PKVS_FP16;
-    e = launch_decode_16bit(a, p->desc.head_dim, f16, p->grid_blocks, stream);
+    e = launch_decode_16bit(a, p->desc.head_dim, f16, p->desc.kv_format, p->grid_blocks, stream);
     if (e != hipSuccess) return fail(PKVS_ERR_HIP, "decode launch: %s", hipGetErrorString(e));
     if (p->merges_cap > 0) {
         // launched whenever the plan can have merges (the kernel reads their

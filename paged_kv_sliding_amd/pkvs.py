@@ -33,6 +33,11 @@ PKVS_ERR_NOT_PLANNED = -7
 PKVS_BF16 = 0
 PKVS_FP32 = 1
 PKVS_FP16 = 2
+PKVS_KV_SAME = 0
+PKVS_KV_FP8_E4M3 = 1
+PKVS_KV_FP8_E5M2 = 2
+_KV_FORMATS = {None: PKVS_KV_SAME, torch.float8_e4m3fn: PKVS_KV_FP8_E4M3,
+               torch.float8_e5m2: PKVS_KV_FP8_E5M2}
 PKVS_PREFILL = 0
 PKVS_DECODE = 1
 PKVS_CASCADE = 2
@@ -58,6 +63,7 @@ class pkvs_desc(ctypes.Structure):
         ("disable_split_kv", ctypes.c_int32), ("batch_capacity", ctypes.c_int32),
         ("prefill_variant", ctypes.c_int32), ("qo_capacity", ctypes.c_int64),
         ("kv_capacity", ctypes.c_int64), ("logits_soft_cap", ctypes.c_float),
+        ("kv_format", ctypes.c_int32),
     ]
 
 
@@ -89,11 +95,13 @@ def _load() -> ctypes.CDLL:
         "pkvs_plan_create": (ctypes.c_int, [ctypes.POINTER(P), ctypes.POINTER(pkvs_desc)]),
         "pkvs_workspace_size": (ctypes.c_int, [P, ctypes.POINTER(sz), ctypes.POINTER(sz)]),
         "pkvs_prefill_plan": (ctypes.c_int, [P, P, P, P, i32, P, sz, P, sz, P]),
-        "pkvs_prefill_run": (ctypes.c_int, [P, P, P, P, i64, P, P, P, f32, i32, i32, P]),
+        "pkvs_prefill_run": (ctypes.c_int, [P, P, P, P, i64, P, P, P, f32, i32, i32, f32, f32,
+                                            P]),
         "pkvs_decode_plan": (ctypes.c_int, [P, P, P, i32, P, sz, P, sz, P]),
-        "pkvs_decode_run": (ctypes.c_int, [P, P, P, P, i64, P, P, P, f32, i32, P]),
+        "pkvs_decode_run": (ctypes.c_int, [P, P, P, P, i64, P, P, P, f32, i32, f32, f32, P]),
         "pkvs_cascade_plan": (ctypes.c_int, [P, P, P, P, i32, P, sz, P, sz, P]),
-        "pkvs_cascade_run": (ctypes.c_int, [P, P, P, P, P, P, i64, P, P, P, f32, i32, P]),
+        "pkvs_cascade_run": (ctypes.c_int, [P, P, P, P, P, P, i64, P, P, P, f32, i32, f32, f32,
+                                            P]),
         "pkvs_merge_state": (ctypes.c_int, [P, P, P, P, P, P, i64, i32, i32, i32, P]),
         "pkvs_append_kv": (ctypes.c_int, [P, P, P, i64, P, P, i64, i32, i32, i32, P, P]),
         "pkvs_build_kv_indices": (ctypes.c_int, [P, i64, i64, P, P, P, i32, P, P, i64, P, P]),
@@ -155,11 +163,14 @@ def make_desc(kind: int, *, num_qo_heads: int, num_kv_heads: int, head_dim: int,
               dtype: torch.dtype, window_left: int, causal: bool = True,
               fixed_split_size: int = -1, disable_split_kv: bool = False,
               batch_capacity: int, qo_capacity: int = 0, kv_capacity: int,
-              prefill_variant: int = 0, logits_soft_cap: float = 0.0) -> pkvs_desc:
+              prefill_variant: int = 0, logits_soft_cap: float = 0.0,
+              kv_dtype: Optional[torch.dtype] = None) -> pkvs_desc:
+    """``kv_dtype``: None (caches in ``dtype``) or torch.float8_e4m3fn /
+    torch.float8_e5m2."""
     return pkvs_desc(kind, num_qo_heads, num_kv_heads, head_dim, page_size, _DTYPES[dtype],
                      int(bool(causal)), window_left, fixed_split_size, int(bool(disable_split_kv)),
                      batch_capacity, prefill_variant, qo_capacity, kv_capacity,
-                     float(logits_soft_cap))
+                     float(logits_soft_cap), _KV_FORMATS[kv_dtype])
 
 
 def pkvs_plan_create(desc: pkvs_desc) -> ctypes.c_void_p:
@@ -214,29 +225,33 @@ def pkvs_cascade_plan(plan, qo_indptr_h, kv_indptr_h, kv_last_page_len_h, batch_
 
 
 def pkvs_cascade_run(plan, q, k_extend, v_extend, k_cache, v_cache, kv_indices, o, lse,
-                     sm_scale: float, window_left: int, stream=None) -> None:
+                     sm_scale: float, window_left: int, k_scale: float = 1.0,
+                     v_scale: float = 1.0, stream=None) -> None:
     _need_device(q, k_extend, v_extend, k_cache, v_cache, kv_indices, o, lse)
     _check(_lib.pkvs_cascade_run(plan, _ptr(q), _ptr(k_extend), _ptr(v_extend), _ptr(k_cache),
                                  _ptr(v_cache), k_cache.shape[0], _ptr(kv_indices), _ptr(o),
-                                 _ptr(lse), float(sm_scale), window_left, _stream(stream)),
-           "pkvs_cascade_run")
+                                 _ptr(lse), float(sm_scale), window_left, float(k_scale),
+                                 float(v_scale), _stream(stream)), "pkvs_cascade_run")
 
 
 def pkvs_prefill_run(plan, q, k_cache, v_cache, kv_indices, o, lse, sm_scale: float,
-                     window_left: int, causal: bool = True, stream=None) -> None:
+                     window_left: int, causal: bool = True, k_scale: float = 1.0,
+                     v_scale: float = 1.0, stream=None) -> None:
     _need_device(q, k_cache, v_cache, kv_indices, o, lse)
     _check(_lib.pkvs_prefill_run(plan, _ptr(q), _ptr(k_cache), _ptr(v_cache), k_cache.shape[0],
                                  _ptr(kv_indices), _ptr(o), _ptr(lse), float(sm_scale),
-                                 window_left, int(bool(causal)), _stream(stream)),
-           "pkvs_prefill_run")
+                                 window_left, int(bool(causal)), float(k_scale), float(v_scale),
+                                 _stream(stream)), "pkvs_prefill_run")
 
 
 def pkvs_decode_run(plan, q, k_cache, v_cache, kv_indices, o, lse, sm_scale: float,
-                    window_left: int, stream=None) -> None:
+                    window_left: int, k_scale: float = 1.0, v_scale: float = 1.0,
+                    stream=None) -> None:
     _need_device(q, k_cache, v_cache, kv_indices, o, lse)
     _check(_lib.pkvs_decode_run(plan, _ptr(q), _ptr(k_cache), _ptr(v_cache), k_cache.shape[0],
                                 _ptr(kv_indices), _ptr(o), _ptr(lse), float(sm_scale),
-                                window_left, _stream(stream)), "pkvs_decode_run")
+                                window_left, float(k_scale), float(v_scale), _stream(stream)),
+           "pkvs_decode_run")
 
 
 def pkvs_merge_state(v_a, s_a, v_b, s_b, v_out=None, s_out=None, stream=None):
@@ -357,9 +372,10 @@ class BatchAttention:
         if out.shape != q.shape or out.dtype != dt:
             raise ValueError("out must match q")
         kv_shape = (d.page_size, d.num_kv_heads, d.head_dim)
+        kv_dt = {v: k for k, v in _KV_FORMATS.items()}[d.kv_format] or dt
         for c in (k_cache, v_cache):
-            if c.dim() != 4 or tuple(c.shape[1:]) != kv_shape or c.dtype != dt:
-                raise ValueError(f"caches must be {dt} [num_pages, {kv_shape}]")
+            if c.dim() != 4 or tuple(c.shape[1:]) != kv_shape or c.dtype != kv_dt:
+                raise ValueError(f"caches must be {kv_dt} [num_pages, {kv_shape}]")
         if k_cache.shape[0] != v_cache.shape[0]:
             raise ValueError("k_cache and v_cache page counts differ")
         if kv_indices.dtype != torch.int32 or kv_indices.numel() < self._nnz_pages:
@@ -368,7 +384,8 @@ class BatchAttention:
             raise ValueError(f"lse must be float32 {exp_q[:2]}")
 
     def run(self, q, k_cache, v_cache, kv_indices, *, sm_scale: float, window_left: int,
-            causal: bool = True, return_lse: bool = True, out=None, lse=None, stream=None):
+            causal: bool = True, return_lse: bool = True, out=None, lse=None, stream=None,
+            k_scale: float = 1.0, v_scale: float = 1.0):
         if out is None:
             out = torch.empty_like(q)
         if return_lse and lse is None:
@@ -376,10 +393,10 @@ class BatchAttention:
         self._check_shapes(q, k_cache, v_cache, kv_indices, out, lse)
         if self.kind == PKVS_PREFILL:
             pkvs_prefill_run(self.handle, q, k_cache, v_cache, kv_indices, out, lse, sm_scale,
-                             window_left, causal, stream)
+                             window_left, causal, k_scale, v_scale, stream)
         else:
             pkvs_decode_run(self.handle, q, k_cache, v_cache, kv_indices, out, lse, sm_scale,
-                            window_left, stream)
+                            window_left, k_scale, v_scale, stream)
         return (out, lse) if return_lse else out
 
     def info(self) -> pkvs_plan_info:
@@ -434,9 +451,10 @@ class CascadeAttention:
                 raise ValueError(f"k_extend / v_extend must be {dt} [>= {self._nnz_qo}, "
                                  f"{d.num_kv_heads}, {d.head_dim}]")
         kv_shape = (d.page_size, d.num_kv_heads, d.head_dim)
+        kv_dt = {v: k for k, v in _KV_FORMATS.items()}[d.kv_format] or dt
         for c in (k_cache, v_cache):
-            if c.dim() != 4 or tuple(c.shape[1:]) != kv_shape or c.dtype != dt:
-                raise ValueError(f"caches must be {dt} [num_pages, {kv_shape}]")
+            if c.dim() != 4 or tuple(c.shape[1:]) != kv_shape or c.dtype != kv_dt:
+                raise ValueError(f"caches must be {kv_dt} [num_pages, {kv_shape}]")
         if k_cache.shape[0] != v_cache.shape[0]:
             raise ValueError("k_cache and v_cache page counts differ")
         if kv_indices.dtype != torch.int32 or kv_indices.numel() < self._nnz_pages:
@@ -446,14 +464,15 @@ class CascadeAttention:
             raise ValueError(f"lse must be float32 {(rows, d.num_qo_heads)}")
 
     def run(self, q, k_extend, v_extend, k_cache, v_cache, kv_indices, *, sm_scale: float,
-            window_left: int, return_lse: bool = True, out=None, lse=None, stream=None):
+            window_left: int, return_lse: bool = True, out=None, lse=None, stream=None,
+            k_scale: float = 1.0, v_scale: float = 1.0):
         if out is None:
             out = torch.empty_like(q)
         if return_lse and lse is None:
             lse = torch.empty(q.shape[0], q.shape[1], dtype=torch.float32, device=q.device)
         self._check_shapes(q, k_extend, v_extend, k_cache, v_cache, kv_indices, out, lse)
         pkvs_cascade_run(self.handle, q, k_extend, v_extend, k_cache, v_cache, kv_indices, out,
-                         lse, sm_scale, window_left, stream)
+                         lse, sm_scale, window_left, k_scale, v_scale, stream)
         return (out, lse) if return_lse else out
 
     def info(self) -> pkvs_plan_info:

@@ -325,13 +325,22 @@ def cascade_inputs(case: Case, trim_to: Optional[int] = None) -> CascadeInputs:
             keep[pg, : (P if i + 1 < np_ else last[-1])] = True
     pg_t = torch.tensor(rows_pg, dtype=torch.long, device=dev)
     sl_t = torch.tensor(rows_slot, dtype=torch.long, device=dev)
-    k_ext = case.k_cache[pg_t, sl_t].contiguous()
-    v_ext = case.v_cache[pg_t, sl_t].contiguous()
     drop = (~keep).to(dev)
-    k_cache = case.k_cache.clone()
-    v_cache = case.v_cache.clone()
-    k_cache[drop] = float("nan")
-    v_cache[drop] = float("nan")
+    eight_bit = case.k_cache.element_size() == 1
+    caches = []
+    for cache in (case.k_cache, case.v_cache):
+        if eight_bit:
+            # 8-bit floats: move raw bytes; 0x7f is NaN in both e4m3 and e5m2
+            raw = cache.view(torch.uint8)
+            ext = raw[pg_t, sl_t].contiguous().view(cache.dtype)
+            poisoned = raw.clone()
+            poisoned[drop] = 0x7F
+            caches.append((ext, poisoned.view(cache.dtype)))
+        else:
+            poisoned = cache.clone()
+            poisoned[drop] = float("nan")
+            caches.append((cache[pg_t, sl_t].contiguous(), poisoned))
+    (k_ext, k_cache), (v_ext, v_cache) = caches
     kv_indices = torch.cat(new_idx).to(torch.int32) if new_idx else torch.zeros(0, dtype=torch.int32)
     return CascadeInputs(
         k_extend=k_ext, v_extend=v_ext, k_cache=k_cache, v_cache=v_cache,

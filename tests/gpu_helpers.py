@@ -18,6 +18,12 @@ def log(msg: str) -> None:
     print(msg, flush=True)
 
 
+def kv_dtype_of(case: Case):
+    """The 8-bit cache type of a case, or None when the cache is in its dtype."""
+    return case.k_cache.dtype if case.k_cache.dtype in (torch.float8_e4m3fn,
+                                                        torch.float8_e5m2) else None
+
+
 def make_attention(case: Case, window_left=None, fixed_split_size=None, disable_split_kv=False,
                    batch_capacity=None, kv_capacity=None, qo_capacity=None, prefill_variant=0):
     W = case.window_left if window_left is None else window_left
@@ -30,7 +36,8 @@ def make_attention(case: Case, window_left=None, fixed_split_size=None, disable_
         batch_capacity=batch_capacity or max(case.batch_size, 1),
         qo_capacity=qo_capacity or max(int(case.qo_indptr[-1]), 1),
         kv_capacity=kv_capacity or max(max(case.kv_lens, default=1), 1),
-        prefill_variant=prefill_variant, logits_soft_cap=case.logits_soft_cap)
+        prefill_variant=prefill_variant, logits_soft_cap=case.logits_soft_cap,
+        kv_dtype=kv_dtype_of(case))
 
 
 def gpu_run(case: Case, window_left=None, att=None, return_lse=True, **kw):
@@ -40,7 +47,8 @@ def gpu_run(case: Case, window_left=None, att=None, return_lse=True, **kw):
     att.plan(qo_indptr=case.qo_indptr.cpu(), kv_indptr=case.kv_indptr.cpu(),
              kv_last_page_len=case.kv_last_page_len.cpu())
     res = att.run(case.q, case.k_cache, case.v_cache, case.kv_indices, sm_scale=case.sm_scale,
-                  window_left=W, causal=case.causal, return_lse=return_lse)
+                  window_left=W, causal=case.causal, return_lse=return_lse,
+                  k_scale=case.k_scale, v_scale=case.v_scale)
     torch.cuda.synchronize()
     return res
 

@@ -10,7 +10,8 @@ import pytest
 import torch
 
 import oracle
-from gpu_helpers import (compare, gpu_run, log, make_attention, oracle_for, sub_case)
+from gpu_helpers import (compare, gpu_run, kv_dtype_of, log, make_attention, oracle_for,
+                         sub_case)
 from paged_kv_sliding_amd import pkvs as P
 from paged_kv_sliding_amd.synth import build_case, cascade_inputs, case_from_lengths
 
@@ -19,11 +20,12 @@ DEV = "cuda"
 
 
 def small(qo, kv, *, H_q=4, H_kv=1, D=128, P_=16, W=31, seed=0, dtype=torch.bfloat16,
-          decode=False, split=-1, spare=3, cap=0.0):
+          decode=False, split=-1, spare=3, cap=0.0, kv_dtype=None, k_scale=1.0, v_scale=1.0):
     return case_from_lengths("small", qo, kv, num_qo_heads=H_q, num_kv_heads=H_kv, head_dim=D,
                              page_size=P_, dtype=dtype, window_left=W, seed=seed,
                              spare_pages=spare, device=DEV, is_decode=decode,
-                             fixed_split_size=split, logits_soft_cap=cap)
+                             fixed_split_size=split, logits_soft_cap=cap, kv_dtype=kv_dtype,
+                             k_scale=k_scale, v_scale=v_scale)
 
 
 # ----------------------------------------------------------------- the five workloads
@@ -476,7 +478,8 @@ def make_cascade(case, window_left=None, prefill_variant=0, qo_capacity=None,
         batch_capacity=batch_capacity or max(case.batch_size, 1),
         qo_capacity=qo_capacity or max(int(case.qo_indptr[-1]), 1),
         kv_capacity=kv_capacity or max(max(prefix, default=1), 1),
-        prefill_variant=prefill_variant, logits_soft_cap=case.logits_soft_cap)
+        prefill_variant=prefill_variant, logits_soft_cap=case.logits_soft_cap,
+        kv_dtype=kv_dtype_of(case))
 
 
 def cascade_run(case, trim=False, att=None, return_lse=True, **kw):
@@ -486,8 +489,15 @@ def cascade_run(case, trim=False, att=None, return_lse=True, **kw):
         att = make_cascade(case, **kw)
     att.plan(qo_indptr=case.qo_indptr.cpu(), kv_indptr=cin.kv_indptr,
              kv_last_page_len=cin.kv_last_page_len)
-    res = att.run(case.q, cin.k_extend, cin.v_extend, cin.k_cache, cin.v_cache, cin.kv_indices,
-                  sm_scale=case.sm_scale, window_left=W, return_lse=return_lse)
+    k_ext, v_ext = cin.k_extend, cin.v_extend
+    if kv_dtype_of(case) is not None:
+        # the new tokens' K/V arrive in the query dtype (the cache values times
+        # their scales: power-of-two scales keep them exact)
+        k_ext = (k_ext.float() * case.k_scale).to(case.dtype)
+        v_ext = (v_ext.float() * case.v_scale).to(case.dtype)
+    res = att.run(case.q, k_ext, v_ext, cin.k_cache, cin.v_cache, cin.kv_indices,
+                  sm_scale=case.sm_scale, window_left=W, return_lse=return_lse,
+                  k_scale=case.k_scale, v_scale=case.v_scale)
     torch.cuda.synchronize()
     return res, att
 
@@ -855,3 +865,68 @@ def test_fp16_cascade_and_soft_cap():
     o, lse = gpu_run(capped)
     ro, rl = oracle_for(capped)
     compare(o, lse, ro, rl, tag="fp16 soft cap")
+
+
+# ----------------------------------------------------------------- 8-bit KV caches
+# sglang flashinfer_backend.py passes k_scale / v_scale with the cache; an
+# 8-bit (OCP e4m3 / e5m2) cache holds K / k_scale and V / v_scale.  The oracle
+# widens every byte exactly; the kernels widen on the way to the matrix cores.
+
+FP8 = [torch.float8_e4m3fn, torch.float8_e5m2]
+
+
+@pytest.mark.parametrize("kv_dtype", FP8)
+@pytest.mark.parametrize("variant", [0, 1, 2])
+@pytest.mark.parametrize("W", [-1, 33])
+def test_fp8_kv_prefill(kv_dtype, variant, W):
+    qo = [1, 70, 0, 33, 129, 5, 300]
+    kv = [1, 70, 9, 300, 129, 700, 301]
+    case = small(qo, kv, H_q=8, H_kv=2, D=128, P_=16, W=W, seed=800 + variant * 10 + W,
+                 kv_dtype=kv_dtype, k_scale=0.05, v_scale=0.07)
+    att = make_attention(case, prefill_variant=variant)
+    o, lse = gpu_run(case, att=att)
+    assert att.info().prefill_variant in (1, 2)
+    ro, rl = oracle_for(case)
+    compare(o, lse, ro, rl, tag=f"fp8 {kv_dtype} prefill variant={variant} W={W}")
+
+
+@pytest.mark.parametrize("kv_dtype", FP8)
+@pytest.mark.parametrize("D,G", [(64, 4), (128, 8), (256, 2)])
+@pytest.mark.parametrize("W,split", [(-1, 64), (127, -1)])
+def test_fp8_kv_decode(kv_dtype, D, G, W, split):
+    kv = [1, 300, 77, 2000, 64, 900]
+    case = small([1] * len(kv), kv, H_q=2 * G, H_kv=2, D=D, P_=16, W=W, seed=D + G + W,
+                 decode=True, split=split, kv_dtype=kv_dtype, k_scale=0.05, v_scale=0.07)
+    o, lse = gpu_run(case)
+    ro, rl = oracle_for(case)
+    compare(o, lse, ro, rl, tag=f"fp8 {kv_dtype} decode D={D} G={G} W={W} split={split}")
+
+
+@pytest.mark.parametrize("kv_dtype", FP8)
+def test_fp8_kv_head_shapes_fp16_cascade(kv_dtype):
+    for D, G in ((64, 8), (256, 1)):
+        case = small([40, 130, 7], [90, 130, 500], H_q=2 * G, H_kv=2, D=D, P_=16, W=63,
+                     seed=D * G, kv_dtype=kv_dtype, k_scale=0.05, v_scale=0.07)
+        o, lse = gpu_run(case)
+        ro, rl = oracle_for(case)
+        compare(o, lse, ro, rl, tag=f"fp8 prefill D={D} G={G}")
+    case = small([70, 33], [70, 300], H_q=8, H_kv=2, D=128, P_=16, W=-1, seed=81,
+                 dtype=torch.float16, kv_dtype=kv_dtype, k_scale=0.05, v_scale=0.07)
+    o, lse = gpu_run(case)
+    assert o.dtype == torch.float16
+    ro, rl = oracle_for(case)
+    compare(o, lse, ro, rl, tag="fp8 K/V with fp16 queries")
+    cas = small([40, 130, 7], [90, 130, 500], H_q=8, H_kv=2, D=128, P_=16, W=63, seed=82,
+                kv_dtype=kv_dtype, k_scale=0.0625, v_scale=0.125)
+    (o, lse), _ = cascade_run(cas, trim=True)
+    ro, rl = oracle_for(cas)
+    compare(o, lse, ro, rl, tag="fp8 cascade")
+
+
+def test_kv_scales_on_a_16_bit_cache():
+    """The scales apply to every cache type: a bf16 cache read as 0.5 K, 1.5 V."""
+    case = small([30, 9], [90, 40], H_q=8, H_kv=2, D=128, W=10, seed=83, k_scale=0.5,
+                 v_scale=1.5)
+    o, lse = gpu_run(case)
+    ro, rl = oracle_for(case)
+    compare(o, lse, ro, rl, tag="scales on bf16")

@@ -271,14 +271,17 @@ def test_run_rejects_a_window_other_than_the_planned_one():
     qop, kvp, last = csr([5], [5], 16)
     P.pkvs_prefill_plan(h, qop, kvp, last, 1, None, None)
     lib = P._lib
-    rc = lib.pkvs_prefill_run(h, None, None, None, 1, None, None, None, 1.0, 30, 1, None)
+    rc = lib.pkvs_prefill_run(h, None, None, None, 1, None, None, None, 1.0, 30, 1, 1.0, 1.0,
+                              None)
     assert rc == P.PKVS_ERR_PLAN_MISMATCH
-    rc = lib.pkvs_prefill_run(h, None, None, None, 1, None, None, None, 1.0, 31, 0, None)
+    rc = lib.pkvs_prefill_run(h, None, None, None, 1, None, None, None, 1.0, 31, 0, 1.0, 1.0,
+                              None)
     assert rc == P.PKVS_ERR_PLAN_MISMATCH
-    rc = lib.pkvs_prefill_run(h, None, None, None, 1, None, None, None, 1.0, 31, 1, None)
+    rc = lib.pkvs_prefill_run(h, None, None, None, 1, None, None, None, 1.0, 31, 1, 1.0, 1.0,
+                              None)
     assert rc == P.PKVS_ERR_NOT_PLANNED  # a dry plan cannot run
     hd = P.pkvs_plan_create(desc(P.PKVS_DECODE, num_qo_heads=4, window_left=0))
-    rc = lib.pkvs_decode_run(hd, None, None, None, 1, None, None, None, 1.0, -1, None)
+    rc = lib.pkvs_decode_run(hd, None, None, None, 1, None, None, None, 1.0, -1, 1.0, 1.0, None)
     assert rc == P.PKVS_ERR_PLAN_MISMATCH
 
 
@@ -388,11 +391,14 @@ def test_cascade_workspace_and_errors():
     assert rc == P.PKVS_ERR_WORKSPACE, P.last_error()
     # run: window other than the planned one, a dry plan, the wrong kind
     lib = P._lib
-    rc = lib.pkvs_cascade_run(h, None, None, None, None, None, 1, None, None, None, 1.0, 30, None)
+    rc = lib.pkvs_cascade_run(h, None, None, None, None, None, 1, None, None, None, 1.0, 30,
+                              1.0, 1.0, None)
     assert rc == P.PKVS_ERR_PLAN_MISMATCH
-    rc = lib.pkvs_cascade_run(h, None, None, None, None, None, 1, None, None, None, 1.0, 31, None)
+    rc = lib.pkvs_cascade_run(h, None, None, None, None, None, 1, None, None, None, 1.0, 31,
+                              1.0, 1.0, None)
     assert rc == P.PKVS_ERR_NOT_PLANNED
-    rc = lib.pkvs_cascade_run(hp, None, None, None, None, None, 1, None, None, None, 1.0, 31, None)
+    rc = lib.pkvs_cascade_run(hp, None, None, None, None, None, 1, None, None, None, 1.0, 31,
+                              1.0, 1.0, None)
     assert rc == P.PKVS_ERR_INVALID_ARG
     # a window needs causal attention, as for prefill
     assert err_code(lambda: P.pkvs_plan_create(desc(P.PKVS_CASCADE, causal=False))) == \
@@ -437,3 +443,30 @@ def test_append_and_build_reject_bad_arguments():
 def test_soft_cap_must_be_zero_or_positive_finite(cap):
     assert err_code(lambda: P.pkvs_plan_create(desc(logits_soft_cap=cap))) == \
         P.PKVS_ERR_INVALID_ARG
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(kv_dtype=torch.float8_e4m3fn, dtype=torch.float32), P.PKVS_ERR_UNSUPPORTED),
+    (dict(kv_dtype=torch.float8_e5m2, prefill_variant=4), P.PKVS_ERR_UNSUPPORTED),
+    (dict(kv_dtype=torch.float8_e5m2, prefill_variant=3), P.PKVS_ERR_UNSUPPORTED),
+])
+def test_fp8_kv_descriptor_rules(kw, code):
+    assert err_code(lambda: P.pkvs_plan_create(desc(**kw))) == code
+
+
+def test_fp8_kv_format_and_scales_are_checked():
+    d = desc()
+    d.kv_format = 7
+    assert err_code(lambda: P.pkvs_plan_create(d)) == P.PKVS_ERR_INVALID_ARG
+    # an 8-bit cache never takes the direct-to-LDS kernel, even where it would be chosen
+    h = P.pkvs_plan_create(desc(kv_dtype=torch.float8_e4m3fn, head_dim=128, num_qo_heads=32,
+                                num_kv_heads=8, qo_capacity=32768, kv_capacity=32768))
+    assert P.pkvs_plan_get_info(h).prefill_variant in (1, 2)
+    lib = P._lib
+    for ks, vs in ((0.0, 1.0), (1.0, -2.0), (float("inf"), 1.0), (1.0, float("nan"))):
+        rc = lib.pkvs_prefill_run(h, None, None, None, 1, None, None, None, 1.0, 31, 1, ks, vs,
+                                  None)
+        assert rc == P.PKVS_ERR_INVALID_ARG, (ks, vs)
+        rc = lib.pkvs_decode_run(h, None, None, None, 1, None, None, None, 1.0, 31, ks, vs, None)
+        assert rc == P.PKVS_ERR_INVALID_ARG, (ks, vs)
+    P.pkvs_plan_destroy(h)
