@@ -25,6 +25,7 @@ Reported (one JSON line):
                  prefixes, beside the one paged prefill of the same batch
   pool           cache writes of a 32768-token prompt's K/V and the split
                  decode's page-table build, timed apart
+  decode_fp8_kv  the split decode over an e4m3 copy of its cache, timed apart
 
     python bench.py [--steps K] [--warmup W] [--gpus 1] [--no-cpu-baseline]
 """
@@ -176,6 +177,53 @@ def bench_cascade(reps: int) -> dict:
         del ci, c
         torch.cuda.empty_cache()
     return out
+
+
+def bench_decode_fp8(dec, W: int, reps: int) -> dict:
+    """The split decode batch over an e4m3 copy of its cache (K / k_scale,
+    V / v_scale, converted in chunks on the device), same plan otherwise; KV
+    bytes counted at one byte per element."""
+    import torch
+
+    from paged_kv_sliding_amd import pkvs as P
+
+    ks, vs = 0.0625, 0.0625
+    k8 = torch.empty(dec.k_cache.shape, dtype=torch.float8_e4m3fn, device="cuda")
+    v8 = torch.empty_like(k8)
+    step = 16384
+    for i in range(0, k8.shape[0], step):
+        k8[i:i + step] = (dec.k_cache[i:i + step].float() / ks).to(torch.float8_e4m3fn)
+        v8[i:i + step] = (dec.v_cache[i:i + step].float() / vs).to(torch.float8_e4m3fn)
+    att = P.BatchAttention(P.PKVS_DECODE, num_qo_heads=dec.num_qo_heads,
+                           num_kv_heads=dec.num_kv_heads, head_dim=dec.head_dim,
+                           page_size=dec.page_size, dtype=dec.dtype, window_left=W,
+                           fixed_split_size=dec.fixed_split_size, batch_capacity=dec.batch_size,
+                           kv_capacity=max(dec.kv_lens), kv_dtype=torch.float8_e4m3fn)
+    att.plan(kv_indptr=dec.kv_indptr.cpu(), kv_last_page_len=dec.kv_last_page_len.cpu())
+    o = torch.empty_like(dec.q)
+    lse = torch.empty(dec.q.shape[:2], dtype=torch.float32, device="cuda")
+
+    def run():
+        att.run(dec.q, k8, v8, dec.kv_indices, sm_scale=dec.sm_scale, window_left=W, out=o,
+                lse=lse, k_scale=ks, v_scale=vs)
+
+    for _ in range(3):
+        run()
+    ts = []
+    for _ in range(reps):
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record()
+        run()
+        b.record()
+        torch.cuda.synchronize()
+        ts.append(a.elapsed_time(b))
+    ms = sum(ts) / len(ts)
+    nb = decode_bytes(dec, W) // 2
+    del k8, v8
+    torch.cuda.empty_cache()
+    return {"format": "e4m3", "ms": round(ms, 4), "kv_bytes": nb,
+            "GB/s": round(nb / (ms * 1e-3) / 1e9, 1),
+            "frac_of_hbm_peak": round(nb / (ms * 1e-3) / 1e9 / PEAK_HBM_GBPS, 4)}
 
 
 def bench_pool(reps: int) -> dict:
@@ -494,7 +542,10 @@ def main():
 
     # the no-window decode of the same batch, timed apart (not part of the step)
     full = None
+    fp8 = None
     if args.only == "all":
+        print("bench: decode over an 8-bit cache", file=sys.stderr, flush=True)
+        fp8 = bench_decode_fp8(dec, W_dec, max(5, args.steps // 2))
         dec_att_full.plan(kv_indptr=dec_host[0], kv_last_page_len=dec_host[1])
         for _ in range(2):
             dec_att_full.run(dec.q, dec.k_cache, dec.v_cache, dec.kv_indices,
@@ -560,6 +611,8 @@ def main():
                                    "work_per_launch": nbytes}
     if full is not None:
         line["decode_no_window"] = full
+    if fp8 is not None:
+        line["decode_fp8_kv"] = fp8
     if args.only == "all":
         print("bench: cascade prefill", file=sys.stderr, flush=True)
         line["cascade"] = bench_cascade(max(5, args.steps // 2))

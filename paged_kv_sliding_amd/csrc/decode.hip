@@ -267,8 +267,8 @@ __device__ __forceinline__ void decode_compute(const DecodeBuf<D, KVF> &buf, Dec
 // Register buffers in the pipeline: for D <= 128 one wave holds three 32-key
 // buffers (two in flight while the third is consumed) and still fits in one
 // wave's 512 registers; D = 256 keeps two.
-template <int D>
-constexpr int decode_stages() { return D >= 256 ? 2 : 3; }
+template <int D, int KVF>
+constexpr int decode_stages() { return KVF == 0 ? (D >= 256 ? 2 : 3) : (D >= 256 ? 3 : 4); }
 
 // NS register buffers of 32 keys each: NS-1 blocks are in flight while one is
 // being computed.
@@ -432,13 +432,13 @@ static hipError_t launch_decode_t(const DecodeArgs &a, int head_dim, int grid, h
 {
     switch (head_dim) {
     case 64:
-        decode_kernel<64, decode_stages<64>(), F16, KVF><<<grid, kDecodeThreads, 0, s>>>(a);
+        decode_kernel<64, decode_stages<64, KVF>(), F16, KVF><<<grid, kDecodeThreads, 0, s>>>(a);
         break;
     case 128:
-        decode_kernel<128, decode_stages<128>(), F16, KVF><<<grid, kDecodeThreads, 0, s>>>(a);
+        decode_kernel<128, decode_stages<128, KVF>(), F16, KVF><<<grid, kDecodeThreads, 0, s>>>(a);
         break;
     case 256:
-        decode_kernel<256, decode_stages<256>(), F16, KVF><<<grid, kDecodeThreads, 0, s>>>(a);
+        decode_kernel<256, decode_stages<256, KVF>(), F16, KVF><<<grid, kDecodeThreads, 0, s>>>(a);
         break;
     default: return hipErrorInvalidValue;
     }
@@ -491,15 +491,15 @@ static int decode_blocks_per_cu_t(int head_dim)
     switch (head_dim) {
     case 64:
         e = hipOccupancyMaxActiveBlocksPerMultiprocessor(
-            &n, decode_kernel<64, decode_stages<64>(), F16, KVF>, kDecodeThreads, 0);
+            &n, decode_kernel<64, decode_stages<64, KVF>(), F16, KVF>, kDecodeThreads, 0);
         break;
     case 128:
         e = hipOccupancyMaxActiveBlocksPerMultiprocessor(
-            &n, decode_kernel<128, decode_stages<128>(), F16, KVF>, kDecodeThreads, 0);
+            &n, decode_kernel<128, decode_stages<128, KVF>(), F16, KVF>, kDecodeThreads, 0);
         break;
     case 256:
         e = hipOccupancyMaxActiveBlocksPerMultiprocessor(
-            &n, decode_kernel<256, decode_stages<256>(), F16, KVF>, kDecodeThreads, 0);
+            &n, decode_kernel<256, decode_stages<256, KVF>(), F16, KVF>, kDecodeThreads, 0);
         break;
     }
     return e == hipSuccess ? n : 0;
