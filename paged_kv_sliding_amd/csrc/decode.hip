@@ -51,16 +51,48 @@ __device__ __forceinline__ u32x2 load_stream8(const void *p)
     return __builtin_nontemporal_load(reinterpret_cast<const u32x2 *>(p));
 }
 
-// Loaded K/V of one 32-key block, as stored: 8 elements per slot (16 bytes of
-// a 16-bit cache, 8 bytes of an 8-bit one, widened where they are used).
+__device__ __forceinline__ u32x4 load_stream16(const void *p)
+{
+    return __builtin_nontemporal_load(reinterpret_cast<const u32x4 *>(p));
+}
+
+// Loaded K/V of one 32-key block, as stored, widened where they are used.
+// V: 8 elements per slot (16 bytes of a 16-bit cache, 8 of an 8-bit one).
+// K: a 16-bit slot holds the 8 dims of one k-step; an 8-bit slot holds 16
+// contiguous bytes, the dims of two k-steps (k-step 2t+h of lane group g
+// takes dims 64t + 16g + 8h ..+7; the query operand uses the same map), so
+// every K load moves 16 bytes per lane.
 template <int D, int KVF>
 struct DecodeBuf {
     static constexpr int KS = D / 32;            // QK k-steps (32 dims each)
     static constexpr int NV = D >= 128 ? D / 128 : 1;
+    static constexpr int KN = KVF == 0 ? KS : KS / 2;  // K slots per key row
     using Raw = typename std::conditional<KVF == 0, bf16x8, u32x2>::type;
-    Raw k0[KS], k1[KS];                          // keys blk+r, blk+16+r
+    using KRaw = typename std::conditional<KVF == 0, bf16x8, u32x4>::type;
+    KRaw k0[KN], k1[KN];                         // keys blk+r, blk+16+r
     Raw v[NV][8];                                // 8 keys x 8 dims per 128-dim chunk
 };
+
+// first dim of k-step s for lane group g (see DecodeBuf)
+template <int KVF>
+__device__ __forceinline__ int kstep_dim(int s, int g)
+{
+    return KVF == 0 ? 32 * s + 8 * g : 64 * (s >> 1) + 16 * g + 8 * (s & 1);
+}
+
+// the K operand of k-step s from a key's slots
+template <int D, bool F16, int KVF>
+__device__ __forceinline__ bf16x8 k_operand(const typename DecodeBuf<D, KVF>::KRaw (&k)[DecodeBuf<D, KVF>::KN],
+                                            int s)
+{
+    if constexpr (KVF == 0) {
+        return k[s];
+    } else {
+        const u32x4 x = k[s >> 1];
+        const u32x2 h = (s & 1) ? u32x2{x[2], x[3]} : u32x2{x[0], x[1]};
+        return widen_fp8<KVF, F16>(h);
+    }
+}
 
 template <bool F16, int KVF>
 __device__ __forceinline__ bf16x8 widen_slot(const typename DecodeBuf<64, KVF>::Raw &x)
@@ -173,10 +205,18 @@ __device__ __forceinline__ void decode_load(DecodeBuf<D, KVF> &buf, const Decode
         if constexpr (KVF == 0) return load_stream(p);
         else return load_stream8(p);
     };
+    if constexpr (KVF == 0) {
 #pragma unroll
-    for (int s = 0; s < KS; ++s) {
-        buf.k0[s] = load(K + rk0 + 32 * s + 8 * g);
-        buf.k1[s] = load(K + rk1 + 32 * s + 8 * g);
+        for (int s = 0; s < KS; ++s) {
+            buf.k0[s] = load_stream(K + rk0 + 32 * s + 8 * g);
+            buf.k1[s] = load_stream(K + rk1 + 32 * s + 8 * g);
+        }
+    } else {
+#pragma unroll
+        for (int t = 0; t < Buf::KN; ++t) {
+            buf.k0[t] = load_stream16(K + rk0 + 64 * t + 16 * g);
+            buf.k1[t] = load_stream16(K + rk1 + 64 * t + 16 * g);
+        }
     }
     // (D = 64: lanes r >= 8 read a valid slice of the row and drop it)
     const int dv = min(8 * r, D - 8);
@@ -207,8 +247,8 @@ __device__ __forceinline__ void decode_compute(const DecodeBuf<D, KVF> &buf, Dec
     f32x4 s0 = {0.f, 0.f, 0.f, 0.f}, s1 = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
     for (int s = 0; s < KS; ++s) {
-        s0 = mfma16x16x32<F16>(widen_slot<F16, KVF>(buf.k0[s]), qf[s], s0);
-        s1 = mfma16x16x32<F16>(widen_slot<F16, KVF>(buf.k1[s]), qf[s], s1);
+        s0 = mfma16x16x32<F16>(k_operand<D, F16, KVF>(buf.k0, s), qf[s], s0);
+        s1 = mfma16x16x32<F16>(k_operand<D, F16, KVF>(buf.k1, s), qf[s], s1);
     }
     // lane holds keys blk+4g+i (s0[i]) and blk+16+4g+i (s1[i]) of head lane%16
     float x[8];
@@ -289,12 +329,13 @@ __global__ __launch_bounds__(kDecodeThreads) void decode_kernel(DecodeArgs a)
         const int page_base = w[kDiPageBase], slot = w[kDiSlot];
         (void)r;
 
-        // Q^T operand: head r of the group, dims 32s+8g..+8 (zero for padding heads)
+        // Q^T operand: head r of the group, the dims of k-step s for lane
+        // group g (kstep_dim; zero for padding heads)
         bf16x8 qf[KS];
         const int64_t qrow = (int64_t(b) * a.num_qo_heads + hk * G + r) * D;
 #pragma unroll
         for (int s = 0; s < KS; ++s)
-            qf[s] = r < G ? load_bf16x8(Q + qrow + 32 * s + 8 * g) : zero_bf16x8();
+            qf[s] = r < G ? load_bf16x8(Q + qrow + kstep_dim<KVF>(s, g)) : zero_bf16x8();
 
         DecodeState<D> st;
         st.m = kNegInf;
