@@ -66,6 +66,13 @@ class OracleLib:
         lib.oracle_widen.argtypes = [i32, P, i64, P]
         lib.oracle_append_kv.restype = i64
         lib.oracle_append_kv.argtypes = [i64, P, i64, P, P, i64, P, P]
+        lib.oracle_quantize.restype = ctypes.c_uint8
+        lib.oracle_quantize.argtypes = [i32, f64, ctypes.c_float, i32]
+        lib.oracle_quantize_many.restype = None
+        lib.oracle_quantize_many.argtypes = [i32, P, i64, ctypes.c_float, i32, P]
+        lib.oracle_append_kv_quant.restype = i64
+        lib.oracle_append_kv_quant.argtypes = [i64, P, i64, i32, P, P, i64, i32, ctypes.c_float,
+                                               ctypes.c_float, P, P]
         lib.oracle_build_kv_indices.restype = i64
         lib.oracle_build_kv_indices.argtypes = [i32, P, i64, i64, P, P, P, P, P, i64]
         self.lib = lib
@@ -240,4 +247,44 @@ def widen(t, impl: Optional[OracleLib] = None) -> np.ndarray:
     out = np.empty(a.size, dtype=np.float64)
     lib.oracle_widen(code, _ptr(a), a.size, _ptr(out))
     return out
+
+
+def quantize(x, scale: float, kv_dtype, impl: Optional[OracleLib] = None):
+    """uint8 codes of the elements of tensor ``x`` divided by ``scale`` and
+    rounded to the 8-bit type ``kv_dtype`` (torch.float8_e4m3fn / e5m2), the
+    way an 8-bit cache write does it."""
+    import torch
+
+    lib = (impl or _load()).lib
+    a, code = _as_stored(x)
+    a = np.ascontiguousarray(a).reshape(-1)
+    kd = FP8_E4M3 if kv_dtype == torch.float8_e4m3fn else FP8_E5M2
+    out = np.empty(a.size, dtype=np.uint8)
+    lib.oracle_quantize_many(code, _ptr(a), a.size, float(scale), kd, _ptr(out))
+    return out
+
+
+def append_kv_quant(k_new, v_new, loc, k_cache, v_cache, k_scale: float, v_scale: float,
+                    impl: Optional[OracleLib] = None):
+    """Host copies of 8-bit caches after writing row i of k_new / v_new (16 or
+    32-bit), divided by the scales and rounded, to slot loc[i]; returns
+    (k_cache, v_cache, skipped rows)."""
+    import torch
+
+    lib = (impl or _load()).lib
+    kc = k_cache.detach().cpu().contiguous().clone()
+    vc = v_cache.detach().cpu().contiguous().clone()
+    ka, code = _as_stored(k_new)
+    va, code2 = _as_stored(v_new)
+    assert code == code2
+    _, kd = _as_stored(kc)
+    n = k_new.shape[0]
+    elems = k_new[0].numel() if n else 0
+    num_slots = kc.numel() // elems if elems else 0
+    lo = np.ascontiguousarray(torch.as_tensor(loc).cpu().numpy().astype(np.int64))
+    kb, vb = kc.view(torch.uint8).numpy(), vc.view(torch.uint8).numpy()
+    skipped = lib.oracle_append_kv_quant(n, _ptr(lo), elems, code, _ptr(np.ascontiguousarray(ka)),
+                                         _ptr(np.ascontiguousarray(va)), num_slots, kd,
+                                         float(k_scale), float(v_scale), _ptr(kb), _ptr(vb))
+    return kc, vc, int(skipped)
 

@@ -335,6 +335,123 @@ int64_t oracle_append_kv(int64_t n, const int64_t *loc, int64_t row_bytes, const
 }
 
 /*
+ * Rounding to the 8-bit cache formats (the cast of set_kv_buffer when the
+ * pool holds 8-bit floats): round to nearest, ties to even mantissa.  E4M3
+ * ("fn", bias 7, 3 mantissa bits, largest 448, no infinities): a value that
+ * rounds past 448, an infinity or a NaN becomes NaN (S.1111.111).  E5M2 (bias
+ * 15, 2 mantissa bits, largest 57344): a value that rounds past 57344 becomes
+ * +-inf, a NaN stays NaN.  Subnormals are kept (steps of 2^-9 and 2^-16).
+ */
+/* binade of a > 0: the e with 2^e <= a < 2^(e+1) */
+static int binade(double a)
+{
+    int e = (int)floor(log2(a));
+    if (ldexp(1.0, e) > a)
+        --e;
+    if (ldexp(1.0, e + 1) <= a)
+        ++e;
+    return e;
+}
+
+/* a >= 0 rounded to the grid of a float format with mbits mantissa bits and
+ * smallest normal exponent emin (subnormal steps below it), ties to even */
+static double round_to_grid(double a, int mbits, int emin)
+{
+    if (a == 0.0)
+        return 0.0;
+    int e = binade(a);
+    if (e < emin)
+        e = emin;
+    const double q = ldexp(1.0, e - mbits); /* the step of that binade */
+    double r = floor(a / q);                /* a / q is exact: q is 2^k */
+    const double frac = a / q - r;
+    if (frac > 0.5 || (frac == 0.5 && fmod(r, 2.0) != 0.0))
+        r += 1.0;
+    return r * q;
+}
+
+static uint8_t round_to_fp8(double v, int e4)
+{
+    const int mbits = e4 ? 3 : 2, bias = e4 ? 7 : 15;
+    const uint8_t sign = signbit(v) ? 0x80 : 0;
+    if (isnan(v))
+        return (uint8_t)(sign | 0x7f);
+    const double a = fabs(v);
+    /* E4M3: 464 ties to 448 (even); above it the value rounds onto the NaN
+     * pattern.  E5M2: 61440 ties to 65536 (even), i.e. overflows to inf. */
+    if (e4 ? (a > 464.0) : (a >= 61440.0))
+        return (uint8_t)(sign | (e4 ? 0x7f : 0x7c));
+    const double r = round_to_grid(a, mbits, 1 - bias);
+    if (r == 0.0)
+        return sign;
+    const int e = binade(r);
+    if (e < 1 - bias) /* subnormal: r = f * 2^(1 - bias - mbits) */
+        return (uint8_t)(sign | (int)ldexp(r, bias - 1 + mbits));
+    const int f = (int)ldexp(r, mbits - e) - (1 << mbits);
+    return (uint8_t)(sign | ((e + bias) << mbits) | f);
+}
+
+/* RNE to bf16 or IEEE half (fp32: unchanged) */
+static double round_to_16(double v, int dtype)
+{
+    if (isnan(v) || isinf(v) || dtype == ORACLE_FP32)
+        return v;
+    const double a = fabs(v), sv = signbit(v) ? -1.0 : 1.0;
+    if (dtype == ORACLE_BF16) /* 8 exponent bits: overflow only past fp32's range */
+        return sv * round_to_grid(a, 7, -126);
+    if (a >= 65520.0) /* half: 65520 ties to 65536 (even), i.e. inf */
+        return sv * INFINITY;
+    return sv * round_to_grid(a, 10, -14);
+}
+
+/* The 8-bit encoding of one stored element x of in_dtype divided by scale the
+ * way set_kv_buffer does it: the quotient in fp32 (a correctly rounded single
+ * division), rounded to in_dtype, then to the 8-bit format. */
+uint8_t oracle_quantize(int32_t in_dtype, double x, float scale, int32_t kv_dtype)
+{
+    const float y = (float)x / scale;
+    return round_to_fp8(round_to_16((double)y, in_dtype), kv_dtype == ORACLE_FP8_E4M3);
+}
+
+/* oracle_quantize over n stored elements */
+void oracle_quantize_many(int32_t in_dtype, const void *src, int64_t n, float scale,
+                          int32_t kv_dtype, uint8_t *dst)
+{
+    for (int64_t i = 0; i < n; ++i)
+        dst[i] = oracle_quantize(in_dtype, load_elem(src, in_dtype, i), scale, kv_dtype);
+}
+
+/*
+ * Writing new keys and values into an 8-bit cache: row i of k_new / v_new
+ * (in_dtype, elems per row) goes to slot loc[i], each element quantized as
+ * oracle_quantize with k_scale / v_scale.  Out-of-pool slots are skipped and
+ * counted (returned).
+ */
+int64_t oracle_append_kv_quant(int64_t n, const int64_t *loc, int64_t elems, int32_t in_dtype,
+                               const void *k_new, const void *v_new, int64_t num_slots,
+                               int32_t kv_dtype, float k_scale, float v_scale, uint8_t *k_cache,
+                               uint8_t *v_cache)
+{
+    int64_t skipped = 0;
+    for (int64_t i = 0; i < n; ++i) {
+        const int64_t s = loc[i];
+        if (s < 0 || s >= num_slots) {
+            ++skipped;
+            continue;
+        }
+        for (int64_t e = 0; e < elems; ++e) {
+            k_cache[s * elems + e] =
+                oracle_quantize(in_dtype, load_elem(k_new, in_dtype, i * elems + e), k_scale,
+                                kv_dtype);
+            v_cache[s * elems + e] =
+                oracle_quantize(in_dtype, load_elem(v_new, in_dtype, i * elems + e), v_scale,
+                                kv_dtype);
+        }
+    }
+    return skipped;
+}
+
+/*
  * Building the page table on the device ([FIB] call_begin_forward: kv_indptr
  * is the running sum of the per-request lengths, and the gather
  * create_flashinfer_kv_indices_triton copies, for request b, entries

@@ -413,6 +413,23 @@ def check_kv_scales(impl=None):
         assert close(l3, l4) and close(o3, 1.9 * o4), dt
 
 
+def check_quantize_every_16_bit_pattern(impl=None):
+    """An 8-bit cache write divides by the scale in the input dtype and
+    rounds to the 8-bit type: for every bf16 and half bit pattern and three
+    scales the code equals torch's (x / scale).to(float8) (a NaN input gives a
+    NaN code; its sign is the platform's)."""
+    bits = torch.arange(-32768, 32768, dtype=torch.int32).to(torch.int16)
+    for src in (torch.bfloat16, torch.float16):
+        x = bits.view(src)
+        nan = torch.isnan(x).numpy()
+        for dt in (torch.float8_e4m3fn, torch.float8_e5m2):
+            for sc in (1.0, 0.0625, 0.37):
+                want = (x / torch.tensor(sc, dtype=torch.float32)).to(dt).view(torch.uint8).numpy()
+                got = oracle.quantize(x, sc, dt, impl=impl)
+                assert np.array_equal(got[~nan], want[~nan]), (src, dt, sc)
+                assert (got[nan] & 0x7F == 0x7F).all(), (src, dt, sc)
+
+
 def check_widening_every_16_bit_pattern(impl=None):
     """Every bf16 and every IEEE half bit pattern widens to the float64 that
     torch's / numpy's own conversions give (NaN patterns to NaN); fp32 values
@@ -527,6 +544,28 @@ def check_append_matches_scatter(impl=None):
         assert np.array_equal(got.view(torch.int16).numpy().reshape(24, 2, 8), want)
 
 
+def check_append_into_8_bit_cache(impl=None):
+    """Rows written into an 8-bit cache land at their slots as torch's
+    (row / scale).to(float8) (bf16 rows, e4m3 and e5m2, K and V with their
+    own scales); other slots keep their bytes; out-of-pool slots are counted."""
+    g = torch.Generator().manual_seed(8)
+    for dt in (torch.float8_e4m3fn, torch.float8_e5m2):
+        cache_k = (torch.randn(5, 4, 2, 8, generator=g) * 3).to(dt)
+        cache_v = (torch.randn(5, 4, 2, 8, generator=g) * 3).to(dt)
+        k_new = (torch.randn(6, 2, 8, generator=g) * 40).to(torch.bfloat16)
+        v_new = (torch.randn(6, 2, 8, generator=g) * 40).to(torch.bfloat16)
+        loc = torch.tensor([19, 0, -1, 7, 20, 3])
+        kc, vc, skipped = oracle.append_kv_quant(k_new, v_new, loc, cache_k, cache_v, 0.25, 0.4,
+                                                 impl=impl)
+        assert skipped == 2
+        for got, cache, new, sc in ((kc, cache_k, k_new, 0.25), (vc, cache_v, v_new, 0.4)):
+            want = cache.view(torch.uint8).reshape(20, 2, 8).clone()
+            ok = (loc >= 0) & (loc < 20)
+            q = (new / torch.tensor(sc, dtype=torch.float32)).to(dt).view(torch.uint8)
+            want[loc[ok]] = q[ok]
+            assert torch.equal(got.view(torch.uint8).reshape(20, 2, 8), want), dt
+
+
 def check_build_indices_golden(impl=None):
     """The hand-derived example of tests/golden/kv_indices_build.txt."""
     rows = {}
@@ -596,12 +635,14 @@ ALL_CHECKS = [
     check_decode_trim,
     check_widening_every_16_bit_pattern,
     check_widening_every_8_bit_pattern,
+    check_quantize_every_16_bit_pattern,
     check_kv_scales,
     check_soft_cap_brute_force,
     check_soft_cap_saturation,
     check_soft_cap_large_is_no_cap,
     check_append_round_trip,
     check_append_matches_scatter,
+    check_append_into_8_bit_cache,
     check_build_indices_golden,
     check_build_indices_reproduce_page_tables,
     check_build_indices_errors,

@@ -46,17 +46,32 @@ MUTANTS = {
                         "(load_elem(k_cache, kv_dtype, koff + d))"),
     "v_scale_on_keys": ("(k_scale * load_elem(k_cache, kv_dtype, koff + d))",
                         "(v_scale * load_elem(k_cache, kv_dtype, koff + d))"),
-    "fp8_bias": ("const int mbits = e4 ? 3 : 2, bias = e4 ? 7 : 15;",
-                 "const int mbits = e4 ? 3 : 2, bias = e4 ? 8 : 15;"),
+    "fp8_bias": ("const int e4 = dtype == ORACLE_FP8_E4M3;\n        const int mbits = e4 ? 3 : 2, bias = e4 ? 7 : 15;",
+                 "const int e4 = dtype == ORACLE_FP8_E4M3;\n        const int mbits = e4 ? 3 : 2, bias = e4 ? 8 : 15;"),
+    "fp8_encode_bias": ("static uint8_t round_to_fp8(double v, int e4)\n{\n    const int mbits = e4 ? 3 : 2, bias = e4 ? 7 : 15;",
+                        "static uint8_t round_to_fp8(double v, int e4)\n{\n    const int mbits = e4 ? 3 : 2, bias = e4 ? 8 : 15;"),
     "fp8_subnormal_scale": ("v = ldexp((double)f, 1 - bias - mbits);",
                             "v = ldexp((double)f, -bias - mbits);"),
+    "fp8_ties_away": ("if (frac > 0.5 || (frac == 0.5 && fmod(r, 2.0) != 0.0))\n        r += 1.0;\n    return r * q;",
+                      "if (frac >= 0.5)\n        r += 1.0;\n    return r * q;"),
+    "fp8_overflow_saturates": ("return (uint8_t)(sign | (e4 ? 0x7f : 0x7c));",
+                               "return (uint8_t)(sign | (e4 ? 0x7e : 0x7b));"),
+    "quantize_multiplies": ("const float y = (float)x / scale;", "const float y = (float)x * scale;"),
+    "quantize_skips_16_bit_rounding": (
+        "return round_to_fp8(round_to_16((double)y, in_dtype), kv_dtype == ORACLE_FP8_E4M3);",
+        "return round_to_fp8((double)y, kv_dtype == ORACLE_FP8_E4M3);"),
     "cap_of_unscaled_logit": ("s[j] = soft_cap * tanh(s[j] / soft_cap);",
                               "s[j] = soft_cap * tanh(dot / soft_cap);"),
     "cap_factor_dropped": ("s[j] = soft_cap * tanh(s[j] / soft_cap);",
                            "s[j] = tanh(s[j] / soft_cap);"),
     "append_values_from_keys": ("memcpy(v_cache + s * row_bytes, v_new + i * row_bytes",
                                 "memcpy(v_cache + s * row_bytes, k_new + i * row_bytes"),
-    "append_ignores_loc": ("const int64_t s = loc[i];", "const int64_t s = i;"),
+    "append_ignores_loc": ("memcpy(k_cache + s * row_bytes, k_new + i * row_bytes",
+                           "memcpy(k_cache + i * row_bytes, k_new + i * row_bytes"),
+    "append_quant_scale_swapped": (
+        "oracle_quantize(in_dtype, load_elem(k_new, in_dtype, i * elems + e), k_scale,",
+        "oracle_quantize(in_dtype, load_elem(k_new, in_dtype, i * elems + e), v_scale,"),
+    "append_quant_row_offset": ("k_cache[s * elems + e] =", "k_cache[(s ^ 1) * elems + e] ="),
     "indices_start_ignored": ("const int64_t s0 = start ? start[b] : 0;", "const int64_t s0 = 0;"),
     "indptr_not_cumulative": ("kv_indptr[b + 1] = (int32_t)(kv_indptr[b] + n);",
                               "kv_indptr[b + 1] = (int32_t)n;"),
