@@ -264,7 +264,14 @@ def bench_pool(reps: int) -> dict:
     out["kv_append"] = {"rows": n, "row_bytes": H * D * 2, "ms": round(ms, 4),
                         "bytes": nbytes, "GB/s": round(nbytes / (ms * 1e-3) / 1e9, 1),
                         "frac_of_hbm_peak": round(nbytes / (ms * 1e-3) / 1e9 / PEAK_HBM_GBPS, 4)}
-    del k_new, v_new, kc, vc
+    k8 = torch.empty(kc.shape, dtype=torch.float8_e4m3fn, device="cuda")
+    v8 = torch.empty_like(k8)
+    ms = timed(lambda: P.pkvs_append_kv(k_new, v_new, loc, k8, v8, k_scale=0.0625,
+                                        v_scale=0.0625))
+    nbytes = 2 * n * H * D * (2 + 1)  # bf16 rows read, e4m3 rows written
+    out["kv_append_e4m3"] = {"rows": n, "ms": round(ms, 4), "bytes": nbytes,
+                             "GB/s": round(nbytes / (ms * 1e-3) / 1e9, 1)}
+    del k_new, v_new, kc, vc, k8, v8
     gen = torch.Generator().manual_seed(5)
     kv = torch.randint(1024, 32769, (256,), generator=gen)
     npg = ((kv + 15) // 16).to(torch.int32)

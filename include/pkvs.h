@@ -282,16 +282,24 @@ int pkvs_merge_state(const void *v_a, const float *s_a, const void *v_b, const f
  *  loc_d         [num_tokens] int64 (device): the cache slot of each row,
  *                slot = page * page_size + position in the page
  *  k_cache, v_cache  the cache viewed as [num_slots, num_kv_heads, head_dim]
- *                (num_slots = num_pages * page_size), 16-byte aligned
+ *                (num_slots = num_pages * page_size), 16-byte aligned, in dtype
+ *                (kv_format PKVS_KV_SAME: rows copied bit for bit) or 8-bit
+ *                (PKVS_KV_FP8_E4M3 / _E5M2: every element x becomes the 8-bit
+ *                value of x / k_scale -- v_scale for values -- computed in fp32,
+ *                rounded to dtype, then to the 8-bit format to nearest even;
+ *                e4m3 overflow, infinities and NaN give NaN, e5m2 overflow
+ *                gives +-inf, as the cast of set_kv_buffer does)
+ *  k_scale, v_scale  positive finite; read only for an 8-bit cache
  *  status_d      nullable device int32: the kernel adds the number of rows
  *                whose slot lies outside [0, num_slots) (they are not written)
  * Slots must be distinct (two rows to one slot leave either).  One launch on
  * `stream`, no allocation.  Errors: INVALID_ARG (shape, null or misaligned
- * pointer), UNSUPPORTED (dtype, a row not a multiple of 16 bytes), HIP. */
+ * pointer, kv_format, scales), UNSUPPORTED (dtype, a row not a multiple of 16
+ * bytes), HIP. */
 int pkvs_append_kv(const void *k_new, const void *v_new, const int64_t *loc_d,
                    int64_t num_tokens, void *k_cache, void *v_cache, int64_t num_slots,
-                   int32_t num_kv_heads, int32_t head_dim, int32_t dtype, int32_t *status_d,
-                   hipStream_t stream);
+                   int32_t num_kv_heads, int32_t head_dim, int32_t dtype, int32_t kv_format,
+                   float k_scale, float v_scale, int32_t *status_d, hipStream_t stream);
 
 /* Build the page table on the device ([FIB] call_begin_forward: kv_indptr is
  * the running sum of the per-request lengths; create_flashinfer_kv_indices_triton

@@ -131,6 +131,10 @@ hipError_t launch_merge_state(const void *va, const float *sa, const void *vb, c
 hipError_t launch_append_kv(const void *k_new, const void *v_new, const int64_t *loc, int64_t n,
                             int64_t row_bytes, void *k_cache, void *v_cache, int64_t num_slots,
                             int32_t *status, int grid, hipStream_t s);
+hipError_t launch_append_kv_quant(const void *k_new, const void *v_new, const int64_t *loc,
+                                  int64_t n, int64_t row_elems, int in_dtype, int kv_format,
+                                  void *k_cache, void *v_cache, int64_t num_slots, float k_scale,
+                                  float v_scale, int32_t *status, int grid, hipStream_t s);
 hipError_t launch_build_kv_indices(const int32_t *map, int64_t map_rows, int64_t map_cols,
                                    const int32_t *slot, const int32_t *start, const int32_t *len,
                                    int32_t batch, int32_t *kv_indptr, int32_t *kv_indices,

@@ -280,8 +280,8 @@ int pkvs_merge_state(const void *v_a, const float *s_a, const void *v_b, const f
 
 int pkvs_append_kv(const void *k_new, const void *v_new, const int64_t *loc_d,
                    int64_t num_tokens, void *k_cache, void *v_cache, int64_t num_slots,
-                   int32_t num_kv_heads, int32_t head_dim, int32_t dtype, int32_t *status_d,
-                   hipStream_t stream)
+                   int32_t num_kv_heads, int32_t head_dim, int32_t dtype, int32_t kv_format,
+                   float k_scale, float v_scale, int32_t *status_d, hipStream_t stream)
 {
     clear_error();
     if (num_tokens < 0 || num_slots < 0 || num_kv_heads <= 0 || head_dim <= 0)
@@ -290,10 +290,18 @@ int pkvs_append_kv(const void *k_new, const void *v_new, const int64_t *loc_d,
                     head_dim);
     if (dtype != PKVS_BF16 && dtype != PKVS_FP32 && dtype != PKVS_FP16)
         return fail(PKVS_ERR_UNSUPPORTED, "dtype %d not built (bf16, fp16, fp32)", dtype);
-    const int64_t row_bytes = int64_t(num_kv_heads) * head_dim * (dtype == PKVS_FP32 ? 4 : 2);
-    if (row_bytes % 16)
+    if (kv_format < PKVS_KV_SAME || kv_format > PKVS_KV_FP8_E5M2)
+        return fail(PKVS_ERR_INVALID_ARG, "kv_format %d: must be 0, 1 or 2", kv_format);
+    const bool eight = kv_format != PKVS_KV_SAME;
+    if (eight && (bad_scale(k_scale) || bad_scale(v_scale)))
+        return fail(PKVS_ERR_INVALID_ARG, "k_scale %g / v_scale %g must be positive and finite",
+                    double(k_scale), double(v_scale));
+    const int64_t row_elems = int64_t(num_kv_heads) * head_dim;
+    const int64_t row_bytes = row_elems * (dtype == PKVS_FP32 ? 4 : 2);
+    if (row_bytes % 16 || row_elems % 8)
         return fail(PKVS_ERR_UNSUPPORTED, "a cache row (num_kv_heads x head_dim elements) "
-                    "must be a multiple of 16 bytes, got %lld", (long long)row_bytes);
+                    "must be a multiple of 16 bytes and of 8 elements, got %lld elements",
+                    (long long)row_elems);
     if (num_tokens == 0) return PKVS_OK;
     if (!k_new || !v_new || !loc_d || !k_cache || !v_cache)
         return fail(PKVS_ERR_INVALID_ARG, "null pointer");
@@ -302,8 +310,12 @@ int pkvs_append_kv(const void *k_new, const void *v_new, const int64_t *loc_d,
         if (reinterpret_cast<uintptr_t>(ptr) % 16)
             return fail(PKVS_ERR_INVALID_ARG, "k/v rows and caches must be 16-byte aligned");
     const int grid = int(std::min<int64_t>(num_tokens, int64_t(device_cus()) * 16));
-    hipError_t e = launch_append_kv(k_new, v_new, loc_d, num_tokens, row_bytes, k_cache, v_cache,
-                                    num_slots, status_d, grid, stream);
+    hipError_t e =
+        eight ? launch_append_kv_quant(k_new, v_new, loc_d, num_tokens, row_elems, dtype,
+                                       kv_format, k_cache, v_cache, num_slots, k_scale, v_scale,
+                                       status_d, grid, stream)
+              : launch_append_kv(k_new, v_new, loc_d, num_tokens, row_bytes, k_cache, v_cache,
+                                 num_slots, status_d, grid, stream);
     if (e != hipSuccess) return fail(PKVS_ERR_HIP, "append launch: %s", hipGetErrorString(e));
     return PKVS_OK;
 }

@@ -103,7 +103,8 @@ def _load() -> ctypes.CDLL:
         "pkvs_cascade_run": (ctypes.c_int, [P, P, P, P, P, P, i64, P, P, P, f32, i32, f32, f32,
                                             P]),
         "pkvs_merge_state": (ctypes.c_int, [P, P, P, P, P, P, i64, i32, i32, i32, P]),
-        "pkvs_append_kv": (ctypes.c_int, [P, P, P, i64, P, P, i64, i32, i32, i32, P, P]),
+        "pkvs_append_kv": (ctypes.c_int, [P, P, P, i64, P, P, i64, i32, i32, i32, i32, f32, f32,
+                                          P, P]),
         "pkvs_build_kv_indices": (ctypes.c_int, [P, i64, i64, P, P, P, i32, P, P, i64, P, P]),
         "pkvs_plan_get_info": (ctypes.c_int, [P, ctypes.POINTER(pkvs_plan_info)]),
         "pkvs_plan_copy_items": (ctypes.c_int, [P, P, i64, ctypes.POINTER(i64)]),
@@ -268,23 +269,29 @@ def pkvs_merge_state(v_a, s_a, v_b, s_b, v_out=None, s_out=None, stream=None):
     return v_out, s_out
 
 
-def pkvs_append_kv(k_new, v_new, loc, k_cache, v_cache, status=None, stream=None) -> None:
+def pkvs_append_kv(k_new, v_new, loc, k_cache, v_cache, status=None, stream=None,
+                   k_scale: float = 1.0, v_scale: float = 1.0) -> None:
     """k_cache.view(-1, H_kv, D)[loc[i]] = k_new[i] (same for v) on the GPU;
-    ``loc`` int64 device slots; ``status`` optional int32 device counter."""
+    an 8-bit cache (torch.float8_e4m3fn / e5m2) receives k_new / k_scale and
+    v_new / v_scale rounded to its type.  ``loc`` int64 device slots;
+    ``status`` optional int32 device counter."""
     _need_device(k_new, v_new, loc, k_cache, v_cache, status)
     n, h, d = k_new.shape
     if v_new.shape != k_new.shape or k_cache.shape != v_cache.shape:
         raise ValueError("pkvs_append_kv: k/v shapes differ")
-    if k_cache.dtype != k_new.dtype or v_cache.dtype != k_new.dtype or v_new.dtype != k_new.dtype:
-        raise ValueError("pkvs_append_kv: one dtype for new rows and caches")
+    kv_format = _KV_FORMATS.get(k_cache.dtype, PKVS_KV_SAME)
+    if v_new.dtype != k_new.dtype or v_cache.dtype != k_cache.dtype or (
+            kv_format == PKVS_KV_SAME and k_cache.dtype != k_new.dtype):
+        raise ValueError("pkvs_append_kv: one dtype for new rows, and the caches in it or 8-bit")
     if tuple(k_cache.shape[-2:]) != (h, d):
         raise ValueError("pkvs_append_kv: cache rows must be [.., num_kv_heads, head_dim]")
     if loc.dtype != torch.int64 or loc.numel() < n:
         raise ValueError("pkvs_append_kv: loc must be int64 with one slot per row")
     num_slots = k_cache.numel() // (h * d)
     _check(_lib.pkvs_append_kv(_ptr(k_new), _ptr(v_new), _ptr(loc), n, _ptr(k_cache),
-                               _ptr(v_cache), num_slots, h, d, _DTYPES[k_new.dtype], _ptr(status),
-                               _stream(stream)), "pkvs_append_kv")
+                               _ptr(v_cache), num_slots, h, d, _DTYPES[k_new.dtype], kv_format,
+                               float(k_scale), float(v_scale), _ptr(status), _stream(stream)),
+           "pkvs_append_kv")
 
 
 def pkvs_build_kv_indices(page_map, slot, length, start=None, kv_indptr=None, kv_indices=None,

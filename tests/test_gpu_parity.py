@@ -3,6 +3,7 @@
 Tolerances: max |O - O_ref| <= 2e-2 and max |LSE - LSE_ref| <= 1e-3, compared
 in fp32; masking is checked bit-exactly (window_left = 0 returns V at the
 query's own position; one-hot values expose the attention support)."""
+import dataclasses
 import math
 
 import numpy as np
@@ -930,3 +931,74 @@ def test_kv_scales_on_a_16_bit_cache():
     o, lse = gpu_run(case)
     ro, rl = oracle_for(case)
     compare(o, lse, ro, rl, tag="scales on bf16")
+
+
+@pytest.mark.parametrize("kv_dtype", FP8)
+@pytest.mark.parametrize("src", [torch.bfloat16, torch.float16, torch.float32])
+def test_append_into_8_bit_cache_bit_exact(kv_dtype, src):
+    """Every new element x lands as the 8-bit code of x / scale (fp32 quotient
+    rounded to the input type, then to nearest even; overflow, infinities and
+    NaN by the format's rules), bit for bit against the oracle: for 16-bit
+    inputs every bit pattern of the type, for fp32 a spread with the edge
+    values."""
+    H, D = 8, 128
+    if src == torch.float32:
+        g = torch.Generator().manual_seed(3)
+        x = torch.randn(65536, generator=g) * torch.logspace(-12, 6, 65536, base=2.0)
+        x[:12] = torch.tensor([0.0, -0.0, 464.0, 464.01, 448.0, 61440.0, 57344.0, 1e-40,
+                               float("inf"), float("-inf"), float("nan"), -2.0 ** -17])
+    else:
+        x = torch.arange(-32768, 32768, dtype=torch.int32).to(torch.int16).view(src)
+    rows = x.numel() // (H * D)
+    k_new = x.reshape(rows, H, D).contiguous()
+    v_new = k_new.flip(0).contiguous()
+    pages, Psz = 16, 8
+    g = torch.Generator().manual_seed(7)
+    k_cache = torch.randint(0, 256, (pages, Psz, H, D), generator=g,
+                            dtype=torch.uint8).view(kv_dtype)
+    v_cache = torch.randint(0, 256, (pages, Psz, H, D), generator=g,
+                            dtype=torch.uint8).view(kv_dtype)
+    loc = torch.randperm(pages * Psz, generator=g)[:rows].to(torch.int64)
+    loc[1] = -1  # skipped and counted
+    rk, rv, skipped = oracle.append_kv_quant(k_new, v_new, loc, k_cache, v_cache, 0.37, 0.0625)
+    kc, vc = k_cache.to(DEV), v_cache.to(DEV)
+    status = torch.zeros(1, dtype=torch.int32, device=DEV)
+    log(f"8-bit append {src} -> {kv_dtype}: {rows} rows")
+    P.pkvs_append_kv(k_new.to(DEV), v_new.to(DEV), loc.to(DEV), kc, vc, status=status,
+                     k_scale=0.37, v_scale=0.0625)
+    torch.cuda.synchronize()
+    assert int(status) == skipped == 1
+    nan_mask = 0x7F if kv_dtype == torch.float8_e4m3fn else 0x7C
+    for got, want in ((kc.cpu().view(torch.uint8), rk.view(torch.uint8)),
+                      (vc.cpu().view(torch.uint8), rv.view(torch.uint8))):
+        g8, w8 = got.reshape(-1).numpy(), want.reshape(-1).numpy()
+        # NaN codes may differ in sign; every other code is exact
+        wnan = ((w8 & 0x7F) > nan_mask) | ((w8 & 0x7F) == 0x7F)
+        gnan = ((g8 & 0x7F) > nan_mask) | ((g8 & 0x7F) == 0x7F)
+        assert np.array_equal(gnan, wnan)
+        diff = np.nonzero((g8 != w8) & ~wnan)[0]
+        assert diff.size == 0, [(int(i), hex(g8[i]), hex(w8[i])) for i in diff[:8]]
+
+
+@pytest.mark.parametrize("kv_dtype", FP8)
+def test_decode_over_an_8_bit_cache_written_by_append(kv_dtype):
+    """A decode batch whose 8-bit cache was filled by pkvs_append_kv from bf16
+    keys and values equals the oracle over that cache."""
+    kv = [1, 300, 77, 900]
+    src = small([1] * len(kv), kv, H_q=16, H_kv=2, D=128, P_=16, W=127, seed=95, decode=True)
+    Psz = src.page_size
+    kvp = src.kv_indptr.cpu().tolist()
+    loc = []
+    for b in range(len(kv)):
+        pages = src.kv_indices.cpu()[kvp[b]:kvp[b + 1]]
+        loc += [int(pages[j // Psz]) * Psz + j % Psz for j in range(kv[b])]
+    loc_t = torch.tensor(loc, device=DEV)
+    flat = lambda t: t.view(-1, src.num_kv_heads, src.head_dim)
+    k_rows, v_rows = flat(src.k_cache)[loc_t].contiguous(), flat(src.v_cache)[loc_t].contiguous()
+    k8 = torch.zeros(src.k_cache.shape, dtype=torch.uint8, device=DEV).view(kv_dtype)
+    v8 = torch.zeros_like(k8)
+    P.pkvs_append_kv(k_rows, v_rows, loc_t, k8, v8, k_scale=0.05, v_scale=0.07)
+    case = dataclasses.replace(src, k_cache=k8, v_cache=v8, k_scale=0.05, v_scale=0.07)
+    o, lse = gpu_run(case)
+    ro, rl = oracle_for(case)
+    compare(o, lse, ro, rl, tag=f"decode over an appended {kv_dtype} cache")

@@ -417,17 +417,27 @@ def test_append_and_build_reject_bad_arguments():
     p = ctypes.c_void_p(buf.data_ptr())
     odd = ctypes.c_void_p(buf.data_ptr() + 2)
     # append: negative count, unsupported dtype, a row that is not 16 bytes, nulls, misalignment
-    assert lib.pkvs_append_kv(p, p, p, -1, p, p, 4, 1, 64, P.PKVS_BF16, None, None) == \
+    assert lib.pkvs_append_kv(p, p, p, -1, p, p, 4, 1, 64,
+                              P.PKVS_BF16, 0, 1.0, 1.0, None, None) == \
         P.PKVS_ERR_INVALID_ARG
-    assert lib.pkvs_append_kv(p, p, p, 1, p, p, 4, 1, 64, 7, None, None) == P.PKVS_ERR_UNSUPPORTED
-    assert lib.pkvs_append_kv(p, p, p, 1, p, p, 4, 1, 4, P.PKVS_BF16, None, None) == \
+    assert lib.pkvs_append_kv(p, p, p, 1, p, p, 4, 1, 64,
+                              7, 0, 1.0, 1.0, None, None) == P.PKVS_ERR_UNSUPPORTED
+    assert lib.pkvs_append_kv(p, p, p, 1, p, p, 4, 1, 4, P.PKVS_BF16, 0, 1.0, 1.0, None, None) == \
         P.PKVS_ERR_UNSUPPORTED
-    assert lib.pkvs_append_kv(None, p, p, 1, p, p, 4, 1, 64, P.PKVS_BF16, None, None) == \
+    assert lib.pkvs_append_kv(None, p, p, 1, p, p, 4, 1, 64,
+                              P.PKVS_BF16, 0, 1.0, 1.0, None, None) == \
         P.PKVS_ERR_INVALID_ARG
-    assert lib.pkvs_append_kv(odd, p, p, 1, p, p, 4, 1, 64, P.PKVS_BF16, None, None) == \
+    assert lib.pkvs_append_kv(odd, p, p, 1, p, p, 4, 1, 64,
+                              P.PKVS_BF16, 0, 1.0, 1.0, None, None) == \
         P.PKVS_ERR_INVALID_ARG
-    assert lib.pkvs_append_kv(None, None, None, 0, None, None, 0, 1, 64, P.PKVS_BF16, None,
-                              None) == P.PKVS_OK  # nothing to write
+    assert lib.pkvs_append_kv(None, None, None, 0, None, None, 0, 1, 64, P.PKVS_BF16, 0, 1.0,
+                              1.0, None, None) == P.PKVS_OK  # nothing to write
+    # 8-bit cache: a kv_format outside the enum, scales that are not positive finite
+    assert lib.pkvs_append_kv(p, p, p, 1, p, p, 4, 1, 64, P.PKVS_BF16, 3, 1.0, 1.0, None,
+                              None) == P.PKVS_ERR_INVALID_ARG
+    for ks, vs in ((0.0, 1.0), (1.0, float("nan")), (-1.0, 1.0)):
+        assert lib.pkvs_append_kv(p, p, p, 1, p, p, 4, 1, 64, P.PKVS_BF16, 1, ks, vs, None,
+                                  None) == P.PKVS_ERR_INVALID_ARG
     # build: negative sizes, missing outputs or inputs
     assert lib.pkvs_build_kv_indices(p, 2, 2, p, None, p, -1, p, p, 4, None, None) == \
         P.PKVS_ERR_INVALID_ARG
