@@ -26,6 +26,8 @@ Reported (one JSON line):
   pool           cache writes of a 32768-token prompt's K/V and the split
                  decode's page-table build, timed apart
   decode_fp8_kv  the split decode over an e4m3 copy of its cache, timed apart
+  decode_sweep   the 64-request decode over its window sweep (W -1, 1023, 127,
+                 31, 0), the last-level cache flushed before each timed run
 
     python bench.py [--steps K] [--warmup W] [--gpus 1] [--no-cpu-baseline]
 """
@@ -224,6 +226,55 @@ def bench_decode_fp8(dec, W: int, reps: int) -> dict:
     return {"format": "e4m3", "ms": round(ms, 4), "kv_bytes": nb,
             "GB/s": round(nb / (ms * 1e-3) / 1e9, 1),
             "frac_of_hbm_peak": round(nb / (ms * 1e-3) / 1e9 / PEAK_HBM_GBPS, 4)}
+
+
+def bench_decode_sweep(reps: int) -> dict:
+    """The 64-request decode (kv U[1,4096], 32/8 heads, head_dim 128) over its
+    window sweep.  Its K/V (0.26-537 MB) fit the 256 MB last-level cache, so
+    before each timed run 1 GiB is written to flush it; each run is timed
+    apart with HIP events around run()."""
+    import torch
+
+    from paged_kv_sliding_amd import pkvs as P
+    from paged_kv_sliding_amd.synth import build_case
+
+    c = build_case("decode_sweep", device="cuda")
+    flush = torch.empty(1 << 30, dtype=torch.uint8, device="cuda")
+    o = torch.empty_like(c.q)
+    lse = torch.empty(c.q.shape[:2], dtype=torch.float32, device="cuda")
+    out = {}
+    for W in (-1, 1023, 127, 31, 0):
+        att = P.BatchAttention(P.PKVS_DECODE, num_qo_heads=c.num_qo_heads,
+                               num_kv_heads=c.num_kv_heads, head_dim=c.head_dim,
+                               page_size=c.page_size, dtype=c.dtype, window_left=W,
+                               batch_capacity=c.batch_size, kv_capacity=max(c.kv_lens))
+        att.plan(kv_indptr=c.kv_indptr.cpu(), kv_last_page_len=c.kv_last_page_len.cpu())
+
+        def run():
+            att.run(c.q, c.k_cache, c.v_cache, c.kv_indices, sm_scale=c.sm_scale,
+                    window_left=W, out=o, lse=lse)
+
+        for _ in range(3):
+            run()
+        ts = []
+        for _ in range(reps):
+            flush.fill_(1)
+            a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            a.record()
+            run()
+            b.record()
+            torch.cuda.synchronize()
+            ts.append(a.elapsed_time(b))
+        ms = sorted(ts)[len(ts) // 2]
+        nb = decode_bytes(c, W)
+        out[f"W{W}"] = {"ms_median": round(ms, 4), "kv_bytes": nb,
+                        "GB/s": round(nb / (ms * 1e-3) / 1e9, 1),
+                        "frac_of_hbm_peak": round(nb / (ms * 1e-3) / 1e9 / PEAK_HBM_GBPS, 4),
+                        "split_size": att.info().split_size, "items": att.info().num_items}
+        att.close()
+    del flush
+    torch.cuda.empty_cache()
+    return out
 
 
 def bench_pool(reps: int) -> dict:
@@ -433,7 +484,7 @@ def main():
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-budget", type=float, default=15.0)
-    ap.add_argument("--only", choices=["prefill", "decode", "cascade", "pool", "all"],
+    ap.add_argument("--only", choices=["prefill", "decode", "cascade", "pool", "sweep", "all"],
                     default="all",
                     help="restrict the timed step (for profiling runs)")
     ap.add_argument("--profile-kernel", choices=["prefill", "decode", "copy"],
@@ -459,6 +510,9 @@ def main():
         return
     if args.only == "pool":
         print(json.dumps({"pool": bench_pool(args.steps)}), flush=True)
+        return
+    if args.only == "sweep":
+        print(json.dumps({"decode_sweep": bench_decode_sweep(args.steps)}), flush=True)
         return
 
     import torch
@@ -621,6 +675,8 @@ def main():
     if fp8 is not None:
         line["decode_fp8_kv"] = fp8
     if args.only == "all":
+        print("bench: decode sweep", file=sys.stderr, flush=True)
+        line["decode_sweep"] = bench_decode_sweep(max(5, args.steps // 2))
         print("bench: cascade prefill", file=sys.stderr, flush=True)
         line["cascade"] = bench_cascade(max(5, args.steps // 2))
         print("bench: cache writes and page-table build", file=sys.stderr, flush=True)

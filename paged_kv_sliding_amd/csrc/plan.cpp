@@ -296,8 +296,8 @@ static void build_prefill(Plan *p, const std::vector<Req> &reqs)
 }
 
 // Keys per decode chunk when the caller leaves it to the planner: aim for
-// about auto_target_items chunks over the whole batch so every wave slot of
-// the fixed grid gets work, but never cut below kMinAutoSplit keys.
+// about auto_target_items chunks over the whole batch (one per resident wave)
+// so every wave gets work in one round, but never cut below kMinAutoSplit keys.
 static int64_t choose_split(const Plan *p, const std::vector<Req> &reqs)
 {
     const pkvs_desc &d = p->desc;
@@ -480,7 +480,10 @@ static int create_plan(const pkvs_desc *desc, bool ragged, Plan **out)
         p->block_threads = fp32 ? kGenericThreads : kDecodeThreads;
         int per_cu = p->have_gpu && !fp32 ? decode_blocks_per_cu(desc->head_dim, f16, kvf) : 0;
         p->grid_blocks = p->num_cus * std::max(per_cu, fp32 ? 2 : 8);
-        p->auto_target_items = 2 * p->grid_blocks;
+        // one chunk per resident wave (one wave per SIMD when the occupancy
+        // cannot be queried): a second, partial round of chunks or chunks of
+        // a few blocks each measured slower
+        p->auto_target_items = int64_t(p->num_cus) * (per_cu > 0 ? per_cu : 4);
     }
     (void)hipGetLastError();
     size_plan(p);
