@@ -46,6 +46,9 @@ if ROOT not in sys.path:
 
 PEAK_BF16_TFLOPS = 2500.0   # MI355X dense bf16 MFMA
 PEAK_HBM_GBPS = 8000.0      # MI355X HBM3E
+# the kernel the 32k-token prefill runs (the planner's choice for head_dim 128,
+# bf16), as rocprofv3 names it, without the closing bracket
+PREFILL_KERNEL = "prefill_big_kernel<false"
 
 
 def prefill_flops(case) -> int:
@@ -425,7 +428,7 @@ def ingest_counters(d: str) -> None:
     res = {"calibration": {"copy_bytes": COPY_BYTES,
                            "fetch_factor": round(cal["FETCH_SIZE"], 4),
                            "write_factor": round(cal["WRITE_SIZE"], 4)}}
-    for kind, kernels in (("prefill", ["prefill_kernel<128"]),
+    for kind, kernels in (("prefill", [PREFILL_KERNEL]),
                           ("decode", ["decode_kernel<128", "decode_merge_kernel<128"])):
         fm, wm = pass_means(kind, "FETCH_SIZE"), pass_means(kind, "WRITE_SIZE")
         for key in kernels:
@@ -655,9 +658,9 @@ def main():
         line["roofline"] = {"bound": "mfma", "achieved": round(tflops, 2),
                             "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
                             "frac": round(tflops / PEAK_BF16_TFLOPS, 4),
-                            "traffic": load_traffic("prefill_kernel<128>"),
+                            "traffic": load_traffic(PREFILL_KERNEL + ">"),
                             "algorithmic_bytes": prefill_algorithmic_bytes(pre),
-                            "kernel": "prefill_kernel<128>",
+                            "kernel": PREFILL_KERNEL + ">",
                             "work_per_launch": flops}
     if "dec" in res:
         dec_ms, gbps, nbytes = res["dec"]

@@ -109,8 +109,10 @@ typedef enum pkvs_kind { PKVS_PREFILL = 0, PKVS_DECODE = 1, PKVS_CASCADE = 2 } p
  *                   qo_capacity), 1 = 4 waves x 32 rows, 2 = 8 waves x 32 rows,
  *                   3 = 4 waves x 64 rows, software-pipelined (2 and 3: head_dim
  *                   <= 128), 4 = 8 waves x 32 rows with K/V rows loaded straight
- *                   into LDS (head_dim 128; a plan() whose items span more than
- *                   2048 pages of keys runs variant 2 instead); rows are (query
+ *                   into LDS, 5 = as 4 with 64-key steps and 16-byte loads
+ *                   into an XOR-swizzled LDS layout (4 and 5: head_dim 128,
+ *                   16-bit K/V; a plan() whose items span more than 2048
+ *                   pages of keys runs variant 2 instead); rows are (query
  *                   token, head) pairs
  *  batch_capacity   largest batch a plan() call may describe
  *  qo_capacity      prefill, cascade: largest total number of query tokens

@@ -61,7 +61,10 @@ enum PrefillVariant {
     kPrefillDma = 4,      // 8 waves x 32 rows, K/V rows loaded straight into LDS
                           // (head_dim 128; an item's key range spans at most
                           // kPrefillDmaPages pages)
+    kPrefillBig = 5,      // as 4 with 64-key steps and 16-byte loads into an
+                          // XOR-swizzled unpadded LDS layout
 };
+constexpr int kPrefillBigTile = 64;    // keys per step of kPrefillBig
 constexpr int kPrefillDmaPages = 2048;
 // A contiguous ("ragged") K/V of [tokens, kv heads, head_dim] is addressed like
 // a paged cache whose page-table entries are row indices: entry t of a request

@@ -136,7 +136,8 @@ static int validate_desc(const pkvs_desc *d)
     if (d->kv_format != PKVS_KV_SAME && d->dtype == PKVS_FP32)
         return fail(PKVS_ERR_UNSUPPORTED, "8-bit K/V are built for bf16 and fp16 queries");
     if (d->kv_format != PKVS_KV_SAME &&
-        (d->prefill_variant == kPrefillWide || d->prefill_variant == kPrefillDma))
+        (d->prefill_variant == kPrefillWide || d->prefill_variant == kPrefillDma ||
+         d->prefill_variant == kPrefillBig))
         return fail(PKVS_ERR_UNSUPPORTED, "8-bit K/V are widened on the register-staged prefill "
                     "variants (1, 2)");
     if (d->window_left < -1)
@@ -148,12 +149,13 @@ static int validate_desc(const pkvs_desc *d)
                                       d->fixed_split_size % kDecodeBlock))
         return fail(PKVS_ERR_INVALID_ARG, "fixed_split_size %d must be -1 or a positive "
                     "multiple of %d", d->fixed_split_size, kDecodeBlock);
-    if (d->prefill_variant < 0 || d->prefill_variant > 4)
-        return fail(PKVS_ERR_INVALID_ARG, "prefill_variant %d must be 0..4", d->prefill_variant);
+    if (d->prefill_variant < 0 || d->prefill_variant > 5)
+        return fail(PKVS_ERR_INVALID_ARG, "prefill_variant %d must be 0..5", d->prefill_variant);
     if (d->prefill_variant > 1 && d->head_dim > 128)
         return fail(PKVS_ERR_UNSUPPORTED, "256-row prefill variants are built for head_dim <= 128");
-    if (d->prefill_variant == kPrefillDma && d->head_dim != 128)
-        return fail(PKVS_ERR_UNSUPPORTED, "the direct-to-LDS prefill variant is built for "
+    if ((d->prefill_variant == kPrefillDma || d->prefill_variant == kPrefillBig) &&
+        d->head_dim != 128)
+        return fail(PKVS_ERR_UNSUPPORTED, "the direct-to-LDS prefill variants are built for "
                     "head_dim 128");
     if (d->batch_capacity <= 0 || d->kv_capacity <= 0 ||
         (prefill_like && d->qo_capacity <= 0))
@@ -222,6 +224,7 @@ static void build_prefill(Plan *p, const std::vector<Req> &reqs)
 {
     const pkvs_desc &d = p->desc;
     const int tq = p->query_tile;
+    const int kv_tile = p->prefill_variant == kPrefillBig ? kPrefillBigTile : kPrefillKvTile;
     struct It { int64_t cost; int32_t w[kPrefillItemWords]; };
     std::vector<It> items;
     for (size_t b = 0; b < reqs.size(); ++b) {
@@ -234,7 +237,7 @@ static void build_prefill(Plan *p, const std::vector<Req> &reqs)
             const int64_t pos0 = prefix + t0;
             int64_t kv_begin = 0;
             if (d.window_left >= 0) kv_begin = std::max<int64_t>(0, pos0 - d.window_left);
-            kv_begin = kv_begin / kPrefillKvTile * kPrefillKvTile;
+            kv_begin = kv_begin / kv_tile * kv_tile;
             const int64_t kv_end = d.causal ? std::min<int64_t>(r.kv_len, pos0 + qn) : r.kv_len;
             for (int32_t hk = 0; hk < d.num_kv_heads; ++hk) {
                 It it;
@@ -256,7 +259,7 @@ static void build_prefill(Plan *p, const std::vector<Req> &reqs)
     // the direct-to-LDS variant keeps an item's page ids in LDS: the key range
     // it loads (whole tiles, cut at the request's end) must fit the table
     p->run_variant = p->prefill_variant;
-    if (p->prefill_variant == kPrefillDma) {
+    if (p->prefill_variant == kPrefillDma || p->prefill_variant == kPrefillBig) {
         for (const It &it : items) {
             const int64_t kb = it.w[kPiKvBegin];
             const int64_t kv_len = it.w[kPiKvLen];
@@ -264,8 +267,8 @@ static void build_prefill(Plan *p, const std::vector<Req> &reqs)
                 d.causal ? std::min<int64_t>(kv_len, int64_t(it.w[kPiPos0]) + it.w[kPiQCount])
                          : kv_len;
             if (kv_end <= kb) continue;
-            const int64_t last = std::min(kb + ceil_div(kv_end - kb, kPrefillKvTile) *
-                                                   kPrefillKvTile, kv_len) - 1;
+            const int64_t last = std::min(kb + ceil_div(kv_end - kb, kv_tile) * kv_tile,
+                                          kv_len) - 1;
             if (last / d.page_size - kb / d.page_size + 1 > kPrefillDmaPages) {
                 p->run_variant = kPrefillRows256;
                 break;
@@ -453,16 +456,18 @@ static int create_plan(const pkvs_desc *desc, bool ragged, Plan **out)
     if (desc->kind == PKVS_PREFILL) {
         // Kernel variant: 256-row workgroups (8 waves x 32 rows) share each
         // staged key tile between more rows and keep two waves per SIMD; they
-        // are the fastest measured for head_dim <= 128.  128-row workgroups
-        // serve head_dim 256 and batches too small to fill the device with
-        // 256-row tiles.  The wide variant is available on request.
+        // are the fastest measured for head_dim <= 128, and for head_dim 128
+        // with 16-bit K/V the 64-key-step direct-to-LDS kernel is the fastest
+        // of them.  128-row workgroups serve head_dim 256 and batches too small
+        // to fill the device with 256-row tiles.  Variants 3 and 4 are
+        // available on request.
         const int64_t big_tiles = ceil_div(desc->qo_capacity, 256 / group) * desc->num_kv_heads;
         int v = kPrefillRows128;
         if (desc->head_dim <= 128 && big_tiles >= 2 * p->num_cus)
-            v = desc->head_dim == 128 && kvf == PKVS_KV_SAME ? kPrefillDma : kPrefillRows256;
+            v = desc->head_dim == 128 && kvf == PKVS_KV_SAME ? kPrefillBig : kPrefillRows256;
         if (desc->prefill_variant) v = desc->prefill_variant;
-        // the direct-to-LDS variant needs ~156 KiB of LDS per workgroup
-        if (v == kPrefillDma && p->have_gpu && !fp32 &&
+        // the direct-to-LDS variants need 136-156 KiB of LDS per workgroup
+        if ((v == kPrefillDma || v == kPrefillBig) && p->have_gpu && !fp32 &&
             prefill_blocks_per_cu(desc->head_dim, v, f16, kvf) < 1)
             v = kPrefillRows256;
         p->prefill_variant = p->run_variant = v;
@@ -470,7 +475,8 @@ static int create_plan(const pkvs_desc *desc, bool ragged, Plan **out)
         p->query_tile = fp32 ? kGenericQTile : rows / group;
         p->item_words = kPrefillItemWords;
         p->block_threads =
-            fp32 ? kGenericThreads : (v == kPrefillRows256 || v == kPrefillDma ? 512 : 256);
+            fp32 ? kGenericThreads
+                 : (v == kPrefillRows256 || v == kPrefillDma || v == kPrefillBig ? 512 : 256);
         int per_cu =
             p->have_gpu && !fp32 ? prefill_blocks_per_cu(desc->head_dim, v, f16, kvf) : 0;
         p->grid_blocks = p->num_cus * std::max(per_cu, fp32 ? 2 : 1);

@@ -956,6 +956,404 @@ __global__ __launch_bounds__(256) void prefill_wide_kernel(PrefillArgs a)
     }
 }
 
+// 64-key steps with 16-byte direct-to-LDS loads (variant 5: head_dim 128,
+// 8 waves x 32 rows, 16-bit K/V).
+//
+// Each step covers a 64-key tile as two 32-key halves, so a wave's S^T of
+// the next tile is two independent MFMA chains (one per half) and the row
+// maximum, the lazy-rescale test, the page-id read, the load issue and the
+// barrier are paid once per 64 keys.  The iteration for tile j runs four
+// quarters (half h, 16-key step kk); each quarter issues four MFMAs of
+// S^T(j+1), makes the next quarter's probabilities on the vector ALU and
+// issues the four O^T += V^T.P^T MFMAs of its own 16 keys.
+//
+// Staging.  A K or V tile is 64 rows of 256 bytes stored unpadded; one
+// global_load_lds_dwordx4 moves four rows (lane i writes LDS bytes
+// 16i..16i+15 of the 1 KiB group), so a wave stages its 8 K rows and 8 V
+// rows of a tile with four instructions from one scalar base when the 8 keys
+// share a page.  Bank conflicts of the operand reads are avoided by an XOR
+// swizzle of the 16-byte chunks, applied on the global side (the lane that
+// writes LDS chunk c of a row fetches chunk c ^ f(row)):
+//   K: f(r) = r & 15 -- the 16 rows read by a 16-lane group for one k-step
+//      land in 16 distinct chunk positions;
+//   V: f(r) = 4 (r & 3) -- the four rows of a transposing read by 32 lanes
+//      (two chunks each) land in 16 distinct chunk positions.
+constexpr int BIG_T = 64;                     // keys per step
+constexpr int BIG_SETS = 4;                   // LDS tile sets
+constexpr int BIG_ROW = 256;                  // bytes per K / V row
+constexpr int BIG_HALF = BIG_T * BIG_ROW;     // K (or V) bytes of one tile
+constexpr int BIG_SET = 2 * BIG_HALF;         // K then V
+constexpr int BIG_LOADS = 4;                  // loads per wave per tile
+
+// Four 16-byte row-group loads from one scalar base per tensor: K rows to
+// LDS mk and mk + 1024 (lane offsets dk0, dk1), V rows to mv and mv + 1024
+// (dv0, dv1).  M0 holds the LDS destination and is restored afterwards.
+__device__ __forceinline__ void big_dma4(uint32_t mk, uint32_t mv, uint32_t dk0, uint32_t dk1,
+                                         uint32_t dv0, uint32_t dv1, const void *kb,
+                                         const void *vb)
+{
+    uint32_t saved;
+    asm volatile("s_mov_b32 %0, m0\n\t"
+                 "s_mov_b32 m0, %1\n\tglobal_load_lds_dwordx4 %5, %9\n\t"
+                 "s_mov_b32 m0, %2\n\tglobal_load_lds_dwordx4 %6, %9\n\t"
+                 "s_mov_b32 m0, %3\n\tglobal_load_lds_dwordx4 %7, %10\n\t"
+                 "s_mov_b32 m0, %4\n\tglobal_load_lds_dwordx4 %8, %10\n\t"
+                 "s_mov_b32 m0, %0"
+                 : "=&s"(saved)
+                 : "s"(mk), "s"(mk + 1024u), "s"(mv), "s"(mv + 1024u), "v"(dk0), "v"(dk1),
+                   "v"(dv0), "v"(dv1), "s"(kb), "s"(vb)
+                 : "memory");
+}
+
+// One 16-byte row-group load with a per-lane 64-bit address.
+__device__ __forceinline__ void big_dma1(uint32_t m, const void *src)
+{
+    uint32_t saved;
+    asm volatile("s_mov_b32 %0, m0\n\ts_mov_b32 m0, %1\n\tglobal_load_lds_dwordx4 %2, off\n\t"
+                 "s_mov_b32 m0, %0"
+                 : "=&s"(saved)
+                 : "s"(m), "v"(src)
+                 : "memory");
+}
+
+// A wave-uniform value the optimiser must treat as unknown (kept in an SGPR).
+__device__ __forceinline__ uint32_t opaque_sgpr(uint32_t x)
+{
+    asm volatile("" : "+s"(x));
+    return x;
+}
+
+__device__ __forceinline__ bf16x8 lds_b128(uint32_t addr)
+{
+    return *reinterpret_cast<const __attribute__((address_space(3))) bf16x8 *>(
+        static_cast<uintptr_t>(addr));
+}
+
+__device__ __forceinline__ i16x4 lds_tr(uint32_t addr)
+{
+    return __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+        reinterpret_cast<lds_i16x4 *>(static_cast<uintptr_t>(addr)));
+}
+
+template <bool F16>
+__global__ __launch_bounds__(512) void prefill_big_kernel(PrefillArgs a)
+{
+    constexpr int D = 128, KS = D / 16, DT = D / 32;
+    struct Lds {
+        uint8_t set[BIG_SETS][BIG_SET];
+        int32_t pages[kPrefillDmaPages];
+    };
+    __shared__ __attribute__((aligned(1024))) Lds sh;
+
+    const int tid = threadIdx.x;
+    const int wave = tid >> 6, lane = tid & 63, l32 = lane & 31, hw = lane >> 5;
+    const int uwave = __builtin_amdgcn_readfirstlane(wave);
+    const int G = 1 << a.log2_group;
+    const int n_items = a.ws[kHdrNumItems];
+    const uint16_t *Q = static_cast<const uint16_t *>(a.q);
+    const int W = a.window_left;
+    const float c = a.scale_log2;
+    const float cap_a = a.cap_a;
+
+    const uint32_t lds_sets =
+        uint32_t(reinterpret_cast<uintptr_t>((__attribute__((address_space(3))) void *)sh.set));
+    // operand reads (byte offsets inside a set): K row 32h + l32, chunk 2ks+hw;
+    // V^T transposing read of rows 4hw + e (+ 16kk, + 8, + 32h), dims
+    // 32dt + 16s + 4q (lane = 16s + 4e + q within its half-wave)
+    // (the k-step and the dim tile only flip bits that the lane's base leaves
+    // to the swizzle, so each offset is the base XOR a constant)
+    const uint32_t kbase = uint32_t(l32 * BIG_ROW + ((hw ^ (l32 & 15)) << 4));
+    const uint32_t vbase = [&] {
+        const int e = (lane & 15) >> 2, q = lane & 3, s16 = (lane >> 4) & 1;
+        const int chunk = 2 * s16 + (q >> 1);
+        return uint32_t(BIG_HALF + (4 * hw + e) * BIG_ROW + ((chunk ^ (4 * e)) << 4) + (q & 1) * 8);
+    }();
+    // staging: lane (r' = lane / 16, position p = lane % 16) of load i writes
+    // LDS chunk p of row 8*wave + 4i + r' and fetches the chunk that the
+    // swizzle puts there
+    const int64_t slot_stride = int64_t(a.num_kv_heads) * D;
+    const int32_t slot_bytes = int32_t(slot_stride * 2);
+    const uint32_t page_bytes = uint32_t(slot_stride * a.page_rows * 2);
+    // (slot_bytes is a multiple of 256, so the swizzled chunk offset is the low
+    // byte of each lane offset; load 1 fetches rows 4 further on, and for K
+    // the swizzle of its rows differs from load 0's in bit 2 of the chunk)
+    const int rr = lane >> 4, pp = lane & 15;
+    const uint32_t dk0 = uint32_t(rr * slot_bytes + ((pp ^ rr ^ (8 * (wave & 1))) << 4));
+    const uint32_t dv0 = uint32_t(rr * slot_bytes + ((pp ^ (4 * rr)) << 4));
+    const uint32_t row4 = uint32_t(4 * slot_bytes);
+    const char *const Kb = static_cast<const char *>(a.k);
+    const char *const Vb = static_cast<const char *>(a.v);
+    const int page_mask = a.page_size - 1;
+
+    for (int it = blockIdx.x; it < n_items; it += gridDim.x) {
+        const int32_t *w = a.ws + kHeaderWords + int64_t(it) * kPrefillItemWords;
+        const int hk = w[kPiKvHead], q_begin = w[kPiQBegin], q_count = w[kPiQCount];
+        const int pos0 = w[kPiPos0], kv_len = w[kPiKvLen];
+        const int kv_begin = w[kPiKvBegin];
+        const int page_base = w[kPiPageBase];
+        const int kv_end = a.causal ? min(kv_len, pos0 + q_count) : kv_len;
+        const int pos_last = pos0 + q_count - 1;
+        const int ntiles = kv_end > kv_begin ? (kv_end - kv_begin + BIG_T - 1) / BIG_T : 0;
+        const int pt_lo = kv_begin >> a.log2_page;
+        const int32_t head_bytes = int32_t(hk * D * 2);
+        // keys loaded past the item's tiles or the request read its last key
+        const int kv_last = min(kv_begin + ntiles * BIG_T, kv_len) - 1;
+
+        const int row = wave * 32 + l32;
+        const int row_tok = row >> a.log2_group, row_head = row & (G - 1);
+        const bool row_valid = row_tok < q_count;
+        const int p_row = pos0 + row_tok;
+        const int64_t qrow = (int64_t(q_begin + row_tok) * a.num_qo_heads + hk * G + row_head) * D;
+        bf16x8 qf[KS];
+#pragma unroll
+        for (int ks = 0; ks < KS; ++ks)
+            qf[ks] = row_valid ? load_bf16x8(Q + qrow + ks * 16 + hw * 8) : zero_bf16x8();
+
+        float m = kNegInf, l = 0.f;
+        f32x16 o[DT];
+#pragma unroll
+        for (int dt = 0; dt < DT; ++dt)
+#pragma unroll
+            for (int i = 0; i < 16; ++i) o[dt][i] = 0.f;
+
+        // page id of `key` from the LDS table (clamped into it and the cache)
+        auto page_entry = [&](int key) __attribute__((always_inline)) {
+            const int e = min(max((key >> a.log2_page) - pt_lo, 0), kPrefillDmaPages - 1);
+            return min(max(sh.pages[e], 0), int32_t(a.num_pages - 1));
+        };
+        // the wave's 8 rows of tile t: K and V, four loads
+        auto dma_tile = [&](int t, int32_t pg0) __attribute__((always_inline)) {
+            const int key0 = kv_begin + t * BIG_T + 8 * uwave;
+            const uint32_t set_b = lds_sets + uint32_t((t & (BIG_SETS - 1)) * BIG_SET);
+            const uint32_t mk = set_b + uint32_t(8 * uwave * BIG_ROW);
+            const uint32_t mv = mk + uint32_t(BIG_HALF);
+            if (key0 + 7 <= kv_last && (key0 & page_mask) + 8 <= a.page_size) {
+                const int64_t off = int64_t(uint64_t(uint32_t(pg0)) * page_bytes) +
+                                    int32_t((key0 & page_mask) * slot_bytes + head_bytes);
+                big_dma4(mk, mv, dk0, (dk0 ^ 64u) + row4, dv0, dv0 + row4, Kb + off, Vb + off);
+            } else {
+#pragma unroll
+                for (int i = 0; i < 2; ++i) {
+                    const int key = min(key0 + 4 * i + (lane >> 4), kv_last);
+                    const int32_t pg = page_entry(key);
+                    const int64_t off = int64_t(uint64_t(uint32_t(pg)) * page_bytes) +
+                                        int32_t((key & page_mask) * slot_bytes + head_bytes);
+                    big_dma1(mk + uint32_t(i * 1024),
+                             Kb + (off + int32_t((i ? dk0 ^ 64u : dk0) & 255u)));
+                    big_dma1(mv + uint32_t(i * 1024), Vb + (off + int32_t(dv0 & 255u)));
+                }
+            }
+        };
+        auto dma_page = [&](int t) __attribute__((always_inline)) {
+            return __builtin_amdgcn_readfirstlane(
+                page_entry(min(kv_begin + t * BIG_T + 8 * uwave, kv_last)));
+        };
+
+        // prologue: page table, then tiles 0..2 in flight; tiles 0 and 1 landed
+        {
+            const int pt_n =
+                ntiles > 0 ? min((kv_last >> a.log2_page) - pt_lo + 1, kPrefillDmaPages) : 0;
+            for (int e = tid; e < pt_n; e += 512) {
+                const int32_t pg = a.kv_indices[page_base + pt_lo + e];
+                sh.pages[e] = min(max(pg, 0), int32_t(a.num_pages - 1));
+            }
+        }
+        __builtin_amdgcn_s_waitcnt(0);
+        __syncthreads();
+        if (ntiles > 0) {
+#pragma unroll 1
+            for (int t = 0; t < min(ntiles, 3); ++t) dma_tile(t, dma_page(t));
+            __builtin_amdgcn_s_waitcnt(0);
+        }
+        __syncthreads();
+
+        // S^T of tile 0, both halves
+        f32x16 s[2];
+#pragma unroll
+        for (int h = 0; h < 2; ++h)
+#pragma unroll
+            for (int i = 0; i < 16; ++i) s[h][i] = 0.f;
+        if (ntiles > 0) {
+#pragma unroll
+            for (int ks = 0; ks < KS; ++ks)
+#pragma unroll
+                for (int h = 0; h < 2; ++h)
+                    s[h] = mfma32x32x16<F16>(
+                        lds_b128(kbase ^ opaque_sgpr(lds_sets | uint32_t(h * 32 * BIG_ROW + 32 * ks))),
+                        qf[ks], s[h]);
+        }
+
+        // A 64-key step for tile j is a head and four quarters, in program
+        // order fixed by scheduling fences.  S^T(j) is held in two of three
+        // 16-register accumulators (half 0 in sb[x], half 1 in sb[y]; sb[z] is
+        // free), and the roles rotate (x, y, z) -> (z, x, y) from step to step.
+        // The head masks S^T(j) and takes the row maximum.  Quarter q (half
+        // h = q/2, 16-key step kk = q%2) runs four MFMAs of S^T(j+1) and then
+        // the four P.V MFMAs of its own 16 keys; between the MFMAs of quarters
+        // 0-1 the vector ALU makes the four 8-key probability blocks, two
+        // scores per MFMA, each block ahead of the P.V MFMAs that use it.
+        // S^T(j+1, half 0) goes to sb[z] in quarters 0-1, S^T(j+1, half 1) to
+        // sb[x] (free once blocks 0-1 are made) in quarters 2-3.  Quarter 2
+        // takes tile j+1's half-0 maximum, so for a tile that needs no mask and
+        // no soft cap the head only adds half 1's.
+        float mu = 0.f, ahead_max = kNegInf;
+        bf16x8 pb[4];
+        f32x16 sb[3];
+        sb[0] = s[0];
+        sb[1] = s[1];
+        // two probabilities of block b (scores 8(b%2)+2i, +1 of half b/2)
+        auto prob2 = [&](const f32x16 &sh, int b, int i) __attribute__((always_inline)) {
+            const int t = 8 * (b & 1) + 2 * i;
+            const float p0 = fast_exp2(__builtin_fmaf(sh[t], c, -mu));
+            const float p1 = fast_exp2(__builtin_fmaf(sh[t + 1], c, -mu));
+            l += p0 + p1;
+            const bf16x2 pk = to16x2<F16>(f32x2{p0, p1});
+            pb[b][2 * i] = pk[0];
+            pb[b][2 * i + 1] = pk[1];
+        };
+        auto head = [&](int j, f32x16 &s0, f32x16 &s1) __attribute__((always_inline)) {
+            const int k0 = kv_begin + j * BIG_T;
+            const bool interior = k0 + BIG_T <= kv_len &&
+                                  (!a.causal || k0 + BIG_T - 1 <= pos0) &&
+                                  (W < 0 || k0 >= pos_last - W);
+            float mx;
+            if (j > 0 && interior && cap_a == 0.f) {
+                mx = fmaxf(ahead_max, max16(s1));
+            } else {
+                if (cap_a != 0.f) {
+#pragma unroll
+                    for (int i = 0; i < 16; ++i) {
+                        s0[i] = soft_cap_unit(s0[i], cap_a);
+                        s1[i] = soft_cap_unit(s1[i], cap_a);
+                    }
+                }
+                if (!interior) {
+                    mask_tile(s0, k0, hw, p_row, kv_len, a.causal, W);
+                    mask_tile(s1, k0 + 32, hw, p_row, kv_len, a.causal, W);
+                }
+                mx = fmaxf(max16(s0), max16(s1));
+            }
+            {
+                const auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(mx),
+                                                                 __float_as_uint(mx), false, false);
+                mx = fmaxf(__uint_as_float(sw[0]), __uint_as_float(sw[1])) * c;
+            }
+            if (__any(mx > m + kRescaleLog2)) {
+                const float m_new = fmaxf(m, mx);
+                const float alpha = m_new == kNegInf ? 1.f : fast_exp2(m - m_new);
+                l *= alpha;
+#pragma unroll
+                for (int dt = 0; dt < DT; ++dt) o[dt] *= alpha;
+                m = m_new;
+            }
+            mu = m == kNegInf ? 0.f : m;
+            __builtin_amdgcn_sched_barrier(0);
+        };
+        auto quarter = [&](int j, int q, const f32x16 &s0, const f32x16 &s1, f32x16 &dst)
+            __attribute__((always_inline)) {
+            const int h = q >> 1, kk = q & 1;
+            const uint32_t cur = lds_sets + uint32_t((j & (BIG_SETS - 1)) * BIG_SET);
+            const uint32_t nxt = lds_sets + uint32_t(((j + 1) & (BIG_SETS - 1)) * BIG_SET);
+            // LDS reads: K operands of S^T(j+1, half h), k-steps 4kk..4kk+3,
+            // and the V^T operands of this quarter.  The lane bases and the
+            // wave-uniform parts occupy disjoint bits, so each address is one
+            // XOR; the uniform part is kept opaque so that the per-k-step and
+            // per-dim-tile offsets are not hoisted into registers of their own.
+            const uint32_t tk = kbase ^ opaque_sgpr(nxt | uint32_t(h * 32 * BIG_ROW + 128 * kk));
+            const uint32_t tv = vbase ^ opaque_sgpr(cur | uint32_t((32 * h + 16 * kk) * BIG_ROW));
+            bf16x8 kq[4], va[DT];
+#pragma unroll
+            for (int u = 0; u < 4; ++u) kq[u] = lds_b128(tk ^ uint32_t(32 * u));
+#pragma unroll
+            for (int dt = 0; dt < DT; ++dt) {
+                const uint32_t v0 = tv ^ uint32_t(64 * dt);
+                const i16x4 lo = lds_tr(v0), hi = lds_tr(v0 + 8 * BIG_ROW);
+                va[dt] =
+                    __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
+            }
+            __builtin_amdgcn_sched_barrier(0);
+            if (kk == 0) {
+#pragma unroll
+                for (int i = 0; i < 16; ++i) dst[i] = 0.f;
+            }
+            // quarter 0 makes blocks 0 (during its QK MFMAs) and 1 (during its
+            // P.V MFMAs, which use block 0); quarter 1 makes blocks 2 and 3
+#pragma unroll
+            for (int u = 0; u < 4; ++u) {
+                dst = mfma32x32x16<F16>(kq[u], qf[4 * kk + u], dst);
+                if (q < 2) prob2(q == 0 ? s0 : s1, 2 * q, u);
+                __builtin_amdgcn_sched_barrier(0);
+            }
+#pragma unroll
+            for (int u = 0; u < 4; ++u) {
+                o[u] = mfma32x32x16<F16>(va[u], pb[q], o[u]);
+                if (q < 2) prob2(q == 0 ? s0 : s1, 2 * q + 1, u);
+                __builtin_amdgcn_sched_barrier(0);
+            }
+        };
+        // Tile j+3 goes into the set tile j-1 used; tile j+2 must have landed
+        // (in every wave) before the barrier that ends step j.
+        auto sync = [&](int j) __attribute__((always_inline)) {
+            if (j + 3 < ntiles) {
+                dma_tile(j + 3, dma_page(j + 3));
+                wait_vmcnt<BIG_LOADS>();
+            } else {
+                __builtin_amdgcn_s_waitcnt(0);
+            }
+            __syncthreads();
+        };
+        auto step = [&](int j, f32x16 &sx, f32x16 &sy, f32x16 &sz) __attribute__((always_inline)) {
+            head(j, sx, sy);
+            quarter(j, 0, sx, sy, sz);
+            quarter(j, 1, sx, sy, sz);
+            ahead_max = max16(sz);  // S^T(j+1, half 0) is complete
+            quarter(j, 2, sx, sy, sx);
+            quarter(j, 3, sx, sy, sx);
+            sync(j);
+        };
+        for (int j = 0; j < ntiles; j += 3) {
+            step(j, sb[0], sb[1], sb[2]);
+            if (j + 1 < ntiles) step(j + 1, sb[2], sb[0], sb[1]);
+            if (j + 2 < ntiles) step(j + 2, sb[1], sb[2], sb[0]);
+        }
+
+        l += __shfl_xor(l, 32);
+        if (row_valid) {
+            const int64_t lrow = int64_t(q_begin + row_tok) * a.num_qo_heads + hk * G + row_head;
+            float w_self = l > 0.f ? a.v_scale / l : 0.f, w_other = 0.f;
+            float lse_row = l > 0.f ? (m + fast_log2(l)) * kLn2 : kNegInf;
+            if (a.fold_lse) {
+                const Fold f = fold_weights(lse_row, a.fold_lse[lrow]);
+                w_self *= f.self;
+                w_other = f.other;
+                lse_row = f.lse;
+            }
+            uint16_t *O = static_cast<uint16_t *>(a.o);
+            const uint16_t *FO = static_cast<const uint16_t *>(a.fold_o);
+#pragma unroll
+            for (int dt = 0; dt < DT; ++dt)
+#pragma unroll
+                for (int m0 = 0; m0 < 4; ++m0) {
+                    const int64_t at = qrow + dt * 32 + 8 * m0 + 4 * hw;
+                    f32x4 v4;
+#pragma unroll
+                    for (int m1 = 0; m1 < 4; ++m1) v4[m1] = o[dt][4 * m0 + m1] * w_self;
+                    if (FO) {
+                        const f32x4 f4 = from16x4<F16>(*reinterpret_cast<const bf16x4 *>(FO + at));
+#pragma unroll
+                        for (int m1 = 0; m1 < 4; ++m1) v4[m1] += f4[m1] * w_other;
+                    }
+                    *reinterpret_cast<bf16x4 *>(O + at) = to16x4<F16>(v4);
+                }
+            if (a.lse && hw == 0) a.lse[lrow] = lse_row;
+        }
+        // the loads of the tiles past the last are still in flight: drain them
+        // before the next item's prologue rewrites the table and the sets
+        __builtin_amdgcn_s_waitcnt(0);
+        __syncthreads();
+    }
+}
+
 // fp32 inputs: one wave per (query token, head) row, keys visited in order
 // with a running maximum, all arithmetic in fp32.
 __global__ __launch_bounds__(kGenericThreads) void attention_fp32_kernel(PrefillArgs a, int D)
@@ -1031,6 +1429,11 @@ static hipError_t launch_prefill_t(const PrefillArgs &a, int head_dim, int varia
             prefill_kernel<128, 8, true, F16, 0><<<grid, 512, 0, s>>>(a);
             return hipGetLastError();
         }
+        if (variant == kPrefillBig) {
+            if (head_dim != 128) return hipErrorInvalidValue;
+            prefill_big_kernel<F16><<<grid, 512, 0, s>>>(a);
+            return hipGetLastError();
+        }
         if (variant == kPrefillWide) {
             switch (head_dim) {
             case 64: prefill_wide_kernel<64, F16><<<grid, 256, 0, s>>>(a); break;
@@ -1039,7 +1442,7 @@ static hipError_t launch_prefill_t(const PrefillArgs &a, int head_dim, int varia
             }
             return hipGetLastError();
         }
-    } else if (variant == kPrefillDma || variant == kPrefillWide) {
+    } else if (variant == kPrefillDma || variant == kPrefillWide || variant == kPrefillBig) {
         return hipErrorInvalidValue;  // 8-bit K/V are widened on the register-staged path
     }
     if (variant == kPrefillRows256) {
@@ -1098,12 +1501,14 @@ static int prefill_blocks_per_cu_t(int head_dim, int variant)
     if constexpr (KVF == 0) {
         if (variant == kPrefillDma)
             return head_dim == 128 ? blocks_per_cu(prefill_kernel<128, 8, true, F16, 0>, 512) : 0;
+        if (variant == kPrefillBig)
+            return head_dim == 128 ? blocks_per_cu(prefill_big_kernel<F16>, 512) : 0;
         if (variant == kPrefillWide) {
             if (head_dim == 64) return blocks_per_cu(prefill_wide_kernel<64, F16>, 256);
             if (head_dim == 128) return blocks_per_cu(prefill_wide_kernel<128, F16>, 256);
             return 0;
         }
-    } else if (variant == kPrefillDma || variant == kPrefillWide) {
+    } else if (variant == kPrefillDma || variant == kPrefillWide || variant == kPrefillBig) {
         return 0;
     }
     if (variant == kPrefillRows256) {

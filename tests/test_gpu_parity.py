@@ -91,7 +91,7 @@ def test_long_prefill_sampled():
     log("long_prefill run")
     att = make_attention(case)
     o, lse = gpu_run(case, att=att)
-    assert att.info().prefill_variant == 4  # the direct-to-LDS kernel the bench times
+    assert att.info().prefill_variant == 5  # the 64-key-step kernel the bench times
     rng = np.random.default_rng(4)
     rows = sorted(set(LONG_ROWS + rng.integers(0, 32768, size=20).tolist()))
     log(f"long_prefill oracle on {len(rows)} rows")
@@ -136,10 +136,12 @@ def test_prefill_small_ragged(P_, W):
 
 # every bf16 prefill kernel variant on the ragged batch: 1 = 4x32 rows, 2 = 8x32
 # rows (register staging), 3 = 4x64 rows, 4 = 8x32 rows with direct-to-LDS
-# row loads (page sizes 1 and 2 take its per-row page path, the others its
-# same-page path; the last tile of each item its clamped-row path)
-@pytest.mark.parametrize("variant", [1, 2, 3, 4])
-@pytest.mark.parametrize("P_", [1, 2, 4, 16])
+# row loads, 5 = 4 with 64-key steps and 16-byte loads into a swizzled layout
+# (page sizes 1, 2 and 4 take their per-row page paths (variant 4: below 4),
+# the others their same-page paths; the last tile of each item the
+# clamped-row path)
+@pytest.mark.parametrize("variant", [1, 2, 3, 4, 5])
+@pytest.mark.parametrize("P_", [1, 2, 4, 8, 16])
 @pytest.mark.parametrize("W", [-1, 0, 33, 200])
 def test_prefill_variants_ragged(variant, P_, W):
     qo = [1, 70, 0, 33, 129, 5, 300]
@@ -152,19 +154,20 @@ def test_prefill_variants_ragged(variant, P_, W):
     compare(o, lse, ro, rl, tag=f"prefill variant={variant} P={P_} W={W}")
 
 
-def test_prefill_dma_variant_prefix_non_causal_and_fallback():
+@pytest.mark.parametrize("variant", [4, 5])
+def test_prefill_dma_variant_prefix_non_causal_and_fallback(variant):
     # non-causal, no window: every item loads all keys of its request
     case = small([20, 7, 64], [50, 7, 400], H_q=8, H_kv=2, D=128, W=-1, seed=21)
     case.causal = False
-    att = make_attention(case, prefill_variant=4)
+    att = make_attention(case, prefill_variant=variant)
     o, lse = gpu_run(case, att=att)
-    assert att.info().prefill_variant == 4
+    assert att.info().prefill_variant == variant
     ro, rl = oracle_for(case)
-    compare(o, lse, ro, rl, tag="dma non-causal")
+    compare(o, lse, ro, rl, tag=f"dma variant {variant} non-causal")
     # page size 1 and 2100 keys: an item spans more pages than the LDS page
     # table holds, so the plan runs the register-staged 256-row kernel
     case = small([40], [2100], H_q=8, H_kv=2, D=128, P_=1, W=-1, seed=22)
-    att = make_attention(case, prefill_variant=4)
+    att = make_attention(case, prefill_variant=variant)
     o, lse = gpu_run(case, att=att)
     assert att.info().prefill_variant == 2
     ro, rl = oracle_for(case)
@@ -516,7 +519,7 @@ def test_cascade_equals_one_paged_prefill(P_, W, trim):
                                 f"variant={att.info().prefill_variant}")
 
 
-@pytest.mark.parametrize("variant", [1, 2, 3, 4])
+@pytest.mark.parametrize("variant", [1, 2, 3, 4, 5])
 def test_cascade_prefill_variants(variant):
     qo = [64, 1, 257, 33, 600]
     kv = [64, 800, 300, 1000, 700]
@@ -762,7 +765,7 @@ def test_decode_step_appends_and_builds_its_page_table(W):
 # sm_scale 0.3 on N(0,1) data puts many logits near and past the cap.
 
 
-@pytest.mark.parametrize("variant", [1, 2, 3, 4])
+@pytest.mark.parametrize("variant", [1, 2, 3, 4, 5])
 @pytest.mark.parametrize("cap", [2.0, 30.0])
 @pytest.mark.parametrize("W", [-1, 33])
 def test_soft_cap_prefill_variants(variant, cap, W):
@@ -819,7 +822,7 @@ def test_soft_cap_fp32_and_cascade():
 # and bf16; the 16-bit kernels read IEEE half on the fp16 matrix instructions.
 
 
-@pytest.mark.parametrize("variant", [1, 2, 3, 4])
+@pytest.mark.parametrize("variant", [1, 2, 3, 4, 5])
 @pytest.mark.parametrize("W", [-1, 0, 33])
 def test_fp16_prefill_variants(variant, W):
     qo = [1, 70, 0, 33, 129, 5, 300]

@@ -99,13 +99,15 @@ def test_prefill_items_cover_every_query_once(W, G):
     items = P.pkvs_plan_copy_items(h)
     assert info.query_tile in (128 // G, 256 // G)
     assert items.shape[0] == info.num_items
+    # key tiles of the kernel the plan runs: 64 keys for variant 5, else 32
+    kt = 64 if info.prefill_variant == 5 else 32
     seen = {}
     for it in items.tolist():
         b, hk, q0, qn, pos0, kv_len, pbase, kvb = it
         assert 1 <= qn <= info.query_tile and kv_len == kv[b] and pbase == kvp[b]
         prefix = kv[b] - qo[b]
         assert pos0 == prefix + (q0 - qop[b])
-        assert kvb % 32 == 0
+        assert kvb % kt == 0
         kve = min(kv_len, pos0 + qn)
         for t in range(q0, q0 + qn):
             seen[(b, hk, t)] = seen.get((b, hk, t), 0) + 1
@@ -114,9 +116,9 @@ def test_prefill_items_cover_every_query_once(W, G):
             first_vis = max(0, p - W) if W >= 0 else 0
             assert kvb <= first_vis and p < kve
         # no key tile of the range is wholly invisible to the item's queries
-        for k0 in range(kvb, kve, 32):
+        for k0 in range(kvb, kve, kt):
             assert any(visible(pos0 + i, j, W) for i in range(qn)
-                       for j in range(k0, min(k0 + 32, kve))), (it, k0)
+                       for j in range(k0, min(k0 + kt, kve))), (it, k0)
     expect = {(b, hk, t) for b in range(len(kv)) for hk in range(2)
               for t in range(qop[b], qop[b + 1])}
     assert set(seen) == expect and set(seen.values()) == {1}
@@ -186,29 +188,33 @@ def test_decode_chunks_partition_the_window(W, split):
 
 
 def test_prefill_variant_choice_and_page_table_fallback():
-    """Large head_dim-128 prefill plans pick the direct-to-LDS kernel (variant
-    4); a plan() whose items span more pages than its LDS page table (2048)
-    runs the register-staged 256-row kernel (variant 2) instead."""
+    """Large head_dim-128 prefill plans pick the 64-key-step direct-to-LDS
+    kernel (variant 5); a plan() whose items span more pages than its LDS page
+    table (2048) runs the register-staged 256-row kernel (variant 2) instead,
+    for both direct-to-LDS variants."""
     big = dict(num_qo_heads=32, num_kv_heads=8, window_left=-1, qo_capacity=32768,
                kv_capacity=65536, batch_capacity=4)
     h = P.pkvs_plan_create(desc(page_size=16, **big))
     qop, kvp, last = csr([4096], [4096], 16)
     P.pkvs_prefill_plan(h, qop, kvp, last, 1, None, None)
-    assert P.pkvs_plan_get_info(h).prefill_variant == 4
-    qop, kvp, last = csr([64], [32768], 16)   # 2048 pages of 16 keys: fits
-    P.pkvs_prefill_plan(h, qop, kvp, last, 1, None, None)
-    assert P.pkvs_plan_get_info(h).prefill_variant == 4
-    qop, kvp, last = csr([64], [32769], 16)   # 2049 pages
-    P.pkvs_prefill_plan(h, qop, kvp, last, 1, None, None)
-    assert P.pkvs_plan_get_info(h).prefill_variant == 2
+    assert P.pkvs_plan_get_info(h).prefill_variant == 5
+    for v in (0, 4, 5):
+        hv = P.pkvs_plan_create(desc(page_size=16, prefill_variant=v, **big))
+        qop, kvp, last = csr([64], [32768], 16)   # 2048 pages of 16 keys: fits
+        P.pkvs_prefill_plan(hv, qop, kvp, last, 1, None, None)
+        assert P.pkvs_plan_get_info(hv).prefill_variant == (v or 5)
+        qop, kvp, last = csr([64], [32769], 16)   # 2049 pages
+        P.pkvs_prefill_plan(hv, qop, kvp, last, 1, None, None)
+        assert P.pkvs_plan_get_info(hv).prefill_variant == 2
     h1 = P.pkvs_plan_create(desc(page_size=1, **dict(big, window_left=1023)))
     qop, kvp, last = csr([8192], [8192], 1)   # windowed items span ~1100 pages
     P.pkvs_prefill_plan(h1, qop, kvp, last, 1, None, None)
-    assert P.pkvs_plan_get_info(h1).prefill_variant == 4
+    assert P.pkvs_plan_get_info(h1).prefill_variant == 5
     # head_dim 64 keeps the register-staged kernel; asking for 4 is refused
     assert P.pkvs_plan_get_info(P.pkvs_plan_create(desc(head_dim=64, **big))).prefill_variant == 2
-    assert err_code(lambda: P.pkvs_plan_create(desc(head_dim=64, prefill_variant=4))) == \
-        P.PKVS_ERR_UNSUPPORTED
+    for v in (4, 5):
+        assert err_code(lambda: P.pkvs_plan_create(desc(head_dim=64, prefill_variant=v))) == \
+            P.PKVS_ERR_UNSUPPORTED
 
 
 def test_grid_does_not_depend_on_the_batch():
@@ -458,6 +464,7 @@ def test_soft_cap_must_be_zero_or_positive_finite(cap):
 @pytest.mark.parametrize("kw,code", [
     (dict(kv_dtype=torch.float8_e4m3fn, dtype=torch.float32), P.PKVS_ERR_UNSUPPORTED),
     (dict(kv_dtype=torch.float8_e5m2, prefill_variant=4), P.PKVS_ERR_UNSUPPORTED),
+    (dict(kv_dtype=torch.float8_e4m3fn, prefill_variant=5), P.PKVS_ERR_UNSUPPORTED),
     (dict(kv_dtype=torch.float8_e5m2, prefill_variant=3), P.PKVS_ERR_UNSUPPORTED),
 ])
 def test_fp8_kv_descriptor_rules(kw, code):
