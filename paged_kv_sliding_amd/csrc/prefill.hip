@@ -1249,21 +1249,28 @@ __global__ __launch_bounds__(512) void prefill_big_kernel(PrefillArgs a)
             mu = m == kNegInf ? 0.f : m;
             __builtin_amdgcn_sched_barrier(0);
         };
-        auto quarter = [&](int j, int q, const f32x16 &s0, const f32x16 &s1, f32x16 &dst)
-            __attribute__((always_inline)) {
+        // Operand reads: K operands of S^T(j+1, half h), k-steps 4kk..4kk+3,
+        // and the V^T operands of quarter q of tile j.  The lane bases and the
+        // wave-uniform parts occupy disjoint bits, so each address is one XOR;
+        // the uniform part is kept opaque so that the per-k-step and
+        // per-dim-tile offsets are not hoisted into registers of their own.
+        // Each read is issued one MFMA group ahead of its use, into the
+        // registers the group before has just consumed: a quarter's K reads
+        // follow the previous quarter's QK MFMAs and its V reads follow the
+        // previous quarter's P.V MFMAs.  Tile j+1's first K reads wait for the
+        // barrier that makes its tile visible; they run under the head.
+        bf16x8 kq[4], va[DT];
+        auto load_k = [&](int j, int q) __attribute__((always_inline)) {
             const int h = q >> 1, kk = q & 1;
-            const uint32_t cur = lds_sets + uint32_t((j & (BIG_SETS - 1)) * BIG_SET);
             const uint32_t nxt = lds_sets + uint32_t(((j + 1) & (BIG_SETS - 1)) * BIG_SET);
-            // LDS reads: K operands of S^T(j+1, half h), k-steps 4kk..4kk+3,
-            // and the V^T operands of this quarter.  The lane bases and the
-            // wave-uniform parts occupy disjoint bits, so each address is one
-            // XOR; the uniform part is kept opaque so that the per-k-step and
-            // per-dim-tile offsets are not hoisted into registers of their own.
             const uint32_t tk = kbase ^ opaque_sgpr(nxt | uint32_t(h * 32 * BIG_ROW + 128 * kk));
-            const uint32_t tv = vbase ^ opaque_sgpr(cur | uint32_t((32 * h + 16 * kk) * BIG_ROW));
-            bf16x8 kq[4], va[DT];
 #pragma unroll
             for (int u = 0; u < 4; ++u) kq[u] = lds_b128(tk ^ uint32_t(32 * u));
+        };
+        auto load_v = [&](int j, int q) __attribute__((always_inline)) {
+            const int h = q >> 1, kk = q & 1;
+            const uint32_t cur = lds_sets + uint32_t((j & (BIG_SETS - 1)) * BIG_SET);
+            const uint32_t tv = vbase ^ opaque_sgpr(cur | uint32_t((32 * h + 16 * kk) * BIG_ROW));
 #pragma unroll
             for (int dt = 0; dt < DT; ++dt) {
                 const uint32_t v0 = tv ^ uint32_t(64 * dt);
@@ -1271,7 +1278,10 @@ __global__ __launch_bounds__(512) void prefill_big_kernel(PrefillArgs a)
                 va[dt] =
                     __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
             }
-            __builtin_amdgcn_sched_barrier(0);
+        };
+        auto quarter = [&](int j, int q, const f32x16 &s0, const f32x16 &s1, f32x16 &dst)
+            __attribute__((always_inline)) {
+            const int kk = q & 1;
             if (kk == 0) {
 #pragma unroll
                 for (int i = 0; i < 16; ++i) dst[i] = 0.f;
@@ -1284,12 +1294,17 @@ __global__ __launch_bounds__(512) void prefill_big_kernel(PrefillArgs a)
                 if (q < 2) prob2(q == 0 ? s0 : s1, 2 * q, u);
                 __builtin_amdgcn_sched_barrier(0);
             }
+            if (q < 3) load_k(j, q + 1);
+            __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
             for (int u = 0; u < 4; ++u) {
                 o[u] = mfma32x32x16<F16>(va[u], pb[q], o[u]);
                 if (q < 2) prob2(q == 0 ? s0 : s1, 2 * q + 1, u);
                 __builtin_amdgcn_sched_barrier(0);
             }
+            if (q < 3) load_v(j, q + 1);
+            else if (j + 1 < ntiles) load_v(j + 1, 0);
+            __builtin_amdgcn_sched_barrier(0);
         };
         // Tile j+3 goes into the set tile j-1 used; tile j+2 must have landed
         // (in every wave) before the barrier that ends step j.
@@ -1303,6 +1318,9 @@ __global__ __launch_bounds__(512) void prefill_big_kernel(PrefillArgs a)
             __syncthreads();
         };
         auto step = [&](int j, f32x16 &sx, f32x16 &sy, f32x16 &sz) __attribute__((always_inline)) {
+            load_k(j, 0);
+            if (j == 0) load_v(0, 0);
+            __builtin_amdgcn_sched_barrier(0);
             head(j, sx, sy);
             quarter(j, 0, sx, sy, sz);
             quarter(j, 1, sx, sy, sz);
