@@ -322,7 +322,17 @@ __global__ __launch_bounds__(kDecodeThreads) void decode_kernel(DecodeArgs a)
     const int n_items = a.ws[kHdrNumItems];
     const uint16_t *Q = static_cast<const uint16_t *>(a.q);
 
-    for (int it = blockIdx.x; it < n_items; it += gridDim.x) {
+    // Items are handed out at run time: each wave starts with item blockIdx.x
+    // and then takes the next untaken one from a counter in the workspace
+    // header, so waves that stream faster take more items and the launch
+    // ends when the slowest wave finishes its last item, not its fourth.
+    int32_t *const ctr = a.ws;
+    auto next_item = [&]() __attribute__((always_inline)) {
+        int v = 0;
+        if (lane == 0) v = atomicAdd(ctr + kHdrNextItem, 1);
+        return int(gridDim.x) + __builtin_amdgcn_readfirstlane(v);
+    };
+    for (int it = blockIdx.x; it < n_items; it = next_item()) {
         const int32_t *w = a.ws + kHeaderWords + int64_t(it) * kDecodeItemWords;
         const int b = w[kDiRequest], hk = w[kDiKvHead];
         const int t0 = w[kDiTokBegin], t1 = w[kDiTokEnd], lo = w[kDiVisLo];
@@ -421,6 +431,12 @@ __global__ __launch_bounds__(kDecodeThreads) void decode_kernel(DecodeArgs a)
                 if (g == 0) a.part_lse[int64_t(slot) * G + r] = lse;
             }
         }
+    }
+    // the last wave of the launch puts the counters back to 0 (every wave has
+    // taken its last item before it counts itself finished)
+    if (lane == 0 && atomicAdd(ctr + kHdrDoneGroups, 1) == int(gridDim.x) - 1) {
+        ctr[kHdrNextItem] = 0;
+        ctr[kHdrDoneGroups] = 0;
     }
 }
 

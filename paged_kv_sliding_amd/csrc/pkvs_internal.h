@@ -19,6 +19,12 @@ enum HeaderField {
     kHdrNumMerges = 1,
     kHdrMergeOffset = 2,  // in int32 words from the start of the workspace
     kHdrItemWords = 3,
+    // work counters of the kernels that hand out items at run time: the next
+    // item past the first grid-stride round, and the workgroups that have
+    // finished; plan() uploads them as 0 and the last workgroup of a launch
+    // puts them back to 0, so every launch (and graph replay) starts from 0
+    kHdrNextItem = 4,
+    kHdrDoneGroups = 5,
 };
 
 // Prefill item: one (request, kv head, query tile).
@@ -86,7 +92,7 @@ struct PrefillArgs {
     const int32_t *kv_indices;
     void *o;
     float *lse;
-    const int32_t *ws;  // int workspace (header + items)
+    int32_t *ws;        // int workspace: header (with the work counters) + items
     int64_t num_pages;
     float scale_log2;   // sm_scale * log2(e), or cap * log2(e) with a soft cap
     float cap_a;        // soft cap: 2 log2(e) sm_scale / cap (soft_cap_unit), 0 = none
@@ -106,7 +112,7 @@ struct DecodeArgs {
     const int32_t *kv_indices;
     void *o;
     float *lse;
-    const int32_t *ws;
+    int32_t *ws;      // int workspace: header (with the work counters) + items
     float *part_o;    // [slots, group, head_dim]
     float *part_lse;  // [slots, group]
     int64_t num_pages;

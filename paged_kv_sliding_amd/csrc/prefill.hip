@@ -1042,6 +1042,7 @@ __global__ __launch_bounds__(512) void prefill_big_kernel(PrefillArgs a)
     struct Lds {
         uint8_t set[BIG_SETS][BIG_SET];
         int32_t pages[kPrefillDmaPages];
+        int32_t next_item;
     };
     __shared__ __attribute__((aligned(1024))) Lds sh;
 
@@ -1085,7 +1086,14 @@ __global__ __launch_bounds__(512) void prefill_big_kernel(PrefillArgs a)
     const char *const Vb = static_cast<const char *>(a.v);
     const int page_mask = a.page_size - 1;
 
-    for (int it = blockIdx.x; it < n_items; it += gridDim.x) {
+    // Items are handed out at run time: each workgroup starts with item
+    // blockIdx.x, claims its next item from a counter in the workspace header
+    // as it starts one, and learns it through LDS at the item's end, so
+    // workgroups that run faster take more items.
+    int32_t *const ctr = a.ws;
+    for (int it = blockIdx.x; it < n_items;) {
+        int claimed = 0;
+        if (tid == 0) claimed = atomicAdd(ctr + kHdrNextItem, 1);
         const int32_t *w = a.ws + kHeaderWords + int64_t(it) * kPrefillItemWords;
         const int hk = w[kPiKvHead], q_begin = w[kPiQBegin], q_count = w[kPiQCount];
         const int pos0 = w[kPiPos0], kv_len = w[kPiKvLen];
@@ -1367,8 +1375,16 @@ __global__ __launch_bounds__(512) void prefill_big_kernel(PrefillArgs a)
         }
         // the loads of the tiles past the last are still in flight: drain them
         // before the next item's prologue rewrites the table and the sets
+        if (tid == 0) sh.next_item = int(gridDim.x) + claimed;
         __builtin_amdgcn_s_waitcnt(0);
         __syncthreads();
+        it = sh.next_item;
+    }
+    // the last workgroup of the launch puts the counters back to 0 (every
+    // workgroup has claimed its last item before it counts itself finished)
+    if (tid == 0 && atomicAdd(ctr + kHdrDoneGroups, 1) == int(gridDim.x) - 1) {
+        ctr[kHdrNextItem] = 0;
+        ctr[kHdrDoneGroups] = 0;
     }
 }
 

@@ -90,7 +90,7 @@ hipError_t launch_prefill_pass(const pkvs_plan *p, const void *q, const void *k,
                                float sm_scale, float k_scale, float v_scale, hipStream_t stream,
                                const void *fold_o = nullptr, const float *fold_lse = nullptr)
 {
-    const int32_t *ws = static_cast<const int32_t *>(p->int_ws);
+    int32_t *ws = static_cast<int32_t *>(p->int_ws);
     PrefillArgs a{};
     a.q = q;
     a.k = k;
@@ -205,7 +205,7 @@ int pkvs_decode_run(const pkvs_plan *p, const void *q, const void *k_cache, cons
         a.kv_indices = kv_indices_d;
         a.o = o;
         a.lse = lse;
-        a.ws = static_cast<const int32_t *>(p->int_ws);
+        a.ws = static_cast<int32_t *>(p->int_ws);
         a.num_pages = num_pages;
         a.scale_log2 = scale_log2;
         a.cap_a = cap_a;
@@ -229,7 +229,7 @@ int pkvs_decode_run(const pkvs_plan *p, const void *q, const void *k_cache, cons
     a.kv_indices = kv_indices_d;
     a.o = o;
     a.lse = lse;
-    a.ws = static_cast<const int32_t *>(p->int_ws);
+    a.ws = static_cast<int32_t *>(p->int_ws);
     const int group = p->desc.num_qo_heads / p->desc.num_kv_heads;
     a.part_o = static_cast<float *>(p->float_ws);
     a.part_lse = a.part_o ? a.part_o + p->slots_cap * group * p->desc.head_dim : nullptr;
