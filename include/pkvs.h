@@ -173,7 +173,12 @@ typedef struct pkvs_plan pkvs_plan;
 int pkvs_plan_create(pkvs_plan **out, const pkvs_desc *desc);
 
 /* Worst-case workspace sizes for the plan's capacities, in bytes.  Callers
- * allocate device buffers at least this large (float_ws may be 0 bytes). */
+ * allocate device buffers at least this large (float_ws may be 0 bytes).
+ * int_ws holds the work list that plan() copies in; the decode kernel and the
+ * default prefill kernel also keep two work counters in its header, which
+ * plan() uploads as 0 and every run() leaves at 0 when it completes, so the
+ * same plan can be run (or a captured run replayed) any number of times, one
+ * run at a time per workspace. */
 int pkvs_workspace_size(const pkvs_plan *plan, size_t *float_ws_bytes, size_t *int_ws_bytes);
 
 /* Plan a causal paged prefill (extend with cached prefix) batch.
