@@ -20,12 +20,17 @@ enum HeaderField {
     kHdrMergeOffset = 2,  // in int32 words from the start of the workspace
     kHdrItemWords = 3,
     // work counters of the kernels that hand out items at run time: the next
-    // item past the first grid-stride round, and the workgroups that have
-    // finished; plan() uploads them as 0 and the last workgroup of a launch
-    // puts them back to 0, so every launch (and graph replay) starts from 0
+    // item past the first grid-stride round (the decode kernel: one counter;
+    // the prefill kernel: one per XCD, kXcds words), and the workgroups that
+    // have finished; plan() uploads them as 0 and the last workgroup of a
+    // launch puts them back to 0, so every launch (and graph replay) starts
+    // from 0
     kHdrNextItem = 4,
-    kHdrDoneGroups = 5,
+    kHdrDoneGroups = 12,
 };
+// XCDs of the device: consecutive workgroups of a launch go to consecutive
+// XCDs (each with its own L2), so workgroup b runs on XCD b mod kXcds
+constexpr int kXcds = 8;
 
 // Prefill item: one (request, kv head, query tile).
 constexpr int kPrefillItemWords = 8;

@@ -1086,14 +1086,19 @@ __global__ __launch_bounds__(512) void prefill_big_kernel(PrefillArgs a)
     const char *const Vb = static_cast<const char *>(a.v);
     const int page_mask = a.page_size - 1;
 
-    // Items are handed out at run time: each workgroup starts with item
-    // blockIdx.x, claims its next item from a counter in the workspace header
-    // as it starts one, and learns it through LDS at the item's end, so
+    // Items are handed out at run time, per XCD: item i belongs to XCD
+    // i mod kXcds, where the grid-stride order would have run it, so items
+    // that share key tiles (the same kv head, neighbouring query tiles) keep
+    // sharing that XCD's L2.  Each workgroup starts with item blockIdx.x,
+    // claims its XCD's next item from a counter in the workspace header as
+    // it starts one, and learns it through LDS at the item's end, so
     // workgroups that run faster take more items.
     int32_t *const ctr = a.ws;
+    const int xcd = blockIdx.x % kXcds;
+    const int xcd_groups = (int(gridDim.x) - xcd + kXcds - 1) / kXcds;
     for (int it = blockIdx.x; it < n_items;) {
         int claimed = 0;
-        if (tid == 0) claimed = atomicAdd(ctr + kHdrNextItem, 1);
+        if (tid == 0) claimed = atomicAdd(ctr + kHdrNextItem + xcd, 1);
         const int32_t *w = a.ws + kHeaderWords + int64_t(it) * kPrefillItemWords;
         const int hk = w[kPiKvHead], q_begin = w[kPiQBegin], q_count = w[kPiQCount];
         const int pos0 = w[kPiPos0], kv_len = w[kPiKvLen];
@@ -1375,7 +1380,7 @@ __global__ __launch_bounds__(512) void prefill_big_kernel(PrefillArgs a)
         }
         // the loads of the tiles past the last are still in flight: drain them
         // before the next item's prologue rewrites the table and the sets
-        if (tid == 0) sh.next_item = int(gridDim.x) + claimed;
+        if (tid == 0) sh.next_item = xcd + kXcds * (xcd_groups + claimed);
         __builtin_amdgcn_s_waitcnt(0);
         __syncthreads();
         it = sh.next_item;
@@ -1383,7 +1388,7 @@ __global__ __launch_bounds__(512) void prefill_big_kernel(PrefillArgs a)
     // the last workgroup of the launch puts the counters back to 0 (every
     // workgroup has claimed its last item before it counts itself finished)
     if (tid == 0 && atomicAdd(ctr + kHdrDoneGroups, 1) == int(gridDim.x) - 1) {
-        ctr[kHdrNextItem] = 0;
+        for (int x = 0; x < kXcds; ++x) ctr[kHdrNextItem + x] = 0;
         ctr[kHdrDoneGroups] = 0;
     }
 }
