@@ -300,7 +300,10 @@ static void build_prefill(Plan *p, const std::vector<Req> &reqs)
 
 // Keys per decode chunk when the caller leaves it to the planner: aim for
 // about auto_target_items chunks over the whole batch (one per resident wave)
-// so every wave gets work in one round, but never cut below kMinAutoSplit keys.
+// so every wave gets work in one round, but never cut below kMinAutoSplit keys,
+// and split only when the estimated time of the split batch (its bytes at the
+// chip's rate, or its longest chunk at one wave's, plus the merge) beats one
+// wave per request and kv head streaming the longest request.
 static int64_t choose_split(const Plan *p, const std::vector<Req> &reqs)
 {
     const pkvs_desc &d = p->desc;
@@ -319,7 +322,13 @@ static int64_t choose_split(const Plan *p, const std::vector<Req> &reqs)
     if (units >= target) return no_split;
     int64_t c = ceil_div(total * d.num_kv_heads, target);
     c = ceil_div(c, kDecodeBlock) * kDecodeBlock;
-    return std::min(no_split, std::max<int64_t>(c, kMinAutoSplit));
+    c = std::min(no_split, std::max<int64_t>(c, kMinAutoSplit));
+    const double key_bytes =
+        2.0 * d.head_dim * (d.kv_format != PKVS_KV_SAME ? 1 : 2);  // K and V of one key, one head
+    const double t_whole = double(longest) * key_bytes / kWaveBytesPerUs;
+    const double t_split = std::max(double(total) * d.num_kv_heads * key_bytes / kChipBytesPerUs,
+                                    double(c) * key_bytes / kWaveBytesPerUs) + kMergeUs;
+    return t_whole <= t_split ? no_split : c;
 }
 
 static int build_decode(Plan *p, const std::vector<Req> &reqs)

@@ -14,6 +14,12 @@ namespace pkvs {
 constexpr int kStages = 4;             // pinned staging buffers for the work-list copy
 constexpr int kDefaultCus = 256;       // compute units assumed when no device is visible
 constexpr int64_t kMinAutoSplit = 256; // smallest key chunk the planner picks by itself
+// Decode cost model of the automatic split (measured on MI355X): one wave
+// streams one item's K/V at about kWaveBytesPerUs, all waves together at about
+// kChipBytesPerUs, and splitting costs a merge launch of about kMergeUs.
+constexpr double kWaveBytesPerUs = 10.0e3;
+constexpr double kChipBytesPerUs = 5.5e6;
+constexpr double kMergeUs = 10.0;
 
 int fail(int code, const char *fmt, ...);
 void clear_error();
