@@ -475,7 +475,7 @@ static int create_plan(const pkvs_desc *desc, bool ragged, Plan **out)
         if (desc->head_dim <= 128 && big_tiles >= 2 * p->num_cus)
             v = desc->head_dim == 128 && kvf == PKVS_KV_SAME ? kPrefillBig : kPrefillRows256;
         if (desc->prefill_variant) v = desc->prefill_variant;
-        // the direct-to-LDS variants need 136-156 KiB of LDS per workgroup
+        // the direct-to-LDS variants need 104-156 KiB of LDS per workgroup
         if ((v == kPrefillDma || v == kPrefillBig) && p->have_gpu && !fp32 &&
             prefill_blocks_per_cu(desc->head_dim, v, f16, kvf) < 1)
             v = kPrefillRows256;

@@ -969,21 +969,17 @@ __global__ __launch_bounds__(256) void prefill_wide_kernel(PrefillArgs a)
 //
 // Staging.  A K or V tile is 64 rows of 256 bytes stored unpadded; one
 // global_load_lds_dwordx4 moves four rows (lane i writes LDS bytes
-// 16i..16i+15 of the 1 KiB group), so a wave stages its 8 K rows and 8 V
+// 16i..16i+15 of the 1 KiB block), so a wave stages its 8 K rows and 8 V
 // rows of a tile with four instructions from one scalar base when the 8 keys
-// share a page.  Bank conflicts of the operand reads are avoided by an XOR
-// swizzle of the 16-byte chunks, applied on the global side (the lane that
-// writes LDS chunk c of a row fetches chunk c ^ f(row)):
-//   K: f(r) = r & 15 -- the 16 rows read by a 16-lane group for one k-step
-//      land in 16 distinct chunk positions;
-//   V: f(r) = 4 (r & 3) -- the four rows of a transposing read by 32 lanes
-//      (two chunks each) land in 16 distinct chunk positions.
+// share a page.  Each lane may fetch any 16-byte chunk of the four rows, so
+// the chunks are placed within a block to suit the operand reads: no two
+// lanes of a read group share a bank position, and the four reads of a
+// quarter lie 256 bytes apart (one lane base plus immediate offsets).  K and
+// V tiles sit in two three-tile rings, so with the loop unrolled by three
+// every ring position is a compile-time constant.
 constexpr int BIG_T = 64;                     // keys per step
-constexpr int BIG_SETS = 4;                   // LDS tile sets
 constexpr int BIG_ROW = 256;                  // bytes per K / V row
 constexpr int BIG_HALF = BIG_T * BIG_ROW;     // K (or V) bytes of one tile
-constexpr int BIG_SET = 2 * BIG_HALF;         // K then V
-constexpr int BIG_LOADS = 4;                  // loads per wave per tile
 
 // Four 16-byte row-group loads from one scalar base per tensor: K rows to
 // LDS mk and mk + 1024 (lane offsets dk0, dk1), V rows to mv and mv + 1024
@@ -1040,7 +1036,8 @@ __global__ __launch_bounds__(512) void prefill_big_kernel(PrefillArgs a)
 {
     constexpr int D = 128, KS = D / 16, DT = D / 32;
     struct Lds {
-        uint8_t set[BIG_SETS][BIG_SET];
+        uint8_t kset[3][BIG_HALF];  // K ring: tile t in kset[t % 3]
+        uint8_t vset[3][BIG_HALF];  // V ring: tile t in vset[t % 3]
         int32_t pages[kPrefillDmaPages];
         int32_t next_item;
     };
@@ -1057,31 +1054,46 @@ __global__ __launch_bounds__(512) void prefill_big_kernel(PrefillArgs a)
     const float cap_a = a.cap_a;
 
     const uint32_t lds_sets =
-        uint32_t(reinterpret_cast<uintptr_t>((__attribute__((address_space(3))) void *)sh.set));
-    // operand reads (byte offsets inside a set): K row 32h + l32, chunk 2ks+hw;
-    // V^T transposing read of rows 4hw + e (+ 16kk, + 8, + 32h), dims
-    // 32dt + 16s + 4q (lane = 16s + 4e + q within its half-wave)
-    // (the k-step and the dim tile only flip bits that the lane's base leaves
-    // to the swizzle, so each offset is the base XOR a constant)
-    const uint32_t kbase = uint32_t(l32 * BIG_ROW + ((hw ^ (l32 & 15)) << 4));
-    const uint32_t vbase = [&] {
+        uint32_t(reinterpret_cast<uintptr_t>((__attribute__((address_space(3))) void *)sh.kset));
+    const uint32_t lds_v = lds_sets + uint32_t(3 * BIG_HALF);
+    // LDS layout of a K or V tile: 1 KiB blocks of four rows; the 16-byte
+    // chunk c (dims 8c..8c+7) of row R sits at position
+    //   K: 16 (c / 4) + 4 ((c % 4 + R / 4) % 4) + R % 4
+    //   V: 16 (c / 4) + 4 (R % 4) + c % 4
+    // of block R / 4.  A 16-lane group of K operand reads (rows R..R+15, one
+    // chunk) and a 32-lane group of V transposing reads (rows 4hw..4hw+3,
+    // four chunks) then cover 16 distinct 16-byte bank positions, and the
+    // four reads of a quarter (K: chunks c, c+4, c+8, c+12; V: dim tiles 0-3)
+    // lie 256 bytes apart, so every operand address is a lane base plus an
+    // immediate offset.
+    // K operand of lane (l32, hw), k-step kk + 2u of half h: row 32h + l32,
+    // chunk 4u + 2kk + hw.
+    const uint32_t kvar0 = lds_sets + uint32_t(1024 * (l32 >> 2) + 16 * (l32 & 3) +
+                                               64 * ((hw + (l32 >> 2)) & 3));
+    const uint32_t kvar1 = lds_sets + uint32_t(1024 * (l32 >> 2) + 16 * (l32 & 3) +
+                                               64 * ((2 + hw + (l32 >> 2)) & 3));
+    // V^T transposing read of lane (hw, e, s16, q): row 4hw + e (+ 16kk, + 8,
+    // + 32h), dims 32dt + 16s16 + 4q
+    const uint32_t vvar = [&] {
         const int e = (lane & 15) >> 2, q = lane & 3, s16 = (lane >> 4) & 1;
-        const int chunk = 2 * s16 + (q >> 1);
-        return uint32_t(BIG_HALF + (4 * hw + e) * BIG_ROW + ((chunk ^ (4 * e)) << 4) + (q & 1) * 8);
+        return lds_v + uint32_t(1024 * hw + 64 * e + 16 * (2 * s16 + (q >> 1)) + 8 * (q & 1));
     }();
-    // staging: lane (r' = lane / 16, position p = lane % 16) of load i writes
-    // LDS chunk p of row 8*wave + 4i + r' and fetches the chunk that the
-    // swizzle puts there
+    // staging: load i of a wave's rows 8 wave + 4i .. + 3 (block b = 2 wave + i)
+    // writes LDS byte 16L of the block from lane L, which fetches
+    //   K: row L % 4, chunk 4 (L / 16) + ((L / 4 - b) % 4)
+    //   V: row (L / 4) % 4, chunk 4 (L / 16) + L % 4
     const int64_t slot_stride = int64_t(a.num_kv_heads) * D;
     const int32_t slot_bytes = int32_t(slot_stride * 2);
     const uint32_t page_bytes = uint32_t(slot_stride * a.page_rows * 2);
-    // (slot_bytes is a multiple of 256, so the swizzled chunk offset is the low
-    // byte of each lane offset; load 1 fetches rows 4 further on, and for K
-    // the swizzle of its rows differs from load 0's in bit 2 of the chunk)
-    const int rr = lane >> 4, pp = lane & 15;
-    const uint32_t dk0 = uint32_t(rr * slot_bytes + ((pp ^ rr ^ (8 * (wave & 1))) << 4));
-    const uint32_t dv0 = uint32_t(rr * slot_bytes + ((pp ^ (4 * rr)) << 4));
+    const int kr = lane & 3, vr = (lane >> 2) & 3;
+    const uint32_t kc0 = uint32_t(16 * (4 * (lane >> 4) + (((lane >> 2) - 2 * (wave & 1)) & 3)));
+    const uint32_t kc1 = uint32_t(16 * (4 * (lane >> 4) + (((lane >> 2) - 2 * (wave & 1) - 1) & 3)));
+    const uint32_t vc = uint32_t(16 * (4 * (lane >> 4) + (lane & 3)));
     const uint32_t row4 = uint32_t(4 * slot_bytes);
+    const uint32_t dk0 = uint32_t(kr * slot_bytes) + kc0;
+    const uint32_t dk1 = uint32_t(kr * slot_bytes) + row4 + kc1;
+    const uint32_t dv0 = uint32_t(vr * slot_bytes) + vc;
+    const uint32_t dv1 = dv0 + row4;
     const char *const Kb = static_cast<const char *>(a.k);
     const char *const Vb = static_cast<const char *>(a.v);
     const int page_mask = a.page_size - 1;
@@ -1134,26 +1146,27 @@ __global__ __launch_bounds__(512) void prefill_big_kernel(PrefillArgs a)
             const int e = min(max((key >> a.log2_page) - pt_lo, 0), kPrefillDmaPages - 1);
             return min(max(sh.pages[e], 0), int32_t(a.num_pages - 1));
         };
-        // the wave's 8 rows of tile t: K and V, four loads
-        auto dma_tile = [&](int t, int32_t pg0) __attribute__((always_inline)) {
+        // the wave's 8 rows of tile t (ring position p = t % 3): K and V, four loads
+        auto dma_tile = [&](int t, int p, int32_t pg0) __attribute__((always_inline)) {
             const int key0 = kv_begin + t * BIG_T + 8 * uwave;
-            const uint32_t set_b = lds_sets + uint32_t((t & (BIG_SETS - 1)) * BIG_SET);
-            const uint32_t mk = set_b + uint32_t(8 * uwave * BIG_ROW);
-            const uint32_t mv = mk + uint32_t(BIG_HALF);
+            const uint32_t mk = lds_sets + uint32_t(p * BIG_HALF + 8 * uwave * BIG_ROW);
+            const uint32_t mv = lds_v + uint32_t(p * BIG_HALF + 8 * uwave * BIG_ROW);
             if (key0 + 7 <= kv_last && (key0 & page_mask) + 8 <= a.page_size) {
                 const int64_t off = int64_t(uint64_t(uint32_t(pg0)) * page_bytes) +
                                     int32_t((key0 & page_mask) * slot_bytes + head_bytes);
-                big_dma4(mk, mv, dk0, (dk0 ^ 64u) + row4, dv0, dv0 + row4, Kb + off, Vb + off);
+                big_dma4(mk, mv, dk0, dk1, dv0, dv1, Kb + off, Vb + off);
             } else {
 #pragma unroll
                 for (int i = 0; i < 2; ++i) {
-                    const int key = min(key0 + 4 * i + (lane >> 4), kv_last);
-                    const int32_t pg = page_entry(key);
-                    const int64_t off = int64_t(uint64_t(uint32_t(pg)) * page_bytes) +
-                                        int32_t((key & page_mask) * slot_bytes + head_bytes);
-                    big_dma1(mk + uint32_t(i * 1024),
-                             Kb + (off + int32_t((i ? dk0 ^ 64u : dk0) & 255u)));
-                    big_dma1(mv + uint32_t(i * 1024), Vb + (off + int32_t(dv0 & 255u)));
+                    const int keyk = min(key0 + 4 * i + kr, kv_last);
+                    const int keyv = min(key0 + 4 * i + vr, kv_last);
+                    const int32_t pk = page_entry(keyk), pv = page_entry(keyv);
+                    const int64_t offk = int64_t(uint64_t(uint32_t(pk)) * page_bytes) +
+                                         int32_t((keyk & page_mask) * slot_bytes + head_bytes);
+                    const int64_t offv = int64_t(uint64_t(uint32_t(pv)) * page_bytes) +
+                                         int32_t((keyv & page_mask) * slot_bytes + head_bytes);
+                    big_dma1(mk + uint32_t(i * 1024), Kb + (offk + int32_t(i ? kc1 : kc0)));
+                    big_dma1(mv + uint32_t(i * 1024), Vb + (offv + int32_t(vc)));
                 }
             }
         };
@@ -1162,7 +1175,7 @@ __global__ __launch_bounds__(512) void prefill_big_kernel(PrefillArgs a)
                 page_entry(min(kv_begin + t * BIG_T + 8 * uwave, kv_last)));
         };
 
-        // prologue: page table, then tiles 0..2 in flight; tiles 0 and 1 landed
+        // prologue: page table, then tiles 0 and 1 landed (step j loads tile j+2)
         {
             const int pt_n =
                 ntiles > 0 ? min((kv_last >> a.log2_page) - pt_lo + 1, kPrefillDmaPages) : 0;
@@ -1175,7 +1188,7 @@ __global__ __launch_bounds__(512) void prefill_big_kernel(PrefillArgs a)
         __syncthreads();
         if (ntiles > 0) {
 #pragma unroll 1
-            for (int t = 0; t < min(ntiles, 3); ++t) dma_tile(t, dma_page(t));
+            for (int t = 0; t < min(ntiles, 2); ++t) dma_tile(t, t, dma_page(t));
             __builtin_amdgcn_s_waitcnt(0);
         }
         __syncthreads();
@@ -1192,7 +1205,7 @@ __global__ __launch_bounds__(512) void prefill_big_kernel(PrefillArgs a)
 #pragma unroll
                 for (int h = 0; h < 2; ++h)
                     s[h] = mfma32x32x16<F16>(
-                        lds_b128(kbase ^ opaque_sgpr(lds_sets | uint32_t(h * 32 * BIG_ROW + 32 * ks))),
+                        lds_b128((ks & 1 ? kvar1 : kvar0) + uint32_t(h * 32 * BIG_ROW + 256 * (ks >> 1))),
                         qf[ks], s[h]);
         }
 
@@ -1262,37 +1275,38 @@ __global__ __launch_bounds__(512) void prefill_big_kernel(PrefillArgs a)
             mu = m == kNegInf ? 0.f : m;
             __builtin_amdgcn_sched_barrier(0);
         };
-        // Operand reads: K operands of S^T(j+1, half h), k-steps 4kk..4kk+3,
-        // and the V^T operands of quarter q of tile j.  The lane bases and the
-        // wave-uniform parts occupy disjoint bits, so each address is one XOR;
-        // the uniform part is kept opaque so that the per-k-step and
-        // per-dim-tile offsets are not hoisted into registers of their own.
+        // Operand reads: K operands of S^T(j+1, half h), k-steps kk, kk+2,
+        // kk+4, kk+6, and the V^T operands of quarter q of tile j.
         // Each read is issued one MFMA group ahead of its use, into the
         // registers the group before has just consumed: a quarter's K reads
         // follow the previous quarter's QK MFMAs and its V reads follow the
         // previous quarter's P.V MFMAs.  Tile j+1's first K reads wait for the
         // barrier that makes its tile visible; they run under the head.
         bf16x8 kq[4], va[DT];
-        auto load_k = [&](int j, int q) __attribute__((always_inline)) {
+        // lane bases of the step (copied once per step, so that each read's
+        // constant offset stays an immediate of the read)
+        uint32_t kv0 = kvar0, kv1 = kvar1, vv = vvar;
+        // K operands of S^T(j+1, half h), k-steps kk, kk+2, kk+4, kk+6 (tile
+        // j+1 in ring position p1)
+        auto load_k = [&](int p1, int q) __attribute__((always_inline)) {
             const int h = q >> 1, kk = q & 1;
-            const uint32_t nxt = lds_sets + uint32_t(((j + 1) & (BIG_SETS - 1)) * BIG_SET);
-            const uint32_t tk = kbase ^ opaque_sgpr(nxt | uint32_t(h * 32 * BIG_ROW + 128 * kk));
+            const uint32_t kb = kk ? kv1 : kv0;
 #pragma unroll
-            for (int u = 0; u < 4; ++u) kq[u] = lds_b128(tk ^ uint32_t(32 * u));
+            for (int u = 0; u < 4; ++u)
+                kq[u] = lds_b128(kb + uint32_t(p1 * BIG_HALF + h * 32 * BIG_ROW + 256 * u));
         };
-        auto load_v = [&](int j, int q) __attribute__((always_inline)) {
+        // V^T operands of quarter q of the tile in ring position p
+        auto load_v = [&](int p, int q) __attribute__((always_inline)) {
             const int h = q >> 1, kk = q & 1;
-            const uint32_t cur = lds_sets + uint32_t((j & (BIG_SETS - 1)) * BIG_SET);
-            const uint32_t tv = vbase ^ opaque_sgpr(cur | uint32_t((32 * h + 16 * kk) * BIG_ROW));
 #pragma unroll
             for (int dt = 0; dt < DT; ++dt) {
-                const uint32_t v0 = tv ^ uint32_t(64 * dt);
+                const uint32_t v0 = vv + uint32_t(p * BIG_HALF + (32 * h + 16 * kk) * BIG_ROW + 256 * dt);
                 const i16x4 lo = lds_tr(v0), hi = lds_tr(v0 + 8 * BIG_ROW);
                 va[dt] =
                     __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
             }
         };
-        auto quarter = [&](int j, int q, const f32x16 &s0, const f32x16 &s1, f32x16 &dst)
+        auto quarter = [&](int j, int p, int q, const f32x16 &s0, const f32x16 &s1, f32x16 &dst)
             __attribute__((always_inline)) {
             const int kk = q & 1;
             if (kk == 0) {
@@ -1303,11 +1317,11 @@ __global__ __launch_bounds__(512) void prefill_big_kernel(PrefillArgs a)
             // P.V MFMAs, which use block 0); quarter 1 makes blocks 2 and 3
 #pragma unroll
             for (int u = 0; u < 4; ++u) {
-                dst = mfma32x32x16<F16>(kq[u], qf[4 * kk + u], dst);
+                dst = mfma32x32x16<F16>(kq[u], qf[kk + 2 * u], dst);
                 if (q < 2) prob2(q == 0 ? s0 : s1, 2 * q, u);
                 __builtin_amdgcn_sched_barrier(0);
             }
-            if (q < 3) load_k(j, q + 1);
+            if (q < 3) load_k((p + 1) % 3, q + 1);
             __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
             for (int u = 0; u < 4; ++u) {
@@ -1315,37 +1329,38 @@ __global__ __launch_bounds__(512) void prefill_big_kernel(PrefillArgs a)
                 if (q < 2) prob2(q == 0 ? s0 : s1, 2 * q + 1, u);
                 __builtin_amdgcn_sched_barrier(0);
             }
-            if (q < 3) load_v(j, q + 1);
-            else if (j + 1 < ntiles) load_v(j + 1, 0);
+            if (q < 3) load_v(p, q + 1);
+            else if (j + 1 < ntiles) load_v((p + 1) % 3, 0);
             __builtin_amdgcn_sched_barrier(0);
         };
-        // Tile j+3 goes into the set tile j-1 used; tile j+2 must have landed
-        // (in every wave) before the barrier that ends step j.
-        auto sync = [&](int j) __attribute__((always_inline)) {
-            if (j + 3 < ntiles) {
-                dma_tile(j + 3, dma_page(j + 3));
-                wait_vmcnt<BIG_LOADS>();
-            } else {
-                __builtin_amdgcn_s_waitcnt(0);
+        // Step j loads tile j+2 into ring position (j+2) % 3, which tile j-1
+        // left at the barrier that began the step; it lands before the
+        // barrier that ends the step, when tile j+1's K is read next.
+        auto step = [&](int j, int p, f32x16 &sx, f32x16 &sy, f32x16 &sz) __attribute__((always_inline)) {
+            if (j + 2 < ntiles) dma_tile(j + 2, (p + 2) % 3, dma_page(j + 2));
+            {
+                uint32_t x0 = kvar0, x1 = kvar1, x2 = vvar;
+                asm volatile("" : "+v"(x0), "+v"(x1), "+v"(x2));
+                kv0 = x0;
+                kv1 = x1;
+                vv = x2;
             }
-            __syncthreads();
-        };
-        auto step = [&](int j, f32x16 &sx, f32x16 &sy, f32x16 &sz) __attribute__((always_inline)) {
-            load_k(j, 0);
-            if (j == 0) load_v(0, 0);
+            load_k((p + 1) % 3, 0);
+            if (j == 0) load_v(p, 0);
             __builtin_amdgcn_sched_barrier(0);
             head(j, sx, sy);
-            quarter(j, 0, sx, sy, sz);
-            quarter(j, 1, sx, sy, sz);
+            quarter(j, p, 0, sx, sy, sz);
+            quarter(j, p, 1, sx, sy, sz);
             ahead_max = max16(sz);  // S^T(j+1, half 0) is complete
-            quarter(j, 2, sx, sy, sx);
-            quarter(j, 3, sx, sy, sx);
-            sync(j);
+            quarter(j, p, 2, sx, sy, sx);
+            quarter(j, p, 3, sx, sy, sx);
+            __builtin_amdgcn_s_waitcnt(0);
+            __syncthreads();
         };
         for (int j = 0; j < ntiles; j += 3) {
-            step(j, sb[0], sb[1], sb[2]);
-            if (j + 1 < ntiles) step(j + 1, sb[2], sb[0], sb[1]);
-            if (j + 2 < ntiles) step(j + 2, sb[1], sb[2], sb[0]);
+            step(j, 0, sb[0], sb[1], sb[2]);
+            if (j + 1 < ntiles) step(j + 1, 1, sb[2], sb[0], sb[1]);
+            if (j + 2 < ntiles) step(j + 2, 2, sb[1], sb[2], sb[0]);
         }
 
         l += __shfl_xor(l, 32);
