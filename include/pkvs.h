@@ -110,7 +110,7 @@ typedef enum pkvs_kind { PKVS_PREFILL = 0, PKVS_DECODE = 1, PKVS_CASCADE = 2 } p
  *                   3 = 4 waves x 64 rows, software-pipelined (2 and 3: head_dim
  *                   <= 128), 4 = 8 waves x 32 rows with K/V rows loaded straight
  *                   into LDS, 5 = as 4 with 64-key steps and 16-byte loads
- *                   into an XOR-swizzled LDS layout (4 and 5: head_dim 128,
+ *                   into a chunk-permuted LDS layout (4 and 5: head_dim 128,
  *                   16-bit K/V; a plan() whose items span more than 2048
  *                   pages of keys runs variant 2 instead); rows are (query
  *                   token, head) pairs
@@ -123,6 +123,15 @@ typedef enum pkvs_kind { PKVS_PREFILL = 0, PKVS_DECODE = 1, PKVS_CASCADE = 2 } p
  *                   on the way to the matrix cores; prefill variants 1 and 2,
  *                   the planner picks one).  A cascade's new-token K/V stay in
  *                   dtype; only its cache is 8-bit.
+ *  decode_waves     decode: waves that share one work item (request, kv
+ *                   head, chunk): 1, or 4 (each streams a quarter of the
+ *                   chunk's keys and the four combine their partial results
+ *                   in LDS, as pkvs_merge_state would); 0 = planner's choice:
+ *                   4 when batch_capacity x num_kv_heads x 32 is at most the
+ *                   device's resident one-wave items (32 pairs on a 256-CU
+ *                   MI355X) and kv_capacity (cut to window_left + 1) exceeds
+ *                   2048 keys, else 1.  Fixed for the plan's lifetime (every
+ *                   plan() runs the same kernel).
  *  logits_soft_cap  0 (off) or c > 0: every logit x = sm_scale * q.k becomes
  *                   c * tanh(x / c) before the softmax and the LSE ([FIB]
  *                   forward_extend / forward_decode pass logits_soft_cap to
@@ -148,6 +157,7 @@ typedef struct pkvs_desc {
     int64_t kv_capacity;
     float logits_soft_cap;
     int32_t kv_format;
+    int32_t decode_waves;
 } pkvs_desc;
 
 /* Read-only facts about a plan (for callers, tests and profilers). */
@@ -163,6 +173,7 @@ typedef struct pkvs_plan_info {
     int32_t query_tile;      /* prefill: query tokens per item */
     int32_t num_cus;         /* compute units the grid was sized for */
     int32_t prefill_variant; /* prefill: kernel variant the last plan() runs */
+    int32_t decode_waves;    /* decode: waves that share one work item */
 } pkvs_plan_info;
 
 typedef struct pkvs_plan pkvs_plan;

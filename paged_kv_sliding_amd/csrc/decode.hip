@@ -312,32 +312,58 @@ constexpr int decode_stages() { return KVF == 0 ? (D >= 256 ? 2 : 3) : (D >= 256
 
 // NS register buffers of 32 keys each: NS-1 blocks are in flight while one is
 // being computed.
-template <int D, int NS, bool F16, int KVF>
-__global__ __launch_bounds__(kDecodeThreads) void decode_kernel(DecodeArgs a)
+// NW waves share a work item: wave w streams the w-th of NW contiguous runs of
+// the chunk's key blocks with its own running maximum, sum and O, and the
+// waves combine them through LDS (the LSE-weighted sum of merge_state), so a
+// small batch streams each (request, kv head) at NW waves' rate with no
+// partials in memory and no merge launch.
+template <int D, int NW>
+struct DecodeMergeLds {
+    static constexpr int NV = DecodeBuf<D, 0>::NV;
+    float m[NW][16], l[NW][16];
+    float o[NW > 1 ? NW - 1 : 1][NW > 1 ? NV * 32 : 1][64];  // waves 1.., element, lane
+    int32_t next_item;
+};
+
+template <int D, int NS, bool F16, int KVF, int NW>
+__global__ __launch_bounds__(kDecodeThreads * NW) void decode_kernel(DecodeArgs a)
 {
     constexpr int KS = D / 32, NV = DecodeBuf<D, KVF>::NV;
-    const int lane = threadIdx.x;
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int wave = NW > 1 ? __builtin_amdgcn_readfirstlane(tid >> 6) : 0;
     const int r = lane & 15, g = lane >> 4;
     const int G = 1 << a.log2_group;
     const int n_items = a.ws[kHdrNumItems];
     const uint16_t *Q = static_cast<const uint16_t *>(a.q);
+    __shared__ DecodeMergeLds<D, NW> sh;
 
-    // Items are handed out at run time: each wave starts with item blockIdx.x
-    // and then takes the next untaken one from a counter in the workspace
-    // header, so waves that stream faster take more items and the launch
-    // ends when the slowest wave finishes its last item, not its fourth.
+    // Items are handed out at run time: each workgroup starts with item
+    // blockIdx.x and then takes the next untaken one from a counter in the
+    // workspace header, so workgroups that stream faster take more items and
+    // the launch ends when the slowest finishes its last item, not its fourth.
+    // (One wave: claimed at the item's end; several: claimed by thread 0 at the
+    // item's start and passed on through LDS at its end.)
     int32_t *const ctr = a.ws;
     auto next_item = [&]() __attribute__((always_inline)) {
         int v = 0;
         if (lane == 0) v = atomicAdd(ctr + kHdrNextItem, 1);
         return int(gridDim.x) + __builtin_amdgcn_readfirstlane(v);
     };
-    for (int it = blockIdx.x; it < n_items; it = next_item()) {
+    // Workgroups past the item count have nothing to claim: they leave without
+    // touching the counters, and only the others count themselves finished.
+    if (int(blockIdx.x) >= n_items) return;
+    const int participants = min(int(gridDim.x), n_items);
+    for (int it = blockIdx.x; it < n_items;) {
+        int claimed = 0;
+        if (NW > 1 && tid == 0) claimed = atomicAdd(ctr + kHdrNextItem, 1);
         const int32_t *w = a.ws + kHeaderWords + int64_t(it) * kDecodeItemWords;
         const int b = w[kDiRequest], hk = w[kDiKvHead];
         const int t0 = w[kDiTokBegin], t1 = w[kDiTokEnd], lo = w[kDiVisLo];
         const int page_base = w[kDiPageBase], slot = w[kDiSlot];
-        (void)r;
+        // this wave's run of the chunk's key blocks: [s0, s1)
+        const int nblk = t0 < t1 ? (t1 - t0 + kDecodeBlock - 1) / kDecodeBlock : 0;
+        const int s0 = t0 + kDecodeBlock * (nblk * wave / NW);
+        const int s1 = min(t1, t0 + kDecodeBlock * (nblk * (wave + 1) / NW));
 
         // Q^T operand: head r of the group, the dims of k-step s for lane
         // group g (kstep_dim; zero for padding heads)
@@ -355,11 +381,11 @@ __global__ __launch_bounds__(kDecodeThreads) void decode_kernel(DecodeArgs a)
 #pragma unroll
             for (int e = 0; e < 8; ++e) st.o[u][e] = f32x4{0.f, 0.f, 0.f, 0.f};
 
-        if (t0 < t1) {
+        if (s0 < s1) {
             PageWindow pw;
             pw.page_base = page_base;
-            pw.base = __builtin_amdgcn_readfirstlane(t0 >> a.log2_page);
-            pw.last_pg = (t1 - 1) >> a.log2_page;
+            pw.base = __builtin_amdgcn_readfirstlane(s0 >> a.log2_page);
+            pw.last_pg = (s1 - 1) >> a.log2_page;
             pw.cur = load_page_id(a, pw, pw.base + lane);
             pw.nxt = load_page_id(a, pw, pw.base + 64 + lane);
             DecodeBuf<D, KVF> buf[NS];
@@ -367,17 +393,17 @@ __global__ __launch_bounds__(kDecodeThreads) void decode_kernel(DecodeArgs a)
             // are never computed
 #pragma unroll
             for (int s = 0; s + 1 < NS; ++s)
-                decode_load<D, KVF>(buf[s], a, pw, t0 + kDecodeBlock * s, t1, hk, lane);
-            int blk = t0;
+                decode_load<D, KVF>(buf[s], a, pw, s0 + kDecodeBlock * s, s1, hk, lane);
+            int blk = s0;
             bool done = false;
             while (!done) {
 #pragma unroll
                 for (int s = 0; s < NS; ++s) {
                     decode_load<D, KVF>(buf[(s + NS - 1) % NS], a, pw, blk + kDecodeBlock * (NS - 1),
-                                   t1, hk, lane);
-                    decode_compute<D, F16, KVF>(buf[s], st, qf, blk, lo, t1, a.scale_log2, a.cap_a, lane);
+                                   s1, hk, lane);
+                    decode_compute<D, F16, KVF>(buf[s], st, qf, blk, lo, s1, a.scale_log2, a.cap_a, lane);
                     blk += kDecodeBlock;
-                    if (blk >= t1) {
+                    if (blk >= s1) {
                         done = true;
                         break;
                     }
@@ -386,12 +412,54 @@ __global__ __launch_bounds__(kDecodeThreads) void decode_kernel(DecodeArgs a)
         }
 
         // the four lane groups hold disjoint keys of the same head: sum them
-        float l = st.l;
+        float l = st.l, m = st.m;
         l += __shfl_xor(l, 16);
         l += __shfl_xor(l, 32);
+        if constexpr (NW > 1) {
+            // every wave rescales its sum and O to the largest maximum; waves
+            // 1.. leave O in LDS (element-major, lane-contiguous) for wave 0
+            if (g == 0) {
+                sh.m[wave][r] = m;
+                sh.l[wave][r] = l;
+            }
+            __syncthreads();
+            float mx = kNegInf;
+#pragma unroll
+            for (int w2 = 0; w2 < NW; ++w2) mx = fmaxf(mx, sh.m[w2][r]);
+            const float mu = mx == kNegInf ? 0.f : mx;
+            float lt = 0.f;
+#pragma unroll
+            for (int w2 = 0; w2 < NW; ++w2) lt += sh.l[w2][r] * fast_exp2(sh.m[w2][r] - mu);
+            const float f = fast_exp2(m - mu);
+            if (wave > 0) {
+#pragma unroll
+                for (int u = 0; u < NV; ++u)
+#pragma unroll
+                    for (int e = 0; e < 8; ++e)
+#pragma unroll
+                        for (int i = 0; i < 4; ++i)
+                            sh.o[wave - 1][(u * 8 + e) * 4 + i][lane] = st.o[u][e][i] * f;
+            }
+            __syncthreads();
+            if (wave == 0) {
+#pragma unroll
+                for (int u = 0; u < NV; ++u)
+#pragma unroll
+                    for (int e = 0; e < 8; ++e)
+#pragma unroll
+                        for (int i = 0; i < 4; ++i) {
+                            float acc = st.o[u][e][i] * f;
+#pragma unroll
+                            for (int w2 = 1; w2 < NW; ++w2) acc += sh.o[w2 - 1][(u * 8 + e) * 4 + i][lane];
+                            st.o[u][e][i] = acc;
+                        }
+            }
+            m = mx;
+            l = lt;
+        }
         const float inv = l > 0.f ? a.v_scale / l : 0.f;
-        const float lse = l > 0.f ? (st.m + fast_log2(l)) * kLn2 : kNegInf;
-        if (r < G) {
+        const float lse = l > 0.f ? (m + fast_log2(l)) * kLn2 : kNegInf;
+        if (wave == 0 && r < G) {
             // O^T accumulator: lane (head r, group g) holds dims 128u+32g+8i+e
             const int h = hk * G + r;
             if (slot < 0) {
@@ -431,10 +499,18 @@ __global__ __launch_bounds__(kDecodeThreads) void decode_kernel(DecodeArgs a)
                 if (g == 0) a.part_lse[int64_t(slot) * G + r] = lse;
             }
         }
+        if constexpr (NW > 1) {
+            // also orders this item's LDS reads before the next item's writes
+            if (tid == 0) sh.next_item = int(gridDim.x) + claimed;
+            __syncthreads();
+            it = sh.next_item;
+        } else {
+            it = next_item();
+        }
     }
-    // the last wave of the launch puts the counters back to 0 (every wave has
+    // the last participating workgroup puts the counters back to 0 (each has
     // taken its last item before it counts itself finished)
-    if (lane == 0 && atomicAdd(ctr + kHdrDoneGroups, 1) == int(gridDim.x) - 1) {
+    if (tid == 0 && atomicAdd(ctr + kHdrDoneGroups, 1) == participants - 1) {
         ctr[kHdrNextItem] = 0;
         ctr[kHdrDoneGroups] = 0;
     }
@@ -484,41 +560,52 @@ __global__ __launch_bounds__(kMergeThreads) void decode_merge_kernel(DecodeArgs 
 
 }  // namespace
 
-template <bool F16, int KVF>
-static hipError_t launch_decode_t(const DecodeArgs &a, int head_dim, int grid, hipStream_t s)
+template <bool F16, int KVF, int NW>
+static hipError_t launch_decode_w(const DecodeArgs &a, int head_dim, int grid, hipStream_t s)
 {
     switch (head_dim) {
     case 64:
-        decode_kernel<64, decode_stages<64, KVF>(), F16, KVF><<<grid, kDecodeThreads, 0, s>>>(a);
+        decode_kernel<64, decode_stages<64, KVF>(), F16, KVF, NW><<<grid, kDecodeThreads * NW, 0, s>>>(a);
         break;
     case 128:
-        decode_kernel<128, decode_stages<128, KVF>(), F16, KVF><<<grid, kDecodeThreads, 0, s>>>(a);
+        decode_kernel<128, decode_stages<128, KVF>(), F16, KVF, NW><<<grid, kDecodeThreads * NW, 0, s>>>(a);
         break;
     case 256:
-        decode_kernel<256, decode_stages<256, KVF>(), F16, KVF><<<grid, kDecodeThreads, 0, s>>>(a);
+        decode_kernel<256, decode_stages<256, KVF>(), F16, KVF, NW><<<grid, kDecodeThreads * NW, 0, s>>>(a);
         break;
     default: return hipErrorInvalidValue;
     }
     return hipGetLastError();
 }
 
-template <bool F16>
-static hipError_t launch_decode_f(const DecodeArgs &a, int head_dim, int kv_format, int grid,
+template <bool F16, int KVF>
+static hipError_t launch_decode_t(const DecodeArgs &a, int head_dim, int waves, int grid,
                                   hipStream_t s)
 {
+    switch (waves) {
+    case 1: return launch_decode_w<F16, KVF, 1>(a, head_dim, grid, s);
+    case 4: return launch_decode_w<F16, KVF, 4>(a, head_dim, grid, s);
+    default: return hipErrorInvalidValue;
+    }
+}
+
+template <bool F16>
+static hipError_t launch_decode_f(const DecodeArgs &a, int head_dim, int kv_format, int waves,
+                                  int grid, hipStream_t s)
+{
     switch (kv_format) {
-    case 0: return launch_decode_t<F16, 0>(a, head_dim, grid, s);
-    case PKVS_KV_FP8_E4M3: return launch_decode_t<F16, 1>(a, head_dim, grid, s);
-    case PKVS_KV_FP8_E5M2: return launch_decode_t<F16, 2>(a, head_dim, grid, s);
+    case 0: return launch_decode_t<F16, 0>(a, head_dim, waves, grid, s);
+    case PKVS_KV_FP8_E4M3: return launch_decode_t<F16, 1>(a, head_dim, waves, grid, s);
+    case PKVS_KV_FP8_E5M2: return launch_decode_t<F16, 2>(a, head_dim, waves, grid, s);
     default: return hipErrorInvalidValue;
     }
 }
 
 hipError_t launch_decode_16bit(const DecodeArgs &a, int head_dim, bool f16, int kv_format,
-                               int grid, hipStream_t s)
+                               int waves, int grid, hipStream_t s)
 {
-    return f16 ? launch_decode_f<true>(a, head_dim, kv_format, grid, s)
-               : launch_decode_f<false>(a, head_dim, kv_format, grid, s);
+    return f16 ? launch_decode_f<true>(a, head_dim, kv_format, waves, grid, s)
+               : launch_decode_f<false>(a, head_dim, kv_format, waves, grid, s);
 }
 
 template <bool F16>
@@ -540,43 +627,53 @@ hipError_t launch_decode_merge(const DecodeArgs &a, int head_dim, bool f16, int 
                : launch_merge_t<false>(a, head_dim, grid, s);
 }
 
-template <bool F16, int KVF>
-static int decode_blocks_per_cu_t(int head_dim)
+template <bool F16, int KVF, int NW>
+static int decode_blocks_per_cu_w(int head_dim)
 {
     int n = 0;
     hipError_t e = hipErrorInvalidValue;
     switch (head_dim) {
     case 64:
         e = hipOccupancyMaxActiveBlocksPerMultiprocessor(
-            &n, decode_kernel<64, decode_stages<64, KVF>(), F16, KVF>, kDecodeThreads, 0);
+            &n, decode_kernel<64, decode_stages<64, KVF>(), F16, KVF, NW>, kDecodeThreads * NW, 0);
         break;
     case 128:
         e = hipOccupancyMaxActiveBlocksPerMultiprocessor(
-            &n, decode_kernel<128, decode_stages<128, KVF>(), F16, KVF>, kDecodeThreads, 0);
+            &n, decode_kernel<128, decode_stages<128, KVF>(), F16, KVF, NW>, kDecodeThreads * NW, 0);
         break;
     case 256:
         e = hipOccupancyMaxActiveBlocksPerMultiprocessor(
-            &n, decode_kernel<256, decode_stages<256, KVF>(), F16, KVF>, kDecodeThreads, 0);
+            &n, decode_kernel<256, decode_stages<256, KVF>(), F16, KVF, NW>, kDecodeThreads * NW, 0);
         break;
     }
     return e == hipSuccess ? n : 0;
 }
 
-template <bool F16>
-static int decode_blocks_per_cu_f(int head_dim, int kv_format)
+template <bool F16, int KVF>
+static int decode_blocks_per_cu_t(int head_dim, int waves)
 {
-    switch (kv_format) {
-    case 0: return decode_blocks_per_cu_t<F16, 0>(head_dim);
-    case PKVS_KV_FP8_E4M3: return decode_blocks_per_cu_t<F16, 1>(head_dim);
-    case PKVS_KV_FP8_E5M2: return decode_blocks_per_cu_t<F16, 2>(head_dim);
+    switch (waves) {
+    case 1: return decode_blocks_per_cu_w<F16, KVF, 1>(head_dim);
+    case 4: return decode_blocks_per_cu_w<F16, KVF, 4>(head_dim);
     default: return 0;
     }
 }
 
-int decode_blocks_per_cu(int head_dim, bool f16, int kv_format)
+template <bool F16>
+static int decode_blocks_per_cu_f(int head_dim, int kv_format, int waves)
 {
-    return f16 ? decode_blocks_per_cu_f<true>(head_dim, kv_format)
-               : decode_blocks_per_cu_f<false>(head_dim, kv_format);
+    switch (kv_format) {
+    case 0: return decode_blocks_per_cu_t<F16, 0>(head_dim, waves);
+    case PKVS_KV_FP8_E4M3: return decode_blocks_per_cu_t<F16, 1>(head_dim, waves);
+    case PKVS_KV_FP8_E5M2: return decode_blocks_per_cu_t<F16, 2>(head_dim, waves);
+    default: return 0;
+    }
+}
+
+int decode_blocks_per_cu(int head_dim, bool f16, int kv_format, int waves)
+{
+    return f16 ? decode_blocks_per_cu_f<true>(head_dim, kv_format, waves)
+               : decode_blocks_per_cu_f<false>(head_dim, kv_format, waves);
 }
 
 }  // namespace pkvs

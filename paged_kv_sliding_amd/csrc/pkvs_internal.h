@@ -86,7 +86,7 @@ constexpr int kPrefillKvTile = 32;     // keys per step
 constexpr int kGenericQTile = 16;      // fp32 path: query tokens per item
 constexpr int kGenericThreads = 256;
 constexpr int kDecodeBlock = 32;       // keys per decode step
-constexpr int kDecodeThreads = 64;     // one wave per workgroup
+constexpr int kDecodeThreads = 64;     // threads per wave of a decode work item
 constexpr int kMergeThreads = 64;
 constexpr int kAppendThreads = 256;    // cache writes: threads per workgroup (max)
 constexpr int kIndptrThreads = 1024;   // page-table build: the running-sum workgroup
@@ -133,8 +133,9 @@ struct DecodeArgs {
 hipError_t launch_prefill_16bit(const PrefillArgs &a, int head_dim, int variant, bool f16,
                                 int kv_format, int grid, hipStream_t s);
 hipError_t launch_attention_fp32(const PrefillArgs &a, int head_dim, int grid, hipStream_t s);
+// waves: 1 or 4 waves share each decode work item (pkvs_desc.decode_waves)
 hipError_t launch_decode_16bit(const DecodeArgs &a, int head_dim, bool f16, int kv_format,
-                               int grid, hipStream_t s);
+                               int waves, int grid, hipStream_t s);
 hipError_t launch_decode_merge(const DecodeArgs &a, int head_dim, bool f16, int grid,
                                hipStream_t s);
 hipError_t launch_merge_state(const void *va, const float *sa, const void *vb, const float *sb,
@@ -156,6 +157,6 @@ hipError_t launch_build_kv_indices(const int32_t *map, int64_t map_rows, int64_t
 
 // Resident workgroups per CU of each kernel (occupancy query; 0 if unknown).
 int prefill_blocks_per_cu(int head_dim, int variant, bool f16, int kv_format);
-int decode_blocks_per_cu(int head_dim, bool f16, int kv_format);
+int decode_blocks_per_cu(int head_dim, bool f16, int kv_format, int waves);
 
 }  // namespace pkvs

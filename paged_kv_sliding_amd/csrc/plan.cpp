@@ -149,6 +149,9 @@ static int validate_desc(const pkvs_desc *d)
                                       d->fixed_split_size % kDecodeBlock))
         return fail(PKVS_ERR_INVALID_ARG, "fixed_split_size %d must be -1 or a positive "
                     "multiple of %d", d->fixed_split_size, kDecodeBlock);
+    if (d->decode_waves != 0 && d->decode_waves != 1 && d->decode_waves != 4)
+        return fail(PKVS_ERR_INVALID_ARG, "decode_waves %d must be 0 (planner's choice), 1 or 4",
+                    d->decode_waves);
     if (d->prefill_variant < 0 || d->prefill_variant > 5)
         return fail(PKVS_ERR_INVALID_ARG, "prefill_variant %d must be 0..5", d->prefill_variant);
     if (d->prefill_variant > 1 && d->head_dim > 128)
@@ -325,9 +328,10 @@ static int64_t choose_split(const Plan *p, const std::vector<Req> &reqs)
     c = std::min(no_split, std::max<int64_t>(c, kMinAutoSplit));
     const double key_bytes =
         2.0 * d.head_dim * (d.kv_format != PKVS_KV_SAME ? 1 : 2);  // K and V of one key, one head
-    const double t_whole = double(longest) * key_bytes / kWaveBytesPerUs;
+    const double item_rate = kWaveBytesPerUs * p->decode_waves;  // one item's streaming rate
+    const double t_whole = double(longest) * key_bytes / item_rate;
     const double t_split = std::max(double(total) * d.num_kv_heads * key_bytes / kChipBytesPerUs,
-                                    double(c) * key_bytes / kWaveBytesPerUs) + kMergeUs;
+                                    double(c) * key_bytes / item_rate) + kMergeUs;
     return t_whole <= t_split ? no_split : c;
 }
 
@@ -492,13 +496,36 @@ static int create_plan(const pkvs_desc *desc, bool ragged, Plan **out)
     } else {
         p->query_tile = 1;
         p->item_words = fp32 ? kPrefillItemWords : kDecodeItemWords;
-        p->block_threads = fp32 ? kGenericThreads : kDecodeThreads;
-        int per_cu = p->have_gpu && !fp32 ? decode_blocks_per_cu(desc->head_dim, f16, kvf) : 0;
-        p->grid_blocks = p->num_cus * std::max(per_cu, fp32 ? 2 : 8);
-        // one chunk per resident wave (one wave per SIMD when the occupancy
-        // cannot be queried): a second, partial round of chunks or chunks of
-        // a few blocks each measured slower
-        p->auto_target_items = int64_t(p->num_cus) * (per_cu > 0 ? per_cu : 4);
+        // Waves per work item: four when the batch has at most one (request,
+        // kv head) pair per kFourWavePairShare resident one-wave items (one
+        // wave per SIMD when the occupancy cannot be queried) and a request
+        // can present more than kFourWaveKeys keys after the window trim.
+        // One wave per item would then cut each pair into many short chunks
+        // whose merge dominates; four waves per item need a quarter of the
+        // chunks and combine within the item in LDS.  For larger batches or
+        // shorter requests one wave per item measured as fast or faster.
+        const int per_cu1 =
+            p->have_gpu && !fp32 ? decode_blocks_per_cu(desc->head_dim, f16, kvf, 1) : 0;
+        int nw = desc->decode_waves;
+        if (nw == 0) {
+            int64_t keys = desc->kv_capacity;
+            if (desc->window_left >= 0) keys = std::min<int64_t>(keys, int64_t(desc->window_left) + 1);
+            nw = int64_t(desc->batch_capacity) * desc->num_kv_heads * kFourWavePairShare <=
+                             int64_t(p->num_cus) * (per_cu1 > 0 ? per_cu1 : 4) &&
+                         keys > kFourWaveKeys
+                     ? 4
+                     : 1;
+        }
+        if (fp32) nw = 1;
+        p->decode_waves = nw;
+        p->block_threads = fp32 ? kGenericThreads : kDecodeThreads * nw;
+        const int per_cu =
+            p->have_gpu && !fp32 ? decode_blocks_per_cu(desc->head_dim, f16, kvf, nw) : 0;
+        p->grid_blocks = p->num_cus * (per_cu > 0 ? (nw == 1 ? std::max(per_cu, 8) : per_cu)
+                                                  : (fp32 ? 2 : 8 / nw));
+        // one chunk per resident work item (workgroup): a second, partial
+        // round of chunks or chunks of a few blocks each measured slower
+        p->auto_target_items = int64_t(p->num_cus) * (per_cu > 0 ? per_cu : std::max(1, 4 / nw));
     }
     (void)hipGetLastError();
     size_plan(p);
@@ -724,6 +751,7 @@ int pkvs_plan_get_info(const pkvs_plan *p, pkvs_plan_info *info)
     info->query_tile = p->query_tile;
     info->prefill_variant = p->desc.kind != PKVS_DECODE ? p->run_variant : 0;
     info->num_cus = p->num_cus;
+    info->decode_waves = p->desc.kind == PKVS_DECODE ? p->decode_waves : 0;
     return PKVS_OK;
 }
 

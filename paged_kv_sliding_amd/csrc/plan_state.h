@@ -20,6 +20,11 @@ constexpr int64_t kMinAutoSplit = 256; // smallest key chunk the planner picks b
 constexpr double kWaveBytesPerUs = 10.0e3;
 constexpr double kChipBytesPerUs = 5.5e6;
 constexpr double kMergeUs = 10.0;
+// decode, pkvs_desc.decode_waves = 0: four waves per work item for batches of
+// at most one (request, kv head) pair per kFourWavePairShare resident one-wave
+// items whose requests can exceed kFourWaveKeys keys after the window trim
+constexpr int64_t kFourWaveKeys = 2048;
+constexpr int64_t kFourWavePairShare = 32;
 
 int fail(int code, const char *fmt, ...);
 void clear_error();
@@ -35,6 +40,7 @@ struct pkvs_plan {
     int prefill_variant = 1;  // bf16 prefill kernel variant (PrefillVariant)
     int run_variant = 1;      // the variant the last plan() launches
     int64_t auto_target_items = 0;
+    int decode_waves = 1;     // waves per decode work item (1 or 4)
     int64_t items_cap = 0, slots_cap = 0, merges_cap = 0;
     size_t int_ws_need = 0, float_ws_need = 0;
 

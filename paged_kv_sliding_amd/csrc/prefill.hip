@@ -1108,6 +1108,10 @@ __global__ __launch_bounds__(512) void prefill_big_kernel(PrefillArgs a)
     int32_t *const ctr = a.ws;
     const int xcd = blockIdx.x % kXcds;
     const int xcd_groups = (int(gridDim.x) - xcd + kXcds - 1) / kXcds;
+    // Workgroups past the item count have nothing to claim: they leave without
+    // touching the counters, and only the others count themselves finished.
+    if (int(blockIdx.x) >= n_items) return;
+    const int participants = min(int(gridDim.x), n_items);
     for (int it = blockIdx.x; it < n_items;) {
         int claimed = 0;
         if (tid == 0) claimed = atomicAdd(ctr + kHdrNextItem + xcd, 1);
@@ -1400,9 +1404,9 @@ __global__ __launch_bounds__(512) void prefill_big_kernel(PrefillArgs a)
         __syncthreads();
         it = sh.next_item;
     }
-    // the last workgroup of the launch puts the counters back to 0 (every
-    // workgroup has claimed its last item before it counts itself finished)
-    if (tid == 0 && atomicAdd(ctr + kHdrDoneGroups, 1) == int(gridDim.x) - 1) {
+    // the last participating workgroup puts the counters back to 0 (each has
+    // claimed its last item before it counts itself finished)
+    if (tid == 0 && atomicAdd(ctr + kHdrDoneGroups, 1) == participants - 1) {
         for (int x = 0; x < kXcds; ++x) ctr[kHdrNextItem + x] = 0;
         ctr[kHdrDoneGroups] = 0;
     }

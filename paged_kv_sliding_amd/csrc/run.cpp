@@ -243,7 +243,8 @@ int pkvs_decode_run(const pkvs_plan *p, const void *q, const void *k_cache, cons
     a.page_size = p->desc.page_size;
     a.log2_page = log2_exact(p->desc.page_size);
     const bool f16 = p->desc.dtype == PKVS_FP16;
-    e = launch_decode_16bit(a, p->desc.head_dim, f16, p->desc.kv_format, p->grid_blocks, stream);
+    e = launch_decode_16bit(a, p->desc.head_dim, f16, p->desc.kv_format, p->decode_waves,
+                            p->grid_blocks, stream);
     if (e != hipSuccess) return fail(PKVS_ERR_HIP, "decode launch: %s", hipGetErrorString(e));
     if (p->merges_cap > 0) {
         // launched whenever the plan can have merges (the kernel reads their

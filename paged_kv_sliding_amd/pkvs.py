@@ -63,7 +63,7 @@ class pkvs_desc(ctypes.Structure):
         ("disable_split_kv", ctypes.c_int32), ("batch_capacity", ctypes.c_int32),
         ("prefill_variant", ctypes.c_int32), ("qo_capacity", ctypes.c_int64),
         ("kv_capacity", ctypes.c_int64), ("logits_soft_cap", ctypes.c_float),
-        ("kv_format", ctypes.c_int32),
+        ("kv_format", ctypes.c_int32), ("decode_waves", ctypes.c_int32),
     ]
 
 
@@ -74,7 +74,7 @@ class pkvs_plan_info(ctypes.Structure):
         ("grid_blocks", ctypes.c_int32), ("block_threads", ctypes.c_int32),
         ("split_size", ctypes.c_int32), ("item_words", ctypes.c_int32),
         ("query_tile", ctypes.c_int32), ("num_cus", ctypes.c_int32),
-        ("prefill_variant", ctypes.c_int32),
+        ("prefill_variant", ctypes.c_int32), ("decode_waves", ctypes.c_int32),
     ]
 
 
@@ -165,13 +165,13 @@ def make_desc(kind: int, *, num_qo_heads: int, num_kv_heads: int, head_dim: int,
               fixed_split_size: int = -1, disable_split_kv: bool = False,
               batch_capacity: int, qo_capacity: int = 0, kv_capacity: int,
               prefill_variant: int = 0, logits_soft_cap: float = 0.0,
-              kv_dtype: Optional[torch.dtype] = None) -> pkvs_desc:
+              kv_dtype: Optional[torch.dtype] = None, decode_waves: int = 0) -> pkvs_desc:
     """``kv_dtype``: None (caches in ``dtype``) or torch.float8_e4m3fn /
-    torch.float8_e5m2."""
+    torch.float8_e5m2.  ``decode_waves``: 0 (planner's choice), 1 or 4."""
     return pkvs_desc(kind, num_qo_heads, num_kv_heads, head_dim, page_size, _DTYPES[dtype],
                      int(bool(causal)), window_left, fixed_split_size, int(bool(disable_split_kv)),
                      batch_capacity, prefill_variant, qo_capacity, kv_capacity,
-                     float(logits_soft_cap), _KV_FORMATS[kv_dtype])
+                     float(logits_soft_cap), _KV_FORMATS[kv_dtype], decode_waves)
 
 
 def pkvs_plan_create(desc: pkvs_desc) -> ctypes.c_void_p:

@@ -25,7 +25,8 @@ def kv_dtype_of(case: Case):
 
 
 def make_attention(case: Case, window_left=None, fixed_split_size=None, disable_split_kv=False,
-                   batch_capacity=None, kv_capacity=None, qo_capacity=None, prefill_variant=0):
+                   batch_capacity=None, kv_capacity=None, qo_capacity=None, prefill_variant=0,
+                   decode_waves=0):
     W = case.window_left if window_left is None else window_left
     kind = P.PKVS_DECODE if case.is_decode else P.PKVS_PREFILL
     split = case.fixed_split_size if fixed_split_size is None else fixed_split_size
@@ -37,7 +38,7 @@ def make_attention(case: Case, window_left=None, fixed_split_size=None, disable_
         qo_capacity=qo_capacity or max(int(case.qo_indptr[-1]), 1),
         kv_capacity=kv_capacity or max(max(case.kv_lens, default=1), 1),
         prefill_variant=prefill_variant, logits_soft_cap=case.logits_soft_cap,
-        kv_dtype=kv_dtype_of(case))
+        kv_dtype=kv_dtype_of(case), decode_waves=decode_waves)
 
 
 def gpu_run(case: Case, window_left=None, att=None, return_lse=True, **kw):

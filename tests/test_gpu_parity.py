@@ -240,6 +240,56 @@ def test_decode_split_invariance(split, disable):
     compare(o, lse, ro, rl, tag=f"split={split} disable={disable}")
 
 
+@pytest.mark.parametrize("nw", [1, 4])
+@pytest.mark.parametrize("W,split,P_", [(-1, -1, 16), (-1, 64, 4), (100, -1, 1), (0, -1, 16),
+                                        (2047, 96, 8), (-1, 2048, 16), (4095, -1, 2)])
+def test_decode_waves_per_item(nw, W, split, P_):
+    """One or four waves per work item (the four split the item's key blocks
+    into contiguous runs and combine in LDS): ragged lengths around block and
+    run boundaries, windows, chunked and whole requests, a keyless request."""
+    kv = [1, 2, 31, 33, 64, 97, 128, 129, 200, 1000, 3000, 5000, 0]
+    case = small([1] * len(kv), kv, H_q=32, H_kv=8, D=128, P_=P_, W=W, seed=7 * nw + W + P_,
+                 decode=True, split=split)
+    att = make_attention(case, decode_waves=nw)
+    o, lse = gpu_run(case, att=att)
+    info = att.info()
+    assert info.decode_waves == nw and info.block_threads == 64 * nw
+    ro, rl = oracle_for(case)
+    compare(o, lse, ro, rl, tag=f"decode nw={nw} W={W} split={split} P={P_}")
+    assert (o[-1] == 0).all() and torch.isneginf(lse[-1]).all()
+
+
+@pytest.mark.parametrize("D,G,dtype,kv_dtype,cap", [
+    (64, 4, torch.bfloat16, None, 0.0), (128, 16, torch.bfloat16, None, 0.0),
+    (256, 2, torch.bfloat16, None, 0.0), (128, 8, torch.float16, None, 0.0),
+    (128, 4, torch.bfloat16, torch.float8_e4m3fn, 0.0), (128, 4, torch.float16, torch.float8_e5m2, 0.0),
+    (128, 4, torch.bfloat16, None, 30.0)])
+def test_decode_four_waves_shapes_and_types(D, G, dtype, kv_dtype, cap):
+    kv = [7, 300, 1500, 64, 4100, 0]
+    case = small([1] * len(kv), kv, H_q=2 * G, H_kv=2, D=D, P_=16, W=-1, seed=D + G, decode=True,
+                 dtype=dtype, kv_dtype=kv_dtype, cap=cap)
+    att = make_attention(case, decode_waves=4)
+    o, lse = gpu_run(case, att=att)
+    assert att.info().decode_waves == 4
+    ro, rl = oracle_for(case)
+    compare(o, lse, ro, rl, tag=f"decode nw=4 D={D} G={G} {dtype} kv={kv_dtype} cap={cap}")
+
+
+def test_decode_waves_automatic_choice():
+    """A batch of a few long requests takes four waves per item; short requests
+    (or a window of at most 2048 keys) and larger batches one."""
+    long_kv = [5000, 3000, 100, 4500]
+    case = small([1] * 4, long_kv, H_q=32, H_kv=8, D=128, P_=16, W=-1, seed=5, decode=True)
+    att = make_attention(case)
+    o, lse = gpu_run(case, att=att)
+    assert att.info().decode_waves == 4
+    ro, rl = oracle_for(case)
+    compare(o, lse, ro, rl, tag="decode auto nw")
+    assert make_attention(case, window_left=2047).info().decode_waves == 1
+    assert make_attention(case, kv_capacity=2048).info().decode_waves == 1
+    assert make_attention(case, batch_capacity=4096).info().decode_waves == 1
+
+
 # ----------------------------------------------------------------- exact masking
 
 
@@ -320,8 +370,8 @@ def _sub_layout(case, picks):
             torch.tensor(kv_ind, **i32), torch.tensor(last, **i32))
 
 
-@pytest.mark.parametrize("decode", [False, True])
-def test_graph_replay_follows_replans(decode):
+@pytest.mark.parametrize("decode,nw", [(False, 0), (True, 1), (True, 4)])
+def test_graph_replay_follows_replans(decode, nw):
     """run() captured once in a HIP graph stays valid for every later plan() of
     the same capacities (AMD-Ecosystem/flashinfer PR 234, "Why each fix" 2: the
     grid and the launch set come from the capacities, the work from the
@@ -333,7 +383,9 @@ def test_graph_replay_follows_replans(decode):
     else:
         qo, kv = [40, 1, 130, 7, 64], [300, 1, 130, 500, 64]
         case = small(qo, kv, H_q=8, H_kv=2, D=128, P_=16, W=100, seed=62)
-    att = make_attention(case)
+    att = make_attention(case, decode_waves=nw)
+    if decode:
+        assert att.info().decode_waves == nw
     B, n_q = case.batch_size, case.q.shape[0]
     q_buf = case.q.clone()
     idx_buf = case.kv_indices.clone()
@@ -390,7 +442,7 @@ def test_graph_replay_follows_replans(decode):
             assert torch.equal(l_buf[:n], want_l), (k, rep)
         if k == 0:
             ro, rl = oracle_for(case)
-            compare(want_o, want_l, ro, rl, tag=f"graph decode={decode}")
+            compare(want_o, want_l, ro, rl, tag=f"graph decode={decode} nw={nw}")
 
 
 def test_replan_in_place_then_capacity_error():

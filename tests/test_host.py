@@ -228,6 +228,32 @@ def test_grid_does_not_depend_on_the_batch():
     assert len(set(grids)) == 1
 
 
+def test_decode_waves_choice_and_validation():
+    """decode_waves: 1 or 4 as asked; 0 lets the planner take four waves per
+    item only for a batch of at most one (request, kv head) pair per 32
+    resident one-wave items (32 pairs on 256 CUs without an occupancy query)
+    whose requests can present more than 2048 keys after the window trim;
+    anything else is an error.  The plan reports the choice and sizes its
+    workgroups by it."""
+    base = dict(num_qo_heads=32, num_kv_heads=8, batch_capacity=4, kv_capacity=8192)
+    for nw in (1, 4):
+        h = P.pkvs_plan_create(desc(P.PKVS_DECODE, window_left=-1, decode_waves=nw, **base))
+        info = P.pkvs_plan_get_info(h)
+        assert info.decode_waves == nw and info.block_threads == 64 * nw
+        P.pkvs_plan_destroy(h)
+    auto = lambda **kw: P.pkvs_plan_get_info(
+        P.pkvs_plan_create(desc(P.PKVS_DECODE, **dict(dict(base, window_left=-1), **kw)))).decode_waves
+    assert auto() == 4
+    assert auto(window_left=2047) == 1 and auto(window_left=2048) == 4
+    assert auto(kv_capacity=2048) == 1
+    assert auto(batch_capacity=5) == 1 and auto(batch_capacity=4096) == 1
+    for bad in (2, 3, -1, 8):
+        assert err_code(lambda: P.pkvs_plan_create(desc(P.PKVS_DECODE, decode_waves=bad, **base))) \
+            == P.PKVS_ERR_INVALID_ARG
+    # prefill plans report no decode waves
+    assert P.pkvs_plan_get_info(P.pkvs_plan_create(desc())).decode_waves == 0
+
+
 def test_capacity_is_enforced_not_underlaunched():
     """A larger batch than the plan was made for is rejected at plan time
     (AMD-Ecosystem/flashinfer PR 234, "Why each fix" 2)."""
