@@ -314,9 +314,9 @@ constexpr int decode_stages() { return KVF == 0 ? (D >= 256 ? 2 : 3) : (D >= 256
 // being computed.
 // NW waves share a work item: wave w streams the w-th of NW contiguous runs of
 // the chunk's key blocks with its own running maximum, sum and O, and the
-// waves combine them through LDS (the LSE-weighted sum of merge_state), so a
-// small batch streams each (request, kv head) at NW waves' rate with no
-// partials in memory and no merge launch.
+// waves combine them through LDS (the LSE-weighted sum of merge_state).  A
+// batch of a few (request, kv head) pairs then needs 1/NW of the chunks, and
+// of the partials and merge work, that it needs with one wave per item.
 template <int D, int NW>
 struct DecodeMergeLds {
     static constexpr int NV = DecodeBuf<D, 0>::NV;
