@@ -22,9 +22,10 @@ enum HeaderField {
     // work counters of the kernels that hand out items at run time: the next
     // item past the first grid-stride round (the decode kernel: one counter;
     // the prefill kernel: one per XCD, kXcds words), and the workgroups that
-    // have finished; plan() uploads them as 0 and the last workgroup of a
-    // launch puts them back to 0, so every launch (and graph replay) starts
-    // from 0
+    // have finished; plan() uploads them as 0 and the last of a launch's
+    // participating workgroups (the first min(grid, items); the others leave
+    // without touching the counters) puts them back to 0, so every launch
+    // (and graph replay) starts from 0
     kHdrNextItem = 4,
     kHdrDoneGroups = 12,
 };
