@@ -33,7 +33,7 @@ FP8_E5M2 = 4
 def compile_source(src: str, out: str) -> str:
     """gcc -O2 a copy of the oracle source into a shared library at ``out``."""
     tmp = out + f".tmp{os.getpid()}"
-    subprocess.run(["gcc", "-O2", "-std=c99", "-Wall", "-Wextra", "-shared", "-fPIC",
+    subprocess.run(["gcc", "-O2", "-std=c99", "-Wall", "-Wextra", "-shared", "-fPIC", "-pthread",
                     "-o", tmp, src, "-lm"], check=True)
     os.replace(tmp, out)
     return out
@@ -58,7 +58,7 @@ class OracleLib:
         lib.oracle_paged_attention.restype = ctypes.c_int
         lib.oracle_paged_attention.argtypes = [
             i32, P, P, P, P, i32, i32, i32, i32, i32, i32, f64, f64, i32, P, i32, f64, f64, P, P,
-            P, i64, i64, i64, P, P,
+            P, i64, i64, i64, P, P, i32,
         ]
         lib.oracle_merge_state.restype = None
         lib.oracle_merge_state.argtypes = [i64, i32, i32, P, P, P, P, P, P]
@@ -84,6 +84,15 @@ def _load():
     if _lib is None:
         _lib = OracleLib(build())
     return _lib
+
+
+def default_threads() -> int:
+    """Threads the oracle uses unless told otherwise: ORACLE_THREADS, else the
+    host's cores, at most 16 (the CPU share of one GPU on a shared host)."""
+    env = os.environ.get("ORACLE_THREADS")
+    if env:
+        return max(1, int(env))
+    return max(1, min(16, os.cpu_count() or 1))
 
 
 def _ptr(a: np.ndarray):
@@ -121,13 +130,17 @@ def paged_attention(q, k_cache, v_cache, qo_indptr, kv_indptr, kv_indices, kv_la
                     causal: bool, window_left: int, sm_scale: float, soft_cap: float = 0.0,
                     k_scale: float = 1.0, v_scale: float = 1.0,
                     rows: Optional[Sequence[int]] = None, key_lo: int = 0,
-                    key_hi: int = np.iinfo(np.int64).max, impl: Optional[OracleLib] = None):
+                    key_hi: int = np.iinfo(np.int64).max, impl: Optional[OracleLib] = None,
+                    threads: Optional[int] = None):
     """Reference (O, LSE) in float64.
 
     ``q``/``k_cache``/``v_cache`` are torch tensors (bf16 or fp32, any device;
     they are copied to the host).  Returns ``o`` ``[nnz_qo, H_q, D]`` and ``lse``
     ``[nnz_qo, H_q]``; with ``rows`` (global query-token indices) the outputs
-    are compact: ``[len(rows), H_q, D]`` and ``[len(rows), H_q]``.
+    are compact: ``[len(rows), H_q, D]`` and ``[len(rows), H_q]``.  Rows are
+    spread over ``threads`` POSIX threads (default ``default_threads()``); each
+    row is computed by one thread with unchanged arithmetic, so the result does
+    not depend on the thread count.
     """
     lib = (impl or _load()).lib
     qa, qd = _as_stored(q)
@@ -153,7 +166,8 @@ def paged_attention(q, k_cache, v_cache, qo_indptr, kv_indptr, kv_indices, kv_la
         batch, _ptr(qo), _ptr(kvp), _ptr(kvi), _ptr(last), page_size, num_qo_heads,
         num_kv_heads, head_dim, int(bool(causal)), window_left, float(sm_scale),
         float(soft_cap), qd, _ptr(qa), kd, float(k_scale), float(v_scale),
-        _ptr(ka), _ptr(va), rp, nr, int(key_lo), int(key_hi), _ptr(o), _ptr(lse))
+        _ptr(ka), _ptr(va), rp, nr, int(key_lo), int(key_hi), _ptr(o), _ptr(lse),
+        int(default_threads() if threads is None else threads))
     if rc != 0:
         raise ValueError(f"oracle_paged_attention: malformed layout (rc={rc})")
     return o, lse

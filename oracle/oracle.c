@@ -22,7 +22,9 @@
  *             backend gaps -- sliding window, CUDA graph, return_lse",
  *             sections "Why each fix" 1 (sliding window) and 3 (return_lse).
  */
+#define _POSIX_C_SOURCE 200809L
 #include <math.h>
+#include <pthread.h>
 #include <stdint.h>
 #include <stdlib.h>
 #include <string.h>
@@ -130,6 +132,135 @@ static int key_visible(int64_t j, int64_t p, int32_t causal, int32_t window_left
     return 1;
 }
 
+/* Arguments of one oracle_paged_attention call, shared by its threads. */
+struct attention_call {
+    int32_t batch;
+    const int32_t *qo_indptr, *kv_indptr, *kv_indices, *kv_last_page_len;
+    int32_t page_size, num_qo_heads, num_kv_heads, head_dim, causal, window_left;
+    double sm_scale, soft_cap;
+    int32_t in_dtype, kv_dtype;
+    const void *q;
+    double k_scale, v_scale;
+    const void *k_cache, *v_cache;
+    const int64_t *rows;
+    int64_t count, nnz_qo, max_kv, key_lo, key_hi;
+    double *o, *lse;
+    /* the next output row to take (threads claim rows one at a time) */
+    pthread_mutex_t lock;
+    int64_t next_row;
+    int failed;
+};
+
+/*
+ * One output row r: every query head of query token t = rows[r] (or t = r).
+ * s holds max_kv logits and acc head_dim sums (scratch of the calling thread).
+ */
+static void attention_row(const struct attention_call *c, int64_t r, double *s, double *acc)
+{
+    const int32_t batch = c->batch, page_size = c->page_size, num_qo_heads = c->num_qo_heads;
+    const int32_t num_kv_heads = c->num_kv_heads, head_dim = c->head_dim, causal = c->causal;
+    const int32_t window_left = c->window_left, in_dtype = c->in_dtype, kv_dtype = c->kv_dtype;
+    const int32_t *qo_indptr = c->qo_indptr, *kv_indptr = c->kv_indptr;
+    const int32_t *kv_indices = c->kv_indices, *kv_last_page_len = c->kv_last_page_len;
+    const double sm_scale = c->sm_scale, soft_cap = c->soft_cap;
+    const double k_scale = c->k_scale, v_scale = c->v_scale;
+    const void *q = c->q, *k_cache = c->k_cache, *v_cache = c->v_cache;
+    const int64_t *rows = c->rows;
+    const int64_t key_lo = c->key_lo, key_hi = c->key_hi;
+    double *o = c->o, *lse = c->lse;
+    const int32_t group = num_qo_heads / num_kv_heads;
+
+    const int64_t t = rows ? rows[r] : r;
+    if (t < 0 || t >= c->nnz_qo)
+        return;
+    int32_t b = 0;
+    while (b + 1 < batch && qo_indptr[b + 1] <= t)
+        ++b;
+    const int64_t kv_len = request_kv_len(kv_indptr, kv_last_page_len, page_size, b);
+    const int64_t qo_len = (int64_t)qo_indptr[b + 1] - qo_indptr[b];
+    const int64_t p = (kv_len - qo_len) + (t - qo_indptr[b]);
+
+    const int64_t out_row = rows ? r : t;
+    for (int32_t h = 0; h < num_qo_heads; ++h) {
+        const int32_t hk = h / group;
+        const int64_t qoff = (t * num_qo_heads + h) * (int64_t)head_dim;
+        const int64_t ooff = (out_row * num_qo_heads + h) * (int64_t)head_dim;
+
+        /* logits of the visible keys, and their maximum */
+        double m = -INFINITY;
+        for (int64_t j = 0; j < kv_len; ++j) {
+            if (!key_visible(j, p, causal, window_left, key_lo, key_hi))
+                continue;
+            const int64_t koff = key_offset(kv_indptr, kv_indices, page_size, num_kv_heads,
+                                            head_dim, b, j, hk);
+            double dot = 0.0;
+            for (int32_t d = 0; d < head_dim; ++d)
+                dot += load_elem(q, in_dtype, qoff + d) *
+                       (k_scale * load_elem(k_cache, kv_dtype, koff + d));
+            s[j] = sm_scale * dot;
+            if (soft_cap > 0.0)
+                s[j] = soft_cap * tanh(s[j] / soft_cap);
+            if (s[j] > m)
+                m = s[j];
+        }
+
+        for (int32_t d = 0; d < head_dim; ++d)
+            acc[d] = 0.0;
+        double l = 0.0;
+        if (m != -INFINITY) {
+            for (int64_t j = 0; j < kv_len; ++j) {
+                if (!key_visible(j, p, causal, window_left, key_lo, key_hi))
+                    continue;
+                const double w = exp(s[j] - m);
+                l += w;
+                const int64_t voff = key_offset(kv_indptr, kv_indices, page_size,
+                                                num_kv_heads, head_dim, b, j, hk);
+                for (int32_t d = 0; d < head_dim; ++d)
+                    acc[d] += w * (v_scale * load_elem(v_cache, kv_dtype, voff + d));
+            }
+        }
+        double *orow = o + ooff;
+        if (l > 0.0) {
+            for (int32_t d = 0; d < head_dim; ++d)
+                orow[d] = acc[d] / l;
+            lse[out_row * num_qo_heads + h] = m + log(l);
+        } else {
+            for (int32_t d = 0; d < head_dim; ++d)
+                orow[d] = 0.0;
+            lse[out_row * num_qo_heads + h] = -INFINITY;
+        }
+    }
+}
+
+/* A worker: claims output rows one at a time until none is left.  Every row is
+ * computed by exactly one thread, with the same arithmetic as a single thread
+ * would use; only the order in which rows are finished changes. */
+static void *attention_worker(void *arg)
+{
+    struct attention_call *c = (struct attention_call *)arg;
+    double *s = (double *)malloc(sizeof(double) * (size_t)(c->max_kv > 0 ? c->max_kv : 1));
+    double *acc = (double *)malloc(sizeof(double) * (size_t)c->head_dim);
+    if (!s || !acc) {
+        pthread_mutex_lock(&c->lock);
+        c->failed = 1;
+        pthread_mutex_unlock(&c->lock);
+        free(s);
+        free(acc);
+        return NULL;
+    }
+    for (;;) {
+        pthread_mutex_lock(&c->lock);
+        const int64_t r = c->failed ? c->count : c->next_row++;
+        pthread_mutex_unlock(&c->lock);
+        if (r >= c->count)
+            break;
+        attention_row(c, r, s, acc);
+    }
+    free(s);
+    free(acc);
+    return NULL;
+}
+
 /*
  * Attention of every query row (or of the listed rows) over its request's
  * paged keys.
@@ -166,6 +297,9 @@ static int key_visible(int64_t j, int64_t p, int32_t causal, int32_t window_left
  *  indices to compute; then o and lse are compact, [n_rows, H_q, D] and
  *  [n_rows, H_q], row r holding query token rows[r].
  *
+ *  n_threads > 1 computes the rows on that many POSIX threads (each row by one
+ *  thread, unchanged arithmetic: the results are bit-identical).
+ *
  *  Returns 0 on success, -1 on a malformed layout, -2 when out of memory.
  */
 int oracle_paged_attention(int32_t batch, const int32_t *qo_indptr, const int32_t *kv_indptr,
@@ -176,96 +310,66 @@ int oracle_paged_attention(int32_t batch, const int32_t *qo_indptr, const int32_
                            int32_t kv_dtype, double k_scale, double v_scale,
                            const void *k_cache, const void *v_cache, const int64_t *rows,
                            int64_t n_rows, int64_t key_lo, int64_t key_hi, double *o,
-                           double *lse)
+                           double *lse, int32_t n_threads)
 {
     if (batch < 0 || page_size <= 0 || num_kv_heads <= 0 || num_qo_heads % num_kv_heads)
         return -1;
-    const int32_t group = num_qo_heads / num_kv_heads;
-    const int64_t nnz_qo = qo_indptr[batch];
-    const int64_t count = rows ? n_rows : nnz_qo;
+    struct attention_call c;
+    memset(&c, 0, sizeof c);
+    c.batch = batch;
+    c.qo_indptr = qo_indptr;
+    c.kv_indptr = kv_indptr;
+    c.kv_indices = kv_indices;
+    c.kv_last_page_len = kv_last_page_len;
+    c.page_size = page_size;
+    c.num_qo_heads = num_qo_heads;
+    c.num_kv_heads = num_kv_heads;
+    c.head_dim = head_dim;
+    c.causal = causal;
+    c.window_left = window_left;
+    c.sm_scale = sm_scale;
+    c.soft_cap = soft_cap;
+    c.in_dtype = in_dtype;
+    c.kv_dtype = kv_dtype;
+    c.q = q;
+    c.k_scale = k_scale;
+    c.v_scale = v_scale;
+    c.k_cache = k_cache;
+    c.v_cache = v_cache;
+    c.rows = rows;
+    c.nnz_qo = qo_indptr[batch];
+    c.count = rows ? n_rows : c.nnz_qo;
+    c.key_lo = key_lo;
+    c.key_hi = key_hi;
+    c.o = o;
+    c.lse = lse;
 
-    int64_t max_kv = 0;
     for (int32_t b = 0; b < batch; ++b) {
         int64_t n = request_kv_len(kv_indptr, kv_last_page_len, page_size, b);
         int64_t nq = (int64_t)qo_indptr[b + 1] - qo_indptr[b];
         if (nq < 0 || (nq > n && n > 0))
             return -1;
-        if (n > max_kv)
-            max_kv = n;
+        if (n > c.max_kv)
+            c.max_kv = n;
     }
-    double *s = (double *)malloc(sizeof(double) * (size_t)(max_kv > 0 ? max_kv : 1));
-    double *acc = (double *)malloc(sizeof(double) * (size_t)head_dim);
-    if (!s || !acc) {
-        free(s);
-        free(acc);
+
+    if (pthread_mutex_init(&c.lock, NULL) != 0)
         return -2;
-    }
-
-    for (int64_t r = 0; r < count; ++r) {
-        const int64_t t = rows ? rows[r] : r;
-        if (t < 0 || t >= nnz_qo)
-            continue;
-        int32_t b = 0;
-        while (b + 1 < batch && qo_indptr[b + 1] <= t)
-            ++b;
-        const int64_t kv_len = request_kv_len(kv_indptr, kv_last_page_len, page_size, b);
-        const int64_t qo_len = (int64_t)qo_indptr[b + 1] - qo_indptr[b];
-        const int64_t p = (kv_len - qo_len) + (t - qo_indptr[b]);
-
-        const int64_t out_row = rows ? r : t;
-        for (int32_t h = 0; h < num_qo_heads; ++h) {
-            const int32_t hk = h / group;
-            const int64_t qoff = (t * num_qo_heads + h) * (int64_t)head_dim;
-            const int64_t ooff = (out_row * num_qo_heads + h) * (int64_t)head_dim;
-
-            /* logits of the visible keys, and their maximum */
-            double m = -INFINITY;
-            for (int64_t j = 0; j < kv_len; ++j) {
-                if (!key_visible(j, p, causal, window_left, key_lo, key_hi))
-                    continue;
-                const int64_t koff = key_offset(kv_indptr, kv_indices, page_size, num_kv_heads,
-                                                head_dim, b, j, hk);
-                double dot = 0.0;
-                for (int32_t d = 0; d < head_dim; ++d)
-                    dot += load_elem(q, in_dtype, qoff + d) *
-                           (k_scale * load_elem(k_cache, kv_dtype, koff + d));
-                s[j] = sm_scale * dot;
-                if (soft_cap > 0.0)
-                    s[j] = soft_cap * tanh(s[j] / soft_cap);
-                if (s[j] > m)
-                    m = s[j];
-            }
-
-            for (int32_t d = 0; d < head_dim; ++d)
-                acc[d] = 0.0;
-            double l = 0.0;
-            if (m != -INFINITY) {
-                for (int64_t j = 0; j < kv_len; ++j) {
-                    if (!key_visible(j, p, causal, window_left, key_lo, key_hi))
-                        continue;
-                    const double w = exp(s[j] - m);
-                    l += w;
-                    const int64_t voff = key_offset(kv_indptr, kv_indices, page_size,
-                                                    num_kv_heads, head_dim, b, j, hk);
-                    for (int32_t d = 0; d < head_dim; ++d)
-                        acc[d] += w * (v_scale * load_elem(v_cache, kv_dtype, voff + d));
-                }
-            }
-            double *orow = o + ooff;
-            if (l > 0.0) {
-                for (int32_t d = 0; d < head_dim; ++d)
-                    orow[d] = acc[d] / l;
-                lse[out_row * num_qo_heads + h] = m + log(l);
-            } else {
-                for (int32_t d = 0; d < head_dim; ++d)
-                    orow[d] = 0.0;
-                lse[out_row * num_qo_heads + h] = -INFINITY;
-            }
-        }
-    }
-    free(s);
-    free(acc);
-    return 0;
+    int32_t nt = n_threads < 1 ? 1 : n_threads;
+    if ((int64_t)nt > c.count)
+        nt = c.count > 0 ? (int32_t)c.count : 1;
+    pthread_t *tid = (pthread_t *)malloc(sizeof(pthread_t) * (size_t)nt);
+    int32_t started = 0;
+    if (tid)
+        for (; started < nt - 1; ++started)
+            if (pthread_create(&tid[started], NULL, attention_worker, &c) != 0)
+                break;
+    attention_worker(&c); /* the calling thread works too */
+    for (int32_t i = 0; i < started; ++i)
+        pthread_join(tid[i], NULL);
+    free(tid);
+    pthread_mutex_destroy(&c.lock);
+    return c.failed ? -2 : 0;
 }
 
 /*
