@@ -111,9 +111,14 @@ typedef enum pkvs_kind { PKVS_PREFILL = 0, PKVS_DECODE = 1, PKVS_CASCADE = 2 } p
  *                   <= 128), 4 = 8 waves x 32 rows with K/V rows loaded straight
  *                   into LDS, 5 = as 4 with 64-key steps and 16-byte loads
  *                   into a chunk-permuted LDS layout (4 and 5: head_dim 128,
- *                   16-bit K/V; a plan() whose items span more than 2048
- *                   pages of keys runs variant 2 instead); rows are (query
- *                   token, head) pairs
+ *                   16-bit K/V; they hold an item's page ids in a 2048-entry
+ *                   LDS table, so a plan whose capacities let one item span
+ *                   more pages -- (kv_capacity - 1) / page_size + 1, or with
+ *                   a window (window_left + query tile + 2 key tiles - 3) /
+ *                   page_size + 2 if smaller, above 2048 -- runs variant 2
+ *                   instead); rows are (query token,
+ *                   head) pairs.  The variant is fixed by pkvs_plan_create
+ *                   and never changes with the planned batch
  *  batch_capacity   largest batch a plan() call may describe
  *  qo_capacity      prefill, cascade: largest total number of query tokens
  *  kv_capacity      largest kv_len of one request (cascade: the most cached
@@ -178,19 +183,38 @@ typedef struct pkvs_plan_info {
 
 typedef struct pkvs_plan pkvs_plan;
 
-/* Create a plan object for `desc` on the current HIP device.  Fails with
- * INVALID_ARG / UNSUPPORTED for a descriptor outside the rules above.  Works
- * without a GPU (then only dry plans, with null workspaces, can be made). */
+/* Create a plan object for `desc` on the current HIP device ([FIB]
+ * _create_full_cg_prefill_wrappers: the wrappers are made once, for the
+ * largest batch they will see, and bound to a workspace sized for it; the
+ * launch grid, the kernel variant and the workspace sizes are fixed here from
+ * the capacities and the device).  Fails with INVALID_ARG / UNSUPPORTED for a
+ * descriptor outside the rules above.  Works without a GPU (then only dry
+ * plans, with null workspaces, can be made).  The plan is a host object owned
+ * by the library until pkvs_plan_destroy. */
 int pkvs_plan_create(pkvs_plan **out, const pkvs_desc *desc);
 
-/* Worst-case workspace sizes for the plan's capacities, in bytes.  Callers
- * allocate device buffers at least this large (float_ws may be 0 bytes).
+/* Worst-case workspace sizes for the plan's capacities, in bytes ([FIB]
+ * _full_cg_prefill_workspace_bytes: the split-KV float workspace is sized for
+ * the largest batch the wrapper will run, once).  Callers allocate device
+ * buffers at least this large (float_ws may be 0 bytes).
  * int_ws holds the work list that plan() copies in; the decode kernel and the
  * default prefill kernel also keep two work counters in its header, which
  * plan() uploads as 0 and every run() leaves at 0 when it completes, so the
  * same plan can be run (or a captured run replayed) any number of times, one
  * run at a time per workspace. */
 int pkvs_workspace_size(const pkvs_plan *plan, size_t *float_ws_bytes, size_t *int_ws_bytes);
+
+/* Worst-case workspace sizes of a descriptor without keeping a plan ([FIB]
+ * _full_cg_prefill_workspace_bytes: the split-KV float workspace a wrapper
+ * needs for the largest batch, computed before the wrappers exist, so a
+ * too-small buffer fails at start-up).  is_decode must agree with desc->kind
+ * (1 for PKVS_DECODE, 0 for PKVS_PREFILL or PKVS_CASCADE); max_kv_len > 0
+ * replaces desc->kv_capacity, 0 keeps it.  Equal to pkvs_workspace_size of
+ * the plan pkvs_plan_create would make for the same descriptor on the current
+ * device.  Errors as pkvs_plan_create, INVALID_ARG for a null output or a
+ * kind that disagrees with is_decode. */
+int pkvs_workspace_bytes(const pkvs_desc *desc, int32_t is_decode, int64_t max_kv_len,
+                         size_t *float_ws_bytes, size_t *int_ws_bytes);
 
 /* Plan a causal paged prefill (extend with cached prefix) batch.
  * Host arrays: qo_indptr_h [batch+1], kv_indptr_h [batch+1],
@@ -230,10 +254,12 @@ int pkvs_decode_plan(pkvs_plan *plan, const int32_t *kv_indptr_h,
                      size_t float_ws_bytes, void *int_ws, size_t int_ws_bytes,
                      hipStream_t stream);
 
-/* Run the planned decode: q, o [batch, num_qo_heads, head_dim], lse
- * [batch, num_qo_heads] (nullable).  Launches the chunk kernel and, when
+/* Run the planned decode ([FIB] FlashInferAttnBackend.forward_decode; LSE on
+ * request, [PR234] "Why each fix" 3): q, o [batch, num_qo_heads, head_dim],
+ * lse [batch, num_qo_heads] (nullable).  Launches the chunk kernel and, when
  * some request was split, the merge of its chunk partials.  window_left must
- * equal the plan's; k_scale / v_scale as pkvs_prefill_run. */
+ * equal the plan's (PLAN_MISMATCH otherwise, [PR31501] "What"); k_scale /
+ * v_scale as pkvs_prefill_run. */
 int pkvs_decode_run(const pkvs_plan *plan, const void *q, const void *k_cache,
                     const void *v_cache, int64_t num_pages, const int32_t *kv_indices_d,
                     void *o, float *lse, float sm_scale, int32_t window_left, float k_scale,
@@ -268,7 +294,8 @@ int pkvs_cascade_plan(pkvs_plan *plan, const int32_t *qo_indptr_h, const int32_t
                       size_t float_ws_bytes, void *int_ws, size_t int_ws_bytes,
                       hipStream_t stream);
 
-/* Run the planned cascade: q, o [nnz_qo, num_qo_heads, head_dim]; k_extend,
+/* Run the planned cascade ([FIB] FlashInferAttnBackend.forward_extend, the
+ * branch with cached prefixes): q, o [nnz_qo, num_qo_heads, head_dim]; k_extend,
  * v_extend [nnz_qo, num_kv_heads, head_dim] (row r is the key / value of query
  * token r); k_cache, v_cache, num_pages and kv_indices_d as pkvs_prefill_run
  * (they may be NULL / 0 when the planned batch has no cached keys); lse
@@ -338,24 +365,32 @@ int pkvs_build_kv_indices(const int32_t *page_map_d, int64_t map_rows, int64_t m
                           int32_t batch_size, int32_t *kv_indptr_d, int32_t *kv_indices_d,
                           int64_t capacity, int32_t *status_d, hipStream_t stream);
 
-/* Facts about the plan (counts refer to the last plan() call). */
+/* Facts about the plan (counts refer to the last plan() call).  Library
+ * utility, no passage: for callers, tests and profilers. */
 int pkvs_plan_get_info(const pkvs_plan *plan, pkvs_plan_info *info);
 
 /* Host copy of the last plan()'s work list: up to max_items items of
  * info.item_words int32 words each into dst; *n_items receives the count.  A
- * cascade lists its ragged pass's items, then its paged pass's. */
+ * cascade lists its ragged pass's items, then its paged pass's.  Library
+ * utility, no passage: it exposes the planner's output to tests. */
 int pkvs_plan_copy_items(const pkvs_plan *plan, int32_t *dst, int64_t max_items,
                          int64_t *n_items);
 
 /* Destroy a plan (waits for its pending host-to-device copies).  NULL is a
- * no-op. */
+ * no-op.  Library utility, no passage. */
 void pkvs_plan_destroy(pkvs_plan *plan);
 
-/* Static description of a status code. */
+/* Static description of a status code.  Library utility, no passage. */
 const char *pkvs_strerror(int code);
 
-/* Detail message of the last error on this thread ("" if none). */
+/* Detail message of the last error on this thread ("" if none); the string
+ * stays valid until the thread's next libpkvs call.  Library utility, no
+ * passage. */
 const char *pkvs_last_error(void);
+
+/* The same thread-local detail message as pkvs_last_error (both names are
+ * exported).  Library utility, no passage. */
+const char *pkvs_last_error_message(void);
 
 #ifdef __cplusplus
 }

@@ -223,7 +223,7 @@ static int read_layout(const Plan *p, const int32_t *qo_indptr, const int32_t *k
 // the one holding its last query's position (causal).  Items are ordered by
 // decreasing key count so a strided persistent grid receives a balanced mix;
 // within one cost the kv head runs fastest.
-static void build_prefill(Plan *p, const std::vector<Req> &reqs)
+static int build_prefill(Plan *p, const std::vector<Req> &reqs)
 {
     const pkvs_desc &d = p->desc;
     const int tq = p->query_tile;
@@ -259,9 +259,9 @@ static void build_prefill(Plan *p, const std::vector<Req> &reqs)
     }
     std::stable_sort(items.begin(), items.end(),
                      [](const It &a, const It &b) { return a.cost > b.cost; });
-    // the direct-to-LDS variant keeps an item's page ids in LDS: the key range
-    // it loads (whole tiles, cut at the request's end) must fit the table
-    p->run_variant = p->prefill_variant;
+    // the direct-to-LDS variants keep an item's page ids in an LDS table; the
+    // variant was fixed at plan creation so that no item within the
+    // capacities can span more pages than the table (dma_table_pages_bound)
     if (p->prefill_variant == kPrefillDma || p->prefill_variant == kPrefillBig) {
         for (const It &it : items) {
             const int64_t kb = it.w[kPiKvBegin];
@@ -272,10 +272,11 @@ static void build_prefill(Plan *p, const std::vector<Req> &reqs)
             if (kv_end <= kb) continue;
             const int64_t last = std::min(kb + ceil_div(kv_end - kb, kv_tile) * kv_tile,
                                           kv_len) - 1;
-            if (last / d.page_size - kb / d.page_size + 1 > kPrefillDmaPages) {
-                p->run_variant = kPrefillRows256;
-                break;
-            }
+            if (last / d.page_size - kb / d.page_size + 1 > kPrefillDmaPages)
+                return fail(PKVS_ERR_CAPACITY, "a prefill item spans %lld pages of keys, more "
+                            "than the %d the plan's kernel holds",
+                            (long long)(last / d.page_size - kb / d.page_size + 1),
+                            kPrefillDmaPages);
         }
     }
     p->n_items = int64_t(items.size());
@@ -299,6 +300,7 @@ static void build_prefill(Plan *p, const std::vector<Req> &reqs)
     w[kHdrItemWords] = kPrefillItemWords;
     for (size_t i = 0; i < items.size(); ++i)
         std::memcpy(w + kHeaderWords + i * kPrefillItemWords, items[i].w, sizeof items[i].w);
+    return PKVS_OK;
 }
 
 // Keys per decode chunk when the caller leaves it to the planner: aim for
@@ -444,6 +446,24 @@ static int finish_plan(Plan *p, void *float_ws, size_t float_bytes, void *int_ws
     return PKVS_OK;
 }
 
+// Most pages of keys one prefill item can span within the plan's capacities.
+// Its first key tile starts at most kv_tile-1 keys before the window start of
+// its first query, and its last (cut at the request's end) ends at most
+// kv_tile-2 keys past its last query's position, so with a window the span is
+// below window_left + query_tile + 2 kv_tile keys; without one it is at most
+// the whole request.  (A cascade's prefix pass places its queries after every
+// key of the table, which only shortens the span.)
+static int64_t item_pages_bound(const pkvs_desc &d, int kv_tile, int query_tile)
+{
+    const int64_t P = d.page_size;
+    int64_t pages = (d.kv_capacity - 1) / P + 1;
+    if (d.window_left >= 0 && d.causal) {
+        const int64_t span = int64_t(d.window_left) + query_tile + 2 * int64_t(kv_tile) - 3;
+        pages = std::min(pages, span / P + 2);
+    }
+    return pages;
+}
+
 // A validated prefill or decode descriptor -> plan object (ragged: a
 // cascade's extend pass, see plan_state.h).
 static int create_plan(const pkvs_desc *desc, bool ragged, Plan **out)
@@ -483,7 +503,15 @@ static int create_plan(const pkvs_desc *desc, bool ragged, Plan **out)
         if ((v == kPrefillDma || v == kPrefillBig) && p->have_gpu && !fp32 &&
             prefill_blocks_per_cu(desc->head_dim, v, f16, kvf) < 1)
             v = kPrefillRows256;
-        p->prefill_variant = p->run_variant = v;
+        // ... and an LDS table of kPrefillDmaPages page ids per item: they are
+        // kept only when no item within the capacities can span more pages.
+        // The choice holds for the plan's lifetime, so a captured run keeps
+        // launching the kernel that every later plan() builds its items for.
+        if ((v == kPrefillDma || v == kPrefillBig) &&
+            item_pages_bound(*desc, v == kPrefillBig ? kPrefillBigTile : kPrefillKvTile,
+                             256 / group) > kPrefillDmaPages)
+            v = kPrefillRows256;
+        p->prefill_variant = v;
         const int rows = v == kPrefillRows128 ? 128 : 256;
         p->query_tile = fp32 ? kGenericQTile : rows / group;
         p->item_words = kPrefillItemWords;
@@ -594,7 +622,7 @@ static int create_cascade(const pkvs_desc *desc, Plan **out)
     p->block_threads = q->block_threads;
     p->query_tile = q->query_tile;
     p->item_words = q->item_words;
-    p->prefill_variant = p->run_variant = q->prefill_variant;
+    p->prefill_variant = q->prefill_variant;
     p->items_cap = p->ext->items_cap + q->items_cap;
     p->pre_int_off = align256(p->ext->int_ws_need);
     p->int_ws_need = p->pre_int_off + q->int_ws_need;
@@ -632,6 +660,28 @@ int pkvs_workspace_size(const pkvs_plan *p, size_t *float_ws_bytes, size_t *int_
     return PKVS_OK;
 }
 
+int pkvs_workspace_bytes(const pkvs_desc *desc, int32_t is_decode, int64_t max_kv_len,
+                         size_t *float_ws_bytes, size_t *int_ws_bytes)
+{
+    clear_error();
+    if (!desc || !float_ws_bytes || !int_ws_bytes)
+        return fail(PKVS_ERR_INVALID_ARG, "null argument");
+    if ((is_decode != 0) != (desc->kind == PKVS_DECODE))
+        return fail(PKVS_ERR_INVALID_ARG, "is_decode %d disagrees with desc->kind %d",
+                    is_decode, desc->kind);
+    if (max_kv_len < 0) return fail(PKVS_ERR_INVALID_ARG, "max_kv_len %lld < 0",
+                                    (long long)max_kv_len);
+    pkvs_desc d = *desc;
+    if (max_kv_len > 0) d.kv_capacity = max_kv_len;
+    pkvs_plan *p = nullptr;
+    int rc = pkvs_plan_create(&p, &d);
+    if (rc) return rc;
+    *float_ws_bytes = p->float_ws_need;
+    *int_ws_bytes = p->int_ws_need;
+    destroy_plan(p);
+    return PKVS_OK;
+}
+
 int pkvs_prefill_plan(pkvs_plan *p, const int32_t *qo_indptr_h, const int32_t *kv_indptr_h,
                       const int32_t *kv_last_page_len_h, int32_t batch_size, void *float_ws,
                       size_t float_ws_bytes, void *int_ws, size_t int_ws_bytes,
@@ -644,7 +694,8 @@ int pkvs_prefill_plan(pkvs_plan *p, const int32_t *qo_indptr_h, const int32_t *k
     std::vector<Req> reqs;
     int rc = read_layout(p, qo_indptr_h, kv_indptr_h, kv_last_page_len_h, batch_size, reqs);
     if (rc) return rc;
-    build_prefill(p, reqs);
+    rc = build_prefill(p, reqs);
+    if (rc) return rc;
     if (p->n_items > p->items_cap)
         return fail(PKVS_ERR_CAPACITY, "prefill work list of %lld items exceeds capacity %lld",
                     (long long)p->n_items, (long long)p->items_cap);
@@ -672,7 +723,8 @@ int pkvs_decode_plan(pkvs_plan *p, const int32_t *kv_indptr_h, const int32_t *kv
         }
         // a keyless request still owns its query row: it becomes an item with
         // an empty key range, which writes o = 0 and lse = -inf
-        build_prefill(p, as_prefill);
+        rc = build_prefill(p, as_prefill);
+        if (rc) return rc;
         p->split_size = 0;
     } else {
         rc = build_decode(p, reqs);
@@ -708,14 +760,14 @@ int pkvs_cascade_plan(pkvs_plan *p, const int32_t *qo_indptr_h, const int32_t *k
         ext_reqs[b] = Req{q.qo_begin, q.qo_len, q.qo_len, entries};
         entries += ceil_div(q.qo_len, kRaggedPage);
     }
-    build_prefill(e, ext_reqs);
-    build_prefill(r, pre_reqs);
+    rc = build_prefill(e, ext_reqs);
+    if (!rc) rc = build_prefill(r, pre_reqs);
+    if (rc) return rc;
     if (e->n_items > e->items_cap || r->n_items > r->items_cap)
         return fail(PKVS_ERR_CAPACITY, "cascade work lists (%lld, %lld items) exceed capacity "
                     "(%lld, %lld)", (long long)e->n_items, (long long)r->n_items,
                     (long long)e->items_cap, (long long)r->items_cap);
     p->n_items = e->n_items + r->n_items;
-    p->run_variant = r->run_variant;
     p->planned_keys = r->planned_keys;
     p->batch = e->batch = r->batch = batch_size;
     if (!int_ws) return PKVS_OK;  // dry plan
@@ -749,7 +801,7 @@ int pkvs_plan_get_info(const pkvs_plan *p, pkvs_plan_info *info)
     info->split_size = p->split_size;
     info->item_words = p->item_words;
     info->query_tile = p->query_tile;
-    info->prefill_variant = p->desc.kind != PKVS_DECODE ? p->run_variant : 0;
+    info->prefill_variant = p->desc.kind != PKVS_DECODE ? p->prefill_variant : 0;
     info->num_cus = p->num_cus;
     info->decode_waves = p->desc.kind == PKVS_DECODE ? p->decode_waves : 0;
     return PKVS_OK;
@@ -797,5 +849,7 @@ const char *pkvs_strerror(int code)
 }
 
 const char *pkvs_last_error(void) { return g_last_error.c_str(); }
+
+const char *pkvs_last_error_message(void) { return g_last_error.c_str(); }
 
 }  // extern "C"

@@ -37,8 +37,7 @@ struct pkvs_plan {
     bool have_gpu = false;
     int num_cus = 0;
     int grid_blocks = 0, block_threads = 0, query_tile = 0, item_words = 0;
-    int prefill_variant = 1;  // bf16 prefill kernel variant (PrefillVariant)
-    int run_variant = 1;      // the variant the last plan() launches
+    int prefill_variant = 1;  // 16-bit prefill kernel variant (PrefillVariant), fixed at creation
     int64_t auto_target_items = 0;
     int decode_waves = 1;     // waves per decode work item (1 or 4)
     int64_t items_cap = 0, slots_cap = 0, merges_cap = 0;

@@ -114,7 +114,7 @@ hipError_t launch_prefill_pass(const pkvs_plan *p, const void *q, const void *k,
     a.fold_lse = fold_lse;
     return p->desc.dtype == PKVS_FP32
                ? launch_attention_fp32(a, p->desc.head_dim, p->grid_blocks, stream)
-               : launch_prefill_16bit(a, p->desc.head_dim, p->run_variant,
+               : launch_prefill_16bit(a, p->desc.head_dim, p->prefill_variant,
                                       p->desc.dtype == PKVS_FP16, p->desc.kv_format,
                                       p->grid_blocks, stream);
 }

@@ -51,6 +51,7 @@ EXPORTED = [
     "pkvs_decode_plan", "pkvs_decode_run", "pkvs_cascade_plan", "pkvs_cascade_run",
     "pkvs_merge_state", "pkvs_append_kv", "pkvs_build_kv_indices", "pkvs_plan_get_info",
     "pkvs_plan_copy_items", "pkvs_plan_destroy", "pkvs_strerror", "pkvs_last_error",
+    "pkvs_workspace_bytes", "pkvs_last_error_message",
 ]
 
 
@@ -111,6 +112,9 @@ def _load() -> ctypes.CDLL:
         "pkvs_plan_destroy": (None, [P]),
         "pkvs_strerror": (ctypes.c_char_p, [ctypes.c_int]),
         "pkvs_last_error": (ctypes.c_char_p, []),
+        "pkvs_workspace_bytes": (ctypes.c_int, [ctypes.POINTER(pkvs_desc), i32, i64,
+                                                ctypes.POINTER(sz), ctypes.POINTER(sz)]),
+        "pkvs_last_error_message": (ctypes.c_char_p, []),
     }
     for name, (res, args) in sig.items():
         fn = getattr(lib, name)
@@ -185,6 +189,17 @@ def pkvs_workspace_size(plan) -> Tuple[int, int]:
     _check(_lib.pkvs_workspace_size(plan, ctypes.byref(f), ctypes.byref(i)),
            "pkvs_workspace_size")
     return f.value, i.value
+
+
+def pkvs_workspace_bytes(desc: pkvs_desc, is_decode: bool, max_kv_len: int = 0) -> Tuple[int, int]:
+    f, i = ctypes.c_size_t(), ctypes.c_size_t()
+    _check(_lib.pkvs_workspace_bytes(ctypes.byref(desc), int(bool(is_decode)), int(max_kv_len),
+                                     ctypes.byref(f), ctypes.byref(i)), "pkvs_workspace_bytes")
+    return f.value, i.value
+
+
+def pkvs_last_error_message() -> str:
+    return _lib.pkvs_last_error_message().decode()
 
 
 def pkvs_prefill_plan(plan, qo_indptr_h, kv_indptr_h, kv_last_page_len_h, batch_size: int,

@@ -41,17 +41,53 @@ def make_attention(case: Case, window_left=None, fixed_split_size=None, disable_
         kv_dtype=kv_dtype_of(case), decode_waves=decode_waves)
 
 
+def poisoned_outputs(q: torch.Tensor):
+    """O and LSE buffers for a run, filled with NaN, so that any output element
+    the kernels leave unwritten fails the comparison."""
+    o = torch.full_like(q, float("nan"))
+    lse = torch.full((q.shape[0], q.shape[1]), float("nan"), dtype=torch.float32,
+                     device=q.device)
+    return o, lse
+
+
 def gpu_run(case: Case, window_left=None, att=None, return_lse=True, **kw):
+    """plan() + run() of `case` through the C ABI into NaN-filled outputs."""
     W = case.window_left if window_left is None else window_left
     if att is None:
         att = make_attention(case, window_left=W, **kw)
     att.plan(qo_indptr=case.qo_indptr.cpu(), kv_indptr=case.kv_indptr.cpu(),
              kv_last_page_len=case.kv_last_page_len.cpu())
+    o, lse = poisoned_outputs(case.q)
     res = att.run(case.q, case.k_cache, case.v_cache, case.kv_indices, sm_scale=case.sm_scale,
                   window_left=W, causal=case.causal, return_lse=return_lse,
-                  k_scale=case.k_scale, v_scale=case.v_scale)
+                  k_scale=case.k_scale, v_scale=case.v_scale, out=o,
+                  lse=lse if return_lse else None)
     torch.cuda.synchronize()
     return res
+
+
+def assert_all_written(case: Case, o: torch.Tensor, lse: torch.Tensor, tag=""):
+    """Every output row of a run into NaN-filled buffers was written: O finite
+    everywhere, LSE finite for every query with a visible key, and (O = 0,
+    LSE = -inf) for the queries of requests without keys."""
+    keyless = torch.zeros(o.shape[0], dtype=torch.bool)
+    qop = case.qo_indptr.cpu()
+    for b, kv in enumerate(case.kv_lens):
+        if kv == 0:
+            keyless[int(qop[b]):int(qop[b + 1])] = True
+    of = torch.isfinite(o.float()).all(dim=2).all(dim=1).cpu()
+    bad_o = int((~of).sum())
+    assert bad_o == 0, f"{tag}: {bad_o} query rows of O hold non-finite values"
+    if lse is None:
+        return
+    lc = lse.cpu()
+    lf = torch.isfinite(lc).all(dim=1)
+    bad_l = int((~lf & ~keyless).sum())
+    assert bad_l == 0, f"{tag}: {bad_l} query rows with keys have a non-finite LSE"
+    if keyless.any():
+        assert torch.isneginf(lc[keyless]).all(), f"{tag}: keyless rows must have LSE = -inf"
+        assert (o[keyless.to(o.device)] == 0).all(), f"{tag}: keyless rows must have O = 0"
+    log(f"  {tag}: all {o.shape[0]} query rows written ({int(keyless.sum())} keyless)")
 
 
 def compare(o, lse, o_ref, lse_ref, rows=None, tag="", o_tol=O_TOL, lse_tol=LSE_TOL):
@@ -70,7 +106,10 @@ def compare(o, lse, o_ref, lse_ref, rows=None, tag="", o_tol=O_TOL, lse_tol=LSE_
         if rows is not None:
             l = l[rows]
         both_inf = np.isneginf(l) & np.isneginf(lr)
-        dl = np.where(both_inf, 0.0, np.abs(l - lr))
+        # (-inf) - (-inf) is never evaluated: equal infinities count as 0 apart
+        dl = np.zeros(l.shape, dtype=np.float64)
+        np.subtract(l, lr, out=dl, where=~both_inf)
+        dl = np.abs(dl)
         badl = ~(dl <= lse_tol)
         msg += (f"; LSE max|d|={np.nanmax(dl) if dl.size else 0:.3e} "
                 f"mismatch={badl.mean() if dl.size else 0:.4%} (tol {lse_tol})")

@@ -11,8 +11,8 @@ import pytest
 import torch
 
 import oracle
-from gpu_helpers import (compare, gpu_run, kv_dtype_of, log, make_attention, oracle_for,
-                         sub_case)
+from gpu_helpers import (assert_all_written, compare, gpu_run, kv_dtype_of, log, make_attention,
+                         oracle_for, poisoned_outputs, sub_case)
 from paged_kv_sliding_amd import pkvs as P
 from paged_kv_sliding_amd.synth import build_case, cascade_inputs, case_from_lengths
 
@@ -84,40 +84,52 @@ LONG_ROWS = [0, 1, 2, 7, 8, 31, 32, 33, 127, 128, 129, 4094, 4095, 4096, 4097, 4
              8192, 12345, 16384, 20000, 24575, 30001, 32735, 32736, 32766, 32767]
 
 
-def test_long_prefill_sampled():
-    """The full 32k-token prefill in the benchmark's launch configuration,
-    checked on sampled query tokens (all heads)."""
+def test_long_prefill_every_item():
+    """The full 32k-token prefill in the benchmark's launch configuration (the
+    64-key-step kernel, work items claimed at run time), into NaN-filled
+    outputs: every output row must be written, and the oracle checks one
+    token of every 64-token query tile (each tile is one work item per kv head;
+    all 32 heads of the token are compared, so every item owns a checked row),
+    plus the window edges."""
     case = build_case("long_prefill", device=DEV)
     log("long_prefill run")
     att = make_attention(case)
     o, lse = gpu_run(case, att=att)
-    assert att.info().prefill_variant == 5  # the 64-key-step kernel the bench times
+    info = att.info()
+    assert info.prefill_variant == 5  # the 64-key-step kernel the bench times
+    tile = info.query_tile
+    assert tile == 64 and info.num_items == (32768 // tile) * case.num_kv_heads
+    assert info.num_items > info.grid_blocks  # workgroups take several items each
+    assert_all_written(case, o, lse, tag="long_prefill")
     rng = np.random.default_rng(4)
-    rows = sorted(set(LONG_ROWS + rng.integers(0, 32768, size=20).tolist()))
-    log(f"long_prefill oracle on {len(rows)} rows")
+    rows = set(LONG_ROWS)
+    rows |= {t0 + int(rng.integers(0, tile)) for t0 in range(0, 32768, tile)}
+    rows = sorted(rows)
+    log(f"long_prefill oracle on {len(rows)} rows ({oracle.default_threads()} threads)")
     ro, rl = oracle_for(case, rows=rows)
-    compare(o, lse, ro, rl, rows=rows, tag="long_prefill sampled")
+    compare(o, lse, ro, rl, rows=rows, tag="long_prefill, a row of every item")
 
 
 @pytest.mark.parametrize("W", [4095, -1])
-def test_split_decode_sampled(W):
-    """The full 256-request split-KV decode (2048-key chunks merged), checked
-    on sampled requests (all heads)."""
+def test_split_decode_every_request(W):
+    """The full 256-request split-KV decode (2048-key chunks merged) in the
+    benchmark's launch configuration, into NaN-filled outputs, against the
+    oracle on every request and head."""
     case = build_case("split_decode", device=DEV, window_left=W)
     log(f"split_decode W={W} run")
     att = make_attention(case)
     o, lse = gpu_run(case, att=att)
     info = att.info()
     assert info.split_size == 2048 and info.num_merges > 0
-    rng = np.random.default_rng(5)
-    kv = np.array(case.kv_lens)
-    picks = {int(np.argmin(kv)), int(np.argmax(kv))}
-    picks |= set(rng.choice(len(kv), size=6, replace=False).tolist())
-    picks = sorted(picks)
-    sub = sub_case(case, picks)
-    log(f"split_decode oracle on requests {picks}")
-    ro, rl = oracle_for(sub)
-    compare(o[picks], lse[picks], ro, rl, tag=f"split_decode W={W}")
+    assert info.num_items > info.grid_blocks  # waves take several items each
+    assert_all_written(case, o, lse, tag=f"split_decode W={W}")
+    log(f"split_decode W={W} oracle on all {case.batch_size} requests "
+        f"({oracle.default_threads()} threads)")
+    host = dataclasses.replace(case, q=case.q.cpu(), k_cache=case.k_cache.cpu(),
+                               v_cache=case.v_cache.cpu())
+    ro, rl = oracle_for(host)
+    del host
+    compare(o, lse, ro, rl, tag=f"split_decode W={W}, every request")
 
 
 # ----------------------------------------------------------------- edge cases and tails
@@ -445,6 +457,68 @@ def test_graph_replay_follows_replans(decode, nw):
             compare(want_o, want_l, ro, rl, tag=f"graph decode={decode} nw={nw}")
 
 
+def _layout_case(case, picks):
+    """The requests `picks` of `case` as a case of their own over the same cache
+    pages (for the oracle)."""
+    rows, pages, qo_ind, kv_ind, last = _sub_layout(case, picks)
+    return dataclasses.replace(
+        case, qo_lens=[case.qo_lens[b] for b in picks], kv_lens=[case.kv_lens[b] for b in picks],
+        q=case.q[torch.tensor(rows, device=case.q.device)], qo_indptr=qo_ind, kv_indptr=kv_ind,
+        kv_indices=pages, kv_last_page_len=last)
+
+
+@pytest.mark.parametrize("W,kv_cap,want", [(-1, 3000, 2), (1023, 8192, 5)])
+def test_graph_replay_variant_fixed_by_capacity(W, kv_cap, want):
+    """The prefill kernel is chosen when the plan is created, from its
+    capacities: a run() captured while a short batch is planned replays the
+    same kernel after a re-plan whose items span thousands of keys (page size 1,
+    so every key is a page; the direct-to-LDS kernels hold 2048 page ids per
+    item).  Every replay matches the oracle of the batch planned last."""
+    case = small([64, 3, 40], [kv_cap, 700, 1000], H_q=8, H_kv=2, D=128, P_=1, W=W,
+                 seed=64 + W)
+    att = make_attention(case, prefill_variant=5)
+    assert att.info().prefill_variant == want
+    n_q = case.q.shape[0]
+    q_buf = torch.zeros_like(case.q)
+    idx_buf = torch.zeros_like(case.kv_indices)
+    o_buf = torch.zeros_like(case.q)
+    l_buf = torch.zeros(n_q, case.num_qo_heads, dtype=torch.float32, device=DEV)
+
+    def load_and_plan(picks):
+        rows, pages, qo_ind, kv_ind, last = _sub_layout(case, picks)
+        q_buf.zero_()
+        q_buf[:len(rows)] = case.q[torch.tensor(rows, device=DEV)]
+        idx_buf.zero_()
+        idx_buf[:len(pages)] = pages.to(DEV)
+        att.plan(qo_indptr=qo_ind, kv_indptr=kv_ind, kv_last_page_len=last)
+        return len(rows)
+
+    def run():
+        att.run(q_buf, case.k_cache, case.v_cache, idx_buf, sm_scale=case.sm_scale,
+                window_left=W, out=o_buf, lse=l_buf)
+
+    load_and_plan([1])
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        run()
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        run()
+    for picks in ([0, 1, 2], [1], [2, 0]):
+        n = load_and_plan(picks)
+        assert att.info().prefill_variant == want
+        ro, rl = oracle_for(_layout_case(case, picks))
+        for rep in range(2):
+            o_buf.fill_(float("nan"))
+            l_buf.fill_(float("nan"))
+            g.replay()
+            torch.cuda.synchronize()
+            compare(o_buf[:n], l_buf[:n], ro, rl, tag=f"replay W={W} picks={picks} rep={rep}")
+
+
 def test_replan_in_place_then_capacity_error():
     big = small([1] * 6, [500, 2000, 33, 4096, 1, 700], H_q=32, H_kv=8, D=128, W=127, seed=61,
                 decode=True)
@@ -551,9 +625,11 @@ def cascade_run(case, trim=False, att=None, return_lse=True, **kw):
         # their scales: power-of-two scales keep them exact)
         k_ext = (k_ext.float() * case.k_scale).to(case.dtype)
         v_ext = (v_ext.float() * case.v_scale).to(case.dtype)
+    o, lse = poisoned_outputs(case.q)
     res = att.run(case.q, k_ext, v_ext, cin.k_cache, cin.v_cache, cin.kv_indices,
                   sm_scale=case.sm_scale, window_left=W, return_lse=return_lse,
-                  k_scale=case.k_scale, v_scale=case.v_scale)
+                  k_scale=case.k_scale, v_scale=case.v_scale, out=o,
+                  lse=lse if return_lse else None)
     torch.cuda.synchronize()
     return res, att
 
@@ -804,7 +880,8 @@ def test_decode_step_appends_and_builds_its_page_table(W):
     for n in npg:
         host_indptr.append(host_indptr[-1] + n)
     att.plan(kv_indptr=host_indptr, kv_last_page_len=last)
-    o, lse = att.run(case.q, kc, vc, ki, sm_scale=case.sm_scale, window_left=W)
+    o, lse = poisoned_outputs(case.q)
+    att.run(case.q, kc, vc, ki, sm_scale=case.sm_scale, window_left=W, out=o, lse=lse)
     torch.cuda.synchronize()
     assert kp.cpu().tolist() == host_indptr
     ro, rl = oracle_for(case)

@@ -36,6 +36,72 @@ def test_library_exports_every_declared_symbol():
         assert hasattr(lib, name)
 
 
+# The calls of the boundary as the hot-path statement lists them, and the
+# exported entry points that provide each (the plan object is created once for
+# its capacities and re-planned in place; run() reads the device layout that
+# plan() uploaded into the int workspace, so it takes only kv_indices).
+BOUNDARY_CALLS = {
+    "pkvs_workspace_bytes": ["pkvs_workspace_bytes", "pkvs_workspace_size"],
+    "pkvs_prefill_plan": ["pkvs_plan_create", "pkvs_prefill_plan"],
+    "pkvs_prefill_run": ["pkvs_prefill_run"],
+    "pkvs_decode_plan": ["pkvs_plan_create", "pkvs_decode_plan"],
+    "pkvs_decode_run": ["pkvs_decode_run"],
+    "pkvs_merge_state": ["pkvs_merge_state"],
+    "pkvs_plan_destroy": ["pkvs_plan_destroy"],
+    "pkvs_strerror": ["pkvs_strerror"],
+    "pkvs_last_error_message": ["pkvs_last_error_message", "pkvs_last_error"],
+}
+
+
+def test_boundary_calls_are_all_provided():
+    declared = set(header_functions())
+    for call, provided_by in BOUNDARY_CALLS.items():
+        assert set(provided_by) <= declared, (call, provided_by)
+    # the names the statement uses are exported under those names where the
+    # signature is kept
+    for name in ("pkvs_workspace_bytes", "pkvs_prefill_plan", "pkvs_prefill_run",
+                 "pkvs_decode_plan", "pkvs_decode_run", "pkvs_merge_state", "pkvs_plan_destroy",
+                 "pkvs_strerror", "pkvs_last_error_message"):
+        assert name in declared
+
+
+def test_every_declaration_cites_a_passage_or_says_utility():
+    """Each function declared in include/pkvs.h is preceded by a comment that
+    cites the passage it follows ([FIB], [PR31501], [PR234]) or says it is a
+    library utility with no passage."""
+    text = open(HEADER).read()
+    for name in header_functions():
+        m = re.search(r"/\*((?:(?!\*/).)*)\*/\s*(?:const\s+)?\w+\s*\**\s*" + name + r"\s*\(",
+                      text, flags=re.S)
+        assert m, f"{name}: no comment right before its declaration"
+        doc = m.group(1)
+        assert re.search(r"\[(FIB|PR31501|PR234)\]", doc) or "Library utility, no passage" \
+            in re.sub(r"\s*\n\s*\*\s*", " ", doc), name
+
+
+def test_workspace_bytes_equals_the_plans_sizes():
+    for kind, kw in ((P.PKVS_PREFILL, {}), (P.PKVS_DECODE, dict(num_qo_heads=64, num_kv_heads=8,
+                                                               window_left=4095, batch_capacity=256,
+                                                               kv_capacity=32768,
+                                                               fixed_split_size=2048)),
+                     (P.PKVS_CASCADE, dict(window_left=511))):
+        d = desc(kind, **kw)
+        h = P.pkvs_plan_create(d)
+        assert P.pkvs_workspace_bytes(d, kind == P.PKVS_DECODE) == P.pkvs_workspace_size(h)
+        P.pkvs_plan_destroy(h)
+        d2 = desc(kind, **dict(kw, kv_capacity=100))
+        h2 = P.pkvs_plan_create(d2)
+        assert P.pkvs_workspace_bytes(d, kind == P.PKVS_DECODE, 100) == \
+            P.pkvs_workspace_size(h2)
+        P.pkvs_plan_destroy(h2)
+    assert err_code(lambda: P.pkvs_workspace_bytes(desc(), True)) == P.PKVS_ERR_INVALID_ARG
+    assert "disagrees" in P.pkvs_last_error_message()
+    assert P.pkvs_last_error_message() == P.last_error()
+    assert err_code(lambda: P.pkvs_workspace_bytes(desc(head_dim=96), False)) == \
+        P.PKVS_ERR_UNSUPPORTED
+    assert err_code(lambda: P.pkvs_workspace_bytes(desc(), False, -1)) == P.PKVS_ERR_INVALID_ARG
+
+
 def desc(kind=P.PKVS_PREFILL, **kw):
     base = dict(num_qo_heads=4, num_kv_heads=1, head_dim=128, page_size=16,
                 dtype=torch.bfloat16, window_left=31, causal=True, batch_capacity=16,
@@ -189,27 +255,53 @@ def test_decode_chunks_partition_the_window(W, split):
 
 def test_prefill_variant_choice_and_page_table_fallback():
     """Large head_dim-128 prefill plans pick the 64-key-step direct-to-LDS
-    kernel (variant 5); a plan() whose items span more pages than its LDS page
-    table (2048) runs the register-staged 256-row kernel (variant 2) instead,
-    for both direct-to-LDS variants."""
+    kernel (variant 5).  The direct-to-LDS variants hold an item's page ids in
+    a 2048-entry LDS table, so a plan whose capacities let one item span more
+    pages runs the register-staged 256-row kernel (variant 2) from creation on;
+    the variant never changes between plan() calls of one plan object (a
+    captured run keeps launching the kernel it was captured with)."""
     big = dict(num_qo_heads=32, num_kv_heads=8, window_left=-1, qo_capacity=32768,
-               kv_capacity=65536, batch_capacity=4)
-    h = P.pkvs_plan_create(desc(page_size=16, **big))
-    qop, kvp, last = csr([4096], [4096], 16)
-    P.pkvs_prefill_plan(h, qop, kvp, last, 1, None, None)
-    assert P.pkvs_plan_get_info(h).prefill_variant == 5
+               kv_capacity=32768, batch_capacity=4)
     for v in (0, 4, 5):
+        # no window, 32768 keys of 16: at most 2048 pages per item -> kept
         hv = P.pkvs_plan_create(desc(page_size=16, prefill_variant=v, **big))
-        qop, kvp, last = csr([64], [32768], 16)   # 2048 pages of 16 keys: fits
-        P.pkvs_prefill_plan(hv, qop, kvp, last, 1, None, None)
         assert P.pkvs_plan_get_info(hv).prefill_variant == (v or 5)
-        qop, kvp, last = csr([64], [32769], 16)   # 2049 pages
+        for qo, kv in (([4096], [4096]), ([64], [32768]), ([1] * 4, [1, 40, 30000, 7])):
+            qop, kvp, last = csr(qo, kv, 16)
+            P.pkvs_prefill_plan(hv, qop, kvp, last, len(kv), None, None)
+            assert P.pkvs_plan_get_info(hv).prefill_variant == (v or 5)
+        # one key more per request allows 2049 pages -> variant 2 from creation
+        hv = P.pkvs_plan_create(desc(page_size=16, prefill_variant=v,
+                                     **dict(big, kv_capacity=32769)))
+        assert P.pkvs_plan_get_info(hv).prefill_variant == 2
+        qop, kvp, last = csr([64], [4096], 16)
         P.pkvs_prefill_plan(hv, qop, kvp, last, 1, None, None)
         assert P.pkvs_plan_get_info(hv).prefill_variant == 2
-    h1 = P.pkvs_plan_create(desc(page_size=1, **dict(big, window_left=1023)))
-    qop, kvp, last = csr([8192], [8192], 1)   # windowed items span ~1100 pages
-    P.pkvs_prefill_plan(h1, qop, kvp, last, 1, None, None)
-    assert P.pkvs_plan_get_info(h1).prefill_variant == 5
+    # page size 1 without a window: 3000 keys are 3000 pages -> variant 2
+    h = P.pkvs_plan_create(desc(page_size=1, prefill_variant=5, **dict(big, kv_capacity=3000)))
+    assert P.pkvs_plan_get_info(h).prefill_variant == 2
+    # with a window the span is bounded by window_left: 1023 + 64 + 128 keys
+    h1 = P.pkvs_plan_create(desc(page_size=1, **dict(big, window_left=1023, kv_capacity=65536)))
+    for qo, kv in (([8192], [8192]), ([100, 3000], [1000, 60000])):
+        qop, kvp, last = csr(qo, kv, 1)
+        P.pkvs_prefill_plan(h1, qop, kvp, last, len(kv), None, None)
+        assert P.pkvs_plan_get_info(h1).prefill_variant == 5
+    # largest window that still fits: W + 64 + 2*64 - 3 keys -> W/1 + 2 pages
+    for W, want in ((1857, 5), (1858, 2)):
+        hw = P.pkvs_plan_create(desc(page_size=1, **dict(big, window_left=W, kv_capacity=65536)))
+        assert P.pkvs_plan_get_info(hw).prefill_variant == want, W
+        if want == 5:
+            # the worst item of that window spans exactly the table or less
+            qop, kvp, last = csr([4096], [65536], 1)
+            P.pkvs_prefill_plan(hw, qop, kvp, last, 1, None, None)
+            items = P.pkvs_plan_copy_items(hw).numpy()
+            spans = []
+            for it in items:
+                kb, kv_len, pos0, qn = it[7], it[5], it[4], it[3]
+                kv_end = min(kv_len, pos0 + qn)
+                lastk = min(kb + -(-(kv_end - kb) // 64) * 64, kv_len) - 1
+                spans.append(lastk - kb + 1)
+            assert max(spans) <= 2048
     # head_dim 64 keeps the register-staged kernel; asking for 4 is refused
     assert P.pkvs_plan_get_info(P.pkvs_plan_create(desc(head_dim=64, **big))).prefill_variant == 2
     for v in (4, 5):
