@@ -17,8 +17,13 @@ Reported (one JSON line):
                  the decode run's duration (chunk kernel + merge kernel)
   roofline       prefill kernel against the bf16 dense MFMA peak
   roofline_decode  decode against the HBM peak
-  cpu_baseline   the CPU oracle (single thread, fp64) on a bounded sample of
-                 the prefill workload, in the same unit
+  cpu_baseline   the CPU oracle (fp64, threads over query rows on the host's
+                 cores) on a bounded sample of the prefill workload, in the same
+                 unit; per_config times it on every workload in that
+                 workload's unit (prefill GFLOP/s, decode KV GB/s)
+  plan_host_us   host time of the plan() calls (median, microseconds)
+  merge_state    the pairwise merge at the split decode's partial shape and
+                 at 32768 tokens x 32 heads, HBM bytes 3*N*H*(D*2+4)
   decode_no_window  the same decode batch with window_left -1, timed apart
   cascade        the cascade prefill (new tokens' K/V contiguous, cached prefix
                  paged, merged), timed apart on two batches with cached
@@ -28,6 +33,9 @@ Reported (one JSON line):
   decode_fp8_kv  the split decode over an e4m3 copy of its cache, timed apart
   decode_sweep   the 64-request decode over its window sweep (W -1, 1023, 127,
                  31, 0), the last-level cache flushed before each timed run
+Every GPU time is reported as the mean (which value and the rooflines use),
+median and minimum over the timed launches; the last-level cache is flushed
+(1 GiB written) before every timed decode launch.
 
     python bench.py [--steps K] [--warmup W] [--gpus 1] [--no-cpu-baseline]
 """
@@ -64,6 +72,30 @@ def prefill_flops(case) -> int:
 def decode_bytes(case, W) -> int:
     n = sum((min(kv, W + 1) if W >= 0 else kv) for kv in case.kv_lens)
     return n * case.num_kv_heads * case.head_dim * 2 * 2
+
+
+def time_stats(ts) -> dict:
+    """Mean, median and minimum of a list of milliseconds."""
+    srt = sorted(ts)
+    return {"mean": sum(ts) / len(ts), "median": srt[len(srt) // 2], "min": srt[0]}
+
+
+def timed_launches(fn, reps: int, flush=None) -> list:
+    """HIP-event times (ms) of `reps` calls of fn on torch's current stream (the
+    stream the binding launches on), each after an optional flush."""
+    import torch
+
+    ts = []
+    for _ in range(reps):
+        if flush is not None:
+            flush()
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record()
+        fn()
+        b.record()
+        torch.cuda.synchronize()
+        ts.append(a.elapsed_time(b))
+    return ts
 
 
 def source_digest() -> str:
@@ -162,19 +194,14 @@ def bench_cascade(reps: int) -> dict:
         for tag, fn in (("cascade", run_cascade), ("paged", run_one)):
             for _ in range(3):
                 fn()
-            ts = []
-            for _ in range(reps):
-                a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-                a.record()
-                fn()
-                b.record()
-                torch.cuda.synchronize()
-                ts.append(a.elapsed_time(b))
-            res[tag] = sum(ts) / len(ts)
+            res[tag] = time_stats(timed_launches(fn, reps))
         flops = prefill_flops(c)
-        out[name] = {"ms": round(res["cascade"], 4),
-                     "tflops": round(flops / (res["cascade"] * 1e-3) / 1e12, 2),
-                     "paged_prefill_ms": round(res["paged"], 4),
+        out[name] = {"ms": round(res["cascade"]["mean"], 4),
+                     "ms_median": round(res["cascade"]["median"], 4),
+                     "ms_min": round(res["cascade"]["min"], 4),
+                     "tflops": round(flops / (res["cascade"]["mean"] * 1e-3) / 1e12, 2),
+                     "paged_prefill_ms": round(res["paged"]["mean"], 4),
+                     "paged_prefill_ms_median": round(res["paged"]["median"], 4),
                      "window_effective_flops": flops,
                      "prefill_variant": cas.info().prefill_variant,
                      "batch": c.batch_size, "new_tokens": sum(c.qo_lens),
@@ -184,7 +211,7 @@ def bench_cascade(reps: int) -> dict:
     return out
 
 
-def bench_decode_fp8(dec, W: int, reps: int) -> dict:
+def bench_decode_fp8(dec, W: int, reps: int, flush) -> dict:
     """The split decode batch over an e4m3 copy of its cache (K / k_scale,
     V / v_scale, converted in chunks on the device), same plan otherwise; KV
     bytes counted at one byte per element."""
@@ -214,19 +241,13 @@ def bench_decode_fp8(dec, W: int, reps: int) -> dict:
 
     for _ in range(3):
         run()
-    ts = []
-    for _ in range(reps):
-        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-        a.record()
-        run()
-        b.record()
-        torch.cuda.synchronize()
-        ts.append(a.elapsed_time(b))
-    ms = sum(ts) / len(ts)
+    st = time_stats(timed_launches(run, reps, flush))
+    ms = st["mean"]
     nb = decode_bytes(dec, W) // 2
     del k8, v8
     torch.cuda.empty_cache()
-    return {"format": "e4m3", "ms": round(ms, 4), "kv_bytes": nb,
+    return {"format": "e4m3", "ms": round(ms, 4), "ms_median": round(st["median"], 4),
+            "ms_min": round(st["min"], 4), "kv_bytes": nb,
             "GB/s": round(nb / (ms * 1e-3) / 1e9, 1),
             "frac_of_hbm_peak": round(nb / (ms * 1e-3) / 1e9 / PEAK_HBM_GBPS, 4)}
 
@@ -259,18 +280,11 @@ def bench_decode_sweep(reps: int) -> dict:
 
         for _ in range(3):
             run()
-        ts = []
-        for _ in range(reps):
-            flush.fill_(1)
-            a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-            a.record()
-            run()
-            b.record()
-            torch.cuda.synchronize()
-            ts.append(a.elapsed_time(b))
-        ms = sorted(ts)[len(ts) // 2]
+        st = time_stats(timed_launches(run, reps, lambda: flush.fill_(1)))
+        ms = st["median"]
         nb = decode_bytes(c, W)
-        out[f"W{W}"] = {"ms_median": round(ms, 4), "kv_bytes": nb,
+        out[f"W{W}"] = {"ms_median": round(ms, 4), "ms_min": round(st["min"], 4),
+                        "ms_mean": round(st["mean"], 4), "kv_bytes": nb,
                         "GB/s": round(nb / (ms * 1e-3) / 1e9, 1),
                         "frac_of_hbm_peak": round(nb / (ms * 1e-3) / 1e9 / PEAK_HBM_GBPS, 4),
                         "split_size": att.info().split_size, "items": att.info().num_items}
@@ -293,15 +307,7 @@ def bench_pool(reps: int) -> dict:
     def timed(fn):
         for _ in range(3):
             fn()
-        ts = []
-        for _ in range(reps):
-            a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-            a.record()
-            fn()
-            b.record()
-            torch.cuda.synchronize()
-            ts.append(a.elapsed_time(b))
-        return sum(ts) / len(ts)
+        return time_stats(timed_launches(fn, reps))["mean"]
 
     out = {}
     g = torch.Generator(device="cuda").manual_seed(41)
@@ -339,6 +345,48 @@ def bench_pool(reps: int) -> dict:
                                                kv_indices=ki, capacity=cap))
     out["page_table_build"] = {"requests": 256, "entries": cap, "ms": round(ms, 4),
                                "bytes": cap * 8 + 256 * 12}
+    return out
+
+
+MERGE_SHAPES = {
+    # the split decode's partials: one (o, lse) pair per request and query head
+    "split_decode_partials": (256, 64, 128),
+    # a long prefill's two halves: 32768 tokens x 32 heads
+    "tokens_32768_heads_32": (32768, 32, 128),
+}
+
+
+def bench_merge_state(reps: int, flush) -> dict:
+    """pkvs_merge_state on bf16 v and fp32 s: bytes = 3*N*H*(D*2 + 4) (two
+    partials read, one written), HIP events around each call, the last-level
+    cache flushed before each."""
+    import torch
+
+    from paged_kv_sliding_amd import pkvs as P
+
+    out = {}
+    g = torch.Generator(device="cuda").manual_seed(17)
+    for name, (n, h, d) in MERGE_SHAPES.items():
+        va = torch.randn(n, h, d, generator=g, device="cuda").to(torch.bfloat16)
+        vb = torch.randn(n, h, d, generator=g, device="cuda").to(torch.bfloat16)
+        sa = torch.randn(n, h, generator=g, device="cuda") * 4
+        sb = torch.randn(n, h, generator=g, device="cuda") * 4
+        vo, so = torch.empty_like(va), torch.empty_like(sa)
+
+        def run():
+            P.pkvs_merge_state(va, sa, vb, sb, v_out=vo, s_out=so)
+
+        for _ in range(3):
+            run()
+        st = time_stats(timed_launches(run, reps, flush))
+        nb = 3 * n * h * (d * 2 + 4)
+        gbps = nb / (st["mean"] * 1e-3) / 1e9
+        out[name] = {"tokens": n, "heads": h, "head_dim": d, "v_dtype": "bf16",
+                     "ms": round(st["mean"], 4), "ms_median": round(st["median"], 4),
+                     "ms_min": round(st["min"], 4), "bytes": nb, "GB/s": round(gbps, 1),
+                     "frac_of_hbm_peak": round(gbps / PEAK_HBM_GBPS, 4)}
+        del va, vb, sa, sb, vo, so
+    torch.cuda.empty_cache()
     return out
 
 
@@ -446,37 +494,124 @@ def ingest_counters(d: str) -> None:
     print(json.dumps(res, indent=1))
 
 
-def cpu_baseline(case, budget_s: float = 15.0):
-    """Time the CPU oracle on a bounded sample of the prefill workload."""
+def cpu_model() -> str:
+    try:
+        with open("/proc/cpuinfo") as f:
+            for ln in f:
+                if ln.startswith("model name"):
+                    return ln.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    import platform
+
+    return platform.processor() or "unknown"
+
+
+def window_sample(case, requests, W: int):
+    """The listed decode requests of `case` as a host case holding only the
+    pages their window reaches: the dropped leading pages hold no visible key,
+    and the query keeps its place relative to the kept keys."""
+    import dataclasses
+
+    import torch
+
+    P = case.page_size
+    kvp, idx = case.kv_indptr.cpu(), case.kv_indices.cpu()
+    pages, npg, lens, last = [], [], [], []
+    for b in requests:
+        n = case.kv_lens[b]
+        drop = max(0, n - 1 - W) // P if W >= 0 else 0
+        pg = idx[int(kvp[b]) + drop:int(kvp[b + 1])]
+        pages.append(pg)
+        npg.append(len(pg))
+        lens.append(n - drop * P)
+        last.append(int(case.kv_last_page_len[b]))
+    pages = torch.cat(pages).long().to(case.k_cache.device)
+    kvp2 = torch.zeros(len(requests) + 1, dtype=torch.int32)
+    kvp2[1:] = torch.tensor(npg).cumsum(0)
+    return dataclasses.replace(
+        case, qo_lens=[1] * len(requests), kv_lens=lens,
+        q=case.q[torch.tensor(list(requests), device=case.q.device)].cpu(),
+        k_cache=case.k_cache.index_select(0, pages).cpu(),
+        v_cache=case.v_cache.index_select(0, pages).cpu(),
+        qo_indptr=torch.arange(len(requests) + 1, dtype=torch.int32), kv_indptr=kvp2,
+        kv_indices=torch.arange(int(kvp2[-1]), dtype=torch.int32),
+        kv_last_page_len=torch.tensor(last, dtype=torch.int32), window_left=W)
+
+
+def cpu_baseline(pre, dec, budget_s: float = 10.0) -> dict:
+    """The CPU oracle (fp64, query rows spread over the host cores it is given)
+    timed on every workload, each in that workload's unit: the whole 8-request
+    prefix prefill, the whole 64-request decode at W -1 and 1023, a sample of
+    the 32768-token prefill's query tokens (about budget_s seconds) and a sample
+    of the 256-request decode's requests.  The top-level value is the long
+    prefill sample, in the unit of the bench's value."""
     import numpy as np
 
     import oracle
+    from paged_kv_sliding_amd.synth import build_case
 
-    qcpu = case.q.cpu()
-    kc, vc = case.k_cache.cpu(), case.v_cache.cpu()
-    W = case.window_left
-    rng = np.random.default_rng(0)
-    rows, flops, elapsed = [], 0, 0.0
-    # sample query tokens past the window (full W+1 keys each), a few at a time
-    while elapsed < budget_s and len(rows) < 4096:
-        batch = rng.integers(W, case.qo_lens[0], size=4).tolist()
+    threads = oracle.default_threads()
+    per = {}
+
+    def timed(fn):
         t0 = time.perf_counter()
-        oracle.paged_attention(qcpu, kc, vc, case.qo_indptr, case.kv_indptr, case.kv_indices,
-                               case.kv_last_page_len, num_qo_heads=case.num_qo_heads,
-                               num_kv_heads=case.num_kv_heads, head_dim=case.head_dim,
-                               page_size=case.page_size, causal=True, window_left=W,
-                               sm_scale=case.sm_scale, rows=batch)
-        elapsed += time.perf_counter() - t0
-        rows += batch
-        flops += 4 * case.head_dim * case.num_qo_heads * (W + 1) * len(batch)
+        fn()
+        return time.perf_counter() - t0
+
+    c2 = build_case("prefix_prefill", device="cpu")
+    dt = timed(lambda: oracle.case_attention(c2, threads=threads))
+    per["prefix_prefill"] = {"value": round(prefill_flops(c2) / dt / 1e9, 3), "unit": "GFLOP/s",
+                             "seconds": round(dt, 3), "sample": "the whole 8-request batch"}
+    c3 = build_case("decode_sweep", device="cpu")
+    for W in (-1, 1023):
+        dt = timed(lambda: oracle.case_attention(c3, window_left=W, threads=threads))
+        per[f"decode_sweep_W{W}"] = {"value": round(decode_bytes(c3, W) / dt / 1e9, 3),
+                                     "unit": "GB/s (K/V read)", "seconds": round(dt, 3),
+                                     "sample": "all 64 requests"}
+    del c2, c3
+
+    # long prefill: query tokens past the window (W+1 keys each), a batch of
+    # 4 rows per thread at a time, until the budget is spent
+    qcpu, kc, vc = pre.q.cpu(), pre.k_cache.cpu(), pre.v_cache.cpu()
+    W = pre.window_left
+    rng = np.random.default_rng(0)
+    rows, flops, elapsed = 0, 0, 0.0
+    while elapsed < budget_s and rows < 32768:
+        batch = rng.integers(W, pre.qo_lens[0], size=4 * threads).tolist()
+        elapsed += timed(lambda: oracle.paged_attention(
+            qcpu, kc, vc, pre.qo_indptr, pre.kv_indptr, pre.kv_indices, pre.kv_last_page_len,
+            num_qo_heads=pre.num_qo_heads, num_kv_heads=pre.num_kv_heads,
+            head_dim=pre.head_dim, page_size=pre.page_size, causal=True, window_left=W,
+            sm_scale=pre.sm_scale, rows=batch, threads=threads))
+        rows += len(batch)
+        flops += 4 * pre.head_dim * pre.num_qo_heads * (W + 1) * len(batch)
+    del qcpu, kc, vc
+    long_rate = flops / elapsed
+    per["long_prefill"] = {"value": round(long_rate / 1e9, 3), "unit": "GFLOP/s",
+                           "seconds": round(elapsed, 3),
+                           "sample": f"{rows} query tokens (all {pre.num_qo_heads} heads, {W + 1} "
+                                     f"visible keys each) of the {pre.qo_lens[0]} tokens"}
+
+    # split decode, W = 4095: 4 requests per thread, only the pages each window reaches
+    Wd = dec.window_left
+    picks = sorted(np.random.default_rng(5).choice(dec.batch_size, size=min(dec.batch_size,
+                                                                              4 * threads),
+                                                   replace=False).tolist())
+    sub = window_sample(dec, picks, Wd)
+    dt = timed(lambda: oracle.case_attention(sub, threads=threads))
+    per[f"split_decode_W{Wd}"] = {"value": round(decode_bytes(sub, Wd) / dt / 1e9, 3),
+                                  "unit": "GB/s (K/V read)", "seconds": round(dt, 3),
+                                  "sample": f"{len(picks)} of the {dec.batch_size} requests"}
     return {
-        "value": flops / elapsed / 1e12,
+        "value": long_rate / 1e12,
         "unit": "TFLOP/s",
-        "cores": 1,
+        "cores": threads,
+        "cpu_model": cpu_model(),
         "kind": "oracle",
-        "sample": (f"{len(rows)} query tokens (all {case.num_qo_heads} heads, {W + 1} visible "
-                   f"keys each) of the 32768-token prefill, fp64 C oracle, one thread, "
-                   f"{elapsed:.1f} s"),
+        "sample": per["long_prefill"]["sample"] + f", fp64 C oracle, {threads} threads, "
+                                                  f"{elapsed:.1f} s",
+        "per_config": per,
     }
 
 
@@ -486,8 +621,9 @@ def main():
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--cpu-budget", type=float, default=15.0)
-    ap.add_argument("--only", choices=["prefill", "decode", "cascade", "pool", "sweep", "all"],
+    ap.add_argument("--cpu-budget", type=float, default=10.0)
+    ap.add_argument("--only", choices=["prefill", "decode", "cascade", "pool", "sweep", "merge",
+                                       "cpu", "all"],
                     default="all",
                     help="restrict the timed step (for profiling runs)")
     ap.add_argument("--profile-kernel", choices=["prefill", "decode", "copy"],
@@ -517,6 +653,13 @@ def main():
     if args.only == "sweep":
         print(json.dumps({"decode_sweep": bench_decode_sweep(args.steps)}), flush=True)
         return
+    if args.only == "merge":
+        import torch
+
+        buf = torch.empty(1 << 30, dtype=torch.uint8, device="cuda")
+        print(json.dumps({"merge_state": bench_merge_state(args.steps, lambda: buf.fill_(1))}),
+              flush=True)
+        return
 
     import torch
 
@@ -544,6 +687,9 @@ def main():
                                 fixed_split_size=dec.fixed_split_size,
                                 batch_capacity=dec.batch_size, kv_capacity=max(dec.kv_lens))
 
+    if args.only == "cpu":
+        print(json.dumps({"cpu_baseline": cpu_baseline(pre, dec, args.cpu_budget)}), flush=True)
+        return
     dec_att_w = dec_att(W_dec)
     dec_att_full = dec_att(-1)
     o_pre = torch.empty_like(pre.q)
@@ -556,20 +702,33 @@ def main():
     ev = {k: (torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
           for k in ("pre", "dec")}
     times = {"pre": [], "dec": []}
+    plan_us = {"pre": [], "dec": []}
+    # written before every timed decode launch: the 64-request decode's K/V
+    # (up to 0.6 GB) and part of the 4 GB split decode would otherwise be
+    # served from the 256 MB last-level cache
+    flush_buf = torch.empty(1 << 30, dtype=torch.uint8, device=dev)
+
+    def flush():
+        flush_buf.fill_(1)
 
     def step(record: bool):
         if args.only in ("prefill", "all"):
+            t0 = time.perf_counter()
             pre_att.plan(qo_indptr=pre_host[0], kv_indptr=pre_host[1],
                          kv_last_page_len=pre_host[2])
             if record:
+                plan_us["pre"].append((time.perf_counter() - t0) * 1e6)
                 ev["pre"][0].record()
             pre_att.run(pre.q, pre.k_cache, pre.v_cache, pre.kv_indices, sm_scale=pre.sm_scale,
                         window_left=pre.window_left, out=o_pre, lse=l_pre)
             if record:
                 ev["pre"][1].record()
         if args.only in ("decode", "all"):
+            flush()
+            t0 = time.perf_counter()
             dec_att_w.plan(kv_indptr=dec_host[0], kv_last_page_len=dec_host[1])
             if record:
+                plan_us["dec"].append((time.perf_counter() - t0) * 1e6)
                 ev["dec"][0].record()
             dec_att_w.run(dec.q, dec.k_cache, dec.v_cache, dec.kv_indices, sm_scale=dec.sm_scale,
                           window_left=W_dec, out=o_dec, lse=l_dec)
@@ -596,36 +755,32 @@ def main():
     res = {}
     flops = prefill_flops(pre)
     if times["pre"]:
-        pre_ms = sum(times["pre"]) / len(times["pre"])
-        tflops = flops / (pre_ms * 1e-3) / 1e12
-        res["pre"] = (pre_ms, tflops)
+        st = time_stats(times["pre"])
+        res["pre"] = (st, flops / (st["mean"] * 1e-3) / 1e12)
     if times["dec"]:
-        dec_ms = sum(times["dec"]) / len(times["dec"])
+        st = time_stats(times["dec"])
         nbytes = decode_bytes(dec, W_dec)
-        res["dec"] = (dec_ms, nbytes / (dec_ms * 1e-3) / 1e9, nbytes)
+        res["dec"] = (st, nbytes / (st["mean"] * 1e-3) / 1e9, nbytes)
 
     # the no-window decode of the same batch, timed apart (not part of the step)
     full = None
     fp8 = None
     if args.only == "all":
         print("bench: decode over an 8-bit cache", file=sys.stderr, flush=True)
-        fp8 = bench_decode_fp8(dec, W_dec, max(5, args.steps // 2))
+        fp8 = bench_decode_fp8(dec, W_dec, max(5, args.steps // 2), flush)
         dec_att_full.plan(kv_indptr=dec_host[0], kv_last_page_len=dec_host[1])
+
+        def run_full():
+            dec_att_full.run(dec.q, dec.k_cache, dec.v_cache, dec.kv_indices,
+                             sm_scale=dec.sm_scale, window_left=-1, out=o_dec, lse=l_dec)
+
         for _ in range(2):
-            dec_att_full.run(dec.q, dec.k_cache, dec.v_cache, dec.kv_indices,
-                             sm_scale=dec.sm_scale, window_left=-1, out=o_dec, lse=l_dec)
-        ts = []
-        for _ in range(max(3, args.steps // 2)):
-            a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-            a.record()
-            dec_att_full.run(dec.q, dec.k_cache, dec.v_cache, dec.kv_indices,
-                             sm_scale=dec.sm_scale, window_left=-1, out=o_dec, lse=l_dec)
-            b.record()
-            torch.cuda.synchronize()
-            ts.append(a.elapsed_time(b))
-        ms = sum(ts) / len(ts)
+            run_full()
+        st = time_stats(timed_launches(run_full, max(3, args.steps // 2), flush))
+        ms = st["mean"]
         nb = decode_bytes(dec, -1)
         full = {"value": nb / (ms * 1e-3) / 1e9, "unit": "GB/s", "ms": round(ms, 4),
+                "ms_median": round(st["median"], 4), "ms_min": round(st["min"], 4),
                 "kv_bytes": nb, "frac_of_hbm_peak": nb / (ms * 1e-3) / 1e9 / PEAK_HBM_GBPS}
 
     line = {
@@ -653,8 +808,11 @@ def main():
         },
     }
     if "pre" in res:
-        pre_ms, tflops = res["pre"]
+        st, tflops = res["pre"]
+        pre_ms = st["mean"]
         line["prefill_ms"] = round(pre_ms, 4)
+        line["prefill_ms_median"] = round(st["median"], 4)
+        line["prefill_ms_min"] = round(st["min"], 4)
         line["roofline"] = {"bound": "mfma", "achieved": round(tflops, 2),
                             "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
                             "frac": round(tflops / PEAK_BF16_TFLOPS, 4),
@@ -663,9 +821,10 @@ def main():
                             "kernel": PREFILL_KERNEL + ">",
                             "work_per_launch": flops}
     if "dec" in res:
-        dec_ms, gbps, nbytes = res["dec"]
-        line["decode"] = {"value": round(gbps, 1), "unit": "GB/s", "ms": round(dec_ms, 4),
-                          "kv_bytes": nbytes}
+        st, gbps, nbytes = res["dec"]
+        line["decode"] = {"value": round(gbps, 1), "unit": "GB/s", "ms": round(st["mean"], 4),
+                          "ms_median": round(st["median"], 4), "ms_min": round(st["min"], 4),
+                          "kv_bytes": nbytes, "llc_flushed": True}
         line["roofline_decode"] = {"bound": "hbm", "achieved": round(gbps, 1),
                                    "peak": PEAK_HBM_GBPS, "unit": "GB/s",
                                    "frac": round(gbps / PEAK_HBM_GBPS, 4),
@@ -673,6 +832,9 @@ def main():
                                                            "decode_merge_kernel<128>"),
                                    "kernel": "decode_kernel<128> + decode_merge_kernel<128>",
                                    "work_per_launch": nbytes}
+    line["plan_host_us"] = {k2: round(time_stats(v)["median"], 1)
+                            for k2, v in (("prefill", plan_us["pre"]), ("decode", plan_us["dec"]))
+                            if v}
     if full is not None:
         line["decode_no_window"] = full
     if fp8 is not None:
@@ -684,9 +846,11 @@ def main():
         line["cascade"] = bench_cascade(max(5, args.steps // 2))
         print("bench: cache writes and page-table build", file=sys.stderr, flush=True)
         line["pool"] = bench_pool(max(5, args.steps // 2))
+        print("bench: merge_state", file=sys.stderr, flush=True)
+        line["merge_state"] = bench_merge_state(max(5, args.steps // 2), flush)
     if not args.no_cpu_baseline and args.only == "all":
         print("bench: cpu baseline (oracle)", file=sys.stderr, flush=True)
-        line["cpu_baseline"] = cpu_baseline(pre, args.cpu_budget)
+        line["cpu_baseline"] = cpu_baseline(pre, dec, args.cpu_budget)
     print(json.dumps(line), flush=True)
 
 

@@ -7,6 +7,8 @@
 // count never enters the block shape (the failure mode the same sglang
 // function works around: a block of head_dim/vec x num_heads threads exceeds
 // the per-block thread limit for large head counts).
+#include <type_traits>
+
 #include "device_common.h"
 #include "pkvs_internal.h"
 
@@ -74,7 +76,115 @@ __global__ __launch_bounds__(kMergeThreads) void merge_state_kernel(
     }
 }
 
+// The same combine with 16 bytes of v per lane (8 16-bit or 4 fp32 elements):
+// lane c of the grid-stride loop takes 16-byte chunk c of the flattened
+// [units, head_dim] arrays, chunk c belongs to unit c >> log2_cpu.  The host
+// picks this kernel only when a unit is a power-of-two number of chunks, at
+// most 64, so every unit lies within one wave: all its lanes read s_a / s_b
+// before its first lane stores s, which keeps in-place use (s_out = s_a) safe.
+template <typename T>
+__device__ __forceinline__ void widen16(u32x4 x, float (&f)[16 / sizeof(T)])
+{
+    if constexpr (sizeof(T) == 4) {
+#pragma unroll
+        for (int j = 0; j < 4; ++j) f[j] = __uint_as_float(x[j]);
+    } else if constexpr (std::is_same<T, _Float16>::value) {
+        const f32x8 v = __builtin_convertvector(__builtin_bit_cast(f16x8, x), f32x8);
+#pragma unroll
+        for (int j = 0; j < 8; ++j) f[j] = v[j];
+    } else {
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            f[2 * j] = __uint_as_float(x[j] << 16);
+            f[2 * j + 1] = __uint_as_float(x[j] & 0xffff0000u);
+        }
+    }
+}
+
+template <typename T>
+__device__ __forceinline__ u32x4 narrow16(const float (&f)[16 / sizeof(T)])
+{
+    if constexpr (sizeof(T) == 4) {
+        u32x4 x;
+#pragma unroll
+        for (int j = 0; j < 4; ++j) x[j] = __float_as_uint(f[j]);
+        return x;
+    } else {
+        f32x8 v;
+#pragma unroll
+        for (int j = 0; j < 8; ++j) v[j] = f[j];
+        return __builtin_bit_cast(u32x4, to16x8<std::is_same<T, _Float16>::value>(v));
+    }
+}
+
+template <typename T>
+__global__ __launch_bounds__(kMergeVecThreads) void merge_state_vec_kernel(
+    const u32x4 *va, const float *sa, const u32x4 *vb, const float *sb, u32x4 *vo, float *so,
+    int64_t chunks, int log2_cpu)
+{
+    constexpr int E = 16 / sizeof(T);
+    constexpr float kLog2e = 1.44269504088896340736f;
+    const int64_t stride = int64_t(gridDim.x) * kMergeVecThreads;
+    for (int64_t c = int64_t(blockIdx.x) * kMergeVecThreads + threadIdx.x; c < chunks;
+         c += stride) {
+        const int64_t u = c >> log2_cpu;
+        const float a = sa[u], b = sb[u];
+        const u32x4 xa = __builtin_nontemporal_load(va + c);
+        const u32x4 xb = __builtin_nontemporal_load(vb + c);
+        const float M = fmaxf(a, b);
+        float wa = 0.f, wb = 0.f, s = kNegInf;
+        if (M != kNegInf) {
+            const float ea = fast_exp2((a - M) * kLog2e), eb = fast_exp2((b - M) * kLog2e);
+            const float sum = ea + eb;
+            s = M + fast_log2(sum) * kLn2;
+            wa = ea / sum;
+            wb = eb / sum;
+        }
+        float fa[E], fb[E], fo[E];
+        widen16<T>(xa, fa);
+        widen16<T>(xb, fb);
+        // (a partial with weight 0 contributes nothing, whatever its v holds)
+#pragma unroll
+        for (int j = 0; j < E; ++j)
+            fo[j] = (wa != 0.f ? wa * fa[j] : 0.f) + (wb != 0.f ? wb * fb[j] : 0.f);
+        __builtin_nontemporal_store(narrow16<T>(fo), vo + c);
+        if ((c & ((int64_t(1) << log2_cpu) - 1)) == 0) so[u] = s;
+    }
+}
+
 }  // namespace
+
+int merge_state_vec_chunks(int32_t head_dim, int32_t dtype)
+{
+    const int bytes = head_dim * (dtype == PKVS_FP32 ? 4 : 2);
+    if (bytes % 16) return 0;
+    const int cpu = bytes / 16;
+    return (cpu & (cpu - 1)) == 0 && cpu <= 64 ? cpu : 0;
+}
+
+hipError_t launch_merge_state_vec(const void *va, const float *sa, const void *vb,
+                                  const float *sb, void *vo, float *so, int64_t n, int32_t heads,
+                                  int32_t head_dim, int32_t dtype, int grid, hipStream_t s)
+{
+    const int cpu = merge_state_vec_chunks(head_dim, dtype);
+    const int64_t chunks = n * heads * cpu;
+    if (chunks == 0) return hipSuccess;
+    int log2_cpu = 0;
+    while ((1 << log2_cpu) < cpu) ++log2_cpu;
+    const auto *a = static_cast<const u32x4 *>(va);
+    const auto *b = static_cast<const u32x4 *>(vb);
+    auto *o = static_cast<u32x4 *>(vo);
+    if (dtype == PKVS_FP16)
+        merge_state_vec_kernel<_Float16><<<grid, kMergeVecThreads, 0, s>>>(a, sa, b, sb, o, so,
+                                                                          chunks, log2_cpu);
+    else if (dtype == PKVS_BF16)
+        merge_state_vec_kernel<uint16_t><<<grid, kMergeVecThreads, 0, s>>>(a, sa, b, sb, o, so,
+                                                                          chunks, log2_cpu);
+    else
+        merge_state_vec_kernel<float><<<grid, kMergeVecThreads, 0, s>>>(a, sa, b, sb, o, so,
+                                                                       chunks, log2_cpu);
+    return hipGetLastError();
+}
 
 hipError_t launch_merge_state(const void *va, const float *sa, const void *vb, const float *sb,
                               void *vo, float *so, int64_t n, int32_t heads, int32_t head_dim,

@@ -89,6 +89,7 @@ constexpr int kGenericThreads = 256;
 constexpr int kDecodeBlock = 32;       // keys per decode step
 constexpr int kDecodeThreads = 64;     // threads per wave of a decode work item
 constexpr int kMergeThreads = 64;
+constexpr int kMergeVecThreads = 256;  // merge_state, 16 bytes of v per lane
 constexpr int kAppendThreads = 256;    // cache writes: threads per workgroup (max)
 constexpr int kIndptrThreads = 1024;   // page-table build: the running-sum workgroup
 constexpr int kGatherThreads = 256;    // page-table build: threads per request
@@ -142,6 +143,13 @@ hipError_t launch_decode_merge(const DecodeArgs &a, int head_dim, bool f16, int 
 hipError_t launch_merge_state(const void *va, const float *sa, const void *vb, const float *sb,
                               void *vo, float *so, int64_t n, int32_t heads, int32_t head_dim,
                               int32_t dtype, int grid, hipStream_t s);
+// 16 bytes per lane: usable when one (token, head) unit of v is a power of two
+// of 16-byte chunks, at most 64 (merge_state_vec_chunks > 0) and every v
+// pointer is 16-byte aligned; grid in workgroups of kMergeVecThreads
+int merge_state_vec_chunks(int32_t head_dim, int32_t dtype);
+hipError_t launch_merge_state_vec(const void *va, const float *sa, const void *vb,
+                                  const float *sb, void *vo, float *so, int64_t n, int32_t heads,
+                                  int32_t head_dim, int32_t dtype, int grid, hipStream_t s);
 
 // Cache writes and page-table build (pool.hip).
 hipError_t launch_append_kv(const void *k_new, const void *v_new, const int64_t *loc, int64_t n,

@@ -246,10 +246,16 @@ int pkvs_decode_run(const pkvs_plan *p, const void *q, const void *k_cache, cons
     e = launch_decode_16bit(a, p->desc.head_dim, f16, p->desc.kv_format, p->decode_waves,
                             p->grid_blocks, stream);
     if (e != hipSuccess) return fail(PKVS_ERR_HIP, "decode launch: %s", hipGetErrorString(e));
-    if (p->merges_cap > 0) {
-        // launched whenever the plan can have merges (the kernel reads their
-        // count), with a fixed grid sized from the capacity, never from this
-        // batch: a captured graph stays valid for every later plan
+    // The merge of split requests' chunk partials.  Under stream capture it is
+    // launched whenever the plan can have merges (the kernel reads their
+    // count), with a fixed grid sized from the capacity, never from this
+    // batch, so a captured graph stays valid for every later plan; an eager
+    // run whose planned batch split no request skips it.
+    hipStreamCaptureStatus capture = hipStreamCaptureStatusNone;
+    if (p->merges_cap > 0 && p->n_merges == 0 &&
+        hipStreamIsCapturing(stream, &capture) != hipSuccess)
+        return fail(PKVS_ERR_HIP, "hipStreamIsCapturing failed");
+    if (p->merges_cap > 0 && (p->n_merges > 0 || capture != hipStreamCaptureStatusNone)) {
         const int grid = int(std::min<int64_t>(p->merges_cap * group, int64_t(p->num_cus) * 16));
         e = launch_decode_merge(a, p->desc.head_dim, f16, std::max(grid, 1), stream);
         if (e != hipSuccess)
@@ -272,9 +278,23 @@ int pkvs_merge_state(const void *v_a, const float *s_a, const void *v_b, const f
     if (!v_a || !s_a || !v_b || !s_b || !v_out || !s_out)
         return fail(PKVS_ERR_INVALID_ARG, "null pointer");
     const int64_t units = num_tokens * num_heads;
-    const int grid = int(std::min<int64_t>(units, int64_t(device_cus()) * 32));
-    hipError_t e = launch_merge_state(v_a, s_a, v_b, s_b, v_out, s_out, num_tokens, num_heads,
-                                      head_dim, v_dtype, grid, stream);
+    hipError_t e;
+    const int cpu = merge_state_vec_chunks(head_dim, v_dtype);
+    const bool aligned = (reinterpret_cast<uintptr_t>(v_a) | reinterpret_cast<uintptr_t>(v_b) |
+                          reinterpret_cast<uintptr_t>(v_out)) % 16 == 0;
+    if (cpu > 0 && aligned) {
+        // 16 bytes per lane; about eight resident workgroups per CU keep
+        // enough loads in flight to stream at the HBM rate
+        const int64_t chunks = units * cpu;
+        const int grid = int(std::min<int64_t>((chunks + kMergeVecThreads - 1) / kMergeVecThreads,
+                                               int64_t(device_cus()) * 8));
+        e = launch_merge_state_vec(v_a, s_a, v_b, s_b, v_out, s_out, num_tokens, num_heads,
+                                   head_dim, v_dtype, grid, stream);
+    } else {
+        const int grid = int(std::min<int64_t>(units, int64_t(device_cus()) * 32));
+        e = launch_merge_state(v_a, s_a, v_b, s_b, v_out, s_out, num_tokens, num_heads, head_dim,
+                               v_dtype, grid, stream);
+    }
     if (e != hipSuccess) return fail(PKVS_ERR_HIP, "merge_state launch: %s", hipGetErrorString(e));
     return PKVS_OK;
 }

@@ -382,16 +382,22 @@ def _sub_layout(case, picks):
             torch.tensor(kv_ind, **i32), torch.tensor(last, **i32))
 
 
-@pytest.mark.parametrize("decode,nw", [(False, 0), (True, 1), (True, 4)])
-def test_graph_replay_follows_replans(decode, nw):
+@pytest.mark.parametrize("decode,nw,split", [(False, 0, -1), (True, 1, 64), (True, 4, 64),
+                                              (True, 1, -1)])
+def test_graph_replay_follows_replans(decode, nw, split):
     """run() captured once in a HIP graph stays valid for every later plan() of
     the same capacities (AMD-Ecosystem/flashinfer PR 234, "Why each fix" 2: the
     grid and the launch set come from the capacities, the work from the
     workspace).  Each replay, with eager work and synchronisations between
     replays, must equal an eager run() of the batch planned last, bit for bit."""
     if decode:
+        # split = -1: the planner's choice; the first planned batch (request 2
+        # alone, 77 keys) splits nothing, the later ones split their long
+        # requests, so the graph must hold the merge launch an eager run of
+        # the first batch skips
         qo, kv = [1] * 6, [300, 1, 77, 2000, 64, 900]
-        case = small(qo, kv, H_q=16, H_kv=2, D=128, P_=16, W=255, seed=61, decode=True, split=64)
+        case = small(qo, kv, H_q=16, H_kv=2, D=128, P_=16, W=-1 if split < 0 else 255, seed=61,
+                     decode=True, split=split)
     else:
         qo, kv = [40, 1, 130, 7, 64], [300, 1, 130, 500, 64]
         case = small(qo, kv, H_q=8, H_kv=2, D=128, P_=16, W=100, seed=62)
@@ -424,8 +430,12 @@ def test_graph_replay_follows_replans(decode, nw):
 
     layouts = [_sub_layout(case, list(range(B))), _sub_layout(case, [2]),
                _sub_layout(case, [0, 3, 4]), _sub_layout(case, list(range(B)))]
+    if decode and split < 0:
+        layouts = [_sub_layout(case, [2])] + layouts
     load(layouts[0])
     plan(layouts[0])
+    if decode and split < 0:
+        assert att.info().num_merges == 0
     side = torch.cuda.Stream()
     side.wait_stream(torch.cuda.current_stream())
     with torch.cuda.stream(side):
@@ -452,9 +462,11 @@ def test_graph_replay_follows_replans(decode, nw):
             assert torch.isfinite(junk).all()
             assert torch.equal(o_buf[:n], want_o), (k, rep)
             assert torch.equal(l_buf[:n], want_l), (k, rep)
-        if k == 0:
+        if decode and split < 0 and len(layout[0]) == B:
+            assert att.info().num_merges > 0
+        if len(layout[0]) == B:
             ro, rl = oracle_for(case)
-            compare(want_o, want_l, ro, rl, tag=f"graph decode={decode} nw={nw}")
+            compare(want_o, want_l, ro, rl, tag=f"graph decode={decode} nw={nw} split={split}")
 
 
 def _layout_case(case, picks):
@@ -558,18 +570,30 @@ def test_run_rejects_mismatched_window_on_gpu():
 
 
 @pytest.mark.parametrize("dtype", [torch.bfloat16, torch.float32, torch.float16])
-@pytest.mark.parametrize("H,D", [(64, 128), (128, 64), (128, 256), (8, 96)])
-def test_merge_state_against_oracle(dtype, H, D):
-    g = torch.Generator(device=DEV).manual_seed(H * D)
-    n = 37
+@pytest.mark.parametrize("H,D,n", [(64, 128, 37), (128, 64, 37), (128, 256, 37), (8, 96, 37),
+                                   (64, 128, 3001), (32, 64, 4099)])
+def test_merge_state_against_oracle(dtype, H, D, n):
+    """merge_state against the oracle (16 bytes per lane where a (token, head)
+    row is a power of two of 16-byte chunks, one wave per row otherwise), into
+    NaN-filled outputs; a partial whose LSE is -inf contributes nothing even
+    when its values are NaN; in place equals out of place."""
+    g = torch.Generator(device=DEV).manual_seed(H * D + n)
     va = torch.randn(n, H, D, generator=g, device=DEV).to(dtype)
     vb = torch.randn(n, H, D, generator=g, device=DEV).to(dtype)
     sa = torch.randn(n, H, generator=g, device=DEV) * 5
     sb = torch.randn(n, H, generator=g, device=DEV) * 5
     sa[0, :3] = float("-inf")
     sb[0, 1:4] = float("-inf")
-    v, s = P.pkvs_merge_state(va, sa, vb, sb)
+    va[0, :3] = float("nan")
+    vb[0, 1:4] = float("nan")
+    v = torch.full_like(va, float("nan"))
+    s = torch.full_like(sa, float("nan"))
+    P.pkvs_merge_state(va, sa, vb, sb, v_out=v, s_out=s)
     torch.cuda.synchronize()
+    va = va.clone()
+    vb = vb.clone()
+    va[0, :3] = 0
+    vb[0, 1:4] = 0
     rv, rs = oracle.merge_state(va.double().cpu().numpy(), sa.double().cpu().numpy(),
                                 vb.double().cpu().numpy(), sb.double().cpu().numpy())
     compare(v, s, rv, rs, tag=f"merge {dtype} H={H} D={D}")
@@ -579,6 +603,20 @@ def test_merge_state_against_oracle(dtype, H, D):
     P.pkvs_merge_state(va2, sa2, vb, sb, v_out=va2, s_out=sa2)
     torch.cuda.synchronize()
     assert torch.equal(va2, v) and torch.equal(sa2, s)
+    # v not 16-byte aligned: the one-wave-per-row kernel, same arithmetic
+    off = 16 // va.element_size() - 1 if va.element_size() < 16 else 0
+    if off:
+        def shifted(t):
+            buf = torch.empty(t.numel() + off, dtype=t.dtype, device=DEV)
+            view = buf[off:].view(t.shape)
+            view.copy_(t)
+            return view
+        va3, vb3 = shifted(va), shifted(vb)
+        v3 = shifted(torch.full_like(v, float("nan")))
+        s3 = torch.full_like(s, float("nan"))
+        P.pkvs_merge_state(va3, sa, vb3, sb, v_out=v3, s_out=s3)
+        torch.cuda.synchronize()
+        assert torch.equal(v3, v) and torch.equal(s3, s)
 
 
 def test_merge_state_of_prefill_split_equals_unsplit():
