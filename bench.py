@@ -57,6 +57,7 @@ PEAK_HBM_GBPS = 8000.0      # MI355X HBM3E
 # the kernel the 32k-token prefill runs (the planner's choice for head_dim 128,
 # bf16), as rocprofv3 names it, without the closing bracket
 PREFILL_KERNEL = "prefill_big_kernel<false"
+kXCDS = 8                   # XCDs of an MI355X (GRBM counters are summed over them)
 
 
 def prefill_flops(case) -> int:
@@ -494,6 +495,97 @@ def ingest_counters(d: str) -> None:
     print(json.dumps(res, indent=1))
 
 
+# rocprofv3 --pmc passes for the prefill kernel's execution counters (each
+# within one pass's limits: at most 8 SQ and 2 GRBM counters)
+PREFILL_COUNTER_PASSES = {
+    "issue": ["SQ_WAVES", "SQ_BUSY_CYCLES", "SQ_WAVE_CYCLES", "SQ_WAIT_ANY", "SQ_WAIT_INST_ANY",
+              "SQ_WAIT_INST_LDS", "SQ_ACTIVE_INST_ANY", "SQ_LDS_CMD_FIFO_FULL", "GRBM_GUI_ACTIVE",
+              "GRBM_COUNT"],
+    "insts": ["SQ_INSTS_VALU", "SQ_INSTS_MFMA", "SQ_INSTS_LDS", "SQ_INSTS_SALU",
+              "SQ_VALU_MFMA_BUSY_CYCLES", "SQ_VALU_MFMA_COEXEC_CYCLES", "SQ_ACTIVE_INST_VALU",
+              "SQ_ACTIVE_INST_LDS", "GRBM_GUI_ACTIVE"],
+    "lds": ["SQ_INSTS_VALU_TRANS_F32", "SQ_LDS_DATA_FIFO_FULL", "SQ_LDS_BANK_CONFLICT",
+            "SQ_INST_LEVEL_LDS", "SQ_BUSY_CU_CYCLES", "SQ_ACTIVE_INST_SCA", "SQ_INSTS_SMEM",
+            "SQ_INSTS_VMEM", "GRBM_GUI_ACTIVE"],
+}
+
+
+def summarize_prefill_counters(d: str, out_md: str) -> None:
+    """Turn the PREFILL_COUNTER_PASSES runs under `d` (one rocprofv3 --pmc run
+    of `bench.py --profile-kernel prefill` per pass, in d/<pass>/p_*) into a
+    markdown summary of the prefill kernel's per-launch counters."""
+    import glob
+
+    digest = source_digest()
+    for out in glob.glob(os.path.join(d, "*.out")):
+        for ln in open(out):
+            if ln.startswith("source_digest=") and ln.strip().split("=")[1] != digest:
+                sys.exit(f"summarize: {out} was taken on other kernel sources")
+    vals, n_disp = {}, None
+    for pas, ctrs in PREFILL_COUNTER_PASSES.items():
+        path = os.path.join(d, pas, "p_counter_collection.csv")
+        for ctr in ctrs:
+            means, counts = _counter_means(path, ctr)
+            names = [k for k in means if PREFILL_KERNEL in k]
+            if len(names) != 1:
+                sys.exit(f"summarize: {ctr}: expected one prefill kernel in {path}, got {names}")
+            vals.setdefault(ctr, means[names[0]])
+            n_disp = counts[names[0]]
+    props = {}
+    try:
+        import torch
+
+        pr = torch.cuda.get_device_properties(0)
+        props = {"cus": pr.multi_processor_count}
+    except Exception:
+        pass
+    cus = props.get("cus", 256)
+    simds = 4 * cus
+    xcd_cycles = vals["GRBM_GUI_ACTIVE"] / kXCDS
+    mfma = vals["SQ_INSTS_MFMA"]
+    rows = [
+        ("launches measured (mean per launch below)", f"{n_disp}"),
+        ("GRBM_GUI_ACTIVE / 8 (GPU cycles of one XCD)", f"{xcd_cycles:,.0f}"),
+        ("MFMA busy: SQ_VALU_MFMA_BUSY_CYCLES / (SIMDs x XCD cycles)",
+         f"{vals['SQ_VALU_MFMA_BUSY_CYCLES'] / (simds * xcd_cycles):.3f}"),
+        ("VALU and MFMA co-issued: SQ_VALU_MFMA_COEXEC_CYCLES / SQ_VALU_MFMA_BUSY_CYCLES",
+         f"{vals['SQ_VALU_MFMA_COEXEC_CYCLES'] / vals['SQ_VALU_MFMA_BUSY_CYCLES']:.3f}"),
+        ("SQ_INSTS_MFMA", f"{mfma:,.0f}"),
+        ("SQ_INSTS_VALU (MFMA included) / SQ_INSTS_MFMA",
+         f"{vals['SQ_INSTS_VALU'] / mfma:.2f}"),
+        ("(SQ_INSTS_VALU - SQ_INSTS_MFMA) / SQ_INSTS_MFMA",
+         f"{(vals['SQ_INSTS_VALU'] - mfma) / mfma:.2f}"),
+        ("SQ_INSTS_VALU_TRANS_F32 / SQ_INSTS_MFMA",
+         f"{vals['SQ_INSTS_VALU_TRANS_F32'] / mfma:.2f}"),
+        ("SQ_INSTS_LDS / SQ_INSTS_MFMA", f"{vals['SQ_INSTS_LDS'] / mfma:.2f}"),
+        ("SQ_INSTS_SALU / SQ_INSTS_MFMA", f"{vals['SQ_INSTS_SALU'] / mfma:.2f}"),
+        ("SQ_WAIT_INST_LDS / SQ_WAVE_CYCLES",
+         f"{vals['SQ_WAIT_INST_LDS'] / vals['SQ_WAVE_CYCLES']:.3f}"),
+        ("SQ_WAIT_ANY / SQ_WAVE_CYCLES", f"{vals['SQ_WAIT_ANY'] / vals['SQ_WAVE_CYCLES']:.3f}"),
+        ("SQ_ACTIVE_INST_LDS / SQ_WAVE_CYCLES",
+         f"{vals['SQ_ACTIVE_INST_LDS'] / vals['SQ_WAVE_CYCLES']:.3f}"),
+        ("SQ_LDS_CMD_FIFO_FULL", f"{vals['SQ_LDS_CMD_FIFO_FULL']:,.0f}"),
+        ("SQ_LDS_DATA_FIFO_FULL", f"{vals['SQ_LDS_DATA_FIFO_FULL']:,.0f}"),
+        ("SQ_LDS_BANK_CONFLICT", f"{vals['SQ_LDS_BANK_CONFLICT']:,.0f}"),
+    ]
+    lines = [f"# Execution counters: `{PREFILL_KERNEL}>` on the 32768-token prefill", "",
+             "Workload: one request, 32768 query tokens, no prefix, window_left 4095, "
+             "32 query / 8 KV heads, head_dim 128, page_size 16, bf16.",
+             f"Kernel sources at digest `{digest}`.  Device: {cus} CUs, {simds} SIMDs.", "",
+             "Commands (from the repository root, on the GPU box; one pass per run):", "", "```"]
+    for pas, ctrs in PREFILL_COUNTER_PASSES.items():
+        lines.append(f"rocprofv3 --pmc {' '.join(ctrs)} -d <dir>/{pas} -o p --output-format csv "
+                     f"-- python3 bench.py --profile-kernel prefill --reps 5")
+    lines += [f"python3 bench.py --summarize-counters <dir>", "```", "",
+              "| quantity | per launch |", "|---|---|"]
+    lines += [f"| {k} | {v} |" for k, v in rows]
+    lines += ["", "Raw means per launch:", "", "| counter | value |", "|---|---|"]
+    lines += [f"| {k} | {v:,.0f} |" for k, v in sorted(vals.items())]
+    with open(out_md, "w") as f:
+        f.write("\n".join(lines) + "\n")
+    print("\n".join(lines))
+
+
 def cpu_model() -> str:
     try:
         with open("/proc/cpuinfo") as f:
@@ -629,11 +721,20 @@ def main():
     ap.add_argument("--profile-kernel", choices=["prefill", "decode", "copy"],
                     help="launch only this kernel --reps times (rocprofv3 counter passes)")
     ap.add_argument("--reps", type=int, default=5)
+    ap.add_argument("--prefill-variant", type=int, default=0,
+                    help="prefill kernel variant of the long prefill (0: the planner's choice)")
     ap.add_argument("--ingest-counters", metavar="DIR",
                     help="write profiles/traffic.json from FETCH_SIZE/WRITE_SIZE passes in DIR")
+    ap.add_argument("--summarize-counters", metavar="DIR",
+                    help="write profiles/prefill_counters.md from the PREFILL_COUNTER_PASSES "
+                         "runs in DIR")
     args = ap.parse_args()
     if args.ingest_counters:
         ingest_counters(args.ingest_counters)
+        return
+    if args.summarize_counters:
+        summarize_prefill_counters(args.summarize_counters,
+                                   os.path.join(ROOT, "profiles", "prefill_counters.md"))
         return
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py: this build measures one GPU only; multi-GPU sharding is a design "
@@ -678,7 +779,8 @@ def main():
                                num_kv_heads=pre.num_kv_heads, head_dim=pre.head_dim,
                                page_size=pre.page_size, dtype=pre.dtype,
                                window_left=pre.window_left, batch_capacity=1,
-                               qo_capacity=pre.qo_lens[0], kv_capacity=pre.kv_lens[0])
+                               qo_capacity=pre.qo_lens[0], kv_capacity=pre.kv_lens[0],
+                               prefill_variant=args.prefill_variant)
 
     def dec_att(W):
         return P.BatchAttention(P.PKVS_DECODE, num_qo_heads=dec.num_qo_heads,
@@ -813,6 +915,7 @@ def main():
         line["prefill_ms"] = round(pre_ms, 4)
         line["prefill_ms_median"] = round(st["median"], 4)
         line["prefill_ms_min"] = round(st["min"], 4)
+        line["prefill_variant"] = pre_att.info().prefill_variant
         line["roofline"] = {"bound": "mfma", "achieved": round(tflops, 2),
                             "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
                             "frac": round(tflops / PEAK_BF16_TFLOPS, 4),

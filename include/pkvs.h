@@ -110,7 +110,8 @@ typedef enum pkvs_kind { PKVS_PREFILL = 0, PKVS_DECODE = 1, PKVS_CASCADE = 2 } p
  *                   3 = 4 waves x 64 rows, software-pipelined (2 and 3: head_dim
  *                   <= 128), 4 = 8 waves x 32 rows with K/V rows loaded straight
  *                   into LDS, 5 = as 4 with 64-key steps and 16-byte loads
- *                   into a chunk-permuted LDS layout (4 and 5: head_dim 128,
+ *                   into a chunk-permuted LDS layout, 6 = as 5 with 4 waves
+ *                   x 32 rows and two workgroups per CU (4, 5 and 6: head_dim 128,
  *                   16-bit K/V; they hold an item's page ids in a 2048-entry
  *                   LDS table, so a plan whose capacities let one item span
  *                   more pages -- (kv_capacity - 1) / page_size + 1, or with

@@ -75,6 +75,9 @@ enum PrefillVariant {
                           // kPrefillDmaPages pages)
     kPrefillBig = 5,      // as 4 with 64-key steps and 16-byte loads into an
                           // XOR-swizzled unpadded LDS layout
+    kPrefillDuo = 6,      // as 5 with 4 waves x 32 rows, two workgroups per CU
+                          // (K and V in two-tile rings, a page table sized
+                          // from the plan)
 };
 constexpr int kPrefillBigTile = 64;    // keys per step of kPrefillBig
 constexpr int kPrefillDmaPages = 2048;
@@ -112,6 +115,7 @@ struct PrefillArgs {
     // with it (merge_state folded into the epilogue)
     const void *fold_o;
     const float *fold_lse;
+    int32_t table_pages;  // kPrefillDuo: entries of its LDS page table (dynamic LDS)
 };
 
 struct DecodeArgs {
@@ -165,7 +169,11 @@ hipError_t launch_build_kv_indices(const int32_t *map, int64_t map_rows, int64_t
                                    int64_t capacity, int32_t *status, int grid, hipStream_t s);
 
 // Resident workgroups per CU of each kernel (occupancy query; 0 if unknown).
-int prefill_blocks_per_cu(int head_dim, int variant, bool f16, int kv_format);
+// (table_pages: the page-table entries of a kPrefillDuo launch)
+int prefill_blocks_per_cu(int head_dim, int variant, bool f16, int kv_format,
+                          int table_pages = kPrefillDmaPages);
+// dynamic LDS bytes of a kPrefillDuo launch with a page table of table_pages entries
+size_t prefill_duo_lds_bytes(int table_pages);
 int decode_blocks_per_cu(int head_dim, bool f16, int kv_format, int waves);
 
 }  // namespace pkvs

@@ -137,7 +137,7 @@ static int validate_desc(const pkvs_desc *d)
         return fail(PKVS_ERR_UNSUPPORTED, "8-bit K/V are built for bf16 and fp16 queries");
     if (d->kv_format != PKVS_KV_SAME &&
         (d->prefill_variant == kPrefillWide || d->prefill_variant == kPrefillDma ||
-         d->prefill_variant == kPrefillBig))
+         d->prefill_variant == kPrefillBig || d->prefill_variant == kPrefillDuo))
         return fail(PKVS_ERR_UNSUPPORTED, "8-bit K/V are widened on the register-staged prefill "
                     "variants (1, 2)");
     if (d->window_left < -1)
@@ -152,11 +152,12 @@ static int validate_desc(const pkvs_desc *d)
     if (d->decode_waves != 0 && d->decode_waves != 1 && d->decode_waves != 4)
         return fail(PKVS_ERR_INVALID_ARG, "decode_waves %d must be 0 (planner's choice), 1 or 4",
                     d->decode_waves);
-    if (d->prefill_variant < 0 || d->prefill_variant > 5)
-        return fail(PKVS_ERR_INVALID_ARG, "prefill_variant %d must be 0..5", d->prefill_variant);
+    if (d->prefill_variant < 0 || d->prefill_variant > 6)
+        return fail(PKVS_ERR_INVALID_ARG, "prefill_variant %d must be 0..6", d->prefill_variant);
     if (d->prefill_variant > 1 && d->head_dim > 128)
         return fail(PKVS_ERR_UNSUPPORTED, "256-row prefill variants are built for head_dim <= 128");
-    if ((d->prefill_variant == kPrefillDma || d->prefill_variant == kPrefillBig) &&
+    if ((d->prefill_variant == kPrefillDma || d->prefill_variant == kPrefillBig ||
+         d->prefill_variant == kPrefillDuo) &&
         d->head_dim != 128)
         return fail(PKVS_ERR_UNSUPPORTED, "the direct-to-LDS prefill variants are built for "
                     "head_dim 128");
@@ -227,7 +228,9 @@ static int build_prefill(Plan *p, const std::vector<Req> &reqs)
 {
     const pkvs_desc &d = p->desc;
     const int tq = p->query_tile;
-    const int kv_tile = p->prefill_variant == kPrefillBig ? kPrefillBigTile : kPrefillKvTile;
+    const int kv_tile = p->prefill_variant == kPrefillBig || p->prefill_variant == kPrefillDuo
+                            ? kPrefillBigTile
+                            : kPrefillKvTile;
     struct It { int64_t cost; int32_t w[kPrefillItemWords]; };
     std::vector<It> items;
     for (size_t b = 0; b < reqs.size(); ++b) {
@@ -262,7 +265,10 @@ static int build_prefill(Plan *p, const std::vector<Req> &reqs)
     // the direct-to-LDS variants keep an item's page ids in an LDS table; the
     // variant was fixed at plan creation so that no item within the
     // capacities can span more pages than the table (dma_table_pages_bound)
-    if (p->prefill_variant == kPrefillDma || p->prefill_variant == kPrefillBig) {
+    if (p->prefill_variant == kPrefillDma || p->prefill_variant == kPrefillBig ||
+        p->prefill_variant == kPrefillDuo) {
+        const int64_t table =
+            p->prefill_variant == kPrefillDuo ? p->table_pages : int64_t(kPrefillDmaPages);
         for (const It &it : items) {
             const int64_t kb = it.w[kPiKvBegin];
             const int64_t kv_len = it.w[kPiKvLen];
@@ -272,11 +278,11 @@ static int build_prefill(Plan *p, const std::vector<Req> &reqs)
             if (kv_end <= kb) continue;
             const int64_t last = std::min(kb + ceil_div(kv_end - kb, kv_tile) * kv_tile,
                                           kv_len) - 1;
-            if (last / d.page_size - kb / d.page_size + 1 > kPrefillDmaPages)
+            if (last / d.page_size - kb / d.page_size + 1 > table)
                 return fail(PKVS_ERR_CAPACITY, "a prefill item spans %lld pages of keys, more "
-                            "than the %d the plan's kernel holds",
+                            "than the %lld the plan's kernel holds",
                             (long long)(last / d.page_size - kb / d.page_size + 1),
-                            kPrefillDmaPages);
+                            (long long)table);
         }
     }
     p->n_items = int64_t(items.size());
@@ -500,26 +506,33 @@ static int create_plan(const pkvs_desc *desc, bool ragged, Plan **out)
             v = desc->head_dim == 128 && kvf == PKVS_KV_SAME ? kPrefillBig : kPrefillRows256;
         if (desc->prefill_variant) v = desc->prefill_variant;
         // the direct-to-LDS variants need 104-156 KiB of LDS per workgroup
-        if ((v == kPrefillDma || v == kPrefillBig) && p->have_gpu && !fp32 &&
-            prefill_blocks_per_cu(desc->head_dim, v, f16, kvf) < 1)
-            v = kPrefillRows256;
-        // ... and an LDS table of kPrefillDmaPages page ids per item: they are
-        // kept only when no item within the capacities can span more pages.
-        // The choice holds for the plan's lifetime, so a captured run keeps
-        // launching the kernel that every later plan() builds its items for.
-        if ((v == kPrefillDma || v == kPrefillBig) &&
-            item_pages_bound(*desc, v == kPrefillBig ? kPrefillBigTile : kPrefillKvTile,
-                             256 / group) > kPrefillDmaPages)
+        // ... and an LDS table of at most kPrefillDmaPages page ids per item:
+        // they are kept only when no item within the capacities can span more
+        // pages (kPrefillDuo sizes its table to that span).  The choice holds
+        // for the plan's lifetime, so a captured run keeps launching the
+        // kernel that every later plan() builds its items for.
+        const bool dma_v = v == kPrefillDma || v == kPrefillBig || v == kPrefillDuo;
+        int64_t span = 0;
+        if (dma_v) {
+            span = item_pages_bound(*desc, v == kPrefillDma ? kPrefillKvTile : kPrefillBigTile,
+                                    (v == kPrefillDuo ? 128 : 256) / group);
+            if (span > kPrefillDmaPages) v = kPrefillRows256;
+        }
+        if (v == kPrefillDuo) p->table_pages = int(std::min<int64_t>(kPrefillDmaPages,
+                                                                     (span + 15) / 16 * 16));
+        if ((v == kPrefillDma || v == kPrefillBig || v == kPrefillDuo) && p->have_gpu && !fp32 &&
+            prefill_blocks_per_cu(desc->head_dim, v, f16, kvf, p->table_pages) < 1)
             v = kPrefillRows256;
         p->prefill_variant = v;
-        const int rows = v == kPrefillRows128 ? 128 : 256;
+        const int rows = v == kPrefillRows128 || v == kPrefillDuo ? 128 : 256;
         p->query_tile = fp32 ? kGenericQTile : rows / group;
         p->item_words = kPrefillItemWords;
         p->block_threads =
             fp32 ? kGenericThreads
                  : (v == kPrefillRows256 || v == kPrefillDma || v == kPrefillBig ? 512 : 256);
-        int per_cu =
-            p->have_gpu && !fp32 ? prefill_blocks_per_cu(desc->head_dim, v, f16, kvf) : 0;
+        int per_cu = p->have_gpu && !fp32
+                         ? prefill_blocks_per_cu(desc->head_dim, v, f16, kvf, p->table_pages)
+                         : 0;
         p->grid_blocks = p->num_cus * std::max(per_cu, fp32 ? 2 : 1);
     } else {
         p->query_tile = 1;

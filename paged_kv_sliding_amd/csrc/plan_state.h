@@ -38,6 +38,7 @@ struct pkvs_plan {
     int num_cus = 0;
     int grid_blocks = 0, block_threads = 0, query_tile = 0, item_words = 0;
     int prefill_variant = 1;  // 16-bit prefill kernel variant (PrefillVariant), fixed at creation
+    int table_pages = 0;      // kPrefillDuo: entries of its LDS page table
     int64_t auto_target_items = 0;
     int decode_waves = 1;     // waves per decode work item (1 or 4)
     int64_t items_cap = 0, slots_cap = 0, merges_cap = 0;

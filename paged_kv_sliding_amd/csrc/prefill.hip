@@ -1412,6 +1412,373 @@ __global__ __launch_bounds__(512) void prefill_big_kernel(PrefillArgs a)
     }
 }
 
+// Two workgroups per CU (variant 6: head_dim 128, 4 waves x 32 rows, 16-bit
+// K/V, 64-key steps).  The step of prefill_big_kernel (a head, then four
+// quarters of S^T(j+1) and P.V MFMAs with the probabilities made between
+// them), but with 128 rows per workgroup and two workgroups resident on
+// each CU: the two waves that share a SIMD belong to different workgroups,
+// whose barriers are independent, so one can run its MFMAs while the other
+// runs its softmax or waits at its barrier.  To fit two workgroups in LDS, K
+// and V sit in rings of two tiles each (64 KiB): step j loads K(j+2) into the
+// slot K(j) left (S^T(j) was made in step j-1) and V(j+1) into the slot
+// V(j-1) left, and waits for both at its end.  The page table holds as many
+// entries as the plan's longest item can span (dynamic LDS).
+constexpr size_t kDuoRingBytes = 4 * size_t(BIG_HALF);  // K ring + V ring
+
+// Four 16-byte row-group loads from one scalar base: blocks m, m + 1 KiB,
+// m + 2 KiB, m + 3 KiB (lane offsets d0..d3).  M0 is restored afterwards.
+__device__ __forceinline__ void duo_dma4(uint32_t m, uint32_t d0, uint32_t d1, uint32_t d2,
+                                         uint32_t d3, const void *base)
+{
+    uint32_t saved;
+    asm volatile("s_mov_b32 %0, m0\n\t"
+                 "s_mov_b32 m0, %1\n\tglobal_load_lds_dwordx4 %5, %9\n\t"
+                 "s_mov_b32 m0, %2\n\tglobal_load_lds_dwordx4 %6, %9\n\t"
+                 "s_mov_b32 m0, %3\n\tglobal_load_lds_dwordx4 %7, %9\n\t"
+                 "s_mov_b32 m0, %4\n\tglobal_load_lds_dwordx4 %8, %9\n\t"
+                 "s_mov_b32 m0, %0"
+                 : "=&s"(saved)
+                 : "s"(m), "s"(m + 1024u), "s"(m + 2048u), "s"(m + 3072u), "v"(d0), "v"(d1),
+                   "v"(d2), "v"(d3), "s"(base)
+                 : "memory");
+}
+
+template <bool F16>
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2)))
+void prefill_duo_kernel(PrefillArgs a)
+{
+    constexpr int D = 128, KS = D / 16, DT = D / 32;
+    extern __shared__ __attribute__((aligned(1024))) uint8_t duo_lds[];
+    int32_t *const pages = reinterpret_cast<int32_t *>(duo_lds + kDuoRingBytes);
+    int32_t *const next_item_slot = pages + a.table_pages;
+
+    const int tid = threadIdx.x;
+    const int wave = tid >> 6, lane = tid & 63, l32 = lane & 31, hw = lane >> 5;
+    const int uwave = __builtin_amdgcn_readfirstlane(wave);
+    const int G = 1 << a.log2_group;
+    const int n_items = a.ws[kHdrNumItems];
+    const uint16_t *Q = static_cast<const uint16_t *>(a.q);
+    const int W = a.window_left;
+    const float c = a.scale_log2;
+    const float cap_a = a.cap_a;
+
+    const uint32_t lds_k =
+        uint32_t(reinterpret_cast<uintptr_t>((__attribute__((address_space(3))) void *)duo_lds));
+    const uint32_t lds_v = lds_k + uint32_t(2 * BIG_HALF);
+    // operand addresses: the chunk-permuted layout of prefill_big_kernel
+    const uint32_t kvar0 = lds_k + uint32_t(1024 * (l32 >> 2) + 16 * (l32 & 3) +
+                                            64 * ((hw + (l32 >> 2)) & 3));
+    const uint32_t kvar1 = lds_k + uint32_t(1024 * (l32 >> 2) + 16 * (l32 & 3) +
+                                            64 * ((2 + hw + (l32 >> 2)) & 3));
+    const uint32_t vvar = [&] {
+        const int e = (lane & 15) >> 2, q = lane & 3, s16 = (lane >> 4) & 1;
+        return lds_v + uint32_t(1024 * hw + 64 * e + 16 * (2 * s16 + (q >> 1)) + 8 * (q & 1));
+    }();
+    // staging: wave w stages keys 16w .. 16w+15 of a tile, four 1 KiB blocks
+    // b = 4w + i of four rows; lane L writes LDS byte 16L of the block and
+    // fetches K: row L % 4, chunk 4 (L / 16) + ((L / 4 - i) % 4);
+    //         V: row (L / 4) % 4, chunk 4 (L / 16) + L % 4
+    const int64_t slot_stride = int64_t(a.num_kv_heads) * D;
+    const int32_t slot_bytes = int32_t(slot_stride * 2);
+    const uint32_t page_bytes = uint32_t(slot_stride * a.page_rows * 2);
+    const int kr = lane & 3, vr = (lane >> 2) & 3;
+    uint32_t kc[4], dk[4], dv[4];
+    const uint32_t vc = uint32_t(16 * (4 * (lane >> 4) + (lane & 3)));
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        kc[i] = uint32_t(16 * (4 * (lane >> 4) + (((lane >> 2) - i) & 3)));
+        dk[i] = uint32_t((4 * i + kr) * slot_bytes) + kc[i];
+        dv[i] = uint32_t((4 * i + vr) * slot_bytes) + vc;
+    }
+    const char *const Kb = static_cast<const char *>(a.k);
+    const char *const Vb = static_cast<const char *>(a.v);
+    const int page_mask = a.page_size - 1;
+    const int table_last = a.table_pages - 1;
+
+    // run-time item claiming per XCD, as prefill_big_kernel
+    int32_t *const ctr = a.ws;
+    const int xcd = blockIdx.x % kXcds;
+    const int xcd_groups = (int(gridDim.x) - xcd + kXcds - 1) / kXcds;
+    if (int(blockIdx.x) >= n_items) return;
+    const int participants = min(int(gridDim.x), n_items);
+    for (int it = blockIdx.x; it < n_items;) {
+        int claimed = 0;
+        if (tid == 0) claimed = atomicAdd(ctr + kHdrNextItem + xcd, 1);
+        const int32_t *w = a.ws + kHeaderWords + int64_t(it) * kPrefillItemWords;
+        const int hk = w[kPiKvHead], q_begin = w[kPiQBegin], q_count = w[kPiQCount];
+        const int pos0 = w[kPiPos0], kv_len = w[kPiKvLen];
+        const int kv_begin = w[kPiKvBegin];
+        const int page_base = w[kPiPageBase];
+        const int kv_end = a.causal ? min(kv_len, pos0 + q_count) : kv_len;
+        const int pos_last = pos0 + q_count - 1;
+        const int ntiles = kv_end > kv_begin ? (kv_end - kv_begin + BIG_T - 1) / BIG_T : 0;
+        const int pt_lo = kv_begin >> a.log2_page;
+        const int32_t head_bytes = int32_t(hk * D * 2);
+        const int kv_last = min(kv_begin + ntiles * BIG_T, kv_len) - 1;
+
+        const int row = wave * 32 + l32;
+        const int row_tok = row >> a.log2_group, row_head = row & (G - 1);
+        const bool row_valid = row_tok < q_count;
+        const int p_row = pos0 + row_tok;
+        const int64_t qrow = (int64_t(q_begin + row_tok) * a.num_qo_heads + hk * G + row_head) * D;
+        bf16x8 qf[KS];
+#pragma unroll
+        for (int ks = 0; ks < KS; ++ks)
+            qf[ks] = row_valid ? load_bf16x8(Q + qrow + ks * 16 + hw * 8) : zero_bf16x8();
+
+        float m = kNegInf, l = 0.f;
+        f32x16 o[DT];
+#pragma unroll
+        for (int dt = 0; dt < DT; ++dt)
+#pragma unroll
+            for (int i = 0; i < 16; ++i) o[dt][i] = 0.f;
+
+        auto page_entry = [&](int key) __attribute__((always_inline)) {
+            const int e = min(max((key >> a.log2_page) - pt_lo, 0), table_last);
+            return min(max(pages[e], 0), int32_t(a.num_pages - 1));
+        };
+        // the wave's 16 rows of tile t of one tensor (K: base Kb, V: Vb) into
+        // the LDS tile at `set`
+        auto dma_rows = [&](int t, uint32_t set, const char *base, const uint32_t (&d)[4],
+                            bool is_k) __attribute__((always_inline)) {
+            const int key0 = kv_begin + t * BIG_T + 16 * uwave;
+            const uint32_t mrow = set + uint32_t(16 * uwave * BIG_ROW);
+            const int32_t pg0 = __builtin_amdgcn_readfirstlane(page_entry(min(key0, kv_last)));
+            if (key0 + 15 <= kv_last && (key0 & page_mask) + 16 <= a.page_size) {
+                const int64_t off = int64_t(uint64_t(uint32_t(pg0)) * page_bytes) +
+                                    int32_t((key0 & page_mask) * slot_bytes + head_bytes);
+                duo_dma4(mrow, d[0], d[1], d[2], d[3], base + off);
+            } else {
+#pragma unroll
+                for (int i = 0; i < 4; ++i) {
+                    const int key = min(key0 + 4 * i + (is_k ? kr : vr), kv_last);
+                    const int32_t pg = page_entry(key);
+                    const int64_t off = int64_t(uint64_t(uint32_t(pg)) * page_bytes) +
+                                        int32_t((key & page_mask) * slot_bytes + head_bytes);
+                    big_dma1(mrow + uint32_t(i * 1024),
+                             base + (off + int32_t(is_k ? kc[i] : vc)));
+                }
+            }
+        };
+        auto dma_k = [&](int t, int p) __attribute__((always_inline)) {
+            dma_rows(t, lds_k + uint32_t(p * BIG_HALF), Kb, dk, true);
+        };
+        auto dma_v = [&](int t, int p) __attribute__((always_inline)) {
+            dma_rows(t, lds_v + uint32_t(p * BIG_HALF), Vb, dv, false);
+        };
+
+        // prologue: page table, then K(0), K(1) and V(0) landed
+        {
+            const int pt_n =
+                ntiles > 0 ? min((kv_last >> a.log2_page) - pt_lo + 1, a.table_pages) : 0;
+            for (int e = tid; e < pt_n; e += 256) {
+                const int32_t pg = a.kv_indices[page_base + pt_lo + e];
+                pages[e] = min(max(pg, 0), int32_t(a.num_pages - 1));
+            }
+        }
+        __builtin_amdgcn_s_waitcnt(0);
+        __syncthreads();
+        if (ntiles > 0) {
+            dma_k(0, 0);
+            if (ntiles > 1) dma_k(1, 1);
+            dma_v(0, 0);
+            __builtin_amdgcn_s_waitcnt(0);
+        }
+        __syncthreads();
+
+        // S^T of tile 0, both halves
+        f32x16 s[2];
+#pragma unroll
+        for (int h = 0; h < 2; ++h)
+#pragma unroll
+            for (int i = 0; i < 16; ++i) s[h][i] = 0.f;
+        if (ntiles > 0) {
+#pragma unroll
+            for (int ks = 0; ks < KS; ++ks)
+#pragma unroll
+                for (int h = 0; h < 2; ++h)
+                    s[h] = mfma32x32x16<F16>(
+                        lds_b128((ks & 1 ? kvar1 : kvar0) + uint32_t(h * 32 * BIG_ROW + 256 * (ks >> 1))),
+                        qf[ks], s[h]);
+        }
+        // step 0 loads K(2) into K(0)'s slot: every wave's reads of K(0) first
+        __syncthreads();
+
+        float mu = 0.f, ahead_max = kNegInf;
+        bf16x8 pb[4];
+        f32x16 sb[3];
+        sb[0] = s[0];
+        sb[1] = s[1];
+        auto prob2 = [&](const f32x16 &sh, int b, int i) __attribute__((always_inline)) {
+            const int t = 8 * (b & 1) + 2 * i;
+            const float p0 = fast_exp2(__builtin_fmaf(sh[t], c, -mu));
+            const float p1 = fast_exp2(__builtin_fmaf(sh[t + 1], c, -mu));
+            l += p0 + p1;
+            const bf16x2 pk = to16x2<F16>(f32x2{p0, p1});
+            pb[b][2 * i] = pk[0];
+            pb[b][2 * i + 1] = pk[1];
+        };
+        auto head = [&](int j, f32x16 &s0, f32x16 &s1) __attribute__((always_inline)) {
+            const int k0 = kv_begin + j * BIG_T;
+            const bool interior = k0 + BIG_T <= kv_len &&
+                                  (!a.causal || k0 + BIG_T - 1 <= pos0) &&
+                                  (W < 0 || k0 >= pos_last - W);
+            float mx;
+            if (j > 0 && interior && cap_a == 0.f) {
+                mx = fmaxf(ahead_max, max16(s1));
+            } else {
+                if (cap_a != 0.f) {
+#pragma unroll
+                    for (int i = 0; i < 16; ++i) {
+                        s0[i] = soft_cap_unit(s0[i], cap_a);
+                        s1[i] = soft_cap_unit(s1[i], cap_a);
+                    }
+                }
+                if (!interior) {
+                    mask_tile(s0, k0, hw, p_row, kv_len, a.causal, W);
+                    mask_tile(s1, k0 + 32, hw, p_row, kv_len, a.causal, W);
+                }
+                mx = fmaxf(max16(s0), max16(s1));
+            }
+            {
+                const auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(mx),
+                                                                 __float_as_uint(mx), false, false);
+                mx = fmaxf(__uint_as_float(sw[0]), __uint_as_float(sw[1])) * c;
+            }
+            if (__any(mx > m + kRescaleLog2)) {
+                const float m_new = fmaxf(m, mx);
+                const float alpha = m_new == kNegInf ? 1.f : fast_exp2(m - m_new);
+                l *= alpha;
+#pragma unroll
+                for (int dt = 0; dt < DT; ++dt) o[dt] *= alpha;
+                m = m_new;
+            }
+            mu = m == kNegInf ? 0.f : m;
+            __builtin_amdgcn_sched_barrier(0);
+        };
+        bf16x8 kq[4], va[DT];
+        uint32_t kv0 = kvar0, kv1 = kvar1, vv = vvar;
+        // K operands of S^T(j+1, half h), k-steps kk, kk+2, kk+4, kk+6 (K slot pk)
+        auto load_k = [&](int pk, int q) __attribute__((always_inline)) {
+            const int h = q >> 1, kk = q & 1;
+            const uint32_t kb = kk ? kv1 : kv0;
+#pragma unroll
+            for (int u = 0; u < 4; ++u)
+                kq[u] = lds_b128(kb + uint32_t(pk * BIG_HALF + h * 32 * BIG_ROW + 256 * u));
+        };
+        // V^T operands of quarter q of the tile in V slot pv
+        auto load_v = [&](int pv, int q) __attribute__((always_inline)) {
+            const int h = q >> 1, kk = q & 1;
+#pragma unroll
+            for (int dt = 0; dt < DT; ++dt) {
+                const uint32_t v0 = vv + uint32_t(pv * BIG_HALF + (32 * h + 16 * kk) * BIG_ROW + 256 * dt);
+                const i16x4 lo = lds_tr(v0), hi = lds_tr(v0 + 8 * BIG_ROW);
+                va[dt] =
+                    __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
+            }
+        };
+        auto quarter = [&](int pk, int pv, int q, const f32x16 &s0, const f32x16 &s1, f32x16 &dst)
+            __attribute__((always_inline)) {
+            const int kk = q & 1;
+            if (kk == 0) {
+#pragma unroll
+                for (int i = 0; i < 16; ++i) dst[i] = 0.f;
+            }
+#pragma unroll
+            for (int u = 0; u < 4; ++u) {
+                dst = mfma32x32x16<F16>(kq[u], qf[kk + 2 * u], dst);
+                if (q < 2) prob2(q == 0 ? s0 : s1, 2 * q, u);
+                __builtin_amdgcn_sched_barrier(0);
+            }
+            if (q < 3) load_k(pk, q + 1);
+            __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+            for (int u = 0; u < 4; ++u) {
+                o[u] = mfma32x32x16<F16>(va[u], pb[q], o[u]);
+                if (q < 2) prob2(q == 0 ? s0 : s1, 2 * q + 1, u);
+                __builtin_amdgcn_sched_barrier(0);
+            }
+            if (q < 3) load_v(pv, q + 1);
+            __builtin_amdgcn_sched_barrier(0);
+        };
+        // Step j: K(j+1) in slot pk = (j+1) % 2, V(j) in slot pv = j % 2.  It
+        // loads K(j+2) into slot pv (K(j) is no longer read) and V(j+1) into
+        // slot pk (V(j-1) is no longer read), and waits for them at its end.
+        auto step = [&](int j, int pk, int pv, f32x16 &sx, f32x16 &sy, f32x16 &sz)
+            __attribute__((always_inline)) {
+            if (j + 2 < ntiles) dma_k(j + 2, pv);
+            if (j + 1 < ntiles) dma_v(j + 1, pk);
+            {
+                uint32_t x0 = kvar0, x1 = kvar1, x2 = vvar;
+                asm volatile("" : "+v"(x0), "+v"(x1), "+v"(x2));
+                kv0 = x0;
+                kv1 = x1;
+                vv = x2;
+            }
+            load_k(pk, 0);
+            load_v(pv, 0);
+            __builtin_amdgcn_sched_barrier(0);
+            head(j, sx, sy);
+            quarter(pk, pv, 0, sx, sy, sz);
+            quarter(pk, pv, 1, sx, sy, sz);
+            ahead_max = max16(sz);  // S^T(j+1, half 0) is complete
+            quarter(pk, pv, 2, sx, sy, sx);
+            quarter(pk, pv, 3, sx, sy, sx);
+            __builtin_amdgcn_s_waitcnt(0);
+            __syncthreads();
+        };
+        // unrolled by six: the slots repeat every two steps, the score
+        // accumulators' roles every three
+        for (int j = 0; j < ntiles; j += 6) {
+            step(j, 1, 0, sb[0], sb[1], sb[2]);
+            if (j + 1 < ntiles) step(j + 1, 0, 1, sb[2], sb[0], sb[1]);
+            if (j + 2 < ntiles) step(j + 2, 1, 0, sb[1], sb[2], sb[0]);
+            if (j + 3 < ntiles) step(j + 3, 0, 1, sb[0], sb[1], sb[2]);
+            if (j + 4 < ntiles) step(j + 4, 1, 0, sb[2], sb[0], sb[1]);
+            if (j + 5 < ntiles) step(j + 5, 0, 1, sb[1], sb[2], sb[0]);
+        }
+
+        l += __shfl_xor(l, 32);
+        if (row_valid) {
+            const int64_t lrow = int64_t(q_begin + row_tok) * a.num_qo_heads + hk * G + row_head;
+            float w_self = l > 0.f ? a.v_scale / l : 0.f, w_other = 0.f;
+            float lse_row = l > 0.f ? (m + fast_log2(l)) * kLn2 : kNegInf;
+            if (a.fold_lse) {
+                const Fold f = fold_weights(lse_row, a.fold_lse[lrow]);
+                w_self *= f.self;
+                w_other = f.other;
+                lse_row = f.lse;
+            }
+            uint16_t *O = static_cast<uint16_t *>(a.o);
+            const uint16_t *FO = static_cast<const uint16_t *>(a.fold_o);
+#pragma unroll
+            for (int dt = 0; dt < DT; ++dt)
+#pragma unroll
+                for (int m0 = 0; m0 < 4; ++m0) {
+                    const int64_t at = qrow + dt * 32 + 8 * m0 + 4 * hw;
+                    f32x4 v4;
+#pragma unroll
+                    for (int m1 = 0; m1 < 4; ++m1) v4[m1] = o[dt][4 * m0 + m1] * w_self;
+                    if (FO) {
+                        const f32x4 f4 = from16x4<F16>(*reinterpret_cast<const bf16x4 *>(FO + at));
+#pragma unroll
+                        for (int m1 = 0; m1 < 4; ++m1) v4[m1] += f4[m1] * w_other;
+                    }
+                    *reinterpret_cast<bf16x4 *>(O + at) = to16x4<F16>(v4);
+                }
+            if (a.lse && hw == 0) a.lse[lrow] = lse_row;
+        }
+        if (tid == 0) *next_item_slot = xcd + kXcds * (xcd_groups + claimed);
+        __builtin_amdgcn_s_waitcnt(0);
+        __syncthreads();
+        it = *next_item_slot;
+    }
+    if (tid == 0 && atomicAdd(ctr + kHdrDoneGroups, 1) == participants - 1) {
+        for (int x = 0; x < kXcds; ++x) ctr[kHdrNextItem + x] = 0;
+        ctr[kHdrDoneGroups] = 0;
+    }
+}
+
 // fp32 inputs: one wave per (query token, head) row, keys visited in order
 // with a running maximum, all arithmetic in fp32.
 __global__ __launch_bounds__(kGenericThreads) void attention_fp32_kernel(PrefillArgs a, int D)
@@ -1477,6 +1844,11 @@ __global__ __launch_bounds__(kGenericThreads) void attention_fp32_kernel(Prefill
 
 }  // namespace
 
+size_t prefill_duo_lds_bytes(int table_pages)
+{
+    return kDuoRingBytes + 4 * size_t(table_pages) + 16;
+}
+
 template <bool F16, int KVF>
 static hipError_t launch_prefill_t(const PrefillArgs &a, int head_dim, int variant, int grid,
                                    hipStream_t s)
@@ -1492,6 +1864,13 @@ static hipError_t launch_prefill_t(const PrefillArgs &a, int head_dim, int varia
             prefill_big_kernel<F16><<<grid, 512, 0, s>>>(a);
             return hipGetLastError();
         }
+        if (variant == kPrefillDuo) {
+            if (head_dim != 128 || a.table_pages < 1 || a.table_pages > kPrefillDmaPages)
+                return hipErrorInvalidValue;
+            prefill_duo_kernel<F16><<<grid, 256, prefill_duo_lds_bytes(a.table_pages), s>>>(a);
+            return hipGetLastError();
+        }
+
         if (variant == kPrefillWide) {
             switch (head_dim) {
             case 64: prefill_wide_kernel<64, F16><<<grid, 256, 0, s>>>(a); break;
@@ -1500,7 +1879,8 @@ static hipError_t launch_prefill_t(const PrefillArgs &a, int head_dim, int varia
             }
             return hipGetLastError();
         }
-    } else if (variant == kPrefillDma || variant == kPrefillWide || variant == kPrefillBig) {
+    } else if (variant == kPrefillDma || variant == kPrefillWide || variant == kPrefillBig ||
+               variant == kPrefillDuo) {
         return hipErrorInvalidValue;  // 8-bit K/V are widened on the register-staged path
     }
     if (variant == kPrefillRows256) {
@@ -1554,19 +1934,30 @@ static int blocks_per_cu(K kernel, int threads)
 }
 
 template <bool F16, int KVF>
-static int prefill_blocks_per_cu_t(int head_dim, int variant)
+static int prefill_blocks_per_cu_t(int head_dim, int variant, int table_pages)
 {
     if constexpr (KVF == 0) {
         if (variant == kPrefillDma)
             return head_dim == 128 ? blocks_per_cu(prefill_kernel<128, 8, true, F16, 0>, 512) : 0;
         if (variant == kPrefillBig)
             return head_dim == 128 ? blocks_per_cu(prefill_big_kernel<F16>, 512) : 0;
+        if (variant == kPrefillDuo) {
+            int n = 0;
+            return head_dim == 128 &&
+                           hipOccupancyMaxActiveBlocksPerMultiprocessor(
+                               &n, prefill_duo_kernel<F16>, 256,
+                               prefill_duo_lds_bytes(table_pages)) == hipSuccess
+                       ? n
+                       : 0;
+        }
+
         if (variant == kPrefillWide) {
             if (head_dim == 64) return blocks_per_cu(prefill_wide_kernel<64, F16>, 256);
             if (head_dim == 128) return blocks_per_cu(prefill_wide_kernel<128, F16>, 256);
             return 0;
         }
-    } else if (variant == kPrefillDma || variant == kPrefillWide || variant == kPrefillBig) {
+    } else if (variant == kPrefillDma || variant == kPrefillWide || variant == kPrefillBig ||
+               variant == kPrefillDuo) {
         return 0;
     }
     if (variant == kPrefillRows256) {
@@ -1581,20 +1972,20 @@ static int prefill_blocks_per_cu_t(int head_dim, int variant)
 }
 
 template <bool F16>
-static int prefill_blocks_per_cu_f(int head_dim, int variant, int kv_format)
+static int prefill_blocks_per_cu_f(int head_dim, int variant, int kv_format, int table_pages)
 {
     switch (kv_format) {
-    case 0: return prefill_blocks_per_cu_t<F16, 0>(head_dim, variant);
-    case PKVS_KV_FP8_E4M3: return prefill_blocks_per_cu_t<F16, 1>(head_dim, variant);
-    case PKVS_KV_FP8_E5M2: return prefill_blocks_per_cu_t<F16, 2>(head_dim, variant);
+    case 0: return prefill_blocks_per_cu_t<F16, 0>(head_dim, variant, table_pages);
+    case PKVS_KV_FP8_E4M3: return prefill_blocks_per_cu_t<F16, 1>(head_dim, variant, table_pages);
+    case PKVS_KV_FP8_E5M2: return prefill_blocks_per_cu_t<F16, 2>(head_dim, variant, table_pages);
     default: return 0;
     }
 }
 
-int prefill_blocks_per_cu(int head_dim, int variant, bool f16, int kv_format)
+int prefill_blocks_per_cu(int head_dim, int variant, bool f16, int kv_format, int table_pages)
 {
-    return f16 ? prefill_blocks_per_cu_f<true>(head_dim, variant, kv_format)
-               : prefill_blocks_per_cu_f<false>(head_dim, variant, kv_format);
+    return f16 ? prefill_blocks_per_cu_f<true>(head_dim, variant, kv_format, table_pages)
+               : prefill_blocks_per_cu_f<false>(head_dim, variant, kv_format, table_pages);
 }
 
 }  // namespace pkvs

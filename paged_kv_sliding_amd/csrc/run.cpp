@@ -112,6 +112,7 @@ hipError_t launch_prefill_pass(const pkvs_plan *p, const void *q, const void *k,
     a.causal = p->desc.causal;
     a.fold_o = fold_o;
     a.fold_lse = fold_lse;
+    a.table_pages = p->table_pages;
     return p->desc.dtype == PKVS_FP32
                ? launch_attention_fp32(a, p->desc.head_dim, p->grid_blocks, stream)
                : launch_prefill_16bit(a, p->desc.head_dim, p->prefill_variant,

@@ -152,7 +152,7 @@ def test_prefill_small_ragged(P_, W):
 # (page sizes 1, 2 and 4 take their per-row page paths (variant 4: below 4),
 # the others their same-page paths; the last tile of each item the
 # clamped-row path)
-@pytest.mark.parametrize("variant", [1, 2, 3, 4, 5])
+@pytest.mark.parametrize("variant", [1, 2, 3, 4, 5, 6])
 @pytest.mark.parametrize("P_", [1, 2, 4, 8, 16])
 @pytest.mark.parametrize("W", [-1, 0, 33, 200])
 def test_prefill_variants_ragged(variant, P_, W):
@@ -166,7 +166,7 @@ def test_prefill_variants_ragged(variant, P_, W):
     compare(o, lse, ro, rl, tag=f"prefill variant={variant} P={P_} W={W}")
 
 
-@pytest.mark.parametrize("variant", [4, 5])
+@pytest.mark.parametrize("variant", [4, 5, 6])
 def test_prefill_dma_variant_prefix_non_causal_and_fallback(variant):
     # non-causal, no window: every item loads all keys of its request
     case = small([20, 7, 64], [50, 7, 400], H_q=8, H_kv=2, D=128, W=-1, seed=21)
@@ -685,7 +685,7 @@ def test_cascade_equals_one_paged_prefill(P_, W, trim):
                                 f"variant={att.info().prefill_variant}")
 
 
-@pytest.mark.parametrize("variant", [1, 2, 3, 4, 5])
+@pytest.mark.parametrize("variant", [1, 2, 3, 4, 5, 6])
 def test_cascade_prefill_variants(variant):
     qo = [64, 1, 257, 33, 600]
     kv = [64, 800, 300, 1000, 700]
@@ -932,7 +932,7 @@ def test_decode_step_appends_and_builds_its_page_table(W):
 # sm_scale 0.3 on N(0,1) data puts many logits near and past the cap.
 
 
-@pytest.mark.parametrize("variant", [1, 2, 3, 4, 5])
+@pytest.mark.parametrize("variant", [1, 2, 3, 4, 5, 6])
 @pytest.mark.parametrize("cap", [2.0, 30.0])
 @pytest.mark.parametrize("W", [-1, 33])
 def test_soft_cap_prefill_variants(variant, cap, W):
@@ -989,7 +989,7 @@ def test_soft_cap_fp32_and_cascade():
 # and bf16; the 16-bit kernels read IEEE half on the fp16 matrix instructions.
 
 
-@pytest.mark.parametrize("variant", [1, 2, 3, 4, 5])
+@pytest.mark.parametrize("variant", [1, 2, 3, 4, 5, 6])
 @pytest.mark.parametrize("W", [-1, 0, 33])
 def test_fp16_prefill_variants(variant, W):
     qo = [1, 70, 0, 33, 129, 5, 300]

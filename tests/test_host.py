@@ -126,7 +126,7 @@ def err_code(fn):
     (dict(num_qo_heads=3, num_kv_heads=1, dtype=torch.float16), P.PKVS_ERR_UNSUPPORTED),
     (dict(fixed_split_size=100), P.PKVS_ERR_INVALID_ARG),
     (dict(batch_capacity=0), P.PKVS_ERR_INVALID_ARG),
-    (dict(prefill_variant=6), P.PKVS_ERR_INVALID_ARG),
+    (dict(prefill_variant=7), P.PKVS_ERR_INVALID_ARG),
     (dict(prefill_variant=2, head_dim=256), P.PKVS_ERR_UNSUPPORTED),
     (dict(prefill_variant=3, head_dim=256), P.PKVS_ERR_UNSUPPORTED),
     # one page of 1024 slots x 8192 kv heads x 256 dims is 2^31 elements
@@ -262,7 +262,7 @@ def test_prefill_variant_choice_and_page_table_fallback():
     captured run keeps launching the kernel it was captured with)."""
     big = dict(num_qo_heads=32, num_kv_heads=8, window_left=-1, qo_capacity=32768,
                kv_capacity=32768, batch_capacity=4)
-    for v in (0, 4, 5):
+    for v in (0, 4, 5, 6):
         # no window, 32768 keys of 16: at most 2048 pages per item -> kept
         hv = P.pkvs_plan_create(desc(page_size=16, prefill_variant=v, **big))
         assert P.pkvs_plan_get_info(hv).prefill_variant == (v or 5)
@@ -304,7 +304,7 @@ def test_prefill_variant_choice_and_page_table_fallback():
             assert max(spans) <= 2048
     # head_dim 64 keeps the register-staged kernel; asking for 4 is refused
     assert P.pkvs_plan_get_info(P.pkvs_plan_create(desc(head_dim=64, **big))).prefill_variant == 2
-    for v in (4, 5):
+    for v in (4, 5, 6):
         assert err_code(lambda: P.pkvs_plan_create(desc(head_dim=64, prefill_variant=v))) == \
             P.PKVS_ERR_UNSUPPORTED
 
