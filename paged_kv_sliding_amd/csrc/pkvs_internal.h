@@ -34,7 +34,7 @@ enum HeaderField {
 constexpr int kXcds = 8;
 
 // Prefill item: one (request, kv head, query tile).
-constexpr int kPrefillItemWords = 8;
+constexpr int kPrefillItemWords = 12;
 enum PrefillItem {
     kPiRequest = 0,
     kPiKvHead = 1,
@@ -44,6 +44,9 @@ enum PrefillItem {
     kPiKvLen = 5,
     kPiPageBase = 6, // kv_indptr[request]
     kPiKvBegin = 7,  // first key processed (window start rounded down to a key tile)
+    kPiSplit = 8,    // one-pass cascade: keys from here on are the request's new
+                     // tokens, read from the contiguous K/V (key k on row
+                     // k + q_begin - pos0); INT32_MAX: every key is in the cache
 };
 
 // Decode item: one (request, kv head, key chunk).
@@ -116,6 +119,9 @@ struct PrefillArgs {
     const void *fold_o;
     const float *fold_lse;
     int32_t table_pages;  // kPrefillDuo: entries of its LDS page table (dynamic LDS)
+    // one-pass cascade (kPrefillBig): the new tokens' K/V, [tokens, kv heads,
+    // head_dim], for the keys at or past each item's kPiSplit; null otherwise
+    const void *k_ext, *v_ext;
 };
 
 struct DecodeArgs {

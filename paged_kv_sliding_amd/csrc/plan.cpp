@@ -172,6 +172,8 @@ static int validate_desc(const pkvs_desc *d)
 // Host view of one request's layout, validated.
 struct Req {
     int64_t qo_begin, qo_len, kv_len, page_base;
+    // one-pass cascade: the request's keys from here on are its new tokens
+    int64_t split = INT32_MAX;
 };
 
 static int read_layout(const Plan *p, const int32_t *qo_indptr, const int32_t *kv_indptr,
@@ -256,6 +258,8 @@ static int build_prefill(Plan *p, const std::vector<Req> &reqs)
                 it.w[kPiKvLen] = int32_t(r.kv_len);
                 it.w[kPiPageBase] = int32_t(r.page_base);
                 it.w[kPiKvBegin] = int32_t(kv_begin);
+                it.w[kPiSplit] = int32_t(std::min<int64_t>(r.split, INT32_MAX));
+                it.w[9] = it.w[10] = it.w[11] = 0;
                 items.push_back(it);
             }
         }
@@ -611,6 +615,45 @@ static size_t align256(size_t x) { return (x + 255) / 256 * 256; }
 // workspace, and the extend pass folds them into its own in its epilogue.
 static int create_cascade(const pkvs_desc *desc, Plan **out)
 {
+    // One pass when the default kernel serves the combined problem: each
+    // request's cached keys followed by its new tokens form one causal
+    // sequence (cached key j at position j, new token i at kv_len_b + i), and
+    // the window mask over it is exactly the pair of masks the two passes
+    // apply; the kernel reads keys before a request's split from the cache
+    // and the rest from the contiguous new-token K/V.
+    if (desc->kv_format == PKVS_KV_SAME && desc->dtype != PKVS_FP32 &&
+        desc->kv_capacity + desc->qo_capacity <= (int64_t(1) << 30)) {
+        pkvs_desc f = *desc;
+        f.kind = PKVS_PREFILL;
+        f.causal = 1;
+        f.kv_capacity = desc->kv_capacity + desc->qo_capacity;
+        Plan *fp = nullptr;
+        if (create_plan(&f, false, &fp) == PKVS_OK && fp->prefill_variant == kPrefillBig) {
+            Plan *p = new (std::nothrow) Plan();
+            if (!p) {
+                destroy_plan(fp);
+                return fail(PKVS_ERR_INVALID_ARG, "out of host memory");
+            }
+            p->desc = *desc;
+            p->fused = true;
+            p->pre = fp;
+            p->device = fp->device;
+            p->have_gpu = fp->have_gpu;
+            p->num_cus = fp->num_cus;
+            p->grid_blocks = fp->grid_blocks;
+            p->block_threads = fp->block_threads;
+            p->query_tile = fp->query_tile;
+            p->item_words = fp->item_words;
+            p->prefill_variant = fp->prefill_variant;
+            p->items_cap = fp->items_cap;
+            p->int_ws_need = fp->int_ws_need;
+            p->float_ws_need = 0;
+            *out = p;
+            return PKVS_OK;
+        }
+        destroy_plan(fp);
+        clear_error();
+    }
     pkvs_desc e = *desc, r = *desc;
     e.kind = r.kind = PKVS_PREFILL;
     e.page_size = kRaggedPage;          // row-index table entries
@@ -759,6 +802,41 @@ int pkvs_cascade_plan(pkvs_plan *p, const int32_t *qo_indptr_h, const int32_t *k
     if (!p) return fail(PKVS_ERR_INVALID_ARG, "plan is null");
     if (p->desc.kind != PKVS_CASCADE) return fail(PKVS_ERR_INVALID_ARG, "not a cascade plan");
     p->planned_device = false;
+    if (p->fused) {
+        // the cached layout, read with the cascade's own rules (a request may
+        // have more new tokens than cached keys), then each request as one
+        // prefill request over its cached keys followed by its new tokens
+        Plan lay;
+        lay.desc = p->desc;
+        lay.desc.kind = PKVS_PREFILL;
+        lay.queries_after_kv = true;
+        std::vector<Req> reqs;
+        int rc = read_layout(&lay, qo_indptr_h, kv_indptr_h, kv_last_page_len_h, batch_size,
+                             reqs);
+        if (rc) return rc;
+        int64_t cached = 0;
+        for (Req &q : reqs) {
+            cached += q.kv_len;
+            q.split = q.kv_len;
+            q.kv_len += q.qo_len;
+        }
+        Plan *f = p->pre;
+        f->planned_device = false;
+        rc = build_prefill(f, reqs);
+        if (rc) return rc;
+        if (f->n_items > f->items_cap)
+            return fail(PKVS_ERR_CAPACITY, "cascade work list of %lld items exceeds capacity %lld",
+                        (long long)f->n_items, (long long)f->items_cap);
+        p->n_items = f->n_items;
+        p->planned_keys = cached;
+        p->batch = f->batch = batch_size;
+        rc = finish_plan(f, nullptr, 0, int_ws, int_ws_bytes, stream);
+        if (rc || !int_ws) return rc;
+        p->int_ws = int_ws;
+        p->float_ws = float_ws;
+        p->planned_device = true;
+        return PKVS_OK;
+    }
     Plan *e = p->ext, *r = p->pre;
     e->planned_device = r->planned_device = false;
     std::vector<Req> pre_reqs;

@@ -55,8 +55,10 @@ struct pkvs_plan {
     int64_t planned_keys = 0;  // keys of all requests in the last plan()
 
     // A cascade plan (kind PKVS_CASCADE) owns its two passes and splits the
-    // caller's workspaces between them.
+    // caller's workspaces between them -- or, when `fused`, one prefill plan
+    // (pre) over each request's cached keys followed by its new tokens.
     pkvs_plan *ext = nullptr, *pre = nullptr;
+    bool fused = false;
     size_t pre_int_off = 0;                         // bytes into int_ws
     size_t o2_off = 0, lse2_off = 0;                // bytes into float_ws
 

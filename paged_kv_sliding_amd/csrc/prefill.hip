@@ -1096,6 +1096,8 @@ __global__ __launch_bounds__(512) void prefill_big_kernel(PrefillArgs a)
     const uint32_t dv1 = dv0 + row4;
     const char *const Kb = static_cast<const char *>(a.k);
     const char *const Vb = static_cast<const char *>(a.v);
+    const char *const Ke = static_cast<const char *>(a.k_ext);
+    const char *const Ve = static_cast<const char *>(a.v_ext);
     const int page_mask = a.page_size - 1;
 
     // Items are handed out at run time, per XCD: item i belongs to XCD
@@ -1120,6 +1122,9 @@ __global__ __launch_bounds__(512) void prefill_big_kernel(PrefillArgs a)
         const int pos0 = w[kPiPos0], kv_len = w[kPiKvLen];
         const int kv_begin = w[kPiKvBegin];
         const int page_base = w[kPiPageBase];
+        // one-pass cascade: keys from `split` on are the new tokens' rows
+        const int split = w[kPiSplit];
+        const int ext_row0 = q_begin - pos0;
         const int kv_end = a.causal ? min(kv_len, pos0 + q_count) : kv_len;
         const int pos_last = pos0 + q_count - 1;
         const int ntiles = kv_end > kv_begin ? (kv_end - kv_begin + BIG_T - 1) / BIG_T : 0;
@@ -1151,26 +1156,35 @@ __global__ __launch_bounds__(512) void prefill_big_kernel(PrefillArgs a)
             return min(max(sh.pages[e], 0), int32_t(a.num_pages - 1));
         };
         // the wave's 8 rows of tile t (ring position p = t % 3): K and V, four loads
+        // byte offset of key `key` of this kv head: a cache row before the
+        // split, a new-token row from it on (row key + ext_row0)
+        auto key_offset = [&](int key) __attribute__((always_inline)) {
+            if (key >= split) return int64_t(key + ext_row0) * slot_bytes + head_bytes;
+            const int32_t pg = page_entry(key);
+            return int64_t(uint64_t(uint32_t(pg)) * page_bytes) +
+                   int32_t((key & page_mask) * slot_bytes + head_bytes);
+        };
         auto dma_tile = [&](int t, int p, int32_t pg0) __attribute__((always_inline)) {
             const int key0 = kv_begin + t * BIG_T + 8 * uwave;
             const uint32_t mk = lds_sets + uint32_t(p * BIG_HALF + 8 * uwave * BIG_ROW);
             const uint32_t mv = lds_v + uint32_t(p * BIG_HALF + 8 * uwave * BIG_ROW);
-            if (key0 + 7 <= kv_last && (key0 & page_mask) + 8 <= a.page_size) {
+            if (key0 + 7 <= kv_last && key0 + 7 < split && (key0 & page_mask) + 8 <= a.page_size) {
                 const int64_t off = int64_t(uint64_t(uint32_t(pg0)) * page_bytes) +
                                     int32_t((key0 & page_mask) * slot_bytes + head_bytes);
                 big_dma4(mk, mv, dk0, dk1, dv0, dv1, Kb + off, Vb + off);
+            } else if (key0 >= split && key0 + 7 <= kv_last) {
+                // eight consecutive new-token rows
+                const int64_t off = int64_t(key0 + ext_row0) * slot_bytes + head_bytes;
+                big_dma4(mk, mv, dk0, dk1, dv0, dv1, Ke + off, Ve + off);
             } else {
 #pragma unroll
                 for (int i = 0; i < 2; ++i) {
                     const int keyk = min(key0 + 4 * i + kr, kv_last);
                     const int keyv = min(key0 + 4 * i + vr, kv_last);
-                    const int32_t pk = page_entry(keyk), pv = page_entry(keyv);
-                    const int64_t offk = int64_t(uint64_t(uint32_t(pk)) * page_bytes) +
-                                         int32_t((keyk & page_mask) * slot_bytes + head_bytes);
-                    const int64_t offv = int64_t(uint64_t(uint32_t(pv)) * page_bytes) +
-                                         int32_t((keyv & page_mask) * slot_bytes + head_bytes);
-                    big_dma1(mk + uint32_t(i * 1024), Kb + (offk + int32_t(i ? kc1 : kc0)));
-                    big_dma1(mv + uint32_t(i * 1024), Vb + (offv + int32_t(vc)));
+                    const char *bk = keyk >= split ? Ke : Kb;
+                    const char *bv = keyv >= split ? Ve : Vb;
+                    big_dma1(mk + uint32_t(i * 1024), bk + (key_offset(keyk) + int32_t(i ? kc1 : kc0)));
+                    big_dma1(mv + uint32_t(i * 1024), bv + (key_offset(keyv) + int32_t(vc)));
                 }
             }
         };
@@ -1179,10 +1193,13 @@ __global__ __launch_bounds__(512) void prefill_big_kernel(PrefillArgs a)
                 page_entry(min(kv_begin + t * BIG_T + 8 * uwave, kv_last)));
         };
 
-        // prologue: page table, then tiles 0 and 1 landed (step j loads tile j+2)
+        // prologue: page table (of the cached keys), then tiles 0 and 1 landed
+        // (step j loads tile j+2)
         {
-            const int pt_n =
-                ntiles > 0 ? min((kv_last >> a.log2_page) - pt_lo + 1, kPrefillDmaPages) : 0;
+            const int cache_last = min(kv_last, split - 1);
+            const int pt_n = ntiles > 0 && cache_last >= kv_begin
+                                 ? min((cache_last >> a.log2_page) - pt_lo + 1, kPrefillDmaPages)
+                                 : 0;
             for (int e = tid; e < pt_n; e += 512) {
                 const int32_t pg = a.kv_indices[page_base + pt_lo + e];
                 sh.pages[e] = min(max(pg, 0), int32_t(a.num_pages - 1));

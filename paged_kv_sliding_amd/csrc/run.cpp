@@ -88,7 +88,8 @@ int check_run(const pkvs_plan *p, int kind, const void *q, const void *k, const 
 hipError_t launch_prefill_pass(const pkvs_plan *p, const void *q, const void *k, const void *v,
                                int64_t num_pages, const int32_t *kv_indices, void *o, float *lse,
                                float sm_scale, float k_scale, float v_scale, hipStream_t stream,
-                               const void *fold_o = nullptr, const float *fold_lse = nullptr)
+                               const void *fold_o = nullptr, const float *fold_lse = nullptr,
+                               const void *k_ext = nullptr, const void *v_ext = nullptr)
 {
     int32_t *ws = static_cast<int32_t *>(p->int_ws);
     PrefillArgs a{};
@@ -113,6 +114,8 @@ hipError_t launch_prefill_pass(const pkvs_plan *p, const void *q, const void *k,
     a.fold_o = fold_o;
     a.fold_lse = fold_lse;
     a.table_pages = p->table_pages;
+    a.k_ext = k_ext;
+    a.v_ext = v_ext;
     return p->desc.dtype == PKVS_FP32
                ? launch_attention_fp32(a, p->desc.head_dim, p->grid_blocks, stream)
                : launch_prefill_16bit(a, p->desc.head_dim, p->prefill_variant,
@@ -165,6 +168,15 @@ int pkvs_cascade_run(const pkvs_plan *p, const void *q, const void *k_extend,
     if (p->planned_keys > 0 && (!k_cache || !v_cache || !kv_indices_d || num_pages <= 0))
         return fail(PKVS_ERR_INVALID_ARG, "the planned batch has cached keys: null cache, page "
                     "table or num_pages <= 0");
+    if (p->fused) {
+        // one pass: cached keys from the pages, new keys from k_extend / v_extend
+        hipError_t e = launch_prefill_pass(p->pre, q, k_cache, v_cache,
+                                           std::max<int64_t>(num_pages, 1), kv_indices_d, o, lse,
+                                           sm_scale, k_scale, v_scale, stream, nullptr, nullptr,
+                                           k_extend, v_extend);
+        if (e != hipSuccess) return fail(PKVS_ERR_HIP, "cascade launch: %s", hipGetErrorString(e));
+        return PKVS_OK;
+    }
     char *fws = static_cast<char *>(p->float_ws);
     void *o2 = fws + p->o2_off;
     float *lse2 = reinterpret_cast<float *>(fws + p->lse2_off);

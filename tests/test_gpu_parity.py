@@ -675,11 +675,18 @@ def cascade_run(case, trim=False, att=None, return_lse=True, **kw):
 @pytest.mark.parametrize("P_", [1, 16])
 @pytest.mark.parametrize("W", [-1, 0, 5, 100, 511])
 @pytest.mark.parametrize("trim", [False, True])
-def test_cascade_equals_one_paged_prefill(P_, W, trim):
+@pytest.mark.parametrize("variant", [0, 5])
+def test_cascade_equals_one_paged_prefill(P_, W, trim, variant):
+    """Cascade prefill against the one paged prefill over prefix + new keys;
+    variant 5 runs the cascade in one pass (cached keys from the pages, new
+    keys from the contiguous K/V, split per request), the planner's choice for
+    this small batch runs the two passes and their merge."""
     qo = [1, 70, 0, 33, 129, 5, 300, 40]
     kv = [1, 90, 9, 300, 129, 700, 301, 1000]
     case = small(qo, kv, H_q=8, H_kv=2, D=128, P_=P_, W=W, seed=P_ * 31 + W + 7 * trim)
-    (o, lse), att = cascade_run(case, trim=trim)
+    (o, lse), att = cascade_run(case, trim=trim, prefill_variant=variant)
+    if variant:
+        assert att.info().prefill_variant == variant
     ro, rl = oracle_for(case)
     compare(o, lse, ro, rl, tag=f"cascade P={P_} W={W} trim={trim} "
                                 f"variant={att.info().prefill_variant}")
@@ -728,26 +735,47 @@ def test_cascade_prefix_prefill_workload():
     compare(o, lse, ro, rl, tag="cascade prefix_prefill")
 
 
-def test_cascade_without_lse_and_without_cached_keys():
+@pytest.mark.parametrize("variant", [0, 5])
+def test_cascade_without_lse_and_without_cached_keys(variant):
     case = small([30, 9], [90, 40], H_q=4, H_kv=1, D=128, W=10, seed=73)
-    (o), _ = cascade_run(case, return_lse=False)
+    (o), _ = cascade_run(case, return_lse=False, prefill_variant=variant)
     ro, _ = oracle_for(case)
     compare(o, None, ro, None, tag="cascade no lse")
-    # no request has cached keys: the paged pass sees empty tables
+    # no request has cached keys: the paged pass sees empty tables (one pass:
+    # every key comes from the contiguous K/V, the cache is never read)
     case = small([30, 9], [30, 9], H_q=4, H_kv=1, D=128, W=10, seed=74)
-    (o, lse), _ = cascade_run(case)
+    (o, lse), _ = cascade_run(case, prefill_variant=variant)
     ro, rl = oracle_for(case)
     compare(o, lse, ro, rl, tag="cascade without cached keys")
 
 
-def test_cascade_graph_replay_follows_replans():
-    """The cascade's three launches captured once replay correctly after
-    re-plans of the same capacities (the merge reads the token count from the
-    workspace), bit for bit against eager runs."""
+@pytest.mark.parametrize("P_", [1, 16])
+def test_cascade_one_pass_split_mid_group(P_):
+    """One-pass cascade where the boundary between cached and new keys falls
+    inside a wave's 8-key staging group and inside a page (tables of 13, 4101
+    -- 1501 with single-key pages, whose plan must not span more than 2048
+    pages -- 1 and 30 cached keys), long new-token runs, window and no
+    window."""
+    qo = [200, 77, 1, 130]
+    tab = [13, 4101 if P_ > 1 else 1501, 1, 30]
+    kv = [t + q for t, q in zip(tab, qo)]
+    for W in (-1, 300):
+        case = small(qo, kv, H_q=8, H_kv=2, D=128, P_=P_, W=W, seed=77 + W + P_)
+        (o, lse), att = cascade_run(case, prefill_variant=5)
+        assert att.info().prefill_variant == 5
+        ro, rl = oracle_for(case)
+        compare(o, lse, ro, rl, tag=f"one-pass cascade P={P_} W={W}")
+
+
+@pytest.mark.parametrize("variant", [0, 5])
+def test_cascade_graph_replay_follows_replans(variant):
+    """The cascade's launches captured once replay correctly after re-plans of
+    the same capacities (the kernels read their work from the workspace), bit
+    for bit against eager runs; variant 5 is the one-pass cascade."""
     qo, kv = [40, 1, 130, 7, 64], [300, 1, 200, 500, 64]
     case = small(qo, kv, H_q=8, H_kv=2, D=128, P_=16, W=100, seed=64)
     cin = cascade_inputs(case)
-    att = make_cascade(case)
+    att = make_cascade(case, prefill_variant=variant)
     qop = case.qo_indptr.cpu().tolist()
     q_buf = case.q.clone()
     ke_buf, ve_buf = cin.k_extend.clone(), cin.v_extend.clone()

@@ -166,10 +166,11 @@ def test_prefill_items_cover_every_query_once(W, G):
     assert info.query_tile in (128 // G, 256 // G)
     assert items.shape[0] == info.num_items
     # key tiles of the kernel the plan runs: 64 keys for variant 5, else 32
-    kt = 64 if info.prefill_variant == 5 else 32
+    kt = 64 if info.prefill_variant in (5, 6) else 32
     seen = {}
     for it in items.tolist():
-        b, hk, q0, qn, pos0, kv_len, pbase, kvb = it
+        b, hk, q0, qn, pos0, kv_len, pbase, kvb, split = it[:9]
+        assert split == 2**31 - 1  # every key in the cache
         assert 1 <= qn <= info.query_tile and kv_len == kv[b] and pbase == kvp[b]
         prefix = kv[b] - qo[b]
         assert pos0 == prefix + (q0 - qop[b])
@@ -201,7 +202,7 @@ def test_prefill_first_tile_matches_paged_trim():
     qop, kvp, last = csr(qo, kv, 16)
     P.pkvs_prefill_plan(h, qop, kvp, last, 3, None, None)
     for it in P.pkvs_plan_copy_items(h).tolist():
-        b, _, q0, _, _, _, _, kvb = it
+        b, _, q0, _, _, _, _, kvb = it[:8]
         if q0 == qop[b]:
             seq, prefix = kv[b], kv[b] - qo[b]
             kv_start = seq - min(seq, W + seq - prefix)
@@ -456,7 +457,7 @@ def test_cascade_passes_cover_every_query_once():
     ext, pre = items[:n_ext], items[n_ext:]
     for part, name in ((ext, "extend"), (pre, "prefix")):
         seen = {}
-        for b, hk, q0, qn, pos0, kv_len, pbase, kvb in part:
+        for b, hk, q0, qn, pos0, kv_len, pbase, kvb in (it[:8] for it in part):
             i0 = q0 - qop[b]
             if name == "extend":
                 assert kv_len == qo[b] and pos0 == i0
@@ -473,6 +474,40 @@ def test_cascade_passes_cover_every_query_once():
     for (b0, p0), (b1, p1) in zip(bases, bases[1:]):
         assert p1 - p0 >= (qo[b0] + 255) // 256
     P.pkvs_plan_destroy(h)
+
+
+def test_cascade_one_pass_work_list():
+    """With the default head_dim-128 kernel a cascade runs in one pass: one
+    prefill item list over each request's cached keys followed by its new
+    tokens (kv_len = table + new, queries at the end, split = table length),
+    no float workspace; other kernels keep the two passes."""
+    W = 40
+    qo = [1, 70, 0, 33, 129, 300]
+    tab = [0, 20, 9, 267, 2, 100]
+    h = P.pkvs_plan_create(desc(P.PKVS_CASCADE, num_qo_heads=8, num_kv_heads=2, window_left=W,
+                                prefill_variant=5))
+    assert P.pkvs_plan_get_info(h).prefill_variant == 5
+    assert P.pkvs_workspace_size(h)[0] == 0
+    qop, kvp, last = csr(qo, tab, 16)
+    P.pkvs_cascade_plan(h, qop, kvp, last, len(qo), None, None)
+    items = P.pkvs_plan_copy_items(h).tolist()
+    assert len(items) == P.pkvs_plan_get_info(h).num_items
+    seen = {}
+    for it in items:
+        b, hk, q0, qn, pos0, kv_len, pbase, kvb, split = it[:9]
+        assert kv_len == tab[b] + qo[b] and split == tab[b] and pbase == kvp[b]
+        assert pos0 == tab[b] + (q0 - qop[b]) and kvb % 64 == 0 and kvb <= max(0, pos0 - W)
+        for t in range(q0, q0 + qn):
+            seen[(b, hk, t)] = seen.get((b, hk, t), 0) + 1
+    expect = {(b, hk, t) for b in range(len(qo)) for hk in range(2)
+              for t in range(qop[b], qop[b + 1])}
+    assert set(seen) == expect and set(seen.values()) == {1}
+    P.pkvs_plan_destroy(h)
+    # an explicit other kernel keeps the two passes (and their float workspace)
+    h2 = P.pkvs_plan_create(desc(P.PKVS_CASCADE, num_qo_heads=8, num_kv_heads=2, window_left=W,
+                                 prefill_variant=2))
+    assert P.pkvs_workspace_size(h2)[0] > 0
+    P.pkvs_plan_destroy(h2)
 
 
 def test_cascade_workspace_and_errors():
