@@ -35,7 +35,9 @@ Reported (one JSON line):
                  31, 0), the last-level cache flushed before each timed run
 Every GPU time is reported as the mean (which value and the rooflines use),
 median and minimum over the timed launches; the last-level cache is flushed
-(1 GiB written) before every timed decode launch.
+(1 GiB written) before every timed decode launch, and a short spin kernel
+keeps the GPU busy across each start event, so that the events time the
+kernels and not the host's launch latency.
 
     python bench.py [--steps K] [--warmup W] [--gpus 1] [--no-cpu-baseline]
 """
@@ -81,15 +83,46 @@ def time_stats(ts) -> dict:
     return {"mean": sum(ts) / len(ts), "median": srt[len(srt) // 2], "min": srt[0]}
 
 
+_SPIN_CYCLES = None
+
+
+def keep_gpu_busy() -> None:
+    """Enqueue a short spin kernel (about 0.1 ms) on torch's current stream.
+
+    Called right before a start event is recorded: the host then enqueues the
+    timed launch while the GPU is still spinning, so the event pair measures
+    the timed kernels, not the host's launch latency (with an idle GPU the
+    start event fires at once and the kernel only starts after the host has
+    prepared and launched it)."""
+    import torch
+
+    global _SPIN_CYCLES
+    if _SPIN_CYCLES is None:
+        # calibrate: the spin counts GPU clock ticks, whose rate is not known here
+        n = 100000
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        torch.cuda._sleep(n)  # first call loads the kernel
+        torch.cuda.synchronize()
+        a.record()
+        torch.cuda._sleep(n)
+        b.record()
+        torch.cuda.synchronize()
+        per_ms = n / max(a.elapsed_time(b), 1e-3)
+        _SPIN_CYCLES = max(1000, int(per_ms * 0.1))
+    torch.cuda._sleep(_SPIN_CYCLES)
+
+
 def timed_launches(fn, reps: int, flush=None) -> list:
     """HIP-event times (ms) of `reps` calls of fn on torch's current stream (the
-    stream the binding launches on), each after an optional flush."""
+    stream the binding launches on), each after an optional flush, with the
+    GPU kept busy across the start event (keep_gpu_busy)."""
     import torch
 
     ts = []
     for _ in range(reps):
         if flush is not None:
             flush()
+        keep_gpu_busy()
         a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
         a.record()
         fn()
@@ -820,6 +853,7 @@ def main():
                          kv_last_page_len=pre_host[2])
             if record:
                 plan_us["pre"].append((time.perf_counter() - t0) * 1e6)
+                keep_gpu_busy()
                 ev["pre"][0].record()
             pre_att.run(pre.q, pre.k_cache, pre.v_cache, pre.kv_indices, sm_scale=pre.sm_scale,
                         window_left=pre.window_left, out=o_pre, lse=l_pre)
@@ -831,6 +865,7 @@ def main():
             dec_att_w.plan(kv_indptr=dec_host[0], kv_last_page_len=dec_host[1])
             if record:
                 plan_us["dec"].append((time.perf_counter() - t0) * 1e6)
+                keep_gpu_busy()
                 ev["dec"][0].record()
             dec_att_w.run(dec.q, dec.k_cache, dec.v_cache, dec.kv_indices, sm_scale=dec.sm_scale,
                           window_left=W_dec, out=o_dec, lse=l_dec)

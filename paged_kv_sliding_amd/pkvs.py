@@ -19,7 +19,9 @@ from typing import Optional, Tuple
 import torch
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
-LIB_PATH = os.path.join(_HERE, "libpkvs.so")
+# PKVS_LIBRARY names another build of the same C ABI (the tests load a
+# sanitizer-instrumented host-only build this way); default: the in-tree one
+LIB_PATH = os.environ.get("PKVS_LIBRARY") or os.path.join(_HERE, "libpkvs.so")
 
 PKVS_OK = 0
 PKVS_ERR_INVALID_ARG = -1
