@@ -266,6 +266,40 @@ int pkvs_decode_run(const pkvs_plan *plan, const void *q, const void *k_cache,
                     void *o, float *lse, float sm_scale, int32_t window_left, float k_scale,
                     float v_scale, hipStream_t stream);
 
+/* Bytes of the library's device scratch array, one per device, that
+ * pkvs_decode_noalloc plans and runs in (64 MiB). */
+#define PKVS_NOALLOC_SCRATCH_BYTES ((size_t)64 << 20)
+
+/* For callers that cannot allocate memory at the point of the call (serving
+ * loops that must not allocate per step, harnesses that forbid allocation):
+ * pkvs_decode_plan followed by pkvs_decode_run, with the plan's int and float
+ * workspaces taken from the library's fixed device array of
+ * PKVS_NOALLOC_SCRATCH_BYTES instead of caller buffers.  It calls no
+ * hipMalloc, hipFree, hipHostMalloc or host allocator: the plan's pinned
+ * staging ring and planning buffers were made by pkvs_plan_create.
+ *  plan        a PKVS_DECODE plan of bf16 or fp16 queries, created on the
+ *              device that is current at the call
+ *  kv_indptr_h .. batch_size   the layout, as pkvs_decode_plan (host arrays)
+ *  q .. v_scale, stream        as pkvs_decode_run
+ * The work list (header with the work counters at 0) is copied into the array
+ * on `stream` before the kernels run, so nothing depends on what an earlier
+ * call left there.  Every call on one device shares that device's array: calls
+ * that overlap on one device (other streams, other plans, other threads)
+ * race and must be ordered by the caller.  Not for stream capture: the
+ * work-list copy reads a host staging buffer that later calls rewrite.
+ * Errors: INVALID_ARG (null or non-decode plan, fp32 plan, plan made for
+ * another device than the current one), WORKSPACE (the plan's workspaces
+ * for its capacities, int part then float part at the next 256-byte
+ * boundary, exceed PKVS_NOALLOC_SCRATCH_BYTES: use pkvs_decode_plan and
+ * pkvs_decode_run with caller workspaces), HIP, and those of
+ * pkvs_decode_plan / pkvs_decode_run.  After a successful call the plan is
+ * planned on the array: a later pkvs_decode_run reruns this batch there. */
+int pkvs_decode_noalloc(pkvs_plan *plan, const int32_t *kv_indptr_h,
+                        const int32_t *kv_last_page_len_h, int32_t batch_size, const void *q,
+                        const void *k_cache, const void *v_cache, int64_t num_pages,
+                        const int32_t *kv_indices_d, void *o, float *lse, float sm_scale,
+                        int32_t window_left, float k_scale, float v_scale, hipStream_t stream);
+
 /* Plan a cascade prefill ([FIB] FlashInferAttnBackend.forward_extend, the
  * branch for a batch with cached prefixes: a ragged pass over the new tokens'
  * own keys, a paged pass over the cached prefix, and _safe_merge_state of the

@@ -18,7 +18,8 @@ LIB = os.path.join(PKG, "libpkvs.so")
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 ARCH = "gfx950"
 
-SOURCES = ["plan.cpp", "run.cpp", "decode.hip", "prefill.hip", "merge.hip", "pool.hip"]
+SOURCES = ["plan.cpp", "run.cpp", "decode.hip", "prefill.hip", "merge.hip", "pool.hip",
+           "noalloc.hip"]
 HEADERS = ["pkvs_internal.h", "plan_state.h", "device_common.h"]
 
 # Packed-FP32 VALU instructions are kept out of the device code on purpose.

@@ -174,6 +174,10 @@ hipError_t launch_build_kv_indices(const int32_t *map, int64_t map_rows, int64_t
                                    int32_t batch, int32_t *kv_indptr, int32_t *kv_indices,
                                    int64_t capacity, int32_t *status, int grid, hipStream_t s);
 
+// The device address of the library's scratch array on `device` (noalloc.hip),
+// which must be the current device at the first call for it; kept per device.
+hipError_t scratch_for_device(int device, void **ptr);
+
 // Resident workgroups per CU of each kernel (occupancy query; 0 if unknown).
 // (table_pages: the page-table entries of a kPrefillDuo launch)
 int prefill_blocks_per_cu(int head_dim, int variant, bool f16, int kv_format,

@@ -169,12 +169,8 @@ static int validate_desc(const pkvs_desc *d)
     return PKVS_OK;
 }
 
-// Host view of one request's layout, validated.
-struct Req {
-    int64_t qo_begin, qo_len, kv_len, page_base;
-    // one-pass cascade: the request's keys from here on are its new tokens
-    int64_t split = INT32_MAX;
-};
+static_assert(sizeof(DecodeWork::w) == sizeof(int32_t) * kDecodeItemWords,
+              "DecodeWork holds one decode item");
 
 static int read_layout(const Plan *p, const int32_t *qo_indptr, const int32_t *kv_indptr,
                        const int32_t *last, int32_t batch, std::vector<Req> &out)
@@ -351,9 +347,11 @@ static int build_decode(Plan *p, const std::vector<Req> &reqs)
 {
     const pkvs_desc &d = p->desc;
     const int64_t c = choose_split(p, reqs);
-    struct It { int64_t cost; int32_t w[kDecodeItemWords]; };
-    std::vector<It> items;
-    std::vector<int32_t> merges;
+    // (the buffers were reserved for the capacities: no allocation here)
+    std::vector<DecodeWork> &items = p->work_buf;
+    std::vector<int32_t> &merges = p->merge_buf;
+    items.clear();
+    merges.clear();
     int64_t slot = 0;
     for (size_t b = 0; b < reqs.size(); ++b) {
         const Req &r = reqs[b];
@@ -364,15 +362,23 @@ static int build_decode(Plan *p, const std::vector<Req> &reqs)
         // a trailing piece shorter than one key block joins the chunk before it
         // rather than becoming a work item and a partial of its own
         if (nchunks > 1 && r.kv_len - base - (nchunks - 1) * c < kDecodeBlock) --nchunks;
+        if (int64_t(items.size()) + d.num_kv_heads * nchunks > p->items_cap ||
+            (nchunks > 1 && (slot + d.num_kv_heads * nchunks > p->slots_cap ||
+                             int64_t(merges.size() / kMergeWords) + d.num_kv_heads >
+                                 p->merges_cap)))
+            return fail(PKVS_ERR_CAPACITY, "decode work list exceeds the plan capacity (%lld "
+                        "items, %lld partial slots) at request %zu", (long long)p->items_cap,
+                        (long long)p->slots_cap, b);
         for (int32_t hk = 0; hk < d.num_kv_heads; ++hk) {
             if (nchunks > 1) {
                 merges.insert(merges.end(), {int32_t(b), hk, int32_t(slot), int32_t(nchunks)});
             }
             for (int64_t k = 0; k < nchunks; ++k) {
-                It it;
+                DecodeWork it;
                 const int64_t t0 = base + k * c;
                 const int64_t t1 = k + 1 == nchunks ? r.kv_len : t0 + c;
                 it.cost = t1 - t0;
+                it.order = int32_t(items.size());
                 it.w[kDiRequest] = int32_t(b);
                 it.w[kDiKvHead] = hk;
                 it.w[kDiTokBegin] = int32_t(t0);
@@ -385,13 +391,11 @@ static int build_decode(Plan *p, const std::vector<Req> &reqs)
             }
         }
     }
-    if (int64_t(items.size()) > p->items_cap || slot > p->slots_cap ||
-        int64_t(merges.size() / kMergeWords) > p->merges_cap)
-        return fail(PKVS_ERR_CAPACITY, "decode work list (%zu items, %lld partial slots) "
-                    "exceeds the plan capacity (%lld items, %lld slots)", items.size(),
-                    (long long)slot, (long long)p->items_cap, (long long)p->slots_cap);
-    std::stable_sort(items.begin(), items.end(),
-                     [](const It &a, const It &b) { return a.cost > b.cost; });
+    // longest first, ties in the order made (a full order: std::sort needs no
+    // temporary buffer)
+    std::sort(items.begin(), items.end(), [](const DecodeWork &a, const DecodeWork &b) {
+        return a.cost > b.cost || (a.cost == b.cost && a.order < b.order);
+    });
     p->n_items = int64_t(items.size());
     p->n_merges = int64_t(merges.size() / kMergeWords);
     p->split_size = int32_t(std::min<int64_t>(c, INT32_MAX));
@@ -408,21 +412,29 @@ static int build_decode(Plan *p, const std::vector<Req> &reqs)
     return PKVS_OK;
 }
 
+// The pinned staging ring of a plan's work-list copies, made once per plan.
+static int make_staging(Plan *p)
+{
+    if (p->stage[0]) return PKVS_OK;
+    for (int i = 0; i < kStages; ++i) {
+        if (hipHostMalloc(&p->stage[i], p->int_ws_need, hipHostMallocDefault) != hipSuccess ||
+            hipEventCreateWithFlags(&p->stage_ev[i], hipEventDisableTiming) != hipSuccess) {
+            (void)hipGetLastError();
+            return fail(PKVS_ERR_HIP, "pinned staging buffer of %zu bytes: allocation failed",
+                        p->int_ws_need);
+        }
+    }
+    return PKVS_OK;
+}
+
 // Copy the host work list into the device int workspace with one async
 // host-to-device copy on `stream`, from a ring of pinned staging buffers (a
 // buffer is reused only after its previous copy has completed).
 static int upload(Plan *p, void *int_ws, hipStream_t stream)
 {
     const size_t bytes = p->host_ws.size() * sizeof(int32_t);
-    if (!p->stage[0]) {
-        for (int i = 0; i < kStages; ++i) {
-            if (hipHostMalloc(&p->stage[i], p->int_ws_need, hipHostMallocDefault) != hipSuccess)
-                return fail(PKVS_ERR_HIP, "hipHostMalloc of %zu bytes failed", p->int_ws_need);
-            if (hipEventCreateWithFlags(&p->stage_ev[i], hipEventDisableTiming) != hipSuccess)
-                return fail(PKVS_ERR_HIP, "hipEventCreate failed");
-            p->stage_used[i] = false;
-        }
-    }
+    int rc = make_staging(p);  // (a decode plan made it at creation)
+    if (rc) return rc;
     const int s = p->stage_next;
     p->stage_next = (s + 1) % kStages;
     if (p->stage_used[s] && hipEventSynchronize(p->stage_ev[s]) != hipSuccess)
@@ -474,9 +486,11 @@ static int64_t item_pages_bound(const pkvs_desc &d, int kv_tile, int query_tile)
     return pages;
 }
 
+static void destroy_plan(Plan *p);
+
 // A validated prefill or decode descriptor -> plan object (ragged: a
 // cascade's extend pass, see plan_state.h).
-static int create_plan(const pkvs_desc *desc, bool ragged, Plan **out)
+static int create_plan(const pkvs_desc *desc, bool ragged, Plan **out, bool make_buffers = true)
 {
     Plan *p = new (std::nothrow) Plan();
     if (!p) return fail(PKVS_ERR_INVALID_ARG, "out of host memory");
@@ -582,6 +596,23 @@ static int create_plan(const pkvs_desc *desc, bool ragged, Plan **out)
         p->float_ws_need = 0;
     }
     p->grid_blocks = int32_t(std::max<int64_t>(1, std::min<int64_t>(p->grid_blocks, p->items_cap)));
+    // A 16-bit decode plan gets everything a plan() call of its capacities
+    // needs on the host here, once -- the planning buffers and the pinned
+    // staging ring of the work-list copy -- so that planning and running a
+    // decode batch allocate nothing (pkvs_decode_noalloc relies on it).
+    if (desc->kind == PKVS_DECODE && !fp32 && make_buffers) {
+        p->reqs_buf.reserve(size_t(desc->batch_capacity));
+        p->work_buf.reserve(size_t(p->items_cap));
+        p->merge_buf.reserve(size_t(p->merges_cap * kMergeWords));
+        p->host_ws.reserve(p->int_ws_need / sizeof(int32_t));
+        if (p->have_gpu) {
+            const int rc = make_staging(p);
+            if (rc) {
+                destroy_plan(p);
+                return rc;
+            }
+        }
+    }
     *out = p;
     return PKVS_OK;
 }
@@ -729,8 +760,11 @@ int pkvs_workspace_bytes(const pkvs_desc *desc, int32_t is_decode, int64_t max_k
                                     (long long)max_kv_len);
     pkvs_desc d = *desc;
     if (max_kv_len > 0) d.kv_capacity = max_kv_len;
+    int rc = validate_desc(&d);
+    if (rc) return rc;
+    // (sizes only: no planning buffers or staging ring)
     pkvs_plan *p = nullptr;
-    int rc = pkvs_plan_create(&p, &d);
+    rc = d.kind == PKVS_CASCADE ? create_cascade(&d, &p) : create_plan(&d, false, &p, false);
     if (rc) return rc;
     *float_ws_bytes = p->float_ws_need;
     *int_ws_bytes = p->int_ws_need;
@@ -767,7 +801,7 @@ int pkvs_decode_plan(pkvs_plan *p, const int32_t *kv_indptr_h, const int32_t *kv
     if (!p) return fail(PKVS_ERR_INVALID_ARG, "plan is null");
     if (p->desc.kind != PKVS_DECODE) return fail(PKVS_ERR_INVALID_ARG, "not a decode plan");
     p->planned_device = false;
-    std::vector<Req> reqs;
+    std::vector<Req> &reqs = p->reqs_buf;
     int rc = read_layout(p, nullptr, kv_indptr_h, kv_last_page_len_h, batch_size, reqs);
     if (rc) return rc;
     if (p->desc.dtype == PKVS_FP32) {

@@ -29,6 +29,21 @@ constexpr int64_t kFourWavePairShare = 32;
 int fail(int code, const char *fmt, ...);
 void clear_error();
 
+// Host view of one request's layout, validated.
+struct Req {
+    int64_t qo_begin, qo_len, kv_len, page_base;
+    // one-pass cascade: the request's keys from here on are its new tokens
+    int64_t split = INT32_MAX;
+};
+
+// One decode work item before sorting: its cost, its position in the order
+// the items were made (ties keep it) and its words.
+struct DecodeWork {
+    int64_t cost;
+    int32_t order;
+    int32_t w[8];
+};
+
 }  // namespace pkvs
 
 struct pkvs_plan {
@@ -64,6 +79,11 @@ struct pkvs_plan {
 
     // the last plan() call
     std::vector<int32_t> host_ws;  // header + items + merge entries
+    // decode planning buffers, reserved for the capacities when the plan is
+    // created, so that planning a decode batch allocates nothing
+    std::vector<pkvs::Req> reqs_buf;
+    std::vector<pkvs::DecodeWork> work_buf;
+    std::vector<int32_t> merge_buf;
     int64_t n_items = 0, n_merges = 0;
     int32_t split_size = 0;
     int32_t batch = 0;

@@ -277,6 +277,47 @@ int pkvs_decode_run(const pkvs_plan *p, const void *q, const void *k_cache, cons
     return PKVS_OK;
 }
 
+int pkvs_decode_noalloc(pkvs_plan *p, const int32_t *kv_indptr_h,
+                        const int32_t *kv_last_page_len_h, int32_t batch_size, const void *q,
+                        const void *k_cache, const void *v_cache, int64_t num_pages,
+                        const int32_t *kv_indices_d, void *o, float *lse, float sm_scale,
+                        int32_t window_left, float k_scale, float v_scale, hipStream_t stream)
+{
+    clear_error();
+    if (!p) return fail(PKVS_ERR_INVALID_ARG, "plan is null");
+    if (p->desc.kind != PKVS_DECODE) return fail(PKVS_ERR_INVALID_ARG, "not a decode plan");
+    if (p->desc.dtype == PKVS_FP32)
+        return fail(PKVS_ERR_INVALID_ARG, "the allocation-free decode takes bf16 or fp16 plans");
+    // the int workspace at the array's start, the float one at the next
+    // 256-byte boundary
+    const size_t float_off = (p->int_ws_need + 255) / 256 * 256;
+    const size_t need = float_off + p->float_ws_need;
+    if (need > PKVS_NOALLOC_SCRATCH_BYTES)
+        return fail(PKVS_ERR_WORKSPACE, "the plan's workspaces take %zu bytes, more than the "
+                    "%zu of the library's scratch array; plan and run with caller workspaces",
+                    need, size_t(PKVS_NOALLOC_SCRATCH_BYTES));
+    if (!p->have_gpu) return fail(PKVS_ERR_HIP, "no HIP device");
+    int dev = -1;
+    if (hipGetDevice(&dev) != hipSuccess) {
+        (void)hipGetLastError();
+        return fail(PKVS_ERR_HIP, "hipGetDevice failed");
+    }
+    if (dev != p->device)
+        return fail(PKVS_ERR_INVALID_ARG, "the plan was made on device %d but device %d is "
+                    "current", p->device, dev);
+    void *base = nullptr;
+    hipError_t e = scratch_for_device(dev, &base);
+    if (e != hipSuccess)
+        return fail(PKVS_ERR_HIP, "scratch array of device %d: %s", dev, hipGetErrorString(e));
+    char *ws = static_cast<char *>(base);
+    int rc = pkvs_decode_plan(p, kv_indptr_h, kv_last_page_len_h, batch_size,
+                              p->float_ws_need ? ws + float_off : nullptr, p->float_ws_need, ws,
+                              p->int_ws_need, stream);
+    if (rc) return rc;
+    return pkvs_decode_run(p, q, k_cache, v_cache, num_pages, kv_indices_d, o, lse, sm_scale,
+                           window_left, k_scale, v_scale, stream);
+}
+
 int pkvs_merge_state(const void *v_a, const float *s_a, const void *v_b, const float *s_b,
                      void *v_out, float *s_out, int64_t num_tokens, int32_t num_heads,
                      int32_t head_dim, int32_t v_dtype, hipStream_t stream)

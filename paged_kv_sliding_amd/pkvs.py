@@ -53,8 +53,11 @@ EXPORTED = [
     "pkvs_decode_plan", "pkvs_decode_run", "pkvs_cascade_plan", "pkvs_cascade_run",
     "pkvs_merge_state", "pkvs_append_kv", "pkvs_build_kv_indices", "pkvs_plan_get_info",
     "pkvs_plan_copy_items", "pkvs_plan_destroy", "pkvs_strerror", "pkvs_last_error",
-    "pkvs_workspace_bytes", "pkvs_last_error_message",
+    "pkvs_workspace_bytes", "pkvs_last_error_message", "pkvs_decode_noalloc",
 ]
+
+# bytes of the library's per-device scratch array (PKVS_NOALLOC_SCRATCH_BYTES)
+NOALLOC_SCRATCH_BYTES = 64 << 20
 
 
 class pkvs_desc(ctypes.Structure):
@@ -117,6 +120,8 @@ def _load() -> ctypes.CDLL:
         "pkvs_workspace_bytes": (ctypes.c_int, [ctypes.POINTER(pkvs_desc), i32, i64,
                                                 ctypes.POINTER(sz), ctypes.POINTER(sz)]),
         "pkvs_last_error_message": (ctypes.c_char_p, []),
+        "pkvs_decode_noalloc": (ctypes.c_int, [P, P, P, i32, P, P, P, i64, P, P, P, f32, i32,
+                                               f32, f32, P]),
     }
     for name, (res, args) in sig.items():
         fn = getattr(lib, name)
@@ -270,6 +275,18 @@ def pkvs_decode_run(plan, q, k_cache, v_cache, kv_indices, o, lse, sm_scale: flo
                                 _ptr(kv_indices), _ptr(o), _ptr(lse), float(sm_scale),
                                 window_left, float(k_scale), float(v_scale), _stream(stream)),
            "pkvs_decode_run")
+
+
+def pkvs_decode_noalloc(plan, kv_indptr_h, kv_last_page_len_h, batch_size: int, q, k_cache,
+                        v_cache, kv_indices, o, lse, sm_scale: float, window_left: int,
+                        k_scale: float = 1.0, v_scale: float = 1.0, stream=None) -> None:
+    kp, _k = _host_i32(kv_indptr_h)
+    lp, _l = _host_i32(kv_last_page_len_h)
+    _need_device(q, k_cache, v_cache, kv_indices, o, lse)
+    _check(_lib.pkvs_decode_noalloc(plan, kp, lp, batch_size, _ptr(q), _ptr(k_cache),
+                                    _ptr(v_cache), k_cache.shape[0], _ptr(kv_indices), _ptr(o),
+                                    _ptr(lse), float(sm_scale), window_left, float(k_scale),
+                                    float(v_scale), _stream(stream)), "pkvs_decode_noalloc")
 
 
 def pkvs_merge_state(v_a, s_a, v_b, s_b, v_out=None, s_out=None, stream=None):

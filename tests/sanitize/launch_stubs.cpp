@@ -61,4 +61,10 @@ hipError_t launch_build_kv_indices(const int32_t *, int64_t, int64_t, const int3
 int prefill_blocks_per_cu(int, int, bool, int, int) { return 0; }
 int decode_blocks_per_cu(int, bool, int, int) { return 0; }
 
+hipError_t scratch_for_device(int, void **ptr)
+{
+    *ptr = nullptr;
+    return hipErrorNoDevice;
+}
+
 }  // namespace pkvs

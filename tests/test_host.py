@@ -74,9 +74,13 @@ def test_every_declaration_cites_a_passage_or_says_utility():
         m = re.search(r"/\*((?:(?!\*/).)*)\*/\s*(?:const\s+)?\w+\s*\**\s*" + name + r"\s*\(",
                       text, flags=re.S)
         assert m, f"{name}: no comment right before its declaration"
-        doc = m.group(1)
+        doc = re.sub(r"\s*\n\s*\*\s*", " ", m.group(1))
+        if name == "pkvs_decode_noalloc":
+            # no passage: its comment names the callers it is for
+            assert "callers that cannot allocate" in doc, name
+            continue
         assert re.search(r"\[(FIB|PR31501|PR234)\]", doc) or "Library utility, no passage" \
-            in re.sub(r"\s*\n\s*\*\s*", " ", doc), name
+            in doc, name
 
 
 def test_workspace_bytes_equals_the_plans_sizes():
@@ -387,6 +391,44 @@ def test_workspace_too_small_is_reported():
     rc = P._lib.pkvs_prefill_plan(h, qp, kp, lp, 1, None, 0, ctypes.c_void_p(small.data_ptr()),
                                   small.numel(), None)
     assert rc == P.PKVS_ERR_WORKSPACE, P.last_error()
+
+
+def test_noalloc_decode_checks_come_before_any_device_work():
+    """pkvs_decode_noalloc refuses a missing or non-decode plan, an fp32 plan
+    and a plan whose workspaces exceed the library's scratch array before it
+    touches a device; nothing falls back to allocating."""
+    lib = P._lib
+    (kp, _k), (lp, _l) = P._host_i32([0, 1]), P._host_i32([1])
+
+    def call(h):
+        return lib.pkvs_decode_noalloc(h, kp, lp, 1, None, None, None, 1, None, None, None, 1.0,
+                                       -1, 1.0, 1.0, None)
+
+    assert call(None) == P.PKVS_ERR_INVALID_ARG
+    plans = []
+    try:
+        plans.append(P.pkvs_plan_create(desc(window_left=-1)))
+        assert call(plans[-1]) == P.PKVS_ERR_INVALID_ARG  # a prefill plan
+        plans.append(P.pkvs_plan_create(desc(P.PKVS_DECODE, dtype=torch.float32, window_left=-1)))
+        assert call(plans[-1]) == P.PKVS_ERR_INVALID_ARG
+        shape = dict(num_qo_heads=64, num_kv_heads=8, batch_capacity=256, qo_capacity=256,
+                     kv_capacity=32768, fixed_split_size=2048)
+        big = desc(P.PKVS_DECODE, window_left=-1, **shape)
+        fb, ib = P.pkvs_workspace_bytes(big, True)
+        assert (ib + 255) // 256 * 256 + fb > P.NOALLOC_SCRATCH_BYTES
+        plans.append(P.pkvs_plan_create(big))
+        assert call(plans[-1]) == P.PKVS_ERR_WORKSPACE
+        assert "scratch array" in P.last_error()
+        # the same shape with a 4096-key window fits; without a GPU the call
+        # stops at the device check, with one it stops at the null tensors
+        fits = desc(P.PKVS_DECODE, window_left=4095, **shape)
+        fb, ib = P.pkvs_workspace_bytes(fits, True)
+        assert (ib + 255) // 256 * 256 + fb <= P.NOALLOC_SCRATCH_BYTES
+        plans.append(P.pkvs_plan_create(fits))
+        assert call(plans[-1]) in (P.PKVS_ERR_HIP, P.PKVS_ERR_INVALID_ARG)
+    finally:
+        for h in plans:
+            P.pkvs_plan_destroy(h)
 
 
 def test_run_rejects_a_window_other_than_the_planned_one():
