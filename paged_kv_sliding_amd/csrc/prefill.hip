@@ -1236,9 +1236,9 @@ __global__ __launch_bounds__(512) void prefill_big_kernel(PrefillArgs a)
         // free), and the roles rotate (x, y, z) -> (z, x, y) from step to step.
         // The head masks S^T(j) and takes the row maximum.  Quarter q (half
         // h = q/2, 16-key step kk = q%2) runs four MFMAs of S^T(j+1) and then
-        // the four P.V MFMAs of its own 16 keys; between the MFMAs of quarters
-        // 0-1 the vector ALU makes the four 8-key probability blocks, two
-        // scores per MFMA, each block ahead of the P.V MFMAs that use it.
+        // the four P.V MFMAs of its own 16 keys; between the MFMAs the vector
+        // ALU makes the four 8-key probability blocks, each block ahead of the
+        // P.V MFMAs that use it.
         // S^T(j+1, half 0) goes to sb[z] in quarters 0-1, S^T(j+1, half 1) to
         // sb[x] (free once blocks 0-1 are made) in quarters 2-3.  Quarter 2
         // takes tile j+1's half-0 maximum, so for a tile that needs no mask and
@@ -1334,12 +1334,16 @@ __global__ __launch_bounds__(512) void prefill_big_kernel(PrefillArgs a)
 #pragma unroll
                 for (int i = 0; i < 16; ++i) dst[i] = 0.f;
             }
-            // quarter 0 makes blocks 0 (during its QK MFMAs) and 1 (during its
-            // P.V MFMAs, which use block 0); quarter 1 makes blocks 2 and 3
+            // Block 0 is made during quarter 0's QK MFMAs; block b >= 1 during
+            // quarter b-1's P.V MFMAs and quarter b's QK MFMAs (one pair of
+            // scores every other MFMA), each ahead of the P.V MFMAs that use it
+            // (blocks 0-1: half 0 in s0, blocks 2-3: half 1 in s1), so the
+            // vector ALU work is spread over 28 of the step's 32 MFMAs.
 #pragma unroll
             for (int u = 0; u < 4; ++u) {
                 dst = mfma32x32x16<F16>(kq[u], qf[kk + 2 * u], dst);
-                if (q < 2) prob2(q == 0 ? s0 : s1, 2 * q, u);
+                if (q == 0) prob2(s0, 0, u);
+                else if (u & 1) prob2(q == 1 ? s0 : s1, q, 2 + (u >> 1));
                 __builtin_amdgcn_sched_barrier(0);
             }
             if (q < 3) load_k((p + 1) % 3, q + 1);
@@ -1347,7 +1351,7 @@ __global__ __launch_bounds__(512) void prefill_big_kernel(PrefillArgs a)
 #pragma unroll
             for (int u = 0; u < 4; ++u) {
                 o[u] = mfma32x32x16<F16>(va[u], pb[q], o[u]);
-                if (q < 2) prob2(q == 0 ? s0 : s1, 2 * q + 1, u);
+                if (q < 3 && (u & 1)) prob2(q == 0 ? s0 : s1, q + 1, u >> 1);
                 __builtin_amdgcn_sched_barrier(0);
             }
             if (q < 3) load_v(p, q + 1);
