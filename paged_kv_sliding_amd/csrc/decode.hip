@@ -156,13 +156,37 @@ __device__ __forceinline__ int64_t window_page_uniform(const DecodeArgs &a, cons
     return clamp_page(a, __builtin_amdgcn_readlane(pw.cur, idx & 63));
 }
 
+// Byte offsets of a lane's loads within a 16-key half of a block, from the
+// half's first key row (this kv head), the same for every block: K row r
+// (bytes 16g.. of each 64-byte k-step group), V rows 4g+i (dims dv..).
+struct LaneOffsets {
+    uint32_t k;
+    uint32_t v[4];
+};
+
+template <int D, int KVF>
+__device__ __forceinline__ LaneOffsets lane_offsets(const DecodeArgs &a, int lane)
+{
+    constexpr int esz = KVF == 0 ? 2 : 1;
+    const int r = lane & 15, g = lane >> 4;
+    const uint32_t slot_bytes = uint32_t(a.num_kv_heads) * D * esz;
+    LaneOffsets lo;
+    lo.k = uint32_t(r) * slot_bytes + 16u * uint32_t(g);
+    const uint32_t dv = uint32_t(min(8 * r, D - 8)) * esz;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) lo.v[i] = uint32_t(4 * g + i) * slot_bytes + dv;
+    return lo;
+}
+
 template <int D, int KVF>
 __device__ __forceinline__ void decode_load(DecodeBuf<D, KVF> &buf, const DecodeArgs &a,
-                                            PageWindow &pw, int blk, int t1, int hk, int lane)
+                                            PageWindow &pw, int blk, int t1, int hk, int lane,
+                                            const LaneOffsets &lo)
 {
     using Buf = DecodeBuf<D, KVF>;
     constexpr int KS = Buf::KS, NV = Buf::NV;
     using Elem = typename std::conditional<KVF == 0, uint16_t, uint8_t>::type;
+    constexpr int esz = int(sizeof(Elem));
     const int r = lane & 15, g = lane >> 4;
     const int P = a.page_size;
     const Elem *K = static_cast<const Elem *>(a.k);
@@ -171,6 +195,51 @@ __device__ __forceinline__ void decode_load(DecodeBuf<D, KVF> &buf, const Decode
     // blocks past the end read the request's last key; the window never moves
     // past its page
     window_advance(a, pw, min(blk, last), lane);
+    auto load = [](const void *p) __attribute__((always_inline)) {
+        if constexpr (KVF == 0) return load_stream(p);
+        else return load_stream8(p);
+    };
+
+    if (P >= 16 && blk + kDecodeBlock <= t1) {
+        // A whole block with 16-key pages: each half is 16 consecutive rows of
+        // one page, so every load is a wave-uniform half base (page id read
+        // from the window, scalar arithmetic) plus the lane's fixed offset.
+        const int64_t slot_bytes = int64_t(a.num_kv_heads) * D * esz;
+        const int64_t page_bytes = slot_bytes * P;
+        const int64_t head_bytes = int64_t(hk) * D * esz;
+        const int64_t ha = window_page_uniform(a, pw, blk) * page_bytes + head_bytes +
+                           int64_t(blk & (P - 1)) * slot_bytes;
+        const int64_t hb = window_page_uniform(a, pw, blk + 16) * page_bytes + head_bytes +
+                           int64_t((blk + 16) & (P - 1)) * slot_bytes;
+        const char *const Ka = reinterpret_cast<const char *>(K) + ha;
+        const char *const Kb = reinterpret_cast<const char *>(K) + hb;
+        const char *const Va = reinterpret_cast<const char *>(V) + ha;
+        const char *const Vb = reinterpret_cast<const char *>(V) + hb;
+        if constexpr (KVF == 0) {
+#pragma unroll
+            for (int s = 0; s < KS; ++s) {
+                buf.k0[s] = load_stream(Ka + lo.k + 64 * s);
+                buf.k1[s] = load_stream(Kb + lo.k + 64 * s);
+            }
+        } else {
+#pragma unroll
+            for (int t = 0; t < Buf::KN; ++t) {
+                buf.k0[t] = load_stream16(Ka + lo.k + 64 * t);
+                buf.k1[t] = load_stream16(Kb + lo.k + 64 * t);
+            }
+        }
+#pragma unroll
+        for (int u = 0; u < NV; ++u)
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                const typename Buf::Raw xa = load(Va + lo.v[i] + 128 * esz * u);
+                const typename Buf::Raw xb = load(Vb + lo.v[i] + 128 * esz * u);
+                const typename Buf::Raw z = {};
+                buf.v[u][i] = (8 * r + 128 * u < D) ? xa : z;
+                buf.v[u][4 + i] = (8 * r + 128 * u < D) ? xb : z;
+            }
+        return;
+    }
 
     // key rows of the A operand of S^T: keys blk+r and blk+16+r;
     // value rows: keys blk+4g+i and blk+16+4g+i (i = 0..3), dims 8r..8r+7
@@ -201,10 +270,6 @@ __device__ __forceinline__ void decode_load(DecodeBuf<D, KVF> &buf, const Decode
             rv[j] = nhd_offset(window_page(a, pw, t), t & (P - 1), P, hk, a.num_kv_heads, D);
         }
     }
-    auto load = [](const Elem *p) __attribute__((always_inline)) {
-        if constexpr (KVF == 0) return load_stream(p);
-        else return load_stream8(p);
-    };
     if constexpr (KVF == 0) {
 #pragma unroll
         for (int s = 0; s < KS; ++s) {
@@ -389,18 +454,19 @@ __global__ __launch_bounds__(kDecodeThreads * NW) void decode_kernel(DecodeArgs 
             pw.cur = load_page_id(a, pw, pw.base + lane);
             pw.nxt = load_page_id(a, pw, pw.base + 64 + lane);
             DecodeBuf<D, KVF> buf[NS];
+            const LaneOffsets loff = lane_offsets<D, KVF>(a, lane);
             // blocks past the end load the request's last key (clamped) and
             // are never computed
 #pragma unroll
             for (int s = 0; s + 1 < NS; ++s)
-                decode_load<D, KVF>(buf[s], a, pw, s0 + kDecodeBlock * s, s1, hk, lane);
+                decode_load<D, KVF>(buf[s], a, pw, s0 + kDecodeBlock * s, s1, hk, lane, loff);
             int blk = s0;
             bool done = false;
             while (!done) {
 #pragma unroll
                 for (int s = 0; s < NS; ++s) {
                     decode_load<D, KVF>(buf[(s + NS - 1) % NS], a, pw, blk + kDecodeBlock * (NS - 1),
-                                   s1, hk, lane);
+                                   s1, hk, lane, loff);
                     decode_compute<D, F16, KVF>(buf[s], st, qf, blk, lo, s1, a.scale_log2, a.cap_a, lane);
                     blk += kDecodeBlock;
                     if (blk >= s1) {
