@@ -320,9 +320,14 @@ int pkvs_decode_noalloc(pkvs_plan *plan, const int32_t *kv_indptr_h,
  * i' <= i (causal) and (window_left < 0 or i' >= i - window_left).  The
  * result equals pkvs_prefill_run over one page table holding the table's keys
  * followed by the new keys.  Zero new tokens or zero cached keys are legal.
- * Builds both passes' work lists and enqueues two host-to-device copies into
- * int_ws on `stream` (int_ws == NULL: dry plan).  float_ws holds the paged
- * pass's (o, lse).  Errors as pkvs_prefill_plan (a request may have more new
+ * The plan is one pass when pkvs_plan_create found that the default kernel
+ * serves the combined problem (16-bit K/V in the query dtype, head_dim 128,
+ * capacities within its page table): each request becomes one prefill request
+ * over its cached keys followed by its new tokens, one causal sequence whose
+ * window mask is exactly the two masks above; its float workspace is then 0
+ * bytes.  Otherwise two passes.  Builds the work list(s) and enqueues the
+ * host-to-device copies into int_ws on `stream` (int_ws == NULL: dry plan).
+ * float_ws holds the paged pass's (o, lse) of a two-pass plan.  Errors as pkvs_prefill_plan (a request may have more new
  * tokens than cached keys). */
 int pkvs_cascade_plan(pkvs_plan *plan, const int32_t *qo_indptr_h, const int32_t *kv_indptr_h,
                       const int32_t *kv_last_page_len_h, int32_t batch_size, void *float_ws,
@@ -334,7 +339,10 @@ int pkvs_cascade_plan(pkvs_plan *plan, const int32_t *qo_indptr_h, const int32_t
  * v_extend [nnz_qo, num_kv_heads, head_dim] (row r is the key / value of query
  * token r); k_cache, v_cache, num_pages and kv_indices_d as pkvs_prefill_run
  * (they may be NULL / 0 when the planned batch has no cached keys); lse
- * nullable.  Two launches on `stream`: the paged pass writes its (o, lse) into
+ * nullable.  Where the plan is one pass (see pkvs_cascade_plan's float_ws:
+ * 0 bytes), one launch on `stream` reads each request's cached keys through
+ * the page table and its new keys from k_extend / v_extend in one online
+ * softmax; otherwise two launches: the paged pass writes its (o, lse) into
  * float_ws, then the ragged pass stores the merge_state combine of its own
  * (o, lse) with them into o and lse (the merge runs in its epilogue).
  * window_left must equal the plan's.  k_scale / v_scale apply to the cache
