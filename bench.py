@@ -187,7 +187,7 @@ CASCADE_WORKLOADS = {
 
 def bench_cascade(reps: int) -> dict:
     """Cascade prefill beside the one paged prefill of the same batch, both
-    timed with HIP events around run() on the launch stream."""
+    timed with HIP events around run() on the launch stream, in alternation."""
     import torch
 
     from paged_kv_sliding_amd import pkvs as P
@@ -224,11 +224,16 @@ def bench_cascade(reps: int) -> dict:
             one.run(c.q, c.k_cache, c.v_cache, c.kv_indices, sm_scale=c.sm_scale,
                     window_left=W, out=o, lse=lse)
 
-        res = {}
-        for tag, fn in (("cascade", run_cascade), ("paged", run_one)):
-            for _ in range(3):
-                fn()
-            res[tag] = time_stats(timed_launches(fn, reps))
+        # warmed and timed in alternation, so that neither side gets the
+        # clock's ramp or a colder cache than the other
+        for _ in range(10):
+            run_cascade()
+            run_one()
+        ts = {"cascade": [], "paged": []}
+        for _ in range(reps):
+            ts["cascade"] += timed_launches(run_cascade, 1)
+            ts["paged"] += timed_launches(run_one, 1)
+        res = {tag: time_stats(t) for tag, t in ts.items()}
         flops = prefill_flops(c)
         out[name] = {"ms": round(res["cascade"]["mean"], 4),
                      "ms_median": round(res["cascade"]["median"], 4),
