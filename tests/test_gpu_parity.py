@@ -767,6 +767,22 @@ def test_cascade_one_pass_split_mid_group(P_):
         compare(o, lse, ro, rl, tag=f"one-pass cascade P={P_} W={W}")
 
 
+@pytest.mark.parametrize("dtype,cap", [(torch.float16, 0.0), (torch.bfloat16, 30.0),
+                                       (torch.float16, 20.0)])
+def test_cascade_one_pass_fp16_and_soft_cap(dtype, cap):
+    """The one-pass cascade (variant 5; no float workspace) in IEEE half and
+    with a logits soft cap, against the oracle on the combined layout."""
+    qo = [70, 1, 129, 300]
+    kv = [90, 300, 129, 1000]
+    case = small(qo, kv, H_q=8, H_kv=2, D=128, P_=16, W=100, seed=int(cap) + 3, dtype=dtype,
+                 cap=cap)
+    (o, lse), att = cascade_run(case, prefill_variant=5)
+    info = att.info()
+    assert info.prefill_variant == 5 and info.float_ws_bytes == 0, "expected the one-pass plan"
+    ro, rl = oracle_for(case)
+    compare(o, lse, ro, rl, tag=f"one-pass cascade {dtype} cap={cap}")
+
+
 @pytest.mark.parametrize("variant", [0, 5])
 def test_cascade_graph_replay_follows_replans(variant):
     """The cascade's launches captured once replay correctly after re-plans of
