@@ -224,6 +224,30 @@ def test_decode_small_ragged(P_, W, split):
     assert (o[-1] == 0).all() and torch.isneginf(lse[-1]).all()  # keyless request
 
 
+@pytest.mark.parametrize("decode", [False, True])
+def test_empty_batch_then_a_real_one(decode):
+    """A plan of zero requests launches kernels that find no work and write
+    nothing (the NaN-filled outputs stay NaN); the same plan object then runs
+    a real batch correctly."""
+    qo = [1, 1, 1] if decode else [30, 1, 64]
+    kv = [40, 700, 5] if decode else [30, 200, 64]
+    case = small(qo, kv, H_q=8, H_kv=2, D=128, P_=16, W=63, seed=41, decode=decode,
+                 split=64 if decode else -1)
+    att = make_attention(case)
+    z = torch.zeros(1, dtype=torch.int32)
+    att.plan(qo_indptr=None if decode else z, kv_indptr=z,
+             kv_last_page_len=torch.zeros(0, dtype=torch.int32))
+    assert att.info().num_items == 0
+    o, lse = poisoned_outputs(case.q)
+    att.run(case.q, case.k_cache, case.v_cache, case.kv_indices, sm_scale=case.sm_scale,
+            window_left=63, out=o, lse=lse)
+    torch.cuda.synchronize()
+    assert torch.isnan(o.float()).all() and torch.isnan(lse).all(), "an empty batch wrote outputs"
+    o, lse = gpu_run(case, att=att)
+    ro, rl = oracle_for(case)
+    compare(o, lse, ro, rl, tag=f"after an empty batch, decode={decode}")
+
+
 @pytest.mark.parametrize("D,G", [(64, 4), (128, 1), (128, 8), (128, 16), (256, 2)])
 def test_decode_head_shapes(D, G):
     kv = [7, 300, 1500, 64]
