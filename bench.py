@@ -15,7 +15,9 @@ Reported (one JSON line):
                  average duration, measured with HIP events on the launch stream
   decode         KV-read GB/s of the decode run: sum_b H_kv*n_b*D*2B*2 bytes over
                  the decode run's duration (chunk kernel + merge kernel)
-  roofline       prefill kernel against the bf16 dense MFMA peak
+  roofline       prefill kernel against the bf16 dense MFMA peak (the published
+                 2.5 PFLOP/s; device_peak: CUs x peak clock x 4096 FLOP/clk/CU
+                 from the device's properties, beside it)
   roofline_decode  decode against the HBM peak
   cpu_baseline   the CPU oracle (fp64, threads over query rows on the host's
                  cores) on a bounded sample of the prefill workload, in the same
@@ -60,6 +62,34 @@ PEAK_HBM_GBPS = 8000.0      # MI355X HBM3E
 # bf16), as rocprofv3 names it, without the closing bracket
 PREFILL_KERNEL = "prefill_big_kernel<false"
 kXCDS = 8                   # XCDs of an MI355X (GRBM counters are summed over them)
+
+
+# dense bf16 MFMA FLOPs per clock and CU on gfx950: 4 SIMDs, each finishing a
+# 32x32x16 product (32768 FLOPs) every 32 clocks (the busy cycles rocprofv3
+# counts per MFMA)
+MFMA_BF16_FLOP_PER_CLK_CU = 4 * 1024
+
+
+def device_peak() -> dict:
+    """The bf16 dense MFMA peak from the device's own properties: compute units
+    x peak engine clock (hipDeviceGetAttribute) x MFMA_BF16_FLOP_PER_CLK_CU."""
+    import ctypes
+
+    import torch
+
+    cus = torch.cuda.get_device_properties(0).multi_processor_count
+    clk_khz = ctypes.c_int(0)
+    try:
+        hip = ctypes.CDLL("libamdhip64.so")
+        # hipDeviceAttributeClockRate: entry 5 of hipDeviceAttribute_t (ROCm 7
+        # hip_runtime_api.h), the peak clock in kHz
+        rc = hip.hipDeviceGetAttribute(ctypes.byref(clk_khz), 5, torch.cuda.current_device())
+    except OSError:
+        rc = -1
+    if rc != 0 or clk_khz.value <= 0:
+        return {"cus": cus, "max_clock_mhz": None, "tflops": None}
+    tflops = cus * clk_khz.value * 1e3 * MFMA_BF16_FLOP_PER_CLK_CU / 1e12
+    return {"cus": cus, "max_clock_mhz": round(clk_khz.value / 1e3), "tflops": round(tflops, 1)}
 
 
 def prefill_flops(case) -> int:
@@ -962,7 +992,8 @@ def main():
                             "traffic": load_traffic(PREFILL_KERNEL + ">"),
                             "algorithmic_bytes": prefill_algorithmic_bytes(pre),
                             "kernel": PREFILL_KERNEL + ">",
-                            "work_per_launch": flops}
+                            "work_per_launch": flops,
+                            "device_peak": device_peak()}
     if "dec" in res:
         st, gbps, nbytes = res["dec"]
         line["decode"] = {"value": round(gbps, 1), "unit": "GB/s", "ms": round(st["mean"], 4),
