@@ -640,7 +640,7 @@ def summarize_prefill_counters(d: str, out_md: str) -> None:
              "Workload: one request, 32768 query tokens, no prefix, window_left 4095, "
              "32 query / 8 KV heads, head_dim 128, page_size 16, bf16.",
              f"Kernel sources at digest `{digest}`.  Device: {cus} CUs, {simds} SIMDs.", "",
-             "Commands (from the repository root, on the GPU box; one pass per run):", "", "```"]
+             "Commands (from the repository root, on a machine with the MI355X; one pass per run):", "", "```"]
     for pas, ctrs in PREFILL_COUNTER_PASSES.items():
         lines.append(f"rocprofv3 --pmc {' '.join(ctrs)} -d <dir>/{pas} -o p --output-format csv "
                      f"-- python3 bench.py --profile-kernel prefill --reps 5")
