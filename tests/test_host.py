@@ -393,6 +393,13 @@ def test_workspace_too_small_is_reported():
     assert rc == P.PKVS_ERR_WORKSPACE, P.last_error()
 
 
+def test_noalloc_scratch_size_matches_the_header():
+    m = re.search(r"#define PKVS_NOALLOC_SCRATCH_BYTES \(\(size_t\)(\d+) << (\d+)\)",
+                  open(HEADER).read())
+    assert m, "PKVS_NOALLOC_SCRATCH_BYTES not found in include/pkvs.h"
+    assert int(m.group(1)) << int(m.group(2)) == P.NOALLOC_SCRATCH_BYTES
+
+
 def test_noalloc_decode_checks_come_before_any_device_work():
     """pkvs_decode_noalloc refuses a missing or non-decode plan, an fp32 plan
     and a plan whose workspaces exceed the library's scratch array before it
