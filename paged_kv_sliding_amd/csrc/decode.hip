@@ -408,19 +408,32 @@ __global__ __launch_bounds__(kDecodeThreads * NW) void decode_kernel(DecodeArgs 
     // the launch ends when the slowest finishes its last item, not its fourth.
     // (One wave: claimed at the item's end; several: claimed by thread 0 at the
     // item's start and passed on through LDS at its end.)
+    // With a workgroup for every item there is nothing to hand out: each takes
+    // item blockIdx.x only and the counters are not touched (they stay 0).
     int32_t *const ctr = a.ws;
+    const bool claiming = int(gridDim.x) < n_items;
+    // Every processed item is followed (one wave) or preceded (several) by
+    // exactly one claim, so a launch makes n_items claims, returning 0 ..
+    // n_items-1: the workgroup that draws n_items-1 makes the launch's last
+    // claim and puts the counter back to 0 for the next launch.
     auto next_item = [&]() __attribute__((always_inline)) {
+        if (!claiming) return n_items;
         int v = 0;
-        if (lane == 0) v = atomicAdd(ctr + kHdrNextItem, 1);
+        if (lane == 0) {
+            v = atomicAdd(ctr + kHdrNextItem, 1);
+            if (v == n_items - 1) ctr[kHdrNextItem] = 0;
+        }
         return int(gridDim.x) + __builtin_amdgcn_readfirstlane(v);
     };
     // Workgroups past the item count have nothing to claim: they leave without
-    // touching the counters, and only the others count themselves finished.
+    // touching the counter.
     if (int(blockIdx.x) >= n_items) return;
-    const int participants = min(int(gridDim.x), n_items);
     for (int it = blockIdx.x; it < n_items;) {
         int claimed = 0;
-        if (NW > 1 && tid == 0) claimed = atomicAdd(ctr + kHdrNextItem, 1);
+        if (NW > 1 && claiming && tid == 0) {
+            claimed = atomicAdd(ctr + kHdrNextItem, 1);
+            if (claimed == n_items - 1) ctr[kHdrNextItem] = 0;
+        }
         const int32_t *w = a.ws + kHeaderWords + int64_t(it) * kDecodeItemWords;
         const int b = w[kDiRequest], hk = w[kDiKvHead];
         const int t0 = w[kDiTokBegin], t1 = w[kDiTokEnd], lo = w[kDiVisLo];
@@ -567,18 +580,12 @@ __global__ __launch_bounds__(kDecodeThreads * NW) void decode_kernel(DecodeArgs 
         }
         if constexpr (NW > 1) {
             // also orders this item's LDS reads before the next item's writes
-            if (tid == 0) sh.next_item = int(gridDim.x) + claimed;
+            if (tid == 0) sh.next_item = claiming ? int(gridDim.x) + claimed : n_items;
             __syncthreads();
             it = sh.next_item;
         } else {
             it = next_item();
         }
-    }
-    // the last participating workgroup puts the counters back to 0 (each has
-    // taken its last item before it counts itself finished)
-    if (tid == 0 && atomicAdd(ctr + kHdrDoneGroups, 1) == participants - 1) {
-        ctr[kHdrNextItem] = 0;
-        ctr[kHdrDoneGroups] = 0;
     }
 }
 

@@ -21,13 +21,12 @@ enum HeaderField {
     kHdrItemWords = 3,
     // work counters of the kernels that hand out items at run time: the next
     // item past the first grid-stride round (the decode kernel: one counter;
-    // the prefill kernel: one per XCD, kXcds words), and the workgroups that
-    // have finished; plan() uploads them as 0 and the last of a launch's
-    // participating workgroups (the first min(grid, items); the others leave
-    // without touching the counters) puts them back to 0, so every launch
-    // (and graph replay) starts from 0
+    // the prefill kernel: one per XCD, kXcds words).  plan() uploads them as
+    // 0; a launch with a workgroup for every item never touches them, and in
+    // one with fewer workgroups each processed item makes exactly one claim,
+    // so the claim that draws the last value puts its counter back to 0:
+    // every launch (and graph replay) starts from 0
     kHdrNextItem = 4,
-    kHdrDoneGroups = 12,
 };
 // XCDs of the device: consecutive workgroups of a launch go to consecutive
 // XCDs (each with its own L2), so workgroup b runs on XCD b mod kXcds

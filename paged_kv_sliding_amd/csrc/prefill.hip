@@ -1111,12 +1111,21 @@ __global__ __launch_bounds__(512) void prefill_big_kernel(PrefillArgs a)
     const int xcd = blockIdx.x % kXcds;
     const int xcd_groups = (int(gridDim.x) - xcd + kXcds - 1) / kXcds;
     // Workgroups past the item count have nothing to claim: they leave without
-    // touching the counters, and only the others count themselves finished.
+    // touching the counters.
     if (int(blockIdx.x) >= n_items) return;
-    const int participants = min(int(gridDim.x), n_items);
+    // With a workgroup for every item nothing is handed out and the counters
+    // are not touched.  Otherwise each processed item starts with one claim
+    // on its XCD's counter, so that counter sees exactly as many claims as
+    // the XCD has items, returning 0 .. n-1: the workgroup that draws n-1
+    // makes its last claim and puts it back to 0 for the next launch.
+    const bool claiming = int(gridDim.x) < n_items;
+    const int xcd_items = (n_items - xcd + kXcds - 1) / kXcds;
     for (int it = blockIdx.x; it < n_items;) {
         int claimed = 0;
-        if (tid == 0) claimed = atomicAdd(ctr + kHdrNextItem + xcd, 1);
+        if (claiming && tid == 0) {
+            claimed = atomicAdd(ctr + kHdrNextItem + xcd, 1);
+            if (claimed == xcd_items - 1) ctr[kHdrNextItem + xcd] = 0;
+        }
         const int32_t *w = a.ws + kHeaderWords + int64_t(it) * kPrefillItemWords;
         const int hk = w[kPiKvHead], q_begin = w[kPiQBegin], q_count = w[kPiQCount];
         const int pos0 = w[kPiPos0], kv_len = w[kPiKvLen];
@@ -1420,16 +1429,10 @@ __global__ __launch_bounds__(512) void prefill_big_kernel(PrefillArgs a)
         }
         // the loads of the tiles past the last are still in flight: drain them
         // before the next item's prologue rewrites the table and the sets
-        if (tid == 0) sh.next_item = xcd + kXcds * (xcd_groups + claimed);
+        if (tid == 0) sh.next_item = claiming ? xcd + kXcds * (xcd_groups + claimed) : n_items;
         __builtin_amdgcn_s_waitcnt(0);
         __syncthreads();
         it = sh.next_item;
-    }
-    // the last participating workgroup puts the counters back to 0 (each has
-    // claimed its last item before it counts itself finished)
-    if (tid == 0 && atomicAdd(ctr + kHdrDoneGroups, 1) == participants - 1) {
-        for (int x = 0; x < kXcds; ++x) ctr[kHdrNextItem + x] = 0;
-        ctr[kHdrDoneGroups] = 0;
     }
 }
 
@@ -1521,10 +1524,19 @@ void prefill_duo_kernel(PrefillArgs a)
     const int xcd = blockIdx.x % kXcds;
     const int xcd_groups = (int(gridDim.x) - xcd + kXcds - 1) / kXcds;
     if (int(blockIdx.x) >= n_items) return;
-    const int participants = min(int(gridDim.x), n_items);
+    // With a workgroup for every item nothing is handed out and the counters
+    // are not touched.  Otherwise each processed item starts with one claim
+    // on its XCD's counter, so that counter sees exactly as many claims as
+    // the XCD has items, returning 0 .. n-1: the workgroup that draws n-1
+    // makes its last claim and puts it back to 0 for the next launch.
+    const bool claiming = int(gridDim.x) < n_items;
+    const int xcd_items = (n_items - xcd + kXcds - 1) / kXcds;
     for (int it = blockIdx.x; it < n_items;) {
         int claimed = 0;
-        if (tid == 0) claimed = atomicAdd(ctr + kHdrNextItem + xcd, 1);
+        if (claiming && tid == 0) {
+            claimed = atomicAdd(ctr + kHdrNextItem + xcd, 1);
+            if (claimed == xcd_items - 1) ctr[kHdrNextItem + xcd] = 0;
+        }
         const int32_t *w = a.ws + kHeaderWords + int64_t(it) * kPrefillItemWords;
         const int hk = w[kPiKvHead], q_begin = w[kPiQBegin], q_count = w[kPiQCount];
         const int pos0 = w[kPiPos0], kv_len = w[kPiKvLen];
@@ -1789,14 +1801,10 @@ void prefill_duo_kernel(PrefillArgs a)
                 }
             if (a.lse && hw == 0) a.lse[lrow] = lse_row;
         }
-        if (tid == 0) *next_item_slot = xcd + kXcds * (xcd_groups + claimed);
+        if (tid == 0) *next_item_slot = claiming ? xcd + kXcds * (xcd_groups + claimed) : n_items;
         __builtin_amdgcn_s_waitcnt(0);
         __syncthreads();
         it = *next_item_slot;
-    }
-    if (tid == 0 && atomicAdd(ctr + kHdrDoneGroups, 1) == participants - 1) {
-        for (int x = 0; x < kXcds; ++x) ctr[kHdrNextItem + x] = 0;
-        ctr[kHdrDoneGroups] = 0;
     }
 }
 
