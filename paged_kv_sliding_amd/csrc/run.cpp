@@ -269,7 +269,7 @@ int pkvs_decode_run(const pkvs_plan *p, const void *q, const void *k_cache, cons
         hipStreamIsCapturing(stream, &capture) != hipSuccess)
         return fail(PKVS_ERR_HIP, "hipStreamIsCapturing failed");
     if (p->merges_cap > 0 && (p->n_merges > 0 || capture != hipStreamCaptureStatusNone)) {
-        const int grid = int(std::min<int64_t>(p->merges_cap * group, int64_t(p->num_cus) * 16));
+        const int grid = int(std::min<int64_t>(p->merges_cap * group, int64_t(p->num_cus) * 64));
         e = launch_decode_merge(a, p->desc.head_dim, f16, std::max(grid, 1), stream);
         if (e != hipSuccess)
             return fail(PKVS_ERR_HIP, "decode merge launch: %s", hipGetErrorString(e));
