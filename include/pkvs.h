@@ -320,9 +320,9 @@ int pkvs_decode_noalloc(pkvs_plan *plan, const int32_t *kv_indptr_h,
  * i' <= i (causal) and (window_left < 0 or i' >= i - window_left).  The
  * result equals pkvs_prefill_run over one page table holding the table's keys
  * followed by the new keys.  Zero new tokens or zero cached keys are legal.
- * The plan is one pass when pkvs_plan_create found that the default kernel
- * serves the combined problem (16-bit K/V in the query dtype, head_dim 128,
- * capacities within its page table): each request becomes one prefill request
+ * The plan is one pass when pkvs_plan_create found that a kernel reading
+ * split key ranges serves the combined problem (16-bit K/V in the query dtype;
+ * prefill_variant 0, 1, 2 or 5): each request becomes one prefill request
  * over its cached keys followed by its new tokens, one causal sequence whose
  * window mask is exactly the two masks above; its float workspace is then 0
  * bytes.  Otherwise two passes.  Builds the work list(s) and enqueues the

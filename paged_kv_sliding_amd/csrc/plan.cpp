@@ -646,20 +646,24 @@ static size_t align256(size_t x) { return (x + 255) / 256 * 256; }
 // workspace, and the extend pass folds them into its own in its epilogue.
 static int create_cascade(const pkvs_desc *desc, Plan **out)
 {
-    // One pass when the default kernel serves the combined problem: each
-    // request's cached keys followed by its new tokens form one causal
-    // sequence (cached key j at position j, new token i at kv_len_b + i), and
-    // the window mask over it is exactly the pair of masks the two passes
-    // apply; the kernel reads keys before a request's split from the cache
-    // and the rest from the contiguous new-token K/V.
+    // One pass when a kernel that reads split key ranges (the default 64-key
+    // kernel, or the register-staged 128- and 256-row ones) serves the
+    // combined problem: each request's cached keys followed by its new tokens
+    // form one causal sequence (cached key j at position j, new token i at
+    // kv_len_b + i), and the window mask over it is exactly the pair of masks
+    // the two passes apply; the kernel reads keys before a request's split
+    // from the cache and the rest from the contiguous new-token K/V.
     if (desc->kv_format == PKVS_KV_SAME && desc->dtype != PKVS_FP32 &&
         desc->kv_capacity + desc->qo_capacity <= (int64_t(1) << 30)) {
+        // (the cascade's own causality: causal, the window mask described
+        // above; non-causal (no window), every key of the sequence)
         pkvs_desc f = *desc;
         f.kind = PKVS_PREFILL;
-        f.causal = 1;
         f.kv_capacity = desc->kv_capacity + desc->qo_capacity;
         Plan *fp = nullptr;
-        if (create_plan(&f, false, &fp) == PKVS_OK && fp->prefill_variant == kPrefillBig) {
+        if (create_plan(&f, false, &fp) == PKVS_OK &&
+            (fp->prefill_variant == kPrefillBig || fp->prefill_variant == kPrefillRows128 ||
+             fp->prefill_variant == kPrefillRows256)) {
             Plan *p = new (std::nothrow) Plan();
             if (!p) {
                 destroy_plan(fp);

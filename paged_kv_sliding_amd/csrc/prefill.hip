@@ -102,11 +102,16 @@ struct RowAddr {
     const int32_t *kv_indices;
     int64_t num_pages, page_stride, slot_stride, head_off;
     int page_base, log2_page, page_mask, kv_len;
+    // one-pass cascade: keys from `split` on are new-token rows of the
+    // contiguous K/V (key k on row k + ext_row0); INT32_MAX: none
+    int split = INT32_MAX, ext_row0 = 0;
 
     __device__ __forceinline__ int clamp_key(int key) const { return min(key, kv_len - 1); }
+    // (keys past the split have no page: their entry is never read)
     __device__ __forceinline__ int32_t page_id(int key) const
     {
-        return kv_indices[page_base + (clamp_key(key) >> log2_page)];
+        const int k = min(clamp_key(key), split - 1);
+        return k < 0 ? 0 : kv_indices[page_base + (k >> log2_page)];
     }
     // element offset of `key` (clamped into the request) on page `pg`; the
     // planner keeps page_stride below 2^31, so one 32x32->64 multiply does
@@ -152,9 +157,18 @@ __device__ __forceinline__ void stage_load(Stage<D, NW, KVF> &st, const PrefillA
     for (int i = 0; i < S::KCH; ++i) {
         const int c = tid + i * S::T;
         if (chunk_exists<D, NW>(c)) {
-            const int64_t off = ra.offset(st.page[i], k0 + c / CPR) + (c % CPR) * 8;
-            st.k[i] = *reinterpret_cast<const Raw *>(K + off);
-            st.v[i] = *reinterpret_cast<const Raw *>(V + off);
+            const int key = k0 + c / CPR;
+            if (KVF == 0 && ra.clamp_key(key) >= ra.split) {
+                // a new token's row of the contiguous K/V (16-bit, like the cache)
+                const int64_t off = int64_t(ra.clamp_key(key) + ra.ext_row0) * ra.slot_stride +
+                                    ra.head_off + (c % CPR) * 8;
+                st.k[i] = *reinterpret_cast<const Raw *>(static_cast<const Elem *>(a.k_ext) + off);
+                st.v[i] = *reinterpret_cast<const Raw *>(static_cast<const Elem *>(a.v_ext) + off);
+            } else {
+                const int64_t off = ra.offset(st.page[i], key) + (c % CPR) * 8;
+                st.k[i] = *reinterpret_cast<const Raw *>(K + off);
+                st.v[i] = *reinterpret_cast<const Raw *>(V + off);
+            }
         }
     }
 }
@@ -375,6 +389,8 @@ __global__ __launch_bounds__(NW * 64) void prefill_kernel(PrefillArgs a)
         ra.page_base = w[kPiPageBase];
         ra.kv_len = kv_len;
         ra.head_off = int64_t(hk) * D;
+        ra.split = DMA ? INT32_MAX : w[kPiSplit];
+        ra.ext_row0 = q_begin - pos0;
         const int pt_lo = kv_begin >> a.log2_page;
         const int32_t head_bytes = int32_t(ra.head_off * 2);
 

@@ -742,11 +742,14 @@ def test_cascade_fp32_and_no_window_non_causal():
     (o, lse), _ = cascade_run(case)
     ro, rl = oracle_for(case)
     compare(o, lse, ro, rl, tag="cascade fp32")
-    case = small([20, 7, 64], [50, 7, 400], H_q=8, H_kv=2, D=128, W=-1, seed=23)
-    case.causal = False
-    (o, lse), _ = cascade_run(case)
-    ro, rl = oracle_for(case)
-    compare(o, lse, ro, rl, tag="cascade non-causal")
+    # non-causal (no window): the one-pass plans (variants 1 and 5) keep the
+    # cascade's causality, the two-pass one (variant 3) its passes'
+    for variant in (0, 1, 3, 5):
+        case = small([20, 7, 64], [50, 7, 400], H_q=8, H_kv=2, D=128, W=-1, seed=23)
+        case.causal = False
+        (o, lse), att = cascade_run(case, prefill_variant=variant)
+        ro, rl = oracle_for(case)
+        compare(o, lse, ro, rl, tag=f"cascade non-causal, variant {att.info().prefill_variant}")
 
 
 def test_cascade_prefix_prefill_workload():

@@ -489,14 +489,17 @@ def test_workload_plans_fit_their_capacities():
 
 
 def test_cascade_passes_cover_every_query_once():
-    """A cascade plan lists its extend pass (keys = the request's own query
+    """A two-pass cascade plan (a kernel variant without split key ranges: the
+    4x64-row one) lists its extend pass (keys = the request's own query
     tokens, read through a row-index table) and then its prefix pass (queries
     placed after every cached key of the table), each covering every query
     once.  A request may have more new tokens than cached keys."""
     W = 40
     qo = [1, 70, 0, 33, 129, 300]
     tab = [0, 20, 9, 267, 2, 100]  # cached keys in each request's table
-    h = P.pkvs_plan_create(desc(P.PKVS_CASCADE, num_qo_heads=8, num_kv_heads=2, window_left=W))
+    h = P.pkvs_plan_create(desc(P.PKVS_CASCADE, num_qo_heads=8, num_kv_heads=2, window_left=W,
+                                prefill_variant=3))
+    assert P.pkvs_plan_get_info(h).float_ws_bytes > 0, "expected the two-pass plan"
     qop, kvp, last = csr(qo, tab, 16)
     P.pkvs_cascade_plan(h, qop, kvp, last, len(qo), None, None)
     info = P.pkvs_plan_get_info(h)
@@ -526,10 +529,11 @@ def test_cascade_passes_cover_every_query_once():
 
 
 def test_cascade_one_pass_work_list():
-    """With the default head_dim-128 kernel a cascade runs in one pass: one
-    prefill item list over each request's cached keys followed by its new
+    """With a kernel that reads split key ranges (variant 5, the default for
+    head_dim 128, and the register-staged 1 and 2) a cascade runs in one pass:
+    one prefill item list over each request's cached keys followed by its new
     tokens (kv_len = table + new, queries at the end, split = table length),
-    no float workspace; other kernels keep the two passes."""
+    no float workspace; the other kernels keep the two passes."""
     W = 40
     qo = [1, 70, 0, 33, 129, 300]
     tab = [0, 20, 9, 267, 2, 100]
@@ -552,17 +556,19 @@ def test_cascade_one_pass_work_list():
               for t in range(qop[b], qop[b + 1])}
     assert set(seen) == expect and set(seen.values()) == {1}
     P.pkvs_plan_destroy(h)
-    # an explicit other kernel keeps the two passes (and their float workspace)
-    h2 = P.pkvs_plan_create(desc(P.PKVS_CASCADE, num_qo_heads=8, num_kv_heads=2, window_left=W,
-                                 prefill_variant=2))
-    assert P.pkvs_workspace_size(h2)[0] > 0
-    P.pkvs_plan_destroy(h2)
+    for variant, one_pass in ((1, True), (2, True), (3, False), (4, False), (6, False)):
+        h2 = P.pkvs_plan_create(desc(P.PKVS_CASCADE, num_qo_heads=8, num_kv_heads=2,
+                                     window_left=W, prefill_variant=variant))
+        assert (P.pkvs_workspace_size(h2)[0] == 0) == one_pass, variant
+        P.pkvs_plan_destroy(h2)
 
 
 def test_cascade_workspace_and_errors():
+    """The two-pass form (variant 3 reads no split key ranges): its float
+    workspace holds the paged pass's (o, lse)."""
     kw = dict(num_qo_heads=8, num_kv_heads=2, window_left=31, qo_capacity=1000,
               kv_capacity=500, batch_capacity=4)
-    h = P.pkvs_plan_create(desc(P.PKVS_CASCADE, **kw))
+    h = P.pkvs_plan_create(desc(P.PKVS_CASCADE, prefill_variant=3, **kw))
     fb, ib = P.pkvs_workspace_size(h)
     rows = 1000 * 8
     assert fb >= rows * 128 * 2 + rows * 4  # the paged pass's (o, lse)
