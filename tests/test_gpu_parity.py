@@ -493,6 +493,86 @@ def test_graph_replay_follows_replans(decode, nw, split):
             compare(want_o, want_l, ro, rl, tag=f"graph decode={decode} nw={nw} split={split}")
 
 
+@pytest.mark.parametrize("decode", [False, True])
+def test_run_time_claiming_repeats_and_replays(decode):
+    """Batches with more work items than the launch has workgroups, so items
+    are handed out at run time and each launch must leave its claim counters
+    at 0: three eager runs in a row into NaN-filled outputs, each checked
+    row by row against the oracle, then one captured run replayed after
+    re-plans that alternate between batches with and without run-time
+    claiming, every replay equal to an eager run of the batch planned last."""
+    rng = np.random.default_rng(5 + decode)
+    if decode:
+        B = 300
+        kv = [int(x) for x in rng.integers(1, 200, size=B)]
+        case = small([1] * B, kv, H_q=32, H_kv=8, D=128, P_=16, W=31, seed=71, decode=True,
+                     spare=5)
+        att = make_attention(case, disable_split_kv=True)
+        few = list(range(0, B, 8))
+    else:
+        qo = [1200, 900, 1100, 1000]
+        case = small(qo, [q + 50 for q in qo], H_q=32, H_kv=8, D=128, P_=16, W=127, seed=72)
+        att = make_attention(case, prefill_variant=5)
+        few = [1]
+    ro, rl = oracle_for(case)
+    for rep in range(3):
+        o, lse = gpu_run(case, att=att)
+        info = att.info()
+        assert info.num_items > info.grid_blocks, (info.num_items, info.grid_blocks)
+        assert_all_written(case, o, lse, tag=f"claiming run {rep}")
+        compare(o, lse, ro, rl, tag=f"claiming run {rep}, decode={decode}")
+    # one captured run, replayed after re-plans with and without claiming
+    B, n_q = case.batch_size, case.q.shape[0]
+    q_buf, idx_buf = case.q.clone(), case.kv_indices.clone()
+    o_buf = torch.zeros_like(case.q)
+    l_buf = torch.zeros(n_q, case.num_qo_heads, dtype=torch.float32, device=DEV)
+
+    def plan(layout):
+        _, pages, qo_ind, kv_ind, last = layout
+        q_buf.zero_()
+        q_buf[:len(layout[0])] = case.q[torch.tensor(layout[0], device=DEV)]
+        idx_buf.zero_()
+        idx_buf[:len(pages)] = pages.to(DEV)
+        if decode:
+            att.plan(kv_indptr=kv_ind, kv_last_page_len=last)
+        else:
+            att.plan(qo_indptr=qo_ind, kv_indptr=kv_ind, kv_last_page_len=last)
+
+    def run():
+        att.run(q_buf, case.k_cache, case.v_cache, idx_buf, sm_scale=case.sm_scale,
+                window_left=case.window_left, out=o_buf, lse=l_buf)
+
+    everything = _sub_layout(case, list(range(B)))
+    plan(everything)
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        run()
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        run()
+    for k, picks in enumerate([list(range(B)), few, list(range(B)), few]):
+        layout = _sub_layout(case, picks)
+        plan(layout)
+        claims = att.info().num_items > att.info().grid_blocks
+        assert claims == (len(picks) == B), (k, att.info().num_items)
+        n = len(layout[0])
+        run()
+        torch.cuda.synchronize()
+        want_o, want_l = o_buf[:n].clone(), l_buf[:n].clone()
+        for rep in range(2):
+            o_buf.fill_(float("nan"))
+            l_buf.fill_(float("nan"))
+            g.replay()
+            torch.cuda.synchronize()
+            assert torch.equal(o_buf[:n], want_o), (k, rep)
+            assert torch.equal(l_buf[:n], want_l), (k, rep)
+        if len(picks) == B:
+            compare(want_o, want_l, ro, rl, tag=f"claiming replay {k}, decode={decode}")
+
+
 def _layout_case(case, picks):
     """The requests `picks` of `case` as a case of their own over the same cache
     pages (for the oracle)."""
