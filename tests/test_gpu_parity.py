@@ -493,8 +493,8 @@ def test_graph_replay_follows_replans(decode, nw, split):
             compare(want_o, want_l, ro, rl, tag=f"graph decode={decode} nw={nw} split={split}")
 
 
-@pytest.mark.parametrize("decode", [False, True])
-def test_run_time_claiming_repeats_and_replays(decode):
+@pytest.mark.parametrize("decode,variant", [(False, 5), (False, 6), (True, 0)])
+def test_run_time_claiming_repeats_and_replays(decode, variant):
     """Batches with more work items than the launch has workgroups, so items
     are handed out at run time and each launch must leave its claim counters
     at 0: three eager runs in a row into NaN-filled outputs, each checked
@@ -512,7 +512,8 @@ def test_run_time_claiming_repeats_and_replays(decode):
     else:
         qo = [1200, 900, 1100, 1000]
         case = small(qo, [q + 50 for q in qo], H_q=32, H_kv=8, D=128, P_=16, W=127, seed=72)
-        att = make_attention(case, prefill_variant=5)
+        att = make_attention(case, prefill_variant=variant)
+        assert att.info().prefill_variant == variant
         few = [1]
     ro, rl = oracle_for(case)
     for rep in range(3):
