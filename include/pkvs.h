@@ -104,7 +104,8 @@ typedef enum pkvs_kind { PKVS_PREFILL = 0, PKVS_DECODE = 1, PKVS_CASCADE = 2 } p
  *  fixed_split_size decode: keys per KV chunk (a multiple of 32), or -1 to let
  *                   the planner choose; the partial (o, lse) of the chunks of
  *                   one request are combined by the merge of pkvs_merge_state
- *  disable_split_kv decode: 1 = one chunk per request
+ *  disable_split_kv decode: 1 = one chunk per request; prefill, cascade: 1 =
+ *                   never split a query tile's keys (see pkvs_prefill_plan)
  *  prefill_variant  prefill kernel shape: 0 = planner's choice (from head_dim and
  *                   qo_capacity), 1 = 4 waves x 32 rows, 2 = 8 waves x 32 rows,
  *                   3 = 4 waves x 64 rows, software-pipelined (2 and 3: head_dim
@@ -169,7 +170,8 @@ typedef struct pkvs_desc {
 /* Read-only facts about a plan (for callers, tests and profilers). */
 typedef struct pkvs_plan_info {
     int64_t num_items;       /* work items of the last plan() */
-    int64_t num_merges;      /* (request, kv head) pairs whose chunks are merged */
+    int64_t num_merges;      /* (request, kv head) pairs whose chunks are merged; key-split
+                                prefill: (query token, kv head) pairs */
     int64_t float_ws_bytes;  /* required float workspace (fp32 partials) */
     int64_t int_ws_bytes;    /* required int workspace (work list) */
     int32_t grid_blocks;     /* fixed grid of the main kernel */
@@ -180,6 +182,9 @@ typedef struct pkvs_plan_info {
     int32_t num_cus;         /* compute units the grid was sized for */
     int32_t prefill_variant; /* prefill: kernel variant the last plan() runs */
     int32_t decode_waves;    /* decode: waves that share one work item */
+    int32_t cascade_passes;  /* cascade: 1 (one launch over cached and new keys) or 2 */
+    int32_t key_chunks;      /* prefill, cascade: most key chunks per query tile a plan()
+                                may cut (1: never; see pkvs_prefill_plan) */
 } pkvs_plan_info;
 
 typedef struct pkvs_plan pkvs_plan;
@@ -225,6 +230,14 @@ int pkvs_workspace_bytes(const pkvs_desc *desc, int32_t is_decode, int64_t max_k
  * skip) and enqueues one host-to-device copy of it into int_ws on `stream`.
  * With int_ws == NULL the plan is built on the host only ("dry plan",
  * inspectable with pkvs_plan_copy_items, not runnable).
+ * Key split (split-KV for prefill, the combine of [FIB] _safe_merge_state):
+ * on prefill variants 1 and 2 with 16-bit queries, a plan whose capacities
+ * can never give more query tiles than half the workgroups its grid keeps
+ * resident may cut the key range of a batch's longest tiles into chunks of
+ * whole key tiles, each a work item writing a partial (o, lse) per query
+ * token into the float workspace; run() then merges each token's chunks.  A
+ * batch is cut when that shortens its longest item by more than the merge
+ * costs; disable_split_kv = 1 turns the split off (float_ws then 0 bytes).
  * Errors: INVALID_ARG (qo_len_b > kv_len_b, last page length outside
  * [1, page_size], decreasing indptr), CAPACITY, WORKSPACE, HIP. */
 int pkvs_prefill_plan(pkvs_plan *plan, const int32_t *qo_indptr_h, const int32_t *kv_indptr_h,
@@ -239,7 +252,10 @@ int pkvs_prefill_plan(pkvs_plan *plan, const int32_t *qo_indptr_h, const int32_t
  * per-element window mask is always applied.  Keys and values are read as
  * k_scale * k and v_scale * v (positive finite; 1 for an unscaled cache;
  * INVALID_ARG otherwise), k_scale folded into the logit scale and v_scale
- * into the output normalisation, for every cache type. */
+ * into the output normalisation, for every cache type.  After a batch whose
+ * plan cut key ranges, a second launch merges the chunk partials (under
+ * stream capture it is launched whenever the plan can cut, and reads the
+ * merge count from the workspace). */
 int pkvs_prefill_run(const pkvs_plan *plan, const void *q, const void *k_cache,
                      const void *v_cache, int64_t num_pages, const int32_t *kv_indices_d,
                      void *o, float *lse, float sm_scale, int32_t window_left, int32_t causal,
@@ -324,11 +340,14 @@ int pkvs_decode_noalloc(pkvs_plan *plan, const int32_t *kv_indptr_h,
  * split key ranges serves the combined problem (16-bit K/V in the query dtype;
  * prefill_variant 0, 1, 2 or 5): each request becomes one prefill request
  * over its cached keys followed by its new tokens, one causal sequence whose
- * window mask is exactly the two masks above; its float workspace is then 0
- * bytes.  Otherwise two passes.  Builds the work list(s) and enqueues the
- * host-to-device copies into int_ws on `stream` (int_ws == NULL: dry plan).
- * float_ws holds the paged pass's (o, lse) of a two-pass plan.  Errors as pkvs_prefill_plan (a request may have more new
- * tokens than cached keys). */
+ * window mask is exactly the two masks above, and the key split of
+ * pkvs_prefill_plan applies to it.  Otherwise two passes
+ * (pkvs_plan_info.cascade_passes tells which).  Builds the work list(s) and
+ * enqueues the host-to-device copies into int_ws on `stream` (int_ws == NULL:
+ * dry plan).  float_ws holds the paged pass's (o, lse) of a two-pass plan, the
+ * key split's partials of a one-pass plan (0 bytes when it cannot split).
+ * Errors as pkvs_prefill_plan (a request may have more new tokens than cached
+ * keys). */
 int pkvs_cascade_plan(pkvs_plan *plan, const int32_t *qo_indptr_h, const int32_t *kv_indptr_h,
                       const int32_t *kv_last_page_len_h, int32_t batch_size, void *float_ws,
                       size_t float_ws_bytes, void *int_ws, size_t int_ws_bytes,
@@ -339,10 +358,11 @@ int pkvs_cascade_plan(pkvs_plan *plan, const int32_t *qo_indptr_h, const int32_t
  * v_extend [nnz_qo, num_kv_heads, head_dim] (row r is the key / value of query
  * token r); k_cache, v_cache, num_pages and kv_indices_d as pkvs_prefill_run
  * (they may be NULL / 0 when the planned batch has no cached keys); lse
- * nullable.  Where the plan is one pass (see pkvs_cascade_plan's float_ws:
- * 0 bytes), one launch on `stream` reads each request's cached keys through
- * the page table and its new keys from k_extend / v_extend in one online
- * softmax; otherwise two launches: the paged pass writes its (o, lse) into
+ * nullable.  Where the plan is one pass (pkvs_plan_info.cascade_passes 1),
+ * one launch on `stream` reads each request's cached keys through the page
+ * table and its new keys from k_extend / v_extend in one online softmax
+ * (followed by the merge of a key-split batch, as pkvs_prefill_run);
+ * otherwise two launches: the paged pass writes its (o, lse) into
  * float_ws, then the ragged pass stores the merge_state combine of its own
  * (o, lse) with them into o and lse (the merge runs in its epilogue).
  * window_left must equal the plan's.  k_scale / v_scale apply to the cache

@@ -591,8 +591,10 @@ __global__ __launch_bounds__(kDecodeThreads * NW) void decode_kernel(DecodeArgs 
 
 // Combine the chunk partials of every split (request, kv head): one wave per
 // (merge entry, query head of the group); the LSE-weighted sum of
-// pkvs_merge_state, folded over all chunks at once.
-template <int D, bool F16>
+// pkvs_merge_state, folded over all chunks at once.  P16: the partial o is in
+// the query dtype (part_o16; a key-split prefill's merge entries are (query
+// token, kv head) pairs), else fp32.
+template <int D, bool F16, bool P16>
 __global__ __launch_bounds__(kMergeThreads) void decode_merge_kernel(DecodeArgs a)
 {
     constexpr int E = D / 64;  // elements per lane
@@ -615,9 +617,15 @@ __global__ __launch_bounds__(kMergeThreads) void decode_merge_kernel(DecodeArgs 
                 const int64_t sl = int64_t(first + k) * G + h;
                 const float wk = fast_exp2((a.part_lse[sl] - M) * 1.44269504088896340736f);
                 sum += wk;
-                const float *po = a.part_o + sl * D;
+                if constexpr (P16) {
+                    const uint16_t *po = a.part_o16 + sl * D;
 #pragma unroll
-                for (int e = 0; e < E; ++e) acc[e] += wk * po[lane + 64 * e];
+                    for (int e = 0; e < E; ++e) acc[e] += wk * from16<F16>(po[lane + 64 * e]);
+                } else {
+                    const float *po = a.part_o + sl * D;
+#pragma unroll
+                    for (int e = 0; e < E; ++e) acc[e] += wk * po[lane + 64 * e];
+                }
             }
         }
         const float inv = sum > 0.f ? 1.f / sum : 0.f;
@@ -681,23 +689,26 @@ hipError_t launch_decode_16bit(const DecodeArgs &a, int head_dim, bool f16, int 
                : launch_decode_f<false>(a, head_dim, kv_format, waves, grid, s);
 }
 
-template <bool F16>
+template <bool F16, bool P16>
 static hipError_t launch_merge_t(const DecodeArgs &a, int head_dim, int grid, hipStream_t s)
 {
     switch (head_dim) {
-    case 64: decode_merge_kernel<64, F16><<<grid, kMergeThreads, 0, s>>>(a); break;
-    case 128: decode_merge_kernel<128, F16><<<grid, kMergeThreads, 0, s>>>(a); break;
-    case 256: decode_merge_kernel<256, F16><<<grid, kMergeThreads, 0, s>>>(a); break;
+    case 64: decode_merge_kernel<64, F16, P16><<<grid, kMergeThreads, 0, s>>>(a); break;
+    case 128: decode_merge_kernel<128, F16, P16><<<grid, kMergeThreads, 0, s>>>(a); break;
+    case 256: decode_merge_kernel<256, F16, P16><<<grid, kMergeThreads, 0, s>>>(a); break;
     default: return hipErrorInvalidValue;
     }
     return hipGetLastError();
 }
 
-hipError_t launch_decode_merge(const DecodeArgs &a, int head_dim, bool f16, int grid,
+hipError_t launch_decode_merge(const DecodeArgs &a, int head_dim, bool f16, bool p16, int grid,
                                hipStream_t s)
 {
-    return f16 ? launch_merge_t<true>(a, head_dim, grid, s)
-               : launch_merge_t<false>(a, head_dim, grid, s);
+    if (p16)
+        return f16 ? launch_merge_t<true, true>(a, head_dim, grid, s)
+                   : launch_merge_t<false, true>(a, head_dim, grid, s);
+    return f16 ? launch_merge_t<true, false>(a, head_dim, grid, s)
+               : launch_merge_t<false, false>(a, head_dim, grid, s);
 }
 
 template <bool F16, int KVF, int NW>

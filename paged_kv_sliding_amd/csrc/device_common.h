@@ -111,6 +111,13 @@ __device__ __forceinline__ uint16_t to16(float x)
 }
 
 template <bool F16>
+__device__ __forceinline__ float from16(uint16_t x)
+{
+    if constexpr (F16) return float(__builtin_bit_cast(_Float16, x));
+    else return float(__builtin_bit_cast(__bf16, x));
+}
+
+template <bool F16>
 __device__ __forceinline__ f32x4 from16x4(bf16x4 v)
 {
     if constexpr (F16) return __builtin_convertvector(__builtin_bit_cast(f16x4, v), f32x4);

@@ -46,6 +46,12 @@ enum PrefillItem {
     kPiSplit = 8,    // one-pass cascade: keys from here on are the request's new
                      // tokens, read from the contiguous K/V (key k on row
                      // k + q_begin - pos0); INT32_MAX: every key is in the cache
+    kPiKvEnd = 9,    // one past the last key processed (a multiple of the key tile
+                     // past kv_begin unless it is the causal end of the queries)
+    kPiSlot = 10,    // -1: write o / lse; else the item is one key chunk of a
+                     // split query tile and token r of it writes its partial
+                     // (o, lse) to slot kPiSlot + r * kPiSlotStride
+    kPiSlotStride = 11,
 };
 
 // Decode item: one (request, kv head, key chunk).
@@ -61,7 +67,9 @@ enum DecodeItem {
     kDiKvLen = 7,
 };
 
-// Merge entry: the chunks of one (request, kv head) to combine.
+// Merge entry: the chunks of one (request, kv head) to combine -- for a
+// key-split prefill, of one (query token, kv head): kMeRequest is then the
+// token's row in q / o.  Both are written to o / lse row kMeRequest.
 constexpr int kMergeWords = 4;
 enum MergeEntry { kMeRequest = 0, kMeKvHead = 1, kMeFirstSlot = 2, kMeNumSlots = 3 };
 
@@ -121,6 +129,11 @@ struct PrefillArgs {
     // one-pass cascade (kPrefillBig): the new tokens' K/V, [tokens, kv heads,
     // head_dim], for the keys at or past each item's kPiSplit; null otherwise
     const void *k_ext, *v_ext;
+    // key-split prefill (items with kPiSlot >= 0): partial slots of the float
+    // workspace: o in the query dtype (normalised over the chunk's keys), lse
+    // in fp32
+    void *part_o;     // [slots, group, head_dim]
+    float *part_lse;  // [slots, group], natural log
 };
 
 struct DecodeArgs {
@@ -131,6 +144,9 @@ struct DecodeArgs {
     int32_t *ws;      // int workspace: header (with the work counters) + items
     float *part_o;    // [slots, group, head_dim]
     float *part_lse;  // [slots, group]
+    // the merge of a key-split prefill: its partial o in the query dtype
+    // ([slots, group, head_dim]) instead of part_o
+    const uint16_t *part_o16;
     int64_t num_pages;
     float scale_log2;   // as PrefillArgs
     float cap_a;
@@ -147,7 +163,8 @@ hipError_t launch_attention_fp32(const PrefillArgs &a, int head_dim, int grid, h
 // waves: 1 or 4 waves share each decode work item (pkvs_desc.decode_waves)
 hipError_t launch_decode_16bit(const DecodeArgs &a, int head_dim, bool f16, int kv_format,
                                int waves, int grid, hipStream_t s);
-hipError_t launch_decode_merge(const DecodeArgs &a, int head_dim, bool f16, int grid,
+// p16: the partial o is part_o16, in the query dtype (key-split prefill)
+hipError_t launch_decode_merge(const DecodeArgs &a, int head_dim, bool f16, bool p16, int grid,
                                hipStream_t s);
 hipError_t launch_merge_state(const void *va, const float *sa, const void *vb, const float *sb,
                               void *vo, float *so, int64_t n, int32_t heads, int32_t head_dim,

@@ -60,7 +60,13 @@ static void size_plan(Plan *p)
     const int64_t group = d.num_qo_heads / d.num_kv_heads;
     int64_t items = 0, slots = 0, merges = 0;
     if (d.kind == PKVS_PREFILL) {
-        items = hkv * (ceil_div(d.qo_capacity, p->query_tile) + B);
+        items = hkv * (ceil_div(d.qo_capacity, p->query_tile) + B) * p->key_chunks_max;
+        if (p->key_chunks_max > 1) {
+            // a split tile of n tokens cut into c chunks takes n * c slots and
+            // n merge entries
+            slots = int64_t(d.qo_capacity) * hkv * p->key_chunks_max;
+            merges = int64_t(d.qo_capacity) * hkv;
+        }
         // a ragged pass's row-index table: at most one entry per kRaggedPage
         // tokens of each request, rounded up per request
         if (p->ragged) p->lead_words = (ceil_div(d.qo_capacity, kRaggedPage) + B + 15) / 16 * 16;
@@ -93,7 +99,10 @@ static void size_plan(Plan *p)
     p->merges_cap = merges;
     p->int_ws_need = sizeof(int32_t) * size_t(p->lead_words + kHeaderWords +
                                               items * p->item_words + merges * kMergeWords);
-    p->float_ws_need = sizeof(float) * size_t(slots * group * (d.head_dim + 1));
+    // partial (o, lse) per slot and query head: fp32 o for decode, o in the
+    // query dtype for a key-split prefill; fp32 lse
+    p->float_ws_need = size_t(slots * group) *
+                       (size_t(d.head_dim) * (d.kind == PKVS_PREFILL ? 2 : 4) + sizeof(float));
 }
 
 static int validate_desc(const pkvs_desc *d)
@@ -255,9 +264,68 @@ static int build_prefill(Plan *p, const std::vector<Req> &reqs)
                 it.w[kPiPageBase] = int32_t(r.page_base);
                 it.w[kPiKvBegin] = int32_t(kv_begin);
                 it.w[kPiSplit] = int32_t(std::min<int64_t>(r.split, INT32_MAX));
-                it.w[9] = it.w[10] = it.w[11] = 0;
+                it.w[kPiKvEnd] = int32_t(std::max(kv_end, kv_begin));
+                it.w[kPiSlot] = -1;
+                it.w[kPiSlotStride] = 0;
                 items.push_back(it);
             }
+        }
+    }
+    // Key-split: with fewer tiles than resident workgroups, cut the longest
+    // tiles' key ranges into chunks of whole key tiles (each a work item with
+    // partial slots) when the longest item then ends sooner by more than the
+    // merge costs; the merge entries combine each token's chunks.
+    std::vector<int32_t> merges;
+    if (p->key_chunks_max > 1 && int64_t(items.size()) < p->grid_blocks) {
+        auto tiles_of = [&](const It &it) { return ceil_div(std::max<int64_t>(it.cost, 0), kv_tile); };
+        int64_t total = 0, longest = 0;
+        for (const It &it : items) {
+            total += tiles_of(it);
+            longest = std::max(longest, tiles_of(it));
+        }
+        const int64_t c = std::max<int64_t>(kMinChunkTiles, ceil_div(total, p->grid_blocks));
+        auto chunks_of = [&](int64_t t) {
+            return std::max<int64_t>(1, std::min<int64_t>(p->key_chunks_max, ceil_div(t, c)));
+        };
+        int64_t longest_chunk = 0;
+        for (const It &it : items) {
+            const int64_t t = tiles_of(it);
+            longest_chunk = std::max(longest_chunk, ceil_div(t, chunks_of(t)));
+        }
+        if (longest > longest_chunk + kMergeTiles) {
+            std::vector<It> cut;
+            int64_t slot = 0;
+            for (const It &it : items) {
+                const int64_t t = tiles_of(it);
+                const int64_t per = ceil_div(t, chunks_of(t));
+                const int64_t n = per > 0 ? ceil_div(t, per) : 1;
+                if (n <= 1) {
+                    cut.push_back(it);
+                    continue;
+                }
+                const int64_t qn = it.w[kPiQCount];
+                if (slot + qn * n > p->slots_cap ||
+                    int64_t(merges.size() / kMergeWords) + qn > p->merges_cap)
+                    return fail(PKVS_ERR_CAPACITY, "key-split prefill needs more partial slots "
+                                "than the plan's %lld", (long long)p->slots_cap);
+                for (int64_t r = 0; r < qn; ++r)
+                    merges.insert(merges.end(), {int32_t(it.w[kPiQBegin] + r), it.w[kPiKvHead],
+                                                 int32_t(slot + r * n), int32_t(n)});
+                const int64_t kb = it.w[kPiKvBegin], ke = it.w[kPiKvEnd];
+                for (int64_t k = 0; k < n; ++k) {
+                    It ch = it;
+                    const int64_t b0 = kb + k * per * kv_tile;
+                    const int64_t b1 = k + 1 == n ? ke : b0 + per * kv_tile;
+                    ch.cost = b1 - b0;
+                    ch.w[kPiKvBegin] = int32_t(b0);
+                    ch.w[kPiKvEnd] = int32_t(b1);
+                    ch.w[kPiSlot] = int32_t(slot + k);
+                    ch.w[kPiSlotStride] = int32_t(n);
+                    cut.push_back(ch);
+                }
+                slot += qn * n;
+            }
+            items.swap(cut);
         }
     }
     std::stable_sort(items.begin(), items.end(),
@@ -286,9 +354,10 @@ static int build_prefill(Plan *p, const std::vector<Req> &reqs)
         }
     }
     p->n_items = int64_t(items.size());
-    p->n_merges = 0;
+    p->n_merges = int64_t(merges.size() / kMergeWords);
     p->split_size = 0;
-    p->host_ws.assign(p->lead_words + kHeaderWords + items.size() * kPrefillItemWords, 0);
+    const size_t merge_off = kHeaderWords + items.size() * kPrefillItemWords;
+    p->host_ws.assign(p->lead_words + merge_off + merges.size(), 0);
     int64_t keys = 0;
     for (const Req &r : reqs) keys += r.kv_len;
     p->planned_keys = keys;
@@ -301,11 +370,12 @@ static int build_prefill(Plan *p, const std::vector<Req> &reqs)
     }
     int32_t *w = p->host_ws.data() + p->lead_words;
     w[kHdrNumItems] = int32_t(items.size());
-    w[kHdrNumMerges] = 0;
-    w[kHdrMergeOffset] = int32_t(p->host_ws.size() - p->lead_words);
+    w[kHdrNumMerges] = int32_t(p->n_merges);
+    w[kHdrMergeOffset] = int32_t(merge_off);
     w[kHdrItemWords] = kPrefillItemWords;
     for (size_t i = 0; i < items.size(); ++i)
         std::memcpy(w + kHeaderWords + i * kPrefillItemWords, items[i].w, sizeof items[i].w);
+    std::copy(merges.begin(), merges.end(), w + merge_off);
     return PKVS_OK;
 }
 
@@ -490,7 +560,8 @@ static void destroy_plan(Plan *p);
 
 // A validated prefill or decode descriptor -> plan object (ragged: a
 // cascade's extend pass, see plan_state.h).
-static int create_plan(const pkvs_desc *desc, bool ragged, Plan **out, bool make_buffers = true)
+static int create_plan(const pkvs_desc *desc, bool ragged, Plan **out, bool make_buffers = true,
+                       bool key_split = true)
 {
     Plan *p = new (std::nothrow) Plan();
     if (!p) return fail(PKVS_ERR_INVALID_ARG, "out of host memory");
@@ -552,6 +623,18 @@ static int create_plan(const pkvs_desc *desc, bool ragged, Plan **out, bool make
                          ? prefill_blocks_per_cu(desc->head_dim, v, f16, kvf, p->table_pages)
                          : 0;
         p->grid_blocks = p->num_cus * std::max(per_cu, fp32 ? 2 : 1);
+        // Key-split (the register-staged 128- and 256-row kernels): allowed
+        // when the capacities can never give more than one query tile per
+        // kSplitFillShare resident workgroups, with enough chunks per tile to
+        // reach about one item per workgroup.  Fixed here, like the partial
+        // slots it needs, so that a captured run stays valid for every plan.
+        if (key_split && !desc->disable_split_kv && !ragged && !fp32 &&
+            (v == kPrefillRows128 || v == kPrefillRows256)) {
+            const int64_t tiles = int64_t(desc->num_kv_heads) *
+                                  (ceil_div(desc->qo_capacity, p->query_tile) + desc->batch_capacity);
+            if (tiles * kSplitFillShare <= p->grid_blocks)
+                p->key_chunks_max = int(std::min<int64_t>(kMaxKeyChunks, p->grid_blocks / tiles));
+        }
     } else {
         p->query_tile = 1;
         p->item_words = fp32 ? kPrefillItemWords : kDecodeItemWords;
@@ -682,7 +765,8 @@ static int create_cascade(const pkvs_desc *desc, Plan **out)
             p->prefill_variant = fp->prefill_variant;
             p->items_cap = fp->items_cap;
             p->int_ws_need = fp->int_ws_need;
-            p->float_ws_need = 0;
+            // (the partial slots of a key-split plan; 0 otherwise)
+            p->float_ws_need = fp->float_ws_need;
             *out = p;
             return PKVS_OK;
         }
@@ -699,7 +783,8 @@ static int create_cascade(const pkvs_desc *desc, Plan **out)
     if (!p) return fail(PKVS_ERR_INVALID_ARG, "out of host memory");
     p->desc = *desc;
     int rc = create_plan(&e, true, &p->ext);
-    if (!rc) rc = create_plan(&r, false, &p->pre);
+    // (the prefix pass writes the (o, lse) the extend pass folds: no key split)
+    if (!rc) rc = create_plan(&r, false, &p->pre, true, false);
     if (rc) {
         destroy_plan(p);
         return rc;
@@ -866,9 +951,10 @@ int pkvs_cascade_plan(pkvs_plan *p, const int32_t *qo_indptr_h, const int32_t *k
             return fail(PKVS_ERR_CAPACITY, "cascade work list of %lld items exceeds capacity %lld",
                         (long long)f->n_items, (long long)f->items_cap);
         p->n_items = f->n_items;
+        p->n_merges = f->n_merges;
         p->planned_keys = cached;
         p->batch = f->batch = batch_size;
-        rc = finish_plan(f, nullptr, 0, int_ws, int_ws_bytes, stream);
+        rc = finish_plan(f, float_ws, float_ws_bytes, int_ws, int_ws_bytes, stream);
         if (rc || !int_ws) return rc;
         p->int_ws = int_ws;
         p->float_ws = float_ws;
@@ -933,6 +1019,10 @@ int pkvs_plan_get_info(const pkvs_plan *p, pkvs_plan_info *info)
     info->prefill_variant = p->desc.kind != PKVS_DECODE ? p->prefill_variant : 0;
     info->num_cus = p->num_cus;
     info->decode_waves = p->desc.kind == PKVS_DECODE ? p->decode_waves : 0;
+    info->cascade_passes = p->desc.kind != PKVS_CASCADE ? 0 : p->fused ? 1 : 2;
+    info->key_chunks = p->desc.kind == PKVS_DECODE ? 1
+                       : p->desc.kind == PKVS_CASCADE && p->fused ? p->pre->key_chunks_max
+                                                                  : p->key_chunks_max;
     return PKVS_OK;
 }
 

@@ -20,6 +20,19 @@ constexpr int64_t kMinAutoSplit = 256; // smallest key chunk the planner picks b
 constexpr double kWaveBytesPerUs = 10.0e3;
 constexpr double kChipBytesPerUs = 5.5e6;
 constexpr double kMergeUs = 10.0;
+// Key-split prefill (small batches on the register-staged kernels): a plan
+// whose capacities allow fewer query tiles than kSplitFillShare of the
+// resident workgroups may cut a tile's key range into up to kMaxKeyChunks
+// chunks of whole key tiles, each a work item of its own, whose partials a
+// merge combines.  A batch is split when its longest item, in key tiles plus
+// kItemStartTiles, exceeds the longest chunk's plus kMergeTiles (the merge
+// launch, in key tiles of the chunk's kernel), and never into chunks shorter
+// than kMinChunkTiles.
+constexpr int kMaxKeyChunks = 8;
+constexpr int64_t kSplitFillShare = 2;
+constexpr int64_t kItemStartTiles = 2;
+constexpr int64_t kMergeTiles = 3;
+constexpr int64_t kMinChunkTiles = 3;
 // decode, pkvs_desc.decode_waves = 0: four waves per work item for batches of
 // at most one (request, kv head) pair per kFourWavePairShare resident one-wave
 // items whose requests can exceed kFourWaveKeys keys after the window trim
@@ -53,6 +66,7 @@ struct pkvs_plan {
     int num_cus = 0;
     int grid_blocks = 0, block_threads = 0, query_tile = 0, item_words = 0;
     int prefill_variant = 1;  // 16-bit prefill kernel variant (PrefillVariant), fixed at creation
+    int key_chunks_max = 1;   // prefill: most key chunks per query tile (1: never split)
     int table_pages = 0;      // kPrefillDuo: entries of its LDS page table
     int64_t auto_target_items = 0;
     int decode_waves = 1;     // waves per decode work item (1 or 4)

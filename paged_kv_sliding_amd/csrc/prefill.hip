@@ -383,7 +383,9 @@ __global__ __launch_bounds__(NW * 64) void prefill_kernel(PrefillArgs a)
         const int hk = w[kPiKvHead], q_begin = w[kPiQBegin], q_count = w[kPiQCount];
         const int pos0 = w[kPiPos0], kv_len = w[kPiKvLen];
         const int kv_begin = w[kPiKvBegin];
-        const int kv_end = a.causal ? min(kv_len, pos0 + q_count) : kv_len;
+        // (a key chunk of a split tile ends at a key tile boundary)
+        const int kv_end = min(a.causal ? min(kv_len, pos0 + q_count) : kv_len, w[kPiKvEnd]);
+        const int slot0 = w[kPiSlot], slot_stride = w[kPiSlotStride];
         const int pos_last = pos0 + q_count - 1;
         const int ntiles = kv_end > kv_begin ? (kv_end - kv_begin + KT - 1) / KT : 0;
         ra.page_base = w[kPiPageBase];
@@ -632,7 +634,23 @@ __global__ __launch_bounds__(NW * 64) void prefill_kernel(PrefillArgs a)
 
         // epilogue: the two half-waves hold disjoint keys of each row
         l += __shfl_xor(l, 32);
-        if (row_valid) {
+        if (row_valid && slot0 >= 0) {
+            // one key chunk of a split tile: the row's partial (o normalised
+            // over the chunk's keys, lse) to its slot, for the merge
+            const int64_t sl = int64_t(slot0 + row_tok * slot_stride) * G + row_head;
+            const float w_self = l > 0.f ? a.v_scale / l : 0.f;
+            uint16_t *PO = static_cast<uint16_t *>(a.part_o) + sl * D;
+#pragma unroll
+            for (int dt = 0; dt < DT; ++dt)
+#pragma unroll
+                for (int m0 = 0; m0 < 4; ++m0) {
+                    f32x4 v4;
+#pragma unroll
+                    for (int m1 = 0; m1 < 4; ++m1) v4[m1] = o[dt][4 * m0 + m1] * w_self;
+                    *reinterpret_cast<bf16x4 *>(PO + dt * 32 + 8 * m0 + 4 * hw) = to16x4<F16>(v4);
+                }
+            if (hw == 0) a.part_lse[sl] = l > 0.f ? (m + fast_log2(l)) * kLn2 : kNegInf;
+        } else if (row_valid) {
             const int64_t lrow = int64_t(q_begin + row_tok) * a.num_qo_heads + hk * G + row_head;
             float w_self = l > 0.f ? a.v_scale / l : 0.f, w_other = 0.f;
             float lse_row = l > 0.f ? (m + fast_log2(l)) * kLn2 : kNegInf;

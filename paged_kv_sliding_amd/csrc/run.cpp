@@ -116,11 +116,49 @@ hipError_t launch_prefill_pass(const pkvs_plan *p, const void *q, const void *k,
     a.table_pages = p->table_pages;
     a.k_ext = k_ext;
     a.v_ext = v_ext;
+    if (p->slots_cap > 0) {
+        // [slots, group, head_dim] 16-bit, then [slots, group] fp32
+        const int group = p->desc.num_qo_heads / p->desc.num_kv_heads;
+        a.part_o = p->float_ws;
+        a.part_lse = reinterpret_cast<float *>(static_cast<uint16_t *>(p->float_ws) +
+                                               p->slots_cap * group * p->desc.head_dim);
+    }
     return p->desc.dtype == PKVS_FP32
                ? launch_attention_fp32(a, p->desc.head_dim, p->grid_blocks, stream)
                : launch_prefill_16bit(a, p->desc.head_dim, p->prefill_variant,
                                       p->desc.dtype == PKVS_FP16, p->desc.kv_format,
                                       p->grid_blocks, stream);
+}
+
+// The merge of a key-split prefill's chunk partials (decode_merge_kernel: one
+// wave per (query token, head), the token's chunks in consecutive slots).  As
+// for decode, it is launched under stream capture whenever the plan can split
+// (the kernel reads the merge count from the workspace), with a grid fixed by
+// the capacities; an eager run of a batch that split nothing skips it.
+int launch_key_split_merge(const pkvs_plan *p, void *o, float *lse, hipStream_t stream)
+{
+    if (p->merges_cap == 0) return PKVS_OK;
+    hipStreamCaptureStatus capture = hipStreamCaptureStatusNone;
+    if (p->n_merges == 0 && hipStreamIsCapturing(stream, &capture) != hipSuccess)
+        return fail(PKVS_ERR_HIP, "hipStreamIsCapturing failed");
+    if (p->n_merges == 0 && capture == hipStreamCaptureStatusNone) return PKVS_OK;
+    const int group = p->desc.num_qo_heads / p->desc.num_kv_heads;
+    DecodeArgs a{};
+    a.o = o;
+    a.lse = lse;
+    a.ws = static_cast<int32_t *>(p->int_ws) + p->lead_words;
+    a.part_o16 = static_cast<const uint16_t *>(p->float_ws);
+    a.part_lse = reinterpret_cast<float *>(static_cast<uint16_t *>(p->float_ws) +
+                                           p->slots_cap * group * p->desc.head_dim);
+    a.num_qo_heads = p->desc.num_qo_heads;
+    a.num_kv_heads = p->desc.num_kv_heads;
+    a.log2_group = log2_exact(group);
+    const int grid = int(std::min<int64_t>(p->merges_cap * group, int64_t(p->num_cus) * 64));
+    hipError_t e = launch_decode_merge(a, p->desc.head_dim, p->desc.dtype == PKVS_FP16, true,
+                                       std::max(grid, 1), stream);
+    if (e != hipSuccess) return fail(PKVS_ERR_HIP, "key-split merge launch: %s",
+                                     hipGetErrorString(e));
+    return PKVS_OK;
 }
 
 }  // namespace
@@ -142,7 +180,7 @@ int pkvs_prefill_run(const pkvs_plan *p, const void *q, const void *k_cache, con
     hipError_t e = launch_prefill_pass(p, q, k_cache, v_cache, num_pages, kv_indices_d, o, lse,
                                        sm_scale, k_scale, v_scale, stream);
     if (e != hipSuccess) return fail(PKVS_ERR_HIP, "prefill launch: %s", hipGetErrorString(e));
-    return PKVS_OK;
+    return launch_key_split_merge(p, o, lse, stream);
 }
 
 int pkvs_cascade_run(const pkvs_plan *p, const void *q, const void *k_extend,
@@ -175,7 +213,7 @@ int pkvs_cascade_run(const pkvs_plan *p, const void *q, const void *k_extend,
                                            sm_scale, k_scale, v_scale, stream, nullptr, nullptr,
                                            k_extend, v_extend);
         if (e != hipSuccess) return fail(PKVS_ERR_HIP, "cascade launch: %s", hipGetErrorString(e));
-        return PKVS_OK;
+        return launch_key_split_merge(p->pre, o, lse, stream);
     }
     char *fws = static_cast<char *>(p->float_ws);
     void *o2 = fws + p->o2_off;
@@ -270,7 +308,7 @@ int pkvs_decode_run(const pkvs_plan *p, const void *q, const void *k_cache, cons
         return fail(PKVS_ERR_HIP, "hipStreamIsCapturing failed");
     if (p->merges_cap > 0 && (p->n_merges > 0 || capture != hipStreamCaptureStatusNone)) {
         const int grid = int(std::min<int64_t>(p->merges_cap * group, int64_t(p->num_cus) * 64));
-        e = launch_decode_merge(a, p->desc.head_dim, f16, std::max(grid, 1), stream);
+        e = launch_decode_merge(a, p->desc.head_dim, f16, false, std::max(grid, 1), stream);
         if (e != hipSuccess)
             return fail(PKVS_ERR_HIP, "decode merge launch: %s", hipGetErrorString(e));
     }

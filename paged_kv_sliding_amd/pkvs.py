@@ -81,6 +81,7 @@ class pkvs_plan_info(ctypes.Structure):
         ("split_size", ctypes.c_int32), ("item_words", ctypes.c_int32),
         ("query_tile", ctypes.c_int32), ("num_cus", ctypes.c_int32),
         ("prefill_variant", ctypes.c_int32), ("decode_waves", ctypes.c_int32),
+        ("cascade_passes", ctypes.c_int32), ("key_chunks", ctypes.c_int32),
     ]
 
 

@@ -25,7 +25,7 @@ hipError_t launch_decode_16bit(const DecodeArgs &, int, bool, int, int, int, hip
 {
     return hipErrorNoDevice;
 }
-hipError_t launch_decode_merge(const DecodeArgs &, int, bool, int, hipStream_t)
+hipError_t launch_decode_merge(const DecodeArgs &, int, bool, bool, int, hipStream_t)
 {
     return hipErrorNoDevice;
 }

@@ -57,9 +57,17 @@ def test_tiny_prefill_fp32_batched():
 
 
 def test_prefix_prefill_full():
+    """The 8-request batch with cached prefixes: its 56 query tiles leave most
+    CUs idle, so the planner cuts their key ranges (key split) and merges the
+    chunk partials; every row written, against the oracle."""
     case = build_case("prefix_prefill", device=DEV)
     log(f"prefix_prefill qo={case.qo_lens} kv={case.kv_lens}")
-    o, lse = gpu_run(case)
+    att = make_attention(case)
+    o, lse = gpu_run(case, att=att)
+    info = att.info()
+    log(f"  key chunks {info.key_chunks}, items {info.num_items}, merges {info.num_merges}")
+    assert info.num_merges > 0
+    assert_all_written(case, o, lse, "prefix_prefill")
     ro, rl = oracle_for(case)
     compare(o, lse, ro, rl, tag="prefix_prefill")
 
@@ -407,14 +415,19 @@ def _sub_layout(case, picks):
 
 
 @pytest.mark.parametrize("decode,nw,split", [(False, 0, -1), (True, 1, 64), (True, 4, 64),
-                                              (True, 1, -1)])
+                                              (True, 1, -1), (False, 0, -2)])
 def test_graph_replay_follows_replans(decode, nw, split):
     """run() captured once in a HIP graph stays valid for every later plan() of
     the same capacities (AMD-Ecosystem/flashinfer PR 234, "Why each fix" 2: the
     grid and the launch set come from the capacities, the work from the
     workspace).  Each replay, with eager work and synchronisations between
-    replays, must equal an eager run() of the batch planned last, bit for bit."""
-    if decode:
+    replays, must equal an eager run() of the batch planned last, bit for bit.
+    split = -2: a prefill whose full batch is key-split (chunk partials and a
+    merge launch) and whose one-request batch is not."""
+    if not decode and split == -2:
+        qo, kv = [40, 1, 130, 7, 64], [1300, 1, 130, 2500, 64]
+        case = small(qo, kv, H_q=8, H_kv=2, D=128, P_=16, W=-1, seed=63)
+    elif decode:
         # split = -1: the planner's choice; the first planned batch (request 2
         # alone, 77 keys) splits nothing, the later ones split their long
         # requests, so the graph must hold the merge launch an eager run of
@@ -452,10 +465,10 @@ def test_graph_replay_follows_replans(decode, nw, split):
         att.run(q_buf, case.k_cache, case.v_cache, idx_buf, sm_scale=case.sm_scale,
                 window_left=case.window_left, out=o_buf, lse=l_buf)
 
-    layouts = [_sub_layout(case, list(range(B))), _sub_layout(case, [2]),
-               _sub_layout(case, [0, 3, 4]), _sub_layout(case, list(range(B)))]
+    req_sets = [list(range(B)), [2], [0, 3, 4], list(range(B))]
     if decode and split < 0:
-        layouts = [_sub_layout(case, [2])] + layouts
+        req_sets = [[2]] + req_sets
+    layouts = [_sub_layout(case, r) for r in req_sets]
     load(layouts[0])
     plan(layouts[0])
     if decode and split < 0:
@@ -488,6 +501,8 @@ def test_graph_replay_follows_replans(decode, nw, split):
             assert torch.equal(l_buf[:n], want_l), (k, rep)
         if decode and split < 0 and len(layout[0]) == B:
             assert att.info().num_merges > 0
+        if not decode and split == -2:
+            assert (att.info().num_merges > 0) == (len(req_sets[k]) > 1), k
         if len(layout[0]) == B:
             ro, rl = oracle_for(case)
             compare(want_o, want_l, ro, rl, tag=f"graph decode={decode} nw={nw} split={split}")
@@ -739,6 +754,73 @@ def test_merge_state_of_prefill_split_equals_unsplit():
 # branch with cached prefixes): a ragged pass over the new tokens' own keys, a
 # paged pass over the cached prefix, merged.  The result must equal the one
 # paged prefill over prefix + new keys (the oracle on the combined layout).
+
+
+# ----------------------------------------------------------------- key-split prefill
+
+# small batches whose query tiles reach far back: the plan cuts their key ranges
+SPLIT_QO = [3, 70, 129, 1, 40]
+SPLIT_KV = [1500, 900, 2129, 1, 600]
+
+
+@pytest.mark.parametrize("variant,D,G", [(1, 64, 4), (1, 128, 8), (1, 256, 4), (2, 64, 2),
+                                         (2, 128, 4)])
+@pytest.mark.parametrize("W,P_", [(-1, 16), (0, 4), (100, 1), (511, 16), (1023, 2)])
+def test_key_split_prefill(variant, D, G, W, P_):
+    """The key split on the register-staged kernels: chunks of whole key
+    tiles, each writing per-token partials, merged per token; every row
+    written (NaN-filled outputs), against the oracle, and the same batch with
+    the split disabled runs one item per tile."""
+    case = small(SPLIT_QO, SPLIT_KV, H_q=2 * G, H_kv=2, D=D, P_=P_, W=W,
+                 seed=11 * variant + D + W + P_)
+    att = make_attention(case, prefill_variant=variant)
+    o, lse = gpu_run(case, att=att)
+    info = att.info()
+    assert info.prefill_variant == variant and info.key_chunks > 1
+    if W < 0 or W >= 511:
+        assert info.num_merges > 0
+    tag = f"key split v={variant} D={D} G={G} W={W} P={P_} merges={info.num_merges}"
+    assert_all_written(case, o, lse, tag)
+    ro, rl = oracle_for(case)
+    compare(o, lse, ro, rl, tag=tag)
+    whole = make_attention(case, prefill_variant=variant, disable_split_kv=True)
+    assert whole.info().key_chunks == 1 and whole.info().float_ws_bytes == 0
+    o1, l1 = gpu_run(case, att=whole)
+    assert whole.info().num_merges == 0
+    compare(o1, l1, ro, rl, tag=tag + " (no split)")
+
+
+@pytest.mark.parametrize("dtype,kv_dtype,cap", [
+    (torch.float16, None, 0.0), (torch.bfloat16, None, 30.0),
+    (torch.bfloat16, torch.float8_e4m3fn, 0.0), (torch.float16, torch.float8_e5m2, 0.0)])
+def test_key_split_prefill_types(dtype, kv_dtype, cap):
+    """The key split with fp16 queries, a logits soft cap and 8-bit caches
+    (the chunks' partials carry v_scale; the merge rounds once to the dtype)."""
+    case = small(SPLIT_QO, SPLIT_KV, H_q=8, H_kv=2, D=128, P_=16, W=-1, seed=19, dtype=dtype,
+                 kv_dtype=kv_dtype, cap=cap, k_scale=0.5 if kv_dtype else 1.0,
+                 v_scale=0.25 if kv_dtype else 1.0)
+    att = make_attention(case)
+    o, lse = gpu_run(case, att=att)
+    assert att.info().num_merges > 0
+    tag = f"key split {dtype} kv={kv_dtype} cap={cap}"
+    assert_all_written(case, o, lse, tag)
+    ro, rl = oracle_for(case)
+    compare(o, lse, ro, rl, tag=tag)
+
+
+def test_key_split_prefill_non_causal_and_without_lse():
+    """Non-causal without a window (every key of the request), and run()
+    without an LSE output: the merge writes o only."""
+    case = dataclasses.replace(small(SPLIT_QO, SPLIT_KV, H_q=4, H_kv=1, D=128, W=-1, seed=23),
+                               causal=False)
+    att = make_attention(case)
+    o, lse = gpu_run(case, att=att)
+    assert att.info().num_merges > 0
+    ro, rl = oracle_for(case)
+    compare(o, lse, ro, rl, tag="key split non-causal")
+    o2 = gpu_run(case, att=att, return_lse=False)
+    o2 = o2[0] if isinstance(o2, tuple) else o2
+    assert torch.equal(o2, o)
 
 
 def make_cascade(case, window_left=None, prefill_variant=0, qo_capacity=None,

@@ -572,7 +572,7 @@ def test_cascade_workspace_and_errors():
     fb, ib = P.pkvs_workspace_size(h)
     rows = 1000 * 8
     assert fb >= rows * 128 * 2 + rows * 4  # the paged pass's (o, lse)
-    hp = P.pkvs_plan_create(desc(P.PKVS_PREFILL, **kw))
+    hp = P.pkvs_plan_create(desc(P.PKVS_PREFILL, disable_split_kv=1, **kw))
     assert ib > P.pkvs_workspace_size(hp)[1]
     qop, kvp, last = csr([10, 600], [0, 5], 16)
     # the wrong entry point for each kind

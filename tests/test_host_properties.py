@@ -2,10 +2,12 @@
 page sizes, head groups, kernel variants and split sizes, drawn by
 hypothesis, against the invariants the kernels rely on.
 
-Prefill: every (request, kv head, query) in exactly one item; an item's key
-range starts at a multiple of its kernel's key tile at or before the first
-visible key of every query in it, and reaches the last query's position; items
-are ordered by decreasing key count.  Decode: each (request, kv head)'s chunks
+Prefill: every (request, kv head, query) in exactly one query tile; a tile's
+key range starts at a multiple of its kernel's key tile at or before the first
+visible key of every query in it and reaches the last query's position; a tile
+cut by the key split is a run of chunk items whose key ranges partition its
+range at key-tile boundaries, with consecutive partial slots per token and one
+merge entry per token; items are ordered by decreasing key count.  Decode: each (request, kv head)'s chunks
 partition [window start rounded down to 32, kv_len) with the visible bound set
 to the window start, and split pairs own consecutive partial slots, one merge
 entry each.  Cascade: the one-pass plan covers every new token once over the
@@ -66,26 +68,51 @@ def test_prefill_plan_invariants(batch):
         kt = 64 if info.prefill_variant in (5, 6) else 32
         items = P.pkvs_plan_copy_items(h).tolist()
         assert len(items) == info.num_items
-        seen = {}
-        costs = []
-        for it in items:
-            b, hk, q0, qn, pos0, kv_len, pbase, kvb, split = it[:9]
-            assert split == INT32_MAX and kv_len == kv[b] and pbase == kvp[b]
-            assert 1 <= qn <= info.query_tile
-            prefix = kv[b] - qo[b]
-            assert pos0 == prefix + (q0 - qop[b])
-            kve = min(kv_len, pos0 + qn)
-            assert kvb % kt == 0 and kvb <= max(0, pos0 - W if W >= 0 else 0)
-            assert kve == pos0 + qn  # causal: the last query sees its own key
-            costs.append(kve - kvb)
-            for t in range(q0, q0 + qn):
-                seen[(b, hk, t)] = seen.get((b, hk, t), 0) + 1
+        costs = [it[9] - it[7] for it in items]
         assert costs == sorted(costs, reverse=True)
+        seen = check_tiles(items, kt, W, lambda b: kv[b] - qo[b], lambda b: kv[b],
+                           lambda b: INT32_MAX, kvp, qop, info)
         expect = {(b, hk, t) for b in range(len(kv)) for hk in range(2)
                   for t in range(qop[b], qop[b + 1])}
         assert set(seen) == expect and set(seen.values()) <= {1}
     finally:
         P.pkvs_plan_destroy(h)
+
+
+def check_tiles(items, kt, W, prefix_of, kv_len_of, split_of, kvp, qop, info):
+    """Group the items by query tile, check each tile's key range and its
+    chunks (see the module docstring); return the (request, kv head, token)
+    coverage counts."""
+    tiles, seen, slots = {}, {}, set()
+    for it in items:
+        b, hk, q0, qn, pos0, kv_len, pbase, kvb, split, kv_end, slot, stride = it[:12]
+        assert kv_len == kv_len_of(b) and pbase == kvp[b] and split == split_of(b)
+        assert 1 <= qn <= info.query_tile and pos0 == prefix_of(b) + (q0 - qop[b])
+        tiles.setdefault((b, hk, q0, qn, pos0), []).append((kvb, kv_end, slot, stride))
+    merges = 0
+    for (b, hk, q0, qn, pos0), ch in tiles.items():
+        ch.sort()
+        kve = min(kv_len_of(b), pos0 + qn)
+        assert kve == pos0 + qn  # causal: the last query sees its own key
+        assert ch[0][0] % kt == 0 and ch[0][0] <= max(0, pos0 - W if W >= 0 else 0)
+        assert ch[-1][1] == kve
+        for (_, e0, _, _), (b1, _, _, _) in zip(ch, ch[1:]):
+            assert e0 == b1 and b1 % kt == 0
+        if len(ch) == 1:
+            assert ch[0][2] == -1
+        else:
+            n = len(ch)
+            assert info.key_chunks >= n and all(c[3] == n for c in ch)
+            base = ch[0][2]
+            assert [c[2] for c in ch] == list(range(base, base + n))
+            mine = set(range(base, base + qn * n))
+            assert not (mine & slots)
+            slots |= mine
+            merges += qn
+        for t in range(q0, q0 + qn):
+            seen[(b, hk, t)] = seen.get((b, hk, t), 0) + 1
+    assert info.num_merges == merges
+    return seen
 
 
 @st.composite
@@ -162,18 +189,14 @@ def test_one_pass_cascade_plan_invariants(batch):
              prefill_variant=variant, batch_capacity=len(qo), qo_capacity=max(1, sum(qo)),
              kv_capacity=max(1, max(tab)))
     try:
-        assert P.pkvs_workspace_size(h)[0] == 0  # one pass: no float workspace
+        assert P.pkvs_plan_get_info(h).cascade_passes == 1
         qop, kvp, last = csr(qo, tab, page)
         P.pkvs_cascade_plan(h, qop, kvp, last, len(qo), None, None)
+        info = P.pkvs_plan_get_info(h)
+        kt = 64 if info.prefill_variant in (5, 6) else 32
         items = P.pkvs_plan_copy_items(h).tolist()
-        seen = {}
-        for it in items:
-            b, hk, q0, qn, pos0, kv_len, pbase, kvb, split = it[:9]
-            assert kv_len == tab[b] + qo[b] and split == tab[b] and pbase == kvp[b]
-            assert pos0 == tab[b] + (q0 - qop[b])
-            assert kvb <= max(0, pos0 - W if W >= 0 else 0)
-            for t in range(q0, q0 + qn):
-                seen[(b, hk, t)] = seen.get((b, hk, t), 0) + 1
+        seen = check_tiles(items, kt, W, lambda b: tab[b], lambda b: tab[b] + qo[b],
+                           lambda b: tab[b], kvp, qop, info)
         expect = {(b, hk, t) for b in range(len(qo)) for hk in range(2)
                   for t in range(qop[b], qop[b + 1])}
         assert set(seen) == expect and set(seen.values()) <= {1}
