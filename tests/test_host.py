@@ -540,7 +540,8 @@ def test_cascade_one_pass_work_list():
     h = P.pkvs_plan_create(desc(P.PKVS_CASCADE, num_qo_heads=8, num_kv_heads=2, window_left=W,
                                 prefill_variant=5))
     assert P.pkvs_plan_get_info(h).prefill_variant == 5
-    assert P.pkvs_workspace_size(h)[0] == 0
+    assert P.pkvs_plan_get_info(h).cascade_passes == 1
+    assert P.pkvs_workspace_size(h)[0] == 0  # variant 5 never splits key ranges
     qop, kvp, last = csr(qo, tab, 16)
     P.pkvs_cascade_plan(h, qop, kvp, last, len(qo), None, None)
     items = P.pkvs_plan_copy_items(h).tolist()
@@ -559,8 +560,51 @@ def test_cascade_one_pass_work_list():
     for variant, one_pass in ((1, True), (2, True), (3, False), (4, False), (6, False)):
         h2 = P.pkvs_plan_create(desc(P.PKVS_CASCADE, num_qo_heads=8, num_kv_heads=2,
                                      window_left=W, prefill_variant=variant))
-        assert (P.pkvs_workspace_size(h2)[0] == 0) == one_pass, variant
+        info = P.pkvs_plan_get_info(h2)
+        assert info.cascade_passes == (1 if one_pass else 2), variant
+        # (one pass: no float workspace at these capacities, which allow no
+        # key split; two passes: the paged pass's (o, lse))
+        assert info.key_chunks == 1 and (P.pkvs_workspace_size(h2)[0] == 0) == one_pass, variant
         P.pkvs_plan_destroy(h2)
+
+
+@pytest.mark.parametrize("kind", [P.PKVS_PREFILL, P.PKVS_CASCADE])
+def test_key_split_is_fixed_by_the_capacities(kind):
+    """The key split is allowed, with its partial slots and merge entries, only
+    when the capacities can never give more query tiles than half the grid;
+    disable_split_kv turns it off; decode plans and the two-pass cascade never
+    cut.  A dry plan of a small batch with long key ranges cuts them."""
+    small = dict(num_qo_heads=8, num_kv_heads=2, head_dim=128, window_left=-1,
+                 batch_capacity=4, qo_capacity=256, kv_capacity=4096, prefill_variant=1)
+    h = P.pkvs_plan_create(desc(kind, **small))
+    info = P.pkvs_plan_get_info(h)
+    tiles = 2 * (256 // info.query_tile + 4)
+    assert info.key_chunks == min(8, info.grid_blocks // tiles) > 1
+    fb, _ = P.pkvs_workspace_size(h)
+    # 16-bit o + fp32 lse per (slot, head); slots = tokens x kv heads x chunks
+    assert fb == 256 * 2 * info.key_chunks * 4 * (128 * 2 + 4)
+    qop, kvp, last = csr([100, 3], [3000, 1003], 16)
+    plan = P.pkvs_prefill_plan if kind == P.PKVS_PREFILL else P.pkvs_cascade_plan
+    if kind == P.PKVS_CASCADE:
+        qop, kvp, last = csr([100, 3], [2900, 1000], 16)  # cached keys only
+    plan(h, qop, kvp, last, 2, None, None)
+    info = P.pkvs_plan_get_info(h)
+    assert info.num_merges == 2 * 103  # every token of both requests, both kv heads
+    P.pkvs_plan_destroy(h)
+    for extra in (dict(disable_split_kv=1), dict(qo_capacity=8192), dict(prefill_variant=5)):
+        h = P.pkvs_plan_create(desc(kind, **{**small, **extra}))
+        assert P.pkvs_plan_get_info(h).key_chunks == 1, extra
+        assert P.pkvs_workspace_size(h)[0] == 0, extra
+        P.pkvs_plan_destroy(h)
+    if kind == P.PKVS_CASCADE:
+        h = P.pkvs_plan_create(desc(kind, **{**small, "prefill_variant": 3}))
+        assert P.pkvs_plan_get_info(h).cascade_passes == 2
+        assert P.pkvs_plan_get_info(h).key_chunks == 1
+        P.pkvs_plan_destroy(h)
+    h = P.pkvs_plan_create(desc(P.PKVS_DECODE, **{k: v for k, v in small.items()
+                                                 if k != "qo_capacity"}))
+    assert P.pkvs_plan_get_info(h).key_chunks == 1
+    P.pkvs_plan_destroy(h)
 
 
 def test_cascade_workspace_and_errors():
