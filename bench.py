@@ -212,6 +212,10 @@ CASCADE_WORKLOADS = {
     # the last 8192 tokens of a 32768-token prompt over its cached 24576
     "chunk_8192_after_24576": dict(qo=[8192], kv=[32768], H_q=32, H_kv=8, D=128, P=16,
                                    W=4095, seed=6),
+    # a 1024-token chunk of a prompt over its cached 8192: 128 query tiles of
+    # 64 tokens for 256 workgroups, so the plan cuts their key ranges
+    "chunk_1024_after_8192": dict(qo=[1024], kv=[9216], H_q=32, H_kv=8, D=128, P=16, W=4095,
+                                  seed=7),
 }
 
 
@@ -273,6 +277,8 @@ def bench_cascade(reps: int) -> dict:
                      "paged_prefill_ms_median": round(res["paged"]["median"], 4),
                      "window_effective_flops": flops,
                      "prefill_variant": cas.info().prefill_variant,
+                     # (token, kv head) rows merged after a key split: cascade, paged
+                     "key_split_merges": [cas.info().num_merges, one.info().num_merges],
                      "batch": c.batch_size, "new_tokens": sum(c.qo_lens),
                      "cached_keys_in_tables": sum(ci.table_lens)}
         del ci, c

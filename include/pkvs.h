@@ -231,13 +231,15 @@ int pkvs_workspace_bytes(const pkvs_desc *desc, int32_t is_decode, int64_t max_k
  * With int_ws == NULL the plan is built on the host only ("dry plan",
  * inspectable with pkvs_plan_copy_items, not runnable).
  * Key split (split-KV for prefill, the combine of [FIB] _safe_merge_state):
- * on prefill variants 1 and 2 with 16-bit queries, a plan whose capacities
- * can never give more query tiles than half the workgroups its grid keeps
- * resident may cut the key range of a batch's longest tiles into chunks of
- * whole key tiles, each a work item writing a partial (o, lse) per query
- * token into the float workspace; run() then merges each token's chunks.  A
- * batch is cut when that shortens its longest item by more than the merge
- * costs; disable_split_kv = 1 turns the split off (float_ws then 0 bytes).
+ * on prefill variants 1, 2 and 5 with 16-bit queries, a batch with at most
+ * one query tile per two workgroups of the plan's grid may have the key
+ * ranges of its longest tiles cut into chunks of whole key tiles, each a
+ * work item writing a partial (o, lse) per query token into the float
+ * workspace, at most one item per workgroup in all; run() then merges each
+ * token's chunks.  A batch is cut when that shortens its longest item by
+ * more than the merge costs.  The float workspace holds the partial slots
+ * for that (sized from the grid, not the capacities); disable_split_kv = 1
+ * turns the split off (float_ws then 0 bytes).
  * Errors: INVALID_ARG (qo_len_b > kv_len_b, last page length outside
  * [1, page_size], decreasing indptr), CAPACITY, WORKSPACE, HIP. */
 int pkvs_prefill_plan(pkvs_plan *plan, const int32_t *qo_indptr_h, const int32_t *kv_indptr_h,

@@ -593,11 +593,14 @@ __global__ __launch_bounds__(kDecodeThreads * NW) void decode_kernel(DecodeArgs 
 // (merge entry, query head of the group); the LSE-weighted sum of
 // pkvs_merge_state, folded over all chunks at once.  P16: the partial o is in
 // the query dtype (part_o16; a key-split prefill's merge entries are (query
-// token, kv head) pairs), else fp32.
+// token, kv head) pairs), else fp32.  Lane l holds elements E l .. E l + E - 1
+// of the row, so each partial row is one contiguous load per lane.
 template <int D, bool F16, bool P16>
 __global__ __launch_bounds__(kMergeThreads) void decode_merge_kernel(DecodeArgs a)
 {
     constexpr int E = D / 64;  // elements per lane
+    using P16v = uint16_t __attribute__((ext_vector_type(E)));
+    using P32v = float __attribute__((ext_vector_type(E)));
     const int lane = threadIdx.x;
     const int G = 1 << a.log2_group;
     const int n_merges = a.ws[kHdrNumMerges];
@@ -618,21 +621,22 @@ __global__ __launch_bounds__(kMergeThreads) void decode_merge_kernel(DecodeArgs 
                 const float wk = fast_exp2((a.part_lse[sl] - M) * 1.44269504088896340736f);
                 sum += wk;
                 if constexpr (P16) {
-                    const uint16_t *po = a.part_o16 + sl * D;
+                    const P16v v = *reinterpret_cast<const P16v *>(a.part_o16 + sl * D + E * lane);
 #pragma unroll
-                    for (int e = 0; e < E; ++e) acc[e] += wk * from16<F16>(po[lane + 64 * e]);
+                    for (int e = 0; e < E; ++e) acc[e] += wk * from16<F16>(v[e]);
                 } else {
-                    const float *po = a.part_o + sl * D;
+                    const P32v v = *reinterpret_cast<const P32v *>(a.part_o + sl * D + E * lane);
 #pragma unroll
-                    for (int e = 0; e < E; ++e) acc[e] += wk * po[lane + 64 * e];
+                    for (int e = 0; e < E; ++e) acc[e] += wk * v[e];
                 }
             }
         }
         const float inv = sum > 0.f ? 1.f / sum : 0.f;
-        uint16_t *O = static_cast<uint16_t *>(a.o);
         const int64_t orow = (int64_t(b) * a.num_qo_heads + hk * G + h) * D;
+        P16v out;
 #pragma unroll
-        for (int e = 0; e < E; ++e) O[orow + lane + 64 * e] = to16<F16>(acc[e] * inv);
+        for (int e = 0; e < E; ++e) out[e] = to16<F16>(acc[e] * inv);
+        *reinterpret_cast<P16v *>(static_cast<uint16_t *>(a.o) + orow + E * lane) = out;
         if (a.lse && lane == 0)
             a.lse[int64_t(b) * a.num_qo_heads + hk * G + h] =
                 sum > 0.f ? M + fast_log2(sum) * kLn2 : kNegInf;

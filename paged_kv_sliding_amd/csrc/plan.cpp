@@ -60,12 +60,16 @@ static void size_plan(Plan *p)
     const int64_t group = d.num_qo_heads / d.num_kv_heads;
     int64_t items = 0, slots = 0, merges = 0;
     if (d.kind == PKVS_PREFILL) {
-        items = hkv * (ceil_div(d.qo_capacity, p->query_tile) + B) * p->key_chunks_max;
+        items = hkv * (ceil_div(d.qo_capacity, p->query_tile) + B);
         if (p->key_chunks_max > 1) {
-            // a split tile of n tokens cut into c chunks takes n * c slots and
-            // n merge entries
-            slots = int64_t(d.qo_capacity) * hkv * p->key_chunks_max;
-            merges = int64_t(d.qo_capacity) * hkv;
+            // A batch is cut only with at most grid / kSplitFillShare tiles,
+            // into at most grid chunks in all (see build_prefill); a tile of n
+            // tokens cut into c chunks takes n * c slots and n merge entries.
+            const int64_t cut_tiles = p->grid_blocks / kSplitFillShare;
+            const int64_t cut_items = p->grid_blocks;
+            items = std::max(items, cut_items);
+            slots = int64_t(p->query_tile) * cut_items;
+            merges = int64_t(p->query_tile) * cut_tiles;
         }
         // a ragged pass's row-index table: at most one entry per kRaggedPage
         // tokens of each request, rounded up per request
@@ -271,22 +275,44 @@ static int build_prefill(Plan *p, const std::vector<Req> &reqs)
             }
         }
     }
-    // Key-split: with fewer tiles than resident workgroups, cut the longest
-    // tiles' key ranges into chunks of whole key tiles (each a work item with
-    // partial slots) when the longest item then ends sooner by more than the
-    // merge costs; the merge entries combine each token's chunks.
+    // Key split: with at most one tile per kSplitFillShare resident
+    // workgroups, cut the longest tiles' key ranges into chunks of about c
+    // whole key tiles (each a work item with partial slots), c the smallest
+    // chunk length with at most one item per resident workgroup in all (a
+    // second round would undo the cut), when the longest item then ends
+    // sooner by more than the merge costs; the merge entries combine each
+    // token's chunks.
     std::vector<int32_t> merges;
-    if (p->key_chunks_max > 1 && int64_t(items.size()) < p->grid_blocks) {
+    if (p->key_chunks_max > 1 && int64_t(items.size()) * kSplitFillShare <= p->grid_blocks) {
         auto tiles_of = [&](const It &it) { return ceil_div(std::max<int64_t>(it.cost, 0), kv_tile); };
         int64_t total = 0, longest = 0;
         for (const It &it : items) {
             total += tiles_of(it);
             longest = std::max(longest, tiles_of(it));
         }
-        const int64_t c = std::max<int64_t>(kMinChunkTiles, ceil_div(total, p->grid_blocks));
+        int64_t c = 0;
+        // chunks of a tile of t key tiles for chunk length c (at most
+        // key_chunks_max, none empty)
         auto chunks_of = [&](int64_t t) {
-            return std::max<int64_t>(1, std::min<int64_t>(p->key_chunks_max, ceil_div(t, c)));
+            const int64_t n = std::max<int64_t>(1, std::min<int64_t>(p->key_chunks_max, ceil_div(t, c)));
+            return t > 0 ? ceil_div(t, ceil_div(t, n)) : int64_t(1);
         };
+        auto items_at = [&](int64_t len) {
+            c = len;
+            int64_t n = 0;
+            for (const It &it : items) n += chunks_of(tiles_of(it));
+            return n;
+        };
+        // (items_at is non-increasing in the length; at the longest tile it
+        // is the uncut count)
+        int64_t lo = std::max<int64_t>(kMinChunkTiles, ceil_div(total, p->grid_blocks));
+        int64_t hi = std::max(lo, longest);
+        while (lo < hi) {
+            const int64_t mid = (lo + hi) / 2;
+            if (items_at(mid) <= p->grid_blocks) hi = mid;
+            else lo = mid + 1;
+        }
+        items_at(lo);
         int64_t longest_chunk = 0;
         for (const It &it : items) {
             const int64_t t = tiles_of(it);
@@ -297,8 +323,7 @@ static int build_prefill(Plan *p, const std::vector<Req> &reqs)
             int64_t slot = 0;
             for (const It &it : items) {
                 const int64_t t = tiles_of(it);
-                const int64_t per = ceil_div(t, chunks_of(t));
-                const int64_t n = per > 0 ? ceil_div(t, per) : 1;
+                const int64_t n = chunks_of(t);
                 if (n <= 1) {
                     cut.push_back(it);
                     continue;
@@ -311,6 +336,8 @@ static int build_prefill(Plan *p, const std::vector<Req> &reqs)
                 for (int64_t r = 0; r < qn; ++r)
                     merges.insert(merges.end(), {int32_t(it.w[kPiQBegin] + r), it.w[kPiKvHead],
                                                  int32_t(slot + r * n), int32_t(n)});
+                // n chunks of per key tiles, the last one shorter (never empty)
+                const int64_t per = ceil_div(t, n);
                 const int64_t kb = it.w[kPiKvBegin], ke = it.w[kPiKvEnd];
                 for (int64_t k = 0; k < n; ++k) {
                     It ch = it;
@@ -340,9 +367,10 @@ static int build_prefill(Plan *p, const std::vector<Req> &reqs)
         for (const It &it : items) {
             const int64_t kb = it.w[kPiKvBegin];
             const int64_t kv_len = it.w[kPiKvLen];
-            const int64_t kv_end =
+            const int64_t kv_end = std::min<int64_t>(
+                it.w[kPiKvEnd],
                 d.causal ? std::min<int64_t>(kv_len, int64_t(it.w[kPiPos0]) + it.w[kPiQCount])
-                         : kv_len;
+                         : kv_len);
             if (kv_end <= kb) continue;
             const int64_t last = std::min(kb + ceil_div(kv_end - kb, kv_tile) * kv_tile,
                                           kv_len) - 1;
@@ -587,13 +615,30 @@ static int create_plan(const pkvs_desc *desc, bool ragged, Plan **out, bool make
         // are the fastest measured for head_dim <= 128, and for head_dim 128
         // with 16-bit K/V the 64-key-step direct-to-LDS kernel is the fastest
         // of them.  128-row workgroups serve head_dim 256 and batches too small
-        // to fill the device with 256-row tiles.  Variants 3 and 4 are
-        // available on request.
+        // to fill the device with 256-row tiles -- except that with the key
+        // split (which fills the device by cutting key ranges) the 64-key
+        // kernel is also the faster one for head_dim 128 once an item can
+        // span kBigSplitKeys keys (measured: chunks of long prompts, prompts
+        // of 1024 tokens and more).  Variants 3 and 4 are available on request.
         const int64_t big_tiles = ceil_div(desc->qo_capacity, 256 / group) * desc->num_kv_heads;
         int v = kPrefillRows128;
-        if (desc->head_dim <= 128 && big_tiles >= 2 * p->num_cus)
+        bool big_for_split = false;
+        if (desc->head_dim <= 128 && big_tiles >= 2 * p->num_cus) {
             v = desc->head_dim == 128 && kvf == PKVS_KV_SAME ? kPrefillBig : kPrefillRows256;
-        if (desc->prefill_variant) v = desc->prefill_variant;
+        } else if (key_split && !desc->disable_split_kv && !ragged && !fp32 &&
+                   desc->head_dim == 128 && kvf == PKVS_KV_SAME) {
+            int64_t span = desc->kv_capacity;
+            if (desc->window_left >= 0 && desc->causal)
+                span = std::min<int64_t>(span, int64_t(desc->window_left) + 256 / group);
+            if (span >= kBigSplitKeys) {
+                v = kPrefillBig;
+                big_for_split = true;
+            }
+        }
+        if (desc->prefill_variant) {
+            v = desc->prefill_variant;
+            big_for_split = false;
+        }
         // the direct-to-LDS variants need 104-156 KiB of LDS per workgroup
         // ... and an LDS table of at most kPrefillDmaPages page ids per item:
         // they are kept only when no item within the capacities can span more
@@ -605,13 +650,13 @@ static int create_plan(const pkvs_desc *desc, bool ragged, Plan **out, bool make
         if (dma_v) {
             span = item_pages_bound(*desc, v == kPrefillDma ? kPrefillKvTile : kPrefillBigTile,
                                     (v == kPrefillDuo ? 128 : 256) / group);
-            if (span > kPrefillDmaPages) v = kPrefillRows256;
+            if (span > kPrefillDmaPages) v = big_for_split ? kPrefillRows128 : kPrefillRows256;
         }
         if (v == kPrefillDuo) p->table_pages = int(std::min<int64_t>(kPrefillDmaPages,
                                                                      (span + 15) / 16 * 16));
         if ((v == kPrefillDma || v == kPrefillBig || v == kPrefillDuo) && p->have_gpu && !fp32 &&
             prefill_blocks_per_cu(desc->head_dim, v, f16, kvf, p->table_pages) < 1)
-            v = kPrefillRows256;
+            v = big_for_split ? kPrefillRows128 : kPrefillRows256;
         p->prefill_variant = v;
         const int rows = v == kPrefillRows128 || v == kPrefillDuo ? 128 : 256;
         p->query_tile = fp32 ? kGenericQTile : rows / group;
@@ -623,18 +668,13 @@ static int create_plan(const pkvs_desc *desc, bool ragged, Plan **out, bool make
                          ? prefill_blocks_per_cu(desc->head_dim, v, f16, kvf, p->table_pages)
                          : 0;
         p->grid_blocks = p->num_cus * std::max(per_cu, fp32 ? 2 : 1);
-        // Key-split (the register-staged 128- and 256-row kernels): allowed
-        // when the capacities can never give more than one query tile per
-        // kSplitFillShare resident workgroups, with enough chunks per tile to
-        // reach about one item per workgroup.  Fixed here, like the partial
-        // slots it needs, so that a captured run stays valid for every plan.
+        // Key split on the 128- and 256-row register-staged kernels and the
+        // default 64-key one: fixed here, like the partial slots it needs
+        // (sized from the grid), so that a captured run stays valid for every
+        // plan; plan() cuts only batches of few query tiles.
         if (key_split && !desc->disable_split_kv && !ragged && !fp32 &&
-            (v == kPrefillRows128 || v == kPrefillRows256)) {
-            const int64_t tiles = int64_t(desc->num_kv_heads) *
-                                  (ceil_div(desc->qo_capacity, p->query_tile) + desc->batch_capacity);
-            if (tiles * kSplitFillShare <= p->grid_blocks)
-                p->key_chunks_max = int(std::min<int64_t>(kMaxKeyChunks, p->grid_blocks / tiles));
-        }
+            (v == kPrefillRows128 || v == kPrefillRows256 || v == kPrefillBig))
+            p->key_chunks_max = kMaxKeyChunks;
     } else {
         p->query_tile = 1;
         p->item_words = fp32 ? kPrefillItemWords : kDecodeItemWords;

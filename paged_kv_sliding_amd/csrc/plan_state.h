@@ -20,19 +20,23 @@ constexpr int64_t kMinAutoSplit = 256; // smallest key chunk the planner picks b
 constexpr double kWaveBytesPerUs = 10.0e3;
 constexpr double kChipBytesPerUs = 5.5e6;
 constexpr double kMergeUs = 10.0;
-// Key-split prefill (small batches on the register-staged kernels): a plan
-// whose capacities allow fewer query tiles than kSplitFillShare of the
-// resident workgroups may cut a tile's key range into up to kMaxKeyChunks
-// chunks of whole key tiles, each a work item of its own, whose partials a
-// merge combines.  A batch is split when its longest item, in key tiles plus
-// kItemStartTiles, exceeds the longest chunk's plus kMergeTiles (the merge
-// launch, in key tiles of the chunk's kernel), and never into chunks shorter
-// than kMinChunkTiles.
+// Key-split prefill (prefill variants 1, 2 and 5): a batch with at most one
+// query tile per kSplitFillShare resident workgroups may have its tiles' key
+// ranges cut into up to kMaxKeyChunks chunks of whole key tiles, each a work
+// item of its own, whose partials a merge combines.  It is cut when its
+// longest item, in key tiles, exceeds the longest chunk's by more than
+// kMergeTiles (the merge launch, in key tiles of the kernel), and never into
+// chunks shorter than kMinChunkTiles.  The chunks of a cut batch number at
+// most the resident workgroups, which bounds the partial slots whatever the
+// capacities.
 constexpr int kMaxKeyChunks = 8;
 constexpr int64_t kSplitFillShare = 2;
-constexpr int64_t kItemStartTiles = 2;
 constexpr int64_t kMergeTiles = 3;
 constexpr int64_t kMinChunkTiles = 3;
+// prefill_variant = 0, head_dim 128, 16-bit K/V, capacities too small to fill
+// the device with 256-row tiles: the 64-key kernel (with the key split) when
+// an item can span at least this many keys, else the 128-row kernel
+constexpr int64_t kBigSplitKeys = 512;
 // decode, pkvs_desc.decode_waves = 0: four waves per work item for batches of
 // at most one (request, kv head) pair per kFourWavePairShare resident one-wave
 // items whose requests can exceed kFourWaveKeys keys after the window trim

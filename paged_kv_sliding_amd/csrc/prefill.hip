@@ -31,6 +31,12 @@
 // wrapper", section "What": the tile skip alone leaks keys); interior tiles
 // are fully visible and skip the compare.
 //
+// Key split (prefill_kernel and prefill_big_kernel, batches of few query
+// tiles): an item may be one chunk of a tile's key range, ending at a key
+// tile boundary (kPiKvEnd); it then writes
+// each row's partial (o normalised over its keys, in the query dtype; lse in
+// fp32) to the float workspace for the per-token merge instead of o / lse.
+//
 // fp32 path (attention_fp32_kernel): a plain wave-per-row loop in fp32 for
 // fp32 inputs, used for small correctness-critical problems; it serves both
 // prefill items and decode (as one-query items).
@@ -327,6 +333,29 @@ __device__ __forceinline__ void dma_rows4_kv(const uint32_t (&mk)[4], const uint
                    "s"(mv[2]), "s"(mv[3]), "v"(off[0]), "v"(off[1]), "v"(off[2]), "v"(off[3]),
                    "s"(kb), "s"(vb)
                  : "memory");
+}
+
+// Key split: a row's partial over one key chunk -- o normalised over the
+// chunk's keys (times v_scale), rounded to the query dtype, and its lse in
+// fp32 (-inf when no key of the chunk is visible) -- to slot row sl of the
+// float workspace.  Lane (l32, hw) holds dims 32 dt + 8 m0 + 4 hw + m1 of its
+// row in o[dt][4 m0 + m1].
+template <bool F16, int DT>
+__device__ __forceinline__ void store_partial(const PrefillArgs &a, int64_t sl,
+                                              const f32x16 (&o)[DT], float m, float l, int hw)
+{
+    const float w_self = l > 0.f ? a.v_scale / l : 0.f;
+    uint16_t *PO = static_cast<uint16_t *>(a.part_o) + sl * (DT * 32);
+#pragma unroll
+    for (int dt = 0; dt < DT; ++dt)
+#pragma unroll
+        for (int m0 = 0; m0 < 4; ++m0) {
+            f32x4 v4;
+#pragma unroll
+            for (int m1 = 0; m1 < 4; ++m1) v4[m1] = o[dt][4 * m0 + m1] * w_self;
+            *reinterpret_cast<bf16x4 *>(PO + dt * 32 + 8 * m0 + 4 * hw) = to16x4<F16>(v4);
+        }
+    if (hw == 0) a.part_lse[sl] = l > 0.f ? (m + fast_log2(l)) * kLn2 : kNegInf;
 }
 
 template <int D, int NW, bool DMA, bool F16, int KVF>
@@ -635,21 +664,9 @@ __global__ __launch_bounds__(NW * 64) void prefill_kernel(PrefillArgs a)
         // epilogue: the two half-waves hold disjoint keys of each row
         l += __shfl_xor(l, 32);
         if (row_valid && slot0 >= 0) {
-            // one key chunk of a split tile: the row's partial (o normalised
-            // over the chunk's keys, lse) to its slot, for the merge
-            const int64_t sl = int64_t(slot0 + row_tok * slot_stride) * G + row_head;
-            const float w_self = l > 0.f ? a.v_scale / l : 0.f;
-            uint16_t *PO = static_cast<uint16_t *>(a.part_o) + sl * D;
-#pragma unroll
-            for (int dt = 0; dt < DT; ++dt)
-#pragma unroll
-                for (int m0 = 0; m0 < 4; ++m0) {
-                    f32x4 v4;
-#pragma unroll
-                    for (int m1 = 0; m1 < 4; ++m1) v4[m1] = o[dt][4 * m0 + m1] * w_self;
-                    *reinterpret_cast<bf16x4 *>(PO + dt * 32 + 8 * m0 + 4 * hw) = to16x4<F16>(v4);
-                }
-            if (hw == 0) a.part_lse[sl] = l > 0.f ? (m + fast_log2(l)) * kLn2 : kNegInf;
+            // one key chunk of a split tile: the row's partial to its slot
+            store_partial<F16>(a, int64_t(slot0 + row_tok * slot_stride) * G + row_head, o, m, l,
+                               hw);
         } else if (row_valid) {
             const int64_t lrow = int64_t(q_begin + row_tok) * a.num_qo_heads + hk * G + row_head;
             float w_self = l > 0.f ? a.v_scale / l : 0.f, w_other = 0.f;
@@ -1168,7 +1185,8 @@ __global__ __launch_bounds__(512) void prefill_big_kernel(PrefillArgs a)
         // one-pass cascade: keys from `split` on are the new tokens' rows
         const int split = w[kPiSplit];
         const int ext_row0 = q_begin - pos0;
-        const int kv_end = a.causal ? min(kv_len, pos0 + q_count) : kv_len;
+        // (a key chunk of a split tile ends at a key tile boundary)
+        const int kv_end = min(a.causal ? min(kv_len, pos0 + q_count) : kv_len, w[kPiKvEnd]);
         const int pos_last = pos0 + q_count - 1;
         const int ntiles = kv_end > kv_begin ? (kv_end - kv_begin + BIG_T - 1) / BIG_T : 0;
         const int pt_lo = kv_begin >> a.log2_page;
@@ -1432,7 +1450,12 @@ __global__ __launch_bounds__(512) void prefill_big_kernel(PrefillArgs a)
         }
 
         l += __shfl_xor(l, 32);
-        if (row_valid) {
+        const int slot0 = w[kPiSlot];
+        if (row_valid && slot0 >= 0) {
+            // one key chunk of a split tile: the row's partial to its slot
+            store_partial<F16>(a, int64_t(slot0 + row_tok * w[kPiSlotStride]) * G + row_head, o,
+                               m, l, hw);
+        } else if (row_valid) {
             const int64_t lrow = int64_t(q_begin + row_tok) * a.num_qo_heads + hk * G + row_head;
             float w_self = l > 0.f ? a.v_scale / l : 0.f, w_other = 0.f;
             float lse_row = l > 0.f ? (m + fast_log2(l)) * kLn2 : kNegInf;

@@ -414,16 +414,18 @@ def _sub_layout(case, picks):
             torch.tensor(kv_ind, **i32), torch.tensor(last, **i32))
 
 
-@pytest.mark.parametrize("decode,nw,split", [(False, 0, -1), (True, 1, 64), (True, 4, 64),
-                                              (True, 1, -1), (False, 0, -2)])
-def test_graph_replay_follows_replans(decode, nw, split):
+@pytest.mark.parametrize("decode,nw,split,variant", [
+    (False, 0, -1, 0), (True, 1, 64, 0), (True, 4, 64, 0), (True, 1, -1, 0), (False, 0, -2, 1),
+    (False, 0, -2, 5)])
+def test_graph_replay_follows_replans(decode, nw, split, variant):
     """run() captured once in a HIP graph stays valid for every later plan() of
     the same capacities (AMD-Ecosystem/flashinfer PR 234, "Why each fix" 2: the
     grid and the launch set come from the capacities, the work from the
     workspace).  Each replay, with eager work and synchronisations between
     replays, must equal an eager run() of the batch planned last, bit for bit.
     split = -2: a prefill whose full batch is key-split (chunk partials and a
-    merge launch) and whose one-request batch is not."""
+    merge launch) and whose one-request batch is not, on prefill variant
+    `variant`."""
     if not decode and split == -2:
         qo, kv = [40, 1, 130, 7, 64], [1300, 1, 130, 2500, 64]
         case = small(qo, kv, H_q=8, H_kv=2, D=128, P_=16, W=-1, seed=63)
@@ -438,9 +440,11 @@ def test_graph_replay_follows_replans(decode, nw, split):
     else:
         qo, kv = [40, 1, 130, 7, 64], [300, 1, 130, 500, 64]
         case = small(qo, kv, H_q=8, H_kv=2, D=128, P_=16, W=100, seed=62)
-    att = make_attention(case, decode_waves=nw)
+    att = make_attention(case, decode_waves=nw, prefill_variant=variant)
     if decode:
         assert att.info().decode_waves == nw
+    elif variant:
+        assert att.info().prefill_variant == variant
     B, n_q = case.batch_size, case.q.shape[0]
     q_buf = case.q.clone()
     idx_buf = case.kv_indices.clone()
@@ -505,7 +509,8 @@ def test_graph_replay_follows_replans(decode, nw, split):
             assert (att.info().num_merges > 0) == (len(req_sets[k]) > 1), k
         if len(layout[0]) == B:
             ro, rl = oracle_for(case)
-            compare(want_o, want_l, ro, rl, tag=f"graph decode={decode} nw={nw} split={split}")
+            compare(want_o, want_l, ro, rl,
+                    tag=f"graph decode={decode} nw={nw} split={split} variant={variant}")
 
 
 @pytest.mark.parametrize("decode,variant", [(False, 5), (False, 6), (True, 0)])
@@ -764,7 +769,7 @@ SPLIT_KV = [1500, 900, 2129, 1, 600]
 
 
 @pytest.mark.parametrize("variant,D,G", [(1, 64, 4), (1, 128, 8), (1, 256, 4), (2, 64, 2),
-                                         (2, 128, 4)])
+                                         (2, 128, 4), (5, 128, 4), (5, 128, 1)])
 @pytest.mark.parametrize("W,P_", [(-1, 16), (0, 4), (100, 1), (511, 16), (1023, 2)])
 def test_key_split_prefill(variant, D, G, W, P_):
     """The key split on the register-staged kernels: chunks of whole key
@@ -803,6 +808,25 @@ def test_key_split_prefill_types(dtype, kv_dtype, cap):
     o, lse = gpu_run(case, att=att)
     assert att.info().num_merges > 0
     tag = f"key split {dtype} kv={kv_dtype} cap={cap}"
+    assert_all_written(case, o, lse, tag)
+    ro, rl = oracle_for(case)
+    compare(o, lse, ro, rl, tag=tag)
+
+
+@pytest.mark.parametrize("W", [2047, -1])
+@pytest.mark.parametrize("variant", [0, 1, 5])
+def test_key_split_chunked_prefill(W, variant):
+    """A 512-token chunk of a long prompt over its 4096 cached keys (32/8
+    heads, head_dim 128; the 128-row kernel, the 64-key one, and the
+    planner's choice for these capacities, the 64-key one): 128 or 64 query
+    tiles for 256 workgroups, so every tile's keys are cut into chunks; every
+    row written, against the oracle."""
+    case = small([512], [4608], H_q=32, H_kv=8, D=128, P_=16, W=W, seed=29 + variant)
+    att = make_attention(case, prefill_variant=variant)
+    o, lse = gpu_run(case, att=att)
+    info = att.info()
+    assert info.prefill_variant == (variant or 5) and info.num_merges == 512 * 8
+    tag = f"key split chunked prefill W={W} items={info.num_items}"
     assert_all_written(case, o, lse, tag)
     ro, rl = oracle_for(case)
     compare(o, lse, ro, rl, tag=tag)
@@ -862,12 +886,12 @@ def cascade_run(case, trim=False, att=None, return_lse=True, **kw):
 @pytest.mark.parametrize("P_", [1, 16])
 @pytest.mark.parametrize("W", [-1, 0, 5, 100, 511])
 @pytest.mark.parametrize("trim", [False, True])
-@pytest.mark.parametrize("variant", [0, 5])
+@pytest.mark.parametrize("variant", [0, 1, 5])
 def test_cascade_equals_one_paged_prefill(P_, W, trim, variant):
     """Cascade prefill against the one paged prefill over prefix + new keys;
-    variant 5 runs the cascade in one pass (cached keys from the pages, new
-    keys from the contiguous K/V, split per request), the planner's choice for
-    this small batch runs the two passes and their merge."""
+    variants 1 and 5 run the cascade in one pass (cached keys from the pages,
+    new keys from the contiguous K/V, split per request), 0 is the planner's
+    choice for the capacities (variant 5 where an item can span 512 keys)."""
     qo = [1, 70, 0, 33, 129, 5, 300, 40]
     kv = [1, 90, 9, 300, 129, 700, 301, 1000]
     case = small(qo, kv, H_q=8, H_kv=2, D=128, P_=P_, W=W, seed=P_ * 31 + W + 7 * trim)
@@ -960,15 +984,15 @@ def test_cascade_one_pass_split_mid_group(P_):
 @pytest.mark.parametrize("dtype,cap", [(torch.float16, 0.0), (torch.bfloat16, 30.0),
                                        (torch.float16, 20.0)])
 def test_cascade_one_pass_fp16_and_soft_cap(dtype, cap):
-    """The one-pass cascade (variant 5; no float workspace) in IEEE half and
-    with a logits soft cap, against the oracle on the combined layout."""
+    """The one-pass cascade (variant 5) in IEEE half and with a logits soft
+    cap, against the oracle on the combined layout."""
     qo = [70, 1, 129, 300]
     kv = [90, 300, 129, 1000]
     case = small(qo, kv, H_q=8, H_kv=2, D=128, P_=16, W=100, seed=int(cap) + 3, dtype=dtype,
                  cap=cap)
     (o, lse), att = cascade_run(case, prefill_variant=5)
     info = att.info()
-    assert info.prefill_variant == 5 and info.float_ws_bytes == 0, "expected the one-pass plan"
+    assert info.prefill_variant == 5 and info.cascade_passes == 1, "expected the one-pass plan"
     ro, rl = oracle_for(case)
     compare(o, lse, ro, rl, tag=f"one-pass cascade {dtype} cap={cap}")
 

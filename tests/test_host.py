@@ -159,10 +159,15 @@ def visible(p, j, W, causal=True):
 
 @pytest.mark.parametrize("W", [-1, 0, 4, 31, 511])
 @pytest.mark.parametrize("G", [1, 4, 8])
-def test_prefill_items_cover_every_query_once(W, G):
+@pytest.mark.parametrize("cut", [False, True])
+def test_prefill_items_cover_every_query_once(W, G, cut):
+    """Every query in exactly one query tile whose key range holds all its
+    visible keys and no wholly invisible key tile; with the key split allowed
+    (cut) a tile may be several chunk items whose ranges partition it."""
     qo = [1, 0, 40, 300, 7, 129]
     kv = [1, 5, 40, 1000, 600, 129]
-    h = P.pkvs_plan_create(desc(num_qo_heads=2 * G, num_kv_heads=2, window_left=W))
+    h = P.pkvs_plan_create(desc(num_qo_heads=2 * G, num_kv_heads=2, window_left=W,
+                                disable_split_kv=int(not cut)))
     qop, kvp, last = csr(qo, kv, 16)
     P.pkvs_prefill_plan(h, qop, kvp, last, len(kv), None, None)
     info = P.pkvs_plan_get_info(h)
@@ -171,28 +176,36 @@ def test_prefill_items_cover_every_query_once(W, G):
     assert items.shape[0] == info.num_items
     # key tiles of the kernel the plan runs: 64 keys for variant 5, else 32
     kt = 64 if info.prefill_variant in (5, 6) else 32
-    seen = {}
+    tiles = {}
     for it in items.tolist():
-        b, hk, q0, qn, pos0, kv_len, pbase, kvb, split = it[:9]
+        b, hk, q0, qn, pos0, kv_len, pbase, kvb, split, kv_end, slot = it[:11]
         assert split == 2**31 - 1  # every key in the cache
         assert 1 <= qn <= info.query_tile and kv_len == kv[b] and pbase == kvp[b]
-        prefix = kv[b] - qo[b]
-        assert pos0 == prefix + (q0 - qop[b])
-        assert kvb % kt == 0
-        kve = min(kv_len, pos0 + qn)
+        assert pos0 == kv[b] - qo[b] + (q0 - qop[b])
+        assert kvb % kt == 0 and (slot >= 0) <= cut
+        tiles.setdefault((b, hk, q0, qn, pos0), []).append((kvb, kv_end))
+    seen = {}
+    for (b, hk, q0, qn, pos0), ranges in tiles.items():
+        ranges.sort()
+        for (_, e0), (b1, _) in zip(ranges, ranges[1:]):
+            assert e0 == b1 and b1 % kt == 0
+        kvb, kve = ranges[0][0], ranges[-1][1]
+        assert kve == min(kv[b], pos0 + qn)
         for t in range(q0, q0 + qn):
             seen[(b, hk, t)] = seen.get((b, hk, t), 0) + 1
-            p = prefix + (t - qop[b])
-            # every visible key of every query lies inside the item's key range
+            p = pos0 + (t - q0)
+            # every visible key of every query lies inside the tile's key range
             first_vis = max(0, p - W) if W >= 0 else 0
             assert kvb <= first_vis and p < kve
-        # no key tile of the range is wholly invisible to the item's queries
+        # no key tile of the range is wholly invisible to the tile's queries
         for k0 in range(kvb, kve, kt):
             assert any(visible(pos0 + i, j, W) for i in range(qn)
-                       for j in range(k0, min(k0 + kt, kve))), (it, k0)
+                       for j in range(k0, min(k0 + kt, kve))), (b, hk, q0, k0)
     expect = {(b, hk, t) for b in range(len(kv)) for hk in range(2)
               for t in range(qop[b], qop[b + 1])}
     assert set(seen) == expect and set(seen.values()) == {1}
+    if cut and W < 0:
+        assert info.num_merges > 0  # request 3's long tiles are cut
     P.pkvs_plan_destroy(h)
 
 
@@ -538,10 +551,10 @@ def test_cascade_one_pass_work_list():
     qo = [1, 70, 0, 33, 129, 300]
     tab = [0, 20, 9, 267, 2, 100]
     h = P.pkvs_plan_create(desc(P.PKVS_CASCADE, num_qo_heads=8, num_kv_heads=2, window_left=W,
-                                prefill_variant=5))
+                                prefill_variant=5, disable_split_kv=1))
     assert P.pkvs_plan_get_info(h).prefill_variant == 5
     assert P.pkvs_plan_get_info(h).cascade_passes == 1
-    assert P.pkvs_workspace_size(h)[0] == 0  # variant 5 never splits key ranges
+    assert P.pkvs_workspace_size(h)[0] == 0  # no key split: no float workspace
     qop, kvp, last = csr(qo, tab, 16)
     P.pkvs_cascade_plan(h, qop, kvp, last, len(qo), None, None)
     items = P.pkvs_plan_copy_items(h).tolist()
@@ -562,47 +575,68 @@ def test_cascade_one_pass_work_list():
                                      window_left=W, prefill_variant=variant))
         info = P.pkvs_plan_get_info(h2)
         assert info.cascade_passes == (1 if one_pass else 2), variant
-        # (one pass: no float workspace at these capacities, which allow no
-        # key split; two passes: the paged pass's (o, lse))
-        assert info.key_chunks == 1 and (P.pkvs_workspace_size(h2)[0] == 0) == one_pass, variant
+        # one pass: the key split's partial slots (variants 1 and 2 cut key
+        # ranges); two passes: no key split, the paged pass's (o, lse)
+        assert info.key_chunks == (8 if one_pass else 1), variant
+        assert P.pkvs_workspace_size(h2)[0] > 0, variant
         P.pkvs_plan_destroy(h2)
 
 
 @pytest.mark.parametrize("kind", [P.PKVS_PREFILL, P.PKVS_CASCADE])
-def test_key_split_is_fixed_by_the_capacities(kind):
-    """The key split is allowed, with its partial slots and merge entries, only
-    when the capacities can never give more query tiles than half the grid;
-    disable_split_kv turns it off; decode plans and the two-pass cascade never
-    cut.  A dry plan of a small batch with long key ranges cuts them."""
-    small = dict(num_qo_heads=8, num_kv_heads=2, head_dim=128, window_left=-1,
-                 batch_capacity=4, qo_capacity=256, kv_capacity=4096, prefill_variant=1)
-    h = P.pkvs_plan_create(desc(kind, **small))
+@pytest.mark.parametrize("variant", [1, 2, 5])
+def test_key_split_rules(kind, variant):
+    """The key split is fixed at plan creation for prefill variants 1, 2 and 5
+    (one-pass cascades included), whatever the capacities, with partial slots
+    sized from the grid: a batch is cut only with at most one query tile per
+    two resident workgroups, into at most one grid of chunks of whole key
+    tiles.  disable_split_kv turns it off; variants 3, 4 and 6, the two-pass
+    cascade and decode plans never cut."""
+    kw = dict(num_qo_heads=8, num_kv_heads=2, head_dim=128, window_left=-1,
+              batch_capacity=4, qo_capacity=16384, kv_capacity=16384, prefill_variant=variant)
+    h = P.pkvs_plan_create(desc(kind, **kw))
     info = P.pkvs_plan_get_info(h)
-    tiles = 2 * (256 // info.query_tile + 4)
-    assert info.key_chunks == min(8, info.grid_blocks // tiles) > 1
+    assert info.key_chunks == 8 and info.prefill_variant == variant
+    grid, tq = info.grid_blocks, info.query_tile
     fb, _ = P.pkvs_workspace_size(h)
-    # 16-bit o + fp32 lse per (slot, head); slots = tokens x kv heads x chunks
-    assert fb == 256 * 2 * info.key_chunks * 4 * (128 * 2 + 4)
-    qop, kvp, last = csr([100, 3], [3000, 1003], 16)
+    # 16-bit o + fp32 lse per (slot, query head of the group)
+    assert fb == tq * grid * 4 * (128 * 2 + 4)
     plan = P.pkvs_prefill_plan if kind == P.PKVS_PREFILL else P.pkvs_cascade_plan
+    # few tiles with long key ranges: cut
+    qo, kv = [100, 3], [3000, 1003]
     if kind == P.PKVS_CASCADE:
-        qop, kvp, last = csr([100, 3], [2900, 1000], 16)  # cached keys only
+        kv = [k - q for q, k in zip(qo, kv)]  # cached keys only
+    qop, kvp, last = csr(qo, kv, 16)
     plan(h, qop, kvp, last, 2, None, None)
     info = P.pkvs_plan_get_info(h)
     assert info.num_merges == 2 * 103  # every token of both requests, both kv heads
-    P.pkvs_plan_destroy(h)
-    for extra in (dict(disable_split_kv=1), dict(qo_capacity=8192), dict(prefill_variant=5)):
-        h = P.pkvs_plan_create(desc(kind, **{**small, **extra}))
-        assert P.pkvs_plan_get_info(h).key_chunks == 1, extra
-        assert P.pkvs_workspace_size(h)[0] == 0, extra
-        P.pkvs_plan_destroy(h)
+    assert info.num_items <= grid
+    # as many tiles as resident workgroups: not cut
+    qo, kv = [tq * grid // 2], [tq * grid // 2 + 4000]
     if kind == P.PKVS_CASCADE:
-        h = P.pkvs_plan_create(desc(kind, **{**small, "prefill_variant": 3}))
-        assert P.pkvs_plan_get_info(h).cascade_passes == 2
-        assert P.pkvs_plan_get_info(h).key_chunks == 1
+        kv = [4000]
+    qop, kvp, last = csr(qo, kv, 16)
+    plan(h, qop, kvp, last, 1, None, None)
+    assert P.pkvs_plan_get_info(h).num_merges == 0
+    P.pkvs_plan_destroy(h)
+    h = P.pkvs_plan_create(desc(kind, **{**kw, "disable_split_kv": 1}))
+    assert P.pkvs_plan_get_info(h).key_chunks == 1 and P.pkvs_workspace_size(h)[0] == 0
+    P.pkvs_plan_destroy(h)
+
+
+def test_key_split_only_on_its_variants():
+    kw = dict(num_qo_heads=8, num_kv_heads=2, head_dim=128, window_left=-1, batch_capacity=4,
+              qo_capacity=256, kv_capacity=4096)
+    for v in (3, 4, 6):
+        h = P.pkvs_plan_create(desc(P.PKVS_PREFILL, prefill_variant=v, **kw))
+        assert P.pkvs_plan_get_info(h).key_chunks == 1, v
+        assert P.pkvs_workspace_size(h)[0] == 0, v
         P.pkvs_plan_destroy(h)
-    h = P.pkvs_plan_create(desc(P.PKVS_DECODE, **{k: v for k, v in small.items()
-                                                 if k != "qo_capacity"}))
+    h = P.pkvs_plan_create(desc(P.PKVS_CASCADE, prefill_variant=3, **kw))
+    assert P.pkvs_plan_get_info(h).cascade_passes == 2
+    assert P.pkvs_plan_get_info(h).key_chunks == 1
+    P.pkvs_plan_destroy(h)
+    kw.pop("qo_capacity")
+    h = P.pkvs_plan_create(desc(P.PKVS_DECODE, **kw))
     assert P.pkvs_plan_get_info(h).key_chunks == 1
     P.pkvs_plan_destroy(h)
 
