@@ -589,24 +589,30 @@ __global__ __launch_bounds__(kDecodeThreads * NW) void decode_kernel(DecodeArgs 
     }
 }
 
-// Combine the chunk partials of every split (request, kv head): one wave per
-// (merge entry, query head of the group); the LSE-weighted sum of
-// pkvs_merge_state, folded over all chunks at once.  P16: the partial o is in
+// Combine the chunk partials of every split (request, kv head): one unit per
+// (merge entry, query head of the group), the LSE-weighted sum of
+// pkvs_merge_state folded over all chunks at once.  P16: the partial o is in
 // the query dtype (part_o16; a key-split prefill's merge entries are (query
-// token, kv head) pairs), else fp32.  Lane l holds elements E l .. E l + E - 1
-// of the row, so each partial row is one contiguous load per lane.
+// token, kv head) pairs), else fp32.  A wave merges kMergeUnitsPerWave units
+// at once, 64 / kMergeUnitsPerWave lanes each; lane i of a unit holds
+// elements E i .. E i + E - 1 of the row, so each partial row is one
+// contiguous load per lane, and the units' reads overlap.
 template <int D, bool F16, bool P16>
 __global__ __launch_bounds__(kMergeThreads) void decode_merge_kernel(DecodeArgs a)
 {
-    constexpr int E = D / 64;  // elements per lane
+    constexpr int L = 64 / kMergeUnitsPerWave;  // lanes per unit
+    constexpr int E = D / L;                    // elements per lane
     using P16v = uint16_t __attribute__((ext_vector_type(E)));
     using P32v = float __attribute__((ext_vector_type(E)));
-    const int lane = threadIdx.x;
+    const int li = threadIdx.x % L, grp = threadIdx.x / L;
     const int G = 1 << a.log2_group;
     const int n_merges = a.ws[kHdrNumMerges];
     const int32_t *merges = a.ws + a.ws[kHdrMergeOffset];
     const int units = n_merges << a.log2_group;
-    for (int u = blockIdx.x; u < units; u += gridDim.x) {
+    for (int u0 = blockIdx.x * kMergeUnitsPerWave; u0 < units;
+         u0 += gridDim.x * kMergeUnitsPerWave) {
+        const int u = u0 + grp;
+        if (u >= units) continue;
         const int32_t *me = merges + (u >> a.log2_group) * kMergeWords;
         const int h = u & (G - 1);
         const int b = me[kMeRequest], hk = me[kMeKvHead], first = me[kMeFirstSlot],
@@ -621,11 +627,11 @@ __global__ __launch_bounds__(kMergeThreads) void decode_merge_kernel(DecodeArgs 
                 const float wk = fast_exp2((a.part_lse[sl] - M) * 1.44269504088896340736f);
                 sum += wk;
                 if constexpr (P16) {
-                    const P16v v = *reinterpret_cast<const P16v *>(a.part_o16 + sl * D + E * lane);
+                    const P16v v = *reinterpret_cast<const P16v *>(a.part_o16 + sl * D + E * li);
 #pragma unroll
                     for (int e = 0; e < E; ++e) acc[e] += wk * from16<F16>(v[e]);
                 } else {
-                    const P32v v = *reinterpret_cast<const P32v *>(a.part_o + sl * D + E * lane);
+                    const P32v v = *reinterpret_cast<const P32v *>(a.part_o + sl * D + E * li);
 #pragma unroll
                     for (int e = 0; e < E; ++e) acc[e] += wk * v[e];
                 }
@@ -636,8 +642,8 @@ __global__ __launch_bounds__(kMergeThreads) void decode_merge_kernel(DecodeArgs 
         P16v out;
 #pragma unroll
         for (int e = 0; e < E; ++e) out[e] = to16<F16>(acc[e] * inv);
-        *reinterpret_cast<P16v *>(static_cast<uint16_t *>(a.o) + orow + E * lane) = out;
-        if (a.lse && lane == 0)
+        *reinterpret_cast<P16v *>(static_cast<uint16_t *>(a.o) + orow + E * li) = out;
+        if (a.lse && li == 0)
             a.lse[int64_t(b) * a.num_qo_heads + hk * G + h] =
                 sum > 0.f ? M + fast_log2(sum) * kLn2 : kNegInf;
     }

@@ -102,6 +102,8 @@ constexpr int kGenericThreads = 256;
 constexpr int kDecodeBlock = 32;       // keys per decode step
 constexpr int kDecodeThreads = 64;     // threads per wave of a decode work item
 constexpr int kMergeThreads = 64;
+// decode_merge_kernel: (merge entry, head) units merged together by one wave
+constexpr int kMergeUnitsPerWave = 4;
 constexpr int kMergeVecThreads = 256;  // merge_state, 16 bytes of v per lane
 constexpr int kAppendThreads = 256;    // cache writes: threads per workgroup (max)
 constexpr int kIndptrThreads = 1024;   // page-table build: the running-sum workgroup

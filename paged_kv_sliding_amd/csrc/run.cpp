@@ -153,7 +153,8 @@ int launch_key_split_merge(const pkvs_plan *p, void *o, float *lse, hipStream_t 
     a.num_qo_heads = p->desc.num_qo_heads;
     a.num_kv_heads = p->desc.num_kv_heads;
     a.log2_group = log2_exact(group);
-    const int grid = int(std::min<int64_t>(p->merges_cap * group, int64_t(p->num_cus) * 64));
+    const int grid = int(std::min<int64_t>(
+        (p->merges_cap * group + kMergeUnitsPerWave - 1) / kMergeUnitsPerWave, int64_t(p->num_cus) * 64));
     hipError_t e = launch_decode_merge(a, p->desc.head_dim, p->desc.dtype == PKVS_FP16, true,
                                        std::max(grid, 1), stream);
     if (e != hipSuccess) return fail(PKVS_ERR_HIP, "key-split merge launch: %s",
@@ -307,7 +308,8 @@ int pkvs_decode_run(const pkvs_plan *p, const void *q, const void *k_cache, cons
         hipStreamIsCapturing(stream, &capture) != hipSuccess)
         return fail(PKVS_ERR_HIP, "hipStreamIsCapturing failed");
     if (p->merges_cap > 0 && (p->n_merges > 0 || capture != hipStreamCaptureStatusNone)) {
-        const int grid = int(std::min<int64_t>(p->merges_cap * group, int64_t(p->num_cus) * 64));
+        const int grid = int(std::min<int64_t>(
+        (p->merges_cap * group + kMergeUnitsPerWave - 1) / kMergeUnitsPerWave, int64_t(p->num_cus) * 64));
         e = launch_decode_merge(a, p->desc.head_dim, f16, false, std::max(grid, 1), stream);
         if (e != hipSuccess)
             return fail(PKVS_ERR_HIP, "decode merge launch: %s", hipGetErrorString(e));
