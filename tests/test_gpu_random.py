@@ -2,13 +2,15 @@
 shape (batch, lengths, window, page size, head dim and group, dtype, logits
 soft cap, kernel variant, split size, waves per item) is drawn from a fixed
 seed, each run into NaN-filled outputs and compared with the oracle at the
-parity tolerances.  The draws cover combinations the hand-written cases do
-not list one by one."""
+parity tolerances; and chunks of long prompts (few query tiles over many
+cached keys, the shape the key split cuts), checked on sampled rows of every
+query tile.  The draws cover combinations the hand-written cases do not list
+one by one."""
 import numpy as np
 import pytest
 import torch
 
-from gpu_helpers import assert_all_written, compare, gpu_run, oracle_for
+from gpu_helpers import assert_all_written, compare, gpu_run, make_attention, oracle_for
 from paged_kv_sliding_amd.synth import case_from_lengths
 from test_gpu_parity import cascade_run
 
@@ -87,3 +89,33 @@ def test_random_cascade(seed):
     assert_all_written(case, o, lse, tag)
     ro, rl = oracle_for(case)
     compare(o, lse, ro, rl, tag=tag)
+
+
+@pytest.mark.parametrize("seed", range(10))
+def test_random_chunked_prefill(seed):
+    rng = np.random.default_rng(4000 + seed)
+    B = int(rng.integers(1, 4))
+    qo = [int(x) for x in rng.integers(1, 700, size=B)]
+    kv = [q + int(p) for q, p in zip(qo, rng.integers(500, 6000, size=B))]
+    W = int(rng.choice([-1, 511, 2047, 4095]))
+    G = int(rng.choice([1, 4, 8]))
+    P_ = int(rng.choice([1, 16]))
+    dtype = torch.float16 if rng.random() < 0.3 else torch.bfloat16
+    variant = int(rng.choice([0, 1, 2, 5]))
+    case = make_case("rk", qo, kv, 128, G, 2, dtype, 0.0, W, P_, seed)
+    att = make_attention(case, prefill_variant=variant)
+    o, lse = gpu_run(case, att=att)
+    info = att.info()
+    tag = (f"chunked seed={seed} qo={qo} kv={kv} W={W} G={G} P={P_} {dtype} "
+           f"v={info.prefill_variant} items={info.num_items} merges={info.num_merges}")
+    assert_all_written(case, o, lse, tag)
+    # a row of every query tile (and each request's first and last token)
+    rows = set()
+    for b in range(B):
+        q0, q1 = int(case.qo_indptr[b]), int(case.qo_indptr[b + 1])
+        rows |= {q0, q1 - 1}
+        rows |= {t + int(rng.integers(0, min(info.query_tile, q1 - t)))
+                 for t in range(q0, q1, info.query_tile)}
+    rows = sorted(rows)
+    ro, rl = oracle_for(case, rows=rows)
+    compare(o, lse, ro, rl, rows=rows, tag=tag)
