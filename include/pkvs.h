@@ -106,21 +106,21 @@ typedef enum pkvs_kind { PKVS_PREFILL = 0, PKVS_DECODE = 1, PKVS_CASCADE = 2 } p
  *                   one request are combined by the merge of pkvs_merge_state
  *  disable_split_kv decode: 1 = one chunk per request; prefill, cascade: 1 =
  *                   never split a query tile's keys (see pkvs_prefill_plan)
- *  prefill_variant  prefill kernel shape: 0 = planner's choice (from head_dim and
- *                   qo_capacity), 1 = 4 waves x 32 rows, 2 = 8 waves x 32 rows,
- *                   3 = 4 waves x 64 rows, software-pipelined (2 and 3: head_dim
- *                   <= 128), 4 = 8 waves x 32 rows with K/V rows loaded straight
- *                   into LDS, 5 = as 4 with 64-key steps and 16-byte loads
- *                   into a chunk-permuted LDS layout, 6 = as 5 with 4 waves
- *                   x 32 rows and two workgroups per CU (4, 5 and 6: head_dim 128,
- *                   16-bit K/V; they hold an item's page ids in a 2048-entry
- *                   LDS table, so a plan whose capacities let one item span
- *                   more pages -- (kv_capacity - 1) / page_size + 1, or with
- *                   a window (window_left + query tile + 2 key tiles - 3) /
- *                   page_size + 2 if smaller, above 2048 -- runs variant 2
- *                   instead); rows are (query token,
- *                   head) pairs.  The variant is fixed by pkvs_plan_create
- *                   and never changes with the planned batch
+ *  prefill_variant  prefill kernel shape: 0 = planner's choice (from head_dim,
+ *                   page_size and the capacities), 1 = 4 waves x 32 rows, 2 = 8
+ *                   waves x 32 rows, 3 = 4 waves x 64 rows, software-pipelined
+ *                   (2 and 3: head_dim <= 128), 4 = 8 waves x 32 rows with K/V
+ *                   rows loaded straight into LDS, 5 = as 4 with 64-key steps
+ *                   and 16-byte loads into a chunk-permuted LDS layout, 6 = as
+ *                   5 with 4 waves x 32 rows and two workgroups per CU (4, 5
+ *                   and 6: head_dim 128, 16-bit K/V; they hold an item's page
+ *                   ids in an LDS table of 2048 entries, 8192 for variant 5, so
+ *                   a plan whose capacities let one item span more pages --
+ *                   (kv_capacity - 1) / page_size + 1, or with a window
+ *                   (window_left + query tile + 2 key tiles - 3) / page_size +
+ *                   2 if smaller -- runs variant 2 instead); rows are (query
+ *                   token, head) pairs.  The variant is fixed by
+ *                   pkvs_plan_create and never changes with the planned batch
  *  batch_capacity   largest batch a plan() call may describe
  *  qo_capacity      prefill, cascade: largest total number of query tokens
  *  kv_capacity      largest kv_len of one request (cascade: the most cached

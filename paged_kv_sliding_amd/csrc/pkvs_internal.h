@@ -84,13 +84,18 @@ enum PrefillVariant {
                           // (head_dim 128; an item's key range spans at most
                           // kPrefillDmaPages pages)
     kPrefillBig = 5,      // as 4 with 64-key steps and 16-byte loads into an
-                          // XOR-swizzled unpadded LDS layout
+                          // XOR-swizzled unpadded LDS layout (an item's key
+                          // range spans at most kPrefillBigPages pages)
     kPrefillDuo = 6,      // as 5 with 4 waves x 32 rows, two workgroups per CU
                           // (K and V in two-tile rings, a page table sized
                           // from the plan)
 };
 constexpr int kPrefillBigTile = 64;    // keys per step of kPrefillBig
 constexpr int kPrefillDmaPages = 2048;
+// kPrefillBig's LDS page table: with one workgroup per CU its 32 KiB fit
+// beside the K and V rings, and a window of up to about 8000 keys fits at
+// page size 1
+constexpr int kPrefillBigPages = 8192;
 // A contiguous ("ragged") K/V of [tokens, kv heads, head_dim] is addressed like
 // a paged cache whose page-table entries are row indices: entry t of a request
 // starting at row r0 is r0 + t * kRaggedPage, and key j sits on row

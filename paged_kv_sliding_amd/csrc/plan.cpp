@@ -362,8 +362,9 @@ static int build_prefill(Plan *p, const std::vector<Req> &reqs)
     // capacities can span more pages than the table (dma_table_pages_bound)
     if (p->prefill_variant == kPrefillDma || p->prefill_variant == kPrefillBig ||
         p->prefill_variant == kPrefillDuo) {
-        const int64_t table =
-            p->prefill_variant == kPrefillDuo ? p->table_pages : int64_t(kPrefillDmaPages);
+        const int64_t table = p->prefill_variant == kPrefillDuo ? int64_t(p->table_pages)
+                              : p->prefill_variant == kPrefillBig ? int64_t(kPrefillBigPages)
+                                                                  : int64_t(kPrefillDmaPages);
         for (const It &it : items) {
             const int64_t kb = it.w[kPiKvBegin];
             const int64_t kv_len = it.w[kPiKvLen];
@@ -624,7 +625,12 @@ static int create_plan(const pkvs_desc *desc, bool ragged, Plan **out, bool make
         int v = kPrefillRows128;
         bool big_for_split = false;
         if (desc->head_dim <= 128 && big_tiles >= 2 * p->num_cus) {
-            v = desc->head_dim == 128 && kvf == PKVS_KV_SAME ? kPrefillBig : kPrefillRows256;
+            // (below 8 keys per page every lane of the 64-key kernel loads its
+            // own row, and with the device full the 256-row kernel measured
+            // 1.4 % faster at page size 1)
+            v = desc->head_dim == 128 && kvf == PKVS_KV_SAME && desc->page_size >= 8
+                    ? kPrefillBig
+                    : kPrefillRows256;
         } else if (key_split && !desc->disable_split_kv && !ragged && !fp32 &&
                    desc->head_dim == 128 && kvf == PKVS_KV_SAME) {
             int64_t span = desc->kv_capacity;
@@ -640,9 +646,10 @@ static int create_plan(const pkvs_desc *desc, bool ragged, Plan **out, bool make
             big_for_split = false;
         }
         // the direct-to-LDS variants need 104-156 KiB of LDS per workgroup
-        // ... and an LDS table of at most kPrefillDmaPages page ids per item:
-        // they are kept only when no item within the capacities can span more
-        // pages (kPrefillDuo sizes its table to that span).  The choice holds
+        // ... and an LDS table of at most kPrefillDmaPages page ids per item
+        // (kPrefillBig: kPrefillBigPages): they are kept only when no item
+        // within the capacities can span more pages (kPrefillDuo sizes its
+        // table to that span).  The choice holds
         // for the plan's lifetime, so a captured run keeps launching the
         // kernel that every later plan() builds its items for.
         const bool dma_v = v == kPrefillDma || v == kPrefillBig || v == kPrefillDuo;
@@ -650,7 +657,8 @@ static int create_plan(const pkvs_desc *desc, bool ragged, Plan **out, bool make
         if (dma_v) {
             span = item_pages_bound(*desc, v == kPrefillDma ? kPrefillKvTile : kPrefillBigTile,
                                     (v == kPrefillDuo ? 128 : 256) / group);
-            if (span > kPrefillDmaPages) v = big_for_split ? kPrefillRows128 : kPrefillRows256;
+            if (span > (v == kPrefillBig ? kPrefillBigPages : kPrefillDmaPages))
+                v = big_for_split ? kPrefillRows128 : kPrefillRows256;
         }
         if (v == kPrefillDuo) p->table_pages = int(std::min<int64_t>(kPrefillDmaPages,
                                                                      (span + 15) / 16 * 16));

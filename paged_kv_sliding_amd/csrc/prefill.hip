@@ -1089,7 +1089,7 @@ __global__ __launch_bounds__(512) void prefill_big_kernel(PrefillArgs a)
     struct Lds {
         uint8_t kset[3][BIG_HALF];  // K ring: tile t in kset[t % 3]
         uint8_t vset[3][BIG_HALF];  // V ring: tile t in vset[t % 3]
-        int32_t pages[kPrefillDmaPages];
+        int32_t pages[kPrefillBigPages];
         int32_t next_item;
     };
     __shared__ __attribute__((aligned(1024))) Lds sh;
@@ -1213,7 +1213,7 @@ __global__ __launch_bounds__(512) void prefill_big_kernel(PrefillArgs a)
 
         // page id of `key` from the LDS table (clamped into it and the cache)
         auto page_entry = [&](int key) __attribute__((always_inline)) {
-            const int e = min(max((key >> a.log2_page) - pt_lo, 0), kPrefillDmaPages - 1);
+            const int e = min(max((key >> a.log2_page) - pt_lo, 0), kPrefillBigPages - 1);
             return min(max(sh.pages[e], 0), int32_t(a.num_pages - 1));
         };
         // the wave's 8 rows of tile t (ring position p = t % 3): K and V, four loads
@@ -1259,7 +1259,7 @@ __global__ __launch_bounds__(512) void prefill_big_kernel(PrefillArgs a)
         {
             const int cache_last = min(kv_last, split - 1);
             const int pt_n = ntiles > 0 && cache_last >= kv_begin
-                                 ? min((cache_last >> a.log2_page) - pt_lo + 1, kPrefillDmaPages)
+                                 ? min((cache_last >> a.log2_page) - pt_lo + 1, kPrefillBigPages)
                                  : 0;
             for (int e = tid; e < pt_n; e += 512) {
                 const int32_t pg = a.kv_indices[page_base + pt_lo + e];

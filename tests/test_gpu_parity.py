@@ -184,9 +184,11 @@ def test_prefill_dma_variant_prefix_non_causal_and_fallback(variant):
     assert att.info().prefill_variant == variant
     ro, rl = oracle_for(case)
     compare(o, lse, ro, rl, tag=f"dma variant {variant} non-causal")
-    # page size 1 and 2100 keys: an item spans more pages than the LDS page
-    # table holds, so the plan runs the register-staged 256-row kernel
-    case = small([40], [2100], H_q=8, H_kv=2, D=128, P_=1, W=-1, seed=22)
+    # page size 1 and 2100 keys (variant 5: 8300): an item spans more pages
+    # than the LDS page table holds, so the plan runs the register-staged
+    # 256-row kernel
+    case = small([40], [8300 if variant == 5 else 2100], H_q=8, H_kv=2, D=128, P_=1, W=-1,
+                 seed=22)
     att = make_attention(case, prefill_variant=variant)
     o, lse = gpu_run(case, att=att)
     assert att.info().prefill_variant == 2
@@ -604,13 +606,13 @@ def _layout_case(case, picks):
         kv_indices=pages, kv_last_page_len=last)
 
 
-@pytest.mark.parametrize("W,kv_cap,want", [(-1, 3000, 2), (1023, 8192, 5)])
+@pytest.mark.parametrize("W,kv_cap,want", [(-1, 8300, 2), (1023, 8192, 5), (-1, 8000, 5)])
 def test_graph_replay_variant_fixed_by_capacity(W, kv_cap, want):
     """The prefill kernel is chosen when the plan is created, from its
     capacities: a run() captured while a short batch is planned replays the
     same kernel after a re-plan whose items span thousands of keys (page size 1,
-    so every key is a page; the direct-to-LDS kernels hold 2048 page ids per
-    item).  Every replay matches the oracle of the batch planned last."""
+    so every key is a page; the 64-key kernel holds 8192 page ids per item).
+    Every replay matches the oracle of the batch planned last."""
     case = small([64, 3, 40], [kv_cap, 700, 1000], H_q=8, H_kv=2, D=128, P_=1, W=W,
                  seed=64 + W)
     att = make_attention(case, prefill_variant=5)

@@ -273,40 +273,48 @@ def test_decode_chunks_partition_the_window(W, split):
 
 def test_prefill_variant_choice_and_page_table_fallback():
     """Large head_dim-128 prefill plans pick the 64-key-step direct-to-LDS
-    kernel (variant 5).  The direct-to-LDS variants hold an item's page ids in
-    a 2048-entry LDS table, so a plan whose capacities let one item span more
-    pages runs the register-staged 256-row kernel (variant 2) from creation on;
-    the variant never changes between plan() calls of one plan object (a
-    captured run keeps launching the kernel it was captured with)."""
+    kernel (variant 5) at page sizes of 8 keys or more, the 256-row kernel
+    (variant 2) below.  The direct-to-LDS variants hold an item's page ids in
+    an LDS table (variants 4 and 6: 2048 entries, 5: 8192), so a plan whose
+    capacities let one item span more pages runs the register-staged 256-row
+    kernel (variant 2) from creation on; the variant never changes between
+    plan() calls of one plan object (a captured run keeps launching the kernel
+    it was captured with)."""
     big = dict(num_qo_heads=32, num_kv_heads=8, window_left=-1, qo_capacity=32768,
                kv_capacity=32768, batch_capacity=4)
-    for v in (0, 4, 5, 6):
-        # no window, 32768 keys of 16: at most 2048 pages per item -> kept
-        hv = P.pkvs_plan_create(desc(page_size=16, prefill_variant=v, **big))
+    for v, table in ((0, 8192), (4, 2048), (5, 8192), (6, 2048)):
+        # no window, keys of 16 per page: at most `table` pages per item -> kept
+        cap = table * 16
+        hv = P.pkvs_plan_create(desc(page_size=16, prefill_variant=v, **dict(big, kv_capacity=cap)))
         assert P.pkvs_plan_get_info(hv).prefill_variant == (v or 5)
-        for qo, kv in (([4096], [4096]), ([64], [32768]), ([1] * 4, [1, 40, 30000, 7])):
+        for qo, kv in (([4096], [4096]), ([64], [cap]), ([1] * 4, [1, 40, cap - 100, 7])):
             qop, kvp, last = csr(qo, kv, 16)
             P.pkvs_prefill_plan(hv, qop, kvp, last, len(kv), None, None)
             assert P.pkvs_plan_get_info(hv).prefill_variant == (v or 5)
-        # one key more per request allows 2049 pages -> variant 2 from creation
+        # one key more per request allows one page more -> variant 2 from creation
         hv = P.pkvs_plan_create(desc(page_size=16, prefill_variant=v,
-                                     **dict(big, kv_capacity=32769)))
+                                     **dict(big, kv_capacity=cap + 1)))
         assert P.pkvs_plan_get_info(hv).prefill_variant == 2
         qop, kvp, last = csr([64], [4096], 16)
         P.pkvs_prefill_plan(hv, qop, kvp, last, 1, None, None)
         assert P.pkvs_plan_get_info(hv).prefill_variant == 2
-    # page size 1 without a window: 3000 keys are 3000 pages -> variant 2
-    h = P.pkvs_plan_create(desc(page_size=1, prefill_variant=5, **dict(big, kv_capacity=3000)))
+    # page size 1 without a window: 8193 keys are 8193 pages -> variant 2
+    h = P.pkvs_plan_create(desc(page_size=1, prefill_variant=5, **dict(big, kv_capacity=8193)))
+    assert P.pkvs_plan_get_info(h).prefill_variant == 2
+    # the planner's choice at page size 1 with the device full: variant 2
+    h = P.pkvs_plan_create(desc(page_size=1, **dict(big, window_left=1023, kv_capacity=4096)))
     assert P.pkvs_plan_get_info(h).prefill_variant == 2
     # with a window the span is bounded by window_left: 1023 + 64 + 128 keys
-    h1 = P.pkvs_plan_create(desc(page_size=1, **dict(big, window_left=1023, kv_capacity=65536)))
+    h1 = P.pkvs_plan_create(desc(page_size=1, prefill_variant=5,
+                                 **dict(big, window_left=1023, kv_capacity=65536)))
     for qo, kv in (([8192], [8192]), ([100, 3000], [1000, 60000])):
         qop, kvp, last = csr(qo, kv, 1)
         P.pkvs_prefill_plan(h1, qop, kvp, last, len(kv), None, None)
         assert P.pkvs_plan_get_info(h1).prefill_variant == 5
     # largest window that still fits: W + 64 + 2*64 - 3 keys -> W/1 + 2 pages
-    for W, want in ((1857, 5), (1858, 2)):
-        hw = P.pkvs_plan_create(desc(page_size=1, **dict(big, window_left=W, kv_capacity=65536)))
+    for W, want in ((8001, 5), (8002, 2)):
+        hw = P.pkvs_plan_create(desc(page_size=1, prefill_variant=5,
+                                     **dict(big, window_left=W, kv_capacity=65536)))
         assert P.pkvs_plan_get_info(hw).prefill_variant == want, W
         if want == 5:
             # the worst item of that window spans exactly the table or less
@@ -319,7 +327,7 @@ def test_prefill_variant_choice_and_page_table_fallback():
                 kv_end = min(kv_len, pos0 + qn)
                 lastk = min(kb + -(-(kv_end - kb) // 64) * 64, kv_len) - 1
                 spans.append(lastk - kb + 1)
-            assert max(spans) <= 2048
+            assert max(spans) <= 8192
     # head_dim 64 keeps the register-staged kernel; asking for 4 is refused
     assert P.pkvs_plan_get_info(P.pkvs_plan_create(desc(head_dim=64, **big))).prefill_variant == 2
     for v in (4, 5, 6):
