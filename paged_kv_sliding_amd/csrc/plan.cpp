@@ -51,6 +51,15 @@ static bool is_pow2(int64_t x) { return x > 0 && (x & (x - 1)) == 0; }
 
 static int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
 
+// Work-list order key: decreasing cost (0 <= cost < 2^31), then increasing
+// index; sorting the keys as plain integers gives that order (std::sort is in
+// place: a plan of a reserved size allocates nothing).
+static uint64_t sort_key(int64_t cost, int64_t index)
+{
+    return (uint64_t(uint32_t(INT32_MAX - std::min<int64_t>(cost, INT32_MAX))) << 32) |
+           uint32_t(index);
+}
+
 // Capacity-derived sizes; depend on the descriptor and the device only.
 static void size_plan(Plan *p)
 {
@@ -182,9 +191,6 @@ static int validate_desc(const pkvs_desc *d)
     return PKVS_OK;
 }
 
-static_assert(sizeof(DecodeWork::w) == sizeof(int32_t) * kDecodeItemWords,
-              "DecodeWork holds one decode item");
-
 static int read_layout(const Plan *p, const int32_t *qo_indptr, const int32_t *kv_indptr,
                        const int32_t *last, int32_t batch, std::vector<Req> &out)
 {
@@ -233,17 +239,23 @@ static int read_layout(const Plan *p, const int32_t *qo_indptr, const int32_t *k
 // Prefill work list: (request, kv head, query tile).  The first key tile of an
 // item is the one holding the window start of its first query; the last is
 // the one holding its last query's position (causal).  Items are ordered by
-// decreasing key count so a strided persistent grid receives a balanced mix;
-// within one cost the kv head runs fastest.
+// decreasing key count, so the longest start first; the kv heads of one tile
+// (equal counts) are consecutive.  The order is a sort of the query tiles (or
+// key chunks), not of the items: every kv head of a tile has its key count.
 static int build_prefill(Plan *p, const std::vector<Req> &reqs)
 {
     const pkvs_desc &d = p->desc;
     const int tq = p->query_tile;
+    const int64_t H = d.num_kv_heads;
     const int kv_tile = p->prefill_variant == kPrefillBig || p->prefill_variant == kPrefillDuo
                             ? kPrefillBigTile
                             : kPrefillKvTile;
-    struct It { int64_t cost; int32_t w[kPrefillItemWords]; };
-    std::vector<It> items;
+    // a query tile, or one key chunk of one (all kv heads)
+    struct Tile {
+        int32_t b, q_begin, qn, pos0, kv_begin, kv_end;
+        int32_t slot, chunks;  // first partial slot of kv head 0 (-1: not cut), chunks of the tile
+    };
+    std::vector<Tile> tiles;
     for (size_t b = 0; b < reqs.size(); ++b) {
         const Req &r = reqs[b];
         // first query position: after the request's cached prefix, or (a
@@ -256,39 +268,24 @@ static int build_prefill(Plan *p, const std::vector<Req> &reqs)
             if (d.window_left >= 0) kv_begin = std::max<int64_t>(0, pos0 - d.window_left);
             kv_begin = kv_begin / kv_tile * kv_tile;
             const int64_t kv_end = d.causal ? std::min<int64_t>(r.kv_len, pos0 + qn) : r.kv_len;
-            for (int32_t hk = 0; hk < d.num_kv_heads; ++hk) {
-                It it;
-                it.cost = kv_end - kv_begin;
-                it.w[kPiRequest] = int32_t(b);
-                it.w[kPiKvHead] = hk;
-                it.w[kPiQBegin] = int32_t(r.qo_begin + t0);
-                it.w[kPiQCount] = int32_t(qn);
-                it.w[kPiPos0] = int32_t(pos0);
-                it.w[kPiKvLen] = int32_t(r.kv_len);
-                it.w[kPiPageBase] = int32_t(r.page_base);
-                it.w[kPiKvBegin] = int32_t(kv_begin);
-                it.w[kPiSplit] = int32_t(std::min<int64_t>(r.split, INT32_MAX));
-                it.w[kPiKvEnd] = int32_t(std::max(kv_end, kv_begin));
-                it.w[kPiSlot] = -1;
-                it.w[kPiSlotStride] = 0;
-                items.push_back(it);
-            }
+            tiles.push_back(Tile{int32_t(b), int32_t(r.qo_begin + t0), int32_t(qn), int32_t(pos0),
+                                 int32_t(kv_begin), int32_t(std::max(kv_end, kv_begin)), -1, 1});
         }
     }
+    auto tiles_of = [&](const Tile &t) { return ceil_div(int64_t(t.kv_end) - t.kv_begin, kv_tile); };
     // Key split: with at most one tile per kSplitFillShare resident
-    // workgroups, cut the longest tiles' key ranges into chunks of about c
-    // whole key tiles (each a work item with partial slots), c the smallest
-    // chunk length with at most one item per resident workgroup in all (a
-    // second round would undo the cut), when the longest item then ends
-    // sooner by more than the merge costs; the merge entries combine each
-    // token's chunks.
+    // workgroups (per kv head), cut the longest tiles' key ranges into chunks
+    // of about c whole key tiles (each a work item per kv head with partial
+    // slots), c the smallest chunk length with at most one item per resident
+    // workgroup in all (a second round would undo the cut), when the longest
+    // item then ends sooner by more than the merge costs; the merge entries
+    // combine each token's chunks.
     std::vector<int32_t> merges;
-    if (p->key_chunks_max > 1 && int64_t(items.size()) * kSplitFillShare <= p->grid_blocks) {
-        auto tiles_of = [&](const It &it) { return ceil_div(std::max<int64_t>(it.cost, 0), kv_tile); };
+    if (p->key_chunks_max > 1 && int64_t(tiles.size()) * H * kSplitFillShare <= p->grid_blocks) {
         int64_t total = 0, longest = 0;
-        for (const It &it : items) {
-            total += tiles_of(it);
-            longest = std::max(longest, tiles_of(it));
+        for (const Tile &t : tiles) {
+            total += tiles_of(t) * H;
+            longest = std::max(longest, tiles_of(t));
         }
         int64_t c = 0;
         // chunks of a tile of t key tiles for chunk length c (at most
@@ -300,7 +297,7 @@ static int build_prefill(Plan *p, const std::vector<Req> &reqs)
         auto items_at = [&](int64_t len) {
             c = len;
             int64_t n = 0;
-            for (const It &it : items) n += chunks_of(tiles_of(it));
+            for (const Tile &t : tiles) n += chunks_of(tiles_of(t)) * H;
             return n;
         };
         // (items_at is non-increasing in the length; at the longest tile it
@@ -314,66 +311,55 @@ static int build_prefill(Plan *p, const std::vector<Req> &reqs)
         }
         items_at(lo);
         int64_t longest_chunk = 0;
-        for (const It &it : items) {
-            const int64_t t = tiles_of(it);
-            longest_chunk = std::max(longest_chunk, ceil_div(t, chunks_of(t)));
-        }
+        for (const Tile &t : tiles)
+            longest_chunk = std::max(longest_chunk, ceil_div(tiles_of(t), chunks_of(tiles_of(t))));
         if (longest > longest_chunk + kMergeTiles) {
-            std::vector<It> cut;
+            std::vector<Tile> cut;
             int64_t slot = 0;
-            for (const It &it : items) {
-                const int64_t t = tiles_of(it);
-                const int64_t n = chunks_of(t);
+            for (const Tile &t : tiles) {
+                const int64_t kt = tiles_of(t);
+                const int64_t n = chunks_of(kt);
                 if (n <= 1) {
-                    cut.push_back(it);
+                    cut.push_back(t);
                     continue;
                 }
-                const int64_t qn = it.w[kPiQCount];
-                if (slot + qn * n > p->slots_cap ||
-                    int64_t(merges.size() / kMergeWords) + qn > p->merges_cap)
+                // kv head hk's token r, chunk k: slot + (hk qn + r) n + k
+                if (slot + H * t.qn * n > p->slots_cap ||
+                    int64_t(merges.size() / kMergeWords) + H * t.qn > p->merges_cap)
                     return fail(PKVS_ERR_CAPACITY, "key-split prefill needs more partial slots "
                                 "than the plan's %lld", (long long)p->slots_cap);
-                for (int64_t r = 0; r < qn; ++r)
-                    merges.insert(merges.end(), {int32_t(it.w[kPiQBegin] + r), it.w[kPiKvHead],
-                                                 int32_t(slot + r * n), int32_t(n)});
+                for (int64_t hk = 0; hk < H; ++hk)
+                    for (int64_t r = 0; r < t.qn; ++r)
+                        merges.insert(merges.end(), {int32_t(t.q_begin + r), int32_t(hk),
+                                                     int32_t(slot + (hk * t.qn + r) * n),
+                                                     int32_t(n)});
                 // n chunks of per key tiles, the last one shorter (never empty)
-                const int64_t per = ceil_div(t, n);
-                const int64_t kb = it.w[kPiKvBegin], ke = it.w[kPiKvEnd];
+                const int64_t per = ceil_div(kt, n);
                 for (int64_t k = 0; k < n; ++k) {
-                    It ch = it;
-                    const int64_t b0 = kb + k * per * kv_tile;
-                    const int64_t b1 = k + 1 == n ? ke : b0 + per * kv_tile;
-                    ch.cost = b1 - b0;
-                    ch.w[kPiKvBegin] = int32_t(b0);
-                    ch.w[kPiKvEnd] = int32_t(b1);
-                    ch.w[kPiSlot] = int32_t(slot + k);
-                    ch.w[kPiSlotStride] = int32_t(n);
+                    Tile ch = t;
+                    ch.kv_begin = int32_t(t.kv_begin + k * per * kv_tile);
+                    ch.kv_end = k + 1 == n ? t.kv_end : int32_t(ch.kv_begin + per * kv_tile);
+                    ch.slot = int32_t(slot + k);
+                    ch.chunks = int32_t(n);
                     cut.push_back(ch);
                 }
-                slot += qn * n;
+                slot += H * t.qn * n;
             }
-            items.swap(cut);
+            tiles.swap(cut);
         }
     }
-    std::stable_sort(items.begin(), items.end(),
-                     [](const It &a, const It &b) { return a.cost > b.cost; });
     // the direct-to-LDS variants keep an item's page ids in an LDS table; the
     // variant was fixed at plan creation so that no item within the
-    // capacities can span more pages than the table (dma_table_pages_bound)
+    // capacities can span more pages than the table (item_pages_bound)
     if (p->prefill_variant == kPrefillDma || p->prefill_variant == kPrefillBig ||
         p->prefill_variant == kPrefillDuo) {
         const int64_t table = p->prefill_variant == kPrefillDuo ? int64_t(p->table_pages)
                               : p->prefill_variant == kPrefillBig ? int64_t(kPrefillBigPages)
                                                                   : int64_t(kPrefillDmaPages);
-        for (const It &it : items) {
-            const int64_t kb = it.w[kPiKvBegin];
-            const int64_t kv_len = it.w[kPiKvLen];
-            const int64_t kv_end = std::min<int64_t>(
-                it.w[kPiKvEnd],
-                d.causal ? std::min<int64_t>(kv_len, int64_t(it.w[kPiPos0]) + it.w[kPiQCount])
-                         : kv_len);
-            if (kv_end <= kb) continue;
-            const int64_t last = std::min(kb + ceil_div(kv_end - kb, kv_tile) * kv_tile,
+        for (const Tile &t : tiles) {
+            const int64_t kb = t.kv_begin, kv_len = reqs[size_t(t.b)].kv_len;
+            if (t.kv_end <= kb) continue;
+            const int64_t last = std::min(kb + ceil_div(t.kv_end - kb, kv_tile) * kv_tile,
                                           kv_len) - 1;
             if (last / d.page_size - kb / d.page_size + 1 > table)
                 return fail(PKVS_ERR_CAPACITY, "a prefill item spans %lld pages of keys, more "
@@ -382,10 +368,16 @@ static int build_prefill(Plan *p, const std::vector<Req> &reqs)
                             (long long)table);
         }
     }
-    p->n_items = int64_t(items.size());
+    // longest first, ties in the order made
+    std::vector<uint64_t> order(tiles.size());
+    for (size_t i = 0; i < tiles.size(); ++i)
+        order[i] = sort_key(int64_t(tiles[i].kv_end) - tiles[i].kv_begin, int64_t(i));
+    std::sort(order.begin(), order.end());
+    const int64_t n_items = int64_t(tiles.size()) * H;
+    p->n_items = n_items;
     p->n_merges = int64_t(merges.size() / kMergeWords);
     p->split_size = 0;
-    const size_t merge_off = kHeaderWords + items.size() * kPrefillItemWords;
+    const size_t merge_off = kHeaderWords + size_t(n_items) * kPrefillItemWords;
     p->host_ws.assign(p->lead_words + merge_off + merges.size(), 0);
     int64_t keys = 0;
     for (const Req &r : reqs) keys += r.kv_len;
@@ -398,12 +390,38 @@ static int build_prefill(Plan *p, const std::vector<Req> &reqs)
                 p->host_ws[r.page_base + t] = int32_t(r.qo_begin + t * kRaggedPage);
     }
     int32_t *w = p->host_ws.data() + p->lead_words;
-    w[kHdrNumItems] = int32_t(items.size());
+    w[kHdrNumItems] = int32_t(n_items);
     w[kHdrNumMerges] = int32_t(p->n_merges);
     w[kHdrMergeOffset] = int32_t(merge_off);
     w[kHdrItemWords] = kPrefillItemWords;
-    for (size_t i = 0; i < items.size(); ++i)
-        std::memcpy(w + kHeaderWords + i * kPrefillItemWords, items[i].w, sizeof items[i].w);
+    // (ties in the order made: (tile, kv head, chunk) -- each run of
+    // equal-length chunks of one tile is emitted kv head by kv head)
+    int32_t *it = w + kHeaderWords;
+    for (size_t i0 = 0, i1; i0 < order.size(); i0 = i1) {
+        const Tile &t0 = tiles[size_t(uint32_t(order[i0]))];
+        for (i1 = i0 + 1; i1 < order.size() && (order[i1] >> 32) == (order[i0] >> 32) &&
+                          tiles[size_t(uint32_t(order[i1]))].q_begin == t0.q_begin &&
+                          tiles[size_t(uint32_t(order[i1]))].b == t0.b;
+             ++i1) {
+        }
+        for (int64_t hk = 0; hk < H; ++hk)
+            for (size_t i = i0; i < i1; ++i, it += kPrefillItemWords) {
+                const Tile &t = tiles[size_t(uint32_t(order[i]))];
+                const Req &r = reqs[size_t(t.b)];
+                it[kPiRequest] = t.b;
+                it[kPiKvHead] = int32_t(hk);
+                it[kPiQBegin] = t.q_begin;
+                it[kPiQCount] = t.qn;
+                it[kPiPos0] = t.pos0;
+                it[kPiKvLen] = int32_t(r.kv_len);
+                it[kPiPageBase] = int32_t(r.page_base);
+                it[kPiKvBegin] = t.kv_begin;
+                it[kPiSplit] = int32_t(std::min<int64_t>(r.split, INT32_MAX));
+                it[kPiKvEnd] = t.kv_end;
+                it[kPiSlot] = t.slot < 0 ? -1 : int32_t(t.slot + hk * t.qn * t.chunks);
+                it[kPiSlotStride] = t.slot < 0 ? 0 : t.chunks;
+            }
+    }
     std::copy(merges.begin(), merges.end(), w + merge_off);
     return PKVS_OK;
 }
@@ -446,12 +464,20 @@ static int build_decode(Plan *p, const std::vector<Req> &reqs)
 {
     const pkvs_desc &d = p->desc;
     const int64_t c = choose_split(p, reqs);
+    const int64_t H = d.num_kv_heads;
     // (the buffers were reserved for the capacities: no allocation here)
-    std::vector<DecodeWork> &items = p->work_buf;
     std::vector<int32_t> &merges = p->merge_buf;
-    items.clear();
+    std::vector<int64_t> &first_slot = p->req_slot;  // per request: slot of kv head 0, chunk 0
+    std::vector<int32_t> &chunks = p->req_chunks;    // per request: its chunks
+    std::vector<uint64_t> &order = p->order_key;     // per (request, chunk): sort_key
+    std::vector<int32_t> &pair_req = p->pair_req, &pair_chunk = p->pair_chunk;
     merges.clear();
-    int64_t slot = 0;
+    first_slot.clear();
+    chunks.clear();
+    order.clear();
+    pair_req.clear();
+    pair_chunk.clear();
+    int64_t slot = 0, n_items = 0;
     for (size_t b = 0; b < reqs.size(); ++b) {
         const Req &r = reqs[b];
         const int64_t ws =
@@ -461,52 +487,73 @@ static int build_decode(Plan *p, const std::vector<Req> &reqs)
         // a trailing piece shorter than one key block joins the chunk before it
         // rather than becoming a work item and a partial of its own
         if (nchunks > 1 && r.kv_len - base - (nchunks - 1) * c < kDecodeBlock) --nchunks;
-        if (int64_t(items.size()) + d.num_kv_heads * nchunks > p->items_cap ||
-            (nchunks > 1 && (slot + d.num_kv_heads * nchunks > p->slots_cap ||
-                             int64_t(merges.size() / kMergeWords) + d.num_kv_heads >
-                                 p->merges_cap)))
+        if (n_items + H * nchunks > p->items_cap ||
+            (nchunks > 1 && (slot + H * nchunks > p->slots_cap ||
+                             int64_t(merges.size() / kMergeWords) + H > p->merges_cap)))
             return fail(PKVS_ERR_CAPACITY, "decode work list exceeds the plan capacity (%lld "
                         "items, %lld partial slots) at request %zu", (long long)p->items_cap,
                         (long long)p->slots_cap, b);
-        for (int32_t hk = 0; hk < d.num_kv_heads; ++hk) {
-            if (nchunks > 1) {
-                merges.insert(merges.end(), {int32_t(b), hk, int32_t(slot), int32_t(nchunks)});
-            }
-            for (int64_t k = 0; k < nchunks; ++k) {
-                DecodeWork it;
-                const int64_t t0 = base + k * c;
-                const int64_t t1 = k + 1 == nchunks ? r.kv_len : t0 + c;
-                it.cost = t1 - t0;
-                it.order = int32_t(items.size());
-                it.w[kDiRequest] = int32_t(b);
-                it.w[kDiKvHead] = hk;
-                it.w[kDiTokBegin] = int32_t(t0);
-                it.w[kDiTokEnd] = int32_t(t1);
-                it.w[kDiVisLo] = int32_t(std::max(ws, t0));
-                it.w[kDiPageBase] = int32_t(r.page_base);
-                it.w[kDiSlot] = nchunks > 1 ? int32_t(slot++) : -1;
-                it.w[kDiKvLen] = int32_t(r.kv_len);
-                items.push_back(it);
-            }
+        // kv head hk's chunk k of a split request: slot first + hk nchunks + k
+        first_slot.push_back(nchunks > 1 ? slot : -1);
+        chunks.push_back(int32_t(nchunks));
+        if (nchunks > 1) {
+            for (int64_t hk = 0; hk < H; ++hk)
+                merges.insert(merges.end(), {int32_t(b), int32_t(hk), int32_t(slot + hk * nchunks),
+                                             int32_t(nchunks)});
+            slot += H * nchunks;
         }
+        for (int64_t k = 0; k < nchunks; ++k) {
+            const int64_t t0 = base + k * c;
+            const int64_t t1 = k + 1 == nchunks ? r.kv_len : t0 + c;
+            order.push_back(sort_key(t1 - t0, int64_t(pair_req.size())));
+            pair_req.push_back(int32_t(b));
+            pair_chunk.push_back(int32_t(k));
+        }
+        n_items += H * nchunks;
     }
-    // longest first, ties in the order made (a full order: std::sort needs no
-    // temporary buffer)
-    std::sort(items.begin(), items.end(), [](const DecodeWork &a, const DecodeWork &b) {
-        return a.cost > b.cost || (a.cost == b.cost && a.order < b.order);
-    });
-    p->n_items = int64_t(items.size());
+    // longest first, ties in the order made: (request, kv head, chunk) -- the
+    // chunks are sorted and each run of equal-length chunks of one request
+    // is emitted kv head by kv head.  (Kv heads made consecutive items
+    // instead measured 6 % slower on the 64-request decode with no window.)
+    std::sort(order.begin(), order.end());
+    p->n_items = n_items;
     p->n_merges = int64_t(merges.size() / kMergeWords);
     p->split_size = int32_t(std::min<int64_t>(c, INT32_MAX));
-    const size_t merge_off = kHeaderWords + items.size() * kDecodeItemWords;
+    const size_t merge_off = kHeaderWords + size_t(n_items) * kDecodeItemWords;
     p->host_ws.assign(merge_off + merges.size(), 0);
     int32_t *w = p->host_ws.data();
-    w[kHdrNumItems] = int32_t(items.size());
+    w[kHdrNumItems] = int32_t(n_items);
     w[kHdrNumMerges] = int32_t(p->n_merges);
     w[kHdrMergeOffset] = int32_t(merge_off);
     w[kHdrItemWords] = kDecodeItemWords;
-    for (size_t i = 0; i < items.size(); ++i)
-        std::memcpy(w + kHeaderWords + i * kDecodeItemWords, items[i].w, sizeof items[i].w);
+    int32_t *it = w + kHeaderWords;
+    for (size_t i0 = 0, i1; i0 < order.size(); i0 = i1) {
+        const int32_t b = pair_req[size_t(uint32_t(order[i0]))];
+        for (i1 = i0 + 1; i1 < order.size() && (order[i1] >> 32) == (order[i0] >> 32) &&
+                          pair_req[size_t(uint32_t(order[i1]))] == b;
+             ++i1) {
+        }
+        const Req &r = reqs[size_t(b)];
+        const int64_t n = chunks[size_t(b)];
+        const int64_t ws =
+            d.window_left >= 0 ? std::max<int64_t>(0, r.kv_len - 1 - d.window_left) : 0;
+        for (int64_t hk = 0; hk < H; ++hk)
+            for (size_t i = i0; i < i1; ++i, it += kDecodeItemWords) {
+                const int64_t k = pair_chunk[size_t(uint32_t(order[i]))];
+                const int64_t t0 = ws / kDecodeBlock * kDecodeBlock + k * c;
+                const int64_t t1 = k + 1 == n ? r.kv_len : t0 + c;
+                it[kDiRequest] = b;
+                it[kDiKvHead] = int32_t(hk);
+                it[kDiTokBegin] = int32_t(t0);
+                it[kDiTokEnd] = int32_t(t1);
+                it[kDiVisLo] = int32_t(std::max(ws, t0));
+                it[kDiPageBase] = int32_t(r.page_base);
+                it[kDiSlot] = first_slot[size_t(b)] < 0
+                                  ? -1
+                                  : int32_t(first_slot[size_t(b)] + hk * n + k);
+                it[kDiKvLen] = int32_t(r.kv_len);
+            }
+    }
     std::copy(merges.begin(), merges.end(), w + merge_off);
     return PKVS_OK;
 }
@@ -733,7 +780,11 @@ static int create_plan(const pkvs_desc *desc, bool ragged, Plan **out, bool make
     // decode batch allocate nothing (pkvs_decode_noalloc relies on it).
     if (desc->kind == PKVS_DECODE && !fp32 && make_buffers) {
         p->reqs_buf.reserve(size_t(desc->batch_capacity));
-        p->work_buf.reserve(size_t(p->items_cap));
+        p->req_slot.reserve(size_t(desc->batch_capacity));
+        p->req_chunks.reserve(size_t(desc->batch_capacity));
+        p->order_key.reserve(size_t(p->items_cap));
+        p->pair_req.reserve(size_t(p->items_cap));
+        p->pair_chunk.reserve(size_t(p->items_cap));
         p->merge_buf.reserve(size_t(p->merges_cap * kMergeWords));
         p->host_ws.reserve(p->int_ws_need / sizeof(int32_t));
         if (p->have_gpu) {

@@ -53,14 +53,6 @@ struct Req {
     int64_t split = INT32_MAX;
 };
 
-// One decode work item before sorting: its cost, its position in the order
-// the items were made (ties keep it) and its words.
-struct DecodeWork {
-    int64_t cost;
-    int32_t order;
-    int32_t w[8];
-};
-
 }  // namespace pkvs
 
 struct pkvs_plan {
@@ -100,8 +92,11 @@ struct pkvs_plan {
     // decode planning buffers, reserved for the capacities when the plan is
     // created, so that planning a decode batch allocates nothing
     std::vector<pkvs::Req> reqs_buf;
-    std::vector<pkvs::DecodeWork> work_buf;
     std::vector<int32_t> merge_buf;
+    std::vector<int64_t> req_slot;                // per request: its first partial slot
+    std::vector<int32_t> req_chunks;              // per request: its key chunks
+    std::vector<uint64_t> order_key;              // per (request, chunk): the order key
+    std::vector<int32_t> pair_req, pair_chunk;    // per (request, chunk): its indices
     int64_t n_items = 0, n_merges = 0;
     int32_t split_size = 0;
     int32_t batch = 0;
