@@ -33,6 +33,9 @@
  *  - Device pointers are HIP device memory owned by the caller.  The library
  *    owns only the opaque pkvs_plan (and the pinned host staging buffers it
  *    holds).  run() calls allocate nothing and are asynchronous on `stream`.
+ *    q, o, k_cache, v_cache (and a cascade's k_extend, v_extend) and the two
+ *    workspaces must be 16-byte aligned (INVALID_ARG otherwise): the kernels
+ *    move their rows in 16-byte vectors.
  *  - Layouts (all row-major, contiguous):
  *      q, o        [nnz_qo, num_qo_heads, head_dim]   (decode: nnz_qo = batch)
  *      lse         [nnz_qo, num_qo_heads] float32, natural log of the sum of

@@ -605,6 +605,8 @@ static int finish_plan(Plan *p, void *float_ws, size_t float_bytes, void *int_ws
     if (p->float_ws_need && (!float_ws || float_bytes < p->float_ws_need))
         return fail(PKVS_ERR_WORKSPACE, "float workspace %zu bytes < required %zu; increase "
                     "the workspace buffer size", float_ws ? float_bytes : 0, p->float_ws_need);
+    if ((reinterpret_cast<uintptr_t>(int_ws) | reinterpret_cast<uintptr_t>(float_ws)) & 15)
+        return fail(PKVS_ERR_INVALID_ARG, "the workspaces must be 16-byte aligned");
     if (!p->have_gpu) return fail(PKVS_ERR_HIP, "no HIP device: only dry plans are possible");
     int rc = upload(p, int_ws, stream);
     if (rc) return rc;
@@ -1091,6 +1093,8 @@ int pkvs_cascade_plan(pkvs_plan *p, const int32_t *qo_indptr_h, const int32_t *k
     if (!float_ws || float_ws_bytes < p->float_ws_need)
         return fail(PKVS_ERR_WORKSPACE, "float workspace %zu bytes < required %zu; increase "
                     "the workspace buffer size", float_ws ? float_ws_bytes : 0, p->float_ws_need);
+    if (reinterpret_cast<uintptr_t>(float_ws) & 15)
+        return fail(PKVS_ERR_INVALID_ARG, "the workspaces must be 16-byte aligned");
     rc = finish_plan(e, nullptr, 0, int_ws, p->pre_int_off, stream);
     if (!rc)
         rc = finish_plan(r, nullptr, 0, static_cast<char *>(int_ws) + p->pre_int_off,

@@ -5,6 +5,7 @@
 #include <algorithm>
 #include <cstdint>
 #include <cstring>
+#include <initializer_list>
 
 #include "pkvs_internal.h"
 #include "plan_state.h"
@@ -54,6 +55,14 @@ int log2_exact(int x)
     return r;
 }
 
+// The kernels move rows of q, o and the caches in 16-byte vectors.
+bool misaligned16(std::initializer_list<const void *> ptrs)
+{
+    uintptr_t bits = 0;
+    for (const void *x : ptrs) bits |= reinterpret_cast<uintptr_t>(x);
+    return (bits & 15) != 0;
+}
+
 // run() must repeat the window and causality the plan was made for: a run-time
 // window that silently replaces the planned one is the mismatch sglang PR
 // "Pass window_left at plan time for the SWA paged prefill wrapper" fixes.
@@ -71,6 +80,8 @@ int check_run(const pkvs_plan *p, int kind, const void *q, const void *k, const 
     if (kind == PKVS_PREFILL && causal != p->desc.causal)
         return fail(PKVS_ERR_PLAN_MISMATCH, "run causal %d differs from the planned %d", causal,
                     p->desc.causal);
+    if (misaligned16({q, k, v, o}))
+        return fail(PKVS_ERR_INVALID_ARG, "q, k_cache, v_cache and o must be 16-byte aligned");
     if (!p->planned_device)
         return fail(PKVS_ERR_NOT_PLANNED, "no device plan (plan() failed, was dry, or never "
                     "ran)");
@@ -199,6 +210,9 @@ int pkvs_cascade_run(const pkvs_plan *p, const void *q, const void *k_extend,
     if (window_left != p->desc.window_left)
         return fail(PKVS_ERR_PLAN_MISMATCH, "run window_left %d differs from the planned %d",
                     window_left, p->desc.window_left);
+    if (misaligned16({q, k_extend, v_extend, k_cache, v_cache, o}))
+        return fail(PKVS_ERR_INVALID_ARG, "q, k_extend, v_extend, k_cache, v_cache and o must "
+                    "be 16-byte aligned");
     if (!p->planned_device)
         return fail(PKVS_ERR_NOT_PLANNED, "no device plan (plan() failed, was dry, or never "
                     "ran)");

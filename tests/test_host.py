@@ -480,6 +480,39 @@ def test_run_rejects_a_window_other_than_the_planned_one():
     assert rc == P.PKVS_ERR_PLAN_MISMATCH
 
 
+def test_misaligned_tensors_and_workspaces_are_rejected():
+    """q, o, the caches, a cascade's new-token K/V and both workspaces must be
+    16-byte aligned; the checks run before any device work (the pointers are
+    never dereferenced here)."""
+    lib = P._lib
+    A, M = ctypes.c_void_p(1 << 20), ctypes.c_void_p((1 << 20) + 8)  # aligned, misaligned
+    h = P.pkvs_plan_create(desc(window_left=31))
+    qop, kvp, last = csr([5], [5], 16)
+    P.pkvs_prefill_plan(h, qop, kvp, last, 1, None, None)
+    for i in range(4):
+        t = [A, A, A, A]
+        t[i] = M
+        rc = lib.pkvs_prefill_run(h, t[0], t[1], t[2], 1, None, t[3], None, 1.0, 31, 1, 1.0,
+                                  1.0, None)
+        assert rc == P.PKVS_ERR_INVALID_ARG and "aligned" in P.last_error(), i
+    hd = P.pkvs_plan_create(desc(P.PKVS_DECODE, num_qo_heads=4, window_left=0))
+    rc = lib.pkvs_decode_run(hd, M, A, A, 1, None, A, None, 1.0, 0, 1.0, 1.0, None)
+    assert rc == P.PKVS_ERR_INVALID_ARG
+    hc = P.pkvs_plan_create(desc(P.PKVS_CASCADE, window_left=31))
+    rc = lib.pkvs_cascade_run(hc, A, M, A, A, A, 1, None, A, None, 1.0, 31, 1.0, 1.0, None)
+    assert rc == P.PKVS_ERR_INVALID_ARG
+    # a plan into misaligned workspaces (sizes large enough) fails before any copy
+    fb, ib = P.pkvs_workspace_size(h)
+    big = torch.empty(ib + 64, dtype=torch.uint8)
+    (qp, _a), (kp, _b), (lp, _c) = P._host_i32(qop), P._host_i32(kvp), P._host_i32(last)
+    fbig = torch.empty(fb + 64, dtype=torch.uint8)
+    rc = lib.pkvs_prefill_plan(h, qp, kp, lp, 1, ctypes.c_void_p(fbig.data_ptr()), fb,
+                               ctypes.c_void_p(big.data_ptr() + 4), ib, None)
+    assert rc == P.PKVS_ERR_INVALID_ARG and "aligned" in P.last_error()
+    for x in (h, hd, hc):
+        P.pkvs_plan_destroy(x)
+
+
 def test_workload_plans_fit_their_capacities():
     """The five workloads plan within the workspaces their capacities give."""
     for name in ("tiny_prefill", "prefix_prefill", "decode_sweep", "long_prefill",
