@@ -369,11 +369,14 @@ __device__ __forceinline__ void decode_compute(const DecodeBuf<D, KVF> &buf, Dec
     }
 }
 
-// Register buffers in the pipeline: for D <= 128 one wave holds three 32-key
-// buffers (two in flight while the third is consumed) and still fits in one
-// wave's 512 registers; D = 256 keeps two.
+// Register buffers in the pipeline.  16-bit K/V: D = 64 holds three 32-key
+// buffers (two in flight while the third is consumed); D >= 128 holds two,
+// one in flight while the other is consumed.  At D = 128 both fit one wave
+// per SIMD, and the third buffer measured slower: it costs register moves in
+// the loop and a longer pipeline fill at every item's start.  8-bit K/V moves
+// half the bytes per key, so it holds one buffer more at each D.
 template <int D, int KVF>
-constexpr int decode_stages() { return KVF == 0 ? (D >= 256 ? 2 : 3) : (D >= 256 ? 3 : 4); }
+constexpr int decode_stages() { return KVF == 0 ? (D >= 128 ? 2 : 3) : (D >= 256 ? 3 : 4); }
 
 // NS register buffers of 32 keys each: NS-1 blocks are in flight while one is
 // being computed.
