@@ -1315,6 +1315,10 @@ __global__ __launch_bounds__(512) void prefill_big_kernel(PrefillArgs a)
             const float p0 = fast_exp2(__builtin_fmaf(sh[t], c, -mu));
             const float p1 = fast_exp2(__builtin_fmaf(sh[t + 1], c, -mu));
             l += p0 + p1;
+            // keep the pair's add here, between the MFMAs: left free, the
+            // compiler sinks all of a step's adds past its branches into one
+            // dependent chain after the last P.V MFMA, where nothing hides it
+            asm volatile("" : "+v"(l));
             const bf16x2 pk = to16x2<F16>(f32x2{p0, p1});
             pb[b][2 * i] = pk[0];
             pb[b][2 * i + 1] = pk[1];
@@ -1422,8 +1426,13 @@ __global__ __launch_bounds__(512) void prefill_big_kernel(PrefillArgs a)
         // Step j loads tile j+2 into ring position (j+2) % 3, which tile j-1
         // left at the barrier that began the step; it lands before the
         // barrier that ends the step, when tile j+1's K is read next.
+        // The page id of the wave's first row of tile j+2 is read from the LDS
+        // table one step early (during step j-1), so the loads that begin a
+        // step do not wait for an LDS round trip.
+        int32_t pg_ahead = page_entry(min(kv_begin + 2 * BIG_T + 8 * uwave, kv_last));
         auto step = [&](int j, int p, f32x16 &sx, f32x16 &sy, f32x16 &sz) __attribute__((always_inline)) {
-            if (j + 2 < ntiles) dma_tile(j + 2, (p + 2) % 3, dma_page(j + 2));
+            if (j + 2 < ntiles) dma_tile(j + 2, (p + 2) % 3, __builtin_amdgcn_readfirstlane(pg_ahead));
+            pg_ahead = page_entry(min(kv_begin + (j + 3) * BIG_T + 8 * uwave, kv_last));
             {
                 uint32_t x0 = kvar0, x1 = kvar1, x2 = vvar;
                 asm volatile("" : "+v"(x0), "+v"(x1), "+v"(x2));
